@@ -1,0 +1,165 @@
+/*
+ * mxfp4spec.h — C ABI of the MX-FP4 speculative verification library (AMD gfx950).
+ *
+ * The library implements the two parts of the target model's verification step
+ * in speculative decoding:
+ *
+ *   1. a weight-streaming GEMM over OCP MX-FP4 weights that reads every weight
+ *      once and applies it to the T = K+1 draft positions, and
+ *   2. the rejection-sampling acceptance step over the target and draft logits.
+ *
+ * Sources (the pages this library follows):
+ *   [M11]  "Module 11. Speculative Decoding and Quantization" (Modern LLMs
+ *          lecture): §4 acceptance rule a(x) = min(1, p/q), first-rejection
+ *          stop, residual r = norm((p - q)+), bonus token; §5 edge cases
+ *          (q(t) = 0, zero draw); §12 E2M1 / E8M0 / 32-element MX blocks and
+ *          4.25 bits per value; §13 validation refuses, never repairs.
+ *   [NEWS] "Next-Gen Speculative Decoding and FP4 Quantization Shake Up LLM
+ *          Inference Economics", section "Microscaling FP4 (MX-FP4)
+ *          Integration": packed weights [N, K/2] and scales [N, K/32], fp32
+ *          accumulation, one verification pass over all K candidates.
+ *
+ * Conventions for every entry point
+ *   - Every data pointer is a DEVICE pointer, allocated and owned by the caller.
+ *     The library allocates no memory, keeps no mutable global state and is
+ *     safe to call from several host threads.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
+ *     and runs asynchronously: the caller synchronizes before reading outputs.
+ *   - Arrays are row-major and contiguous.
+ *   - Errors that the host can see (NULL pointers, sizes, alignment, workspace
+ *     size) are returned BEFORE any HIP call, and nothing is enqueued.
+ *     MXS_ERR_DEVICE is returned when no HIP device is usable or the current
+ *     device is not gfx950; MXS_ERR_LAUNCH when a kernel launch fails.
+ *   - Conditions only the device can see are OR-ed into the caller's
+ *     `*dev_flags` word (device memory) with the MXS_FLAG_* bits. The library
+ *     never clears it: zero it before a call to read that call's flags alone.
+ *     `dev_flags` may be NULL, in which case nothing is reported.
+ */
+#ifndef MXFP4SPEC_H
+#define MXFP4SPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mxs_status {
+  MXS_OK = 0,
+  MXS_ERR_NULL = 1,      /* a required pointer is NULL */
+  MXS_ERR_SHAPE = 2,     /* a size is out of range (see each entry point) */
+  MXS_ERR_ALIGN = 3,     /* a pointer is not aligned as documented */
+  MXS_ERR_WORKSPACE = 4, /* the workspace is smaller than the query returns */
+  MXS_ERR_DEVICE = 5,    /* no usable HIP device, or it is not gfx950 */
+  MXS_ERR_LAUNCH = 6     /* a kernel launch failed */
+} mxs_status;
+
+/* Device-detected conditions (bits of *dev_flags). */
+#define MXS_FLAG_NONFINITE 1     /* NaN/+inf input (or a logit row with no finite value) */
+#define MXS_FLAG_TOKEN_RANGE 2   /* a draft token outside [0, V) */
+#define MXS_FLAG_Q_ZERO 4        /* a draft token with draft probability 0 */
+#define MXS_FLAG_RESIDUAL_ZERO 8 /* a rejection whose residual (p - q)+ had zero mass */
+
+#define MXS_ABI_VERSION 1
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* mxs_status_string(int status);
+
+/* MXS_ABI_VERSION of the built library. */
+int mxs_abi_version(void);
+
+/*
+ * mxfp4_quantize — fp32 W[n, k] -> MX-FP4 (E2M1 codes + one E8M0 scale per
+ * 32 consecutive elements of a row). [M11 §12] fixes the format; the block
+ * exponent follows the OCP MX v1.0 rule the lecture cites:
+ *   e = floor(log2(max |v|)) - 2, clamped to [-127, 127] (an all-zero block
+ *   gets e = -127), scale byte = e + 127 (value 2^(s-127));
+ *   each element v * 2^-e is rounded to the nearest E2M1 value
+ *   {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even encoding, magnitudes above
+ *   6 saturate to 6; the sign bit is the sign bit of v (so -0 -> code 8).
+ *   A block holding a NaN or infinity gets scale byte 0xFF (the E8M0 NaN),
+ *   codes 0, and sets MXS_FLAG_NONFINITE.
+ *
+ * w       [n, k] fp32, 16-byte aligned.
+ * n, k    n >= 1, k >= 32, k % 32 == 0.
+ * codes   [n, k/2] bytes, 16-byte aligned. Element (r, c) is the nibble of
+ *         byte r*k/2 + c/2: the low nibble when c is even. [NEWS] layout.
+ * scales  [n, k/32] bytes (E8M0), any alignment.
+ * Returns MXS_ERR_NULL (w, codes, scales), MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status mxfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes,
+                          uint8_t* scales, int32_t* dev_flags, void* stream);
+
+/*
+ * mxfp4_verify_gemm — Y[m, n] = X[m, k] · Ŵ[n, k]ᵀ with
+ * Ŵ = E2M1(code) · 2^(scale - 127) decoded in registers and products summed in
+ * fp32. The verification pass reads every weight once for all m = B·T
+ * activation rows ([M11 §4, §10]; [NEWS] fp32-accumulated MX-FP4 GEMV).
+ * Weights are decoded exactly; activations are taken exactly; only the fp32
+ * summation rounds. Dequantized weights below 2^-126 in magnitude (scale
+ * bytes 0 and 1) may be flushed to zero by the matrix cores.
+ *
+ * codes   [n, k/2] bytes as written by mxfp4_quantize, 16-byte aligned.
+ * scales  [n, k/32] E8M0 bytes, any alignment.
+ * n, k    n >= 1, k >= 32, k % 32 == 0.
+ * x       [m, k] bf16 bit patterns (uint16), 16-byte aligned.
+ * m       1 <= m <= 65536 (rows are sequences × positions, sequence-major).
+ * y       [m, n] fp32, 4-byte aligned. Fully overwritten.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status mxfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n,
+                             int64_t k, const uint16_t* x, int64_t m, float* y,
+                             void* stream);
+
+/*
+ * spec_accept_workspace_bytes — device workspace spec_accept needs for
+ * (b, kd, v). Returns 0 when the sizes are out of range.
+ */
+size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v);
+
+/*
+ * spec_accept — one verification cycle for b independent sequences [M11 §4].
+ *
+ * For each sequence, with p_i = softmax(target row i) and q_i = softmax(draft
+ * row i) (temperature 1, no filtering; -inf logits are allowed and mean
+ * probability 0):
+ *   for i = 0 .. kd-1: a_i = min(1, p_i(x_i) / q_i(x_i)), or 0 when
+ *     q_i(x_i) = 0 (MXS_FLAG_Q_ZERO) or x_i is outside [0, v)
+ *     (MXS_FLAG_TOKEN_RANGE); accept x_i iff u_i < a_i; stop at the first
+ *     rejection n = i.
+ *   If all kd are accepted, n = kd and the final weights are w = p_kd
+ *   (bonus token); otherwise w = (p_n - q_n)+ (residual; if it has zero
+ *   mass, MXS_FLAG_RESIDUAL_ZERO and w = p_n).
+ *   Final token t* = min{ t : u_kd · Z < C_t } with C the inclusive prefix
+ *   sums of w and Z = sum w; if rounding leaves no such t, the last t with
+ *   w_t > 0. Probabilities and prefix sums are computed in fp64.
+ *   A sequence with a NaN/+inf logit, or a row whose logits are all -inf, is
+ *   refused: MXS_FLAG_NONFINITE, n = 0 and every output token -1.
+ *
+ * target_logits   [b, kd+1, v] fp32; row kd is the next-position (bonus) law.
+ * draft_logits    [b, kd, v] fp32 (may be NULL when kd == 0).
+ * draft_tokens    [b, kd] int32, drawn from the draft laws by the caller
+ *                 (may be NULL when kd == 0).
+ * uniforms        [b, kd+1] fp32 in [0, 1): u_i for acceptance test i and
+ *                 u_kd for the single final draw.
+ * b, kd, v        1 <= b <= 65535, 0 <= kd <= 32, 2 <= v <= 2^26.
+ * out_tokens      [b, kd+1] int32: the n accepted drafts, then t*, then -1.
+ * out_num_accepted[b] int32: n.
+ * workspace       device scratch of at least spec_accept_workspace_bytes(b, kd, v)
+ *                 bytes, 16-byte aligned; its contents on entry do not matter.
+ * Logit pointers must be 4-byte aligned (16-byte alignment with v % 4 == 0
+ * enables vector loads).
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN, MXS_ERR_WORKSPACE.
+ */
+mxs_status spec_accept(const float* target_logits, const float* draft_logits,
+                       const int32_t* draft_tokens, const float* uniforms, int32_t b,
+                       int32_t kd, int32_t v, int32_t* out_tokens,
+                       int32_t* out_num_accepted, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4SPEC_H */

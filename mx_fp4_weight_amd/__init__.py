@@ -1,0 +1,178 @@
+"""Python binding of libmxfp4spec.so: MX-FP4 verify GEMM and speculative acceptance on gfx950.
+
+Argument marshalling only. Every step runs in the HIP library; there is no
+CPU or PyTorch fallback: the first call raises ImportError when the library
+has not been built. PyTorch supplies device memory and the stream
+(``torch.cuda.current_stream()``); the C functions keep their names:
+``mxfp4_quantize``, ``mxfp4_verify_gemm``, ``spec_accept``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4spec.so")
+
+MXS_OK = 0
+MXS_ERR_NULL = 1
+MXS_ERR_SHAPE = 2
+MXS_ERR_ALIGN = 3
+MXS_ERR_WORKSPACE = 4
+MXS_ERR_DEVICE = 5
+MXS_ERR_LAUNCH = 6
+
+FLAG_NONFINITE = 1
+FLAG_TOKEN_RANGE = 2
+FLAG_Q_ZERO = 4
+FLAG_RESIDUAL_ZERO = 8
+
+EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_verify_gemm",
+           "spec_accept_workspace_bytes", "spec_accept"]
+
+
+class MxsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m mx_fp4_weight_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mxs_status_string.argtypes = [ctypes.c_int]
+    lib.mxs_status_string.restype = ctypes.c_char_p
+    lib.mxs_abi_version.argtypes = []
+    lib.mxs_abi_version.restype = ctypes.c_int
+    lib.mxfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    lib.mxfp4_quantize.restype = ctypes.c_int
+    lib.mxfp4_verify_gemm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    lib.mxfp4_verify_gemm.restype = ctypes.c_int
+    lib.spec_accept_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_accept_workspace_bytes.restype = ctypes.c_size_t
+    lib.spec_accept.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.spec_accept.restype = ctypes.c_int
+    return lib
+
+
+_LIB = None
+
+
+def get_lib() -> ctypes.CDLL:
+    """The loaded library (loaded on first use; raises ImportError if it was never built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return get_lib().mxs_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MXS_OK:
+        raise MxsError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t, dtype, name):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} CUDA/HIP tensor")
+
+
+def mxfp4_quantize(w: torch.Tensor, codes: torch.Tensor | None = None,
+                   scales: torch.Tensor | None = None, dev_flags: torch.Tensor | None = None,
+                   stream=None):
+    """fp32 W[n, k] -> (codes uint8 [n, k/2], scales uint8 [n, k/32]); flags OR-ed into dev_flags (int32[1])."""
+    _want(w, torch.float32, "w")
+    n, k = w.shape
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    _want(codes, torch.uint8, "codes")
+    _want(scales, torch.uint8, "scales")
+    _want(dev_flags, torch.int32, "dev_flags")
+    _check(get_lib().mxfp4_quantize(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(dev_flags),
+                              _stream(stream)), "mxfp4_quantize")
+    return codes, scales
+
+
+def mxfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
+                      y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y[m, n] fp32 = X[m, k] (bf16) · Ŵᵀ with Ŵ the MX-FP4 matrix (codes [n, k/2], scales [n, k/32])."""
+    _want(codes, torch.uint8, "codes")
+    _want(scales, torch.uint8, "scales")
+    _want(x, torch.bfloat16, "x")
+    n, kh = codes.shape
+    k = kh * 2
+    m = x.shape[0]
+    if x.shape[1] != k or scales.shape != (n, k // 32):
+        raise ValueError("shape mismatch between codes, scales and x")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _want(y, torch.float32, "y")
+    if y.shape != (m, n):
+        raise ValueError("y must be [m, n]")
+    _check(get_lib().mxfp4_verify_gemm(_ptr(codes), _ptr(scales), n, k, _ptr(x), m, _ptr(y),
+                                 _stream(stream)), "mxfp4_verify_gemm")
+    return y
+
+
+def spec_accept_workspace_bytes(b: int, kd: int, v: int) -> int:
+    return int(get_lib().spec_accept_workspace_bytes(b, kd, v))
+
+
+def spec_accept(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor | None,
+                uniforms: torch.Tensor, out_tokens: torch.Tensor | None = None,
+                out_num: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                dev_flags: torch.Tensor | None = None, stream=None):
+    """One verification cycle for b sequences.
+
+    target [b, kd+1, v] fp32, draft [b, kd, v] fp32, tokens [b, kd] int32,
+    uniforms [b, kd+1] fp32. Returns (out_tokens [b, kd+1] int32, n [b] int32).
+    """
+    _want(target, torch.float32, "target")
+    b, kd1, v = target.shape
+    kd = kd1 - 1
+    if kd > 0:
+        _want(draft, torch.float32, "draft")
+        _want(tokens, torch.int32, "tokens")
+        if draft.shape != (b, kd, v) or tokens.shape != (b, kd):
+            raise ValueError("draft/tokens shape mismatch")
+    else:
+        draft = tokens = None
+    _want(uniforms, torch.float32, "uniforms")
+    if uniforms.shape != (b, kd + 1):
+        raise ValueError("uniforms must be [b, kd+1]")
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((b, kd + 1), dtype=torch.int32, device=dev)
+    if out_num is None:
+        out_num = torch.empty((b,), dtype=torch.int32, device=dev)
+    need = spec_accept_workspace_bytes(b, kd, v)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _want(workspace, torch.uint8, "workspace")
+    _want(dev_flags, torch.int32, "dev_flags")
+    _check(get_lib().spec_accept(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), b, kd, v,
+                           _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
+                           _ptr(dev_flags), _stream(stream)), "spec_accept")
+    return out_tokens, out_num

@@ -1,0 +1,107 @@
+// C-ABI entry points of the MX-FP4 verification library: argument validation
+// (before any HIP call), the gfx950 device check, and dispatch to the kernels.
+#include <string.h>
+
+#include <atomic>
+
+#include "internal.hpp"
+#include "mxfp4spec.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mxs_status check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return MXS_ERR_DEVICE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MXS_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int cached = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (cached == 1) return MXS_OK;
+    if (cached == 2) return MXS_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXS_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MXS_OK : MXS_ERR_DEVICE;
+}
+
+mxs_status launched(hipError_t e) { return e == hipSuccess ? MXS_OK : MXS_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxs_status_string(int status) {
+  switch (status) {
+    case MXS_OK: return "MXS_OK";
+    case MXS_ERR_NULL: return "MXS_ERR_NULL: a required pointer is NULL";
+    case MXS_ERR_SHAPE: return "MXS_ERR_SHAPE: a size is out of range";
+    case MXS_ERR_ALIGN: return "MXS_ERR_ALIGN: a pointer is misaligned";
+    case MXS_ERR_WORKSPACE: return "MXS_ERR_WORKSPACE: workspace too small";
+    case MXS_ERR_DEVICE: return "MXS_ERR_DEVICE: no usable gfx950 HIP device";
+    case MXS_ERR_LAUNCH: return "MXS_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown mxs_status";
+  }
+}
+
+int mxs_abi_version(void) { return MXS_ABI_VERSION; }
+
+mxs_status mxfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                          int32_t* dev_flags, void* stream) {
+  if (!w || !codes || !scales) return MXS_ERR_NULL;
+  if (n < 1 || k < 32 || k % 32 != 0) return MXS_ERR_SHAPE;
+  if (n > (int64_t(1) << 40) / k) return MXS_ERR_SHAPE;  // element count below 2^40
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(dev_flags, 4)) return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_quantize(w, n, k, codes, scales, dev_flags,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mxs_status mxfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                             const uint16_t* x, int64_t m, float* y, void* stream) {
+  if (!codes || !scales || !x || !y) return MXS_ERR_NULL;
+  if (n < 1 || k < 32 || k % 32 != 0 || m < 1 || m > 65536) return MXS_ERR_SHAPE;
+  if (n > (int64_t(1) << 31) - 16 || k > (int64_t(1) << 30)) return MXS_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4)) return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(
+      mxs::launch_verify_gemm(codes, scales, n, k, x, m, y, static_cast<hipStream_t>(stream)));
+}
+
+size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
+  if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
+  return mxs::accept_workspace_bytes(b, kd, v);
+}
+
+mxs_status spec_accept(const float* target_logits, const float* draft_logits,
+                       const int32_t* draft_tokens, const float* uniforms, int32_t b, int32_t kd,
+                       int32_t v, int32_t* out_tokens, int32_t* out_num_accepted, void* workspace,
+                       size_t workspace_bytes, int32_t* dev_flags, void* stream) {
+  if (!target_logits || !uniforms || !out_tokens || !out_num_accepted || !workspace)
+    return MXS_ERR_NULL;
+  if (kd > 0 && (!draft_logits || !draft_tokens)) return MXS_ERR_NULL;
+  if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return MXS_ERR_SHAPE;
+  if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      !aligned(workspace, 16) || !aligned(dev_flags, 4))
+    return MXS_ERR_ALIGN;
+  if (workspace_bytes < mxs::accept_workspace_bytes(b, kd, v)) return MXS_ERR_WORKSPACE;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  const bool vec4 = (v % 4 == 0) && aligned(target_logits, 16) &&
+                    (kd == 0 || aligned(draft_logits, 16));
+  return launched(mxs::launch_spec_accept(target_logits, draft_logits, draft_tokens, uniforms, b,
+                                          kd, v, out_tokens, out_num_accepted, workspace, dev_flags,
+                                          vec4, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

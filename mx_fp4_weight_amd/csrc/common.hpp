@@ -1,0 +1,118 @@
+// Device helpers shared by the gfx950 kernels of the MX-FP4 verification library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxfp4spec.h"
+
+namespace mxs {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// OR a device-detected condition into the caller's flag word (vector atomic).
+__device__ inline void raise_flag(int32_t* flags, int32_t bit) {
+  if (flags) atomicOr(flags, bit);
+}
+
+// exp(d) in fp64 for d <= 0 (d = -inf gives 0), relative error below 1e-14.
+// Cody–Waite reduction d = k ln2 + r with |r| <= ln2/2, then a degree-12
+// Taylor polynomial of e^r in Horner form and a scale by 2^k.
+__device__ inline double exp_neg_f64(double d) {
+  if (!(d > -745.0)) return 0.0;  // also catches -inf; NaN never reaches here
+  const double kLog2e = 1.4426950408889634;
+  const double kLn2Hi = 6.93147180369123816490e-01;
+  const double kLn2Lo = 1.90821492927058770002e-10;
+  double k = __builtin_rint(d * kLog2e);
+  double r = __builtin_fma(-k, kLn2Hi, d);
+  r = __builtin_fma(-k, kLn2Lo, r);
+  // 1/n! for n = 12 .. 1
+  double p = 2.08767569878680989792e-09;
+  p = __builtin_fma(p, r, 2.50521083854417187751e-08);
+  p = __builtin_fma(p, r, 2.75573192239858906526e-07);
+  p = __builtin_fma(p, r, 2.75573192239858906526e-06);
+  p = __builtin_fma(p, r, 2.48015873015873015873e-05);
+  p = __builtin_fma(p, r, 1.98412698412698412698e-04);
+  p = __builtin_fma(p, r, 1.38888888888888888889e-03);
+  p = __builtin_fma(p, r, 8.33333333333333333333e-03);
+  p = __builtin_fma(p, r, 4.16666666666666666667e-02);
+  p = __builtin_fma(p, r, 1.66666666666666666667e-01);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return __builtin_ldexp(p, (int)k);
+}
+
+// Block-wide reductions through LDS for blockDim.x == kThreads (a multiple of 64).
+template <int kThreads>
+__device__ inline float block_max(float v, float* lds) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
+  __syncthreads();
+  float r = lds[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) r = fmaxf(r, lds[i]);
+  __syncthreads();
+  return r;
+}
+
+// Deterministic fp64 block sum: a fixed butterfly inside each wave, then the
+// wave totals in wave order.
+template <int kThreads>
+__device__ inline double block_sum_f64(double v, double* lds) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
+  __syncthreads();
+  double r = lds[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) r += lds[i];
+  __syncthreads();
+  return r;
+}
+
+template <int kThreads>
+__device__ inline int block_or(int v, int* lds) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
+  __syncthreads();
+  int r = lds[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) r |= lds[i];
+  __syncthreads();
+  return r;
+}
+
+// Inclusive fp64 scan of one value per thread over the block, in thread order:
+// Hillis–Steele steps inside each wave, then the exclusive prefix of the wave
+// totals. Same inputs always give bit-identical outputs.
+template <int kThreads>
+__device__ inline double block_inclusive_scan_f64(double v, double* lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    double t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  if (lane == kWave - 1) lds[w] = v;
+  __syncthreads();
+  double base = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i)
+    if (i < w) base += lds[i];
+  __syncthreads();
+  return base + v;
+}
+
+}  // namespace mxs

@@ -1,0 +1,23 @@
+// Kernel launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxs {
+
+hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                           int32_t* flags, hipStream_t stream);
+
+hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                              const uint16_t* x, int64_t m, float* y, hipStream_t stream);
+
+size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v);
+
+hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens,
+                              const float* uniforms, int32_t b, int32_t kd, int32_t v,
+                              int32_t* out_tokens, int32_t* out_num, void* workspace,
+                              int32_t* flags, bool vec4, hipStream_t stream);
+
+}  // namespace mxs

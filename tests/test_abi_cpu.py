@@ -1,0 +1,142 @@
+"""C-ABI checks that run without a GPU.
+
+* the shared library loads and exports every function include/mxfp4spec.h declares;
+* host-detected errors come back before any HIP call (NULL, shape, alignment,
+  workspace), so they are testable here with fake, never-dereferenced pointers;
+* with valid arguments and no usable device the library answers MXS_ERR_DEVICE;
+* the Python binding fails loudly when the library is missing (no fallback).
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import mx_fp4_weight_amd as mxs
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxfp4spec.h")
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)
+    keep = [n for n in names if n.startswith(("mxs_", "mxfp4_", "spec_accept"))]
+    return sorted(set(keep))
+
+
+def test_header_functions_exported():
+    names = declared_functions()
+    assert set(names) == set(mxs.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", mxs.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+
+
+def test_status_strings_and_version():
+    lib = mxs.get_lib()
+    assert lib.mxs_abi_version() == 1
+    for s in range(7):
+        assert mxs.status_string(s).startswith("MXS_")
+    assert mxs.status_string(99) == "unknown mxs_status"
+
+
+def test_workspace_query():
+    lib = mxs.get_lib()
+    assert lib.spec_accept_workspace_bytes(0, 4, 1024) == 0
+    assert lib.spec_accept_workspace_bytes(1, -1, 1024) == 0
+    assert lib.spec_accept_workspace_bytes(1, 33, 1024) == 0
+    assert lib.spec_accept_workspace_bytes(1, 4, 1) == 0
+    a = lib.spec_accept_workspace_bytes(1, 4, 128256)
+    b = lib.spec_accept_workspace_bytes(64, 4, 128256)
+    assert 0 < a < b
+    # per (row, chunk): fp32 max + fp64 sum + int32 flag; per (seq, chunk): two fp64 totals
+    rows, chunks = 64 * 9, (128256 + 4095) // 4096
+    assert b >= rows * chunks * 16 + 64 * chunks * 16
+
+
+def _q(w=0x1000, n=4, k=64, codes=0x2000, scales=0x3000, flags=None):
+    return mxs.get_lib().mxfp4_quantize(P(w) if w else None, n, k, P(codes) if codes else None,
+                                        P(scales) if scales else None, P(flags) if flags else None, None)
+
+
+def test_quantize_host_errors():
+    assert _q(w=0) == mxs.MXS_ERR_NULL
+    assert _q(codes=0) == mxs.MXS_ERR_NULL
+    assert _q(scales=0) == mxs.MXS_ERR_NULL
+    assert _q(k=48) == mxs.MXS_ERR_SHAPE
+    assert _q(k=0) == mxs.MXS_ERR_SHAPE
+    assert _q(n=0) == mxs.MXS_ERR_SHAPE
+    assert _q(w=0x1004) == mxs.MXS_ERR_ALIGN
+    assert _q(codes=0x2008) == mxs.MXS_ERR_ALIGN
+    assert _q(flags=0x5002) == mxs.MXS_ERR_ALIGN
+    assert _q(scales=0x3001) == mxs.MXS_ERR_DEVICE     # scales may have any alignment
+    assert _q() == mxs.MXS_ERR_DEVICE                  # valid call, no GPU in this container
+
+
+def _g(codes=0x1000, scales=0x2000, n=4, k=64, x=0x3000, m=5, y=0x4000):
+    return mxs.get_lib().mxfp4_verify_gemm(P(codes) if codes else None, P(scales) if scales else None, n, k,
+                                           P(x) if x else None, m, P(y) if y else None, None)
+
+
+def test_gemm_host_errors():
+    for kw in [dict(codes=0), dict(scales=0), dict(x=0), dict(y=0)]:
+        assert _g(**kw) == mxs.MXS_ERR_NULL
+    for kw in [dict(k=40), dict(k=16), dict(n=0), dict(m=0), dict(m=65537), dict(n=-3)]:
+        assert _g(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(codes=0x1004), dict(x=0x3002), dict(y=0x4002)]:
+        assert _g(**kw) == mxs.MXS_ERR_ALIGN
+    assert _g(m=65536) == mxs.MXS_ERR_DEVICE
+    assert _g() == mxs.MXS_ERR_DEVICE
+
+
+def _a(t=0x1000, d=0x2000, tok=0x3000, u=0x4000, b=1, kd=4, v=1024, ot=0x5000, on=0x6000,
+       ws=0x7000, wsb=None, flags=None):
+    lib = mxs.get_lib()
+    if wsb is None:
+        wsb = lib.spec_accept_workspace_bytes(max(b, 1), max(kd, 0), max(v, 2))
+    f = lambda a: P(a) if a else None
+    return lib.spec_accept(f(t), f(d), f(tok), f(u), b, kd, v, f(ot), f(on), f(ws), wsb, f(flags), None)
+
+
+def test_accept_host_errors():
+    for kw in [dict(t=0), dict(d=0), dict(tok=0), dict(u=0), dict(ot=0), dict(on=0), dict(ws=0)]:
+        assert _a(**kw) == mxs.MXS_ERR_NULL
+    assert _a(d=0, tok=0, kd=0) == mxs.MXS_ERR_DEVICE   # kd = 0 needs no draft inputs
+    for kw in [dict(b=0), dict(kd=-1), dict(kd=33), dict(v=1), dict(v=(1 << 26) + 1)]:
+        assert _a(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(t=0x1002), dict(tok=0x3001), dict(ws=0x7008), dict(flags=0x8001)]:
+        assert _a(**kw) == mxs.MXS_ERR_ALIGN
+    need = mxs.get_lib().spec_accept_workspace_bytes(1, 4, 1024)
+    assert _a(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
+    assert _a(wsb=need) == mxs.MXS_ERR_DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    code = (
+        "import mx_fp4_weight_amd as m\n"
+        f"m.LIB_PATH = {str(tmp_path / 'missing.so')!r}\n"
+        "m._LIB = None\n"
+        "try:\n"
+        "    m.get_lib()\n"
+        "except ImportError as e:\n"
+        "    print('IMPORT_ERROR', 'no fallback' in str(e))\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "IMPORT_ERROR True" in r.stdout, r.stderr
+
+
+def test_product_never_imports_oracle():
+    """The product package and its sources name neither the oracle nor the input generator."""
+    pkg = os.path.join(ROOT, "mx_fp4_weight_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "import synth" not in text and "from synth" not in text, fn

@@ -1,0 +1,154 @@
+"""mxfp4_verify_gemm on the GPU vs the fp64 oracle (relative L2 <= 2e-3, per-element bound)."""
+import numpy as np
+import pytest
+import torch
+
+import mx_fp4_weight_amd as mxs
+import synth
+from oracle import mx as omx
+from tests.gpu_util import check_gemm, dev, dev_bf16, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gemm(codes, scales, xbits):
+    y = mxs.mxfp4_verify_gemm(dev(codes), dev(scales), dev_bf16(xbits))
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def test_tiny_config():
+    say("gemm: tiny 1024x1024 T=5")
+    w = synth.weights(1, 0, 1024, 1024)
+    codes, scales, _ = omx.quantize(w)
+    x = synth.activations(1, 0, 5, 1024)
+    check_gemm(codes, scales, 1024, 1024, x, run_gemm(codes, scales, x), label="tiny")
+
+
+def test_one_hot_columns_exact():
+    """x = e_k returns column k of the dequantized matrix exactly (fp32 sums of one term)."""
+    say("gemm: one-hot")
+    n, k = 80, 256
+    codes, scales, _ = omx.quantize(synth.weights(7, 1, n, k))
+    cols = [0, 1, 31, 32, 127, 128, 255]
+    x = np.zeros((len(cols), k), np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = run_gemm(codes, scales, synth.f32_to_bf16_bits(x))
+    wd = omx.dequantize(codes, scales, k)
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i].astype(np.float64), wd[:, c])
+
+
+@pytest.mark.parametrize("n,k,m", [
+    (1, 32, 1), (17, 32, 5), (16, 96, 3), (33, 160, 8), (1000, 4128, 5), (300, 1056, 16),
+    (64, 512, 17), (129, 640, 33), (5, 8192, 1), (2048, 288, 7),
+])
+def test_ragged_shapes(n, k, m):
+    say(f"gemm: ragged n={n} k={k} m={m}")
+    w = synth.weights(7, n + 3 * k + m, n, k)
+    codes, scales, _ = omx.quantize(w)
+    x = synth.activations(7, n + 3 * k + m, m, k)
+    check_gemm(codes, scales, n, k, x, run_gemm(codes, scales, x), label=f"{n}x{k}x{m}")
+
+
+def test_scale_extremes():
+    """Block scales from 2^-100 to 2^120 (products stay in the fp32 normal range), all-zero blocks."""
+    say("gemm: scale extremes")
+    n, k = 32, 512
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    mags = np.float32(2.0) ** rng.integers(-100, 120, (n, k // 32)).astype(np.float32)
+    w = (w.reshape(n, -1, 32) * mags[..., None]).reshape(n, k).astype(np.float32)
+    w[3] = 0
+    w[5, :64] = -0.0
+    codes, scales, _ = omx.quantize(w)
+    assert scales[3].max() == 0 and scales.max() >= 240
+    x = synth.activations(7, 99, 5, k, sigma=1e-3)
+    check_gemm(codes, scales, n, k, x, run_gemm(codes, scales, x), label="scales")
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)])
+def test_8b_shapes_t_sweep(n, k):
+    """The 8B-class layer shapes at every T = 1..8, full outputs."""
+    say(f"gemm: 8B {n}x{k} T=1..8")
+    w = synth.weights(2, n * 7 + k, n, k)
+    codes, scales, _ = omx.quantize(w)
+    x8 = synth.activations(2, n * 7 + k, 8, k)
+    from oracle import gemm as ogemm
+    ref = ogemm.verify_gemm(codes, scales, n, k, x8)
+    bound = ogemm.abs_bound(codes, scales, n, k, x8)
+    dc, ds = dev(codes), dev(scales)
+    for t in range(1, 9):
+        y = mxs.mxfp4_verify_gemm(dc, ds, dev_bf16(x8[:t]))
+        torch.cuda.synchronize()
+        got = host(y).astype(np.float64)
+        err = got - ref[:t]
+        rel = np.linalg.norm(err) / np.linalg.norm(ref[:t])
+        assert rel <= 2e-3, (t, rel)
+        assert np.all(np.abs(err) <= 1e-4 * bound[:t]), t
+
+
+@pytest.mark.parametrize("n,k", [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)])
+def test_70b_shapes_outliers(n, k):
+    """70B-class shapes at T = 5 with 1% outlier input channels x20; weights quantized on the GPU,
+    codes of the sampled rows checked bit-exact, outputs of the sampled rows against the oracle."""
+    say(f"gemm: 70B {n}x{k} T=5 outliers")
+    idx = n * 3 + k
+    w = synth.weights(3, idx, n, k, outlier_frac=0.01)
+    dcodes, dscales = mxs.mxfp4_quantize(dev(w))
+    x = synth.activations(3, idx, 5, k)
+    y = mxs.mxfp4_verify_gemm(dcodes, dscales, dev_bf16(x))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(idx).choice(n, 254, replace=False), [0, n - 1]]))
+    rc, rs, _ = omx.quantize(w[rows])
+    assert np.array_equal(host(dcodes)[rows], rc) and np.array_equal(host(dscales)[rows], rs)
+    sub_c = np.zeros((n, k // 2), np.uint8)
+    sub_s = np.zeros((n, k // 32), np.uint8)
+    sub_c[rows], sub_s[rows] = rc, rs
+    check_gemm(sub_c, sub_s, n, k, x, host(y)[:, rows], rows=rows, label=f"70B {n}x{k}")
+
+
+def test_70b_lm_head_sampled():
+    """lm_head 128256x8192 at T = 5: generated and quantized on the GPU in row chunks."""
+    say("gemm: 70B lm_head 128256x8192")
+    n, k = 128256, 8192
+    idx = 99
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, k // 32), dtype=torch.uint8, device="cuda")
+    step = 8192
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        w = synth.weights(3, idx, n, k, outlier_frac=0.01, row_start=r0, row_stop=r1)
+        mxs.mxfp4_quantize(dev(w), codes=codes[r0:r1], scales=scales[r0:r1])
+    x = synth.activations(3, idx, 5, k)
+    y = mxs.mxfp4_verify_gemm(codes, scales, dev_bf16(x))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(idx).choice(n, 126, replace=False), [0, n - 1]]))
+    w_rows = np.concatenate([synth.weights(3, idx, n, k, outlier_frac=0.01, row_start=r, row_stop=r + 1)
+                             for r in rows])
+    rc, rs, _ = omx.quantize(w_rows)
+    hc, hs = host(codes[torch.from_numpy(rows).cuda()]), host(scales[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(hc, rc) and np.array_equal(hs, rs)
+    sub_c = np.zeros((n, k // 2), np.uint8)
+    sub_s = np.zeros((n, k // 32), np.uint8)
+    sub_c[rows], sub_s[rows] = rc, rs
+    check_gemm(sub_c, sub_s, n, k, x, host(y)[:, rows], rows=rows, label="lm_head")
+
+
+def test_batched_320_rows_sampled():
+    """64 sequences x 5 positions = 320 rows against 8192x28672 (the batched verification case)."""
+    say("gemm: batched 320x8192x28672")
+    n, k, m = 8192, 28672, 320
+    w = synth.weights(4, 0, n, k)
+    dcodes, dscales = mxs.mxfp4_quantize(dev(w))
+    x = synth.activations(4, 0, m, k)
+    y = mxs.mxfp4_verify_gemm(dcodes, dscales, dev_bf16(x))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(4).choice(n, 126, replace=False), [0, n - 1]]))
+    rc, rs, _ = omx.quantize(w[rows])
+    assert np.array_equal(host(dcodes)[rows], rc) and np.array_equal(host(dscales)[rows], rs)
+    sub_c = np.zeros((n, k // 2), np.uint8)
+    sub_s = np.zeros((n, k // 32), np.uint8)
+    sub_c[rows], sub_s[rows] = rc, rs
+    check_gemm(sub_c, sub_s, n, k, x, host(y)[:, rows], rows=rows, label="batched")
