@@ -7,29 +7,29 @@
 // drawn from (p_n - q_n)+ at a rejection, or from the next-position target law
 // p_K when all K drafts survive, by inverse CDF on the supplied u_K.
 //
-// Four kernels on the caller's stream:
-//   stats    grid (rows, chunks): per 4096-logit chunk of every target/draft
-//            row, the chunk max (exact, fp32) and sum exp(z - max) in fp64.
-//            One read of all logits: the vocab-wide normalizers.
-//   decide   one wave per sequence: combine chunk stats into (max, sum) per
-//            row, gather p_i(x_i), q_i(x_i) in fp64, run the left-to-right
-//            test, record n and the row statistics of the final draw.
-//   wsum     grid (chunks, sequences): per chunk, the final weights w (residual
-//            or bonus row) and their prefix structure; writes the chunk total.
-//   sample   one workgroup per sequence: locate u_K · Z among the chunk
-//            totals, then inside the chunk among the thread totals, then
-//            among the elements; writes t*.
-//
-// Prefix sums are defined hierarchically and used identically by wsum and
-// sample: L = sequential prefix over a thread's 16 consecutive tokens,
-// T_i = T_(i-1) + (thread i total) sequentially over the 256 threads of a
-// chunk, P_(c+1) = P_c + T_255 over chunks, and C_t = P_c + (T_(i-1) + L_j).
-// C is non-decreasing and its value at the end of a thread / chunk is exactly
-// the total used one level up, so the crossing always exists where the upper
-// level says, and a zero-weight token is never chosen.
+// Three kernels on the caller's stream:
+//   stats   grid (rows, chunks): for every 4096-logit chunk of every target
+//           and draft row, the chunk max (exact, fp32) and sum exp(z - max)
+//           in fp64. This is the one full read of the logits.
+//   decide  grid (chunks, sequences): every workgroup combines its sequence's
+//           chunk statistics into (max, sum) per row, gathers p_i(x_i) and
+//           q_i(x_i) in fp64 (one lane per draft position), takes n = first
+//           rejection with a ballot, then sums the final weights w (residual
+//           or bonus row) over its own chunk. Chunk 0 writes the decisions.
+//   sample  one workgroup per sequence: inclusive scan of the chunk totals,
+//           first chunk whose running total exceeds u_K·Z, then a block scan
+//           inside that chunk and a per-thread scan to the token.
+// All probabilities and prefix sums are fp64; the result can differ from an
+// exact-arithmetic draw only when u_K·Z lies within ~1e-15·Z of an interval
+// end. Rounding guards: if no crossing is found where the level above
+// placed it, the last positive-weight token of that range is taken, so a
+// zero-weight token is never returned.
 #include "common.hpp"
 #include "internal.hpp"
 
+// No FMA contraction: p - q with p = e_t/S_t must be exactly 0 when the target
+// and draft rows are equal, and the decide and sample kernels must compute
+// bit-identical weights.
 #pragma clang fp contract(off)
 
 namespace mxs {
@@ -38,53 +38,49 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPer = 16;
 constexpr int kChunk = kThreads * kPer;  // 4096 logits per chunk
+constexpr int kMaxRows = 65;             // 2 * 32 + 1 rows per sequence
+
+struct Decision {
+  int32_t n;      // accepted drafts, or -1 for a refused sequence
+  int32_t pad;
+  double mt, inv_st;  // target row n: max and 1/sum
+  double md, inv_sd;  // draft row n (n < kd)
+};
 
 struct Workspace {
   float* cmax;     // [rows][chunks]
   double* csum;    // [rows][chunks]
   int32_t* cbad;   // [rows][chunks]
-  int32_t* nacc;   // [b]  n, or -1 for a refused sequence
-  double* rstat;   // [b][4]  (max_t, sum_t, max_d, sum_d) of the final draw's rows
-  double* zres;    // [b][chunks]  chunk totals of the final weights
-  double* zp;      // [b][chunks]  chunk totals of p_n (zero-residual fallback)
+  Decision* dec;   // [b]
+  double* zres;    // [b][chunks] chunk totals of the final weights
+  double* zp;      // [b][chunks] chunk totals of p_n (zero-residual fallback)
 };
 
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ __device__ inline Workspace carve(void* base, int64_t b, int64_t kd, int64_t v) {
+struct Layout {
+  size_t cmax, csum, cbad, dec, zres, zp, total;
+};
+
+inline Layout layout(int64_t b, int64_t kd, int64_t v) {
   const int64_t rows = b * (2 * kd + 1);
   const int64_t chunks = (v + kChunk - 1) / kChunk;
-  char* p = static_cast<char*>(base);
-  Workspace w;
+  Layout L;
   size_t off = 0;
-  w.cmax = reinterpret_cast<float*>(p + off);
+  L.cmax = off;
   off = align256(off + sizeof(float) * rows * chunks);
-  w.csum = reinterpret_cast<double*>(p + off);
+  L.csum = off;
   off = align256(off + sizeof(double) * rows * chunks);
-  w.cbad = reinterpret_cast<int32_t*>(p + off);
+  L.cbad = off;
   off = align256(off + sizeof(int32_t) * rows * chunks);
-  w.nacc = reinterpret_cast<int32_t*>(p + off);
-  off = align256(off + sizeof(int32_t) * b);
-  w.rstat = reinterpret_cast<double*>(p + off);
-  off = align256(off + sizeof(double) * 4 * b);
-  w.zres = reinterpret_cast<double*>(p + off);
+  L.dec = off;
+  off = align256(off + sizeof(Decision) * b);
+  L.zres = off;
   off = align256(off + sizeof(double) * b * chunks);
-  w.zp = reinterpret_cast<double*>(p + off);
-  return w;
-}
-
-__host__ __device__ inline size_t carve_bytes(int64_t b, int64_t kd, int64_t v) {
-  const int64_t rows = b * (2 * kd + 1);
-  const int64_t chunks = (v + kChunk - 1) / kChunk;
-  size_t off = 0;
-  off = align256(off + sizeof(float) * rows * chunks);
-  off = align256(off + sizeof(double) * rows * chunks);
-  off = align256(off + sizeof(int32_t) * rows * chunks);
-  off = align256(off + sizeof(int32_t) * b);
-  off = align256(off + sizeof(double) * 4 * b);
+  L.zp = off;
   off = align256(off + sizeof(double) * b * chunks);
-  off = align256(off + sizeof(double) * b * chunks);
-  return off;
+  L.total = off;
+  return L;
 }
 
 // Logit row j of sequence s: rows 0..kd are target rows, kd+1..2kd draft rows.
@@ -102,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   __shared__ double lds_d[kThreads / kWave];
   __shared__ float lds_f[kThreads / kWave];
   __shared__ int lds_i[kThreads / kWave];
-  const int64_t rowg = blockIdx.x;  // global row index over all sequences
+  const int64_t rowg = blockIdx.x;  // row index over all sequences
   const int per_seq = 2 * kd + 1;
   const int64_t s = rowg / per_seq;
   const int j = (int)(rowg % per_seq);
@@ -153,116 +149,18 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   }
 }
 
-// ---------------------------------------------------------------- decide
-__global__ __launch_bounds__(kWave) void decide_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft,
-    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
-    int chunks, Workspace ws, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num,
-    int32_t* __restrict__ flags) {
-  __shared__ double smax[65];
-  __shared__ double ssum[65];
-  __shared__ int sbad;
-  const int64_t s = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int per_seq = 2 * kd + 1;
-  if (lane == 0) sbad = 0;
-  __syncthreads();
-  for (int j = lane; j < per_seq; j += kWave) {
-    const size_t o = ((size_t)s * per_seq + j) * chunks;
-    float m = -INFINITY;
-    int bad = 0;
-    for (int c = 0; c < chunks; ++c) {
-      m = fmaxf(m, ws.cmax[o + c]);
-      bad |= ws.cbad[o + c];
-    }
-    double sum = 0.0;
-    if (m == -INFINITY) bad = 1;
-    if (!bad) {
-      const double m64 = (double)m;
-      for (int c = 0; c < chunks; ++c) {
-        const double cs = ws.csum[o + c];
-        if (cs > 0.0) sum += cs * exp_neg_f64((double)ws.cmax[o + c] - m64);
-      }
-    }
-    smax[j] = (double)m;
-    ssum[j] = sum;
-    if (bad) atomicOr(&sbad, 1);
-  }
-  __syncthreads();
-  int32_t* out = out_tokens + (size_t)s * (kd + 1);
-  if (sbad) {
-    for (int i = lane; i <= kd; i += kWave) out[i] = -1;
-    if (lane == 0) {
-      out_num[s] = 0;
-      ws.nacc[s] = -1;
-      raise_flag(flags, MXS_FLAG_NONFINITE);
-    }
-    return;
-  }
-  if (lane != 0) return;
-  int f = 0;
-  int n = kd;
-  const float* u = uniforms + (size_t)s * (kd + 1);
-  for (int i = 0; i < kd; ++i) {
-    const int32_t x = tokens[(size_t)s * kd + i];
-    double a = 0.0;
-    if (x < 0 || x >= v) {
-      f |= MXS_FLAG_TOKEN_RANGE;
-    } else {
-      const float zt = row_ptr(target, draft, s, kd, i, v)[x];
-      const float zd = row_ptr(target, draft, s, kd, kd + 1 + i, v)[x];
-      const double q = exp_neg_f64((double)zd - smax[kd + 1 + i]) / ssum[kd + 1 + i];
-      const double p = exp_neg_f64((double)zt - smax[i]) / ssum[i];
-      if (q == 0.0) {
-        f |= MXS_FLAG_Q_ZERO;
-      } else {
-        a = p / q;
-        a = a < 1.0 ? a : 1.0;
-      }
-    }
-    if ((double)u[i] < a) {
-      out[i] = x;
-    } else {
-      n = i;
-      break;
-    }
-  }
-  for (int i = n + 1; i <= kd; ++i) out[i] = -1;
-  out_num[s] = n;
-  ws.nacc[s] = n;
-  double* rs = ws.rstat + 4 * s;
-  rs[0] = smax[n];
-  rs[1] = ssum[n];
-  rs[2] = n < kd ? smax[kd + 1 + n] : 0.0;
-  rs[3] = n < kd ? ssum[kd + 1 + n] : 0.0;
-  if (f) raise_flag(flags, f);
-}
-
-// ---------------------------------------------------------------- final weights
+// p_n(t) and the final weight of token t: residual (p - q)+, or p for the bonus row.
 struct FinalRows {
-  const float* zt;  // target row n
-  const float* zd;  // draft row n, or nullptr for the bonus row
-  double mt, st, md, sd;
+  const float* zt;
+  const float* zd;  // nullptr for the bonus row
+  double mt, inv_st, md, inv_sd;
 };
 
-__device__ inline FinalRows final_rows(const float* target, const float* draft, int64_t s, int kd,
-                                       int v, int n, const double* rs) {
-  FinalRows fr;
-  fr.zt = row_ptr(target, draft, s, kd, n, v);
-  fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
-  fr.mt = rs[0];
-  fr.st = rs[1];
-  fr.md = rs[2];
-  fr.sd = rs[3];
-  return fr;
-}
-
-// p_n(t) and the final weight of token t (residual (p - q)+, or p for the bonus row).
 __device__ inline void weights_at(const FinalRows& fr, int t, double& w_final, double& w_p) {
-  const double p = exp_neg_f64((double)fr.zt[t] - fr.mt) / fr.st;
+  const double p = exp_neg_f64((double)fr.zt[t] - fr.mt) * fr.inv_st;
   w_p = p;
   if (fr.zd) {
-    const double q = exp_neg_f64((double)fr.zd[t] - fr.md) / fr.sd;
+    const double q = exp_neg_f64((double)fr.zd[t] - fr.md) * fr.inv_sd;
     const double d = p - q;
     w_final = d > 0.0 ? d : 0.0;
   } else {
@@ -270,180 +168,281 @@ __device__ inline void weights_at(const FinalRows& fr, int t, double& w_final, d
   }
 }
 
-// Thread-local sequential sums of the chunk's 16 consecutive tokens of this thread.
-__device__ inline void thread_sums(const FinalRows& fr, int v, int c, double& tot_final,
-                                   double& tot_p) {
-  const int t0 = c * kChunk + threadIdx.x * kPer;
-  double a = 0.0, b = 0.0;
-  for (int j = 0; j < kPer; ++j) {
-    const int t = t0 + j;
-    if (t < v) {
-      double wf, wp;
-      weights_at(fr, t, wf, wp);
-      a = a + wf;
-      b = b + wp;
-    }
-  }
-  tot_final = a;
-  tot_p = b;
-}
-
-__global__ __launch_bounds__(kThreads) void wsum_kernel(const float* __restrict__ target,
-                                                        const float* __restrict__ draft, int kd,
-                                                        int v, int chunks, Workspace ws) {
-  __shared__ double tf[kThreads];
-  __shared__ double tp[kThreads];
+// ---------------------------------------------------------------- decide + chunk totals
+__global__ __launch_bounds__(kThreads) void decide_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
+    int chunks, Workspace ws, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num,
+    int32_t* __restrict__ flags) {
+  __shared__ double smax[kMaxRows];
+  __shared__ double ssum[kMaxRows];
+  __shared__ int sbad[kMaxRows];
+  __shared__ double lds_d[kThreads / kWave];
+  __shared__ int s_n;
   const int c = blockIdx.x;
   const int64_t s = blockIdx.y;
-  const int n = ws.nacc[s];
-  if (n < 0) {
-    if (threadIdx.x == 0) {
-      ws.zres[s * chunks + c] = 0.0;
-      ws.zp[s * chunks + c] = 0.0;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int per_seq = 2 * kd + 1;
+
+  // 1. per-row max and sum over the chunk statistics: one wave per row
+  for (int j = wave; j < per_seq; j += kThreads / kWave) {
+    const size_t o = ((size_t)s * per_seq + j) * chunks;
+    float m = -INFINITY;
+    int bad = 0;
+    for (int cc = lane; cc < chunks; cc += kWave) {
+      m = fmaxf(m, ws.cmax[o + cc]);
+      bad |= ws.cbad[o + cc];
     }
-    return;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      m = fmaxf(m, __shfl_xor(m, off));
+      bad |= __shfl_xor(bad, off);
+    }
+    bad |= (m == -INFINITY);
+    double sum = 0.0;
+    if (!bad) {
+      const double m64 = (double)m;
+      for (int cc = lane; cc < chunks; cc += kWave) {
+        const double cs = ws.csum[o + cc];
+        if (cs > 0.0) sum += cs * exp_neg_f64((double)ws.cmax[o + cc] - m64);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) {
+      smax[j] = (double)m;
+      ssum[j] = sum;
+      sbad[j] = bad;
+    }
   }
-  const FinalRows fr = final_rows(target, draft, s, kd, v, n, ws.rstat + 4 * s);
-  double a, b;
-  thread_sums(fr, v, c, a, b);
-  tf[threadIdx.x] = a;
-  tp[threadIdx.x] = b;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double sa = 0.0, sb = 0.0;
-    for (int i = 0; i < kThreads; ++i) {
-      sa = sa + tf[i];
-      sb = sb + tp[i];
+
+  // 2. decisions: lane i of wave 0 tests draft position i; n = first rejection
+  if (wave == 0) {
+    int bad = 0;
+    for (int j = lane; j < per_seq; j += kWave) bad |= sbad[j];
+    bad = __any(bad);
+    int f = 0;
+    bool acc = true;
+    int32_t x = -1;
+    if (!bad && lane < kd) {
+      x = tokens[(size_t)s * kd + lane];
+      double a = 0.0;
+      if (x < 0 || x >= v) {
+        f |= MXS_FLAG_TOKEN_RANGE;
+      } else {
+        const float zt = row_ptr(target, draft, s, kd, lane, v)[x];
+        const float zd = row_ptr(target, draft, s, kd, kd + 1 + lane, v)[x];
+        const double q = exp_neg_f64((double)zd - smax[kd + 1 + lane]) / ssum[kd + 1 + lane];
+        const double p = exp_neg_f64((double)zt - smax[lane]) / ssum[lane];
+        if (q == 0.0) {
+          f |= MXS_FLAG_Q_ZERO;
+        } else {
+          a = p / q;
+          a = a < 1.0 ? a : 1.0;
+        }
+      }
+      acc = (double)uniforms[(size_t)s * (kd + 1) + lane] < a;
     }
-    ws.zres[s * chunks + c] = sa;
-    ws.zp[s * chunks + c] = sb;
+    const unsigned long long rej = __ballot(!acc);  // lanes >= kd vote "accept"
+    const int n = bad ? -1 : (rej ? __ffsll(rej) - 1 : kd);
+    if (lane > n) f = 0;  // positions after the first rejection are not examined
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) f |= __shfl_xor(f, off);
+    if (lane == 0) s_n = n;
+    if (c == 0) {
+      // accepted drafts, then -1; slot n (the final draw) is written by the sample kernel
+      int32_t* out = out_tokens + (size_t)s * (kd + 1);
+      if (lane <= kd) {
+        if (n < 0 || lane > n) out[lane] = -1;
+        else if (lane < n) out[lane] = x;
+      }
+      if (lane == 0) {
+        out_num[s] = n < 0 ? 0 : n;
+        Decision d;
+        d.n = n;
+        d.pad = 0;
+        const int nn = n < 0 ? 0 : n;
+        d.mt = smax[nn];
+        d.inv_st = 1.0 / ssum[nn];
+        d.md = (n >= 0 && n < kd) ? smax[kd + 1 + n] : 0.0;
+        d.inv_sd = (n >= 0 && n < kd) ? 1.0 / ssum[kd + 1 + n] : 0.0;
+        ws.dec[s] = d;
+        if (bad) raise_flag(flags, MXS_FLAG_NONFINITE);
+        else if (f) raise_flag(flags, f);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. chunk total of the final weights: thread totals in token order, then
+  // the same block scan the sample kernel uses, so both see identical totals
+  const int n = s_n;
+  double a = 0.0, b = 0.0;
+  if (n >= 0) {
+    FinalRows fr;
+    fr.zt = row_ptr(target, draft, s, kd, n, v);
+    fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
+    fr.mt = smax[n];
+    fr.inv_st = 1.0 / ssum[n];
+    fr.md = n < kd ? smax[kd + 1 + n] : 0.0;
+    fr.inv_sd = n < kd ? 1.0 / ssum[kd + 1 + n] : 0.0;
+    const int t0 = c * kChunk + threadIdx.x * kPer;
+    for (int j = 0; j < kPer; ++j) {
+      const int t = t0 + j;
+      if (t < v) {
+        double wf, wp;
+        weights_at(fr, t, wf, wp);
+        a += wf;
+        b += wp;
+      }
+    }
+  }
+  a = block_inclusive_scan_f64<kThreads>(a, lds_d);
+  b = block_inclusive_scan_f64<kThreads>(b, lds_d);
+  if (threadIdx.x == kThreads - 1) {
+    ws.zres[s * chunks + c] = a;
+    ws.zp[s * chunks + c] = b;
   }
 }
 
 // ---------------------------------------------------------------- sample
+constexpr int kNone = 0x7fffffff;
+
 __global__ __launch_bounds__(kThreads) void sample_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const float* __restrict__ uniforms, int kd, int v, int chunks, Workspace ws,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags) {
-  __shared__ double T[kThreads];
-  __shared__ double s_uz, s_P;
-  __shared__ int s_chunk, s_use_p, s_found;
-  __shared__ int s_last;
+  __shared__ double lds_scan[kThreads / kWave];
+  __shared__ double s_incl[kThreads];
+  __shared__ int s_first, s_last;
   const int64_t s = blockIdx.x;
-  const int n = ws.nacc[s];
+  const Decision d = ws.dec[s];
+  const int n = d.n;
   if (n < 0) return;
-  const FinalRows fr = final_rows(target, draft, s, kd, v, n, ws.rstat + 4 * s);
+  FinalRows fr;
+  fr.zt = row_ptr(target, draft, s, kd, n, v);
+  fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
+  fr.mt = d.mt;
+  fr.inv_st = d.inv_st;
+  fr.md = d.md;
+  fr.inv_sd = d.inv_sd;
+  const int tid = threadIdx.x;
 
-  if (threadIdx.x == 0) {
-    const double* zr = ws.zres + s * chunks;
-    double Z = 0.0;
-    for (int c = 0; c < chunks; ++c) Z = Z + zr[c];
-    int use_p = 0;
-    if (!(Z > 0.0)) {  // zero residual mass: draw from p_n instead
-      use_p = 1;
-      zr = ws.zp + s * chunks;
-      Z = 0.0;
-      for (int c = 0; c < chunks; ++c) Z = Z + zr[c];
-      if (n < kd) raise_flag(flags, MXS_FLAG_RESIDUAL_ZERO);
+  // ---- level 1: chunks. Z = running total over rounds of 256 chunk totals.
+  const double* zr = ws.zres + s * chunks;
+  bool use_p = false;
+  double Z = 0.0;
+  for (int pass = 0; pass < 2; ++pass) {
+    double carry = 0.0;
+    for (int c0 = 0; c0 < chunks; c0 += kThreads) {
+      const int cc = c0 + tid;
+      const double incl = carry + block_inclusive_scan_f64<kThreads>(cc < chunks ? zr[cc] : 0.0, lds_scan);
+      if (tid == kThreads - 1) s_incl[0] = incl;
+      __syncthreads();
+      carry = s_incl[0];
+      __syncthreads();
     }
-    const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
-    double P = 0.0;
-    int cstar = -1;
-    for (int c = 0; c < chunks; ++c) {
-      const double next = P + zr[c];
-      if (uz < next) {
-        cstar = c;
-        break;
-      }
-      P = next;
-    }
-    int last = -1;
-    if (cstar < 0) {  // no crossing (rounding): last chunk holding a positive weight
-      for (int c = chunks - 1; c >= 0; --c)
-        if (zr[c] > 0.0) {
-          last = c;
-          break;
-        }
-    }
-    s_uz = uz;
-    s_P = P;
-    s_chunk = cstar >= 0 ? cstar : last;
-    s_found = cstar >= 0;
-    s_use_p = use_p;
+    Z = carry;
+    if (Z > 0.0 || pass == 1) break;
+    // zero residual mass (rounding): draw from p_n instead
+    use_p = true;
+    zr = ws.zp + s * chunks;
+    if (n < kd && tid == 0) raise_flag(flags, MXS_FLAG_RESIDUAL_ZERO);
+  }
+  const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
+
+  // first positive chunk whose running total exceeds u·Z, and the total before it
+  if (tid == 0) {
+    s_first = kNone;
     s_last = -1;
   }
   __syncthreads();
-  const int c = s_chunk;
-  const bool use_p = s_use_p;
-  if (c < 0) return;  // cannot happen for a valid row (p has positive mass)
-
-  // thread totals of chunk c, identical arithmetic to wsum_kernel
-  double a, b;
-  thread_sums(fr, v, c, a, b);
-  const double mine = use_p ? b : a;
-  T[threadIdx.x] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double run = 0.0;
-    for (int i = 0; i < kThreads; ++i) {
-      run = run + T[i];
-      T[i] = run;  // T_i: inclusive sequential prefix of thread totals
+  double carry = 0.0, base = 0.0;
+  int c = kNone;
+  for (int c0 = 0; c0 < chunks; c0 += kThreads) {
+    const int cc = c0 + tid;
+    const double zc = cc < chunks ? zr[cc] : 0.0;
+    const double incl = carry + block_inclusive_scan_f64<kThreads>(zc, lds_scan);
+    s_incl[tid] = incl;
+    if (cc < chunks && zc > 0.0) {
+      if (uz < incl) atomicMin(&s_first, cc);
+      atomicMax(&s_last, cc);
     }
-  }
-  __syncthreads();
-  const double P = s_P;
-  const double uz = s_uz;
-  const int t0 = c * kChunk + threadIdx.x * kPer;
-  int32_t* out = out_tokens + (size_t)s * (kd + 1) + n;
-  if (s_found) {
-    const double before = threadIdx.x > 0 ? T[threadIdx.x - 1] : 0.0;
-    const bool here = uz < P + T[threadIdx.x];
-    const bool prev = threadIdx.x > 0 ? (uz < P + before) : false;
-    if (here && !prev) {
-      double L = 0.0;
-      int pick = -1, lastpos = -1;
-      for (int j = 0; j < kPer; ++j) {
-        const int t = t0 + j;
-        if (t >= v) break;
-        double wf, wp;
-        weights_at(fr, t, wf, wp);
-        const double w = use_p ? wp : wf;
-        L = L + w;
-        if (w > 0.0) lastpos = t;
-        if (uz < P + (before + L)) {
-          pick = t;
-          break;
-        }
-      }
-      // the crossing exists at this thread's end by construction; keep a guard
-      *out = pick >= 0 ? pick : lastpos;
-    }
-  } else {
-    // fallback: the last token of chunk c with positive weight
-    int lastpos = -1;
-    for (int j = 0; j < kPer; ++j) {
-      const int t = t0 + j;
-      if (t >= v) break;
-      double wf, wp;
-      weights_at(fr, t, wf, wp);
-      if ((use_p ? wp : wf) > 0.0) lastpos = t;
-    }
-    if (lastpos >= 0) atomicMax(&s_last, lastpos);
     __syncthreads();
-    if (threadIdx.x == 0) *out = s_last;
+    c = s_first;
+    if (c != kNone) {
+      base = c > c0 ? s_incl[c - c0 - 1] : carry;
+      break;
+    }
+    carry = s_incl[kThreads - 1];
+    __syncthreads();
   }
+  const bool found = c != kNone;
+  if (!found) c = s_last;  // no crossing (u >= 1 or rounding): last chunk with positive weight
+  if (c < 0) return;       // a valid row always has positive mass
+  __syncthreads();
+
+  // ---- level 2: threads of chunk c (same thread totals and scan as the decide kernel)
+  const int t0 = c * kChunk + tid * kPer;
+  double wl[kPer];
+  double tau = 0.0;
+  int lastpos = -1;
+  for (int j = 0; j < kPer; ++j) {
+    const int t = t0 + j;
+    double wf = 0.0, wp = 0.0;
+    if (t < v) weights_at(fr, t, wf, wp);
+    wl[j] = use_p ? wp : wf;
+    tau += wl[j];
+    if (wl[j] > 0.0) lastpos = t;
+  }
+  const double sincl = block_inclusive_scan_f64<kThreads>(tau, lds_scan);
+  s_incl[tid] = sincl;
+  if (tid == 0) {
+    s_first = kNone;
+    s_last = -1;
+  }
+  __syncthreads();
+  if (found && tau > 0.0 && uz < base + sincl) atomicMin(&s_first, tid);
+  if (lastpos >= 0) atomicMax(&s_last, lastpos);
+  __syncthreads();
+  int32_t* out = out_tokens + (size_t)s * (kd + 1) + n;
+  const int ti = s_first;
+  if (ti == kNone) {  // fallback chunk, or rounding: last positive token of the chunk
+    if (tid == 0) *out = s_last;
+    return;
+  }
+  if (tid != ti) return;
+  // ---- level 3: tokens of thread ti
+  const double before = base + (ti > 0 ? s_incl[ti - 1] : 0.0);
+  double run = 0.0;
+  int pick = -1;
+  for (int j = 0; j < kPer; ++j) {
+    run += wl[j];
+    if (pick < 0 && wl[j] > 0.0 && uz < before + run) pick = t0 + j;
+  }
+  *out = pick >= 0 ? pick : lastpos;
 }
 
 }  // namespace
 
-size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v) { return carve_bytes(b, kd, v); }
+size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v) { return layout(b, kd, v).total; }
 
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens,
                               const float* uniforms, int32_t b, int32_t kd, int32_t v,
                               int32_t* out_tokens, int32_t* out_num, void* workspace,
                               int32_t* flags, bool vec4, hipStream_t stream) {
   const int chunks = (v + kChunk - 1) / kChunk;
-  const Workspace ws = carve(workspace, b, kd, v);
+  const Layout L = layout(b, kd, v);
+  char* base = static_cast<char*>(workspace);
+  Workspace ws;
+  ws.cmax = reinterpret_cast<float*>(base + L.cmax);
+  ws.csum = reinterpret_cast<double*>(base + L.csum);
+  ws.cbad = reinterpret_cast<int32_t*>(base + L.cbad);
+  ws.dec = reinterpret_cast<Decision*>(base + L.dec);
+  ws.zres = reinterpret_cast<double*>(base + L.zres);
+  ws.zp = reinterpret_cast<double*>(base + L.zp);
   const int64_t rows = (int64_t)b * (2 * kd + 1);
   dim3 g1((unsigned)rows, (unsigned)chunks);
   if (vec4)
@@ -452,13 +451,8 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
     stats_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decide_kernel<<<dim3((unsigned)b), dim3(kWave), 0, stream>>>(target, draft, tokens, uniforms, kd,
-                                                               v, chunks, ws, out_tokens, out_num,
-                                                               flags);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  wsum_kernel<<<dim3((unsigned)chunks, (unsigned)b), dim3(kThreads), 0, stream>>>(target, draft, kd,
-                                                                                  v, chunks, ws);
+  decide_kernel<<<dim3((unsigned)chunks, (unsigned)b), dim3(kThreads), 0, stream>>>(
+      target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   sample_kernel<<<dim3((unsigned)b), dim3(kThreads), 0, stream>>>(target, draft, uniforms, kd, v,

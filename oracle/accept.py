@@ -97,8 +97,9 @@ def step(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, u: np.ndarra
     (drawn from the draft laws by the caller), u [K+1] fp32 uniforms.
 
     Returns out_tokens [K+1] (first n+1 valid, rest -1), n (accepted drafts),
-    flags, flagged (a decision or the final draw was within MARGIN of u) and
-    the per-position acceptance probabilities that were evaluated.
+    flags, flagged (a decision or the final draw was within MARGIN of u), the
+    smallest such distance (margin) and the per-position acceptance
+    probabilities that were evaluated.
     """
     target = np.asarray(target, dtype=np.float32)
     draft = np.asarray(draft, dtype=np.float32)
@@ -111,10 +112,10 @@ def step(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, u: np.ndarra
     p_rows = [softmax(target[i]) for i in range(kd + 1)]
     q_rows = [softmax(draft[i]) for i in range(kd)]
     if any(r is None for r in p_rows + q_rows):
-        return dict(out_tokens=out, n=0, flags=FLAG_NONFINITE, flagged=False, a=[])
+        return dict(out_tokens=out, n=0, flags=FLAG_NONFINITE, flagged=False, margin=np.inf, a=[])
 
     flags = 0
-    flagged = False
+    margin_min = np.inf
     a_seen = []
     n = kd
     for i in range(kd):
@@ -123,8 +124,7 @@ def step(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, u: np.ndarra
         flags |= f
         a_seen.append(a)
         ui = float(u[i])
-        if abs(ui - a) < MARGIN:
-            flagged = True
+        margin_min = min(margin_min, abs(ui - a))
         if ui < a:
             out[i] = x
             continue
@@ -139,10 +139,10 @@ def step(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, u: np.ndarra
     else:
         w = p_rows[kd]
     t, margin = inverse_cdf(w, float(u[kd]))
-    if margin < MARGIN:
-        flagged = True
+    margin_min = min(margin_min, margin)
     out[n] = t
-    return dict(out_tokens=out, n=n, flags=flags, flagged=flagged, a=a_seen)
+    return dict(out_tokens=out, n=n, flags=flags, flagged=bool(margin_min < MARGIN),
+                margin=margin_min, a=a_seen)
 
 
 def step_batch(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, u: np.ndarray) -> dict:
@@ -153,10 +153,12 @@ def step_batch(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, u: np.
     n = np.zeros(b, dtype=np.int32)
     flags = np.zeros(b, dtype=np.int32)
     flagged = np.zeros(b, dtype=bool)
+    margin = np.zeros(b)
     for s in range(b):
         r = step(target[s], draft[s], tokens[s], u[s])
-        out[s], n[s], flags[s], flagged[s] = r["out_tokens"], r["n"], r["flags"], r["flagged"]
-    return dict(out_tokens=out, n=n, flags=flags, flagged=flagged)
+        out[s], n[s], flags[s], flagged[s], margin[s] = (r["out_tokens"], r["n"], r["flags"],
+                                                         r["flagged"], r["margin"])
+    return dict(out_tokens=out, n=n, flags=flags, flagged=flagged, margin=margin)
 
 
 def residual_law(p: np.ndarray, q: np.ndarray) -> np.ndarray:

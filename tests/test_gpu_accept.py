@@ -1,9 +1,13 @@
 """spec_accept on the GPU vs the scalar oracle loop.
 
 Accepted counts and emitted tokens must be bit-exact for every sequence the
-oracle does not flag (a decision or the final draw within 1e-6 of u); flagged
-sequences are counted, not compared. Device flags must equal the OR of the
-oracle's per-sequence flags.
+oracle does not flag (a decision or the final draw within 1e-6 of u). Both
+sides compute probabilities and prefix sums in fp64, so flagged sequences are
+compared as well unless their margin is below 1e-12 (stronger than the 1e-6
+contract). With V = 128256 the residual spreads over ~1e5 tokens and the 1e-6
+band around the final draw's interval ends is hit in several percent of
+sequences, so no cap is put on the flagged fraction. Device flags must equal
+the OR of the oracle's per-sequence flags.
 """
 import numpy as np
 import pytest
@@ -26,14 +30,19 @@ def run_accept(target, draft, tokens, u):
     return host(out), host(n), int(flags.item())
 
 
-def compare(target, draft, tokens, u, label, max_flagged_frac=0.01):
+STRICT_MARGIN = 1e-12
+
+
+def compare(target, draft, tokens, u, label):
     out, n, f = run_accept(target, draft, tokens, u)
     ref = oacc.step_batch(target, draft, tokens, u)
-    ok = ~ref["flagged"]
-    assert ref["flagged"].mean() <= max_flagged_frac, (label, ref["flagged"].mean())
-    bad = np.nonzero(ok & ((n != ref["n"]) | np.any(out != ref["out_tokens"], axis=1)))[0]
+    differ = (n != ref["n"]) | np.any(out != ref["out_tokens"], axis=1)
+    bad = np.nonzero(~ref["flagged"] & differ)[0]
     assert bad.size == 0, (label, bad[:5], n[bad[:5]], ref["n"][bad[:5]], out[bad[:5]], ref["out_tokens"][bad[:5]])
+    bad = np.nonzero((ref["margin"] >= STRICT_MARGIN) & differ)[0]
+    assert bad.size == 0, (label, "flagged but fp64-resolvable", bad[:5], ref["margin"][bad[:5]])
     assert f == int(np.bitwise_or.reduce(ref["flags"])), (label, f, ref["flags"])
+    say(f"  {label}: {len(n)} sequences, {int(ref['flagged'].sum())} flagged, mean accepted {n.mean():.2f}")
     return ref
 
 
@@ -69,7 +78,7 @@ def test_vocab_edges(v):
     """Chunk boundaries (4096 logits per chunk) and vocabularies that disable vector loads."""
     say(f"accept: V={v}")
     tgt, dft, tok, u = synth.accept_batch(5, 300, 3, v, 2.0, 1.0, seq0=v)
-    compare(tgt, dft, tok, u, f"v={v}", max_flagged_frac=0.05)
+    compare(tgt, dft, tok, u, f"v={v}")
 
 
 def _logits(p):
@@ -127,7 +136,7 @@ def test_edge_cases_and_flags():
         u = np.asarray(uu, np.float32)[None]
         out, n, f = run_accept(tgt, dft, tok, u)
         ref = oacc.step(tgt[0], dft[0], tok[0], u[0])
-        assert not ref["flagged"] or i in (1,), i
+        assert not ref["flagged"] or i in (1, 6), i   # 1: u = a = 0; 6: u at the top of the last interval
         assert n[0] == ref["n"] and list(out[0]) == list(ref["out_tokens"]), (i, out, ref)
         assert f == ref["flags"], (i, f, ref["flags"])
     # case-specific expectations from the rule itself
@@ -145,3 +154,22 @@ def test_residual_zero_fallback():
     ref = oacc.step(tgt[0], dft[0], [0], np.array([1.0, 0.75], np.float32))
     assert n[0] == ref["n"] == 0 and out[0, 0] == ref["out_tokens"][0] == 1
     assert f == ref["flags"] and f & mxs.FLAG_RESIDUAL_ZERO
+
+
+@pytest.mark.parametrize("v", [6, 4097, 128256])
+def test_equal_rows_forced_rejection(v):
+    """Target row == draft row and an out-of-range draft token: the residual is exactly zero
+    (no FMA residue), so the draw falls back to p and RESIDUAL_ZERO is raised."""
+    say(f"accept: equal rows, forced rejection, V={v}")
+    z = synth.rng(9, 3, v).standard_normal((3, v)).astype(np.float32) * np.float32(3.0)
+    tgt = z[None]
+    dft = z[None, :2].copy()
+    tok = np.array([[0, v + 5]], np.int32)
+    for uk in [0.0, 0.3, 0.77]:
+        u = np.array([[0.5, 0.5, uk]], np.float32)
+        out, n, f = run_accept(tgt, dft, tok, u)
+        ref = oacc.step(tgt[0], dft[0], tok[0], u[0])
+        assert ref["flags"] == (mxs.FLAG_TOKEN_RANGE | mxs.FLAG_RESIDUAL_ZERO)
+        assert f == ref["flags"], (v, uk, f)
+        if ref["margin"] >= 1e-12:
+            assert n[0] == ref["n"] == 1 and list(out[0]) == list(ref["out_tokens"]), (v, uk)
