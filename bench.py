@@ -14,10 +14,12 @@ weights from HBM. Inputs are resident in HBM before the timed region. Weights
 are N(0, 0.02) fp32 drawn on the GPU and quantized by mxfp4_quantize (not
 timed). The logits and uniforms come from the shared seeded generator.
 
-Prints one JSON line. `value` is verify-GEMM algorithmic bytes per step
-(codes + scales + X + Y) times steps, over the wall time of all steps
-(spec_accept and launch gaps included). `roofline` is the verify-GEMM kernel
-alone, from HIP events around each launch on the launch stream.
+Each step is captured once per pool layer as a HIP graph and the timed region
+replays K graphs back to back. Prints one JSON line. `value` is verify-GEMM
+algorithmic bytes per step (codes + scales + X + Y) times steps, over the
+wall time of all steps (spec_accept and the gaps between kernels included).
+`roofline` is the verify-GEMM kernel alone, from HIP events around each launch
+in a separate eager pass on the launch stream.
 """
 from __future__ import annotations
 
@@ -159,7 +161,6 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
 
     layer_bytes = sum(mx_bytes(n, k) for _, n, k in LAYER)
     n_layers = max(1, math.ceil(args.pool_gb * 1e9 / layer_bytes))
@@ -187,32 +188,52 @@ def main():
     torch.cuda.synchronize()
 
     def step(s, ev=None):
+        st = torch.cuda.current_stream()
         mats = pool[s % n_layers]
         for j, (codes, scales, x) in enumerate(mats):
             if ev is not None:
-                ev[j][0].record(stream)
-            mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[j], stream=stream)
+                ev[j][0].record(st)
+            mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[j], stream=st)
             if ev is not None:
-                ev[j][1].record(stream)
+                ev[j][1].record(st)
         if ev is not None:
-            ev[-1][0].record(stream)
+            ev[-1][0].record(st)
         mxs.spec_accept(d_tgt, d_dft, d_tok, d_u, out_tokens=out_tok, out_num=out_n, workspace=ws,
-                        stream=stream)
+                        stream=st)
         if ev is not None:
-            ev[-1][1].record(stream)
+            ev[-1][1].record(st)
 
-    for s in range(args.warmup):
+    # eager warmup, then one HIP graph per pool layer (a graph replays one whole step)
+    for s in range(max(args.warmup, n_layers)):
         step(s)
     torch.cuda.synchronize()
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for li in range(n_layers):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(li)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        graphs[s % n_layers].replay()
+    torch.cuda.synchronize()
 
+    # timed region: K graph replays (one step each)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        graphs[(args.warmup + s) % n_layers].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # kernel durations: an eager pass with one event pair around every launch
     mk = lambda: torch.cuda.Event(enable_timing=True)
     events = [[(mk(), mk()) for _ in range(len(LAYER) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(args.steps):
         step(args.warmup + s, events[s])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     gemm_ms = np.array([[events[s][j][0].elapsed_time(events[s][j][1]) for j in range(len(LAYER))]
                         for s in range(args.steps)])

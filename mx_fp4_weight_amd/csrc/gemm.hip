@@ -28,6 +28,8 @@
 // loads in flight. The activations of a group are loaded once per wave and
 // reused by its R row tiles. Partial 16×16 tiles are summed across waves in
 // LDS in wave order: results are deterministic.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -55,27 +57,207 @@ __device__ inline bf16x8 decode8(uint32_t c, float scale) {
   return r;
 }
 
-template <int R, int S>
-struct Stage {
-  u32x4 c[R][S];     // 16 code bytes (one MX block) per row tile and group
-  uint32_t s[R][S];  // its scale byte
-  u32x4 xb[S][4];    // activations: 4 × 8 bf16 per group
+// ---------------------------------------------------------------------------
+// Main kernel: persistent workgroups, activations staged once in LDS.
+//
+// A workgroup stages X[t0 : t0+mt, :] into LDS once, then walks row blocks
+// rb = blockIdx.x, blockIdx.x + gridDim.x, ... Inside a row block (R×16 rows,
+// all of k) wave w owns the contiguous k-slice of G groups starting at w·G and
+// issues all of its R·G code loads (1 KiB each per wave) plus the scale loads
+// at once. While a row block is computed, the loads of the next one are
+// already in flight (two register buffers, loop unrolled by two so no copy
+// forces a wait). Loads go through buffer descriptors that cover exactly the
+// valid bytes of a row block: rows past n, groups past the slice and a
+// missing next block read as zero without a branch, so the compiler's
+// wait counts stay exact. Partial tiles are reduced in LDS (two buffers
+// alternate between row blocks) behind an LDS-only barrier, which leaves the
+// prefetched global loads in flight.
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // past any num_records: the load reads 0
+
+// X staged in LDS in MFMA-operand order. The 16-byte chunk q (8 bf16) of
+// activation row t goes to unit ((grp*4 + d)*mt + t)*4 + g with grp = q/16,
+// g = (q/4)%4, d = q%4: for one group and MFMA slice d, the lanes (t, g) read
+// consecutive 16-byte units, so ds_read_b128 has no bank conflicts.
+__device__ inline int xunit(int grp, int d, int t, int g, int mt) { return ((grp * 4 + d) * mt + t) * 4 + g; }
+
+template <int R, int G>
+struct Block {
+  u32x4 c[R][G];        // 16 code bytes per row tile and group
+  u32x4 s[R][G / 4];    // 16 scale bytes = 4 groups x 4 blocks of the row
 };
 
-template <int R, int S>
+template <int R, int G>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m, int gpw,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m, int nrb, int nsub,
     int y_vec4) {
-  extern __shared__ f32x4 red[];  // [W][R][64]
+  extern __shared__ u32x4 smem[];
   const int W = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = lane & 15;  // A row of this lane inside a tile; also its B column
   const int g = lane >> 4;  // which 32-k block of a 128-k group
+  const int t0 = blockIdx.y * 16;
+  const int mt = min(16, m - t0);
+  const int t = t0 + r;
+  const bool t_ok = r < mt;
+  const int kb = k >> 5;
+  const int ngroups = (kb + 3) >> 2;
+  const int gs = wave * G * nsub;  // first group of this wave's k-slice
+  const uint32_t row_bytes = (uint32_t)(k >> 1);
+  const int xunits = ngroups * 16 * mt;
+  f32x4* red = reinterpret_cast<f32x4*>(smem + xunits);  // [2][W][R][64]
+
+  // this workgroup's work: its row blocks times the nsub sub-slices of G groups
+  const int my_blocks = blockIdx.x < nrb ? (nrb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int nunits = my_blocks * nsub;
+
+  auto load = [&](int u, Block<R, G>& b) {
+    const int rb = (int)blockIdx.x + (u / nsub) * (int)gridDim.x;
+    const int g0 = gs + (u % nsub) * G;
+    // descriptors covering the valid rows of row block rb (none past the last unit)
+    const int row0 = rb * 16 * R;
+    const int rows = u < nunits ? min(16 * R, n - row0) : 0;
+    const int rowc = u < nunits ? row0 : 0;
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)rowc * kb, (uint32_t)rows * (uint32_t)kb);
+    // The whole offset goes in voffset (soffset = 0): the range check of a raw
+    // buffer load covers voffset + the immediate only.
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int blk = (g0 + j) * 4 + g;
+      const bool ok = blk < kb;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const uint32_t off = ok ? (uint32_t)(16 * i + r) * row_bytes + (uint32_t)blk * 16 : kOutOfRange;
+        b.c[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < G / 4; ++q) {
+      const int grp0 = g0 + 4 * q;
+      const bool ok = grp0 < ngroups;
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const uint32_t off = ok ? (uint32_t)(16 * i + r) * (uint32_t)kb + (uint32_t)grp0 * 4 : kOutOfRange;
+        b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+      }
+    }
+  };
+
+  f32x4 acc[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int parity = 0;
+
+  auto compute = [&](int u, const Block<R, G>& b) {
+    const int g0 = gs + (u % nsub) * G;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int grp = g0 + j;
+      const bool ok = t_ok && grp < ngroups && grp * 4 + g < kb;
+      float sf[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) sf[i] = e8m0_to_f32((b.s[i][j / 4][j % 4] >> (8 * g)) & 0xffu);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        u32x4 bx = u32x4{0u, 0u, 0u, 0u};
+        if (ok) bx = smem[xunit(grp, d, r, g, mt)];
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, bx);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const bf16x8 a = decode8(b.c[i][j][d], sf[i]);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc[i], 0, 0, 0);
+        }
+      }
+    }
+    if (u % nsub != nsub - 1) return;
+    // last sub-slice of the row block: sum the waves' partial tiles and store
+    const int rb = (int)blockIdx.x + (u / nsub) * (int)gridDim.x;
+    f32x4* rp = red + (size_t)parity * W * R * kWave;
+#pragma unroll
+    for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = acc[i];
+    lds_barrier();
+    const int row0 = rb * 16 * R;
+    for (int i = wave; i < R; i += W) {
+      f32x4 sum = rp[i * kWave + lane];
+      for (int w = 1; w < W; ++w) sum += rp[(w * R + i) * kWave + lane];
+      // lane holds C[4g + e][r]: output row row0 + 16 i + 4 g + e, position t
+      const int orow = row0 + 16 * i + 4 * g;
+      if (t_ok) {
+        float* yp = y + (size_t)t * (size_t)n + orow;
+        if (y_vec4 && orow + 3 < n) {
+          *reinterpret_cast<f32x4*>(yp) = sum;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (orow + e < n) yp[e] = sum[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    parity ^= 1;
+  };
+
+  // activations first (L2-resident, short latency), then the first unit's codes
+  const int nq = k >> 3;  // 16-byte chunks per activation row
+  for (int idx = threadIdx.x; idx < mt * nq; idx += blockDim.x) {
+    const int tt = idx / nq;
+    const int q = idx - tt * nq;
+    smem[xunit(q >> 4, q & 3, tt, (q >> 2) & 3, mt)] =
+        *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * (size_t)k + (size_t)q * 8);
+  }
+  Block<R, G> A, B;
+  load(0, A);
+  lds_barrier();
+  for (int u = 0; u < nunits;) {
+    load(u + 1, B);  // past the last unit: a zero-record descriptor, nothing is read
+    compute(u, A);
+    if (++u >= nunits) break;
+    load(u + 1, A);
+    compute(u, B);
+    ++u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fallback when X[mt, k] does not fit in LDS: activations loaded from global
+// memory by every wave, one workgroup per row block, waves split k.
+template <int R, int S>
+struct Stage {
+  u32x4 c[R][S];
+  uint32_t s[R][S];
+  u32x4 xb[S][4];
+};
+
+template <int R, int S>
+__global__ __launch_bounds__(kMaxWaves * kWave) void gemm_xglobal_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m, int gpw,
+    int y_vec4) {
+  extern __shared__ u32x4 smem[];
+  const int W = blockDim.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int r = lane & 15;
+  const int g = lane >> 4;
   const int row_base = blockIdx.x * (16 * R);
-  const int t = blockIdx.y * 16 + r;
-  const bool t_ok = t < m;
+  const int t0 = blockIdx.y * 16;
+  const int mt = min(16, m - t0);
+  const int t = t0 + r;
+  const bool t_ok = r < mt;
   const int kb = k >> 5;
   const int ngroups = (kb + 3) >> 2;
   const int gs = wave * gpw;
@@ -152,14 +334,13 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
     }
   }
 
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [W][R][64]
 #pragma unroll
   for (int i = 0; i < R; ++i) red[(wave * R + i) * kWave + lane] = acc[i];
   __syncthreads();
-  // wave w sums tile w, w + W, ... over all waves in wave order
   for (int i = wave; i < R; i += W) {
     f32x4 sum = red[i * kWave + lane];
     for (int w = 1; w < W; ++w) sum += red[(w * R + i) * kWave + lane];
-    // lane holds C[4g + e][r]: output row row_base + 16 i + 4 g + e, position t
     const int orow = row_base + 16 * i + 4 * g;
     if (t_ok) {
       float* yp = y + (size_t)t * (size_t)n + orow;
@@ -174,45 +355,103 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
   }
 }
 
-template <int R, int S>
-hipError_t launch_rs(int waves, int gpw, const uint8_t* codes, const uint8_t* scales, int64_t n,
-                     int64_t k, const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
-  dim3 grid((unsigned)((n + 16 * R - 1) / (16 * R)), (unsigned)((m + 15) / 16));
-  const size_t lds = sizeof(f32x4) * (size_t)waves * R * kWave;
-  // 16-byte stores of 4 consecutive outputs need n % 4 == 0 and a 16-byte aligned y
-  const int y_vec4 = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
-  gemm_skinny_kernel<R, S><<<grid, dim3(waves * kWave), lds, stream>>>(
-      codes, scales, x, y, (int)n, (int)k, (int)m, gpw, y_vec4);
-  return hipGetLastError();
+constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kMaxDevices = 64;
+constexpr int kCUs = 256;
+
+// Raise a kernel's dynamic-LDS limit once per device.
+template <typename F>
+hipError_t allow_lds(F* kernel, std::atomic<bool>* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < kMaxDevices && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  if (e == hipSuccess && dev < kMaxDevices) done[dev].store(true, std::memory_order_relaxed);
+  return e;
 }
 
 struct Config {
-  int R, S, gpw;
+  int R, G;      // row tiles per row block; 128-k groups per wave
+  int per_cu;    // resident workgroups per CU targeted by the persistent grid
 };
 
-hipError_t launch_cfg(Config c, const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
-                      const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+inline int y_vec4_ok(const float* y, int64_t n) {
+  return (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+}
+
+// Waves per workgroup and sub-slices per wave for a k of `ngroups` 128-k groups.
+inline void split_k(int64_t ngroups, int G, int& waves, int& nsub) {
+  const int64_t slices = (ngroups + G - 1) / G;  // sub-slices of G groups
+  nsub = (int)((slices + kMaxWaves - 1) / kMaxWaves);
+  waves = (int)((ngroups + (int64_t)G * nsub - 1) / ((int64_t)G * nsub));
+}
+
+// LDS bytes the main kernel needs: X[mt, k] in operand order plus two reduction buffers.
+inline size_t main_lds(int64_t k, int64_t m, int R, int G) {
+  const int64_t ngroups = (k / 32 + 3) / 4;
+  int waves, nsub;
+  split_k(ngroups, G, waves, nsub);
+  const int64_t mt = m < 16 ? m : 16;
+  return (size_t)ngroups * 16 * mt * 16 + 2 * sizeof(f32x4) * waves * R * kWave;
+}
+
+template <int R, int G>
+hipError_t launch_main(const Config& c, const uint8_t* codes, const uint8_t* scales, int64_t n,
+                       int64_t k, const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+  static std::atomic<bool> done[kMaxDevices];
+  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G>, done);
+  if (e != hipSuccess) return e;
+  const int64_t ngroups = (k / 32 + 3) / 4;
+  int waves, nsub;
+  split_k(ngroups, G, waves, nsub);
+  const size_t lds = main_lds(k, m, R, G);
+  const int64_t nrb = (n + 16 * R - 1) / (16 * R);
+  int64_t grid = (int64_t)kCUs * c.per_cu;
+  if (grid > nrb) grid = nrb;
+  gemm_skinny_kernel<R, G><<<dim3((unsigned)grid, (unsigned)((m + 15) / 16)), dim3(waves * kWave), lds,
+                             stream>>>(codes, scales, x, y, (int)n, (int)k, (int)m, (int)nrb, nsub,
+                                       y_vec4_ok(y, n));
+  return hipGetLastError();
+}
+
+template <int R, int S>
+hipError_t launch_xglobal(int gpw, const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                          const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
   const int ngroups = (int)((k / 32 + 3) / 4);
-  int gpw = c.gpw < 1 ? 1 : c.gpw;
   int waves = (ngroups + gpw - 1) / gpw;
-  if (waves > kMaxWaves) {  // widen the slices until the workgroup fits
+  if (waves > kMaxWaves) {
     gpw = (ngroups + kMaxWaves - 1) / kMaxWaves;
     waves = (ngroups + gpw - 1) / gpw;
   }
-#define MXS_RS(RR, SS) \
-  if (c.R == RR && c.S == SS) return launch_rs<RR, SS>(waves, gpw, codes, scales, n, k, x, m, y, stream);
-  MXS_RS(1, 1) MXS_RS(1, 2) MXS_RS(1, 4) MXS_RS(2, 1) MXS_RS(2, 2) MXS_RS(2, 4)
-  MXS_RS(4, 1) MXS_RS(4, 2)
-#undef MXS_RS
-  return hipErrorInvalidValue;
+  const size_t lds = sizeof(f32x4) * (size_t)waves * R * kWave;
+  dim3 grid((unsigned)((n + 16 * R - 1) / (16 * R)), (unsigned)((m + 15) / 16));
+  gemm_xglobal_kernel<R, S><<<grid, dim3(waves * kWave), lds, stream>>>(
+      codes, scales, x, y, (int)n, (int)k, (int)m, gpw, y_vec4_ok(y, n));
+  return hipGetLastError();
 }
 
-// Shape-based choice: enough waves in flight to cover HBM latency on 256 CUs.
+hipError_t launch_cfg(Config c, const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                      const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+  // Main kernel: 16-byte scale loads need k % 512 == 0 and 16-byte aligned scales; a row
+  // block's bytes (64 rows at most) must fit a 32-bit buffer range; X must fit in LDS.
+  const bool aligned = (k % 512 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 15) == 0);
+  if (aligned && k <= (int64_t(1) << 24) && main_lds(k, m, c.R, c.G) <= kMaxLds) {
+#define MXS_RG(RR, GG) \
+  if (c.R == RR && c.G == GG) return launch_main<RR, GG>(c, codes, scales, n, k, x, m, y, stream);
+    MXS_RG(1, 4) MXS_RG(1, 8) MXS_RG(2, 4) MXS_RG(2, 8) MXS_RG(4, 4)
+#undef MXS_RG
+    return hipErrorInvalidValue;
+  }
+  return launch_xglobal<2, 4>(4, codes, scales, n, k, x, m, y, stream);
+}
+
+// Shape-based choice: enough bytes in flight to cover HBM latency on 256 CUs.
 Config choose(int64_t n, int64_t k) {
-  const int64_t ngroups = (k / 32 + 3) / 4;
-  Config c{1, 2, 4};
-  if (n >= 8192) c.R = 2;
-  if (ngroups <= 8) c.gpw = 2;
+  Config c{1, 4, 2};
+  if (n >= 16384) c.R = 2;
+  if (k >= 8192) c.G = 8;
   return c;
 }
 
@@ -224,10 +463,10 @@ hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64
 }
 
 #ifdef MXS_TUNING
-hipError_t launch_verify_gemm_cfg(int R, int S, int gpw, const uint8_t* codes,
+hipError_t launch_verify_gemm_cfg(int R, int G, int per_cu, const uint8_t* codes,
                                   const uint8_t* scales, int64_t n, int64_t k, const uint16_t* x,
                                   int64_t m, float* y, hipStream_t stream) {
-  return launch_cfg(Config{R, S, gpw}, codes, scales, n, k, x, m, y, stream);
+  return launch_cfg(Config{R, G, per_cu}, codes, scales, n, k, x, m, y, stream);
 }
 #endif
 
@@ -236,9 +475,9 @@ hipError_t launch_verify_gemm_cfg(int R, int S, int gpw, const uint8_t* codes,
 #ifdef MXS_TUNING
 // Tuning builds only (not part of the product library): explicit tile configuration.
 extern "C" int mxs_tune_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n,
-                                    int64_t k, const uint16_t* x, int64_t m, float* y, int R, int S,
-                                    int gpw, void* stream) {
-  return (int)mxs::launch_verify_gemm_cfg(R, S, gpw, codes, scales, n, k, x, m, y,
+                                    int64_t k, const uint16_t* x, int64_t m, float* y, int R, int G,
+                                    int per_cu, void* stream) {
+  return (int)mxs::launch_verify_gemm_cfg(R, G, per_cu, codes, scales, n, k, x, m, y,
                                           static_cast<hipStream_t>(stream));
 }
 #endif

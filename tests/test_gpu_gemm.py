@@ -41,8 +41,13 @@ def test_one_hot_columns_exact():
 
 
 @pytest.mark.parametrize("n,k,m", [
+    # k % 512 != 0: activations read from global memory by every wave
     (1, 32, 1), (17, 32, 5), (16, 96, 3), (33, 160, 8), (1000, 4128, 5), (300, 1056, 16),
-    (64, 512, 17), (129, 640, 33), (5, 8192, 1), (2048, 288, 7),
+    (129, 640, 33), (2048, 288, 7),
+    # k % 512 == 0: persistent kernel with activations in LDS (partial row blocks,
+    # several column tiles, k split into sub-slices, waves past the last group)
+    (5, 8192, 1), (64, 512, 17), (1000, 4096, 5), (17, 1024, 3), (4100, 512, 9),
+    (130, 14336, 5), (33, 2048, 16), (100, 512, 40), (70000, 512, 2), (3, 11776, 8),
 ])
 def test_ragged_shapes(n, k, m):
     say(f"gemm: ragged n={n} k={k} m={m}")
