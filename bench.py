@@ -2,11 +2,13 @@
 """Benchmark of the speculative verification step on one MI355X.
 
 Workload (8B-class layer shapes at T = K+1 = 5): one step streams one decoder
-layer's MX-FP4 weights through mxfp4_verify_gemm — q and o 4096x4096, k and v
-1024x4096, gate and up 14336x4096, down 4096x14336 (218,103,808 weights,
-115,867,648 bytes of codes + scales) — each against its own bf16 activations
-[5, K], then runs spec_accept on one sequence (K = 4 drafts, vocab 128256,
-fp32 logits N(0, 3), target = draft + N(0, 1)).
+layer's MX-FP4 weights — q and o 4096x4096, k and v 1024x4096, gate and up
+14336x4096, down 4096x14336 (218,103,808 weights, 115,867,648 bytes of codes +
+scales), each against its own bf16 activations [5, K] — in dependency order:
+mxfp4_verify_gemm_grouped over q | k | v, mxfp4_verify_gemm for o,
+mxfp4_verify_gemm_grouped over gate | up, mxfp4_verify_gemm for down. Then it
+runs spec_accept on one sequence (K = 4 drafts, vocab 128256, fp32 logits
+N(0, 3), target = draft + N(0, 1)).
 
 Cold weights: the layers of a pool larger than the 256 MB Infinity Cache
 (default 1.5 GB, 13 layers) are visited in turn, so every step reads its
@@ -14,12 +16,13 @@ weights from HBM. Inputs are resident in HBM before the timed region. Weights
 are N(0, 0.02) fp32 drawn on the GPU and quantized by mxfp4_quantize (not
 timed). The logits and uniforms come from the shared seeded generator.
 
-Each step is captured once per pool layer as a HIP graph and the timed region
-replays K graphs back to back. Prints one JSON line. `value` is verify-GEMM
+Each step is captured once per pool layer as a HIP graph on one stream; the
+timed region replays K graphs back to back. Prints one JSON line. `value` is verify-GEMM
 algorithmic bytes per step (codes + scales + X + Y) times steps, over the
 wall time of all steps (spec_accept and the gaps between kernels included).
-`roofline` is the verify-GEMM kernel alone, from HIP events around each launch
-in a separate eager pass on the launch stream.
+`roofline` is the verify-GEMM kernel alone: for each launch type a graph runs
+it on every pool layer back to back between two HIP events on the replay
+stream, giving the average launch duration without host gaps.
 """
 from __future__ import annotations
 
@@ -42,7 +45,10 @@ V = 128256
 # (name, n, k) of one 8B-class decoder layer
 LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
          ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
+# launches of a layer in dependency order; projections that read the same input share one
+LAUNCHES = [("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,))]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_gemm_8b_layer_t5_traffic.json")
+CALIB_MB = 512
 GEMM_SRC = os.path.join(ROOT, "mx_fp4_weight_amd", "csrc", "gemm.hip")
 
 
@@ -70,6 +76,56 @@ def load_traffic():
     if d.get("gemm_source_sha") != source_sha(GEMM_SRC):
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def summarize_pmc(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
+    """HBM bytes per verify-GEMM launch from two rocprofv3 --pmc runs of this script.
+
+    Each run must use --calib-copy-mb: the counters of that plain elementwise kernel
+    of a known size give the bytes-per-count factor (counter KiB x 1024 / true bytes).
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.
+    """
+    import csv
+    import glob
+
+    def rows(d, counter):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return out
+
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rr = rows(d, counter)
+        copy = [v for name, v in rr if "neg_kernel" in name]
+        gemm = [v for name, v in rr if "gemm_skinny_kernel" in name or "gemm_xglobal_kernel" in name]
+        if not copy or not gemm:
+            raise SystemExit(f"no copy/gemm dispatches with {counter} in {d}")
+        calib_bytes = CALIB_MB * 1024 * 1024
+        factor = max(copy) * 1024 / calib_bytes
+        res[counter] = {"gemm_kib_mean": sum(gemm) / len(gemm), "dispatches": len(gemm),
+                        "copy_kib": max(copy), "factor": factor,
+                        "bytes_per_launch": sum(gemm) / len(gemm) * 1024 / factor}
+    summary = {
+        "kernel": "gemm_skinny_kernel (mxfp4_verify_gemm), 8B-class layer shapes at T=5",
+        "gemm_source_sha": source_sha(GEMM_SRC),
+        "traffic_bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"],
+        "alg_bytes_per_launch": sum(gemm_alg_bytes(n, k, T) for _, n, k in LAYER) / len(LAUNCHES),
+        "counters": res,
+        "calibration": f"torch.neg over {CALIB_MB} MiB of fp32 (reads and writes {CALIB_MB} MiB)",
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o pmc -- "
+            f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mb {CALIB_MB}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o pmc -- "
+            f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mb {CALIB_MB}",
+            f"python3 bench.py --summarize-pmc {fetch_dir} {write_dir}",
+        ],
+    }
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary, indent=1))
 
 
 def cpu_baseline(seconds_budget=15.0):
@@ -143,7 +199,14 @@ def main():
     ap.add_argument("--pool-gb", type=float, default=1.5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs into the committed traffic file")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -186,33 +249,42 @@ def main():
     out_n = torch.empty((1,), dtype=torch.int32, device=dev)
     ws = torch.empty((mxs.spec_accept_workspace_bytes(1, KD, V),), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+    if args.calib_copy_mb:
+        # a plain elementwise kernel that reads and writes exactly this many bytes
+        src = torch.ones((args.calib_copy_mb << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
-    def step(s, ev=None):
+    def step(s):
+        """One layer: [q | k | v] -> o -> [gate | up] -> down (grouped launches), then spec_accept.
+
+        All launches go on the current stream (cross-stream joins inside a graph
+        cost more than the overlap gains on this stack).
+        """
         st = torch.cuda.current_stream()
         mats = pool[s % n_layers]
-        for j, (codes, scales, x) in enumerate(mats):
-            if ev is not None:
-                ev[j][0].record(st)
-            mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[j], stream=st)
-            if ev is not None:
-                ev[j][1].record(st)
-        if ev is not None:
-            ev[-1][0].record(st)
+        for _, idx in LAUNCHES:
+            if len(idx) == 1:
+                codes, scales, x = mats[idx[0]]
+                mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[idx[0]], stream=st)
+            else:
+                mxs.mxfp4_verify_gemm_grouped([mats[i] for i in idx], ys=[ys[i] for i in idx],
+                                              stream=st)
         mxs.spec_accept(d_tgt, d_dft, d_tok, d_u, out_tokens=out_tok, out_num=out_n, workspace=ws,
                         stream=st)
-        if ev is not None:
-            ev[-1][1].record(st)
 
     # eager warmup, then one HIP graph per pool layer (a graph replays one whole step)
     for s in range(max(args.warmup, n_layers)):
         step(s)
     torch.cuda.synchronize()
     graphs = []
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
     for li in range(n_layers):
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
+        with torch.cuda.graph(g, stream=cap):
             step(li)
         graphs.append(g)
     torch.cuda.synchronize()
@@ -227,25 +299,63 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # kernel durations: an eager pass with one event pair around every launch
-    mk = lambda: torch.cuda.Event(enable_timing=True)
-    events = [[(mk(), mk()) for _ in range(len(LAYER) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        step(args.warmup + s, events[s])
-    torch.cuda.synchronize()
+    # Kernel durations: for each launch type one graph that runs it on every pool
+    # layer back to back (cold weights, no host gaps between kernels), bracketed by
+    # two events on the replay stream; the same for spec_accept alone.
+    def launch(j, li):
+        mats = pool[li]
+        _, idx = LAUNCHES[j]
+        st = torch.cuda.current_stream()
+        if len(idx) == 1:
+            codes, scales, x = mats[idx[0]]
+            mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[idx[0]], stream=st)
+        else:
+            mxs.mxfp4_verify_gemm_grouped([mats[i] for i in idx], ys=[ys[i] for i in idx], stream=st)
 
-    gemm_ms = np.array([[events[s][j][0].elapsed_time(events[s][j][1]) for j in range(len(LAYER))]
-                        for s in range(args.steps)])
-    acc_ms = np.array([events[s][-1][0].elapsed_time(events[s][-1][1]) for s in range(args.steps)])
+    def accept_only():
+        mxs.spec_accept(d_tgt, d_dft, d_tok, d_u, out_tokens=out_tok, out_num=out_n, workspace=ws,
+                        stream=torch.cuda.current_stream())
+
+    type_graphs = []
+    for j in range(len(LAUNCHES)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for li in range(n_layers):
+                launch(j, li)
+        type_graphs.append(g)
+    acc_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(acc_graph, stream=cap):
+        for _ in range(n_layers):
+            accept_only()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // n_layers)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def time_graph(g):
+        g.replay()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = mk(), mk()
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * n_layers)  # ms per launch
+
+    launch_ms = [time_graph(g) for g in type_graphs]
+    acc_ms_mean = time_graph(acc_graph)
+
     step_gemm_bytes = sum(gemm_alg_bytes(n, k, T) for _, n, k in LAYER)
     value = step_gemm_bytes * args.steps / wall / 1e9
-    launches = gemm_ms.size
-    avg_launch_ms = gemm_ms.mean()
-    avg_launch_bytes = step_gemm_bytes / len(LAYER)
+    launches = reps * n_layers * len(LAUNCHES)
+    avg_launch_ms = float(np.mean(launch_ms))
+    avg_launch_bytes = step_gemm_bytes / len(LAUNCHES)
     achieved = avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
-    per_shape = {name: round(gemm_alg_bytes(n, k, T) / (gemm_ms[:, j].mean() * 1e-3) / 1e9, 1)
-                 for j, (name, n, k) in enumerate(LAYER)}
+    launch_bytes = [sum(gemm_alg_bytes(LAYER[i][1], LAYER[i][2], T) for i in idx) for _, idx in LAUNCHES]
+    per_shape = {name: {"GBps": round(b / (launch_ms[j] * 1e-3) / 1e9, 1),
+                        "us": round(launch_ms[j] * 1e3, 2)}
+                 for j, ((name, _), b) in enumerate(zip(LAUNCHES, launch_bytes))}
     traffic = load_traffic()
     result = {
         "metric": "MX-FP4 verify-GEMM HBM GB/s (% of peak) at T=5; spec_accept positions/s",
@@ -270,9 +380,9 @@ def main():
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "gemm_kernel_GBps_by_shape": per_shape,
-        "spec_accept_positions_per_s": round((KD + 1) / (acc_ms.mean() * 1e-3), 1),
-        "spec_accept_us": round(acc_ms.mean() * 1e3, 2),
+        "gemm_launches": per_shape,
+        "spec_accept_positions_per_s": round((KD + 1) / (acc_ms_mean * 1e-3), 1),
+        "spec_accept_us": round(acc_ms_mean * 1e3, 2),
         "numerics": "E2M1 weights decoded exactly to bf16, bf16 x bf16 products summed in fp32 (MFMA); "
                     "spec_accept probabilities in fp64",
         "roofline": {
@@ -286,6 +396,8 @@ def main():
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
             "avg_launch_alg_bytes": avg_launch_bytes,
             "launches_timed": int(launches),
+            "timing": "HIP events around graph replays that run one launch type on every pool "
+                      "layer back to back; average over the four launch types of a layer",
         },
     }
     if not args.no_cpu_baseline:

@@ -113,6 +113,31 @@ mxs_status mxfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_
                              void* stream);
 
 /*
+ * mxfp4_verify_gemm_grouped — several independent verify GEMMs with the same k
+ * and m in one launch where possible: Y_i = X_i · Ŵ_iᵀ for i < count, each as
+ * mxfp4_verify_gemm defines it (same numerics, same layouts and alignment).
+ * This is the verification pass over a layer's projections that read the same
+ * input (q, k, v; gate, up) without concatenating their weights [M11 §4, §10].
+ * Groups of up to 8 products share one launch; larger counts use several.
+ *
+ * problems  HOST array of `count` descriptors, read during the call only.
+ * count     1 <= count <= 65536.
+ * k, m      shared by all products: k >= 32, k % 32 == 0; 1 <= m <= 65536.
+ * Returns MXS_ERR_NULL (problems or any pointer in it), MXS_ERR_SHAPE, MXS_ERR_ALIGN;
+ * nothing is enqueued when any descriptor is invalid.
+ */
+typedef struct mxs_gemm_problem {
+  const uint8_t* codes;  /* [n, k/2], 16-byte aligned */
+  const uint8_t* scales; /* [n, k/32] */
+  const uint16_t* x;     /* [m, k] bf16, 16-byte aligned */
+  float* y;              /* [m, n] fp32, 4-byte aligned */
+  int64_t n;             /* output rows of this product, >= 1 */
+} mxs_gemm_problem;
+
+mxs_status mxfp4_verify_gemm_grouped(const mxs_gemm_problem* problems, int32_t count, int64_t k,
+                                     int64_t m, void* stream);
+
+/*
  * spec_accept_workspace_bytes — device workspace spec_accept needs for
  * (b, kd, v). Returns 0 when the sizes are out of range.
  */

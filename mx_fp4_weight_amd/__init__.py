@@ -29,7 +29,13 @@ FLAG_Q_ZERO = 4
 FLAG_RESIDUAL_ZERO = 8
 
 EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_verify_gemm",
-           "spec_accept_workspace_bytes", "spec_accept"]
+           "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept"]
+
+
+class GemmProblem(ctypes.Structure):
+    """mxs_gemm_problem: one product of a grouped verify GEMM."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class MxsError(RuntimeError):
@@ -53,6 +59,8 @@ def _load() -> ctypes.CDLL:
     lib.mxfp4_quantize.restype = ctypes.c_int
     lib.mxfp4_verify_gemm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     lib.mxfp4_verify_gemm.restype = ctypes.c_int
+    lib.mxfp4_verify_gemm_grouped.argtypes = [ctypes.POINTER(GemmProblem), i32, i64, i64, vp]
+    lib.mxfp4_verify_gemm_grouped.restype = ctypes.c_int
     lib.spec_accept_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_accept_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_accept.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
@@ -134,6 +142,36 @@ def mxfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor
     _check(get_lib().mxfp4_verify_gemm(_ptr(codes), _ptr(scales), n, k, _ptr(x), m, _ptr(y),
                                  _stream(stream)), "mxfp4_verify_gemm")
     return y
+
+
+def mxfp4_verify_gemm_grouped(items, ys=None, stream=None):
+    """Several independent verify GEMMs with the same k and m in one launch.
+
+    items: list of (codes [n_i, k/2] uint8, scales [n_i, k/32] uint8, x [m, k] bf16).
+    Returns the list of outputs y_i [m, n_i] fp32 (or fills the given ys).
+    """
+    if not items:
+        raise ValueError("no products")
+    k = items[0][0].shape[1] * 2
+    m = items[0][2].shape[0]
+    arr = (GemmProblem * len(items))()
+    out = []
+    for i, (codes, scales, x) in enumerate(items):
+        _want(codes, torch.uint8, "codes")
+        _want(scales, torch.uint8, "scales")
+        _want(x, torch.bfloat16, "x")
+        n = codes.shape[0]
+        if codes.shape[1] * 2 != k or x.shape != (m, k) or scales.shape != (n, k // 32):
+            raise ValueError("all products must share k and m")
+        y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+        _want(y, torch.float32, "y")
+        if y.shape != (m, n):
+            raise ValueError("y must be [m, n]")
+        arr[i] = GemmProblem(codes.data_ptr(), scales.data_ptr(), x.data_ptr(), y.data_ptr(), n)
+        out.append(y)
+    _check(get_lib().mxfp4_verify_gemm_grouped(arr, len(items), k, m, _stream(stream)),
+           "mxfp4_verify_gemm_grouped")
+    return out
 
 
 def spec_accept_workspace_bytes(b: int, kd: int, v: int) -> int:

@@ -12,13 +12,16 @@
 //           and draft row, the chunk max (exact, fp32) and sum exp(z - max)
 //           in fp64. This is the one full read of the logits.
 //   decide  grid (chunks, sequences): every workgroup combines its sequence's
-//           chunk statistics into (max, sum) per row, gathers p_i(x_i) and
-//           q_i(x_i) in fp64 (one lane per draft position), takes n = first
-//           rejection with a ballot, then sums the final weights w (residual
-//           or bonus row) over its own chunk. Chunk 0 writes the decisions.
-//   sample  one workgroup per sequence: inclusive scan of the chunk totals,
-//           first chunk whose running total exceeds u_K·Z, then a block scan
-//           inside that chunk and a per-thread scan to the token.
+//           chunk statistics into (max, sum) per row, forms p_i(x_i) and
+//           q_i(x_i) in fp64 from the logits the stats kernel gathered (one
+//           lane per draft position), takes n = first rejection with a
+//           ballot, then sums the final weights w (residual or bonus row)
+//           over its own chunk, keeping every thread's total. Chunk 0 writes
+//           the decisions.
+//   sample  one workgroup per sequence: a block scan of the chunk totals
+//           finds the chunk holding u_K·Z, a block scan of that chunk's stored
+//           thread totals finds the thread, and that thread recomputes its 4
+//           tokens' weights to find t*.
 // All probabilities and prefix sums are fp64; the result can differ from an
 // exact-arithmetic draw only when u_K·Z lies within ~1e-15·Z of an interval
 // end. Rounding guards: if no crossing is found where the level above
@@ -35,10 +38,15 @@
 namespace mxs {
 namespace {
 
+// stats: 256 threads x 16 logits; decide/sample: 1024 threads x 4 logits. Both
+// cover the same 4096-logit chunk, so the chunk totals of the final weights
+// written by decide are the ones sample walks.
 constexpr int kThreads = 256;
 constexpr int kPer = 16;
 constexpr int kChunk = kThreads * kPer;  // 4096 logits per chunk
-constexpr int kMaxRows = 65;             // 2 * 32 + 1 rows per sequence
+constexpr int kWThreads = 1024;
+constexpr int kWPer = kChunk / kWThreads;  // 4 logits per thread in decide / sample
+constexpr int kMaxRows = 65;               // 2 * 32 + 1 rows per sequence
 
 struct Decision {
   int32_t n;      // accepted drafts, or -1 for a refused sequence
@@ -51,15 +59,18 @@ struct Workspace {
   float* cmax;     // [rows][chunks]
   double* csum;    // [rows][chunks]
   int32_t* cbad;   // [rows][chunks]
-  Decision* dec;   // [b]
+  float* gz;       // [rows] logit of the row's draft token (written by the chunk holding it)
+  struct Decision* dec;  // [b] n and the statistics of the final draw's rows
   double* zres;    // [b][chunks] chunk totals of the final weights
   double* zp;      // [b][chunks] chunk totals of p_n (zero-residual fallback)
+  double* tauf;    // [b][chunks][kWThreads] per-thread totals of the final weights
+  double* taup;    // [b][chunks][kWThreads] per-thread totals of p_n
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t cmax, csum, cbad, dec, zres, zp, total;
+  size_t cmax, csum, cbad, gz, dec, zres, zp, tauf, taup, total;
 };
 
 inline Layout layout(int64_t b, int64_t kd, int64_t v) {
@@ -73,12 +84,18 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v) {
   off = align256(off + sizeof(double) * rows * chunks);
   L.cbad = off;
   off = align256(off + sizeof(int32_t) * rows * chunks);
+  L.gz = off;
+  off = align256(off + sizeof(float) * rows);
   L.dec = off;
   off = align256(off + sizeof(Decision) * b);
   L.zres = off;
   off = align256(off + sizeof(double) * b * chunks);
   L.zp = off;
   off = align256(off + sizeof(double) * b * chunks);
+  L.tauf = off;
+  off = align256(off + sizeof(double) * b * chunks * kWThreads);
+  L.taup = off;
+  off = align256(off + sizeof(double) * b * chunks * kWThreads);
   L.total = off;
   return L;
 }
@@ -93,7 +110,8 @@ __device__ inline const float* row_ptr(const float* target, const float* draft, 
 // ---------------------------------------------------------------- stats
 template <bool kVec4>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict__ target,
-                                                         const float* __restrict__ draft, int kd,
+                                                         const float* __restrict__ draft,
+                                                         const int32_t* __restrict__ tokens, int kd,
                                                          int v, int chunks, Workspace ws) {
   __shared__ double lds_d[kThreads / kWave];
   __shared__ float lds_f[kThreads / kWave];
@@ -125,12 +143,19 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
       vals[q] = e < v ? z[e] : -INFINITY;
     }
   }
+  // the logit of this row's draft token x (target row i < kd or draft row i), if it is in this chunk
+  int xi = -1;
+  if (j < kd) xi = tokens[(size_t)s * kd + j];
+  else if (j > kd) xi = tokens[(size_t)s * kd + (j - kd - 1)];
   float mx = -INFINITY;
   int bad = 0;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     bad |= (vals[q] != vals[q]) | (vals[q] == INFINITY);
     mx = fmaxf(mx, vals[q]);
+    const int e = kVec4 ? base + 4 * (threadIdx.x + kThreads * (q / 4)) + (q % 4)
+                        : base + threadIdx.x + kThreads * q;
+    if (e == xi) ws.gz[rowg] = vals[q];
   }
   mx = block_max<kThreads>(mx, lds_f);
   bad = block_or<kThreads>(bad, lds_i);
@@ -156,28 +181,191 @@ struct FinalRows {
   double mt, inv_st, md, inv_sd;
 };
 
-__device__ inline void weights_at(const FinalRows& fr, int t, double& w_final, double& w_p) {
-  const double p = exp_neg_f64((double)fr.zt[t] - fr.mt) * fr.inv_st;
-  w_p = p;
-  if (fr.zd) {
-    const double q = exp_neg_f64((double)fr.zd[t] - fr.md) * fr.inv_sd;
-    const double d = p - q;
-    w_final = d > 0.0 ? d : 0.0;
-  } else {
-    w_final = p;
+// Final weights and p_n of kWPer consecutive tokens from their logits zt, zd.
+__device__ inline void weights_from(const FinalRows& fr, const float (&zt)[kWPer],
+                                    const float (&zd)[kWPer], double (&wf)[kWPer],
+                                    double (&wp)[kWPer]) {
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) {
+    const double p = exp_neg_f64((double)zt[j] - fr.mt) * fr.inv_st;
+    wp[j] = p;
+    if (fr.zd) {
+      const double q = exp_neg_f64((double)zd[j] - fr.md) * fr.inv_sd;
+      const double d = p - q;
+      wf[j] = d > 0.0 ? d : 0.0;
+    } else {
+      wf[j] = p;
+    }
   }
 }
 
+// Final weights and p_n of the kWPer consecutive tokens t0 .. t0+kWPer-1 (zero past v).
+// Both rows are loaded before any arithmetic (one 16-byte load each when aligned).
+__device__ inline void thread_weights(const FinalRows& fr, int t0, int v, bool vec4,
+                                      double (&wf)[kWPer], double (&wp)[kWPer]) {
+  float zt[kWPer], zd[kWPer];
+  if (vec4 && t0 + kWPer <= v) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(fr.zt + t0);
+    f32x4 b = a;
+    if (fr.zd) b = *reinterpret_cast<const f32x4*>(fr.zd + t0);
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      zt[j] = a[j];
+      zd[j] = b[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      const bool in = t0 + j < v;
+      zt[j] = in ? fr.zt[t0 + j] : -INFINITY;
+      zd[j] = (in && fr.zd) ? fr.zd[t0 + j] : -INFINITY;
+    }
+  }
+  weights_from(fr, zt, zd, wf, wp);
+}
+
+// ---------------------------------------------------------------- final draw
+constexpr int kNone = 0x7fffffff;
+
+// The final token of sequence s by inverse CDF over the chunk totals and the
+// per-thread totals written by the decide workgroups of the sequence.
+__device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int chunks, int64_t s,
+                           const Workspace& ws, const float* __restrict__ uniforms,
+                           int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4,
+                           double* lds_scan, double* s_incl, int& s_first, int& s_last) {
+  const int tid = threadIdx.x;
+  // ---- level 1: chunks. Running totals of the chunk totals; Z is the last one.
+  bool use_p = false;
+  double Z = 0.0, base = 0.0;
+  int c = kNone;
+  bool found = false;
+  if (tid == 0) {
+    s_first = kNone;
+    s_last = -1;
+  }
+  if (chunks <= kWThreads) {
+    // one chunk per thread: both totals loaded once, one scan (two on the zero-residual path)
+    const double zres = tid < chunks ? ws.zres[s * chunks + tid] : 0.0;
+    const double zpv = tid < chunks ? ws.zp[s * chunks + tid] : 0.0;
+    double incl = block_inclusive_scan_f64<kWThreads>(zres, lds_scan);
+    if (tid == kWThreads - 1) s_incl[0] = incl;
+    __syncthreads();
+    Z = s_incl[0];
+    double zc = zres;
+    __syncthreads();
+    if (!(Z > 0.0)) {  // zero residual mass (rounding): draw from p_n instead
+      use_p = true;
+      zc = zpv;
+      incl = block_inclusive_scan_f64<kWThreads>(zpv, lds_scan);
+      if (tid == kWThreads - 1) s_incl[0] = incl;
+      __syncthreads();
+      Z = s_incl[0];
+      __syncthreads();
+      if (n < kd && tid == 0) raise_flag(flags, MXS_FLAG_RESIDUAL_ZERO);
+    }
+    const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
+    s_incl[tid] = incl;
+    if (tid < chunks && zc > 0.0) {
+      if (uz < incl) atomicMin(&s_first, tid);
+      atomicMax(&s_last, tid);
+    }
+    __syncthreads();
+    c = s_first;
+    found = c != kNone;
+    if (found) base = c > 0 ? s_incl[c - 1] : 0.0;
+  } else {
+    // many chunks: rounds of kWThreads chunk totals with a carry
+    const double* zr = ws.zres + s * chunks;
+    for (int pass = 0; pass < 2; ++pass) {
+      double carry = 0.0;
+      for (int c0 = 0; c0 < chunks; c0 += kWThreads) {
+        const int cc = c0 + tid;
+        const double incl =
+            carry + block_inclusive_scan_f64<kWThreads>(cc < chunks ? zr[cc] : 0.0, lds_scan);
+        if (tid == kWThreads - 1) s_incl[0] = incl;
+        __syncthreads();
+        carry = s_incl[0];
+        __syncthreads();
+      }
+      Z = carry;
+      if (Z > 0.0 || pass == 1) break;
+      use_p = true;
+      zr = ws.zp + s * chunks;
+      if (n < kd && tid == 0) raise_flag(flags, MXS_FLAG_RESIDUAL_ZERO);
+    }
+    const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
+    double carry = 0.0;
+    for (int c0 = 0; c0 < chunks; c0 += kWThreads) {
+      const int cc = c0 + tid;
+      const double zc = cc < chunks ? zr[cc] : 0.0;
+      const double incl = carry + block_inclusive_scan_f64<kWThreads>(zc, lds_scan);
+      s_incl[tid] = incl;
+      if (cc < chunks && zc > 0.0) {
+        if (uz < incl) atomicMin(&s_first, cc);
+        atomicMax(&s_last, cc);
+      }
+      __syncthreads();
+      c = s_first;
+      if (c != kNone) {
+        base = c > c0 ? s_incl[c - c0 - 1] : carry;
+        break;
+      }
+      carry = s_incl[kWThreads - 1];
+      __syncthreads();
+    }
+    found = c != kNone;
+  }
+  const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
+  if (!found) c = s_last;  // no crossing (u >= 1 or rounding): last chunk with positive weight
+  if (c < 0) return;       // a valid row always has positive mass
+  __syncthreads();
+
+  // ---- level 2: threads of chunk c, from the thread totals its decide workgroup
+  // stored (same values, same scan, so the running totals match its chunk total)
+  const size_t tslot = ((size_t)s * chunks + c) * kWThreads + tid;
+  const double tau = use_p ? ws.taup[tslot] : ws.tauf[tslot];
+  const double sincl = block_inclusive_scan_f64<kWThreads>(tau, lds_scan);
+  s_incl[tid] = sincl;
+  if (tid == 0) {
+    s_first = kNone;
+    s_last = -1;
+  }
+  __syncthreads();
+  if (tau > 0.0) {
+    if (found && uz < base + sincl) atomicMin(&s_first, tid);
+    atomicMax(&s_last, tid);
+  }
+  __syncthreads();
+  // the crossing thread, or (fallback chunk / rounding) the last thread with positive weight
+  const int ti = s_first != kNone ? s_first : s_last;
+  if (tid != ti) return;
+  // ---- level 3: the 4 tokens of thread ti
+  const int t0 = c * kChunk + ti * kWPer;
+  double wf[kWPer], wp[kWPer];
+  thread_weights(fr, t0, v, vec4, wf, wp);
+  const double before = base + (ti > 0 ? s_incl[ti - 1] : 0.0);
+  double run = 0.0;
+  int pick = -1, lastpos = -1;
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) {
+    const double w = use_p ? wp[j] : wf[j];
+    run += w;
+    if (w > 0.0) lastpos = t0 + j;
+    if (found && pick < 0 && w > 0.0 && uz < before + run) pick = t0 + j;
+  }
+  out_tokens[(size_t)s * (kd + 1) + n] = pick >= 0 ? pick : lastpos;
+}
+
 // ---------------------------------------------------------------- decide + chunk totals
-__global__ __launch_bounds__(kThreads) void decide_kernel(
+__global__ __launch_bounds__(kWThreads) void decide_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
     int chunks, Workspace ws, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num,
-    int32_t* __restrict__ flags) {
+    int32_t* __restrict__ flags, int vec4) {
   __shared__ double smax[kMaxRows];
   __shared__ double ssum[kMaxRows];
   __shared__ int sbad[kMaxRows];
-  __shared__ double lds_d[kThreads / kWave];
+  __shared__ double lds_d[kWThreads / kWave];
   __shared__ int s_n;
   const int c = blockIdx.x;
   const int64_t s = blockIdx.y;
@@ -185,35 +373,84 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   const int wave = threadIdx.x / kWave;
   const int per_seq = 2 * kd + 1;
 
-  // 1. per-row max and sum over the chunk statistics: one wave per row
-  for (int j = wave; j < per_seq; j += kThreads / kWave) {
-    const size_t o = ((size_t)s * per_seq + j) * chunks;
-    float m = -INFINITY;
-    int bad = 0;
-    for (int cc = lane; cc < chunks; cc += kWave) {
-      m = fmaxf(m, ws.cmax[o + cc]);
-      bad |= ws.cbad[o + cc];
-    }
+  // For K <= 4 every candidate final row's 4 logits of this thread are fetched
+  // now, together with the statistics, so step 3 needs no further memory trip.
+  constexpr int kPre = 9;
+  const int t0w = c * kChunk + threadIdx.x * kWPer;
+  const bool pre = vec4 && kd <= 4 && t0w + kWPer <= v;
+  f32x4 prow[kPre];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+  for (int r = 0; r < kPre; ++r) {
+    prow[r] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (pre && r < per_seq) prow[r] = *reinterpret_cast<const f32x4*>(row_ptr(target, draft, s, kd, r, v) + t0w);
+  }
+
+  // inputs of the decisions, loaded together with the chunk statistics below
+  int32_t x = -1;
+  float ui = 0.f, gzt = 0.f, gzd = 0.f;
+  if (wave == 0 && lane < kd) {
+    x = tokens[(size_t)s * kd + lane];
+    ui = uniforms[(size_t)s * (kd + 1) + lane];
+    gzt = ws.gz[(size_t)s * per_seq + lane];
+    gzd = ws.gz[(size_t)s * per_seq + kd + 1 + lane];
+  }
+
+  // 1. per-row max and sum over the chunk statistics. With seg = chunks rounded up
+  //    to a power of two (<= 64), thread j*seg + c loads chunk c of row j and the
+  //    row is reduced by xor-shuffles inside its segment: one round for all rows.
+  int seg = 1;
+  while (seg < chunks) seg <<= 1;
+  if (seg <= kWave && per_seq * seg <= kWThreads) {
+    const int j = threadIdx.x / seg;
+    const int cc = threadIdx.x % seg;
+    const bool live = j < per_seq && cc < chunks;
+    const size_t o = ((size_t)s * per_seq + (live ? j : 0)) * chunks + (live ? cc : 0);
+    float cm = live ? ws.cmax[o] : -INFINITY;
+    double cs = live ? ws.csum[o] : 0.0;
+    int bad = live ? ws.cbad[o] : 0;
+    float m = cm;
+    for (int off = 1; off < seg; off <<= 1) {
       m = fmaxf(m, __shfl_xor(m, off));
       bad |= __shfl_xor(bad, off);
     }
     bad |= (m == -INFINITY);
-    double sum = 0.0;
-    if (!bad) {
-      const double m64 = (double)m;
-      for (int cc = lane; cc < chunks; cc += kWave) {
-        const double cs = ws.csum[o + cc];
-        if (cs > 0.0) sum += cs * exp_neg_f64((double)ws.cmax[o + cc] - m64);
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if (lane == 0) {
+    double sum = (!bad && cs > 0.0) ? cs * exp_neg_f64((double)cm - (double)m) : 0.0;
+    for (int off = 1; off < seg; off <<= 1) sum += __shfl_xor(sum, off);
+    if (j < per_seq && cc == 0) {
       smax[j] = (double)m;
       ssum[j] = sum;
       sbad[j] = bad;
+    }
+  } else {
+    for (int j = wave; j < per_seq; j += kWThreads / kWave) {
+      const size_t o = ((size_t)s * per_seq + j) * chunks;
+      float m = -INFINITY;
+      int bad = 0;
+      for (int cc = lane; cc < chunks; cc += kWave) {
+        m = fmaxf(m, ws.cmax[o + cc]);
+        bad |= ws.cbad[o + cc];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, off));
+        bad |= __shfl_xor(bad, off);
+      }
+      bad |= (m == -INFINITY);
+      double sum = 0.0;
+      if (!bad) {
+        const double m64 = (double)m;
+        for (int cc = lane; cc < chunks; cc += kWave) {
+          const double cs = ws.csum[o + cc];
+          if (cs > 0.0) sum += cs * exp_neg_f64((double)ws.cmax[o + cc] - m64);
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      if (lane == 0) {
+        smax[j] = (double)m;
+        ssum[j] = sum;
+        sbad[j] = bad;
+      }
     }
   }
   __syncthreads();
@@ -225,17 +462,14 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     bad = __any(bad);
     int f = 0;
     bool acc = true;
-    int32_t x = -1;
     if (!bad && lane < kd) {
-      x = tokens[(size_t)s * kd + lane];
       double a = 0.0;
       if (x < 0 || x >= v) {
         f |= MXS_FLAG_TOKEN_RANGE;
       } else {
-        const float zt = row_ptr(target, draft, s, kd, lane, v)[x];
-        const float zd = row_ptr(target, draft, s, kd, kd + 1 + lane, v)[x];
-        const double q = exp_neg_f64((double)zd - smax[kd + 1 + lane]) / ssum[kd + 1 + lane];
-        const double p = exp_neg_f64((double)zt - smax[lane]) / ssum[lane];
+        // the draft token's logits were gathered by the stats kernel
+        const double q = exp_neg_f64((double)gzd - smax[kd + 1 + lane]) / ssum[kd + 1 + lane];
+        const double p = exp_neg_f64((double)gzt - smax[lane]) / ssum[lane];
         if (q == 0.0) {
           f |= MXS_FLAG_Q_ZERO;
         } else {
@@ -243,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
           a = a < 1.0 ? a : 1.0;
         }
       }
-      acc = (double)uniforms[(size_t)s * (kd + 1) + lane] < a;
+      acc = (double)ui < a;
     }
     const unsigned long long rej = __ballot(!acc);  // lanes >= kd vote "accept"
     const int n = bad ? -1 : (rej ? __ffsll(rej) - 1 : kd);
@@ -280,149 +514,70 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   // the same block scan the sample kernel uses, so both see identical totals
   const int n = s_n;
   double a = 0.0, b = 0.0;
+  FinalRows fr;
   if (n >= 0) {
-    FinalRows fr;
     fr.zt = row_ptr(target, draft, s, kd, n, v);
     fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
     fr.mt = smax[n];
     fr.inv_st = 1.0 / ssum[n];
     fr.md = n < kd ? smax[kd + 1 + n] : 0.0;
     fr.inv_sd = n < kd ? 1.0 / ssum[kd + 1 + n] : 0.0;
-    const int t0 = c * kChunk + threadIdx.x * kPer;
-    for (int j = 0; j < kPer; ++j) {
-      const int t = t0 + j;
-      if (t < v) {
-        double wf, wp;
-        weights_at(fr, t, wf, wp);
-        a += wf;
-        b += wp;
+    double wf[kWPer], wp[kWPer];
+    if (pre) {
+      float zt[kWPer], zd[kWPer];
+      f32x4 at = prow[0], ad = prow[0];
+#pragma unroll
+      for (int r = 0; r < kPre; ++r) {  // select without indexing registers dynamically
+        if (r == n) at = prow[r];
+        if (r == kd + 1 + n) ad = prow[r];
       }
+#pragma unroll
+      for (int j = 0; j < kWPer; ++j) {
+        zt[j] = at[j];
+        zd[j] = ad[j];
+      }
+      weights_from(fr, zt, zd, wf, wp);
+    } else {
+      thread_weights(fr, t0w, v, vec4, wf, wp);
+    }
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      a += wf[j];
+      b += wp[j];
     }
   }
-  a = block_inclusive_scan_f64<kThreads>(a, lds_d);
-  b = block_inclusive_scan_f64<kThreads>(b, lds_d);
-  if (threadIdx.x == kThreads - 1) {
+  // thread totals kept for the final draw, which re-scans them instead of the tokens
+  const size_t tslot = ((size_t)s * chunks + c) * kWThreads + threadIdx.x;
+  ws.tauf[tslot] = a;
+  ws.taup[tslot] = b;
+  a = block_inclusive_scan_f64<kWThreads>(a, lds_d);
+  b = block_inclusive_scan_f64<kWThreads>(b, lds_d);
+  if (threadIdx.x == kWThreads - 1) {
     ws.zres[s * chunks + c] = a;
     ws.zp[s * chunks + c] = b;
   }
 }
 
 // ---------------------------------------------------------------- sample
-constexpr int kNone = 0x7fffffff;
-
-__global__ __launch_bounds__(kThreads) void sample_kernel(
+__global__ __launch_bounds__(kWThreads) void sample_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const float* __restrict__ uniforms, int kd, int v, int chunks, Workspace ws,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags) {
-  __shared__ double lds_scan[kThreads / kWave];
-  __shared__ double s_incl[kThreads];
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4) {
+  __shared__ double lds_scan[kWThreads / kWave];
+  __shared__ double s_incl[kWThreads];
   __shared__ int s_first, s_last;
   const int64_t s = blockIdx.x;
   const Decision d = ws.dec[s];
-  const int n = d.n;
-  if (n < 0) return;
+  if (d.n < 0) return;
   FinalRows fr;
-  fr.zt = row_ptr(target, draft, s, kd, n, v);
-  fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
+  fr.zt = row_ptr(target, draft, s, kd, d.n, v);
+  fr.zd = d.n < kd ? row_ptr(target, draft, s, kd, kd + 1 + d.n, v) : nullptr;
   fr.mt = d.mt;
   fr.inv_st = d.inv_st;
   fr.md = d.md;
   fr.inv_sd = d.inv_sd;
-  const int tid = threadIdx.x;
-
-  // ---- level 1: chunks. Z = running total over rounds of 256 chunk totals.
-  const double* zr = ws.zres + s * chunks;
-  bool use_p = false;
-  double Z = 0.0;
-  for (int pass = 0; pass < 2; ++pass) {
-    double carry = 0.0;
-    for (int c0 = 0; c0 < chunks; c0 += kThreads) {
-      const int cc = c0 + tid;
-      const double incl = carry + block_inclusive_scan_f64<kThreads>(cc < chunks ? zr[cc] : 0.0, lds_scan);
-      if (tid == kThreads - 1) s_incl[0] = incl;
-      __syncthreads();
-      carry = s_incl[0];
-      __syncthreads();
-    }
-    Z = carry;
-    if (Z > 0.0 || pass == 1) break;
-    // zero residual mass (rounding): draw from p_n instead
-    use_p = true;
-    zr = ws.zp + s * chunks;
-    if (n < kd && tid == 0) raise_flag(flags, MXS_FLAG_RESIDUAL_ZERO);
-  }
-  const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
-
-  // first positive chunk whose running total exceeds u·Z, and the total before it
-  if (tid == 0) {
-    s_first = kNone;
-    s_last = -1;
-  }
-  __syncthreads();
-  double carry = 0.0, base = 0.0;
-  int c = kNone;
-  for (int c0 = 0; c0 < chunks; c0 += kThreads) {
-    const int cc = c0 + tid;
-    const double zc = cc < chunks ? zr[cc] : 0.0;
-    const double incl = carry + block_inclusive_scan_f64<kThreads>(zc, lds_scan);
-    s_incl[tid] = incl;
-    if (cc < chunks && zc > 0.0) {
-      if (uz < incl) atomicMin(&s_first, cc);
-      atomicMax(&s_last, cc);
-    }
-    __syncthreads();
-    c = s_first;
-    if (c != kNone) {
-      base = c > c0 ? s_incl[c - c0 - 1] : carry;
-      break;
-    }
-    carry = s_incl[kThreads - 1];
-    __syncthreads();
-  }
-  const bool found = c != kNone;
-  if (!found) c = s_last;  // no crossing (u >= 1 or rounding): last chunk with positive weight
-  if (c < 0) return;       // a valid row always has positive mass
-  __syncthreads();
-
-  // ---- level 2: threads of chunk c (same thread totals and scan as the decide kernel)
-  const int t0 = c * kChunk + tid * kPer;
-  double wl[kPer];
-  double tau = 0.0;
-  int lastpos = -1;
-  for (int j = 0; j < kPer; ++j) {
-    const int t = t0 + j;
-    double wf = 0.0, wp = 0.0;
-    if (t < v) weights_at(fr, t, wf, wp);
-    wl[j] = use_p ? wp : wf;
-    tau += wl[j];
-    if (wl[j] > 0.0) lastpos = t;
-  }
-  const double sincl = block_inclusive_scan_f64<kThreads>(tau, lds_scan);
-  s_incl[tid] = sincl;
-  if (tid == 0) {
-    s_first = kNone;
-    s_last = -1;
-  }
-  __syncthreads();
-  if (found && tau > 0.0 && uz < base + sincl) atomicMin(&s_first, tid);
-  if (lastpos >= 0) atomicMax(&s_last, lastpos);
-  __syncthreads();
-  int32_t* out = out_tokens + (size_t)s * (kd + 1) + n;
-  const int ti = s_first;
-  if (ti == kNone) {  // fallback chunk, or rounding: last positive token of the chunk
-    if (tid == 0) *out = s_last;
-    return;
-  }
-  if (tid != ti) return;
-  // ---- level 3: tokens of thread ti
-  const double before = base + (ti > 0 ? s_incl[ti - 1] : 0.0);
-  double run = 0.0;
-  int pick = -1;
-  for (int j = 0; j < kPer; ++j) {
-    run += wl[j];
-    if (pick < 0 && wl[j] > 0.0 && uz < before + run) pick = t0 + j;
-  }
-  *out = pick >= 0 ? pick : lastpos;
+  draw_final(fr, d.n, kd, v, chunks, s, ws, uniforms, out_tokens, flags, vec4, lds_scan, s_incl,
+             s_first, s_last);
 }
 
 }  // namespace
@@ -440,23 +595,26 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
   ws.cmax = reinterpret_cast<float*>(base + L.cmax);
   ws.csum = reinterpret_cast<double*>(base + L.csum);
   ws.cbad = reinterpret_cast<int32_t*>(base + L.cbad);
+  ws.gz = reinterpret_cast<float*>(base + L.gz);
   ws.dec = reinterpret_cast<Decision*>(base + L.dec);
   ws.zres = reinterpret_cast<double*>(base + L.zres);
   ws.zp = reinterpret_cast<double*>(base + L.zp);
+  ws.tauf = reinterpret_cast<double*>(base + L.tauf);
+  ws.taup = reinterpret_cast<double*>(base + L.taup);
   const int64_t rows = (int64_t)b * (2 * kd + 1);
   dim3 g1((unsigned)rows, (unsigned)chunks);
   if (vec4)
-    stats_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, ws);
+    stats_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws);
   else
-    stats_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, ws);
+    stats_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decide_kernel<<<dim3((unsigned)chunks, (unsigned)b), dim3(kThreads), 0, stream>>>(
-      target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags);
+  decide_kernel<<<dim3((unsigned)chunks, (unsigned)b), dim3(kWThreads), 0, stream>>>(
+      target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  sample_kernel<<<dim3((unsigned)b), dim3(kThreads), 0, stream>>>(target, draft, uniforms, kd, v,
-                                                                  chunks, ws, out_tokens, flags);
+  sample_kernel<<<dim3((unsigned)b), dim3(kWThreads), 0, stream>>>(target, draft, uniforms, kd, v,
+                                                                   chunks, ws, out_tokens, flags, vec4);
   return hipGetLastError();
 }
 

@@ -97,12 +97,41 @@ struct Block {
   u32x4 s[R][G / 4];    // 16 scale bytes = 4 groups x 4 blocks of the row
 };
 
+// Up to kMaxGroup independent products with the same k and m share one launch
+// (the projections of one layer that read the same input, or any independent
+// set): the persistent grid is split between them in proportion to their row
+// blocks, so a workgroup stages one problem's activations once.
+constexpr int kMaxGroup = 8;
+
+struct Problem {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint16_t* x;
+  float* y;
+  int n, nrb, y_vec4, pad;
+};
+
+struct Group {
+  Problem p[kMaxGroup];
+  int wg_start[kMaxGroup + 1];  // workgroups [wg_start[i], wg_start[i+1]) serve problem i
+  int count;
+};
+
 template <int R, int G>
-__global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m, int nrb, int nsub,
-    int y_vec4) {
+__global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
+                                                                         int nsub) {
   extern __shared__ u32x4 smem[];
+  int pi = 0;
+  while (pi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[pi + 1]) ++pi;
+  const uint8_t* __restrict__ codes = grp.p[pi].codes;
+  const uint8_t* __restrict__ scales = grp.p[pi].scales;
+  const uint16_t* __restrict__ x = grp.p[pi].x;
+  float* __restrict__ y = grp.p[pi].y;
+  const int n = grp.p[pi].n;
+  const int nrb = grp.p[pi].nrb;
+  const int y_vec4 = grp.p[pi].y_vec4;
+  const int wg = (int)blockIdx.x - grp.wg_start[pi];               // index among this problem's
+  const int ngrid = grp.wg_start[pi + 1] - grp.wg_start[pi];        // workgroups
   const int W = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -120,11 +149,11 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
   f32x4* red = reinterpret_cast<f32x4*>(smem + xunits);  // [2][W][R][64]
 
   // this workgroup's work: its row blocks times the nsub sub-slices of G groups
-  const int my_blocks = blockIdx.x < nrb ? (nrb - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int my_blocks = wg < nrb ? (nrb - 1 - wg) / ngrid + 1 : 0;
   const int nunits = my_blocks * nsub;
 
   auto load = [&](int u, Block<R, G>& b) {
-    const int rb = (int)blockIdx.x + (u / nsub) * (int)gridDim.x;
+    const int rb = wg + (u / nsub) * ngrid;
     const int g0 = gs + (u % nsub) * G;
     // descriptors covering the valid rows of row block rb (none past the last unit)
     const int row0 = rb * 16 * R;
@@ -184,7 +213,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
     }
     if (u % nsub != nsub - 1) return;
     // last sub-slice of the row block: sum the waves' partial tiles and store
-    const int rb = (int)blockIdx.x + (u / nsub) * (int)gridDim.x;
+    const int rb = wg + (u / nsub) * ngrid;
     f32x4* rp = red + (size_t)parity * W * R * kWave;
 #pragma unroll
     for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = acc[i];
@@ -211,7 +240,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
     parity ^= 1;
   };
 
-  // activations first (L2-resident, short latency), then the first unit's codes
+  // the first unit's codes go out before the activation staging, so the HBM and
+  // L2 round trips overlap
+  Block<R, G> A, B;
+  load(0, A);
   const int nq = k >> 3;  // 16-byte chunks per activation row
   for (int idx = threadIdx.x; idx < mt * nq; idx += blockDim.x) {
     const int tt = idx / nq;
@@ -219,8 +251,6 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(
     smem[xunit(q >> 4, q & 3, tt, (q >> 2) & 3, mt)] =
         *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * (size_t)k + (size_t)q * 8);
   }
-  Block<R, G> A, B;
-  load(0, A);
   lds_barrier();
   for (int u = 0; u < nunits;) {
     load(u + 1, B);  // past the last unit: a zero-record descriptor, nothing is read
@@ -398,8 +428,8 @@ inline size_t main_lds(int64_t k, int64_t m, int R, int G) {
 }
 
 template <int R, int G>
-hipError_t launch_main(const Config& c, const uint8_t* codes, const uint8_t* scales, int64_t n,
-                       int64_t k, const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+hipError_t launch_main(const Config& c, const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                       hipStream_t stream) {
   static std::atomic<bool> done[kMaxDevices];
   hipError_t e = allow_lds(&gemm_skinny_kernel<R, G>, done);
   if (e != hipSuccess) return e;
@@ -407,12 +437,25 @@ hipError_t launch_main(const Config& c, const uint8_t* codes, const uint8_t* sca
   int waves, nsub;
   split_k(ngroups, G, waves, nsub);
   const size_t lds = main_lds(k, m, R, G);
-  const int64_t nrb = (n + 16 * R - 1) / (16 * R);
-  int64_t grid = (int64_t)kCUs * c.per_cu;
-  if (grid > nrb) grid = nrb;
-  gemm_skinny_kernel<R, G><<<dim3((unsigned)grid, (unsigned)((m + 15) / 16)), dim3(waves * kWave), lds,
-                             stream>>>(codes, scales, x, y, (int)n, (int)k, (int)m, (int)nrb, nsub,
-                                       y_vec4_ok(y, n));
+  Group grp{};
+  grp.count = count;
+  int64_t total_rb = 0;
+  for (int i = 0; i < count; ++i) total_rb += (pv[i].n + 16 * R - 1) / (16 * R);
+  int64_t budget = (int64_t)kCUs * c.per_cu;
+  int start = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t nrb = (pv[i].n + 16 * R - 1) / (16 * R);
+    int64_t share = (budget * nrb + total_rb - 1) / total_rb;  // proportional, at least 1
+    if (share > nrb) share = nrb;
+    if (share < 1) share = 1;
+    grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, (int)pv[i].n, (int)nrb,
+                       y_vec4_ok(pv[i].y, pv[i].n), 0};
+    grp.wg_start[i] = start;
+    start += (int)share;
+  }
+  grp.wg_start[count] = start;
+  gemm_skinny_kernel<R, G><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(waves * kWave), lds,
+                             stream>>>(grp, (int)k, (int)m, nsub);
   return hipGetLastError();
 }
 
@@ -432,27 +475,43 @@ hipError_t launch_xglobal(int gpw, const uint8_t* codes, const uint8_t* scales, 
   return hipGetLastError();
 }
 
-hipError_t launch_cfg(Config c, const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
-                      const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+// One launch for up to kMaxGroup problems with the same k and m (persistent kernel), or
+// one fallback launch per problem.
+hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                        hipStream_t stream) {
   // Main kernel: 16-byte scale loads need k % 512 == 0 and 16-byte aligned scales; a row
   // block's bytes (64 rows at most) must fit a 32-bit buffer range; X must fit in LDS.
-  const bool aligned = (k % 512 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 15) == 0);
-  if (aligned && k <= (int64_t(1) << 24) && main_lds(k, m, c.R, c.G) <= kMaxLds) {
+  bool aligned = (k % 512 == 0) && k <= (int64_t(1) << 24) && main_lds(k, m, c.R, c.G) <= kMaxLds;
+  for (int i = 0; i < count; ++i)
+    aligned = aligned && ((reinterpret_cast<uintptr_t>(pv[i].scales) & 15) == 0);
+  if (aligned) {
 #define MXS_RG(RR, GG) \
-  if (c.R == RR && c.G == GG) return launch_main<RR, GG>(c, codes, scales, n, k, x, m, y, stream);
+  if (c.R == RR && c.G == GG) return launch_main<RR, GG>(c, pv, count, k, m, stream);
     MXS_RG(1, 4) MXS_RG(1, 8) MXS_RG(2, 4) MXS_RG(2, 8) MXS_RG(4, 4)
 #undef MXS_RG
     return hipErrorInvalidValue;
   }
-  return launch_xglobal<2, 4>(4, codes, scales, n, k, x, m, y, stream);
+  for (int i = 0; i < count; ++i) {
+    const hipError_t e =
+        launch_xglobal<2, 4>(4, pv[i].codes, pv[i].scales, pv[i].n, k, pv[i].x, m, pv[i].y, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-// Shape-based choice: enough bytes in flight to cover HBM latency on 256 CUs.
+hipError_t launch_cfg(Config c, const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                      const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+  const mxs_problem_view pv{codes, scales, x, y, n};
+  return launch_group(c, &pv, 1, k, m, stream);
+}
+
+// Tile choice from a sweep of (R, G, workgroups per CU) over the 8B- and 70B-class
+// shapes at T = 5: one 16-row tile per row block and 4 groups per sub-slice won or
+// tied everywhere; two resident workgroups per CU for k <= 4096 (LDS allows it), one
+// above.
 Config choose(int64_t n, int64_t k) {
-  Config c{1, 4, 2};
-  if (n >= 16384) c.R = 2;
-  if (k >= 8192) c.G = 8;
-  return c;
+  (void)n;
+  return Config{1, 4, k <= 4096 ? 2 : 1};
 }
 
 }  // namespace
@@ -460,6 +519,18 @@ Config choose(int64_t n, int64_t k) {
 hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
   return launch_cfg(choose(n, k), codes, scales, n, k, x, m, y, stream);
+}
+
+hipError_t launch_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                      hipStream_t stream) {
+  int64_t n_total = 0;
+  for (int i = 0; i < count; ++i) n_total += pv[i].n;
+  for (int i0 = 0; i0 < count; i0 += kMaxGroup) {
+    const int cnt = count - i0 < kMaxGroup ? count - i0 : kMaxGroup;
+    const hipError_t e = launch_group(choose(n_total, k), pv + i0, cnt, k, m, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 #ifdef MXS_TUNING

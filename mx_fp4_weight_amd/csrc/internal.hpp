@@ -7,6 +7,18 @@
 
 namespace mxs {
 
+// One product of a grouped verify GEMM (host-side view).
+struct mxs_problem_view {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint16_t* x;
+  float* y;
+  int64_t n;
+};
+
+hipError_t launch_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                      hipStream_t stream);
+
 hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
                            int32_t* flags, hipStream_t stream);
 

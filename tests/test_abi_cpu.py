@@ -140,3 +140,22 @@ def test_product_never_imports_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "import synth" not in text and "from synth" not in text, fn
+
+
+def test_grouped_gemm_host_errors():
+    lib = mxs.get_lib()
+    arr = (mxs.GemmProblem * 3)()
+    for i in range(3):
+        arr[i] = mxs.GemmProblem(0x1000 * (i + 1), 0x20000, 0x30000, 0x40000, 64)
+    assert lib.mxfp4_verify_gemm_grouped(None, 3, 64, 5, None) == mxs.MXS_ERR_NULL
+    assert lib.mxfp4_verify_gemm_grouped(arr, 0, 64, 5, None) == mxs.MXS_ERR_SHAPE
+    assert lib.mxfp4_verify_gemm_grouped(arr, 3, 48, 5, None) == mxs.MXS_ERR_SHAPE
+    assert lib.mxfp4_verify_gemm_grouped(arr, 3, 64, 0, None) == mxs.MXS_ERR_SHAPE
+    assert lib.mxfp4_verify_gemm_grouped(arr, 3, 64, 5, None) == mxs.MXS_ERR_DEVICE
+    arr[1].x = 0
+    assert lib.mxfp4_verify_gemm_grouped(arr, 3, 64, 5, None) == mxs.MXS_ERR_NULL
+    arr[1].x = 0x30008
+    assert lib.mxfp4_verify_gemm_grouped(arr, 3, 64, 5, None) == mxs.MXS_ERR_ALIGN
+    arr[1].x = 0x30000
+    arr[2].n = 0
+    assert lib.mxfp4_verify_gemm_grouped(arr, 3, 64, 5, None) == mxs.MXS_ERR_SHAPE

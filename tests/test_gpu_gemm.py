@@ -157,3 +157,27 @@ def test_batched_320_rows_sampled():
     sub_s = np.zeros((n, k // 32), np.uint8)
     sub_c[rows], sub_s[rows] = rc, rs
     check_gemm(sub_c, sub_s, n, k, x, host(y)[:, rows], rows=rows, label="batched")
+
+
+@pytest.mark.parametrize("shapes,k,m", [
+    ([4096, 1024, 1024], 4096, 5),          # q | k | v
+    ([14336, 14336], 4096, 5),              # gate | up
+    ([17, 300, 1, 4100, 64, 2048, 5, 33, 999], 512, 9),   # ten products: two launches, ragged
+    ([130, 70], 1056, 3),                   # k % 512 != 0: one fallback launch per product
+])
+def test_grouped_matches_oracle(shapes, k, m):
+    say(f"gemm grouped: {shapes} k={k} m={m}")
+    items, hosts = [], []
+    for i, n in enumerate(shapes):
+        c, s_, _ = omx.quantize(synth.weights(8, 40 + i, n, k))
+        x = synth.activations(8, 40 + i, m, k)
+        items.append((dev(c), dev(s_), dev_bf16(x)))
+        hosts.append((c, s_, x, n))
+    ys = mxs.mxfp4_verify_gemm_grouped(items)
+    torch.cuda.synchronize()
+    for (c, s_, x, n), y in zip(hosts, ys):
+        check_gemm(c, s_, n, k, x, host(y), label=f"grouped n={n}")
+    # the single entry point gives bit-identical results for the same tile choice
+    y1 = mxs.mxfp4_verify_gemm(*items[0])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y1), host(ys[0]))

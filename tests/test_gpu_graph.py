@@ -56,3 +56,44 @@ def test_graph_replays_match_eager():
         mxs.mxfp4_verify_gemm(dc, ds, dev_bf16(synth.activations(2, 78, 3, k)))
         torch.cuda.synchronize()
     assert int(flags.item()) == 0
+
+
+def test_multistream_graph_replays_match_eager():
+    """Three independent GEMMs on three streams joined back, as the bench captures a layer."""
+    say("graph: three streams, replay x3")
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096)]
+    mats = []
+    for i, (n, k) in enumerate(shapes):
+        c, s_, _ = omx.quantize(synth.weights(2, 300 + i, n, k))
+        mats.append((dev(c), dev(s_), dev_bf16(synth.activations(2, 300 + i, 5, k)),
+                     torch.empty((5, n), dtype=torch.float32, device="cuda")))
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+    def step():
+        st = torch.cuda.current_stream()
+        for sd in side:
+            sd.wait_stream(st)
+        for (c, s_, x, y), where in zip(mats, [st, side[0], side[1]]):
+            mxs.mxfp4_verify_gemm(c, s_, x, y=y, stream=where)
+        for sd in side:
+            st.wait_stream(sd)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [host(y).copy() for (_, _, _, y) in mats]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for (_, _, _, y) in mats:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, _, _, y), r in zip(mats, ref):
+            assert np.array_equal(host(y), r), rep
+        step()
+        torch.cuda.synchronize()
