@@ -244,12 +244,29 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   // L2 round trips overlap
   Block<R, G> A, B;
   load(0, A);
+  // Staging: kStage branch-free buffer loads per thread are in flight before the
+  // first LDS write (a load-wait-write loop would pay one L2 round trip per chunk).
   const int nq = k >> 3;  // 16-byte chunks per activation row
-  for (int idx = threadIdx.x; idx < mt * nq; idx += blockDim.x) {
-    const int tt = idx / nq;
-    const int q = idx - tt * nq;
-    smem[xunit(q >> 4, q & 3, tt, (q >> 2) & 3, mt)] =
-        *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + tt) * (size_t)k + (size_t)q * 8);
+  const int nchunks = mt * nq;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)nchunks * 16u);
+  constexpr int kStage = 8;
+  for (int base = threadIdx.x; base < nchunks; base += kStage * (int)blockDim.x) {
+    u32x4 v[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const uint32_t off = idx < nchunks ? (uint32_t)idx * 16u : kOutOfRange;
+      v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    }
+    // stores are unconditional (a chunk past the end goes to the first unit of the
+    // reduction area, which is written before it is read) so no load sinks into a branch
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const int tt = idx / nq;
+      const int q = idx - tt * nq;
+      smem[idx < nchunks ? xunit(q >> 4, q & 3, tt, (q >> 2) & 3, mt) : xunits] = v[j];
+    }
   }
   lds_barrier();
   for (int u = 0; u < nunits;) {
@@ -259,6 +276,188 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     load(u + 1, A);
     compute(u, B);
     ++u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dense kernel for many activation rows (a batch of sequences × T positions).
+//
+// With m = 320 the contraction does ~1000 FLOP per weight byte, so the matrix
+// cores, not HBM, bound it. A workgroup owns a tile of 128 weight rows × 16·MC
+// activation rows and all of k. Its four waves form 2 row halves × 2 k halves:
+// wave (rh, kh) decodes the weights of rows [64·rh, 64·rh + 64) of the tile in
+// registers (4 A operands of 16 rows, loaded straight from HBM, one MX block
+// per lane as in the skinny kernel) and multiplies them with the MC B operands
+// of every 128-k group g with g % 2 == kh. The activations of a 256-k window
+// (both halves) are staged in LDS once per workgroup, double-buffered, and each
+// B operand read from LDS feeds 4 MFMAs. The two k halves are summed in LDS at
+// the end, in a fixed order. Tiles are mapped to XCDs so that the position
+// tiles of one weight tile run on the same XCD and share its L2: the weights
+// come from HBM once.
+constexpr int kDenseRows = 128;
+constexpr int kDenseThreads = 256;
+
+template <int MC>
+__global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m, int n_tiles,
+    int m_tiles, int y_vec4) {
+  constexpr int BM = 16 * MC;
+  constexpr int kUnits = 2 * 4 * BM * 4;  // 16-byte LDS units of one 256-k window
+  extern __shared__ u32x4 smem[];
+  // workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight tile
+  const int xcd = (int)blockIdx.x & 7;
+  const int j = (int)blockIdx.x >> 3;
+  const int nt = (j / m_tiles) * 8 + xcd;
+  const int mtile = j - (j / m_tiles) * m_tiles;
+  if (nt >= n_tiles) return;  // uniform for the workgroup, before any barrier
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rh = wave & 1;
+  const int kh = wave >> 1;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int kb = k >> 5;
+  const int ngroups = kb >> 2;
+  const int nsteps = (ngroups + 1) >> 1;
+  const uint32_t row_bytes = (uint32_t)(k >> 1);
+  const int row0 = nt * kDenseRows;
+  const int rows = min(kDenseRows, n - row0);
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)row0 * kb, (uint32_t)rows * (uint32_t)kb);
+  const int t0 = mtile * BM;
+  const int mrows = min(BM, m - t0);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)mrows * (uint32_t)k * 2u);
+
+  // codes and scales of this wave's 4 row tiles for the group of step s
+  struct W4 {
+    u32x4 c[4];
+    uint32_t s[4];
+  };
+  auto load_w = [&](int s, W4& w) {
+    const int grp = 2 * s + kh;
+    const int blk = grp * 4 + g;
+    const bool ok = grp < ngroups;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = (uint32_t)(rh * 64 + 16 * i + r);
+      const uint32_t co = ok ? row * row_bytes + (uint32_t)blk * 16 : kOutOfRange;
+      const uint32_t so = ok ? row * (uint32_t)kb + (uint32_t)blk : kOutOfRange;
+      w.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, co, 0, 0));
+      w.s[i] = __builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
+    }
+  };
+  // activations of the 256-k window of step s: chunk q (8 bf16) of tile row t goes to
+  // unit ((half*4 + d)*BM + t)*4 + gg with half = q/16, gg = (q/4)%4, d = q%4
+  constexpr int kChunks = BM * 32;
+  static_assert(kChunks % kDenseThreads == 0, "every thread stages the same number of chunks");
+  constexpr int kPerThread = kChunks / kDenseThreads;
+  u32x4 xs[kPerThread];
+  auto load_x = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int idx = (int)threadIdx.x + i * kDenseThreads;
+      const int t = idx >> 5;
+      const int q = idx & 31;
+      const bool ok = 2 * s + (q >> 4) < ngroups;
+      const uint32_t off = ok ? ((uint32_t)t * (uint32_t)k + (uint32_t)(s * 256 + q * 8)) * 2u : kOutOfRange;
+      xs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    }
+  };
+  auto store_x = [&](int buf) {
+    u32x4* dst = smem + buf * kUnits;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int idx = (int)threadIdx.x + i * kDenseThreads;
+      const int t = idx >> 5;
+      const int q = idx & 31;
+      dst[(((q >> 4) * 4 + (q & 3)) * BM + t) * 4 + ((q >> 2) & 3)] = xs[i];
+    }
+  };
+
+  f32x4 acc[4][MC];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < MC; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf, const W4& w) {
+    const u32x4* src = smem + buf * kUnits;
+    float sf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sf[i] = e8m0_to_f32(w.s[i] & 0xffu);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      bf16x8 bb[MC];
+#pragma unroll
+      for (int c = 0; c < MC; ++c)
+        bb[c] = __builtin_bit_cast(bf16x8, src[((kh * 4 + d) * BM + 16 * c + r) * 4 + g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 a = decode8(w.c[i][d], sf[i]);
+#pragma unroll
+        for (int c = 0; c < MC; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[c], acc[i][c], 0, 0, 0);
+      }
+    }
+  };
+
+  W4 wa, wb;
+  load_x(0);
+  load_w(0, wa);
+  store_x(0);
+  lds_barrier();
+  // The prefetch of step s + 1 is issued before the MFMAs of step s; the scheduling
+  // barriers keep the compiler from sinking those loads below the compute.
+  for (int s = 0; s < nsteps;) {
+    load_x(s + 1);
+    load_w(s + 1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s & 1, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    store_x((s + 1) & 1);
+    lds_barrier();
+    if (++s >= nsteps) break;
+    load_x(s + 1);
+    load_w(s + 1, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s & 1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    store_x((s + 1) & 1);
+    lds_barrier();
+    ++s;
+  }
+
+  // sum the two k halves in LDS (the staging buffers are free after the last barrier)
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [2 rh][4][MC][64]
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < MC; ++c) red[((rh * 4 + i) * MC + c) * kWave + lane] = acc[i][c];
+  }
+  lds_barrier();
+  if (kh == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int orow = row0 + rh * 64 + 16 * i + 4 * g;  // lane holds C[4g + e][r]
+#pragma unroll
+      for (int c = 0; c < MC; ++c) {
+        const f32x4 sum = acc[i][c] + red[((rh * 4 + i) * MC + c) * kWave + lane];
+        const int tt = t0 + 16 * c + r;
+        if (tt < m) {
+          float* yp = y + (size_t)tt * (size_t)n + orow;
+          if (y_vec4 && orow + 3 < n) {
+            *reinterpret_cast<f32x4*>(yp) = sum;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (orow + e < n) yp[e] = sum[e];
+          }
+        }
+      }
+    }
   }
 }
 
@@ -386,6 +585,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_xglobal_kernel(
 }
 
 constexpr size_t kMaxLds = 160 * 1024;
+constexpr int64_t kDenseMinM = 32;  // above this many activation rows the dense kernel runs
 constexpr int kMaxDevices = 64;
 constexpr int kCUs = 256;
 
@@ -475,10 +675,38 @@ hipError_t launch_xglobal(int gpw, const uint8_t* codes, const uint8_t* scales, 
   return hipGetLastError();
 }
 
+// Dense kernel: 16·MC activation rows per tile.
+constexpr int kDenseMC = 5;
+
+inline bool dense_ok(int64_t k, int64_t m) {
+  return m > kDenseMinM && k % 128 == 0 && k <= (int64_t(1) << 23);
+}
+
+hipError_t launch_dense(const mxs_problem_view& p, int64_t k, int64_t m, hipStream_t stream) {
+  constexpr int MC = kDenseMC;
+  static std::atomic<bool> done[kMaxDevices];
+  hipError_t e = allow_lds(&gemm_dense_kernel<MC>, done);
+  if (e != hipSuccess) return e;
+  const int n_tiles = (int)((p.n + kDenseRows - 1) / kDenseRows);
+  const int m_tiles = (int)((m + 16 * MC - 1) / (16 * MC));
+  const int64_t wgs = (int64_t)((n_tiles + 7) / 8) * 8 * m_tiles;
+  const size_t lds = 2 * sizeof(u32x4) * (2 * 4 * 16 * MC * 4);
+  gemm_dense_kernel<MC><<<dim3((unsigned)wgs), dim3(kDenseThreads), lds, stream>>>(
+      p.codes, p.scales, p.x, p.y, (int)p.n, (int)k, (int)m, n_tiles, m_tiles, y_vec4_ok(p.y, p.n));
+  return hipGetLastError();
+}
+
 // One launch for up to kMaxGroup problems with the same k and m (persistent kernel), or
-// one fallback launch per problem.
+// one dense or fallback launch per problem.
 hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t k, int64_t m,
                         hipStream_t stream) {
+  if (dense_ok(k, m)) {
+    for (int i = 0; i < count; ++i) {
+      const hipError_t e = launch_dense(pv[i], k, m, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   // Main kernel: 16-byte scale loads need k % 512 == 0 and 16-byte aligned scales; a row
   // block's bytes (64 rows at most) must fit a 32-bit buffer range; X must fit in LDS.
   bool aligned = (k % 512 == 0) && k <= (int64_t(1) << 24) && main_lds(k, m, c.R, c.G) <= kMaxLds;

@@ -57,9 +57,40 @@ def test_ragged_shapes(n, k, m):
     check_gemm(codes, scales, n, k, x, run_gemm(codes, scales, x), label=f"{n}x{k}x{m}")
 
 
-def test_scale_extremes():
+@pytest.mark.parametrize("n,k,m", [
+    # m > 32 with k % 128 == 0: the dense kernel (128 weight rows x 80 positions per tile,
+    # k split in two halves of alternating 128-k groups)
+    (1, 128, 33), (130, 384, 80), (257, 1024, 100), (1000, 2304, 161), (64, 128, 320),
+    (300, 896, 81), (129, 3200, 47), (1024, 1024, 240),
+    # m > 32 with k % 128 != 0: fallback kernel
+    (50, 96, 40), (33, 1056, 65),
+])
+def test_dense_ragged_shapes(n, k, m):
+    say(f"gemm: dense ragged n={n} k={k} m={m}")
+    w = synth.weights(9, n + 3 * k + m, n, k)
+    codes, scales, _ = omx.quantize(w)
+    x = synth.activations(9, n + 3 * k + m, m, k)
+    check_gemm(codes, scales, n, k, x, run_gemm(codes, scales, x), label=f"dense {n}x{k}x{m}")
+
+
+def test_one_hot_dense_exact():
+    """One-hot activation rows through the dense kernel return weight columns exactly."""
+    say("gemm: one-hot dense")
+    n, k, m = 200, 640, 96
+    codes, scales, _ = omx.quantize(synth.weights(7, 2, n, k))
+    cols = np.random.default_rng(5).integers(0, k, m)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), cols] = 1.0
+    y = run_gemm(codes, scales, synth.f32_to_bf16_bits(x))
+    wd = omx.dequantize(codes, scales, k)
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i].astype(np.float64), wd[:, c]), i
+
+
+@pytest.mark.parametrize("m", [5, 40])
+def test_scale_extremes(m):
     """Block scales from 2^-100 to 2^120 (products stay in the fp32 normal range), all-zero blocks."""
-    say("gemm: scale extremes")
+    say(f"gemm: scale extremes m={m}")
     n, k = 32, 512
     rng = np.random.default_rng(3)
     w = rng.standard_normal((n, k)).astype(np.float32)
@@ -69,7 +100,7 @@ def test_scale_extremes():
     w[5, :64] = -0.0
     codes, scales, _ = omx.quantize(w)
     assert scales[3].max() == 0 and scales.max() >= 240
-    x = synth.activations(7, 99, 5, k, sigma=1e-3)
+    x = synth.activations(7, 99, m, k, sigma=1e-3)
     check_gemm(codes, scales, n, k, x, run_gemm(codes, scales, x), label="scales")
 
 
@@ -164,6 +195,7 @@ def test_batched_320_rows_sampled():
     ([14336, 14336], 4096, 5),              # gate | up
     ([17, 300, 1, 4100, 64, 2048, 5, 33, 999], 512, 9),   # ten products: two launches, ragged
     ([130, 70], 1056, 3),                   # k % 512 != 0: one fallback launch per product
+    ([300, 129], 1024, 64),                 # m > 32: one dense launch per product
 ])
 def test_grouped_matches_oracle(shapes, k, m):
     say(f"gemm grouped: {shapes} k={k} m={m}")
