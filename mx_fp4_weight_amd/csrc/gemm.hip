@@ -145,8 +145,19 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   const int ngroups = (kb + 3) >> 2;
   const int gs = wave * G * nsub;  // first group of this wave's k-slice
   const uint32_t row_bytes = (uint32_t)(k >> 1);
-  const int xunits = ngroups * 16 * mt;
+  // Activations in LDS, row-major in 16-byte units: row t of the tile starts at unit
+  // t·xrs. A row covers every group a wave touches (W·nsub·G >= ngroups; the units
+  // past k hold zeros, so operand reads need no bounds test) plus one unit of
+  // padding, which shifts consecutive rows by 16 bytes: the 16 lanes of an operand
+  // read hit distinct banks.
+  const int nq = k >> 3;                   // 16-byte chunks per activation row
+  const int nqp = W * nsub * G * 16;       // chunks per padded row (>= nq)
+  const int xrs = nqp + 1;                 // row stride in units
+  const int xunits = mt * xrs;
   f32x4* red = reinterpret_cast<f32x4*>(smem + xunits);  // [2][W][R][64]
+  // Lane (r, g) reads chunk grp·16 + 4g + d of row r; rows past m read row 0, which
+  // only feeds output columns that are never stored.
+  const int xlane = (t_ok ? r : 0) * xrs + 4 * g;
 
   // this workgroup's work: its row blocks times the nsub sub-slices of G groups
   const int my_blocks = wg < nrb ? (nrb - 1 - wg) / ngrid + 1 : 0;
@@ -185,9 +196,13 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     }
   };
 
-  f32x4 acc[R];
+  // four accumulator chains per row tile (one per MFMA slice d), so consecutive
+  // MFMAs do not wait for each other; summed in a fixed order at the end
+  f32x4 acc[R][4];
 #pragma unroll
-  for (int i = 0; i < R; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   int parity = 0;
 
   auto compute = [&](int u, const Block<R, G>& b) {
@@ -195,19 +210,18 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int grp = g0 + j;
-      const bool ok = t_ok && grp < ngroups && grp * 4 + g < kb;
+      bf16x8 bb[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) bb[d] = __builtin_bit_cast(bf16x8, smem[xlane + grp * 16 + d]);
       float sf[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) sf[i] = e8m0_to_f32((b.s[i][j / 4][j % 4] >> (8 * g)) & 0xffu);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        u32x4 bx = u32x4{0u, 0u, 0u, 0u};
-        if (ok) bx = smem[xunit(grp, d, r, g, mt)];
-        const bf16x8 bb = __builtin_bit_cast(bf16x8, bx);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
           const bf16x8 a = decode8(b.c[i][j][d], sf[i]);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc[i], 0, 0, 0);
+          acc[i][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[d], acc[i][d], 0, 0, 0);
         }
       }
     }
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     const int rb = wg + (u / nsub) * ngrid;
     f32x4* rp = red + (size_t)parity * W * R * kWave;
 #pragma unroll
-    for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = acc[i];
+    for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
     lds_barrier();
     const int row0 = rb * 16 * R;
     for (int i = wave; i < R; i += W) {
@@ -236,44 +250,45 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
       }
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     parity ^= 1;
   };
 
-  // the first unit's codes go out before the activation staging, so the HBM and
-  // L2 round trips overlap
+  // Activation staging by direct global-to-LDS loads: wave-load L copies 64
+  // consecutive chunks (1 KiB) of one activation row, so the LDS destination is
+  // contiguous as the load-to-LDS form requires (nq is a multiple of 64). The
+  // first unit's weight loads go out behind them.
   Block<R, G> A, B;
-  load(0, A);
-  // Staging: kStage branch-free buffer loads per thread are in flight before the
-  // first LDS write (a load-wait-write loop would pay one L2 round trip per chunk).
-  const int nq = k >> 3;  // 16-byte chunks per activation row
-  const int nchunks = mt * nq;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)nchunks * 16u);
-  constexpr int kStage = 8;
-  for (int base = threadIdx.x; base < nchunks; base += kStage * (int)blockDim.x) {
-    u32x4 v[kStage];
-#pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const uint32_t off = idx < nchunks ? (uint32_t)idx * 16u : kOutOfRange;
-      v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-    }
-    // stores are unconditional (a chunk past the end goes to the first unit of the
-    // reduction area, which is written before it is read) so no load sinks into a branch
-#pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const int tt = idx / nq;
-      const int q = idx - tt * nq;
-      smem[idx < nchunks ? xunit(q >> 4, q & 3, tt, (q >> 2) & 3, mt) : xunits] = v[j];
+  {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)(mt * nq) * 16u);
+    const int per_row = nq >> 6;
+    for (int L = wave; L < mt * per_row; L += W) {
+      const int tt = L / per_row;
+      const int c = L - tt * per_row;
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(smem + tt * xrs + c * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, (uint32_t)((tt * nq + c * 64 + lane) * 16), 0, 0, 0);
     }
   }
+  load(0, A);
+  // zeros for the chunks past k in every row
+  for (int idx = (int)threadIdx.x; idx < mt * (nqp - nq); idx += (int)blockDim.x) {
+    const int tt = idx / (nqp - nq);
+    smem[tt * xrs + nq + (idx - tt * (nqp - nq))] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // the direct loads are counted by vmcnt; wait for them (and the first unit)
+  __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
+  // The scheduling barriers keep each prefetch ahead of the waits of the compute.
   for (int u = 0; u < nunits;) {
     load(u + 1, B);  // past the last unit: a zero-record descriptor, nothing is read
+    __builtin_amdgcn_sched_barrier(0);
     compute(u, A);
     if (++u >= nunits) break;
     load(u + 1, A);
+    __builtin_amdgcn_sched_barrier(0);
     compute(u, B);
     ++u;
   }
@@ -624,7 +639,8 @@ inline size_t main_lds(int64_t k, int64_t m, int R, int G) {
   int waves, nsub;
   split_k(ngroups, G, waves, nsub);
   const int64_t mt = m < 16 ? m : 16;
-  return (size_t)ngroups * 16 * mt * 16 + 2 * sizeof(f32x4) * waves * R * kWave;
+  const int64_t xrs = (int64_t)waves * nsub * G * 16 + 1;  // padded row stride in 16-byte units
+  return (size_t)(mt * xrs) * 16 + 2 * sizeof(f32x4) * waves * R * kWave;
 }
 
 template <int R, int G>
@@ -715,7 +731,7 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
   if (aligned) {
 #define MXS_RG(RR, GG) \
   if (c.R == RR && c.G == GG) return launch_main<RR, GG>(c, pv, count, k, m, stream);
-    MXS_RG(1, 4) MXS_RG(1, 8) MXS_RG(2, 4) MXS_RG(2, 8) MXS_RG(4, 4)
+    MXS_RG(1, 4) MXS_RG(1, 8) MXS_RG(2, 4) MXS_RG(2, 8)
 #undef MXS_RG
     return hipErrorInvalidValue;
   }
