@@ -10,9 +10,10 @@ mxfp4_verify_gemm_grouped over gate | up, mxfp4_verify_gemm for down. Then it
 runs spec_accept on one sequence (K = 4 drafts, vocab 128256, fp32 logits
 N(0, 3), target = draft + N(0, 1)).
 
-Cold weights: the layers of a pool larger than the 256 MB Infinity Cache
-(default 1.5 GB, 13 layers) are visited in turn, so every step reads its
-weights from HBM. Inputs are resident in HBM before the timed region. Weights
+Cold weights: the layers of a pool (default 4.6 GB, 40 layers) are visited in
+turn, so every step reads its weights from HBM; even one launch type alone
+(e.g. o over all 40 layers, 356 MB) streams more than the 256 MB Infinity
+Cache holds. Inputs are resident in HBM before the timed region. Weights
 are N(0, 0.02) fp32 drawn on the GPU and quantized by mxfp4_quantize (not
 timed). The logits and uniforms come from the shared seeded generator.
 
@@ -23,6 +24,15 @@ wall time of all steps (spec_accept and the gaps between kernels included).
 `roofline` is the verify-GEMM kernel alone: for each launch type a graph runs
 it on every pool layer back to back between two HIP events on the replay
 stream, giving the average launch duration without host gaps.
+
+The same line carries the secondary workloads (skipped with --no-extra):
+`t_sweep_8b` (the four launch types at T = 1..8), `shapes_70b_t5` (70B-class
+shapes with 1% outlier input channels x20, lm_head 128256x8192, and the
+70B tokens/s-equivalent), `batched_64x5` (dense verify GEMM 320x8192x28672 with
+its MFMA utilisation, spec_accept for 64 sequences) and `full_8b_step` (32
+layers + lm_head 128256x4096, then spec_accept on the lm_head output with draft
+rows tuned to acceptance 0.6 / 0.8 / 0.9: step time, tokens/s-equivalent and the
+GPU-measured tokens per step against the closed form).
 """
 from __future__ import annotations
 
@@ -191,13 +201,284 @@ def cpu_baseline(seconds_budget=15.0):
     }
 
 
+# ---------------------------------------------------------------------------
+# Secondary workloads, reported in the same JSON line (not part of `value`).
+
+def _gpu_mx(torch, mxs, gen, n, k, sigma=0.02, outlier_cols=None):
+    """MX-FP4 codes/scales of an N(0, sigma) fp32 matrix drawn on the GPU (optionally
+    with outlier input columns scaled x20)."""
+    w = torch.randn((n, k), generator=gen, device="cuda", dtype=torch.float32) * sigma
+    if outlier_cols is not None and len(outlier_cols):
+        idx = torch.as_tensor(outlier_cols, device="cuda")
+        w[:, idx] *= 20.0
+    c, s = mxs.mxfp4_quantize(w)
+    del w
+    return c, s
+
+
+def _graph_ms(torch, body, reps):
+    """Average ms per replay of a HIP graph that runs body() once (one warm replay first)."""
+    body()  # eager call: one-time library set-up outside the capture
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        body()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del g
+    return ms
+
+
+def _rand_bf16(torch, gen, m, k):
+    return torch.randn((m, k), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def t_sweep(torch, mxs, pool, gen, reps=3):
+    """8B-class shapes at T = 1..8 over the cold pool: per launch type, µs and GB/s."""
+    n_layers = len(pool)
+    out = {}
+    for t in range(1, 9):
+        xs = [[_rand_bf16(torch, gen, t, k) for (_, _, k) in LAYER] for _ in range(n_layers)]
+        ys = [torch.empty((t, n), dtype=torch.float32, device="cuda") for (_, n, _) in LAYER]
+        row = {}
+        for name, idx in LAUNCHES:
+            def body(idx=idx):
+                for li in range(n_layers):
+                    items = [(pool[li][i][0], pool[li][i][1], xs[li][i]) for i in idx]
+                    if len(items) == 1:
+                        mxs.mxfp4_verify_gemm(*items[0], y=ys[idx[0]])
+                    else:
+                        mxs.mxfp4_verify_gemm_grouped(items, ys=[ys[i] for i in idx])
+            us = _graph_ms(torch, body, reps) * 1e3 / n_layers
+            byts = sum(gemm_alg_bytes(LAYER[i][1], LAYER[i][2], t) for i in idx)
+            row[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
+        tot_b = sum(gemm_alg_bytes(n, k, t) for _, n, k in LAYER)
+        tot_us = sum(v["us"] for v in row.values())
+        row["layer_GBps"] = round(tot_b / (tot_us * 1e-6) / 1e9, 1)
+        row["layer_pct_of_hbm_peak"] = round(100 * tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2)
+        out[f"T{t}"] = row
+        del xs, ys
+    return out
+
+
+L70 = [("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192), ("o", 8192, 8192),
+       ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)]
+LM70 = (128256, 8192)
+MODEL70_BYTES = 80 * sum(mx_bytes(n, k) for _, n, k in L70) + mx_bytes(*LM70)
+
+
+def shapes_70b(torch, mxs, synth, gen, reps=3):
+    """70B-class shapes at T=5 with 1% outlier input channels x20: per launch µs and GB/s.
+
+    Copies per shape are chosen so each timed graph streams > 256 MB (cold weights).
+    """
+    import numpy as np
+    copies = {"attn": 8, "mlp": 3, "lm": 2}
+    outl = {k: synth.outlier_columns(3, j, k, 0.01) for j, k in ((0, 8192), (1, 28672))}
+    attn, mlp, lm = [], [], []
+    for c in range(copies["attn"]):
+        attn.append([(*_gpu_mx(torch, mxs, gen, n, k, outlier_cols=outl[k]), _rand_bf16(torch, gen, T, k))
+                     for (_, n, k) in L70[:4]])
+    for c in range(copies["mlp"]):
+        mlp.append([(*_gpu_mx(torch, mxs, gen, n, k, outlier_cols=outl[k]),
+                     _rand_bf16(torch, gen, T, k)) for (_, n, k) in L70[4:]])
+    for c in range(copies["lm"]):
+        lm.append((*_gpu_mx(torch, mxs, gen, *LM70, outlier_cols=outl[8192]), _rand_bf16(torch, gen, T, LM70[1])))
+    y_attn = [torch.empty((T, n), dtype=torch.float32, device="cuda") for (_, n, _) in L70[:4]]
+    y_mlp = [torch.empty((T, n), dtype=torch.float32, device="cuda") for (_, n, _) in L70[4:]]
+    y_lm = torch.empty((T, LM70[0]), dtype=torch.float32, device="cuda")
+    plans = [("qkv", attn, (0, 1, 2), y_attn), ("o", attn, (3,), y_attn), ("gate_up", mlp, (0, 1), y_mlp),
+             ("down", mlp, (2,), y_mlp), ("lm_head", None, None, None)]
+    out = {}
+    layer_b = layer_us = 0.0
+    for name, sets, idx, ybuf in plans:
+        if name == "lm_head":
+            def body():
+                for (c, s, x) in lm:
+                    mxs.mxfp4_verify_gemm(c, s, x, y=y_lm)
+            us = _graph_ms(torch, body, reps) * 1e3 / len(lm)
+            byts = gemm_alg_bytes(LM70[0], LM70[1], T)
+        else:
+            def body(sets=sets, idx=idx, ybuf=ybuf):
+                for st in sets:
+                    items = [st[i] for i in idx]
+                    outs = [ybuf[i] for i in idx]
+                    if len(items) == 1:
+                        mxs.mxfp4_verify_gemm(*items[0], y=outs[0])
+                    else:
+                        mxs.mxfp4_verify_gemm_grouped(items, ys=outs)
+            us = _graph_ms(torch, body, reps) * 1e3 / len(sets)
+            byts = sum(gemm_alg_bytes(sets[0][i][0].shape[0], sets[0][i][0].shape[1] * 2, T) for i in idx)
+            layer_b += byts
+            layer_us += us
+        out[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
+    layer_bps = layer_b / (layer_us * 1e-6)
+    out["layer_GBps"] = round(layer_bps / 1e9, 1)
+    out["layer_pct_of_hbm_peak"] = round(100 * layer_bps / 1e9 / HBM_PEAK_GBPS, 2)
+    out["tokens_per_s_equivalent"] = round(layer_bps / MODEL70_BYTES, 1)
+    out["note"] = ("tokens/s-equivalent = achieved layer bytes/s / 70B-class model MX bytes "
+                   f"({MODEL70_BYTES} B: 80 layers + lm_head), one verification step per token")
+    del attn, mlp, lm
+    return out
+
+
+def batched(torch, mxs, gen, reps=5):
+    """64 sequences x 5 positions: dense verify GEMM (320 x 8192 x 28672) and spec_accept B=64."""
+    n, k, m = 8192, 28672, 320
+    copies = [(*_gpu_mx(torch, mxs, gen, n, k), _rand_bf16(torch, gen, m, k)) for _ in range(3)]
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+    def body():
+        for (c, s, x) in copies:
+            mxs.mxfp4_verify_gemm(c, s, x, y=y)
+    us = _graph_ms(torch, body, reps) * 1e3 / len(copies)
+    flops = 2.0 * m * n * k
+    byts = gemm_alg_bytes(n, k, m)
+    out = {"gemm": {"us": round(us, 1), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                    "mfma_util_vs_bf16_dense_peak": round(flops / (us * 1e-6) / 2.5e15, 4),
+                    "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                    "kernel": "gemm_dense_kernel (v_mfma_f32_16x16x32_bf16; peak 2.5 PFLOP/s dense bf16)"}}
+    del copies
+    b = 64
+    base = torch.randn((b, KD + 1, V), generator=gen, device="cuda", dtype=torch.float32) * 3.0
+    tgt = base + torch.randn((b, KD + 1, V), generator=gen, device="cuda", dtype=torch.float32)
+    dft = base[:, :KD].contiguous()
+    del base
+    tok = torch.multinomial(torch.softmax(dft.double(), -1).reshape(b * KD, V), 1, generator=gen)
+    tok = tok.reshape(b, KD).to(torch.int32)
+    u = torch.rand((b, KD + 1), generator=gen, device="cuda", dtype=torch.float32)
+    ws = torch.empty((mxs.spec_accept_workspace_bytes(b, KD, V),), dtype=torch.uint8, device="cuda")
+    ot = torch.empty((b, KD + 1), dtype=torch.int32, device="cuda")
+    on = torch.empty((b,), dtype=torch.int32, device="cuda")
+
+    def acc():
+        mxs.spec_accept(tgt, dft, tok, u, out_tokens=ot, out_num=on, workspace=ws)
+    us_a = _graph_ms(torch, acc, reps * 4) * 1e3
+    read_b = b * (2 * KD + 1) * V * 4
+    out["spec_accept"] = {"B": b, "us": round(us_a, 1),
+                          "positions_per_s": round(b * (KD + 1) / (us_a * 1e-6), 1),
+                          "logit_read_GBps": round(read_b / (us_a * 1e-6) / 1e9, 1),
+                          "mean_accepted": round(float(on.float().mean()), 3)}
+    del tgt, dft, ws
+    return out
+
+
+def _overlap(torch, p_logits, q_logits):
+    p = torch.softmax(p_logits.double(), -1)
+    q = torch.softmax(q_logits.double(), -1)
+    return float(torch.minimum(p, q).sum())
+
+
+def full_8b_step(torch, mxs, gen, steps=10, trials=4096):
+    """32 decoder layers + lm_head 128256x4096 at T=5, then spec_accept on the lm_head output.
+
+    Draft rows i < 4 are target row i + lam_i * N(0,1), with lam_i bisected (fp64, torch,
+    outside the timed region) so the per-position acceptance alpha = sum_x min(p, q)
+    hits each of 0.6 / 0.8 / 0.9; the GPU acceptance over `trials` cycles gives the
+    measured tokens per step, compared with the closed form (1 - a^(K+1)) / (1 - a).
+    """
+    layers = []
+    for li in range(32):
+        layers.append([(*_gpu_mx(torch, mxs, gen, n, k), _rand_bf16(torch, gen, T, k)) for (_, n, k) in LAYER])
+    lm_c, lm_s = _gpu_mx(torch, mxs, gen, V, 4096)
+    lm_x = _rand_bf16(torch, gen, T, 4096)
+    ys = [torch.empty((T, n), dtype=torch.float32, device="cuda") for (_, n, _) in LAYER]
+    y_lm = torch.empty((1, T, V), dtype=torch.float32, device="cuda")
+    model_bytes = 32 * sum(mx_bytes(n, k) for _, n, k in LAYER) + mx_bytes(V, 4096)
+    step_bytes = 32 * sum(gemm_alg_bytes(n, k, T) for _, n, k in LAYER) + gemm_alg_bytes(V, 4096, T)
+
+    def gemms():
+        for mats in layers:
+            for _, idx in LAUNCHES:
+                if len(idx) == 1:
+                    mxs.mxfp4_verify_gemm(*mats[idx[0]], y=ys[idx[0]])
+                else:
+                    mxs.mxfp4_verify_gemm_grouped([mats[i] for i in idx], ys=[ys[i] for i in idx])
+        mxs.mxfp4_verify_gemm(lm_c, lm_s, lm_x, y=y_lm.view(T, V))
+    gemms()
+    torch.cuda.synchronize()
+    # The lm_head output [1, T, V] is the target law of spec_accept (its rows are the
+    # T = K+1 positions); the graph recomputes it each step from the same inputs.
+    tgt = y_lm
+    tgt_rows = y_lm[0].clone()
+    noise = torch.randn((KD, V), generator=gen, device="cuda", dtype=torch.float32)
+    result = {"per_alpha": {}}
+    ws = torch.empty((mxs.spec_accept_workspace_bytes(1, KD, V),), dtype=torch.uint8, device="cuda")
+    ot = torch.empty((1, KD + 1), dtype=torch.int32, device="cuda")
+    on = torch.empty((1,), dtype=torch.int32, device="cuda")
+    for alpha in (0.6, 0.8, 0.9):
+        lams = []
+        for i in range(KD):
+            lo, hi = 0.0, 64.0
+            for _ in range(60):
+                mid = 0.5 * (lo + hi)
+                if _overlap(torch, tgt_rows[i], tgt_rows[i] + mid * noise[i]) > alpha:
+                    lo = mid
+                else:
+                    hi = mid
+            lams.append(0.5 * (lo + hi))
+        dft = torch.stack([tgt_rows[i] + lams[i] * noise[i] for i in range(KD)]).unsqueeze(0).contiguous()
+        alphas = [_overlap(torch, tgt_rows[i], dft[0, i]) for i in range(KD)]
+        # the timed step: all GEMMs, then spec_accept reading the lm_head output buffer
+        tok = torch.multinomial(torch.softmax(dft[0].double(), -1), 1, generator=gen).reshape(1, KD).to(torch.int32)
+        u = torch.rand((1, KD + 1), generator=gen, device="cuda", dtype=torch.float32)
+
+        def step():
+            gemms()
+            mxs.spec_accept(tgt, dft, tok, u, out_tokens=ot, out_num=on, workspace=ws)
+        ms = _graph_ms(torch, step, steps)
+        # acceptance statistics over many cycles (batched, fresh draft tokens and uniforms)
+        bt = 512
+        tgt_b = tgt_rows.unsqueeze(0).expand(bt, KD + 1, V).contiguous()
+        dft_b = dft.expand(bt, KD, V).contiguous()
+        wsb = torch.empty((mxs.spec_accept_workspace_bytes(bt, KD, V),), dtype=torch.uint8, device="cuda")
+        qd = torch.softmax(dft[0].double(), -1)
+        emitted = []
+        for _ in range(trials // bt):
+            tk = torch.multinomial(qd, bt, replacement=True, generator=gen).t().contiguous().to(torch.int32)
+            ub = torch.rand((bt, KD + 1), generator=gen, device="cuda", dtype=torch.float32)
+            _, nb = mxs.spec_accept(tgt_b, dft_b, tk, ub, workspace=wsb)
+            emitted.append((nb + 1).double())
+        em = torch.cat(emitted)
+        e_closed = (1 - alpha ** (KD + 1)) / (1 - alpha)
+        e_meas = float(em.mean())
+        se = float(em.std()) / math.sqrt(em.numel())
+        steps_per_s = 1e3 / ms
+        result["per_alpha"][str(alpha)] = {
+            "alpha_rows": [round(a, 5) for a in alphas],
+            "E_closed_form": round(e_closed, 4), "E_measured_gpu": round(e_meas, 4),
+            "E_z": round((e_meas - e_closed) / se, 2), "trials": int(em.numel()),
+            "step_us": round(ms * 1e3, 1), "steps_per_s": round(steps_per_s, 1),
+            "tokens_per_s_equivalent": round(e_closed * steps_per_s, 1)}
+        del tgt_b, dft_b, wsb
+    ms0 = min(v["step_us"] for v in result["per_alpha"].values()) * 1e-3
+    result.update({"model_bytes": model_bytes, "gemm_launches_per_step": 32 * len(LAUNCHES) + 1,
+                   "step_GBps": round(step_bytes / (ms0 * 1e-3) / 1e9, 1),
+                   "step_pct_of_hbm_peak": round(100 * step_bytes / (ms0 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)})
+    del layers
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--pool-gb", type=float, default=1.5)
+    ap.add_argument("--pool-gb", type=float, default=4.6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary workloads (T sweep, 70B shapes, batched, full 8B step)")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -400,6 +681,17 @@ def main():
                       "layer back to back; average over the four launch types of a layer",
         },
     }
+    if not args.no_extra:
+        gen2 = torch.Generator(device=dev)
+        gen2.manual_seed(args.seed * 7919 + 17)
+        for key, fn in (("t_sweep_8b", lambda: t_sweep(torch, mxs, pool, gen2)),
+                        ("shapes_70b_t5", lambda: shapes_70b(torch, mxs, synth, gen2)),
+                        ("batched_64x5", lambda: batched(torch, mxs, gen2)),
+                        ("full_8b_step", lambda: full_8b_step(torch, mxs, gen2))):
+            print(f"# workload {key}", file=sys.stderr, flush=True)
+            result[key] = fn()
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline()
