@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kWThreads) void decide_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
     int chunks, Workspace ws, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num,
-    int32_t* __restrict__ flags, int vec4) {
+    int32_t* __restrict__ flags, int vec4, int prefetch) {
   __shared__ double smax[kMaxRows];
   __shared__ double ssum[kMaxRows];
   __shared__ int sbad[kMaxRows];
@@ -373,11 +373,13 @@ __global__ __launch_bounds__(kWThreads) void decide_kernel(
   const int wave = threadIdx.x / kWave;
   const int per_seq = 2 * kd + 1;
 
-  // For K <= 4 every candidate final row's 4 logits of this thread are fetched
-  // now, together with the statistics, so step 3 needs no further memory trip.
+  // For small batches with K <= 4, every candidate final row's 4 logits of this
+  // thread are fetched now, together with the statistics, so step 3 needs no
+  // further memory trip. That reads all 2K+1 rows again, so large batches (where
+  // bandwidth, not latency, bounds the call) load only the rows step 3 needs.
   constexpr int kPre = 9;
   const int t0w = c * kChunk + threadIdx.x * kWPer;
-  const bool pre = vec4 && kd <= 4 && t0w + kWPer <= v;
+  const bool pre = prefetch && vec4 && kd <= 4 && t0w + kWPer <= v;
   f32x4 prow[kPre];
 #pragma unroll
   for (int r = 0; r < kPre; ++r) {
@@ -609,8 +611,11 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
     stats_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // prefetch of all candidate rows while the batch's logits are at most 16 MB
+  const int prefetch = (int64_t)b * (2 * kd + 1) * v * 4 <= (int64_t(16) << 20) ? 1 : 0;
   decide_kernel<<<dim3((unsigned)chunks, (unsigned)b), dim3(kWThreads), 0, stream>>>(
-      target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4);
+      target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4,
+      prefetch);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   sample_kernel<<<dim3((unsigned)b), dim3(kWThreads), 0, stream>>>(target, draft, uniforms, kd, v,
