@@ -119,7 +119,8 @@ struct Group {
 
 template <int R, int G>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
-                                                                         int nsub) {
+                                                                         int nsub, int phases,
+                                                                         int ngroups_p) {
   extern __shared__ u32x4 smem[];
   int pi = 0;
   while (pi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[pi + 1]) ++pi;
@@ -143,15 +144,18 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   const bool t_ok = r < mt;
   const int kb = k >> 5;
   const int ngroups = (kb + 3) >> 2;
-  const int gs = wave * G * nsub;  // first group of this wave's k-slice
+  // k is walked in `phases` phases of ngroups_p groups (one phase unless the
+  // activations of all of k do not fit in LDS); inside a phase wave w owns the
+  // groups [gs, gs + nsub·G) of the phase.
+  const int gs = wave * G * nsub;  // first group of this wave's slice of a phase
   const uint32_t row_bytes = (uint32_t)(k >> 1);
-  // Activations in LDS, row-major in 16-byte units: row t of the tile starts at unit
-  // t·xrs. A row covers every group a wave touches (W·nsub·G >= ngroups; the units
-  // past k hold zeros, so operand reads need no bounds test) plus one unit of
-  // padding, which shifts consecutive rows by 16 bytes: the 16 lanes of an operand
-  // read hit distinct banks.
+  // Activations of one phase in LDS, row-major in 16-byte units: row t of the tile
+  // starts at unit t·xrs. A row covers every group a wave touches (W·nsub·G >=
+  // ngroups_p; the units past the phase or past k hold zeros, so operand reads need
+  // no bounds test) plus one unit of padding, which shifts consecutive rows by 16
+  // bytes: the 16 lanes of an operand read hit distinct banks.
   const int nq = k >> 3;                   // 16-byte chunks per activation row
-  const int nqp = W * nsub * G * 16;       // chunks per padded row (>= nq)
+  const int nqp = W * nsub * G * 16;       // chunks per padded row of a phase
   const int xrs = nqp + 1;                 // row stride in units
   const int xunits = mt * xrs;
   f32x4* red = reinterpret_cast<f32x4*>(smem + xunits);  // [2][W][R][64]
@@ -159,13 +163,17 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   // only feeds output columns that are never stored.
   const int xlane = (t_ok ? r : 0) * xrs + 4 * g;
 
-  // this workgroup's work: its row blocks times the nsub sub-slices of G groups
+  // this workgroup's work: its row blocks times the phases times the nsub
+  // sub-slices of G groups (with several phases a workgroup owns one row block)
+  const int upr = phases * nsub;  // units per row block
   const int my_blocks = wg < nrb ? (nrb - 1 - wg) / ngrid + 1 : 0;
-  const int nunits = my_blocks * nsub;
+  const int nunits = my_blocks * upr;
 
   auto load = [&](int u, Block<R, G>& b) {
-    const int rb = wg + (u / nsub) * ngrid;
-    const int g0 = gs + (u % nsub) * G;
+    const int rb = wg + (u / upr) * ngrid;
+    const int uu = u % upr;
+    const int gl0 = gs + (uu % nsub) * G;            // first group inside the phase
+    const int g0 = (uu / nsub) * ngroups_p + gl0;   // first group of k
     // descriptors covering the valid rows of row block rb (none past the last unit)
     const int row0 = rb * 16 * R;
     const int rows = u < nunits ? min(16 * R, n - row0) : 0;
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int blk = (g0 + j) * 4 + g;
-      const bool ok = blk < kb;
+      const bool ok = gl0 + j < ngroups_p && blk < kb;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const uint32_t off = ok ? (uint32_t)(16 * i + r) * row_bytes + (uint32_t)blk * 16 : kOutOfRange;
@@ -187,12 +195,35 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
 #pragma unroll
     for (int q = 0; q < G / 4; ++q) {
       const int grp0 = g0 + 4 * q;
-      const bool ok = grp0 < ngroups;
+      const bool ok = gl0 + 4 * q < ngroups_p && grp0 < ngroups;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const uint32_t off = ok ? (uint32_t)(16 * i + r) * (uint32_t)kb + (uint32_t)grp0 * 4 : kOutOfRange;
         b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
       }
+    }
+  };
+
+  // Activation staging of phase ph by direct global-to-LDS loads: wave-load L copies
+  // 64 consecutive chunks (1 KiB) of one activation row, so the LDS destination is
+  // contiguous as the load-to-LDS form requires (nq and the phase start are
+  // multiples of 64 chunks); the rest of each padded row is zero-filled.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)(mt * nq) * 16u);
+  auto stage = [&](int ph) {
+    const int q0 = ph * ngroups_p * 16;                  // first chunk of the phase
+    const int nv = min(ngroups_p * 16, nq - q0);         // valid chunks per row
+    const int per_row = nv >> 6;
+    for (int L = wave; L < mt * per_row; L += W) {
+      const int tt = L / per_row;
+      const int c = L - tt * per_row;
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(smem + tt * xrs + c * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, (uint32_t)((tt * nq + q0 + c * 64 + lane) * 16), 0,
+                                               0, 0);
+    }
+    for (int idx = (int)threadIdx.x; idx < mt * (nqp - nv); idx += (int)blockDim.x) {
+      const int tt = idx / (nqp - nv);
+      smem[tt * xrs + nv + (idx - tt * (nqp - nv))] = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -206,13 +237,22 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   int parity = 0;
 
   auto compute = [&](int u, const Block<R, G>& b) {
-    const int g0 = gs + (u % nsub) * G;
+    const int uu = u % upr;
+    if (phases > 1 && uu != 0 && uu % nsub == 0) {
+      // first unit of a later phase: stage its activations once every wave is done
+      // with the previous phase (this also waits for the prefetched unit)
+      lds_barrier();
+      stage(uu / nsub);
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
+    }
+    const int gl0 = gs + (uu % nsub) * G;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int grp = g0 + j;
+      const int gl = gl0 + j;
       bf16x8 bb[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) bb[d] = __builtin_bit_cast(bf16x8, smem[xlane + grp * 16 + d]);
+      for (int d = 0; d < 4; ++d) bb[d] = __builtin_bit_cast(bf16x8, smem[xlane + gl * 16 + d]);
       float sf[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) sf[i] = e8m0_to_f32((b.s[i][j / 4][j % 4] >> (8 * g)) & 0xffu);
@@ -225,9 +265,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
         }
       }
     }
-    if (u % nsub != nsub - 1) return;
-    // last sub-slice of the row block: sum the waves' partial tiles and store
-    const int rb = wg + (u / nsub) * ngrid;
+    if (uu != upr - 1) return;
+    // last unit of the row block: sum the waves' partial tiles and store
+    const int rb = wg + (u / upr) * ngrid;
     f32x4* rp = red + (size_t)parity * W * R * kWave;
 #pragma unroll
     for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
@@ -256,28 +296,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     parity ^= 1;
   };
 
-  // Activation staging by direct global-to-LDS loads: wave-load L copies 64
-  // consecutive chunks (1 KiB) of one activation row, so the LDS destination is
-  // contiguous as the load-to-LDS form requires (nq is a multiple of 64). The
-  // first unit's weight loads go out behind them.
   Block<R, G> A, B;
-  {
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)(mt * nq) * 16u);
-    const int per_row = nq >> 6;
-    for (int L = wave; L < mt * per_row; L += W) {
-      const int tt = L / per_row;
-      const int c = L - tt * per_row;
-      __attribute__((address_space(3))) void* dst =
-          (__attribute__((address_space(3))) void*)(smem + tt * xrs + c * 64);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, (uint32_t)((tt * nq + c * 64 + lane) * 16), 0, 0, 0);
-    }
-  }
+  stage(0);
   load(0, A);
-  // zeros for the chunks past k in every row
-  for (int idx = (int)threadIdx.x; idx < mt * (nqp - nq); idx += (int)blockDim.x) {
-    const int tt = idx / (nqp - nq);
-    smem[tt * xrs + nq + (idx - tt * (nqp - nq))] = u32x4{0u, 0u, 0u, 0u};
-  }
   // the direct loads are counted by vmcnt; wait for them (and the first unit)
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
@@ -633,26 +654,41 @@ inline void split_k(int64_t ngroups, int G, int& waves, int& nsub) {
   waves = (int)((ngroups + (int64_t)G * nsub - 1) / ((int64_t)G * nsub));
 }
 
-// LDS bytes the main kernel needs: X[mt, k] in operand order plus two reduction buffers.
-inline size_t main_lds(int64_t k, int64_t m, int R, int G) {
+// Phase split of k for the main kernel: the fewest phases whose activation tile
+// X[mt, k/phases] (padded rows) plus the two reduction buffers fit in LDS. A later
+// phase starts on a 4-group (512-k) boundary so its activation rows stay in whole
+// 1 KiB windows. Returns false if even 4 groups per phase do not fit.
+struct PhasePlan {
+  int phases, ngroups_p, waves, nsub;
+  size_t lds;
+};
+
+inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp) {
   const int64_t ngroups = (k / 32 + 3) / 4;
-  int waves, nsub;
-  split_k(ngroups, G, waves, nsub);
   const int64_t mt = m < 16 ? m : 16;
-  const int64_t xrs = (int64_t)waves * nsub * G * 16 + 1;  // padded row stride in 16-byte units
-  return (size_t)(mt * xrs) * 16 + 2 * sizeof(f32x4) * waves * R * kWave;
+  for (int64_t phases = 1; phases <= ngroups; ++phases) {
+    int64_t ngp = (ngroups + phases - 1) / phases;
+    if (phases > 1) ngp = (ngp + 3) / 4 * 4;
+    if (phases > 1 && (phases - 1) * ngp >= ngroups) continue;  // no empty phase
+    int waves, nsub;
+    split_k(ngp, G, waves, nsub);
+    const int64_t xrs = (int64_t)waves * nsub * G * 16 + 1;  // padded row stride, 16-byte units
+    const size_t lds = (size_t)(mt * xrs) * 16 + 2 * sizeof(f32x4) * waves * R * kWave;
+    if (lds <= kMaxLds) {
+      pp = PhasePlan{(int)phases, (int)ngp, waves, nsub, lds};
+      return true;
+    }
+    if (ngp <= 4) break;
+  }
+  return false;
 }
 
 template <int R, int G>
-hipError_t launch_main(const Config& c, const mxs_problem_view* pv, int count, int64_t k, int64_t m,
-                       hipStream_t stream) {
+hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
+                       int64_t k, int64_t m, hipStream_t stream) {
   static std::atomic<bool> done[kMaxDevices];
   hipError_t e = allow_lds(&gemm_skinny_kernel<R, G>, done);
   if (e != hipSuccess) return e;
-  const int64_t ngroups = (k / 32 + 3) / 4;
-  int waves, nsub;
-  split_k(ngroups, G, waves, nsub);
-  const size_t lds = main_lds(k, m, R, G);
   Group grp{};
   grp.count = count;
   int64_t total_rb = 0;
@@ -661,7 +697,9 @@ hipError_t launch_main(const Config& c, const mxs_problem_view* pv, int count, i
   int start = 0;
   for (int i = 0; i < count; ++i) {
     const int64_t nrb = (pv[i].n + 16 * R - 1) / (16 * R);
-    int64_t share = (budget * nrb + total_rb - 1) / total_rb;  // proportional, at least 1
+    // persistent grid split in proportion to the row blocks (at least one workgroup
+    // each); with several phases every row block gets its own workgroup
+    int64_t share = pp.phases > 1 ? nrb : (budget * nrb + total_rb - 1) / total_rb;
     if (share > nrb) share = nrb;
     if (share < 1) share = 1;
     grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, (int)pv[i].n, (int)nrb,
@@ -670,8 +708,8 @@ hipError_t launch_main(const Config& c, const mxs_problem_view* pv, int count, i
     start += (int)share;
   }
   grp.wg_start[count] = start;
-  gemm_skinny_kernel<R, G><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(waves * kWave), lds,
-                             stream>>>(grp, (int)k, (int)m, nsub);
+  gemm_skinny_kernel<R, G><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(pp.waves * kWave),
+                             pp.lds, stream>>>(grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p);
   return hipGetLastError();
 }
 
@@ -724,13 +762,25 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
     return hipSuccess;
   }
   // Main kernel: 16-byte scale loads need k % 512 == 0 and 16-byte aligned scales; a row
-  // block's bytes (64 rows at most) must fit a 32-bit buffer range; X must fit in LDS.
-  bool aligned = (k % 512 == 0) && k <= (int64_t(1) << 24) && main_lds(k, m, c.R, c.G) <= kMaxLds;
+  // block's bytes (64 rows at most) must fit a 32-bit buffer range.
+  bool aligned = (k % 512 == 0) && k <= (int64_t(1) << 24);
   for (int i = 0; i < count; ++i)
     aligned = aligned && ((reinterpret_cast<uintptr_t>(pv[i].scales) & 15) == 0);
-  if (aligned) {
+  PhasePlan pp;
+  if (aligned && plan_phases(k, m, c.R, c.G, pp)) {
+    // with several phases a workgroup owns one row block: take two row tiles per
+    // block when that still leaves a workgroup per CU
+    if (pp.phases > 1 && c.R == 1) {
+      int64_t nrb2 = 0;
+      for (int i = 0; i < count; ++i) nrb2 += (pv[i].n + 31) / 32;
+      PhasePlan pp2;
+      if (nrb2 >= kCUs && plan_phases(k, m, 2, c.G, pp2)) {
+        c.R = 2;
+        pp = pp2;
+      }
+    }
 #define MXS_RG(RR, GG) \
-  if (c.R == RR && c.G == GG) return launch_main<RR, GG>(c, pv, count, k, m, stream);
+  if (c.R == RR && c.G == GG) return launch_main<RR, GG>(c, pp, pv, count, k, m, stream);
     MXS_RG(1, 4) MXS_RG(1, 8) MXS_RG(2, 4) MXS_RG(2, 8)
 #undef MXS_RG
     return hipErrorInvalidValue;

@@ -58,6 +58,20 @@ def test_ragged_shapes(n, k, m):
 
 
 @pytest.mark.parametrize("n,k,m", [
+    # activations of all of k do not fit in LDS: k is walked in phases, each staged
+    # in turn (two phases; three phases with a short last one; 16 positions)
+    (300, 14336, 8), (100, 28672, 5), (70, 28672, 16), (33, 14336, 7), (257, 28672, 13),
+    (17, 16384, 11),
+])
+def test_phased_k_shapes(n, k, m):
+    say(f"gemm: phased n={n} k={k} m={m}")
+    w = synth.weights(10, n + 3 * k + m, n, k)
+    codes, scales, _ = omx.quantize(w)
+    x = synth.activations(10, n + 3 * k + m, m, k)
+    check_gemm(codes, scales, n, k, x, run_gemm(codes, scales, x), label=f"phased {n}x{k}x{m}")
+
+
+@pytest.mark.parametrize("n,k,m", [
     # m > 32 with k % 128 == 0: the dense kernel (128 weight rows x 80 positions per tile,
     # k split in two halves of alternating 128-k groups)
     (1, 128, 33), (130, 384, 80), (257, 1024, 100), (1000, 2304, 161), (64, 128, 320),
@@ -196,6 +210,7 @@ def test_batched_320_rows_sampled():
     ([17, 300, 1, 4100, 64, 2048, 5, 33, 999], 512, 9),   # ten products: two launches, ragged
     ([130, 70], 1056, 3),                   # k % 512 != 0: one fallback launch per product
     ([300, 129], 1024, 64),                 # m > 32: one dense launch per product
+    ([300, 129], 14336, 8),                 # k walked in two phases, one row block per workgroup
 ])
 def test_grouped_matches_oracle(shapes, k, m):
     say(f"gemm grouped: {shapes} k={k} m={m}")
