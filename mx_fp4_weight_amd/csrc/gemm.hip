@@ -117,7 +117,7 @@ struct Group {
   int count;
 };
 
-template <int R, int G>
+template <int R, int G, int D>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
                                                                          int nsub, int phases,
                                                                          int ngroups_p) {
@@ -296,22 +296,25 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     parity ^= 1;
   };
 
-  Block<R, G> A, B;
+  // D units in flight: a ring of D register blocks, the loop unrolled by D so every
+  // block keeps a fixed role (no register copies, one path into the loop head). The
+  // loads of unit u + D go out as soon as unit u has been computed; past the last
+  // unit the descriptors have no records and nothing is read. The scheduling
+  // barriers keep each prefetch ahead of the next compute's waits.
+  Block<R, G> buf[D];
   stage(0);
-  load(0, A);
-  // the direct loads are counted by vmcnt; wait for them (and the first unit)
+#pragma unroll
+  for (int i = 0; i < D; ++i) load(i, buf[i]);
+  // the direct loads are counted by vmcnt; wait for them (and the first units)
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
-  // The scheduling barriers keep each prefetch ahead of the waits of the compute.
-  for (int u = 0; u < nunits;) {
-    load(u + 1, B);  // past the last unit: a zero-record descriptor, nothing is read
-    __builtin_amdgcn_sched_barrier(0);
-    compute(u, A);
-    if (++u >= nunits) break;
-    load(u + 1, A);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(u, B);
-    ++u;
+  for (int u = 0; u < nunits; u += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (i == 0 || u + i < nunits) compute(u + i, buf[i]);
+      load(u + i + D, buf[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -639,7 +642,8 @@ hipError_t allow_lds(F* kernel, std::atomic<bool>* done) {
 }
 
 struct Config {
-  int R, G;      // row tiles per row block; 128-k groups per wave
+  int R, G;      // row tiles per row block; 128-k groups per unit
+  int D;         // units in flight per wave
   int per_cu;    // resident workgroups per CU targeted by the persistent grid
 };
 
@@ -683,11 +687,11 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp) {
   return false;
 }
 
-template <int R, int G>
+template <int R, int G, int D>
 hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
                        int64_t k, int64_t m, hipStream_t stream) {
   static std::atomic<bool> done[kMaxDevices];
-  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G>, done);
+  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D>, done);
   if (e != hipSuccess) return e;
   Group grp{};
   grp.count = count;
@@ -708,7 +712,7 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     start += (int)share;
   }
   grp.wg_start[count] = start;
-  gemm_skinny_kernel<R, G><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(pp.waves * kWave),
+  gemm_skinny_kernel<R, G, D><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(pp.waves * kWave),
                              pp.lds, stream>>>(grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p);
   return hipGetLastError();
 }
@@ -779,9 +783,9 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
         pp = pp2;
       }
     }
-#define MXS_RG(RR, GG) \
-  if (c.R == RR && c.G == GG) return launch_main<RR, GG>(c, pp, pv, count, k, m, stream);
-    MXS_RG(1, 4) MXS_RG(1, 8) MXS_RG(2, 4) MXS_RG(2, 8)
+#define MXS_RG(RR, GG, DD) \
+  if (c.R == RR && c.G == GG && c.D == DD) return launch_main<RR, GG, DD>(c, pp, pv, count, k, m, stream);
+    MXS_RG(1, 4, 2) MXS_RG(2, 4, 2) MXS_RG(1, 8, 2) MXS_RG(2, 8, 2)
 #undef MXS_RG
     return hipErrorInvalidValue;
   }
@@ -799,13 +803,13 @@ hipError_t launch_cfg(Config c, const uint8_t* codes, const uint8_t* scales, int
   return launch_group(c, &pv, 1, k, m, stream);
 }
 
-// Tile choice from a sweep of (R, G, workgroups per CU) over the 8B- and 70B-class
-// shapes at T = 5: one 16-row tile per row block and 4 groups per sub-slice won or
-// tied everywhere; two resident workgroups per CU for k <= 4096 (LDS allows it), one
-// above.
+// Tile choice from sweeps of (R, G, units in flight, workgroups per CU) over the 8B-
+// and 70B-class shapes at T = 5 and 8: one 16-row tile per row block, 4 groups per
+// unit and two units in flight won or tied everywhere (four units in flight was
+// 5-30% slower); two resident workgroups per CU for k <= 4096, one above.
 Config choose(int64_t n, int64_t k) {
   (void)n;
-  return Config{1, 4, k <= 4096 ? 2 : 1};
+  return Config{1, 4, 2, k <= 4096 ? 2 : 1};
 }
 
 }  // namespace
@@ -828,10 +832,9 @@ hipError_t launch_verify_gemm_grouped(const mxs_problem_view* pv, int count, int
 }
 
 #ifdef MXS_TUNING
-hipError_t launch_verify_gemm_cfg(int R, int G, int per_cu, const uint8_t* codes,
-                                  const uint8_t* scales, int64_t n, int64_t k, const uint16_t* x,
-                                  int64_t m, float* y, hipStream_t stream) {
-  return launch_cfg(Config{R, G, per_cu}, codes, scales, n, k, x, m, y, stream);
+hipError_t launch_verify_gemm_cfg(int R, int G, int D, int per_cu, const mxs_problem_view* pv,
+                                  int count, int64_t k, int64_t m, hipStream_t stream) {
+  return launch_group(Config{R, G, D, per_cu}, pv, count, k, m, stream);
 }
 #endif
 
@@ -839,10 +842,9 @@ hipError_t launch_verify_gemm_cfg(int R, int G, int per_cu, const uint8_t* codes
 
 #ifdef MXS_TUNING
 // Tuning builds only (not part of the product library): explicit tile configuration.
-extern "C" int mxs_tune_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n,
-                                    int64_t k, const uint16_t* x, int64_t m, float* y, int R, int G,
-                                    int per_cu, void* stream) {
-  return (int)mxs::launch_verify_gemm_cfg(R, G, per_cu, codes, scales, n, k, x, m, y,
+extern "C" int mxs_tune_verify_gemm(const mxs::mxs_problem_view* pv, int count, int64_t k,
+                                    int64_t m, int R, int G, int D, int per_cu, void* stream) {
+  return (int)mxs::launch_verify_gemm_cfg(R, G, D, per_cu, pv, count, k, m,
                                           static_cast<hipStream_t>(stream));
 }
 #endif
