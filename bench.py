@@ -479,6 +479,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (T sweep, 70B shapes, batched, full 8B step)")
+    ap.add_argument("--only", choices=["headline", "t_sweep_8b", "shapes_70b_t5", "batched_64x5",
+                                       "full_8b_step"],
+                    help="run one workload alone (profiling); 'headline' = the default line without "
+                         "the secondary workloads")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -522,6 +526,19 @@ def main():
             mats.append((codes, scales, x))
         pool.append(mats)
     ys = [torch.empty((T, n), dtype=torch.float32, device=dev) for _, n, _ in LAYER]
+
+    gen2 = torch.Generator(device=dev)
+    gen2.manual_seed(args.seed * 7919 + 17)
+    extras = (("t_sweep_8b", lambda: t_sweep(torch, mxs, pool, gen2)),
+              ("shapes_70b_t5", lambda: shapes_70b(torch, mxs, synth, gen2)),
+              ("batched_64x5", lambda: batched(torch, mxs, gen2)),
+              ("full_8b_step", lambda: full_8b_step(torch, mxs, gen2)))
+    if args.only and args.only != "headline":
+        # one secondary workload alone (for per-workload profiles)
+        res = dict(extras)[args.only]()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, args.only: res}), flush=True)
+        return
 
     tgt, dft, tok, u = synth.accept_batch(2, 1, KD, V, 3.0, 1.0, seq0=0)
     d_tgt, d_dft = torch.from_numpy(tgt).to(dev), torch.from_numpy(dft).to(dev)
@@ -681,13 +698,8 @@ def main():
                       "layer back to back; average over the four launch types of a layer",
         },
     }
-    if not args.no_extra:
-        gen2 = torch.Generator(device=dev)
-        gen2.manual_seed(args.seed * 7919 + 17)
-        for key, fn in (("t_sweep_8b", lambda: t_sweep(torch, mxs, pool, gen2)),
-                        ("shapes_70b_t5", lambda: shapes_70b(torch, mxs, synth, gen2)),
-                        ("batched_64x5", lambda: batched(torch, mxs, gen2)),
-                        ("full_8b_step", lambda: full_8b_step(torch, mxs, gen2))):
+    if not args.no_extra and not args.only:
+        for key, fn in extras:
             print(f"# workload {key}", file=sys.stderr, flush=True)
             result[key] = fn()
             torch.cuda.synchronize()
