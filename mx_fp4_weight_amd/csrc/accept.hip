@@ -63,14 +63,12 @@ struct Workspace {
   struct Decision* dec;  // [b] n and the statistics of the final draw's rows
   double* zres;    // [b][chunks] chunk totals of the final weights
   double* zp;      // [b][chunks] chunk totals of p_n (zero-residual fallback)
-  double* tauf;    // [b][chunks][kWThreads] per-thread totals of the final weights
-  double* taup;    // [b][chunks][kWThreads] per-thread totals of p_n
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t cmax, csum, cbad, gz, dec, zres, zp, tauf, taup, total;
+  size_t cmax, csum, cbad, gz, dec, zres, zp, total;
 };
 
 inline Layout layout(int64_t b, int64_t kd, int64_t v) {
@@ -92,10 +90,6 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v) {
   off = align256(off + sizeof(double) * b * chunks);
   L.zp = off;
   off = align256(off + sizeof(double) * b * chunks);
-  L.tauf = off;
-  off = align256(off + sizeof(double) * b * chunks * kWThreads);
-  L.taup = off;
-  off = align256(off + sizeof(double) * b * chunks * kWThreads);
   L.total = off;
   return L;
 }
@@ -227,8 +221,11 @@ __device__ inline void thread_weights(const FinalRows& fr, int t0, int v, bool v
 // ---------------------------------------------------------------- final draw
 constexpr int kNone = 0x7fffffff;
 
-// The final token of sequence s by inverse CDF over the chunk totals and the
-// per-thread totals written by the decide workgroups of the sequence.
+// The final token of sequence s by inverse CDF: the chunk totals written by the
+// decide workgroups of the sequence select a chunk; the weights of that chunk are
+// recomputed here exactly as its workgroup computed them (same code, same
+// summation order, so the running totals inside the chunk add up to its stored
+// total) and select a thread, then a token from that thread's registers.
 __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int chunks, int64_t s,
                            const Workspace& ws, const float* __restrict__ uniforms,
                            int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4,
@@ -320,10 +317,13 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int chunks
   if (c < 0) return;       // a valid row always has positive mass
   __syncthreads();
 
-  // ---- level 2: threads of chunk c, from the thread totals its decide workgroup
-  // stored (same values, same scan, so the running totals match its chunk total)
-  const size_t tslot = ((size_t)s * chunks + c) * kWThreads + tid;
-  const double tau = use_p ? ws.taup[tslot] : ws.tauf[tslot];
+  // ---- level 2: threads of chunk c, from their recomputed totals
+  const int t0 = c * kChunk + tid * kWPer;
+  double wf[kWPer], wp[kWPer];
+  thread_weights(fr, t0, v, vec4, wf, wp);
+  double tau = 0.0;
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) tau += use_p ? wp[j] : wf[j];
   const double sincl = block_inclusive_scan_f64<kWThreads>(tau, lds_scan);
   s_incl[tid] = sincl;
   if (tid == 0) {
@@ -339,10 +339,7 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int chunks
   // the crossing thread, or (fallback chunk / rounding) the last thread with positive weight
   const int ti = s_first != kNone ? s_first : s_last;
   if (tid != ti) return;
-  // ---- level 3: the 4 tokens of thread ti
-  const int t0 = c * kChunk + ti * kWPer;
-  double wf[kWPer], wp[kWPer];
-  thread_weights(fr, t0, v, vec4, wf, wp);
+  // ---- level 3: the 4 tokens of thread ti (its weights are already in registers)
   const double before = base + (ti > 0 ? s_incl[ti - 1] : 0.0);
   double run = 0.0;
   int pick = -1, lastpos = -1;
@@ -357,11 +354,15 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int chunks
 }
 
 // ---------------------------------------------------------------- decide + chunk totals
-__global__ __launch_bounds__(kWThreads) void decide_kernel(
+// kPrefetch: small calls fetch every candidate final row with the statistics (one
+// workgroup per CU holds the extra registers); large calls load only the rows the
+// draw needs and fit two workgroups per CU.
+template <bool kPrefetch>
+__global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
     int chunks, Workspace ws, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num,
-    int32_t* __restrict__ flags, int vec4, int prefetch) {
+    int32_t* __restrict__ flags, int vec4) {
   __shared__ double smax[kMaxRows];
   __shared__ double ssum[kMaxRows];
   __shared__ int sbad[kMaxRows];
@@ -377,9 +378,9 @@ __global__ __launch_bounds__(kWThreads) void decide_kernel(
   // thread are fetched now, together with the statistics, so step 3 needs no
   // further memory trip. That reads all 2K+1 rows again, so large batches (where
   // bandwidth, not latency, bounds the call) load only the rows step 3 needs.
-  constexpr int kPre = 9;
+  constexpr int kPre = kPrefetch ? 9 : 1;
   const int t0w = c * kChunk + threadIdx.x * kWPer;
-  const bool pre = prefetch && vec4 && kd <= 4 && t0w + kWPer <= v;
+  const bool pre = kPrefetch && vec4 && kd <= 4 && t0w + kWPer <= v;
   f32x4 prow[kPre];
 #pragma unroll
   for (int r = 0; r < kPre; ++r) {
@@ -548,10 +549,6 @@ __global__ __launch_bounds__(kWThreads) void decide_kernel(
       b += wp[j];
     }
   }
-  // thread totals kept for the final draw, which re-scans them instead of the tokens
-  const size_t tslot = ((size_t)s * chunks + c) * kWThreads + threadIdx.x;
-  ws.tauf[tslot] = a;
-  ws.taup[tslot] = b;
   a = block_inclusive_scan_f64<kWThreads>(a, lds_d);
   b = block_inclusive_scan_f64<kWThreads>(b, lds_d);
   if (threadIdx.x == kWThreads - 1) {
@@ -601,8 +598,6 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
   ws.dec = reinterpret_cast<Decision*>(base + L.dec);
   ws.zres = reinterpret_cast<double*>(base + L.zres);
   ws.zp = reinterpret_cast<double*>(base + L.zp);
-  ws.tauf = reinterpret_cast<double*>(base + L.tauf);
-  ws.taup = reinterpret_cast<double*>(base + L.taup);
   const int64_t rows = (int64_t)b * (2 * kd + 1);
   dim3 g1((unsigned)rows, (unsigned)chunks);
   if (vec4)
@@ -612,10 +607,13 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // prefetch of all candidate rows while the batch's logits are at most 16 MB
-  const int prefetch = (int64_t)b * (2 * kd + 1) * v * 4 <= (int64_t(16) << 20) ? 1 : 0;
-  decide_kernel<<<dim3((unsigned)chunks, (unsigned)b), dim3(kWThreads), 0, stream>>>(
-      target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4,
-      prefetch);
+  const bool prefetch = (int64_t)b * (2 * kd + 1) * v * 4 <= (int64_t(16) << 20);
+  if (prefetch)
+    decide_kernel<true><<<dim3((unsigned)chunks, (unsigned)b), dim3(kWThreads), 0, stream>>>(
+        target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4);
+  else
+    decide_kernel<false><<<dim3((unsigned)chunks, (unsigned)b), dim3(kWThreads), 0, stream>>>(
+        target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   sample_kernel<<<dim3((unsigned)b), dim3(kWThreads), 0, stream>>>(target, draft, uniforms, kd, v,
