@@ -85,6 +85,11 @@ __device__ inline void lds_barrier() {
 
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // past any num_records: the load reads 0
 
+// s_waitcnt immediate that waits until at most n (< 64) vector memory operations
+// are outstanding and leaves the export and LDS/scalar counters alone: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // X staged in LDS in MFMA-operand order. The 16-byte chunk q (8 bf16) of
 // activation row t goes to unit ((grp*4 + d)*mt + t)*4 + g with grp = q/16,
 // g = (q/4)%4, d = q%4: for one group and MFMA slice d, the lanes (t, g) read
@@ -323,18 +328,17 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
 //
 // With m = 320 the contraction does ~1000 FLOP per weight byte, so the matrix
 // cores, not HBM, bound it. A workgroup owns a tile of 128 weight rows × 16·MC
-// activation rows and all of k. Its four waves form 2 row halves × 2 k halves:
-// wave (rh, kh) decodes the weights of rows [64·rh, 64·rh + 64) of the tile in
-// registers (4 A operands of 16 rows, loaded straight from HBM, one MX block
-// per lane as in the skinny kernel) and multiplies them with the MC B operands
-// of every 128-k group g with g % 2 == kh. The activations of a 256-k window
-// (both halves) are staged in LDS once per workgroup, double-buffered, and each
-// B operand read from LDS feeds 4 MFMAs. The two k halves are summed in LDS at
-// the end, in a fixed order. Tiles are mapped to XCDs so that the position
-// tiles of one weight tile run on the same XCD and share its L2: the weights
-// come from HBM once.
+// activation rows and all of k. Its eight waves (two per SIMD) form 2 row halves ×
+// 4 k quarters: wave (rh, kq) decodes the weights of rows [64·rh, 64·rh + 64) of
+// the tile in registers (4 A operands of 16 rows, loaded straight from HBM, one MX
+// block per lane as in the skinny kernel) and multiplies them with the MC B
+// operands of every 128-k group g with g % 4 == kq. The activations of each 512-k
+// window are staged in LDS by direct global-to-LDS loads, double-buffered, and
+// each B operand read feeds 4 MFMAs. The k quarters are summed in LDS at the end
+// in a fixed order. Tiles are mapped to XCDs so that the position tiles of one
+// weight tile run on the same XCD and share its L2: the weights come from HBM once.
 constexpr int kDenseRows = 128;
-constexpr int kDenseThreads = 256;
+constexpr int kDenseThreads = 512;
 
 template <int MC>
 __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
@@ -342,7 +346,12 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
     const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m, int n_tiles,
     int m_tiles, int y_vec4) {
   constexpr int BM = 16 * MC;
-  constexpr int kUnits = 2 * 4 * BM * 4;  // 16-byte LDS units of one 256-k window
+  constexpr int kWaves = kDenseThreads / kWave;
+  // Activations of one 512-k window in LDS: row t of the tile holds its 64 chunks of
+  // 8 bf16 at units t*64 + (q ^ (t & 15)). A row is 64 consecutive units, so one
+  // direct global-to-LDS load (lane L writes unit base + L) stages it; the XOR
+  // spreads the 16 rows an operand read touches over distinct banks.
+  constexpr int kUnits = BM * 64;
   extern __shared__ u32x4 smem[];
   // workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight tile
   const int xcd = (int)blockIdx.x & 7;
@@ -352,14 +361,15 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   if (nt >= n_tiles) return;  // uniform for the workgroup, before any barrier
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // wave-uniform (a scalar register): the load-to-LDS destination depends on it
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int rh = wave & 1;
-  const int kh = wave >> 1;
+  const int kq = wave >> 1;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int kb = k >> 5;
   const int ngroups = kb >> 2;
-  const int nsteps = (ngroups + 1) >> 1;
+  const int nsteps = (ngroups + 3) >> 2;  // 512-k windows
   const uint32_t row_bytes = (uint32_t)(k >> 1);
   const int row0 = nt * kDenseRows;
   const int rows = min(kDenseRows, n - row0);
@@ -370,13 +380,13 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)mrows * (uint32_t)k * 2u);
 
-  // codes and scales of this wave's 4 row tiles for the group of step s
+  // codes and scales of this wave's 4 row tiles for its group of step s
   struct W4 {
     u32x4 c[4];
     uint32_t s[4];
   };
   auto load_w = [&](int s, W4& w) {
-    const int grp = 2 * s + kh;
+    const int grp = 4 * s + kq;
     const int blk = grp * 4 + g;
     const bool ok = grp < ngroups;
 #pragma unroll
@@ -388,31 +398,20 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
       w.s[i] = __builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
     }
   };
-  // activations of the 256-k window of step s: chunk q (8 bf16) of tile row t goes to
-  // unit ((half*4 + d)*BM + t)*4 + gg with half = q/16, gg = (q/4)%4, d = q%4
-  constexpr int kChunks = BM * 32;
-  static_assert(kChunks % kDenseThreads == 0, "every thread stages the same number of chunks");
-  constexpr int kPerThread = kChunks / kDenseThreads;
-  u32x4 xs[kPerThread];
-  auto load_x = [&](int s) {
+  // Stage the window of step s into buffer buf: wave w stages tile rows w, w + 8, ...;
+  // lane L fetches the chunk that belongs at unit 64t + L. Rows past m and groups
+  // past k are outside the descriptor and read as zero.
+  static_assert(BM % kWaves == 0, "each wave stages the same number of rows");
+  auto stage_x = [&](int s, int buf) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int idx = (int)threadIdx.x + i * kDenseThreads;
-      const int t = idx >> 5;
-      const int q = idx & 31;
-      const bool ok = 2 * s + (q >> 4) < ngroups;
-      const uint32_t off = ok ? ((uint32_t)t * (uint32_t)k + (uint32_t)(s * 256 + q * 8)) * 2u : kOutOfRange;
-      xs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-    }
-  };
-  auto store_x = [&](int buf) {
-    u32x4* dst = smem + buf * kUnits;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int idx = (int)threadIdx.x + i * kDenseThreads;
-      const int t = idx >> 5;
-      const int q = idx & 31;
-      dst[(((q >> 4) * 4 + (q & 3)) * BM + t) * 4 + ((q >> 2) & 3)] = xs[i];
+    for (int i = 0; i < BM / kWaves; ++i) {
+      const int t = wave + kWaves * i;
+      const int q = lane ^ (t & 15);
+      const bool ok = 4 * s + (q >> 4) < ngroups;
+      const uint32_t off = ok ? ((uint32_t)t * (uint32_t)k + (uint32_t)(s * 512 + q * 8)) * 2u : kOutOfRange;
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(smem + buf * kUnits + 64 * t);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
     }
   };
 
@@ -427,63 +426,85 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
     float sf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sf[i] = e8m0_to_f32(w.s[i] & 0xffu);
+    // B operand of slice d, column tile c: lane (r, g) takes chunk kq*16 + 4g + d of
+    // tile row 16c + r (the k permutation of the skinny kernel), stored at slot
+    // (kq*16 + 4g + d) ^ r of that row. The operands of slice d + 1 are read before
+    // the MFMAs of slice d.
+    const int xq = (kq * 16 + 4 * g) ^ r;
+    const u32x4* bsrc = src + r * 64;
+    bf16x8 bb[2][MC];
+#pragma unroll
+    for (int c = 0; c < MC; ++c) bb[0][c] = __builtin_bit_cast(bf16x8, bsrc[16 * c * 64 + xq]);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      bf16x8 bb[MC];
+      if (d < 3) {
 #pragma unroll
-      for (int c = 0; c < MC; ++c)
-        bb[c] = __builtin_bit_cast(bf16x8, src[((kh * 4 + d) * BM + 16 * c + r) * 4 + g]);
+        for (int c = 0; c < MC; ++c)
+          bb[(d + 1) & 1][c] = __builtin_bit_cast(bf16x8, bsrc[16 * c * 64 + (xq ^ (d + 1))]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 a = decode8(w.c[i][d], sf[i]);
 #pragma unroll
-        for (int c = 0; c < MC; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[c], acc[i][c], 0, 0, 0);
+        for (int c = 0; c < MC; ++c)
+          acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[d & 1][c], acc[i][c], 0, 0, 0);
       }
     }
   };
 
+  // The staging and weight loads of step s + 1 are issued before the MFMAs of step
+  // s (scheduling barriers keep them there). After the compute each wave waits for
+  // its staging loads only (the weight loads issued after them stay in flight; the
+  // counter retires in order), then the barrier makes every wave's rows visible.
+  constexpr int kWLoads = 8;  // VMEM loads of one load_w: 4 code + 4 scale loads
   W4 wa, wb;
-  load_x(0);
+  stage_x(0, 0);
   load_w(0, wa);
-  store_x(0);
+  __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
-  // The prefetch of step s + 1 is issued before the MFMAs of step s; the scheduling
-  // barriers keep the compiler from sinking those loads below the compute.
-  for (int s = 0; s < nsteps;) {
-    load_x(s + 1);
+  // Two steps per iteration and a single exit, so the accumulators keep their
+  // registers across the loop; with an odd step count the last step reads only
+  // out-of-range (zero) weights and adds nothing.
+  for (int s = 0; s < nsteps; s += 2) {
+    stage_x(s + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     load_w(s + 1, wb);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s & 1, wa);
+    compute(0, wa);
     __builtin_amdgcn_sched_barrier(0);
-    store_x((s + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
     lds_barrier();
-    if (++s >= nsteps) break;
-    load_x(s + 1);
-    load_w(s + 1, wa);
+    stage_x(s + 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s & 1, wb);
+    load_w(s + 2, wa);
     __builtin_amdgcn_sched_barrier(0);
-    store_x((s + 1) & 1);
+    compute(1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
     lds_barrier();
-    ++s;
   }
 
-  // sum the two k halves in LDS (the staging buffers are free after the last barrier)
-  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [2 rh][4][MC][64]
-  if (kh == 1) {
+  // sum the four k quarters in LDS (the staging buffers are free once every load
+  // has landed: the last iteration's loads target windows past k)
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [3 kq][2 rh][4][MC][64]
+  if (kq > 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int c = 0; c < MC; ++c) red[((rh * 4 + i) * MC + c) * kWave + lane] = acc[i][c];
+      for (int c = 0; c < MC; ++c) red[((((kq - 1) * 2 + rh) * 4 + i) * MC + c) * kWave + lane] = acc[i][c];
   }
   lds_barrier();
-  if (kh == 0) {
+  if (kq == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int orow = row0 + rh * 64 + 16 * i + 4 * g;  // lane holds C[4g + e][r]
 #pragma unroll
       for (int c = 0; c < MC; ++c) {
-        const f32x4 sum = acc[i][c] + red[((rh * 4 + i) * MC + c) * kWave + lane];
+        f32x4 sum = acc[i][c];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) sum += red[(((q * 2 + rh) * 4 + i) * MC + c) * kWave + lane];
         const int tt = t0 + 16 * c + r;
         if (tt < m) {
           float* yp = y + (size_t)tt * (size_t)n + orow;
@@ -748,7 +769,7 @@ hipError_t launch_dense(const mxs_problem_view& p, int64_t k, int64_t m, hipStre
   const int n_tiles = (int)((p.n + kDenseRows - 1) / kDenseRows);
   const int m_tiles = (int)((m + 16 * MC - 1) / (16 * MC));
   const int64_t wgs = (int64_t)((n_tiles + 7) / 8) * 8 * m_tiles;
-  const size_t lds = 2 * sizeof(u32x4) * (2 * 4 * 16 * MC * 4);
+  const size_t lds = 2 * sizeof(u32x4) * (16 * MC * 64);
   gemm_dense_kernel<MC><<<dim3((unsigned)wgs), dim3(kDenseThreads), lds, stream>>>(
       p.codes, p.scales, p.x, p.y, (int)p.n, (int)k, (int)m, n_tiles, m_tiles, y_vec4_ok(p.y, p.n));
   return hipGetLastError();
