@@ -11,17 +11,18 @@
 //   stats   grid (rows, chunks): for every 4096-logit chunk of every target
 //           and draft row, the chunk max (exact, fp32) and sum exp(z - max)
 //           in fp64. This is the one full read of the logits.
-//   decide  grid (chunks, sequences): every workgroup combines its sequence's
-//           chunk statistics into (max, sum) per row, forms p_i(x_i) and
-//           q_i(x_i) in fp64 from the logits the stats kernel gathered (one
-//           lane per draft position), takes n = first rejection with a
-//           ballot, then sums the final weights w (residual or bonus row)
-//           over its own chunk, keeping every thread's total. Chunk 0 writes
-//           the decisions.
-//   sample  one workgroup per sequence: a block scan of the chunk totals
-//           finds the chunk holding u_K·Z, a block scan of that chunk's stored
-//           thread totals finds the thread, and that thread recomputes its 4
-//           tokens' weights to find t*.
+//   decide  grid (pieces, sequences), 1024-logit pieces: every workgroup
+//           combines its sequence's chunk statistics into (max, sum) per row,
+//           forms p_i(x_i) and q_i(x_i) in fp64 from the logits the stats
+//           kernel gathered (one lane per draft position), takes n = first
+//           rejection with a ballot, then sums the final weights w (residual
+//           or bonus row) over its own piece. Piece 0 writes the decisions.
+//   sample  one workgroup per sequence: a block scan of the piece totals
+//           finds the piece holding u_K·Z; its weights are recomputed exactly
+//           as decide computed them, a block scan of the thread totals finds
+//           the thread, and that thread's 4 weights give t*.
+// The fp64 exponentials bound decide and sample at small batches, so their
+// pieces are small: many workgroups share the work of one sequence.
 // All probabilities and prefix sums are fp64; the result can differ from an
 // exact-arithmetic draw only when u_K·Z lies within ~1e-15·Z of an interval
 // end. Rounding guards: if no crossing is found where the level above
@@ -38,14 +39,16 @@
 namespace mxs {
 namespace {
 
-// stats: 256 threads x 16 logits; decide/sample: 1024 threads x 4 logits. Both
-// cover the same 4096-logit chunk, so the chunk totals of the final weights
-// written by decide are the ones sample walks.
+// stats: 256 threads x 16 logits per 4096-logit chunk. decide / sample: 256
+// threads x 4 logits per 1024-logit piece; both walk the same pieces, so the
+// piece totals of the final weights written by decide are the ones sample scans.
 constexpr int kThreads = 256;
 constexpr int kPer = 16;
 constexpr int kChunk = kThreads * kPer;  // 4096 logits per chunk
-constexpr int kWThreads = 1024;
-constexpr int kWPer = kChunk / kWThreads;  // 4 logits per thread in decide / sample
+constexpr int kWThreads = 256;
+constexpr int kWPer = 4;                   // logits per thread in decide / sample
+constexpr int kPiece = kWThreads * kWPer;  // 1024 logits per piece
+constexpr int kPassBatch = 3;              // statistics passes whose loads decide keeps in flight
 constexpr int kMaxRows = 65;               // 2 * 32 + 1 rows per sequence
 
 struct Decision {
@@ -61,8 +64,8 @@ struct Workspace {
   int32_t* cbad;   // [rows][chunks]
   float* gz;       // [rows] logit of the row's draft token (written by the chunk holding it)
   struct Decision* dec;  // [b] n and the statistics of the final draw's rows
-  double* zres;    // [b][chunks] chunk totals of the final weights
-  double* zp;      // [b][chunks] chunk totals of p_n (zero-residual fallback)
+  double* zres;    // [b][pieces] piece totals of the final weights
+  double* zp;      // [b][pieces] piece totals of p_n (zero-residual fallback)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -74,6 +77,7 @@ struct Layout {
 inline Layout layout(int64_t b, int64_t kd, int64_t v) {
   const int64_t rows = b * (2 * kd + 1);
   const int64_t chunks = (v + kChunk - 1) / kChunk;
+  const int64_t pieces = (v + kPiece - 1) / kPiece;
   Layout L;
   size_t off = 0;
   L.cmax = off;
@@ -87,9 +91,9 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v) {
   L.dec = off;
   off = align256(off + sizeof(Decision) * b);
   L.zres = off;
-  off = align256(off + sizeof(double) * b * chunks);
+  off = align256(off + sizeof(double) * b * pieces);
   L.zp = off;
-  off = align256(off + sizeof(double) * b * chunks);
+  off = align256(off + sizeof(double) * b * pieces);
   L.total = off;
   return L;
 }
@@ -221,64 +225,94 @@ __device__ inline void thread_weights(const FinalRows& fr, int t0, int v, bool v
 // ---------------------------------------------------------------- final draw
 constexpr int kNone = 0x7fffffff;
 
-// The final token of sequence s by inverse CDF: the chunk totals written by the
-// decide workgroups of the sequence select a chunk; the weights of that chunk are
-// recomputed here exactly as its workgroup computed them (same code, same
-// summation order, so the running totals inside the chunk add up to its stored
-// total) and select a thread, then a token from that thread's registers.
-__device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int chunks, int64_t s,
-                           const Workspace& ws, const float* __restrict__ uniforms,
-                           int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4,
-                           double* lds_scan, double* s_incl, int& s_first, int& s_last) {
-  const int tid = threadIdx.x;
-  // ---- level 1: chunks. Running totals of the chunk totals; Z is the last one.
-  bool use_p = false;
-  double Z = 0.0, base = 0.0;
-  int c = kNone;
-  bool found = false;
-  if (tid == 0) {
-    s_first = kNone;
-    s_last = -1;
+// The final token of sequence s by inverse CDF, in two levels that every thread
+// of the workgroup enters. select_piece scans the piece totals written by the
+// decide workgroups of the sequence and picks the piece holding u_K·Z;
+// select_token scans the thread totals of that piece's final weights (computed
+// exactly as its decide workgroup computed them: same code, same summation
+// order, so the running totals inside the piece add up to its stored total),
+// picks the thread, and that thread's 4 weights give the token.
+struct PieceChoice {
+  int c;        // chosen piece, or -1 when no piece has positive weight
+  bool found;   // u_K·Z crossed a running total (otherwise c is the last positive piece)
+  bool use_p;   // zero residual mass: the draw is from p_n
+  double base;  // running total before piece c
+  double uz;    // u_K·Z
+};
+
+constexpr int kWWaves = kWThreads / kWave;
+
+// Over the workgroup, index base + threadIdx.x: the first index whose thread has
+// first_cond (kNone if none) and the last whose thread has last_cond (-1 if none).
+// One ballot per wave and the per-wave answers through LDS (lds: 2 * kWWaves
+// ints); the barriers inside also publish LDS writes made before the call.
+__device__ inline int2 block_first_last(bool first_cond, bool last_cond, int base, int* lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const unsigned long long m1 = __ballot(first_cond);
+  const unsigned long long m2 = __ballot(last_cond);
+  if (lane == 0) {
+    lds[w] = m1 ? base + w * kWave + __builtin_ctzll(m1) : kNone;
+    lds[kWWaves + w] = m2 ? base + w * kWave + 63 - __builtin_clzll(m2) : -1;
   }
-  if (chunks <= kWThreads) {
-    // one chunk per thread: both totals loaded once, one scan (two on the zero-residual path)
-    const double zres = tid < chunks ? ws.zres[s * chunks + tid] : 0.0;
-    const double zpv = tid < chunks ? ws.zp[s * chunks + tid] : 0.0;
-    double incl = block_inclusive_scan_f64<kWThreads>(zres, lds_scan);
+  __syncthreads();
+  int2 r = make_int2(kNone, -1);
+#pragma unroll
+  for (int i = 0; i < kWWaves; ++i) {
+    r.x = min(r.x, lds[i]);
+    r.y = max(r.y, lds[kWWaves + i]);
+  }
+  __syncthreads();
+  return r;
+}
+
+// zres0 / zp0: this thread's piece totals, loaded by the caller when
+// pieces <= kWThreads; u_last: the sequence's final uniform u_K. Loading them at
+// kernel entry keeps global loads from waiting behind the block barriers here.
+// flags may be null (the zero-residual flag is then left to another workgroup).
+__device__ PieceChoice select_piece(int n, int kd, int pieces, int64_t s, const Workspace& ws,
+                                    float u_last, int32_t* __restrict__ flags, double zres0,
+                                    double zp0, double* lds_scan, double* s_incl, int* s_fl) {
+  const int tid = threadIdx.x;
+  PieceChoice pc;
+  pc.use_p = false;
+  pc.base = 0.0;
+  double Z = 0.0;
+  int c = kNone, last = -1;
+  if (pieces <= kWThreads) {
+    // one piece per thread: both totals loaded once, one scan (two on the zero-residual path)
+    double incl = block_inclusive_scan_f64<kWThreads>(zres0, lds_scan);
     if (tid == kWThreads - 1) s_incl[0] = incl;
     __syncthreads();
     Z = s_incl[0];
-    double zc = zres;
+    double zc = zres0;
     __syncthreads();
     if (!(Z > 0.0)) {  // zero residual mass (rounding): draw from p_n instead
-      use_p = true;
-      zc = zpv;
-      incl = block_inclusive_scan_f64<kWThreads>(zpv, lds_scan);
+      pc.use_p = true;
+      zc = zp0;
+      incl = block_inclusive_scan_f64<kWThreads>(zp0, lds_scan);
       if (tid == kWThreads - 1) s_incl[0] = incl;
       __syncthreads();
       Z = s_incl[0];
       __syncthreads();
       if (n < kd && tid == 0) raise_flag(flags, MXS_FLAG_RESIDUAL_ZERO);
     }
-    const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
+    const double uz = (double)u_last * Z;
     s_incl[tid] = incl;
-    if (tid < chunks && zc > 0.0) {
-      if (uz < incl) atomicMin(&s_first, tid);
-      atomicMax(&s_last, tid);
-    }
-    __syncthreads();
-    c = s_first;
-    found = c != kNone;
-    if (found) base = c > 0 ? s_incl[c - 1] : 0.0;
+    const bool pos = tid < pieces && zc > 0.0;
+    const int2 fl = block_first_last(pos && uz < incl, pos, 0, s_fl);
+    c = fl.x;
+    last = fl.y;
+    if (c != kNone) pc.base = c > 0 ? s_incl[c - 1] : 0.0;
   } else {
-    // many chunks: rounds of kWThreads chunk totals with a carry
-    const double* zr = ws.zres + s * chunks;
+    // many pieces: rounds of kWThreads piece totals with a carry
+    const double* zr = ws.zres + s * pieces;
     for (int pass = 0; pass < 2; ++pass) {
       double carry = 0.0;
-      for (int c0 = 0; c0 < chunks; c0 += kWThreads) {
+      for (int c0 = 0; c0 < pieces; c0 += kWThreads) {
         const int cc = c0 + tid;
         const double incl =
-            carry + block_inclusive_scan_f64<kWThreads>(cc < chunks ? zr[cc] : 0.0, lds_scan);
+            carry + block_inclusive_scan_f64<kWThreads>(cc < pieces ? zr[cc] : 0.0, lds_scan);
         if (tid == kWThreads - 1) s_incl[0] = incl;
         __syncthreads();
         carry = s_incl[0];
@@ -286,74 +320,85 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int chunks
       }
       Z = carry;
       if (Z > 0.0 || pass == 1) break;
-      use_p = true;
-      zr = ws.zp + s * chunks;
+      pc.use_p = true;
+      zr = ws.zp + s * pieces;
       if (n < kd && tid == 0) raise_flag(flags, MXS_FLAG_RESIDUAL_ZERO);
     }
-    const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
+    const double uz = (double)u_last * Z;
     double carry = 0.0;
-    for (int c0 = 0; c0 < chunks; c0 += kWThreads) {
+    for (int c0 = 0; c0 < pieces; c0 += kWThreads) {
       const int cc = c0 + tid;
-      const double zc = cc < chunks ? zr[cc] : 0.0;
+      const double zc = cc < pieces ? zr[cc] : 0.0;
       const double incl = carry + block_inclusive_scan_f64<kWThreads>(zc, lds_scan);
       s_incl[tid] = incl;
-      if (cc < chunks && zc > 0.0) {
-        if (uz < incl) atomicMin(&s_first, cc);
-        atomicMax(&s_last, cc);
-      }
-      __syncthreads();
-      c = s_first;
-      if (c != kNone) {
-        base = c > c0 ? s_incl[c - c0 - 1] : carry;
+      const bool pos = cc < pieces && zc > 0.0;
+      const int2 fl = block_first_last(pos && uz < incl, pos, c0, s_fl);
+      last = max(last, fl.y);
+      if (fl.x != kNone) {
+        c = fl.x;
+        pc.base = c > c0 ? s_incl[c - c0 - 1] : carry;
         break;
       }
       carry = s_incl[kWThreads - 1];
       __syncthreads();
     }
-    found = c != kNone;
   }
-  const double uz = (double)uniforms[(size_t)s * (kd + 1) + kd] * Z;
-  if (!found) c = s_last;  // no crossing (u >= 1 or rounding): last chunk with positive weight
-  if (c < 0) return;       // a valid row always has positive mass
+  pc.uz = (double)u_last * Z;
+  pc.found = c != kNone;
+  // no crossing (u >= 1 or rounding): the last piece with positive weight (-1 if none;
+  // a valid row always has positive mass)
+  pc.c = pc.found ? c : last;
   __syncthreads();
+  return pc;
+}
 
-  // ---- level 2: threads of chunk c, from their recomputed totals
-  const int t0 = c * kChunk + tid * kWPer;
-  double wf[kWPer], wp[kWPer];
-  thread_weights(fr, t0, v, vec4, wf, wp);
+// Level 2 and 3 inside piece pc.c; wf / wp are this thread's 4 weights of that
+// piece (tokens t0 .. t0+3). The thread that owns the token writes it.
+__device__ void select_token(const PieceChoice& pc, int n, int kd, int64_t s, int t0,
+                             const double (&wf)[kWPer], const double (&wp)[kWPer],
+                             int32_t* __restrict__ out_tokens, double* lds_scan, double* s_incl,
+                             int* s_fl) {
+  const int tid = threadIdx.x;
   double tau = 0.0;
 #pragma unroll
-  for (int j = 0; j < kWPer; ++j) tau += use_p ? wp[j] : wf[j];
+  for (int j = 0; j < kWPer; ++j) tau += pc.use_p ? wp[j] : wf[j];
   const double sincl = block_inclusive_scan_f64<kWThreads>(tau, lds_scan);
   s_incl[tid] = sincl;
-  if (tid == 0) {
-    s_first = kNone;
-    s_last = -1;
-  }
-  __syncthreads();
-  if (tau > 0.0) {
-    if (found && uz < base + sincl) atomicMin(&s_first, tid);
-    atomicMax(&s_last, tid);
-  }
-  __syncthreads();
-  // the crossing thread, or (fallback chunk / rounding) the last thread with positive weight
-  const int ti = s_first != kNone ? s_first : s_last;
+  const bool pos = tau > 0.0;
+  const int2 fl = block_first_last(pos && pc.found && pc.uz < pc.base + sincl, pos, 0, s_fl);
+  // the crossing thread, or (fallback piece / rounding) the last thread with positive weight
+  const int ti = fl.x != kNone ? fl.x : fl.y;
   if (tid != ti) return;
   // ---- level 3: the 4 tokens of thread ti (its weights are already in registers)
-  const double before = base + (ti > 0 ? s_incl[ti - 1] : 0.0);
+  const double before = pc.base + (ti > 0 ? s_incl[ti - 1] : 0.0);
   double run = 0.0;
   int pick = -1, lastpos = -1;
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
-    const double w = use_p ? wp[j] : wf[j];
+    const double w = pc.use_p ? wp[j] : wf[j];
     run += w;
     if (w > 0.0) lastpos = t0 + j;
-    if (found && pick < 0 && w > 0.0 && uz < before + run) pick = t0 + j;
+    if (pc.found && pick < 0 && w > 0.0 && pc.uz < before + run) pick = t0 + j;
   }
   out_tokens[(size_t)s * (kd + 1) + n] = pick >= 0 ? pick : lastpos;
 }
 
-// ---------------------------------------------------------------- decide + chunk totals
+// The whole draw for one sequence by one workgroup (the sample kernel).
+__device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces, int64_t s,
+                           const Workspace& ws, float u_last,
+                           int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4,
+                           double zres0, double zp0, double* lds_scan, double* s_incl,
+                           int* s_fl) {
+  const PieceChoice pc = select_piece(n, kd, pieces, s, ws, u_last, flags, zres0, zp0, lds_scan,
+                                      s_incl, s_fl);
+  if (pc.c < 0) return;
+  const int t0 = pc.c * kPiece + (int)threadIdx.x * kWPer;
+  double wf[kWPer], wp[kWPer];
+  thread_weights(fr, t0, v, vec4, wf, wp);
+  select_token(pc, n, kd, s, t0, wf, wp, out_tokens, lds_scan, s_incl, s_fl);
+}
+
+// ---------------------------------------------------------------- decide + piece totals
 // kPrefetch: small calls fetch every candidate final row with the statistics (one
 // workgroup per CU holds the extra registers); large calls load only the rows the
 // draw needs and fit two workgroups per CU.
@@ -361,8 +406,8 @@ template <bool kPrefetch>
 __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
-    int chunks, Workspace ws, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num,
-    int32_t* __restrict__ flags, int vec4) {
+    int chunks, int pieces, Workspace ws, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ out_num, int32_t* __restrict__ flags, int vec4) {
   __shared__ double smax[kMaxRows];
   __shared__ double ssum[kMaxRows];
   __shared__ int sbad[kMaxRows];
@@ -379,7 +424,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   // further memory trip. That reads all 2K+1 rows again, so large batches (where
   // bandwidth, not latency, bounds the call) load only the rows step 3 needs.
   constexpr int kPre = kPrefetch ? 9 : 1;
-  const int t0w = c * kChunk + threadIdx.x * kWPer;
+  const int t0w = c * kPiece + threadIdx.x * kWPer;
   const bool pre = kPrefetch && vec4 && kd <= 4 && t0w + kWPer <= v;
   f32x4 prow[kPre];
 #pragma unroll
@@ -399,30 +444,46 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   }
 
   // 1. per-row max and sum over the chunk statistics. With seg = chunks rounded up
-  //    to a power of two (<= 64), thread j*seg + c loads chunk c of row j and the
-  //    row is reduced by xor-shuffles inside its segment: one round for all rows.
+  //    to a power of two (<= 64), in pass r thread t loads chunk t % seg of row
+  //    r * (kWThreads / seg) + t / seg, and each row is reduced by xor-shuffles
+  //    inside its segment; the loads of up to kPassBatch passes are issued together.
   int seg = 1;
   while (seg < chunks) seg <<= 1;
-  if (seg <= kWave && per_seq * seg <= kWThreads) {
-    const int j = threadIdx.x / seg;
+  if (seg <= kWave) {
+    const int rpp = kWThreads / seg;  // rows per pass
+    const int passes = (per_seq + rpp - 1) / rpp;
     const int cc = threadIdx.x % seg;
-    const bool live = j < per_seq && cc < chunks;
-    const size_t o = ((size_t)s * per_seq + (live ? j : 0)) * chunks + (live ? cc : 0);
-    float cm = live ? ws.cmax[o] : -INFINITY;
-    double cs = live ? ws.csum[o] : 0.0;
-    int bad = live ? ws.cbad[o] : 0;
-    float m = cm;
-    for (int off = 1; off < seg; off <<= 1) {
-      m = fmaxf(m, __shfl_xor(m, off));
-      bad |= __shfl_xor(bad, off);
-    }
-    bad |= (m == -INFINITY);
-    double sum = (!bad && cs > 0.0) ? cs * exp_neg_f64((double)cm - (double)m) : 0.0;
-    for (int off = 1; off < seg; off <<= 1) sum += __shfl_xor(sum, off);
-    if (j < per_seq && cc == 0) {
-      smax[j] = (double)m;
-      ssum[j] = sum;
-      sbad[j] = bad;
+    for (int p0 = 0; p0 < passes; p0 += kPassBatch) {
+      float cm[kPassBatch];
+      double cs[kPassBatch];
+      int cb[kPassBatch];
+#pragma unroll
+      for (int r = 0; r < kPassBatch; ++r) {
+        const int j = (p0 + r) * rpp + (int)threadIdx.x / seg;
+        const bool live = j < per_seq && cc < chunks;
+        const size_t o = ((size_t)s * per_seq + (live ? j : 0)) * chunks + (live ? cc : 0);
+        cm[r] = live ? ws.cmax[o] : -INFINITY;
+        cs[r] = live ? ws.csum[o] : 0.0;
+        cb[r] = live ? ws.cbad[o] : 0;
+      }
+#pragma unroll
+      for (int r = 0; r < kPassBatch; ++r) {
+        const int j = (p0 + r) * rpp + (int)threadIdx.x / seg;
+        float m = cm[r];
+        int bad = cb[r];
+        for (int off = 1; off < seg; off <<= 1) {
+          m = fmaxf(m, __shfl_xor(m, off));
+          bad |= __shfl_xor(bad, off);
+        }
+        bad |= (m == -INFINITY);
+        double sum = (!bad && cs[r] > 0.0) ? cs[r] * exp_neg_f64((double)cm[r] - (double)m) : 0.0;
+        for (int off = 1; off < seg; off <<= 1) sum += __shfl_xor(sum, off);
+        if (j < per_seq && cc == 0) {
+          smax[j] = (double)m;
+          ssum[j] = sum;
+          sbad[j] = bad;
+        }
+      }
     }
   } else {
     for (int j = wave; j < per_seq; j += kWThreads / kWave) {
@@ -513,7 +574,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   }
   __syncthreads();
 
-  // 3. chunk total of the final weights: thread totals in token order, then
+  // 3. piece total of the final weights: thread totals in token order, then
   // the same block scan the sample kernel uses, so both see identical totals
   const int n = s_n;
   double a = 0.0, b = 0.0;
@@ -552,20 +613,25 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   a = block_inclusive_scan_f64<kWThreads>(a, lds_d);
   b = block_inclusive_scan_f64<kWThreads>(b, lds_d);
   if (threadIdx.x == kWThreads - 1) {
-    ws.zres[s * chunks + c] = a;
-    ws.zp[s * chunks + c] = b;
+    ws.zres[s * pieces + c] = a;
+    ws.zp[s * pieces + c] = b;
   }
 }
 
 // ---------------------------------------------------------------- sample
 __global__ __launch_bounds__(kWThreads) void sample_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
-    const float* __restrict__ uniforms, int kd, int v, int chunks, Workspace ws,
+    const float* __restrict__ uniforms, int kd, int v, int pieces, Workspace ws,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4) {
   __shared__ double lds_scan[kWThreads / kWave];
   __shared__ double s_incl[kWThreads];
-  __shared__ int s_first, s_last;
+  __shared__ int s_fl[2 * kWWaves];
   const int64_t s = blockIdx.x;
+  // the piece totals do not depend on the decision: load them with it
+  const bool mine = pieces <= kWThreads && (int)threadIdx.x < pieces;
+  const double zres0 = mine ? ws.zres[s * pieces + threadIdx.x] : 0.0;
+  const double zp0 = mine ? ws.zp[s * pieces + threadIdx.x] : 0.0;
+  const float u_last = uniforms[(size_t)s * (kd + 1) + kd];
   const Decision d = ws.dec[s];
   if (d.n < 0) return;
   FinalRows fr;
@@ -575,8 +641,8 @@ __global__ __launch_bounds__(kWThreads) void sample_kernel(
   fr.inv_st = d.inv_st;
   fr.md = d.md;
   fr.inv_sd = d.inv_sd;
-  draw_final(fr, d.n, kd, v, chunks, s, ws, uniforms, out_tokens, flags, vec4, lds_scan, s_incl,
-             s_first, s_last);
+  draw_final(fr, d.n, kd, v, pieces, s, ws, u_last, out_tokens, flags, vec4, zres0, zp0, lds_scan,
+             s_incl, s_fl);
 }
 
 }  // namespace
@@ -588,6 +654,7 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
                               int32_t* out_tokens, int32_t* out_num, void* workspace,
                               int32_t* flags, bool vec4, hipStream_t stream) {
   const int chunks = (v + kChunk - 1) / kChunk;
+  const int pieces = (v + kPiece - 1) / kPiece;
   const Layout L = layout(b, kd, v);
   char* base = static_cast<char*>(workspace);
   Workspace ws;
@@ -608,16 +675,17 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
   if (e != hipSuccess) return e;
   // prefetch of all candidate rows while the batch's logits are at most 16 MB
   const bool prefetch = (int64_t)b * (2 * kd + 1) * v * 4 <= (int64_t(16) << 20);
+  const dim3 g2((unsigned)pieces, (unsigned)b);
   if (prefetch)
-    decide_kernel<true><<<dim3((unsigned)chunks, (unsigned)b), dim3(kWThreads), 0, stream>>>(
-        target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4);
+    decide_kernel<true><<<g2, dim3(kWThreads), 0, stream>>>(
+        target, draft, tokens, uniforms, kd, v, chunks, pieces, ws, out_tokens, out_num, flags, vec4);
   else
-    decide_kernel<false><<<dim3((unsigned)chunks, (unsigned)b), dim3(kWThreads), 0, stream>>>(
-        target, draft, tokens, uniforms, kd, v, chunks, ws, out_tokens, out_num, flags, vec4);
+    decide_kernel<false><<<g2, dim3(kWThreads), 0, stream>>>(
+        target, draft, tokens, uniforms, kd, v, chunks, pieces, ws, out_tokens, out_num, flags, vec4);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   sample_kernel<<<dim3((unsigned)b), dim3(kWThreads), 0, stream>>>(target, draft, uniforms, kd, v,
-                                                                   chunks, ws, out_tokens, flags, vec4);
+                                                                   pieces, ws, out_tokens, flags, vec4);
   return hipGetLastError();
 }
 

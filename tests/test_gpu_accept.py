@@ -21,11 +21,11 @@ from tests.gpu_util import dev, host, say
 pytestmark = pytest.mark.gpu
 
 
-def run_accept(target, draft, tokens, u):
+def run_accept(target, draft, tokens, u, workspace=None):
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
     kd = target.shape[1] - 1
     out, n = mxs.spec_accept(dev(target), dev(draft) if kd else None, dev(tokens) if kd else None,
-                             dev(u), dev_flags=flags)
+                             dev(u), workspace=workspace, dev_flags=flags)
     torch.cuda.synchronize()
     return host(out), host(n), int(flags.item())
 
@@ -33,8 +33,8 @@ def run_accept(target, draft, tokens, u):
 STRICT_MARGIN = 1e-12
 
 
-def compare(target, draft, tokens, u, label):
-    out, n, f = run_accept(target, draft, tokens, u)
+def compare(target, draft, tokens, u, label, workspace=None):
+    out, n, f = run_accept(target, draft, tokens, u, workspace)
     ref = oacc.step_batch(target, draft, tokens, u)
     differ = (n != ref["n"]) | np.any(out != ref["out_tokens"], axis=1)
     bad = np.nonzero(~ref["flagged"] & differ)[0]
@@ -81,6 +81,32 @@ def test_vocab_edges(v):
     compare(tgt, dft, tok, u, f"v={v}")
 
 
+# Small calls (few workgroups per launch, all candidate rows prefetched by decide)
+# at vocabulary sizes on and off the 4096-logit chunk grid.
+@pytest.mark.parametrize("b,kd,v", [(1, 4, 128256), (2, 3, 128256), (4, 4, 128256), (3, 0, 128256),
+                                    (128, 4, 4096), (64, 2, 8192), (40, 1, 12288), (5, 4, 8),
+                                    (4, 4, 131072), (2, 4, 262144)])
+def test_small_calls_share_one_workspace(b, kd, v):
+    """Three calls in a row on one workspace filled with garbage first: each must
+    match the oracle, so nothing a call reads from the workspace survives from an
+    earlier one."""
+    say(f"accept: small calls b={b} K={kd} V={v}")
+    ws = torch.full((mxs.spec_accept_workspace_bytes(b, kd, v),), 0xAB, dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        tgt, dft, tok, u = synth.accept_batch(6, b, kd, v, 3.0, 1.0, seq0=1000 * rep + b)
+        compare(tgt, dft, tok, u, f"b={b} kd={kd} v={v} call {rep}", workspace=ws)
+
+
+def test_workspace_shared_by_calls_of_different_sizes():
+    """One workspace sized for the largest call serves smaller ones in any order
+    (b = 64 runs decide without the row prefetch, b <= 4 with it)."""
+    say("accept: one workspace, b = 4, 1, 64, 2, 4")
+    ws = torch.full((mxs.spec_accept_workspace_bytes(64, 4, 128256),), 0xAB, dtype=torch.uint8, device="cuda")
+    for b in (4, 1, 64, 2, 4):
+        tgt, dft, tok, u = synth.accept_batch(6, b, 4, 128256, 3.0, 0.5, seq0=77 + b)
+        compare(tgt, dft, tok, u, f"b={b}", workspace=ws)
+
+
 def _logits(p):
     with np.errstate(divide="ignore"):
         return np.log(np.asarray(p, np.float64)).astype(np.float32)
@@ -102,9 +128,10 @@ def test_hand_worked_cycles():
     assert n[0] == 2 and list(out[0]) == [2, 1, 0]
 
 
-def test_edge_cases_and_flags():
-    say("accept: edge cases")
-    v = 6
+@pytest.mark.parametrize("v", [6, 8])
+def test_edge_cases_and_flags(v):
+    """V = 6 takes the scalar-load path, V = 8 the 16-byte vector loads."""
+    say(f"accept: edge cases V={v}")
     z = np.random.default_rng(1).standard_normal((4, v)).astype(np.float32)
     cases = []
     # 0: p = q never rejects
