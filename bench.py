@@ -127,9 +127,11 @@ def summarize_pmc(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
         "calibration": f"torch.neg over {CALIB_MB} MiB of fp32 (reads and writes {CALIB_MB} MiB)",
         "commands": [
             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o pmc -- "
-            f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mb {CALIB_MB}",
+            f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --only headline "
+            f"--calib-copy-mb {CALIB_MB}",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o pmc -- "
-            f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mb {CALIB_MB}",
+            f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --only headline "
+            f"--calib-copy-mb {CALIB_MB}",
             f"python3 bench.py --summarize-pmc {fetch_dir} {write_dir}",
         ],
     }
