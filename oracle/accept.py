@@ -107,10 +107,18 @@ def step(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray, u: np.ndarra
     v = target.shape[1]
     if target.shape != (kd + 1, v) or draft.shape != (kd, v) or len(tokens) != kd or len(u) != kd + 1:
         raise ValueError("shape mismatch")
-    out = np.full(kd + 1, -1, dtype=np.int32)
-
     p_rows = [softmax(target[i]) for i in range(kd + 1)]
     q_rows = [softmax(draft[i]) for i in range(kd)]
+    return step_laws(p_rows, q_rows, tokens, u)
+
+
+def step_laws(p_rows, q_rows, tokens, u) -> dict:
+    """The cycle of step() on given laws: p_rows [K+1] target laws, q_rows [K] draft laws
+    (fp64 rows over one vocabulary, or None for an invalid row)."""
+    kd = len(q_rows)
+    if len(p_rows) != kd + 1 or len(tokens) != kd or len(u) != kd + 1:
+        raise ValueError("shape mismatch")
+    out = np.full(kd + 1, -1, dtype=np.int32)
     if any(r is None for r in p_rows + q_rows):
         return dict(out_tokens=out, n=0, flags=FLAG_NONFINITE, flagged=False, margin=np.inf, a=[])
 

@@ -23,6 +23,7 @@ ROLE_BASE = 3       # base (draft) logits
 ROLE_NOISE = 4      # target = base + noise
 ROLE_DRAFT = 5      # draft-token sampling noise (Gumbel)
 ROLE_U = 6          # uniforms handed to the acceptance kernel
+ROLE_MASK = 7       # token masks (grammar-mask stand-in)
 
 W_CHUNK_ROWS = 256  # weights are drawn in row chunks so any row range regenerates alone
 
@@ -138,3 +139,20 @@ def accept_batch(config: int, b: int, kd: int, v: int, base_sigma: float, noise_
         tok[i] = gumbel_tokens(config, seq0 + i, d)
         uni[i] = uniforms(config, seq0 + i, kd)
     return tgt, dft, tok, uni
+
+
+def token_mask(config: int, seq: int, rows: int, v: int, keep_frac: float) -> np.ndarray:
+    """bool [rows, v]: each token allowed independently with probability keep_frac."""
+    return rng(config, ROLE_MASK, seq).random((rows, v)) < keep_frac
+
+
+def pack_mask(mask) -> np.ndarray:
+    """bool [..., V] -> uint32 [..., ceil(V/32)] in the library's mask layout: token t is
+    bit t % 32 of word t // 32 (1 = allowed)."""
+    mask = np.asarray(mask, dtype=bool)
+    v = mask.shape[-1]
+    w = (v + 31) // 32
+    pad = np.zeros(mask.shape[:-1] + (w * 32,), dtype=bool)
+    pad[..., :v] = mask
+    bits = pad.reshape(mask.shape[:-1] + (w, 32)).astype(np.uint64)
+    return (bits << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
