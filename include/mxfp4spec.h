@@ -52,7 +52,8 @@ typedef enum mxs_status {
   MXS_ERR_ALIGN = 3,     /* a pointer is not aligned as documented */
   MXS_ERR_WORKSPACE = 4, /* the workspace is smaller than the query returns */
   MXS_ERR_DEVICE = 5,    /* no usable HIP device, or it is not gfx950 */
-  MXS_ERR_LAUNCH = 6     /* a kernel launch failed */
+  MXS_ERR_LAUNCH = 6,    /* a kernel launch failed */
+  MXS_ERR_VALUE = 7      /* an argument value is out of range (see each entry point) */
 } mxs_status;
 
 /* Device-detected conditions (bits of *dev_flags). */
@@ -182,6 +183,55 @@ mxs_status spec_accept(const float* target_logits, const float* draft_logits,
                        int32_t kd, int32_t v, int32_t* out_tokens,
                        int32_t* out_num_accepted, void* workspace, size_t workspace_bytes,
                        int32_t* dev_flags, void* stream);
+
+/*
+ * spec_accept_sampled_workspace_bytes — device workspace spec_accept_sampled
+ * needs for (b, kd, v): spec_accept's plus ~74 KB per logit row for the top-k /
+ * top-p selection. Returns 0 when the sizes are out of range.
+ */
+size_t spec_accept_sampled_workspace_bytes(int32_t b, int32_t kd, int32_t v);
+
+/*
+ * spec_accept_sampled — spec_accept on transformed laws [M11 §4: the laws p_i
+ * and q_i are the ones tokens are actually sampled from, so temperature,
+ * top-k, top-p and a grammar mask apply to both, or the cycle is not exact].
+ *
+ * Every target and draft row is transformed alike, in this order:
+ *   mask       token t of position i is removed when bit t % 32 of word t / 32
+ *              of mask row i is 0 (target row i and draft row i share mask row
+ *              i; the bonus row kd uses mask row kd);
+ *   temperature the logits are divided by temperature;
+ *   top-k      a token stays iff fewer than top_k remaining tokens have a
+ *              strictly larger logit (ties at the k-th value all stay);
+ *   top-p      with e_t = exp((z_t - max z) / temperature) over the tokens
+ *              top-k left and S their sum, a token stays iff the e-mass of
+ *              those with a strictly larger logit is below top_p * S (the
+ *              smallest most-probable set reaching top_p, boundary ties kept).
+ * The law of a row is e_t / sum over the remaining tokens; then the cycle of
+ * spec_accept runs unchanged on these laws (a draft token the transformed
+ * draft law gives probability 0 raises MXS_FLAG_Q_ZERO; a row with no
+ * remaining finite logit refuses its sequence with MXS_FLAG_NONFINITE). The
+ * draft tokens must come from the transformed draft laws.
+ *
+ * temperature     > 0 and finite (1: none).
+ * top_k           >= 0 (0: none; >= v: none).
+ * top_p           in (0, 1] (1: none). The top-p boundary sums are fp64 with
+ *                 an unspecified summation order, so a token whose strictly-
+ *                 larger mass is within ~1e-15 * S of top_p * S can fall on
+ *                 either side.
+ * mask            [b, kd+1, ceil(v/32)] uint32 device bits, 4-byte aligned; or
+ *                 NULL (no mask).
+ * workspace       at least spec_accept_sampled_workspace_bytes(b, kd, v) bytes;
+ *                 other arguments as spec_accept.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_VALUE (temperature, top_k,
+ * top_p), MXS_ERR_ALIGN, MXS_ERR_WORKSPACE.
+ */
+mxs_status spec_accept_sampled(const float* target_logits, const float* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms, int32_t b,
+                               int32_t kd, int32_t v, float temperature, int32_t top_k,
+                               float top_p, const uint32_t* mask, int32_t* out_tokens,
+                               int32_t* out_num_accepted, void* workspace,
+                               size_t workspace_bytes, int32_t* dev_flags, void* stream);
 
 #ifdef __cplusplus
 }

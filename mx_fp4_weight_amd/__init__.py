@@ -22,6 +22,7 @@ MXS_ERR_ALIGN = 3
 MXS_ERR_WORKSPACE = 4
 MXS_ERR_DEVICE = 5
 MXS_ERR_LAUNCH = 6
+MXS_ERR_VALUE = 7
 
 FLAG_NONFINITE = 1
 FLAG_TOKEN_RANGE = 2
@@ -29,7 +30,8 @@ FLAG_Q_ZERO = 4
 FLAG_RESIDUAL_ZERO = 8
 
 EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_verify_gemm",
-           "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept"]
+           "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept",
+           "spec_accept_sampled_workspace_bytes", "spec_accept_sampled"]
 
 
 class GemmProblem(ctypes.Structure):
@@ -65,6 +67,12 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_accept.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.spec_accept.restype = ctypes.c_int
+    lib.spec_accept_sampled_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_accept_sampled_workspace_bytes.restype = ctypes.c_size_t
+    f32 = ctypes.c_float
+    lib.spec_accept_sampled.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp, vp]
+    lib.spec_accept_sampled.restype = ctypes.c_int
     return lib
 
 
@@ -213,4 +221,53 @@ def spec_accept(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
     _check(get_lib().spec_accept(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), b, kd, v,
                            _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
                            _ptr(dev_flags), _stream(stream)), "spec_accept")
+    return out_tokens, out_num
+
+
+def spec_accept_sampled_workspace_bytes(b: int, kd: int, v: int) -> int:
+    return int(get_lib().spec_accept_sampled_workspace_bytes(b, kd, v))
+
+
+def spec_accept_sampled(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor | None,
+                        uniforms: torch.Tensor, temperature: float = 1.0, top_k: int = 0,
+                        top_p: float = 1.0, mask: torch.Tensor | None = None,
+                        out_tokens: torch.Tensor | None = None, out_num: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, dev_flags: torch.Tensor | None = None,
+                        stream=None):
+    """spec_accept on transformed laws: mask, temperature, top-k, top-p (see the C header).
+
+    mask: int32 [b, kd+1, ceil(v/32)] holding the uint32 mask words (bit t % 32 of word
+    t // 32 = token t allowed), or None.
+    """
+    _want(target, torch.float32, "target")
+    b, kd1, v = target.shape
+    kd = kd1 - 1
+    if kd > 0:
+        _want(draft, torch.float32, "draft")
+        _want(tokens, torch.int32, "tokens")
+        if draft.shape != (b, kd, v) or tokens.shape != (b, kd):
+            raise ValueError("draft/tokens shape mismatch")
+    else:
+        draft = tokens = None
+    _want(uniforms, torch.float32, "uniforms")
+    if uniforms.shape != (b, kd + 1):
+        raise ValueError("uniforms must be [b, kd+1]")
+    if mask is not None:
+        _want(mask, torch.int32, "mask")
+        if mask.shape != (b, kd + 1, (v + 31) // 32):
+            raise ValueError("mask must be [b, kd+1, ceil(v/32)]")
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((b, kd + 1), dtype=torch.int32, device=dev)
+    if out_num is None:
+        out_num = torch.empty((b,), dtype=torch.int32, device=dev)
+    need = spec_accept_sampled_workspace_bytes(b, kd, v)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _want(workspace, torch.uint8, "workspace")
+    _want(dev_flags, torch.int32, "dev_flags")
+    _check(get_lib().spec_accept_sampled(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), b, kd, v,
+                                         float(temperature), int(top_k), float(top_p), _ptr(mask),
+                                         _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
+                                         _ptr(dev_flags), _stream(stream)), "spec_accept_sampled")
     return out_tokens, out_num

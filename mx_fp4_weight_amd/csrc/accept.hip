@@ -71,10 +71,15 @@ struct Workspace {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t cmax, csum, cbad, gz, dec, zres, zp, total;
+  size_t cmax, csum, cbad, gz, dec, zres, zp;
+  // sampling transforms only
+  size_t thr, selmax, selcnt[3], selmass[3], selstate[2];
+  size_t total;
 };
 
-inline Layout layout(int64_t b, int64_t kd, int64_t v) {
+struct SelState;
+
+inline Layout layout(int64_t b, int64_t kd, int64_t v, bool sampled = false) {
   const int64_t rows = b * (2 * kd + 1);
   const int64_t chunks = (v + kChunk - 1) / kChunk;
   const int64_t pieces = (v + kPiece - 1) / kPiece;
@@ -94,6 +99,23 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v) {
   off = align256(off + sizeof(double) * b * pieces);
   L.zp = off;
   off = align256(off + sizeof(double) * b * pieces);
+  if (sampled) {
+    constexpr size_t kBuckets = 2048, kStateBytes = 32;
+    L.thr = off;
+    off = align256(off + sizeof(uint32_t) * rows);
+    L.selmax = off;
+    off = align256(off + sizeof(float) * rows * chunks);
+    for (int i = 0; i < 3; ++i) {
+      L.selcnt[i] = off;
+      off = align256(off + sizeof(uint32_t) * rows * kBuckets);
+      L.selmass[i] = off;
+      off = align256(off + sizeof(double) * rows * kBuckets);
+    }
+    for (int i = 0; i < 2; ++i) {
+      L.selstate[i] = off;
+      off = align256(off + kStateBytes * rows);
+    }
+  }
   L.total = off;
   return L;
 }
@@ -105,12 +127,47 @@ __device__ inline const float* row_ptr(const float* target, const float* draft, 
   return draft + ((size_t)s * kd + (j - kd - 1)) * (size_t)v;
 }
 
+// ---------------------------------------------------------------- sampling transforms
+// Temperature, grammar mask and top-k / top-p thresholds, applied to every target
+// and draft row alike. A token of row j is live iff its mask bit (mask row j for
+// target rows, j - kd - 1 for draft rows: one mask per position) is set and the
+// order key of its logit is at least the row's threshold. A removed token's logit
+// is replaced by -inf before any exponential, so it has probability 0; exponents
+// are (z - max) / tau.
+struct Transform {
+  const uint32_t* mask;  // [b][kd+1][words] bits, 1 = allowed; or null
+  const uint32_t* thr;   // [rows] order-key thresholds; or null (no top-k / top-p)
+  double inv_tau;        // 1 / temperature
+  int words;             // ceil(v / 32)
+};
+
+// fp32 -> uint32 with the same order (negatives reversed below the positives; -0 and
+// +0 compare equal as logits, so they get one key).
+__device__ inline uint32_t order_key(float z) {
+  const uint32_t b = __float_as_uint(z == 0.0f ? 0.0f : z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline int mask_row(int j, int kd) { return j <= kd ? j : j - kd - 1; }
+
+// Mask words of mask row mi of sequence s (null without a mask).
+__device__ inline const uint32_t* mask_words(const Transform& tr, int64_t s, int kd, int mi) {
+  return tr.mask ? tr.mask + ((size_t)s * (kd + 1) + mi) * (size_t)tr.words : nullptr;
+}
+
+__device__ inline float live_logit(float z, int t, const uint32_t* words, uint32_t thr) {
+  const bool allowed = words ? ((words[t >> 5] >> (t & 31)) & 1u) != 0u : true;
+  return (allowed && order_key(z) >= thr) ? z : -INFINITY;
+}
+
 // ---------------------------------------------------------------- stats
-template <bool kVec4>
+// kT: the transformed laws (mask, threshold and temperature from tr).
+template <bool kVec4, bool kT>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict__ target,
                                                          const float* __restrict__ draft,
                                                          const int32_t* __restrict__ tokens, int kd,
-                                                         int v, int chunks, Workspace ws) {
+                                                         int v, int chunks, Workspace ws,
+                                                         Transform tr) {
   __shared__ double lds_d[kThreads / kWave];
   __shared__ float lds_f[kThreads / kWave];
   __shared__ int lds_i[kThreads / kWave];
@@ -147,12 +204,21 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   else if (j > kd) xi = tokens[(size_t)s * kd + (j - kd - 1)];
   float mx = -INFINITY;
   int bad = 0;
+  const uint32_t* mw = nullptr;
+  uint32_t thr = 0u;
+  if constexpr (kT) {
+    mw = mask_words(tr, s, kd, mask_row(j, kd));
+    thr = tr.thr ? tr.thr[rowg] : 0u;
+  }
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     bad |= (vals[q] != vals[q]) | (vals[q] == INFINITY);
-    mx = fmaxf(mx, vals[q]);
     const int e = kVec4 ? base + 4 * (threadIdx.x + kThreads * (q / 4)) + (q % 4)
                         : base + threadIdx.x + kThreads * q;
+    if constexpr (kT) {
+      if (e < v) vals[q] = live_logit(vals[q], e, mw, thr);
+    }
+    mx = fmaxf(mx, vals[q]);
     if (e == xi) ws.gz[rowg] = vals[q];
   }
   mx = block_max<kThreads>(mx, lds_f);
@@ -161,7 +227,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   if (mx != -INFINITY && !bad) {
     const double m64 = (double)mx;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) acc += exp_neg_f64((double)vals[q] - m64);
+    for (int q = 0; q < kPer; ++q) {
+      if constexpr (kT) acc += exp_neg_f64(((double)vals[q] - m64) * tr.inv_tau);
+      else acc += exp_neg_f64((double)vals[q] - m64);
+    }
   }
   acc = block_sum_f64<kThreads>(acc, lds_d);
   if (threadIdx.x == 0) {
@@ -177,18 +246,26 @@ struct FinalRows {
   const float* zt;
   const float* zd;  // nullptr for the bonus row
   double mt, inv_st, md, inv_sd;
+  // transformed laws only: 1/tau, the rows' thresholds and the position's mask words
+  double inv_tau;
+  uint32_t thr_t, thr_d;
+  const uint32_t* mw;
 };
 
-// Final weights and p_n of kWPer consecutive tokens from their logits zt, zd.
+// Final weights and p_n of kWPer consecutive tokens from their logits zt, zd (removed
+// tokens already -inf when kT).
+template <bool kT>
 __device__ inline void weights_from(const FinalRows& fr, const float (&zt)[kWPer],
                                     const float (&zd)[kWPer], double (&wf)[kWPer],
                                     double (&wp)[kWPer]) {
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
-    const double p = exp_neg_f64((double)zt[j] - fr.mt) * fr.inv_st;
+    const double dt = kT ? ((double)zt[j] - fr.mt) * fr.inv_tau : (double)zt[j] - fr.mt;
+    const double p = exp_neg_f64(dt) * fr.inv_st;
     wp[j] = p;
     if (fr.zd) {
-      const double q = exp_neg_f64((double)zd[j] - fr.md) * fr.inv_sd;
+      const double dd = kT ? ((double)zd[j] - fr.md) * fr.inv_tau : (double)zd[j] - fr.md;
+      const double q = exp_neg_f64(dd) * fr.inv_sd;
       const double d = p - q;
       wf[j] = d > 0.0 ? d : 0.0;
     } else {
@@ -199,6 +276,7 @@ __device__ inline void weights_from(const FinalRows& fr, const float (&zt)[kWPer
 
 // Final weights and p_n of the kWPer consecutive tokens t0 .. t0+kWPer-1 (zero past v).
 // Both rows are loaded before any arithmetic (one 16-byte load each when aligned).
+template <bool kT>
 __device__ inline void thread_weights(const FinalRows& fr, int t0, int v, bool vec4,
                                       double (&wf)[kWPer], double (&wp)[kWPer]) {
   float zt[kWPer], zd[kWPer];
@@ -219,7 +297,16 @@ __device__ inline void thread_weights(const FinalRows& fr, int t0, int v, bool v
       zd[j] = (in && fr.zd) ? fr.zd[t0 + j] : -INFINITY;
     }
   }
-  weights_from(fr, zt, zd, wf, wp);
+  if constexpr (kT) {
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      if (t0 + j < v) {
+        zt[j] = live_logit(zt[j], t0 + j, fr.mw, fr.thr_t);
+        zd[j] = live_logit(zd[j], t0 + j, fr.mw, fr.thr_d);
+      }
+    }
+  }
+  weights_from<kT>(fr, zt, zd, wf, wp);
 }
 
 // ---------------------------------------------------------------- final draw
@@ -384,6 +471,7 @@ __device__ void select_token(const PieceChoice& pc, int n, int kd, int64_t s, in
 }
 
 // The whole draw for one sequence by one workgroup (the sample kernel).
+template <bool kT>
 __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces, int64_t s,
                            const Workspace& ws, float u_last,
                            int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4,
@@ -394,20 +482,284 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces
   if (pc.c < 0) return;
   const int t0 = pc.c * kPiece + (int)threadIdx.x * kWPer;
   double wf[kWPer], wp[kWPer];
-  thread_weights(fr, t0, v, vec4, wf, wp);
+  thread_weights<kT>(fr, t0, v, vec4, wf, wp);
   select_token(pc, n, kd, s, t0, wf, wp, out_tokens, lds_scan, s_incl, s_fl);
+}
+
+// ---------------------------------------------------------------- top-k / top-p thresholds
+// A row's threshold is an order key: a token stays iff its key is at least the
+// threshold. Both selections are radix walks over the 32-bit keys of the allowed
+// finite logits, top digit (11 bits) first, bottom digit (10 bits) last. A pass over
+// the row histograms the current digit of the tokens whose higher digits equal the
+// prefix found so far (counts for top-k; counts and fp64 masses exp((z - max) / tau)
+// of the tokens top-k kept, for top-p). The next pass walks that histogram from the
+// largest key down and takes the lowest non-empty bucket whose tokens still have
+// fewer than k tokens (top-k) or less than P·S mass (top-p) strictly above them; its
+// digit extends the prefix. After the last digit the prefix is the threshold. The
+// histograms live per row in the workspace in three rotating buffers (a pass fills
+// one, reads the previous one and clears the next one); the walk's state is double
+// buffered between passes.
+constexpr int kSelBuckets = 2048;
+constexpr int kSelDigits = 3;
+__host__ __device__ constexpr int sel_shift(int d) { return d == 0 ? 21 : (d == 1 ? 10 : 0); }
+__host__ __device__ constexpr int sel_width(int d) { return d == 2 ? 10 : 11; }
+
+struct SelState {
+  uint32_t prefix;  // resolved key digits (key >> shift of the last resolved digit)
+  uint32_t thr_k;   // top-k threshold once resolved (0: top-k off)
+  double carry;     // count (top-k) or mass (top-p) strictly above the prefix's key range
+  double s1;        // top-p: mass of the law top-k left
+  float rmax;       // largest allowed finite logit of the row
+  int empty;        // no allowed finite logit (or nothing to select): threshold 0
+};
+
+struct SelBufs {
+  uint32_t* cnt[3];    // [rows][kSelBuckets]
+  double* mass[3];     // [rows][kSelBuckets]
+  SelState* state[2];  // [rows]
+  float* cmax;         // [rows][chunks] chunk maxima of the allowed finite logits
+};
+
+struct SelArgs {
+  int top_k;     // 0: off
+  double top_p;  // >= 1: off
+};
+static_assert(sizeof(SelState) == 32, "workspace layout assumes a 32-byte selection state");
+
+// The allowed logits of this thread's 16 tokens of a chunk (removed ones: NaN), in the
+// stats kernel's order.
+template <bool kVec4>
+__device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t* mw, int base, int v,
+                                    float (&vals)[kPer], int (&idx)[kPer]) {
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    idx[q] = kVec4 ? base + 4 * ((int)threadIdx.x + kThreads * (q / 4)) + (q % 4)
+                   : base + (int)threadIdx.x + kThreads * q;
+    vals[q] = NAN;
+  }
+  if constexpr (kVec4) {
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      const int e = idx[4 * q];
+      if (e < v) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(z + e);
+        vals[4 * q + 0] = t[0];
+        vals[4 * q + 1] = t[1];
+        vals[4 * q + 2] = t[2];
+        vals[4 * q + 3] = t[3];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (idx[q] < v) vals[q] = z[idx[q]];
+  }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int t = idx[q];
+    const bool allowed = t < v && (mw ? ((mw[t >> 5] >> (t & 31)) & 1u) != 0u : true);
+    const bool finite = vals[q] > -INFINITY && vals[q] < INFINITY;
+    if (!allowed || !finite) vals[q] = NAN;
+  }
+}
+
+// Walk the histogram of `digit` (mode 0: counts against k; mode 1: masses against P·S)
+// and extend s.prefix with the boundary bucket. Every thread returns the same state.
+__device__ void sel_resolve(int mode, int digit, const uint32_t* __restrict__ cnt,
+                            const double* __restrict__ mass, const SelArgs& sa, SelState& st,
+                            double* lds_scan, double* s_excl, int* s_fl, int* s_best,
+                            double* s_above) {
+  const int nb = 1 << sel_width(digit);
+  const int per = nb / kThreads;  // 8 or 4 buckets per thread, in descending key order
+  const int tid = threadIdx.x;
+  if (mode == 1 && digit == 0) {
+    // S: the mass of every token top-k kept (all buckets of the first top-p digit)
+    double t = 0.0;
+    for (int i = 0; i < per; ++i) t += mass[nb - 1 - (tid * per + i)];
+    st.s1 = block_sum_f64<kThreads>(t, lds_scan);
+  }
+  const double target = mode == 0 ? (double)sa.top_k : sa.top_p * st.s1;
+  double local = 0.0;
+  for (int i = 0; i < per; ++i) {
+    const int b = nb - 1 - (tid * per + i);
+    local += mode == 0 ? (double)cnt[b] : mass[b];
+  }
+  const double incl = block_inclusive_scan_f64<kThreads>(local, lds_scan);
+  s_excl[tid] = incl;
+  __syncthreads();
+  double run = st.carry + (tid > 0 ? s_excl[tid - 1] : 0.0);
+  int best = -1;
+  double best_above = 0.0;
+  for (int i = 0; i < per; ++i) {
+    const int d = tid * per + i;
+    const int b = nb - 1 - d;
+    const uint32_t c = cnt[b];
+    if (run < target && c > 0u) {
+      best = d;
+      best_above = run;
+    }
+    run += mode == 0 ? (double)c : mass[b];
+  }
+  // descending indices grow with the thread index: the last thread with a candidate
+  // holds the lowest qualifying bucket
+  const int2 fl = block_first_last(false, best >= 0, 0, s_fl);
+  if (tid == fl.y) {
+    *s_best = best;
+    *s_above = best_above;
+  }
+  __syncthreads();
+  if (fl.y < 0) {
+    st.empty = 1;
+  } else {
+    st.prefix = (st.prefix << sel_width(digit)) | (uint32_t)(nb - 1 - *s_best);
+    st.carry = *s_above;
+  }
+  __syncthreads();
+}
+
+// Chunk maxima of the allowed finite logits; clears histogram buffer 0.
+template <bool kVec4>
+__global__ __launch_bounds__(kThreads) void sel_prep_kernel(const float* __restrict__ target,
+                                                            const float* __restrict__ draft, int kd,
+                                                            int v, int chunks, Transform tr,
+                                                            SelBufs sb) {
+  __shared__ float lds_f[kThreads / kWave];
+  const int64_t rowg = blockIdx.x;
+  const int per_seq = 2 * kd + 1;
+  const int64_t s = rowg / per_seq;
+  const int j = (int)(rowg % per_seq);
+  const int c = blockIdx.y;
+  float vals[kPer];
+  int idx[kPer];
+  chunk_logits<kVec4>(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)),
+                      c * kChunk, v, vals, idx);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) mx = fmaxf(mx, vals[q]);  // NaN (removed) is ignored
+  mx = block_max<kThreads>(mx, lds_f);
+  if (threadIdx.x == 0) sb.cmax[rowg * chunks + c] = mx;
+  for (int b = c * kThreads + (int)threadIdx.x; b < kSelBuckets; b += chunks * kThreads) {
+    sb.cnt[0][rowg * kSelBuckets + b] = 0u;
+    sb.mass[0][rowg * kSelBuckets + b] = 0.0;
+  }
+}
+
+// Pass h of the walk: resolve the previous pass's digit, then histogram (mode, digit)
+// over this chunk into buffer h % 3, and clear buffer (h + 1) % 3.
+template <bool kVec4>
+__global__ __launch_bounds__(kThreads) void sel_pass_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft, int kd, int v, int chunks,
+    Transform tr, SelBufs sb, SelArgs sa, int h, int mode, int digit, int prev_mode, int prev_digit) {
+  __shared__ uint32_t hc[kSelBuckets];
+  __shared__ double hm[kSelBuckets];
+  __shared__ double lds_scan[kThreads / kWave];
+  __shared__ double s_excl[kThreads];
+  __shared__ float lds_f[kThreads / kWave];
+  __shared__ int s_fl[2 * (kThreads / kWave)];
+  __shared__ int s_best;
+  __shared__ double s_above;
+  const int64_t rowg = blockIdx.x;
+  const int per_seq = 2 * kd + 1;
+  const int64_t s = rowg / per_seq;
+  const int j = (int)(rowg % per_seq);
+  const int c = blockIdx.y;
+  const int tid = threadIdx.x;
+
+  float vals[kPer];
+  int idx[kPer];
+  chunk_logits<kVec4>(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)),
+                      c * kChunk, v, vals, idx);
+
+  SelState st;
+  if (h == 0) {
+    float m = -INFINITY;
+    for (int cc = tid; cc < chunks; cc += kThreads) m = fmaxf(m, sb.cmax[rowg * chunks + cc]);
+    m = block_max<kThreads>(m, lds_f);
+    st.prefix = 0u;
+    st.thr_k = 0u;
+    st.carry = 0.0;
+    st.s1 = 0.0;
+    st.rmax = m;
+    st.empty = m == -INFINITY;
+  } else {
+    st = sb.state[(h - 1) & 1][rowg];
+    if (!st.empty)
+      sel_resolve(prev_mode, prev_digit, sb.cnt[(h - 1) % 3] + rowg * kSelBuckets,
+                  sb.mass[(h - 1) % 3] + rowg * kSelBuckets, sa, st, lds_scan, s_excl, s_fl,
+                  &s_best, &s_above);
+    if (prev_mode == 0 && prev_digit == kSelDigits - 1) {
+      st.thr_k = st.empty ? 0u : st.prefix;  // top-k resolved
+      if (mode == 1) {
+        st.prefix = 0u;
+        st.carry = 0.0;
+      }
+    }
+  }
+
+  const int nb = 1 << sel_width(digit);
+  for (int b = tid; b < nb; b += kThreads) {
+    hc[b] = 0u;
+    hm[b] = 0.0;
+  }
+  __syncthreads();
+  if (!st.empty) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const float zq = vals[q];
+      if (zq != zq) continue;  // removed, non-finite or past the row
+      const uint32_t key = order_key(zq);
+      if (mode == 1 && key < st.thr_k) continue;
+      if (digit > 0 && (key >> sel_shift(digit - 1)) != st.prefix) continue;
+      const int b = (int)((key >> sel_shift(digit)) & (uint32_t)(nb - 1));
+      atomicAdd(&hc[b], 1u);
+      if (mode == 1) atomicAdd(&hm[b], exp_neg_f64(((double)zq - (double)st.rmax) * tr.inv_tau));
+    }
+  }
+  __syncthreads();
+  uint32_t* gc = sb.cnt[h % 3] + rowg * kSelBuckets;
+  double* gm = sb.mass[h % 3] + rowg * kSelBuckets;
+  for (int b = tid; b < nb; b += kThreads) {
+    if (hc[b] != 0u) {
+      atomicAdd(&gc[b], hc[b]);
+      if (mode == 1) atomicAdd(&gm[b], hm[b]);
+    }
+  }
+  uint32_t* nc = sb.cnt[(h + 1) % 3] + rowg * kSelBuckets;
+  double* nm = sb.mass[(h + 1) % 3] + rowg * kSelBuckets;
+  for (int b = c * kThreads + tid; b < kSelBuckets; b += chunks * kThreads) {
+    nc[b] = 0u;
+    nm[b] = 0.0;
+  }
+  if (c == 0 && tid == 0) sb.state[h & 1][rowg] = st;
+}
+
+// Resolve the last pass's digit: the row's threshold.
+__global__ __launch_bounds__(kThreads) void sel_finish_kernel(SelBufs sb, SelArgs sa, int h_last,
+                                                              int last_mode, uint32_t* __restrict__ thr) {
+  __shared__ double lds_scan[kThreads / kWave];
+  __shared__ double s_excl[kThreads];
+  __shared__ int s_fl[2 * (kThreads / kWave)];
+  __shared__ int s_best;
+  __shared__ double s_above;
+  const int64_t rowg = blockIdx.x;
+  SelState st = sb.state[h_last & 1][rowg];
+  if (!st.empty)
+    sel_resolve(last_mode, kSelDigits - 1, sb.cnt[h_last % 3] + rowg * kSelBuckets,
+                sb.mass[h_last % 3] + rowg * kSelBuckets, sa, st, lds_scan, s_excl, s_fl, &s_best,
+                &s_above);
+  if (threadIdx.x == 0) thr[rowg] = st.empty ? 0u : st.prefix;
 }
 
 // ---------------------------------------------------------------- decide + piece totals
 // kPrefetch: small calls fetch every candidate final row with the statistics (one
 // workgroup per CU holds the extra registers); large calls load only the rows the
 // draw needs and fit two workgroups per CU.
-template <bool kPrefetch>
+template <bool kPrefetch, bool kT>
 __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
     int chunks, int pieces, Workspace ws, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_num, int32_t* __restrict__ flags, int vec4) {
+    int32_t* __restrict__ out_num, int32_t* __restrict__ flags, int vec4, Transform tr) {
   __shared__ double smax[kMaxRows];
   __shared__ double ssum[kMaxRows];
   __shared__ int sbad[kMaxRows];
@@ -476,7 +828,8 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
           bad |= __shfl_xor(bad, off);
         }
         bad |= (m == -INFINITY);
-        double sum = (!bad && cs[r] > 0.0) ? cs[r] * exp_neg_f64((double)cm[r] - (double)m) : 0.0;
+        const double dm = kT ? ((double)cm[r] - (double)m) * tr.inv_tau : (double)cm[r] - (double)m;
+        double sum = (!bad && cs[r] > 0.0) ? cs[r] * exp_neg_f64(dm) : 0.0;
         for (int off = 1; off < seg; off <<= 1) sum += __shfl_xor(sum, off);
         if (j < per_seq && cc == 0) {
           smax[j] = (double)m;
@@ -505,7 +858,9 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
         const double m64 = (double)m;
         for (int cc = lane; cc < chunks; cc += kWave) {
           const double cs = ws.csum[o + cc];
-          if (cs > 0.0) sum += cs * exp_neg_f64((double)ws.cmax[o + cc] - m64);
+          const double dm = kT ? ((double)ws.cmax[o + cc] - m64) * tr.inv_tau
+                               : (double)ws.cmax[o + cc] - m64;
+          if (cs > 0.0) sum += cs * exp_neg_f64(dm);
         }
       }
 #pragma unroll
@@ -531,9 +886,10 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
       if (x < 0 || x >= v) {
         f |= MXS_FLAG_TOKEN_RANGE;
       } else {
-        // the draft token's logits were gathered by the stats kernel
-        const double q = exp_neg_f64((double)gzd - smax[kd + 1 + lane]) / ssum[kd + 1 + lane];
-        const double p = exp_neg_f64((double)gzt - smax[lane]) / ssum[lane];
+        // the draft token's logits were gathered by the stats kernel (-inf if removed)
+        const double itau = kT ? tr.inv_tau : 1.0;
+        const double q = exp_neg_f64(((double)gzd - smax[kd + 1 + lane]) * itau) / ssum[kd + 1 + lane];
+        const double p = exp_neg_f64(((double)gzt - smax[lane]) * itau) / ssum[lane];
         if (q == 0.0) {
           f |= MXS_FLAG_Q_ZERO;
         } else {
@@ -586,6 +942,12 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
     fr.inv_st = 1.0 / ssum[n];
     fr.md = n < kd ? smax[kd + 1 + n] : 0.0;
     fr.inv_sd = n < kd ? 1.0 / ssum[kd + 1 + n] : 0.0;
+    if constexpr (kT) {
+      fr.inv_tau = tr.inv_tau;
+      fr.thr_t = tr.thr ? tr.thr[(size_t)s * per_seq + n] : 0u;
+      fr.thr_d = (tr.thr && n < kd) ? tr.thr[(size_t)s * per_seq + kd + 1 + n] : 0u;
+      fr.mw = mask_words(tr, s, kd, n);
+    }
     double wf[kWPer], wp[kWPer];
     if (pre) {
       float zt[kWPer], zd[kWPer];
@@ -599,10 +961,14 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
       for (int j = 0; j < kWPer; ++j) {
         zt[j] = at[j];
         zd[j] = ad[j];
+        if constexpr (kT) {
+          zt[j] = live_logit(zt[j], t0w + j, fr.mw, fr.thr_t);
+          zd[j] = live_logit(zd[j], t0w + j, fr.mw, fr.thr_d);
+        }
       }
-      weights_from(fr, zt, zd, wf, wp);
+      weights_from<kT>(fr, zt, zd, wf, wp);
     } else {
-      thread_weights(fr, t0w, v, vec4, wf, wp);
+      thread_weights<kT>(fr, t0w, v, vec4, wf, wp);
     }
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) {
@@ -619,10 +985,11 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
 }
 
 // ---------------------------------------------------------------- sample
+template <bool kT>
 __global__ __launch_bounds__(kWThreads) void sample_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const float* __restrict__ uniforms, int kd, int v, int pieces, Workspace ws,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4) {
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ flags, int vec4, Transform tr) {
   __shared__ double lds_scan[kWThreads / kWave];
   __shared__ double s_incl[kWThreads];
   __shared__ int s_fl[2 * kWWaves];
@@ -641,21 +1008,32 @@ __global__ __launch_bounds__(kWThreads) void sample_kernel(
   fr.inv_st = d.inv_st;
   fr.md = d.md;
   fr.inv_sd = d.inv_sd;
-  draw_final(fr, d.n, kd, v, pieces, s, ws, u_last, out_tokens, flags, vec4, zres0, zp0, lds_scan,
+  if constexpr (kT) {
+    const int per_seq = 2 * kd + 1;
+    fr.inv_tau = tr.inv_tau;
+    fr.thr_t = tr.thr ? tr.thr[(size_t)s * per_seq + d.n] : 0u;
+    fr.thr_d = (tr.thr && d.n < kd) ? tr.thr[(size_t)s * per_seq + kd + 1 + d.n] : 0u;
+    fr.mw = mask_words(tr, s, kd, d.n);
+  }
+  draw_final<kT>(fr, d.n, kd, v, pieces, s, ws, u_last, out_tokens, flags, vec4, zres0, zp0, lds_scan,
              s_incl, s_fl);
 }
 
 }  // namespace
 
-size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v) { return layout(b, kd, v).total; }
+size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled) {
+  return layout(b, kd, v, sampled).total;
+}
 
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens,
                               const float* uniforms, int32_t b, int32_t kd, int32_t v,
                               int32_t* out_tokens, int32_t* out_num, void* workspace,
-                              int32_t* flags, bool vec4, hipStream_t stream) {
+                              int32_t* flags, bool vec4, const SamplingParams* sp,
+                              hipStream_t stream) {
   const int chunks = (v + kChunk - 1) / kChunk;
   const int pieces = (v + kPiece - 1) / kPiece;
-  const Layout L = layout(b, kd, v);
+  const bool kt = sp != nullptr;
+  const Layout L = layout(b, kd, v, kt);
   char* base = static_cast<char*>(workspace);
   Workspace ws;
   ws.cmax = reinterpret_cast<float*>(base + L.cmax);
@@ -666,26 +1044,75 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
   ws.zres = reinterpret_cast<double*>(base + L.zres);
   ws.zp = reinterpret_cast<double*>(base + L.zp);
   const int64_t rows = (int64_t)b * (2 * kd + 1);
-  dim3 g1((unsigned)rows, (unsigned)chunks);
-  if (vec4)
-    stats_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws);
-  else
-    stats_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const dim3 g1((unsigned)rows, (unsigned)chunks);
+  hipError_t e = hipSuccess;
+
+  Transform tr{};
+  if (kt) {
+    tr.mask = sp->mask;
+    tr.inv_tau = 1.0 / (double)sp->temperature;
+    tr.words = (v + 31) / 32;
+    const bool use_k = sp->top_k > 0 && sp->top_k < v;
+    const bool use_p = sp->top_p < 1.0f;
+    if (use_k || use_p) {
+      SelBufs sb;
+      for (int i = 0; i < 3; ++i) {
+        sb.cnt[i] = reinterpret_cast<uint32_t*>(base + L.selcnt[i]);
+        sb.mass[i] = reinterpret_cast<double*>(base + L.selmass[i]);
+      }
+      for (int i = 0; i < 2; ++i) sb.state[i] = reinterpret_cast<SelState*>(base + L.selstate[i]);
+      sb.cmax = reinterpret_cast<float*>(base + L.selmax);
+      const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0};
+      if (vec4) sel_prep_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb);
+      else sel_prep_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      // passes: the top-k digits, then the top-p digits
+      int h = 0, prev_mode = -1, prev_digit = -1;
+      for (int mode = 0; mode < 2; ++mode) {
+        if ((mode == 0 && !use_k) || (mode == 1 && !use_p)) continue;
+        for (int d = 0; d < kSelDigits; ++d, ++h) {
+          if (vec4)
+            sel_pass_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb,
+                                                                     sa, h, mode, d, prev_mode, prev_digit);
+          else
+            sel_pass_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb,
+                                                                      sa, h, mode, d, prev_mode, prev_digit);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+          prev_mode = mode;
+          prev_digit = d;
+        }
+      }
+      uint32_t* thr = reinterpret_cast<uint32_t*>(base + L.thr);
+      sel_finish_kernel<<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(sb, sa, h - 1, prev_mode, thr);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      tr.thr = thr;
+    }
+  }
+
+  if (vec4 && kt) stats_kernel<true, true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws, tr);
+  else if (vec4) stats_kernel<true, false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws, tr);
+  else if (kt) stats_kernel<false, true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws, tr);
+  else stats_kernel<false, false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, tokens, kd, v, chunks, ws, tr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   // prefetch of all candidate rows while the batch's logits are at most 16 MB
   const bool prefetch = (int64_t)b * (2 * kd + 1) * v * 4 <= (int64_t(16) << 20);
   const dim3 g2((unsigned)pieces, (unsigned)b);
-  if (prefetch)
-    decide_kernel<true><<<g2, dim3(kWThreads), 0, stream>>>(
-        target, draft, tokens, uniforms, kd, v, chunks, pieces, ws, out_tokens, out_num, flags, vec4);
+#define MXS_DECIDE(P, T)                                                                          \
+  decide_kernel<P, T><<<g2, dim3(kWThreads), 0, stream>>>(target, draft, tokens, uniforms, kd, v, \
+                                                          chunks, pieces, ws, out_tokens, out_num, \
+                                                          flags, vec4, tr)
+  if (prefetch && kt) MXS_DECIDE(true, true);
+  else if (prefetch) MXS_DECIDE(true, false);
+  else if (kt) MXS_DECIDE(false, true);
+  else MXS_DECIDE(false, false);
+#undef MXS_DECIDE
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (kt)
+    sample_kernel<true><<<dim3((unsigned)b), dim3(kWThreads), 0, stream>>>(target, draft, uniforms, kd, v,
+                                                                           pieces, ws, out_tokens, flags, vec4, tr);
   else
-    decide_kernel<false><<<g2, dim3(kWThreads), 0, stream>>>(
-        target, draft, tokens, uniforms, kd, v, chunks, pieces, ws, out_tokens, out_num, flags, vec4);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  sample_kernel<<<dim3((unsigned)b), dim3(kWThreads), 0, stream>>>(target, draft, uniforms, kd, v,
-                                                                   pieces, ws, out_tokens, flags, vec4);
+    sample_kernel<false><<<dim3((unsigned)b), dim3(kWThreads), 0, stream>>>(target, draft, uniforms, kd, v,
+                                                                            pieces, ws, out_tokens, flags, vec4, tr);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // C-ABI entry points of the MX-FP4 verification library: argument validation
 // (before any HIP call), the gfx950 device check, and dispatch to the kernels.
+#include <math.h>
 #include <string.h>
 
 #include <atomic>
@@ -47,6 +48,7 @@ const char* mxs_status_string(int status) {
     case MXS_ERR_WORKSPACE: return "MXS_ERR_WORKSPACE: workspace too small";
     case MXS_ERR_DEVICE: return "MXS_ERR_DEVICE: no usable gfx950 HIP device";
     case MXS_ERR_LAUNCH: return "MXS_ERR_LAUNCH: kernel launch failed";
+    case MXS_ERR_VALUE: return "MXS_ERR_VALUE: an argument value is out of range";
     default: return "unknown mxs_status";
   }
 }
@@ -108,7 +110,12 @@ mxs_status mxfp4_verify_gemm_grouped(const mxs_gemm_problem* problems, int32_t c
 
 size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
   if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
-  return mxs::accept_workspace_bytes(b, kd, v);
+  return mxs::accept_workspace_bytes(b, kd, v, false);
+}
+
+size_t spec_accept_sampled_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
+  if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
+  return mxs::accept_workspace_bytes(b, kd, v, true);
 }
 
 mxs_status spec_accept(const float* target_logits, const float* draft_logits,
@@ -123,14 +130,43 @@ mxs_status spec_accept(const float* target_logits, const float* draft_logits,
       !aligned(uniforms, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
       !aligned(workspace, 16) || !aligned(dev_flags, 4))
     return MXS_ERR_ALIGN;
-  if (workspace_bytes < mxs::accept_workspace_bytes(b, kd, v)) return MXS_ERR_WORKSPACE;
+  if (workspace_bytes < mxs::accept_workspace_bytes(b, kd, v, false)) return MXS_ERR_WORKSPACE;
   const mxs_status d = check_device();
   if (d != MXS_OK) return d;
   const bool vec4 = (v % 4 == 0) && aligned(target_logits, 16) &&
                     (kd == 0 || aligned(draft_logits, 16));
   return launched(mxs::launch_spec_accept(target_logits, draft_logits, draft_tokens, uniforms, b,
                                           kd, v, out_tokens, out_num_accepted, workspace, dev_flags,
-                                          vec4, static_cast<hipStream_t>(stream)));
+                                          vec4, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+mxs_status spec_accept_sampled(const float* target_logits, const float* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms, int32_t b,
+                               int32_t kd, int32_t v, float temperature, int32_t top_k, float top_p,
+                               const uint32_t* mask, int32_t* out_tokens, int32_t* out_num_accepted,
+                               void* workspace, size_t workspace_bytes, int32_t* dev_flags,
+                               void* stream) {
+  if (!target_logits || !uniforms || !out_tokens || !out_num_accepted || !workspace)
+    return MXS_ERR_NULL;
+  if (kd > 0 && (!draft_logits || !draft_tokens)) return MXS_ERR_NULL;
+  if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return MXS_ERR_SHAPE;
+  // NaN fails every comparison below
+  if (!(temperature > 0.0f) || !(temperature < INFINITY) || top_k < 0 || !(top_p > 0.0f) ||
+      !(top_p <= 1.0f))
+    return MXS_ERR_VALUE;
+  if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      !aligned(workspace, 16) || !aligned(dev_flags, 4) || !aligned(mask, 4))
+    return MXS_ERR_ALIGN;
+  if (workspace_bytes < mxs::accept_workspace_bytes(b, kd, v, true)) return MXS_ERR_WORKSPACE;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  const bool vec4 = (v % 4 == 0) && aligned(target_logits, 16) &&
+                    (kd == 0 || aligned(draft_logits, 16));
+  const mxs::SamplingParams sp{temperature, top_k, top_p, mask};
+  return launched(mxs::launch_spec_accept(target_logits, draft_logits, draft_tokens, uniforms, b,
+                                          kd, v, out_tokens, out_num_accepted, workspace, dev_flags,
+                                          vec4, &sp, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

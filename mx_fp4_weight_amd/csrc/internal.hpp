@@ -25,11 +25,21 @@ hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes,
 hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint16_t* x, int64_t m, float* y, hipStream_t stream);
 
-size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v);
+// Sampling transforms of spec_accept_sampled (validated by the caller).
+struct SamplingParams {
+  float temperature;      // > 0
+  int32_t top_k;          // >= 0; 0 = off
+  float top_p;            // (0, 1]; 1 = off
+  const uint32_t* mask;   // [b][kd+1][ceil(v/32)] or null
+};
 
+size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
+
+// sp == nullptr: the plain laws (no transform kernels, the same code as without transforms).
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens,
                               const float* uniforms, int32_t b, int32_t kd, int32_t v,
                               int32_t* out_tokens, int32_t* out_num, void* workspace,
-                              int32_t* flags, bool vec4, hipStream_t stream);
+                              int32_t* flags, bool vec4, const SamplingParams* sp,
+                              hipStream_t stream);
 
 }  // namespace mxs

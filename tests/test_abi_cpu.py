@@ -41,7 +41,7 @@ def test_header_functions_exported():
 def test_status_strings_and_version():
     lib = mxs.get_lib()
     assert lib.mxs_abi_version() == 1
-    for s in range(7):
+    for s in range(8):
         assert mxs.status_string(s).startswith("MXS_")
     assert mxs.status_string(99) == "unknown mxs_status"
 
@@ -159,3 +159,32 @@ def test_grouped_gemm_host_errors():
     arr[1].x = 0x30000
     arr[2].n = 0
     assert lib.mxfp4_verify_gemm_grouped(arr, 3, 64, 5, None) == mxs.MXS_ERR_SHAPE
+
+
+def _as(t=0x1000, d=0x2000, tok=0x3000, u=0x4000, b=1, kd=4, v=1024, tau=1.0, k=0, p=1.0, mask=None,
+        ot=0x5000, on=0x6000, ws=0x7000, wsb=None, flags=None):
+    lib = mxs.get_lib()
+    if wsb is None:
+        wsb = lib.spec_accept_sampled_workspace_bytes(max(b, 1), max(kd, 0), max(v, 2))
+    f = lambda a: P(a) if a else None
+    return lib.spec_accept_sampled(f(t), f(d), f(tok), f(u), b, kd, v, tau, k, p, f(mask), f(ot), f(on),
+                                   f(ws), wsb, f(flags), None)
+
+
+def test_sampled_host_errors():
+    lib = mxs.get_lib()
+    plain = lib.spec_accept_workspace_bytes(2, 4, 128256)
+    sampled = lib.spec_accept_sampled_workspace_bytes(2, 4, 128256)
+    assert sampled >= plain + 2 * 9 * 3 * 2048 * 12   # three rotating count + mass histograms per row
+    assert lib.spec_accept_sampled_workspace_bytes(0, 4, 1024) == 0
+    for kw in [dict(t=0), dict(u=0), dict(ot=0), dict(on=0), dict(ws=0), dict(d=0), dict(tok=0)]:
+        assert _as(**kw) == mxs.MXS_ERR_NULL
+    for kw in [dict(b=0), dict(kd=33), dict(v=1)]:
+        assert _as(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(tau=0.0), dict(tau=-1.0), dict(tau=float("inf")), dict(tau=float("nan")),
+               dict(k=-1), dict(p=0.0), dict(p=1.5), dict(p=float("nan"))]:
+        assert _as(**kw) == mxs.MXS_ERR_VALUE, kw
+    assert _as(mask=0x8002) == mxs.MXS_ERR_ALIGN
+    need = lib.spec_accept_sampled_workspace_bytes(1, 4, 1024)
+    assert _as(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
+    assert _as(wsb=need, tau=0.7, k=50, p=0.9, mask=0x8000) == mxs.MXS_ERR_DEVICE
