@@ -32,7 +32,9 @@ shapes with 1% outlier input channels x20, lm_head 128256x8192, and the
 its MFMA utilisation, spec_accept for 64 sequences) and `full_8b_step` (32
 layers + lm_head 128256x4096, then spec_accept on the lm_head output with draft
 rows tuned to acceptance 0.6 / 0.8 / 0.9: step time, tokens/s-equivalent and the
-GPU-measured tokens per step against the closed form).
+GPU-measured tokens per step against the closed form) and `sampled_accept`
+(spec_accept_sampled at B = 1 and 64 under temperature only, temperature + top-k +
+top-p + a 90% grammar mask, and top-p alone, next to plain spec_accept).
 """
 from __future__ import annotations
 
@@ -376,6 +378,65 @@ def batched(torch, mxs, gen, reps=5):
     return out
 
 
+def _pack_mask_gpu(torch, allowed):
+    """bool [..., V] -> int32 [..., ceil(V/32)] words in the library's mask layout (bit t % 32 of
+    word t // 32), built with torch ops on the GPU (input preparation)."""
+    v = allowed.shape[-1]
+    w = (v + 31) // 32
+    pad = torch.zeros(allowed.shape[:-1] + (w * 32,), dtype=torch.int64, device=allowed.device)
+    pad[..., :v] = allowed.to(torch.int64)
+    bits = pad.view(allowed.shape[:-1] + (w, 32)) << torch.arange(32, device=allowed.device, dtype=torch.int64)
+    words = bits.sum(-1)
+    return torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32).contiguous()
+
+
+SAMPLED_SETTINGS = [  # (name, temperature, top_k, top_p, mask keep fraction)
+    ("tau0.8", 0.8, 0, 1.0, None),
+    ("tau0.8_k50_p0.9_mask0.9", 0.8, 50, 0.9, 0.9),
+    ("p0.95", 1.0, 0, 0.95, None),
+]
+
+
+def sampled_accept(torch, mxs, gen, reps=20):
+    """spec_accept_sampled at K=4, V=128256 for B = 1 and 64 under three transform settings,
+    next to plain spec_accept on the same inputs. Draft tokens are the most probable allowed
+    token of each draft row (always inside the transformed support)."""
+    out = {}
+    for b in (1, 64):
+        base = torch.randn((b, KD + 1, V), generator=gen, device="cuda", dtype=torch.float32) * 3.0
+        tgt = base + torch.randn((b, KD + 1, V), generator=gen, device="cuda", dtype=torch.float32)
+        dft = base[:, :KD].contiguous()
+        del base
+        u = torch.rand((b, KD + 1), generator=gen, device="cuda", dtype=torch.float32)
+        ot = torch.empty((b, KD + 1), dtype=torch.int32, device="cuda")
+        on = torch.empty((b,), dtype=torch.int32, device="cuda")
+        ws = torch.empty((mxs.spec_accept_sampled_workspace_bytes(b, KD, V),), dtype=torch.uint8,
+                         device="cuda")
+        tok_plain = dft.argmax(-1).to(torch.int32).contiguous()
+
+        def plain():
+            mxs.spec_accept(tgt, dft, tok_plain, u, out_tokens=ot, out_num=on, workspace=ws)
+        row = {"plain_us": round(_graph_ms(torch, plain, reps) * 1e3, 1)}
+        for name, tau, k, p, keep in SAMPLED_SETTINGS:
+            mask = None
+            tok = tok_plain
+            if keep is not None:
+                allowed = torch.rand((b, KD + 1, V), generator=gen, device="cuda") < keep
+                mask = _pack_mask_gpu(torch, allowed)
+                tok = dft.masked_fill(~allowed[:, :KD], float("-inf")).argmax(-1).to(torch.int32).contiguous()
+                del allowed
+
+            def call(tau=tau, k=k, p=p, mask=mask, tok=tok):
+                mxs.spec_accept_sampled(tgt, dft, tok, u, tau, k, p, mask, out_tokens=ot, out_num=on,
+                                        workspace=ws)
+            us = _graph_ms(torch, call, reps) * 1e3
+            row[name] = {"us": round(us, 1), "positions_per_s": round(b * (KD + 1) / (us * 1e-6), 1),
+                         "mean_accepted": round(float(on.float().mean()), 3)}
+        out[f"B{b}"] = row
+        del tgt, dft, ws
+    return out
+
+
 def _overlap(torch, p_logits, q_logits):
     p = torch.softmax(p_logits.double(), -1)
     q = torch.softmax(q_logits.double(), -1)
@@ -481,7 +542,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (T sweep, 70B shapes, batched, full 8B step)")
-    ap.add_argument("--only", choices=["headline", "t_sweep_8b", "shapes_70b_t5", "batched_64x5",
+    ap.add_argument("--only", choices=["headline", "t_sweep_8b", "shapes_70b_t5", "batched_64x5", "sampled_accept",
                                        "full_8b_step"],
                     help="run one workload alone (profiling); 'headline' = the default line without "
                          "the secondary workloads")
@@ -534,6 +595,7 @@ def main():
     extras = (("t_sweep_8b", lambda: t_sweep(torch, mxs, pool, gen2)),
               ("shapes_70b_t5", lambda: shapes_70b(torch, mxs, synth, gen2)),
               ("batched_64x5", lambda: batched(torch, mxs, gen2)),
+              ("sampled_accept", lambda: sampled_accept(torch, mxs, gen2)),
               ("full_8b_step", lambda: full_8b_step(torch, mxs, gen2)))
     if args.only and args.only != "headline":
         # one secondary workload alone (for per-workload profiles)

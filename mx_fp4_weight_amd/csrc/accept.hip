@@ -73,7 +73,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
   size_t cmax, csum, cbad, gz, dec, zres, zp;
   // sampling transforms only
-  size_t thr, selmax, selcnt[3], selmass[3], selstate[2];
+  size_t thr, selmax, selcnt, selmass, selstate, selarrive;
   size_t total;
 };
 
@@ -105,16 +105,14 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v, bool sampled = false) {
     off = align256(off + sizeof(uint32_t) * rows);
     L.selmax = off;
     off = align256(off + sizeof(float) * rows * chunks);
-    for (int i = 0; i < 3; ++i) {
-      L.selcnt[i] = off;
-      off = align256(off + sizeof(uint32_t) * rows * kBuckets);
-      L.selmass[i] = off;
-      off = align256(off + sizeof(double) * rows * kBuckets);
-    }
-    for (int i = 0; i < 2; ++i) {
-      L.selstate[i] = off;
-      off = align256(off + kStateBytes * rows);
-    }
+    L.selcnt = off;
+    off = align256(off + sizeof(uint32_t) * rows * kBuckets);
+    L.selmass = off;
+    off = align256(off + sizeof(double) * rows * kBuckets);
+    L.selstate = off;
+    off = align256(off + kStateBytes * rows);
+    L.selarrive = off;
+    off = align256(off + sizeof(uint32_t) * rows);
   }
   L.total = off;
   return L;
@@ -210,13 +208,25 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
     mw = mask_words(tr, s, kd, mask_row(j, kd));
     thr = tr.thr ? tr.thr[rowg] : 0u;
   }
+  // mask words: one per 4 tokens on the vector path; the word index is clamped into the
+  // row (tokens past v are already -inf)
+  uint32_t words[kPer];
+  if constexpr (kT) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = kVec4 ? base + 4 * (threadIdx.x + kThreads * (q / 4)) : base + threadIdx.x + kThreads * q;
+      if (!kVec4 || q % 4 == 0) words[q] = mw ? mw[(e < v ? e : v - 1) >> 5] : 0xFFFFFFFFu;
+      else words[q] = words[q - q % 4];
+    }
+  }
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     bad |= (vals[q] != vals[q]) | (vals[q] == INFINITY);
     const int e = kVec4 ? base + 4 * (threadIdx.x + kThreads * (q / 4)) + (q % 4)
                         : base + threadIdx.x + kThreads * q;
     if constexpr (kT) {
-      if (e < v) vals[q] = live_logit(vals[q], e, mw, thr);
+      const bool ok = ((words[q] >> (e & 31)) & 1u) && order_key(vals[q]) >= thr;
+      vals[q] = ok ? vals[q] : -INFINITY;
     }
     mx = fmaxf(mx, vals[q]);
     if (e == xi) ws.gz[rowg] = vals[q];
@@ -492,13 +502,13 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces
 // finite logits, top digit (11 bits) first, bottom digit (10 bits) last. A pass over
 // the row histograms the current digit of the tokens whose higher digits equal the
 // prefix found so far (counts for top-k; counts and fp64 masses exp((z - max) / tau)
-// of the tokens top-k kept, for top-p). The next pass walks that histogram from the
-// largest key down and takes the lowest non-empty bucket whose tokens still have
-// fewer than k tokens (top-k) or less than P·S mass (top-p) strictly above them; its
-// digit extends the prefix. After the last digit the prefix is the threshold. The
-// histograms live per row in the workspace in three rotating buffers (a pass fills
-// one, reads the previous one and clears the next one); the walk's state is double
-// buffered between passes.
+// of the tokens top-k kept, for top-p), each workgroup in LDS, then added into the
+// row's histogram in the workspace. The last workgroup of the row to finish walks
+// that histogram from the largest key down and takes the lowest non-empty bucket
+// whose tokens still have fewer than k tokens (top-k) or less than P·S mass (top-p)
+// strictly above them; its digit extends the prefix. It then clears the histogram
+// and the arrival counter for the next pass. After the last digit the prefix is the
+// row's threshold.
 constexpr int kSelBuckets = 2048;
 constexpr int kSelDigits = 3;
 __host__ __device__ constexpr int sel_shift(int d) { return d == 0 ? 21 : (d == 1 ? 10 : 0); }
@@ -514,10 +524,12 @@ struct SelState {
 };
 
 struct SelBufs {
-  uint32_t* cnt[3];    // [rows][kSelBuckets]
-  double* mass[3];     // [rows][kSelBuckets]
-  SelState* state[2];  // [rows]
-  float* cmax;         // [rows][chunks] chunk maxima of the allowed finite logits
+  uint32_t* cnt;     // [rows][kSelBuckets]
+  double* mass;      // [rows][kSelBuckets]
+  SelState* state;   // [rows]
+  uint32_t* arrive;  // [rows] workgroups of the current pass that have finished
+  float* cmax;       // [rows][chunks] chunk maxima of the allowed finite logits
+  uint32_t* thr;     // [rows] output thresholds
 };
 
 struct SelArgs {
@@ -530,75 +542,82 @@ static_assert(sizeof(SelState) == 32, "workspace layout assumes a 32-byte select
 // stats kernel's order.
 template <bool kVec4>
 __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t* mw, int base, int v,
-                                    float (&vals)[kPer], int (&idx)[kPer]) {
+                                    float (&vals)[kPer]) {
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    idx[q] = kVec4 ? base + 4 * ((int)threadIdx.x + kThreads * (q / 4)) + (q % 4)
-                   : base + (int)threadIdx.x + kThreads * q;
-    vals[q] = NAN;
-  }
+  for (int q = 0; q < kPer; ++q) vals[q] = NAN;
   if constexpr (kVec4) {
 #pragma unroll
     for (int q = 0; q < kPer / 4; ++q) {
-      const int e = idx[4 * q];
+      const int e = base + 4 * ((int)threadIdx.x + kThreads * q);
       if (e < v) {
         const f32x4 t = *reinterpret_cast<const f32x4*>(z + e);
-        vals[4 * q + 0] = t[0];
-        vals[4 * q + 1] = t[1];
-        vals[4 * q + 2] = t[2];
-        vals[4 * q + 3] = t[3];
+        const uint32_t w = mw ? mw[e >> 5] : 0xFFFFFFFFu;  // the 4 tokens share one mask word
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = ((w >> ((e + i) & 31)) & 1u) && t[i] > -INFINITY && t[i] < INFINITY;
+          vals[4 * q + i] = ok ? t[i] : NAN;
+        }
       }
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (idx[q] < v) vals[q] = z[idx[q]];
-  }
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int t = idx[q];
-    const bool allowed = t < v && (mw ? ((mw[t >> 5] >> (t & 31)) & 1u) != 0u : true);
-    const bool finite = vals[q] > -INFINITY && vals[q] < INFINITY;
-    if (!allowed || !finite) vals[q] = NAN;
+    for (int q = 0; q < kPer; ++q) {
+      const int e = base + (int)threadIdx.x + kThreads * q;
+      if (e < v) {
+        const float t = z[e];
+        const bool ok = (mw ? ((mw[e >> 5] >> (e & 31)) & 1u) != 0u : true) && t > -INFINITY && t < INFINITY;
+        vals[q] = ok ? t : NAN;
+      }
+    }
   }
 }
 
 // Walk the histogram of `digit` (mode 0: counts against k; mode 1: masses against P·S)
-// and extend s.prefix with the boundary bucket. Every thread returns the same state.
-__device__ void sel_resolve(int mode, int digit, const uint32_t* __restrict__ cnt,
-                            const double* __restrict__ mass, const SelArgs& sa, SelState& st,
+// and extend st.prefix with the boundary bucket. Every thread returns the same state.
+// The histogram was filled by atomics of other workgroups of the same launch: it is
+// read with agent-scope atomic loads.
+__device__ void sel_resolve(int mode, int digit, uint32_t* cnt, double* mass, const SelArgs& sa,
+                            SelState& st,
                             double* lds_scan, double* s_excl, int* s_fl, int* s_best,
                             double* s_above) {
   const int nb = 1 << sel_width(digit);
   const int per = nb / kThreads;  // 8 or 4 buckets per thread, in descending key order
   const int tid = threadIdx.x;
+  uint32_t c[8];
+  double w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = nb - 1 - (tid * per + i);
+    c[i] = i < per ? __hip_atomic_load(&cnt[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    const double m = (i < per && mode == 1)
+                         ? __hip_atomic_load(&mass[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.0;
+    w[i] = i < per ? (mode == 0 ? (double)c[i] : m) : 0.0;
+  }
   if (mode == 1 && digit == 0) {
     // S: the mass of every token top-k kept (all buckets of the first top-p digit)
     double t = 0.0;
-    for (int i = 0; i < per; ++i) t += mass[nb - 1 - (tid * per + i)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += w[i];
     st.s1 = block_sum_f64<kThreads>(t, lds_scan);
   }
   const double target = mode == 0 ? (double)sa.top_k : sa.top_p * st.s1;
   double local = 0.0;
-  for (int i = 0; i < per; ++i) {
-    const int b = nb - 1 - (tid * per + i);
-    local += mode == 0 ? (double)cnt[b] : mass[b];
-  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) local += w[i];
   const double incl = block_inclusive_scan_f64<kThreads>(local, lds_scan);
   s_excl[tid] = incl;
   __syncthreads();
   double run = st.carry + (tid > 0 ? s_excl[tid - 1] : 0.0);
   int best = -1;
   double best_above = 0.0;
-  for (int i = 0; i < per; ++i) {
-    const int d = tid * per + i;
-    const int b = nb - 1 - d;
-    const uint32_t c = cnt[b];
-    if (run < target && c > 0u) {
-      best = d;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i < per && run < target && c[i] > 0u) {
+      best = tid * per + i;
       best_above = run;
     }
-    run += mode == 0 ? (double)c : mass[b];
+    run += w[i];
   }
   // descending indices grow with the thread index: the last thread with a candidate
   // holds the lowest qualifying bucket
@@ -617,7 +636,7 @@ __device__ void sel_resolve(int mode, int digit, const uint32_t* __restrict__ cn
   __syncthreads();
 }
 
-// Chunk maxima of the allowed finite logits; clears histogram buffer 0.
+// Chunk maxima of the allowed finite logits; clears the row's histogram and counter.
 template <bool kVec4>
 __global__ __launch_bounds__(kThreads) void sel_prep_kernel(const float* __restrict__ target,
                                                             const float* __restrict__ draft, int kd,
@@ -630,33 +649,34 @@ __global__ __launch_bounds__(kThreads) void sel_prep_kernel(const float* __restr
   const int j = (int)(rowg % per_seq);
   const int c = blockIdx.y;
   float vals[kPer];
-  int idx[kPer];
   chunk_logits<kVec4>(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)),
-                      c * kChunk, v, vals, idx);
+                      c * kChunk, v, vals);
   float mx = -INFINITY;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) mx = fmaxf(mx, vals[q]);  // NaN (removed) is ignored
   mx = block_max<kThreads>(mx, lds_f);
   if (threadIdx.x == 0) sb.cmax[rowg * chunks + c] = mx;
   for (int b = c * kThreads + (int)threadIdx.x; b < kSelBuckets; b += chunks * kThreads) {
-    sb.cnt[0][rowg * kSelBuckets + b] = 0u;
-    sb.mass[0][rowg * kSelBuckets + b] = 0.0;
+    sb.cnt[rowg * kSelBuckets + b] = 0u;
+    sb.mass[rowg * kSelBuckets + b] = 0.0;
   }
+  if (c == 0 && threadIdx.x == 0) sb.arrive[rowg] = 0u;
 }
 
-// Pass h of the walk: resolve the previous pass's digit, then histogram (mode, digit)
-// over this chunk into buffer h % 3, and clear buffer (h + 1) % 3.
+// One pass of the walk: histogram (mode, digit) over this chunk into the row's
+// histogram; the row's last workgroup resolves the digit (and at the end of the walk
+// writes the threshold).
 template <bool kVec4>
 __global__ __launch_bounds__(kThreads) void sel_pass_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, int kd, int v, int chunks,
-    Transform tr, SelBufs sb, SelArgs sa, int h, int mode, int digit, int prev_mode, int prev_digit) {
+    Transform tr, SelBufs sb, SelArgs sa, int first, int mode, int digit, int last) {
   __shared__ uint32_t hc[kSelBuckets];
   __shared__ double hm[kSelBuckets];
   __shared__ double lds_scan[kThreads / kWave];
   __shared__ double s_excl[kThreads];
   __shared__ float lds_f[kThreads / kWave];
   __shared__ int s_fl[2 * (kThreads / kWave)];
-  __shared__ int s_best;
+  __shared__ int s_best, s_last_wg;
   __shared__ double s_above;
   const int64_t rowg = blockIdx.x;
   const int per_seq = 2 * kd + 1;
@@ -666,12 +686,11 @@ __global__ __launch_bounds__(kThreads) void sel_pass_kernel(
   const int tid = threadIdx.x;
 
   float vals[kPer];
-  int idx[kPer];
   chunk_logits<kVec4>(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)),
-                      c * kChunk, v, vals, idx);
+                      c * kChunk, v, vals);
 
   SelState st;
-  if (h == 0) {
+  if (first) {
     float m = -INFINITY;
     for (int cc = tid; cc < chunks; cc += kThreads) m = fmaxf(m, sb.cmax[rowg * chunks + cc]);
     m = block_max<kThreads>(m, lds_f);
@@ -682,18 +701,7 @@ __global__ __launch_bounds__(kThreads) void sel_pass_kernel(
     st.rmax = m;
     st.empty = m == -INFINITY;
   } else {
-    st = sb.state[(h - 1) & 1][rowg];
-    if (!st.empty)
-      sel_resolve(prev_mode, prev_digit, sb.cnt[(h - 1) % 3] + rowg * kSelBuckets,
-                  sb.mass[(h - 1) % 3] + rowg * kSelBuckets, sa, st, lds_scan, s_excl, s_fl,
-                  &s_best, &s_above);
-    if (prev_mode == 0 && prev_digit == kSelDigits - 1) {
-      st.thr_k = st.empty ? 0u : st.prefix;  // top-k resolved
-      if (mode == 1) {
-        st.prefix = 0u;
-        st.carry = 0.0;
-      }
-    }
+    st = sb.state[rowg];
   }
 
   const int nb = 1 << sel_width(digit);
@@ -716,38 +724,44 @@ __global__ __launch_bounds__(kThreads) void sel_pass_kernel(
     }
   }
   __syncthreads();
-  uint32_t* gc = sb.cnt[h % 3] + rowg * kSelBuckets;
-  double* gm = sb.mass[h % 3] + rowg * kSelBuckets;
+  uint32_t* gc = sb.cnt + rowg * kSelBuckets;
+  double* gm = sb.mass + rowg * kSelBuckets;
   for (int b = tid; b < nb; b += kThreads) {
     if (hc[b] != 0u) {
       atomicAdd(&gc[b], hc[b]);
       if (mode == 1) atomicAdd(&gm[b], hm[b]);
     }
   }
-  uint32_t* nc = sb.cnt[(h + 1) % 3] + rowg * kSelBuckets;
-  double* nm = sb.mass[(h + 1) % 3] + rowg * kSelBuckets;
-  for (int b = c * kThreads + tid; b < kSelBuckets; b += chunks * kThreads) {
-    nc[b] = 0u;
-    nm[b] = 0.0;
+  // arrival. The additions are device-scope atomics, performed where every CU reads them
+  // with device-scope loads; each wave waits until its own have completed, so the count
+  // cannot run ahead of them (no L2 write-back is needed: no plain store is shared).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(&sb.arrive[rowg], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    s_last_wg = before == (uint32_t)(chunks - 1);
   }
-  if (c == 0 && tid == 0) sb.state[h & 1][rowg] = st;
-}
+  __syncthreads();
+  if (!s_last_wg) return;
 
-// Resolve the last pass's digit: the row's threshold.
-__global__ __launch_bounds__(kThreads) void sel_finish_kernel(SelBufs sb, SelArgs sa, int h_last,
-                                                              int last_mode, uint32_t* __restrict__ thr) {
-  __shared__ double lds_scan[kThreads / kWave];
-  __shared__ double s_excl[kThreads];
-  __shared__ int s_fl[2 * (kThreads / kWave)];
-  __shared__ int s_best;
-  __shared__ double s_above;
-  const int64_t rowg = blockIdx.x;
-  SelState st = sb.state[h_last & 1][rowg];
-  if (!st.empty)
-    sel_resolve(last_mode, kSelDigits - 1, sb.cnt[h_last % 3] + rowg * kSelBuckets,
-                sb.mass[h_last % 3] + rowg * kSelBuckets, sa, st, lds_scan, s_excl, s_fl, &s_best,
-                &s_above);
-  if (threadIdx.x == 0) thr[rowg] = st.empty ? 0u : st.prefix;
+  // the row's last workgroup: resolve this digit from the complete histogram
+  if (!st.empty) sel_resolve(mode, digit, gc, gm, sa, st, lds_scan, s_excl, s_fl, &s_best, &s_above);
+  const bool k_done = mode == 0 && digit == kSelDigits - 1;
+  if (k_done) {
+    st.thr_k = st.empty ? 0u : st.prefix;  // top-k resolved; a top-p walk starts afresh
+    st.prefix = 0u;
+    st.carry = 0.0;
+  }
+  for (int b = tid; b < nb; b += kThreads) {
+    gc[b] = 0u;
+    gm[b] = 0.0;
+  }
+  if (tid == 0) {
+    sb.arrive[rowg] = 0u;
+    sb.state[rowg] = st;
+    if (last) sb.thr[rowg] = st.empty ? 0u : (k_done ? st.thr_k : st.prefix);
+  }
 }
 
 // ---------------------------------------------------------------- decide + piece totals
@@ -1056,35 +1070,33 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
     const bool use_p = sp->top_p < 1.0f;
     if (use_k || use_p) {
       SelBufs sb;
-      for (int i = 0; i < 3; ++i) {
-        sb.cnt[i] = reinterpret_cast<uint32_t*>(base + L.selcnt[i]);
-        sb.mass[i] = reinterpret_cast<double*>(base + L.selmass[i]);
-      }
-      for (int i = 0; i < 2; ++i) sb.state[i] = reinterpret_cast<SelState*>(base + L.selstate[i]);
+      sb.cnt = reinterpret_cast<uint32_t*>(base + L.selcnt);
+      sb.mass = reinterpret_cast<double*>(base + L.selmass);
+      sb.state = reinterpret_cast<SelState*>(base + L.selstate);
+      sb.arrive = reinterpret_cast<uint32_t*>(base + L.selarrive);
       sb.cmax = reinterpret_cast<float*>(base + L.selmax);
+      sb.thr = reinterpret_cast<uint32_t*>(base + L.thr);
       const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0};
       if (vec4) sel_prep_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb);
       else sel_prep_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       // passes: the top-k digits, then the top-p digits
-      int h = 0, prev_mode = -1, prev_digit = -1;
+      const int npass = kSelDigits * ((use_k ? 1 : 0) + (use_p ? 1 : 0));
+      int h = 0;
       for (int mode = 0; mode < 2; ++mode) {
         if ((mode == 0 && !use_k) || (mode == 1 && !use_p)) continue;
         for (int d = 0; d < kSelDigits; ++d, ++h) {
+          const int first = h == 0, last = h == npass - 1;
           if (vec4)
             sel_pass_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb,
-                                                                     sa, h, mode, d, prev_mode, prev_digit);
+                                                                     sa, first, mode, d, last);
           else
             sel_pass_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb,
-                                                                      sa, h, mode, d, prev_mode, prev_digit);
+                                                                      sa, first, mode, d, last);
           if ((e = hipGetLastError()) != hipSuccess) return e;
-          prev_mode = mode;
-          prev_digit = d;
         }
       }
-      uint32_t* thr = reinterpret_cast<uint32_t*>(base + L.thr);
-      sel_finish_kernel<<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(sb, sa, h - 1, prev_mode, thr);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      uint32_t* thr = sb.thr;
       tr.thr = thr;
     }
   }

@@ -175,7 +175,7 @@ def test_sampled_host_errors():
     lib = mxs.get_lib()
     plain = lib.spec_accept_workspace_bytes(2, 4, 128256)
     sampled = lib.spec_accept_sampled_workspace_bytes(2, 4, 128256)
-    assert sampled >= plain + 2 * 9 * 3 * 2048 * 12   # three rotating count + mass histograms per row
+    assert sampled >= plain + 2 * 9 * 2048 * 12   # a count + mass histogram per logit row
     assert lib.spec_accept_sampled_workspace_bytes(0, 4, 1024) == 0
     for kw in [dict(t=0), dict(u=0), dict(ot=0), dict(on=0), dict(ws=0), dict(d=0), dict(tok=0)]:
         assert _as(**kw) == mxs.MXS_ERR_NULL
