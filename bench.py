@@ -437,6 +437,48 @@ def sampled_accept(torch, mxs, gen, reps=20):
     return out
 
 
+def nv_bytes(n, k):
+    """NVFP4 weight bytes: 4-bit codes + one E4M3 byte per 16 values (the fp32 tensor scale aside)."""
+    return n * k // 2 + n * k // 16
+
+
+def nvfp4_8b(torch, mxs, gen, pool_gb=2.4, reps=3):
+    """NVFP4 weights through the same skinny kernel: the 8B-class layer at T = 1..8, one launch
+    per matrix (no grouped entry point), over a cold pool of > 2 GB of weights."""
+    layer_b = sum(nv_bytes(n, k) for _, n, k in LAYER)
+    n_layers = max(1, math.ceil(pool_gb * 1e9 / layer_b))
+    pool = []
+    for _ in range(n_layers):
+        mats = []
+        for _, n, k in LAYER:
+            w = torch.randn((n, k), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+            mats.append(mxs.nvfp4_quantize(w))
+            del w
+        pool.append(mats)
+    out = {"pool_layers": n_layers, "pool_bytes": layer_b * n_layers}
+    for t in (1, 5, 8):
+        xs = [_rand_bf16(torch, gen, t, k) for (_, _, k) in LAYER]
+        ys = [torch.empty((t, n), dtype=torch.float32, device="cuda") for (_, n, _) in LAYER]
+        row = {}
+        for i, (name, n, k) in enumerate(LAYER):
+            def body(i=i):
+                for li in range(n_layers):
+                    c, s, g = pool[li][i]
+                    mxs.nvfp4_verify_gemm(c, s, g, xs[i], y=ys[i])
+            us = _graph_ms(torch, body, reps) * 1e3 / n_layers
+            byts = nv_bytes(n, k) + t * k * 2 + t * n * 4
+            row[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
+        tot_b = sum(nv_bytes(n, k) + t * k * 2 + t * n * 4 for _, n, k in LAYER)
+        tot_us = sum(v["us"] for v in row.values())
+        row["layer_us"] = round(tot_us, 2)
+        row["layer_GBps"] = round(tot_b / (tot_us * 1e-6) / 1e9, 1)
+        row["layer_pct_of_hbm_peak"] = round(100 * tot_b / (tot_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2)
+        out[f"T{t}"] = row
+        del xs, ys
+    del pool
+    return out
+
+
 def _overlap(torch, p_logits, q_logits):
     p = torch.softmax(p_logits.double(), -1)
     q = torch.softmax(q_logits.double(), -1)
@@ -543,7 +585,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (T sweep, 70B shapes, batched, full 8B step)")
     ap.add_argument("--only", choices=["headline", "t_sweep_8b", "shapes_70b_t5", "batched_64x5", "sampled_accept",
-                                       "full_8b_step"],
+                                       "nvfp4_8b", "full_8b_step"],
                     help="run one workload alone (profiling); 'headline' = the default line without "
                          "the secondary workloads")
     ap.add_argument("--seed", type=int, default=2)
@@ -596,6 +638,7 @@ def main():
               ("shapes_70b_t5", lambda: shapes_70b(torch, mxs, synth, gen2)),
               ("batched_64x5", lambda: batched(torch, mxs, gen2)),
               ("sampled_accept", lambda: sampled_accept(torch, mxs, gen2)),
+              ("nvfp4_8b", lambda: nvfp4_8b(torch, mxs, gen2)),
               ("full_8b_step", lambda: full_8b_step(torch, mxs, gen2)))
     if args.only and args.only != "headline":
         # one secondary workload alone (for per-workload profiles)

@@ -139,6 +139,43 @@ mxs_status mxfp4_verify_gemm_grouped(const mxs_gemm_problem* problems, int32_t c
                                      int64_t m, void* stream);
 
 /*
+ * nvfp4_quantize — fp32 W[n, k] -> NVFP4 [M11 §12: E2M1 values, one E4M3 scale
+ * per 16 values, one fp32 scale for the tensor; 4.5 bits/value counting the
+ * block scales].
+ *
+ * g = amax(|W|) / (6 * 448) over the finite entries (1 for an all-zero tensor);
+ * block scale = E4M3 (bias 7, subnormals, NaN = 0x7F, largest 448) of
+ * amax_block / (6 g), nearest with ties to the even fraction, saturating; each
+ * value is coded from w / (E4M3 * g) as mxfp4_quantize codes (nearest, ties to
+ * even, saturating at 6, sign of zero kept). Each step is one correctly rounded
+ * fp32 operation. A block holding a NaN or +-inf gets scale 0x7F and codes 0,
+ * and raises MXS_FLAG_NONFINITE; such entries are left out of amax.
+ *
+ * w             [n, k] fp32, 16-byte aligned; k % 16 == 0, k >= 16.
+ * codes         [n, k/2] bytes as mxfp4_quantize (low nibble = even column), 2-byte aligned.
+ * scales        [n, k/16] E4M3 bytes.
+ * global_scale  one fp32 in device memory: g (written; also used as scratch).
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status nvfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                          float* global_scale, int32_t* dev_flags, void* stream);
+
+/*
+ * nvfp4_verify_gemm — Y[m, n] = X[m, k] · Ŵ[n, k]ᵀ with
+ * Ŵ = E2M1(code) * E4M3(scale) * g [M11 §12], fp32 accumulation of exact bf16
+ * products (E2M1 * E4M3 is exact in bf16), g applied to each output once.
+ * Layouts as nvfp4_quantize; x bf16 [m, k] row-major; y fp32 [m, n].
+ * k % 512 == 0 (no other k is supported by this kernel), 1 <= m <= 65536
+ * (positions beyond 16 run as further 16-position tiles that re-read the
+ * weights: the batched dense path is MX-FP4 only). codes, scales, x 16-byte
+ * aligned; y, global_scale 4-byte aligned.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                             int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
+                             void* stream);
+
+/*
  * spec_accept_workspace_bytes — device workspace spec_accept needs for
  * (b, kd, v). Returns 0 when the sizes are out of range.
  */

@@ -31,7 +31,8 @@ FLAG_RESIDUAL_ZERO = 8
 
 EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_verify_gemm",
            "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept",
-           "spec_accept_sampled_workspace_bytes", "spec_accept_sampled"]
+           "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
+           "nvfp4_verify_gemm"]
 
 
 class GemmProblem(ctypes.Structure):
@@ -73,6 +74,10 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_sampled.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp, vp]
     lib.spec_accept_sampled.restype = ctypes.c_int
+    lib.nvfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.nvfp4_quantize.restype = ctypes.c_int
+    lib.nvfp4_verify_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp, vp]
+    lib.nvfp4_verify_gemm.restype = ctypes.c_int
     return lib
 
 
@@ -271,3 +276,45 @@ def spec_accept_sampled(target: torch.Tensor, draft: torch.Tensor | None, tokens
                                          _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
                                          _ptr(dev_flags), _stream(stream)), "spec_accept_sampled")
     return out_tokens, out_num
+
+
+def nvfp4_quantize(w: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                   global_scale: torch.Tensor | None = None, dev_flags: torch.Tensor | None = None,
+                   stream=None):
+    """fp32 W[n, k] -> (codes uint8 [n, k/2], scales uint8 [n, k/16] E4M3, global_scale fp32 [1])."""
+    _want(w, torch.float32, "w")
+    n, k = w.shape
+    dev = w.device
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        global_scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    _want(codes, torch.uint8, "codes")
+    _want(scales, torch.uint8, "scales")
+    _want(global_scale, torch.float32, "global_scale")
+    _want(dev_flags, torch.int32, "dev_flags")
+    _check(get_lib().nvfp4_quantize(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(global_scale),
+                                    _ptr(dev_flags), _stream(stream)), "nvfp4_quantize")
+    return codes, scales, global_scale
+
+
+def nvfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
+                      x: torch.Tensor, y: torch.Tensor | None = None, stream=None):
+    """Y[m, n] = X[m, k] · Ŵᵀ over NVFP4 weights (codes [n, k/2], E4M3 scales [n, k/16], fp32 g)."""
+    _want(codes, torch.uint8, "codes")
+    _want(scales, torch.uint8, "scales")
+    _want(global_scale, torch.float32, "global_scale")
+    _want(x, torch.bfloat16, "x")
+    n = codes.shape[0]
+    k = codes.shape[1] * 2
+    m = x.shape[0]
+    if x.shape != (m, k) or scales.shape != (n, k // 16):
+        raise ValueError("shape mismatch")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _want(y, torch.float32, "y")
+    _check(get_lib().nvfp4_verify_gemm(_ptr(codes), _ptr(scales), _ptr(global_scale), n, k, _ptr(x), m,
+                                       _ptr(y), _stream(stream)), "nvfp4_verify_gemm")
+    return y

@@ -108,6 +108,35 @@ mxs_status mxfp4_verify_gemm_grouped(const mxs_gemm_problem* problems, int32_t c
   return MXS_OK;
 }
 
+mxs_status nvfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                          float* global_scale, int32_t* dev_flags, void* stream) {
+  if (!w || !codes || !scales || !global_scale) return MXS_ERR_NULL;
+  if (n < 1 || k < 16 || k % 16 != 0) return MXS_ERR_SHAPE;
+  if (n > (int64_t(1) << 40) / k) return MXS_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(codes, 2) || !aligned(global_scale, 4) || !aligned(dev_flags, 4))
+    return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_nvfp4_quantize(w, n, k, codes, scales, global_scale, dev_flags,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+mxs_status nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                             int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
+                             void* stream) {
+  if (!codes || !scales || !global_scale || !x || !y) return MXS_ERR_NULL;
+  if (n < 1 || n > (int64_t(1) << 31) - 1 || k < 512 || k % 512 != 0 || k > (int64_t(1) << 24) ||
+      m < 1 || m > 65536)
+    return MXS_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(global_scale, 4) || !aligned(x, 16) ||
+      !aligned(y, 4))
+    return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_nvfp4_verify_gemm(codes, scales, global_scale, n, k, x, m, y,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
   if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
   return mxs::accept_workspace_bytes(b, kd, v, false);

@@ -47,6 +47,34 @@ __device__ inline float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(bits);
 }
 
+// E4M3 scale byte (NVFP4 block scale) -> fp32: bias 7, exponent 0 subnormal (m·2^-9),
+// S.1111.111 NaN. Exact.
+__device__ inline float e4m3_to_f32(uint32_t s) {
+  const uint32_t e = (s >> 3) & 15u, m = s & 7u;
+  float v = e == 0u ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  v = (e == 15u && m == 7u) ? __uint_as_float(0x7fc00000u) : v;
+  return (s & 0x80u) ? -v : v;
+}
+
+// Eight E2M1 codes × an arbitrary fp32 block scale -> 8 bf16. The conversion
+// instruction applies only the power-of-two part of its scale operand, so the
+// codes are decoded at scale 1 into fp32, multiplied by the scale (E2M1 × E4M3
+// has at most 6 significant bits: exact) and packed to bf16 (exact as well).
+__device__ inline bf16x8 decode8_scaled(uint32_t c, float scale) {
+  bf16x8 r;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    f32x2 f;
+    if (h == 0) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    else if (h == 1) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    else if (h == 2) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    else f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+    r[2 * h] = (__bf16)(f[0] * scale);
+    r[2 * h + 1] = (__bf16)(f[1] * scale);
+  }
+  return r;
+}
+
 // Eight E2M1 codes (one 32-bit word, element j in nibble j) × scale -> 8 bf16.
 __device__ inline bf16x8 decode8(uint32_t c, float scale) {
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0);
@@ -96,10 +124,12 @@ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // consecutive 16-byte units, so ds_read_b128 has no bank conflicts.
 __device__ inline int xunit(int grp, int d, int t, int g, int mt) { return ((grp * 4 + d) * mt + t) * 4 + g; }
 
-template <int R, int G>
+// kNv: NVFP4 weights (an E4M3 scale per 16 values: 32 scale bytes per 4 groups of a row)
+// instead of MX-FP4 (an E8M0 scale per 32 values: 16 bytes per 4 groups).
+template <int R, int G, bool kNv>
 struct Block {
-  u32x4 c[R][G];        // 16 code bytes per row tile and group
-  u32x4 s[R][G / 4];    // 16 scale bytes = 4 groups x 4 blocks of the row
+  u32x4 c[R][G];                      // 16 code bytes per row tile and group
+  u32x4 s[R][kNv ? G / 2 : G / 4];    // scale bytes of the row for these groups
 };
 
 // Up to kMaxGroup independent products with the same k and m share one launch
@@ -113,6 +143,7 @@ struct Problem {
   const uint8_t* scales;
   const uint16_t* x;
   float* y;
+  const float* gscale;  // NVFP4 tensor scale (device), null for MX-FP4
   int n, nrb, y_vec4, pad;
 };
 
@@ -122,7 +153,7 @@ struct Group {
   int count;
 };
 
-template <int R, int G, int D>
+template <int R, int G, int D, bool kNv>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
                                                                          int nsub, int phases,
                                                                          int ngroups_p) {
@@ -136,6 +167,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   const int n = grp.p[pi].n;
   const int nrb = grp.p[pi].nrb;
   const int y_vec4 = grp.p[pi].y_vec4;
+  const float gscale = kNv ? *grp.p[pi].gscale : 1.0f;
   const int wg = (int)blockIdx.x - grp.wg_start[pi];               // index among this problem's
   const int ngrid = grp.wg_start[pi + 1] - grp.wg_start[pi];        // workgroups
   const int W = blockDim.x / kWave;
@@ -174,7 +206,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   const int my_blocks = wg < nrb ? (nrb - 1 - wg) / ngrid + 1 : 0;
   const int nunits = my_blocks * upr;
 
-  auto load = [&](int u, Block<R, G>& b) {
+  const uint32_t srow = kNv ? (uint32_t)(k >> 4) : (uint32_t)kb;  // scale bytes per row
+  auto load = [&](int u, Block<R, G, kNv>& b) {
     const int rb = wg + (u / upr) * ngrid;
     const int uu = u % upr;
     const int gl0 = gs + (uu % nsub) * G;            // first group inside the phase
@@ -184,7 +217,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     const int rows = u < nunits ? min(16 * R, n - row0) : 0;
     const int rowc = u < nunits ? row0 : 0;
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)rowc * kb, (uint32_t)rows * (uint32_t)kb);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)rowc * srow, (uint32_t)rows * srow);
     // The whole offset goes in voffset (soffset = 0): the range check of a raw
     // buffer load covers voffset + the immediate only.
 #pragma unroll
@@ -203,8 +236,16 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
       const bool ok = gl0 + 4 * q < ngroups_p && grp0 < ngroups;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const uint32_t off = ok ? (uint32_t)(16 * i + r) * (uint32_t)kb + (uint32_t)grp0 * 4 : kOutOfRange;
-        b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+        if constexpr (kNv) {
+          // 8 scale bytes per group: two 16-byte loads for 4 groups
+          const uint32_t off = ok ? (uint32_t)(16 * i + r) * srow + (uint32_t)grp0 * 8 : kOutOfRange;
+          b.s[i][2 * q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+          b.s[i][2 * q + 1] =
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, ok ? off + 16u : kOutOfRange, 0, 0));
+        } else {
+          const uint32_t off = ok ? (uint32_t)(16 * i + r) * srow + (uint32_t)grp0 * 4 : kOutOfRange;
+          b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+        }
       }
     }
   };
@@ -241,7 +282,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     for (int d = 0; d < 4; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   int parity = 0;
 
-  auto compute = [&](int u, const Block<R, G>& b) {
+  auto compute = [&](int u, const Block<R, G, kNv>& b) {
     const int uu = u % upr;
     if (phases > 1 && uu != 0 && uu % nsub == 0) {
       // first unit of a later phase: stage its activations once every wave is done
@@ -258,14 +299,26 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
       bf16x8 bb[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) bb[d] = __builtin_bit_cast(bf16x8, smem[xlane + gl * 16 + d]);
-      float sf[R];
+      float sf[R], sf2[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) sf[i] = e8m0_to_f32((b.s[i][j / 4][j % 4] >> (8 * g)) & 0xffu);
+      for (int i = 0; i < R; ++i) {
+        if constexpr (kNv) {
+          // this lane's 32 codes are NVFP4 blocks 2g and 2g+1 of group j: scale bytes
+          // 8·(j % 4) + 2g and + 1 of the 32 loaded for the group's quadruple
+          const int wi = (j % 4) * 2 + g / 2;
+          const uint32_t word = b.s[i][(j / 4) * 2 + wi / 4][wi % 4] >> (16 * (g & 1));
+          sf[i] = e4m3_to_f32(word & 0xffu);
+          sf2[i] = e4m3_to_f32((word >> 8) & 0xffu);
+        } else {
+          sf[i] = e8m0_to_f32((b.s[i][j / 4][j % 4] >> (8 * g)) & 0xffu);
+          sf2[i] = sf[i];
+        }
+      }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          const bf16x8 a = decode8(b.c[i][j][d], sf[i]);
+          const bf16x8 a = kNv ? decode8_scaled(b.c[i][j][d], d < 2 ? sf[i] : sf2[i]) : decode8(b.c[i][j][d], sf[i]);
           acc[i][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[d], acc[i][d], 0, 0, 0);
         }
       }
@@ -281,6 +334,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     for (int i = wave; i < R; i += W) {
       f32x4 sum = rp[i * kWave + lane];
       for (int w = 1; w < W; ++w) sum += rp[(w * R + i) * kWave + lane];
+      if constexpr (kNv) sum *= gscale;
       // lane holds C[4g + e][r]: output row row0 + 16 i + 4 g + e, position t
       const int orow = row0 + 16 * i + 4 * g;
       if (t_ok) {
@@ -306,7 +360,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   // loads of unit u + D go out as soon as unit u has been computed; past the last
   // unit the descriptors have no records and nothing is read. The scheduling
   // barriers keep each prefetch ahead of the next compute's waits.
-  Block<R, G> buf[D];
+  Block<R, G, kNv> buf[D];
   stage(0);
 #pragma unroll
   for (int i = 0; i < D; ++i) load(i, buf[i]);
@@ -708,11 +762,11 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp) {
   return false;
 }
 
-template <int R, int G, int D>
+template <int R, int G, int D, bool kNv = false>
 hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
-                       int64_t k, int64_t m, hipStream_t stream) {
+                       int64_t k, int64_t m, hipStream_t stream, const float* gscale = nullptr) {
   static std::atomic<bool> done[kMaxDevices];
-  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D>, done);
+  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv>, done);
   if (e != hipSuccess) return e;
   Group grp{};
   grp.count = count;
@@ -727,13 +781,13 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     int64_t share = pp.phases > 1 ? nrb : (budget * nrb + total_rb - 1) / total_rb;
     if (share > nrb) share = nrb;
     if (share < 1) share = 1;
-    grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, (int)pv[i].n, (int)nrb,
+    grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, gscale, (int)pv[i].n, (int)nrb,
                        y_vec4_ok(pv[i].y, pv[i].n), 0};
     grp.wg_start[i] = start;
     start += (int)share;
   }
   grp.wg_start[count] = start;
-  gemm_skinny_kernel<R, G, D><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(pp.waves * kWave),
+  gemm_skinny_kernel<R, G, D, kNv><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(pp.waves * kWave),
                              pp.lds, stream>>>(grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p);
   return hipGetLastError();
 }
@@ -838,6 +892,23 @@ Config choose(int64_t n, int64_t k) {
 hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
   return launch_cfg(choose(n, k), codes, scales, n, k, x, m, y, stream);
+}
+
+// NVFP4 weights: the skinny kernel for every m (a 16-position tile per grid row), k % 512 == 0
+// and 16-byte aligned scales checked by the caller.
+hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                                    int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
+                                    hipStream_t stream) {
+  const mxs_problem_view pv{codes, scales, x, y, n};
+  const Config c = choose(n, k);
+  PhasePlan pp;
+  if (!plan_phases(k, m < 16 ? m : 16, c.R, c.G, pp)) return hipErrorInvalidValue;
+  if (pp.phases > 1) {
+    PhasePlan pp2;
+    if ((n + 31) / 32 >= kCUs && plan_phases(k, m < 16 ? m : 16, 2, c.G, pp2))
+      return launch_main<2, 4, 2, true>(Config{2, c.G, c.D, c.per_cu}, pp2, &pv, 1, k, m, stream, gscale);
+  }
+  return launch_main<1, 4, 2, true>(c, pp, &pv, 1, k, m, stream, gscale);
 }
 
 hipError_t launch_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,

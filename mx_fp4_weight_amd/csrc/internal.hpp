@@ -33,6 +33,13 @@ struct SamplingParams {
   const uint32_t* mask;   // [b][kd+1][ceil(v/32)] or null
 };
 
+hipError_t launch_nvfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                                 float* gscale, int32_t* flags, hipStream_t stream);
+
+hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                                    int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
+                                    hipStream_t stream);
+
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
 
 // sp == nullptr: the plain laws (no transform kernels, the same code as without transforms).

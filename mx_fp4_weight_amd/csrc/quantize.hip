@@ -104,6 +104,126 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   if (__any(live && bad) && (threadIdx.x & (kWave - 1)) == 0) raise_flag(flags, MXS_FLAG_NONFINITE);
 }
 
+// ---------------------------------------------------------------- NVFP4
+// NVFP4 ("Module 11. Speculative Decoding and Quantization" §12): E2M1 values,
+// an E4M3 scale per 16 values and one fp32 scale for the tensor. The tensor
+// scale is g = amax / (6 · 448) over the finite entries (1 for an all-zero
+// tensor); a block's scale is E4M3(amax_block / (6 g)) rounded to nearest, ties
+// to the even fraction, saturating at 448; a value is coded from w / (E4M3 · g)
+// with the MX-FP4 rounding. Every operation is one correctly rounded fp32
+// operation, in that order.
+
+// amax over the finite entries as fp32 bits (non-negative floats order like their bits)
+__global__ void nv_clear_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
+
+__global__ __launch_bounds__(256) void nv_amax_kernel(const float* __restrict__ w, int64_t nvec,
+                                                      uint32_t* __restrict__ amax_bits) {
+  uint32_t m = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(w + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = v[j] & 0x7fffffffu;
+      if (a < 0x7f800000u && a > m) m = a;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t t = __shfl_xor(m, o);
+    m = t > m ? t : m;
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0 && m != 0u) atomicMax(amax_bits, m);
+}
+
+// in: amax bits; out: g as fp32
+__global__ void nv_global_kernel(uint32_t* gbits) {
+  const float amax = __uint_as_float(*gbits);
+  const float g = amax == 0.0f ? 1.0f : amax / 2688.0f;  // 6 * 448
+  *reinterpret_cast<float*>(gbits) = g;
+}
+
+// Non-negative fp32 -> E4M3 byte, nearest with ties to the even fraction, saturating at 448.
+__device__ inline uint32_t e4m3_rne(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;
+  const uint32_t b = __float_as_uint(t);
+  const int e = (int)(b >> 23) - 127;
+  if (e < -6) return (uint32_t)__builtin_rintf(t * 512.0f);  // multiples of 2^-9: 0 .. 8
+  const uint32_t mant = b & 0x7fffffu;
+  const uint32_t keep = mant >> 20, rem = mant & 0xfffffu;
+  const uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (keep & 1u));
+  const uint32_t byte = ((uint32_t)(e + 7) << 3) + keep + up;
+  return byte > 0x7Eu ? 0x7Eu : byte;
+}
+
+__device__ inline float e4m3_value(uint32_t s) {
+  const uint32_t e = (s >> 3) & 15u, m = s & 7u;
+  return e == 0u ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 code of an already scaled fp32 value: nearest, ties to the even code, saturating at 6.
+__device__ inline uint32_t e2m1_code_of(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 31) << 3;
+  const float a = fabsf(x);
+  uint32_t c = 0;
+  c += a > 0.25f;
+  c += a >= 0.75f;
+  c += a > 1.25f;
+  c += a >= 1.75f;
+  c += a > 2.5f;
+  c += a >= 3.5f;
+  c += a > 5.0f;
+  return sign | c;
+}
+
+// 4 lanes per 16-value block (one 16-byte load each); a lane writes its 4 codes (2 bytes).
+__global__ __launch_bounds__(256) void nv_quantize_kernel(const float* __restrict__ w, int64_t nblocks,
+                                                          const float* __restrict__ gscale,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          int32_t* __restrict__ flags) {
+  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = gtid >> 2;
+  const int sub = (int)(gtid & 3);
+  const bool live = blk < nblocks;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (live) v = *reinterpret_cast<const u32x4*>(w + blk * 16 + sub * 4);
+  uint32_t amax = 0;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = v[i] & 0x7fffffffu;
+    bad |= a >= 0x7f800000u;
+    amax = (a < 0x7f800000u && a > amax) ? a : amax;
+  }
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    const uint32_t t = __shfl_xor(amax, o);
+    amax = t > amax ? t : amax;
+    bad |= __shfl_xor(bad, o);
+  }
+  const float g = *gscale;
+  const float denom = 6.0f * g;
+  const uint32_t sbyte = e4m3_rne(__uint_as_float(amax) / denom);
+  const float d = e4m3_value(sbyte) * g;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = d == 0.0f ? __uint_as_float(v[i] & 0x80000000u) : __uint_as_float(v[i]) / d;
+    packed |= e2m1_code_of(x) << (4 * i);
+  }
+  uint32_t sb = sbyte;
+  if (bad) {
+    packed = 0;
+    sb = 0x7Fu;
+  }
+  if (live) {
+    *reinterpret_cast<uint16_t*>(codes + blk * 8 + sub * 2) = (uint16_t)packed;
+    if (sub == 0) scales[blk] = (uint8_t)sb;
+  }
+  if (__any(live && bad) && (threadIdx.x & (kWave - 1)) == 0) raise_flag(flags, MXS_FLAG_NONFINITE);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
@@ -112,6 +232,26 @@ hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes,
   const int64_t threads = nblocks * 8;
   const int64_t grid = (threads + 255) / 256;
   quantize_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(w, nblocks, codes, scales, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                                 float* gscale, int32_t* flags, hipStream_t stream) {
+  uint32_t* gbits = reinterpret_cast<uint32_t*>(gscale);
+  nv_clear_kernel<<<1, 1, 0, stream>>>(gbits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nvec = n * k / 4;
+  int64_t grid = (nvec + 255) / 256;
+  grid = grid > 4096 ? 4096 : grid;
+  nv_amax_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(w, nvec, gbits);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  nv_global_kernel<<<1, 1, 0, stream>>>(gbits);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nblocks = n * (k / 16);
+  const int64_t threads = nblocks * 4;
+  nv_quantize_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(
+      w, nblocks, gscale, codes, scales, flags);
   return hipGetLastError();
 }
 

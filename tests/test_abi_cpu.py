@@ -25,7 +25,7 @@ def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)
-    keep = [n for n in names if n.startswith(("mxs_", "mxfp4_", "spec_accept"))]
+    keep = [n for n in names if n.startswith(("mxs_", "mxfp4_", "nvfp4_", "spec_accept"))]
     return sorted(set(keep))
 
 
@@ -188,3 +188,35 @@ def test_sampled_host_errors():
     need = lib.spec_accept_sampled_workspace_bytes(1, 4, 1024)
     assert _as(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
     assert _as(wsb=need, tau=0.7, k=50, p=0.9, mask=0x8000) == mxs.MXS_ERR_DEVICE
+
+
+def _nq(w=0x1000, n=4, k=64, codes=0x2000, scales=0x3000, g=0x4000, flags=None):
+    f = lambda a: P(a) if a else None
+    return mxs.get_lib().nvfp4_quantize(f(w), n, k, f(codes), f(scales), f(g), f(flags), None)
+
+
+def test_nvfp4_quantize_host_errors():
+    for kw in [dict(w=0), dict(codes=0), dict(scales=0), dict(g=0)]:
+        assert _nq(**kw) == mxs.MXS_ERR_NULL
+    for kw in [dict(k=24), dict(k=0), dict(n=0), dict(k=8)]:
+        assert _nq(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(w=0x1008), dict(codes=0x2001), dict(g=0x4002), dict(flags=0x5001)]:
+        assert _nq(**kw) == mxs.MXS_ERR_ALIGN
+    assert _nq(scales=0x3001, k=16) == mxs.MXS_ERR_DEVICE   # scales may have any alignment
+    assert _nq() == mxs.MXS_ERR_DEVICE
+
+
+def _ng(codes=0x1000, scales=0x2000, g=0x3000, n=4, k=512, x=0x4000, m=5, y=0x5000):
+    f = lambda a: P(a) if a else None
+    return mxs.get_lib().nvfp4_verify_gemm(f(codes), f(scales), f(g), n, k, f(x), m, f(y), None)
+
+
+def test_nvfp4_gemm_host_errors():
+    for kw in [dict(codes=0), dict(scales=0), dict(g=0), dict(x=0), dict(y=0)]:
+        assert _ng(**kw) == mxs.MXS_ERR_NULL
+    for kw in [dict(k=256), dict(k=768), dict(k=0), dict(n=0), dict(m=0), dict(m=65537)]:
+        assert _ng(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(codes=0x1008), dict(scales=0x2004), dict(g=0x3002), dict(x=0x4008), dict(y=0x5002)]:
+        assert _ng(**kw) == mxs.MXS_ERR_ALIGN
+    assert _ng(m=65536, k=1024) == mxs.MXS_ERR_DEVICE
+    assert _ng() == mxs.MXS_ERR_DEVICE
