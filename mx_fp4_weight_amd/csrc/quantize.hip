@@ -133,7 +133,17 @@ __global__ __launch_bounds__(256) void nv_amax_kernel(const float* __restrict__ 
     const uint32_t t = __shfl_xor(m, o);
     m = t > m ? t : m;
   }
-  if ((threadIdx.x & (kWave - 1)) == 0 && m != 0u) atomicMax(amax_bits, m);
+  // one atomic per workgroup, and only when it can raise the value: thousands of
+  // read-modify-writes of one address otherwise serialize in L2
+  __shared__ uint32_t wmax[256 / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 1; i < 256 / kWave; ++i) m = wmax[i] > m ? wmax[i] : m;
+    if (m != 0u && m > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(amax_bits, m);
+  }
 }
 
 // in: amax bits; out: g as fp32
@@ -243,7 +253,7 @@ hipError_t launch_nvfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* 
   if (e != hipSuccess) return e;
   const int64_t nvec = n * k / 4;
   int64_t grid = (nvec + 255) / 256;
-  grid = grid > 4096 ? 4096 : grid;
+  grid = grid > 1024 ? 1024 : grid;
   nv_amax_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(w, nvec, gbits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   nv_global_kernel<<<1, 1, 0, stream>>>(gbits);
