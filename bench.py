@@ -353,6 +353,28 @@ def batched(torch, mxs, gen, reps=5):
                     "mfma_util_vs_bf16_dense_peak": round(flops / (us * 1e-6) / 2.5e15, 4),
                     "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                     "kernel": "gemm_dense_kernel (v_mfma_f32_16x16x32_bf16; peak 2.5 PFLOP/s dense bf16)"}}
+    # the same product with MX-quantized activations (W4A8 / W4A4) on the block-scaled MFMA
+    for fmt, name, peak in ((mxs.ACT_FP8, "gemm_w4a8", 5.0e15), (mxs.ACT_FP4, "gemm_w4a4", 10.1e15)):
+        acts = [mxs.mx_quantize_act(x, fmt) for (_, _, x) in copies]
+
+        def body_q(fmt=fmt):
+            for (_, _, x), (ac, asc) in zip(copies, acts):
+                mxs.mx_quantize_act(x, fmt, codes=ac, scales=asc)
+
+        def body_g(fmt=fmt, acts=acts):
+            for (c, s, _), (ac, asc) in zip(copies, acts):
+                mxs.mx_verify_gemm_act(c, s, ac, asc, fmt, y=y)
+        us_g = _graph_ms(torch, body_g, reps) * 1e3 / len(copies)
+        us_q = _graph_ms(torch, body_q, reps * 4) * 1e3 / len(copies)
+        abytes = acts[0][0].numel() + acts[0][1].numel()
+        out[name] = {"us": round(us_g, 1), "quantize_act_us": round(us_q, 1),
+                     "TFLOPs": round(flops / (us_g * 1e-6) / 1e12, 1),
+                     "mfma_util_vs_dense_peak": round(flops / (us_g * 1e-6) / peak, 4),
+                     "GBps": round((mx_bytes(n, k) + abytes + m * n * 4) / (us_g * 1e-6) / 1e9, 1),
+                     "kernel": "gemm_act_kernel (v_mfma_scale_f32_16x16x128_f8f6f4, "
+                               f"MX-FP4 x {'MX-FP8' if fmt == mxs.ACT_FP8 else 'MX-FP4'}; "
+                               f"dense peak {peak / 1e15:.1f} PFLOP/s)"}
+        del acts
     del copies
     b = 64
     base = torch.randn((b, KD + 1, V), generator=gen, device="cuda", dtype=torch.float32) * 3.0

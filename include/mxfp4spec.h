@@ -62,6 +62,11 @@ typedef enum mxs_status {
 #define MXS_FLAG_Q_ZERO 4        /* a draft token with draft probability 0 */
 #define MXS_FLAG_RESIDUAL_ZERO 8 /* a rejection whose residual (p - q)+ had zero mass */
 
+/* Activation formats of the W4A8 / W4A4 product (the element-format numbers of the
+   block-scaled matrix instruction). */
+#define MXS_ACT_FP8 0  /* MX-FP8: E4M3 elements, E8M0 scale per 32 */
+#define MXS_ACT_FP4 4  /* MX-FP4: E2M1 elements, E8M0 scale per 32 */
+
 #define MXS_ABI_VERSION 1
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -174,6 +179,46 @@ mxs_status nvfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, 
 mxs_status nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                              int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
                              void* stream);
+
+/*
+ * mx_quantize_act — bf16 activations X[m, k] -> MX-FP8 or MX-FP4 [M11 §11: W4A8 /
+ * W4A4 quantize activations as well as weights; §12: E4M3 = 8-bit float with 4
+ * exponent and 3 fraction bits, E8M0 power-of-two scale; news page, "Microscaling
+ * FP4 (MX-FP4) Integration": 32 values per scale].
+ *
+ * Per 32-value block along k: e = floor(log2 amax) - emax (8 for E4M3, whose
+ * largest value is 448 = 1.75 * 2^8; 2 for E2M1), clamped to [-127, 127], scale
+ * byte e + 127 (0 for an all-zero block); each value v * 2^-e goes to the nearest
+ * element value with ties to the even fraction, saturating (at 448 or 6), sign
+ * kept on zeros. A block holding a NaN or +-inf gets scale 0xFF and codes 0, and
+ * raises MXS_FLAG_NONFINITE.
+ *
+ * x       [m, k] bf16, 16-byte aligned; k % 32 == 0.
+ * fmt     MXS_ACT_FP8 or MXS_ACT_FP4 (else MXS_ERR_VALUE).
+ * codes   FP8: [m, k] E4M3 bytes, 8-byte aligned. FP4: [m, k/2] as mxfp4_quantize
+ *         (low nibble = even column), 4-byte aligned.
+ * scales  [m, k/32] E8M0 bytes.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN, MXS_ERR_VALUE.
+ */
+mxs_status mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,
+                           uint8_t* scales, int32_t* dev_flags, void* stream);
+
+/*
+ * mx_verify_gemm_act — Y[m, n] = X^[m, k] · Ŵ[n, k]ᵀ: MX-FP4 weights (mxfp4_quantize
+ * layout) times MX-quantized activations (mx_quantize_act layout, format fmt), the
+ * W4A8 / W4A4 forms of the verify GEMM [M11 §11, §12]. Products of the two decoded
+ * operands (element × element × 2^(sw + sx - 254)) are exact; they are summed in
+ * fp32 by the block-scaled matrix instruction, so Y is the product of the QUANTIZED
+ * activations (a different result from mxfp4_verify_gemm on the bf16 ones).
+ * Built for the batched verification (m = sequences × positions); any 1 <= m <= 65536
+ * is accepted.
+ *
+ * k % 128 == 0, k <= 2^24; codes and act_codes 16-byte aligned; y fp32 [m, n], 4-byte
+ * aligned. Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN, MXS_ERR_VALUE (fmt).
+ */
+mxs_status mx_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                              const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt, int64_t m,
+                              float* y, void* stream);
 
 /*
  * spec_accept_workspace_bytes — device workspace spec_accept needs for

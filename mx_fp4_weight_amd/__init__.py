@@ -32,7 +32,7 @@ FLAG_RESIDUAL_ZERO = 8
 EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_verify_gemm",
            "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept",
            "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
-           "nvfp4_verify_gemm"]
+           "nvfp4_verify_gemm", "mx_quantize_act", "mx_verify_gemm_act"]
 
 
 class GemmProblem(ctypes.Structure):
@@ -78,6 +78,10 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_quantize.restype = ctypes.c_int
     lib.nvfp4_verify_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp, vp]
     lib.nvfp4_verify_gemm.restype = ctypes.c_int
+    lib.mx_quantize_act.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+    lib.mx_quantize_act.restype = ctypes.c_int
+    lib.mx_verify_gemm_act.argtypes = [vp, vp, i64, i64, vp, vp, i32, i64, vp, vp]
+    lib.mx_verify_gemm_act.restype = ctypes.c_int
     return lib
 
 
@@ -317,4 +321,44 @@ def nvfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, global_scale: t
     _want(y, torch.float32, "y")
     _check(get_lib().nvfp4_verify_gemm(_ptr(codes), _ptr(scales), _ptr(global_scale), n, k, _ptr(x), m,
                                        _ptr(y), _stream(stream)), "nvfp4_verify_gemm")
+    return y
+
+
+ACT_FP8 = 0  # MXS_ACT_FP8: MX-FP8 (E4M3) activations
+ACT_FP4 = 4  # MXS_ACT_FP4: MX-FP4 (E2M1) activations
+
+
+def mx_quantize_act(x: torch.Tensor, fmt: int, codes: torch.Tensor | None = None,
+                    scales: torch.Tensor | None = None, dev_flags: torch.Tensor | None = None, stream=None):
+    """bf16 X[m, k] -> (codes, scales): MX-FP8 codes [m, k] or MX-FP4 codes [m, k/2]; scales [m, k/32]."""
+    _want(x, torch.bfloat16, "x")
+    m, k = x.shape
+    if codes is None:
+        codes = torch.empty((m, k if fmt == ACT_FP8 else k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _want(codes, torch.uint8, "codes")
+    _want(scales, torch.uint8, "scales")
+    _want(dev_flags, torch.int32, "dev_flags")
+    _check(get_lib().mx_quantize_act(_ptr(x), m, k, fmt, _ptr(codes), _ptr(scales), _ptr(dev_flags),
+                                     _stream(stream)), "mx_quantize_act")
+    return codes, scales
+
+
+def mx_verify_gemm_act(codes: torch.Tensor, scales: torch.Tensor, act_codes: torch.Tensor,
+                       act_scales: torch.Tensor, fmt: int, y: torch.Tensor | None = None, stream=None):
+    """Y[m, n] = X^ · Ŵᵀ: MX-FP4 weights times MX-FP8 / MX-FP4 activations (fmt ACT_FP8 / ACT_FP4)."""
+    for t, nm in ((codes, "codes"), (scales, "scales"), (act_codes, "act_codes"), (act_scales, "act_scales")):
+        _want(t, torch.uint8, nm)
+    n = codes.shape[0]
+    k = codes.shape[1] * 2
+    m = act_codes.shape[0]
+    want_cols = k if fmt == ACT_FP8 else k // 2
+    if act_codes.shape != (m, want_cols) or act_scales.shape != (m, k // 32) or scales.shape != (n, k // 32):
+        raise ValueError("shape mismatch")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=codes.device)
+    _want(y, torch.float32, "y")
+    _check(get_lib().mx_verify_gemm_act(_ptr(codes), _ptr(scales), n, k, _ptr(act_codes), _ptr(act_scales), fmt,
+                                        m, _ptr(y), _stream(stream)), "mx_verify_gemm_act")
     return y

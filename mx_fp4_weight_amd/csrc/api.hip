@@ -137,6 +137,34 @@ mxs_status nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const 
                                                 static_cast<hipStream_t>(stream)));
 }
 
+mxs_status mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,
+                           uint8_t* scales, int32_t* dev_flags, void* stream) {
+  if (!x || !codes || !scales) return MXS_ERR_NULL;
+  if (fmt != MXS_ACT_FP8 && fmt != MXS_ACT_FP4) return MXS_ERR_VALUE;
+  if (m < 1 || k < 32 || k % 32 != 0 || m > (int64_t(1) << 40) / k) return MXS_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, fmt == MXS_ACT_FP8 ? 8 : 4) || !aligned(dev_flags, 4))
+    return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_quantize_act(x, m, k, fmt, codes, scales, dev_flags,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+mxs_status mx_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                              const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt, int64_t m,
+                              float* y, void* stream) {
+  if (!codes || !scales || !act_codes || !act_scales || !y) return MXS_ERR_NULL;
+  if (fmt != MXS_ACT_FP8 && fmt != MXS_ACT_FP4) return MXS_ERR_VALUE;
+  if (n < 1 || n > (int64_t(1) << 31) - 1 || k < 128 || k % 128 != 0 || k > (int64_t(1) << 24) ||
+      m < 1 || m > 65536)
+    return MXS_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(act_codes, 16) || !aligned(y, 4)) return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_verify_gemm_act(codes, scales, n, k, act_codes, act_scales, fmt, m, y,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
   if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
   return mxs::accept_workspace_bytes(b, kd, v, false);

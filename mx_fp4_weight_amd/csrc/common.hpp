@@ -16,6 +16,25 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer descriptor over [base, base + bytes): loads past the end read zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // past any num_records: the load reads 0
+
+// Workgroup barrier that orders LDS accesses only (global loads stay in flight).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt immediate that waits until at most n (< 64) vector memory operations
+// are outstanding and leaves the export and LDS/scalar counters alone: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // OR a device-detected condition into the caller's flag word (vector atomic).
 __device__ inline void raise_flag(int32_t* flags, int32_t bit) {
   if (flags) atomicOr(flags, bit);

@@ -101,23 +101,6 @@ __device__ inline bf16x8 decode8(uint32_t c, float scale) {
 // alternate between row blocks) behind an LDS-only barrier, which leaves the
 // prefetched global loads in flight.
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // past any num_records: the load reads 0
-
-// s_waitcnt immediate that waits until at most n (< 64) vector memory operations
-// are outstanding and leaves the export and LDS/scalar counters alone: vmcnt bits
-// [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
-constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
 // X staged in LDS in MFMA-operand order. The 16-byte chunk q (8 bf16) of
 // activation row t goes to unit ((grp*4 + d)*mt + t)*4 + g with grp = q/16,
 // g = (q/4)%4, d = q%4: for one group and MFMA slice d, the lanes (t, g) read

@@ -40,6 +40,14 @@ hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales,
                                     int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
                                     hipStream_t stream);
 
+// MX activations (fmt MXS_ACT_FP8 or MXS_ACT_FP4) and the W4A8 / W4A4 product.
+hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,
+                               uint8_t* scales, int32_t* flags, hipStream_t stream);
+
+hipError_t launch_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                                  const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt,
+                                  int64_t m, float* y, hipStream_t stream);
+
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
 
 // sp == nullptr: the plain laws (no transform kernels, the same code as without transforms).

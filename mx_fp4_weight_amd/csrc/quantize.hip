@@ -234,7 +234,121 @@ __global__ __launch_bounds__(256) void nv_quantize_kernel(const float* __restric
   if (__any(live && bad) && (threadIdx.x & (kWave - 1)) == 0) raise_flag(flags, MXS_FLAG_NONFINITE);
 }
 
+// ------------------------------------------------- MX activations (W4A8 / W4A4)
+// bf16 X[m, k] -> MX-FP8 (E4M3 elements) or MX-FP4 (E2M1) with an E8M0 scale per
+// 32 values along k ("Module 11. Speculative Decoding and Quantization" §11 and
+// §12: W4A8 / W4A4 quantize the activations too; E4M3 is the 8-bit float with 4
+// exponent and 3 fraction bits). Shared exponent as for the weights,
+// floor(log2 amax) - emax with emax 8 for E4M3 (448 = 1.75 * 2^8) and 2 for E2M1.
+
+// E4M3 code of v * 2^-e (nearest, ties to the even fraction, saturating at 448, sign
+// kept), in integers on the fp32 bit pattern: x = mant * 2^-sh in units of the E4M3
+// quantum 2^Q at x's binade (Q = max(E, -6) - 3, E = floor(log2 x)).
+__device__ inline uint32_t e4m3_code(uint32_t vbits, int e) {
+  const uint32_t sign = (vbits >> 31) << 7;
+  const uint32_t a = vbits & 0x7fffffffu;
+  if (a == 0u) return sign;
+  const int ef = (int)(a >> 23);
+  const uint32_t mant = ef ? ((a & 0x7fffffu) | 0x800000u) : (a & 0x7fffffu);
+  const int E = floor_log2_bits(a) - e;
+  const int Q = (E > -6 ? E : -6) - 3;
+  const int sh = 150 + e + Q - (ef ? ef : 1);  // >= 13 for every finite input
+  uint32_t q, up;
+  if (sh >= 32) {
+    q = 0u;
+    up = 0u;  // below half a quantum
+  } else {
+    q = mant >> sh;
+    const uint32_t rem = mant & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    up = (rem > half) | ((rem == half) & (q & 1u));
+  }
+  q += up;
+  uint32_t byte;
+  if (E > -6 || q >= 8u) {
+    // normal: q in [8, 16] at exponent E (or the subnormal range rounded up to 2^-6)
+    int EE = E > -6 ? E : -6;
+    if (q == 16u) {
+      q = 8u;
+      ++EE;
+    }
+    byte = ((uint32_t)(EE + 7) << 3) | (q - 8u);
+  } else {
+    byte = q;  // subnormal: q * 2^-9
+  }
+  return sign | (byte > 0x7Eu ? 0x7Eu : byte);
+}
+
+// 4 lanes per 32-value block, one 16-byte load (8 bf16) each.
+template <int kFmt>
+__global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales,
+                                                           int32_t* __restrict__ flags) {
+  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = gtid >> 2;
+  const int sub = (int)(gtid & 3);
+  const bool live = blk < nblocks;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (live) v = *reinterpret_cast<const u32x4*>(x + blk * 32 + sub * 8);
+  uint32_t f[8];  // fp32 bit patterns of the 8 values (element 2i in the low half of word i)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = v[i] << 16;
+    f[2 * i + 1] = v[i] & 0xffff0000u;
+  }
+  uint32_t amax = 0;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = f[i] & 0x7fffffffu;
+    bad |= a >= 0x7f800000u;
+    amax = a > amax ? a : amax;
+  }
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    const uint32_t t = __shfl_xor(amax, o);
+    amax = t > amax ? t : amax;
+    bad |= __shfl_xor(bad, o);
+  }
+  constexpr int kEmax = kFmt == MXS_ACT_FP8 ? 8 : 2;
+  int e = -127;
+  if (amax != 0) {
+    e = floor_log2_bits(amax) - kEmax;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  }
+  const uint8_t sbyte = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+  if (kFmt == MXS_ACT_FP8) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0 |= e4m3_code(f[i], e) << (8 * i);
+      w1 |= e4m3_code(f[4 + i], e) << (8 * i);
+    }
+    if (bad) w0 = w1 = 0u;
+    if (live) *reinterpret_cast<uint2*>(codes + blk * 32 + sub * 8) = make_uint2(w0, w1);
+  } else {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= e2m1_code(f[i], e) << (4 * i);
+    if (bad) packed = 0u;
+    if (live) *reinterpret_cast<uint32_t*>(codes + blk * 16 + sub * 4) = packed;
+  }
+  if (live && sub == 0) scales[blk] = sbyte;
+  if (__any(live && bad) && (threadIdx.x & (kWave - 1)) == 0) raise_flag(flags, MXS_FLAG_NONFINITE);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,
+                               uint8_t* scales, int32_t* flags, hipStream_t stream) {
+  const int64_t nblocks = m * (k / 32);
+  const dim3 grid((unsigned)((nblocks * 4 + 255) / 256)), block(256);
+  if (fmt == MXS_ACT_FP8)
+    quantize_act_kernel<MXS_ACT_FP8><<<grid, block, 0, stream>>>(x, nblocks, codes, scales, flags);
+  else
+    quantize_act_kernel<MXS_ACT_FP4><<<grid, block, 0, stream>>>(x, nblocks, codes, scales, flags);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
                            int32_t* flags, hipStream_t stream) {

@@ -25,7 +25,7 @@ def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)
-    keep = [n for n in names if n.startswith(("mxs_", "mxfp4_", "nvfp4_", "spec_accept"))]
+    keep = [n for n in names if n.startswith(("mxs_", "mx_", "mxfp4_", "nvfp4_", "spec_accept"))]
     return sorted(set(keep))
 
 
@@ -220,3 +220,38 @@ def test_nvfp4_gemm_host_errors():
         assert _ng(**kw) == mxs.MXS_ERR_ALIGN
     assert _ng(m=65536, k=1024) == mxs.MXS_ERR_DEVICE
     assert _ng() == mxs.MXS_ERR_DEVICE
+
+
+def _qa(x=0x1000, m=4, k=64, fmt=0, codes=0x2000, scales=0x3000, flags=None):
+    f = lambda a: P(a) if a else None
+    return mxs.get_lib().mx_quantize_act(f(x), m, k, fmt, f(codes), f(scales), f(flags), None)
+
+
+def test_act_quantize_host_errors():
+    for kw in [dict(x=0), dict(codes=0), dict(scales=0)]:
+        assert _qa(**kw) == mxs.MXS_ERR_NULL
+    for kw in [dict(fmt=1), dict(fmt=2), dict(fmt=-1), dict(fmt=8)]:
+        assert _qa(**kw) == mxs.MXS_ERR_VALUE
+    for kw in [dict(k=48), dict(k=16), dict(m=0), dict(k=0)]:
+        assert _qa(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(x=0x1008), dict(codes=0x2004), dict(codes=0x2002, fmt=4), dict(flags=0x5002)]:
+        assert _qa(**kw) == mxs.MXS_ERR_ALIGN
+    assert _qa(codes=0x2004, fmt=4) == mxs.MXS_ERR_DEVICE
+    assert _qa(scales=0x3001) == mxs.MXS_ERR_DEVICE
+
+
+def _ga(codes=0x1000, scales=0x2000, n=4, k=256, ac=0x3000, asc=0x4000, fmt=0, m=5, y=0x5000):
+    f = lambda a: P(a) if a else None
+    return mxs.get_lib().mx_verify_gemm_act(f(codes), f(scales), n, k, f(ac), f(asc), fmt, m, f(y), None)
+
+
+def test_act_gemm_host_errors():
+    for kw in [dict(codes=0), dict(scales=0), dict(ac=0), dict(asc=0), dict(y=0)]:
+        assert _ga(**kw) == mxs.MXS_ERR_NULL
+    assert _ga(fmt=3) == mxs.MXS_ERR_VALUE
+    for kw in [dict(k=96), dict(k=64), dict(n=0), dict(m=0), dict(m=65537), dict(k=(1 << 24) + 128)]:
+        assert _ga(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(codes=0x1008), dict(ac=0x3004), dict(y=0x5002)]:
+        assert _ga(**kw) == mxs.MXS_ERR_ALIGN
+    assert _ga(scales=0x2001, asc=0x4003, fmt=4) == mxs.MXS_ERR_DEVICE
+    assert _ga() == mxs.MXS_ERR_DEVICE
