@@ -213,8 +213,9 @@ mxs_status mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt,
  * Built for the batched verification (m = sequences × positions); any 1 <= m <= 65536
  * is accepted.
  *
- * k % 128 == 0, k <= 2^24; codes and act_codes 16-byte aligned; y fp32 [m, n], 4-byte
- * aligned. Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN, MXS_ERR_VALUE (fmt).
+ * k % 128 == 0, k <= 2^24; codes and act_codes 16-byte aligned; scales and act_scales
+ * 4-byte aligned; y fp32 [m, n], 4-byte aligned. Returns MXS_ERR_NULL, MXS_ERR_SHAPE,
+ * MXS_ERR_ALIGN, MXS_ERR_VALUE (fmt).
  */
 mxs_status mx_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt, int64_t m,

@@ -158,7 +158,9 @@ mxs_status mx_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64
   if (n < 1 || n > (int64_t(1) << 31) - 1 || k < 128 || k % 128 != 0 || k > (int64_t(1) << 24) ||
       m < 1 || m > 65536)
     return MXS_ERR_SHAPE;
-  if (!aligned(codes, 16) || !aligned(act_codes, 16) || !aligned(y, 4)) return MXS_ERR_ALIGN;
+  if (!aligned(codes, 16) || !aligned(act_codes, 16) || !aligned(scales, 4) || !aligned(act_scales, 4) ||
+      !aligned(y, 4))
+    return MXS_ERR_ALIGN;
   const mxs_status d = check_device();
   if (d != MXS_OK) return d;
   return launched(mxs::launch_verify_gemm_act(codes, scales, n, k, act_codes, act_scales, fmt, m, y,

@@ -13,14 +13,12 @@
 // g/2 + 2 (bytes 0-15 and 16-31) for h = g % 2, while the lane's scale still belongs
 // to block g. A and B therefore keep the natural k order of the group.
 //
-// Work split as in the weight-only dense kernel: a workgroup owns 128 weight rows ×
-// 80 positions and all of k; 8 waves = 2 row halves × 4 k quarters; weights go from
+// Work split as in the weight-only dense kernel: a workgroup owns 128 weight rows × 80
+// positions and all of k; 8 waves = 2 row halves × 4 k quarters; weights go from
 // HBM straight into registers; the activation codes of each 512-k window are staged
 // in LDS by direct global-to-LDS loads into an XOR-swizzled tile, double-buffered;
 // each B operand read feeds 4 MFMAs; the k quarters are summed in LDS in a fixed
 // order; position tiles of one weight tile share an XCD's L2.
-#include <atomic>
-
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -29,23 +27,41 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kRows = 128;     // weight rows per workgroup tile
-constexpr int kThreads = 512;  // 8 waves
-constexpr int kMC = 5;         // 16-position column tiles per workgroup tile
+constexpr int kRows = 128;  // weight rows per workgroup tile
+constexpr int kMC = 5;      // 16-position column tiles per workgroup tile
+constexpr int kRQ = 2;      // row groups per tile: 4·kRQ waves, 8/kRQ row tiles per wave
 
-template <int MC, int AF>
-__global__ __launch_bounds__(kThreads) void gemm_act_kernel(
+template <int MC, int AF, int RQ>
+__global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint8_t* __restrict__ acodes, const uint8_t* __restrict__ ascales, float* __restrict__ y,
     int n, int k, int m, int n_tiles, int m_tiles, int y_vec4) {
   constexpr int BM = 16 * MC;
-  constexpr int kWaves = kThreads / kWave;
+  constexpr int kWaves = 4 * RQ;  // RQ row groups × 4 k quarters
+  constexpr int RT = 8 / RQ;      // 16-row tiles per wave
   // 16-byte units per position in one 512-k window: 32 (8-bit codes) or 16 (4-bit)
   constexpr int kRowUnits = AF == MXS_ACT_FP8 ? 32 : 16;
-  constexpr int kRowsPerLoad = kWave / kRowUnits;  // positions one wave-wide LDS load covers
-  constexpr int kLoads = BM / kRowsPerLoad;        // wave-wide loads per window
-  constexpr int kUnits = BM * kRowUnits;           // units per staging buffer
-  extern __shared__ u32x4 smem[];
+  constexpr int kRowsPerLoad = kWave / kRowUnits;  // positions one wave-wide code load covers
+  constexpr int kLoads = BM / kRowsPerLoad;        // wave-wide code loads per window
+  constexpr int kUnits = BM * kRowUnits;           // code units per staging buffer
+  // A staging buffer holds the window's activation codes, then its scale dwords (one
+  // 16-byte unit of 4 groups per weight row, then one per position), then a 1 KiB pad.
+  // Scales go through LDS like the codes: loaded per lane from global memory they cost
+  // as many address cycles as the codes (16 rows per instruction) for 1/16 the bytes.
+  constexpr int kScaleLoads = (kRows + BM) / 16;   // 4-byte-per-lane loads: 16 rows each
+  constexpr int kPerWave = (kLoads + kWaves - 1) / kWaves;
+  constexpr int kScalePerWave = (kScaleLoads + kWaves - 1) / kWaves;
+  constexpr int kWsc = kUnits;              // first weight-scale unit
+  constexpr int kXsc = kUnits + kRows;      // first activation-scale unit
+  constexpr int kPadU = kUnits + kRows + BM;
+  constexpr int kBufU = kPadU + kWave;
+  // The two staging buffers are separate LDS objects, so the compiler can tell that
+  // the direct loads into one never alias the operand reads of the other and does not
+  // make those reads wait for the loads just issued. Surplus wave-wide loads (when the
+  // loads of a window do not divide evenly among the waves) read nothing into the pad:
+  // every wave issues the same loads without a branch, so wait counts stay exact.
+  __shared__ u32x4 xbuf0[kBufU];
+  __shared__ u32x4 xbuf1[kBufU];
   // workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight tile
   const int xcd = (int)blockIdx.x & 7;
   const int j = (int)blockIdx.x >> 3;
@@ -55,13 +71,17 @@ __global__ __launch_bounds__(kThreads) void gemm_act_kernel(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-  const int rh = wave & 1;
-  const int kq = wave >> 1;
+  const int rq = wave % RQ;
+  const int kq = wave / RQ;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int kb = k >> 5;
   const int ngroups = kb >> 2;
   const int nsteps = (ngroups + 3) >> 2;  // 512-k windows
+  // Each weight tile walks the windows starting at its own offset, so the tiles do not
+  // all read the same column of the matrix at once.
+  const int s0 = (int)(((unsigned)nt * 13u) % (unsigned)max(nsteps, 1));
+  auto window = [&](int s) { return s < nsteps ? (s + s0 < nsteps ? s + s0 : s + s0 - nsteps) : s; };
   const uint32_t row_bytes = (uint32_t)(k >> 1);
   const uint32_t arow_bytes = AF == MXS_ACT_FP8 ? (uint32_t)k : (uint32_t)(k >> 1);
   const int row0 = nt * kRows;
@@ -74,86 +94,115 @@ __global__ __launch_bounds__(kThreads) void gemm_act_kernel(
       make_rsrc(acodes + (size_t)t0 * arow_bytes, (uint32_t)mrows * arow_bytes);
   const __amdgpu_buffer_rsrc_t xsr = make_rsrc(ascales + (size_t)t0 * kb, (uint32_t)mrows * (uint32_t)kb);
 
-  // codes and scale bytes of this wave's 4 row tiles for its group of step s, and the
-  // activation scale bytes of its MC column tiles (positions past m read 0)
+  // Offsets pass through an empty asm: otherwise the compiler folds the unrolled step's
+  // constant into the immediate field and branches around the load on `ok`, and a load
+  // on one side of a branch makes its later wait counts conservative.
+  auto opaque = [](uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  // the codes of this wave's RT row tiles for its group of step s (rows past n read 0)
   struct Ops {
-    u32x4 c[4];
-    uint32_t s[4];
-    uint32_t xs[MC];
+    u32x4 c[RT];
   };
   auto load_ops = [&](int s, Ops& o) {
-    const int grp = 4 * s + kq;
+    const int grp = 4 * window(s) + kq;
     const int blk = grp * 4 + g;
     const bool ok = grp < ngroups;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t row = (uint32_t)(rh * 64 + 16 * i + r);
-      const uint32_t co = ok ? row * row_bytes + (uint32_t)blk * 16 : kOutOfRange;
-      const uint32_t so = ok ? row * (uint32_t)kb + (uint32_t)blk : kOutOfRange;
+    for (int i = 0; i < RT; ++i) {
+      const uint32_t row = (uint32_t)(rq * 16 * RT + 16 * i + r);
+      const uint32_t co = opaque(ok ? row * row_bytes + (uint32_t)blk * 16 : kOutOfRange);
       o.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, co, 0, 0));
-      o.s[i] = __builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < MC; ++c) {
-      const uint32_t xo = ok ? (uint32_t)(16 * c + r) * (uint32_t)kb + (uint32_t)blk : kOutOfRange;
-      o.xs[c] = __builtin_amdgcn_raw_buffer_load_b8(xsr, xo, 0, 0);
     }
   };
-  constexpr int kOpLoads = 8 + MC;  // VMEM loads of one load_ops
+  constexpr int kOpLoads = RT;  // VMEM loads of one load_ops
 
-  // Stage the activation codes of window s into buffer buf. Unit u of position t sits
-  // at t·kRowUnits + u and holds chunk q = u ^ (t mod 16) of the window; one wave-wide
-  // load L writes the kRowsPerLoad positions kRowsPerLoad·L.. contiguously. Positions
-  // past m and chunks past k are outside the descriptor or masked and read as zero.
-  auto stage_x = [&](int s, int buf) {
+  // Stage window s into buffer buf. Codes: unit u of position t sits at t·kRowUnits + u
+  // and holds chunk q = u ^ (t mod 16) of the window; one wave-wide load L writes the
+  // kRowsPerLoad positions kRowsPerLoad·L.. contiguously. Scales: scale load J writes
+  // 16 rows (weight rows for J < kRows/16, then positions) × 4 dwords, dword d of a row
+  // being group 4·window + d. Positions past m, rows past n and groups past k are
+  // outside the descriptors or masked and read as zero.
+  auto stage_x = [&](int sl, u32x4* buf) {
+    const int s = window(sl);
 #pragma unroll
-    for (int i = 0; i < (kLoads + kWaves - 1) / kWaves; ++i) {
+    for (int i = 0; i < kPerWave; ++i) {
       const int L = wave + kWaves * i;
-      if (L < kLoads) {  // wave-uniform
-        const int t = L * kRowsPerLoad + lane / kRowUnits;
-        const int u = lane % kRowUnits;
-        const int q = u ^ (t & 15);
-        const int qg = AF == MXS_ACT_FP8 ? q >> 3 : q >> 2;  // group of the chunk inside the window
-        const bool ok = 4 * s + qg < ngroups;
-        const uint32_t off = ok ? (uint32_t)t * arow_bytes + (uint32_t)(s * kRowUnits + q) * 16u : kOutOfRange;
-        __attribute__((address_space(3))) void* dst =
-            (__attribute__((address_space(3))) void*)(smem + buf * kUnits + kWave * L);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
-      }
+      const bool live = kLoads % kWaves == 0 || L < kLoads;  // wave-uniform
+      const int t = L * kRowsPerLoad + lane / kRowUnits;
+      const int u = lane % kRowUnits;
+      const int q = u ^ (t & 15);
+      const int qg = AF == MXS_ACT_FP8 ? q >> 3 : q >> 2;  // group of the chunk inside the window
+      const bool ok = live && 4 * s + qg < ngroups;
+      const uint32_t off = ok ? (uint32_t)t * arow_bytes + (uint32_t)(s * kRowUnits + q) * 16u : kOutOfRange;
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(buf + (live ? kWave * L : kPadU));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kScalePerWave; ++i) {
+      const int J = wave + kWaves * i;  // wave-uniform
+      const bool wsc = J < kRows / 16;
+      const bool live = J < kScaleLoads;
+      const int row = (wsc ? J : J - kRows / 16) * 16 + lane / 4;
+      const int d = lane & 3;
+      const bool ok = live && 4 * s + d < ngroups;
+      const uint32_t off = ok ? (uint32_t)row * (uint32_t)kb + (uint32_t)(16 * s + 4 * d) : kOutOfRange;
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(buf + (live ? kWsc + 16 * J : kPadU));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wsc ? sr : xsr, dst, 4, off, 0, 0, 0);
     }
   };
 
-  f32x4 acc[4][MC];
+  f32x4 acc[RT][MC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int c = 0; c < MC; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const Ops& o) {
-    const u32x4* src = smem + buf * kUnits;
-    i32x8 bb[MC];
+  auto compute = [&](const u32x4* src, const Ops& o) {
+    // scale byte of block g of group kq: byte 4·kq + g of the row's scale unit
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
+    uint32_t sw[RT], sx[MC];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) sw[i] = sb[(kWsc + rq * 16 * RT + 16 * i + r) * 16 + 4 * kq + g];
+#pragma unroll
+    for (int c = 0; c < MC; ++c) sx[c] = sb[(kXsc + 16 * c + r) * 16 + 4 * kq + g];
+    i32x8 a[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      a[i] = i32x8{(int)o.c[i][0], (int)o.c[i][1], (int)o.c[i][2], (int)o.c[i][3], 0, 0, 0, 0};
+    // one column tile at a time: its B operand is read from LDS and feeds RT MFMAs
 #pragma unroll
     for (int c = 0; c < MC; ++c) {
       const int t = 16 * c + r;  // t mod 16 == r
+      i32x8 bb;
       if constexpr (AF == MXS_ACT_FP8) {
         // values 16h .. 16h+15 of blocks g/2 and g/2 + 2 of group kq: chunks 8kq + g, 8kq + g + 4
         const u32x4 lo = src[t * kRowUnits + ((8 * kq + g) ^ r)];
         const u32x4 hi = src[t * kRowUnits + ((8 * kq + g + 4) ^ r)];
-        bb[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        bb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       } else {
         const u32x4 v = src[t * kRowUnits + ((4 * kq + g) ^ r)];  // block g of group kq
-        bb[c] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        bb = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x8 a = {(int)o.c[i][0], (int)o.c[i][1], (int)o.c[i][2], (int)o.c[i][3], 0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < MC; ++c)
-        acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb[c], acc[i][c], MXS_ACT_FP4, AF, 0,
-                                                                     (int)o.s[i], 0, (int)o.xs[c]);
+      for (int i = 0; i < RT; ++i)
+        acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bb, acc[i][c], MXS_ACT_FP4, AF, 0,
+                                                                     (int)sw[i], 0, (int)sx[c]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // The accumulators pass through an empty asm after each step's MFMAs: the MFMAs are
+  // pure, and without it the compiler sinks them below the next step's loads, where
+  // their operands' wait counts then cover those loads too.
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int c = 0; c < MC; ++c) asm volatile("" : "+v"(acc[i][c]));
   };
 
   // Staging and operand loads of step s + 1 go out before the MFMAs of step s; after
@@ -161,52 +210,65 @@ __global__ __launch_bounds__(kThreads) void gemm_act_kernel(
   // after them stay in flight: the counter retires in order), then the barrier makes
   // every wave's positions visible.
   Ops oa, ob;
-  stage_x(0, 0);
+  stage_x(0, xbuf0);
   load_ops(0, oa);
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
   // two steps per iteration and one exit; with an odd step count the last step reads
   // only out-of-range (zero) operands and adds nothing
   for (int s = 0; s < nsteps; s += 2) {
-    stage_x(s + 1, 1);
+    stage_x(s + 1, xbuf1);
     __builtin_amdgcn_sched_barrier(0);
     load_ops(s + 1, ob);
     __builtin_amdgcn_sched_barrier(0);
-    compute(0, oa);
+    compute(xbuf0, oa);
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(kOpLoads));
     lds_barrier();
-    stage_x(s + 2, 0);
+    stage_x(s + 2, xbuf0);
     __builtin_amdgcn_sched_barrier(0);
     load_ops(s + 2, oa);
     __builtin_amdgcn_sched_barrier(0);
-    compute(1, ob);
+    compute(xbuf1, ob);
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(kOpLoads));
     lds_barrier();
   }
 
-  // sum the four k quarters in LDS (the staging buffers are free once every load has
-  // landed: the last iteration's loads target windows past k)
+  // Sum the four k quarters through the staging buffers (free once every load has
+  // landed: the last iteration's loads target windows past k), one quarter at a time,
+  // the first half of the row groups in one buffer and the second half in the other;
+  // k quarter 0 adds them in the order 1, 2, 3 and stores.
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
-  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [3 kq][2 rh][4][MC][64]
-  if (kq > 0) {
+  constexpr int kTileRegs = RT * MC * kWave;  // f32x4 partial tiles of one wave
+  static_assert(sizeof(xbuf0) >= sizeof(f32x4) * (RQ / 2) * kTileRegs, "half the row groups fit a buffer");
+  f32x4* red = reinterpret_cast<f32x4*>(rq < RQ / 2 ? xbuf0 : xbuf1) + (rq % (RQ / 2)) * kTileRegs;
+  for (int q = 1; q < 4; ++q) {
+    if (kq == q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int c = 0; c < MC; ++c) red[((((kq - 1) * 2 + rh) * 4 + i) * MC + c) * kWave + lane] = acc[i][c];
+        for (int c = 0; c < MC; ++c) red[(i * MC + c) * kWave + lane] = acc[i][c];
+    }
+    lds_barrier();
+    if (kq == 0) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int c = 0; c < MC; ++c) acc[i][c] += red[(i * MC + c) * kWave + lane];
+    }
+    lds_barrier();
   }
-  lds_barrier();
   if (kq == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int orow = row0 + rh * 64 + 16 * i + 4 * g;  // lane holds C[4g + e][r]
+    for (int i = 0; i < RT; ++i) {
+      const int orow = row0 + rq * 16 * RT + 16 * i + 4 * g;  // lane holds C[4g + e][r]
 #pragma unroll
       for (int c = 0; c < MC; ++c) {
-        f32x4 sum = acc[i][c];
-#pragma unroll
-        for (int q = 0; q < 3; ++q) sum += red[(((q * 2 + rh) * 4 + i) * MC + c) * kWave + lane];
+        const f32x4 sum = acc[i][c];
         const int tt = t0 + 16 * c + r;
         if (tt < m) {
           float* yp = y + (size_t)tt * (size_t)n + orow;
@@ -223,30 +285,14 @@ __global__ __launch_bounds__(kThreads) void gemm_act_kernel(
   }
 }
 
-constexpr int kMaxDevices = 64;
-constexpr size_t kRedBytes = sizeof(f32x4) * 3 * 2 * 4 * kMC * kWave;
-
 template <int AF>
 hipError_t launch(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, const uint8_t* acodes,
                   const uint8_t* ascales, int64_t m, float* y, hipStream_t stream) {
-  constexpr int kRowUnits = AF == MXS_ACT_FP8 ? 32 : 16;
-  constexpr size_t kStage = 2 * sizeof(u32x4) * 16 * kMC * kRowUnits;
-  constexpr size_t lds = kStage > kRedBytes ? kStage : kRedBytes;
-  static std::atomic<bool> done[kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= kMaxDevices || !done[dev].load(std::memory_order_relaxed)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_act_kernel<kMC, AF>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    if (dev < kMaxDevices) done[dev].store(true, std::memory_order_relaxed);
-  }
   const int n_tiles = (int)((n + kRows - 1) / kRows);
   const int m_tiles = (int)((m + 16 * kMC - 1) / (16 * kMC));
   const int64_t wgs = (int64_t)((n_tiles + 7) / 8) * 8 * m_tiles;
   const int y_vec4 = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
-  gemm_act_kernel<kMC, AF><<<dim3((unsigned)wgs), dim3(kThreads), lds, stream>>>(
+  gemm_act_kernel<kMC, AF, kRQ><<<dim3((unsigned)wgs), dim3(256 * kRQ), 0, stream>>>(
       codes, scales, acodes, ascales, y, (int)n, (int)k, (int)m, n_tiles, m_tiles, y_vec4);
   return hipGetLastError();
 }

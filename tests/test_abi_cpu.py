@@ -251,7 +251,7 @@ def test_act_gemm_host_errors():
     assert _ga(fmt=3) == mxs.MXS_ERR_VALUE
     for kw in [dict(k=96), dict(k=64), dict(n=0), dict(m=0), dict(m=65537), dict(k=(1 << 24) + 128)]:
         assert _ga(**kw) == mxs.MXS_ERR_SHAPE
-    for kw in [dict(codes=0x1008), dict(ac=0x3004), dict(y=0x5002)]:
+    for kw in [dict(codes=0x1008), dict(ac=0x3004), dict(y=0x5002), dict(scales=0x2001), dict(asc=0x4002)]:
         assert _ga(**kw) == mxs.MXS_ERR_ALIGN
-    assert _ga(scales=0x2001, asc=0x4003, fmt=4) == mxs.MXS_ERR_DEVICE
+    assert _ga(scales=0x2004, asc=0x400C, fmt=4) == mxs.MXS_ERR_DEVICE
     assert _ga() == mxs.MXS_ERR_DEVICE
