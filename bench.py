@@ -465,8 +465,8 @@ def nv_bytes(n, k):
 
 
 def nvfp4_8b(torch, mxs, gen, pool_gb=2.4, reps=3):
-    """NVFP4 weights through the same skinny kernel: the 8B-class layer at T = 1..8, one launch
-    per matrix (no grouped entry point), over a cold pool of > 2 GB of weights."""
+    """NVFP4 weights through the same skinny kernel: the 8B-class layer at T = 1, 5, 8 in the four
+    launches of the MX-FP4 headline (q|k|v and gate|up grouped), over a cold pool of > 2 GB."""
     layer_b = sum(nv_bytes(n, k) for _, n, k in LAYER)
     n_layers = max(1, math.ceil(pool_gb * 1e9 / layer_b))
     pool = []
@@ -477,18 +477,23 @@ def nvfp4_8b(torch, mxs, gen, pool_gb=2.4, reps=3):
             mats.append(mxs.nvfp4_quantize(w))
             del w
         pool.append(mats)
-    out = {"pool_layers": n_layers, "pool_bytes": layer_b * n_layers}
+    out = {"pool_layers": n_layers, "pool_bytes": layer_b * n_layers,
+           "launches": "q|k|v and gate|up grouped (nvfp4_verify_gemm_grouped), o and down single"}
     for t in (1, 5, 8):
         xs = [_rand_bf16(torch, gen, t, k) for (_, _, k) in LAYER]
         ys = [torch.empty((t, n), dtype=torch.float32, device="cuda") for (_, n, _) in LAYER]
         row = {}
-        for i, (name, n, k) in enumerate(LAYER):
-            def body(i=i):
+        for name, idx in LAUNCHES:
+            def body(idx=idx):
                 for li in range(n_layers):
-                    c, s, g = pool[li][i]
-                    mxs.nvfp4_verify_gemm(c, s, g, xs[i], y=ys[i])
+                    items = [(*pool[li][i], xs[i]) for i in idx]
+                    if len(items) == 1:
+                        c, s, g, x = items[0]
+                        mxs.nvfp4_verify_gemm(c, s, g, x, y=ys[idx[0]])
+                    else:
+                        mxs.nvfp4_verify_gemm_grouped(items, ys=[ys[i] for i in idx])
             us = _graph_ms(torch, body, reps) * 1e3 / n_layers
-            byts = nv_bytes(n, k) + t * k * 2 + t * n * 4
+            byts = sum(nv_bytes(LAYER[i][1], LAYER[i][2]) + t * LAYER[i][2] * 2 + t * LAYER[i][1] * 4 for i in idx)
             row[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
         tot_b = sum(nv_bytes(n, k) + t * k * 2 + t * n * 4 for _, n, k in LAYER)
         tot_us = sum(v["us"] for v in row.values())

@@ -181,6 +181,25 @@ mxs_status nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const 
                              void* stream);
 
 /*
+ * nvfp4_verify_gemm_grouped — several independent NVFP4 products with the same k and m
+ * (the projections of a layer that read the same input), up to 8 per launch, as
+ * mxfp4_verify_gemm_grouped does for MX-FP4. Each product has its own tensor scale.
+ * Same argument rules as nvfp4_verify_gemm for every product.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+typedef struct mxs_nvfp4_problem {
+  const uint8_t* codes;       /* [n, k/2] */
+  const uint8_t* scales;      /* [n, k/16] E4M3 */
+  const float* global_scale;  /* one fp32 in device memory */
+  const uint16_t* x;          /* [m, k] bf16 */
+  float* y;                   /* [m, n] fp32 */
+  int64_t n;
+} mxs_nvfp4_problem;
+
+mxs_status nvfp4_verify_gemm_grouped(const mxs_nvfp4_problem* problems, int32_t count, int64_t k, int64_t m,
+                                     void* stream);
+
+/*
  * mx_quantize_act — bf16 activations X[m, k] -> MX-FP8 or MX-FP4 [M11 §11: W4A8 /
  * W4A4 quantize activations as well as weights; §12: E4M3 = 8-bit float with 4
  * exponent and 3 fraction bits, E8M0 power-of-two scale; news page, "Microscaling

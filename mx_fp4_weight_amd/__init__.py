@@ -32,13 +32,19 @@ FLAG_RESIDUAL_ZERO = 8
 EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_verify_gemm",
            "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept",
            "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
-           "nvfp4_verify_gemm", "mx_quantize_act", "mx_verify_gemm_act"]
+           "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act"]
 
 
 class GemmProblem(ctypes.Structure):
     """mxs_gemm_problem: one product of a grouped verify GEMM."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class NvProblem(ctypes.Structure):
+    """mxs_nvfp4_problem: one product of a grouped NVFP4 verify GEMM."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("global_scale", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class MxsError(RuntimeError):
@@ -78,6 +84,8 @@ def _load() -> ctypes.CDLL:
     lib.nvfp4_quantize.restype = ctypes.c_int
     lib.nvfp4_verify_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp, vp]
     lib.nvfp4_verify_gemm.restype = ctypes.c_int
+    lib.nvfp4_verify_gemm_grouped.argtypes = [ctypes.POINTER(NvProblem), i32, i64, i64, vp]
+    lib.nvfp4_verify_gemm_grouped.restype = ctypes.c_int
     lib.mx_quantize_act.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     lib.mx_quantize_act.restype = ctypes.c_int
     lib.mx_verify_gemm_act.argtypes = [vp, vp, i64, i64, vp, vp, i32, i64, vp, vp]
@@ -322,6 +330,37 @@ def nvfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, global_scale: t
     _check(get_lib().nvfp4_verify_gemm(_ptr(codes), _ptr(scales), _ptr(global_scale), n, k, _ptr(x), m,
                                        _ptr(y), _stream(stream)), "nvfp4_verify_gemm")
     return y
+
+
+def nvfp4_verify_gemm_grouped(items, ys=None, stream=None):
+    """Several NVFP4 products with the same k and m in one launch.
+
+    items: list of (codes [n_i, k/2], scales [n_i, k/16], global_scale fp32 [1], x [m, k] bf16).
+    Returns the list of outputs y_i [m, n_i] fp32 (or fills the given ys).
+    """
+    if not items:
+        raise ValueError("no products")
+    k = items[0][0].shape[1] * 2
+    m = items[0][3].shape[0]
+    arr = (NvProblem * len(items))()
+    out = []
+    for i, (codes, scales, g, x) in enumerate(items):
+        _want(codes, torch.uint8, "codes")
+        _want(scales, torch.uint8, "scales")
+        _want(g, torch.float32, "global_scale")
+        _want(x, torch.bfloat16, "x")
+        n = codes.shape[0]
+        if codes.shape[1] * 2 != k or x.shape != (m, k) or scales.shape != (n, k // 16):
+            raise ValueError("all products must share k and m")
+        y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+        _want(y, torch.float32, "y")
+        if y.shape != (m, n):
+            raise ValueError("y must be [m, n]")
+        arr[i] = NvProblem(codes.data_ptr(), scales.data_ptr(), g.data_ptr(), x.data_ptr(), y.data_ptr(), n)
+        out.append(y)
+    _check(get_lib().nvfp4_verify_gemm_grouped(arr, len(items), k, m, _stream(stream)),
+           "nvfp4_verify_gemm_grouped")
+    return out
 
 
 ACT_FP8 = 0  # MXS_ACT_FP8: MX-FP8 (E4M3) activations

@@ -747,7 +747,7 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp) {
 
 template <int R, int G, int D, bool kNv = false>
 hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
-                       int64_t k, int64_t m, hipStream_t stream, const float* gscale = nullptr) {
+                       int64_t k, int64_t m, hipStream_t stream) {
   static std::atomic<bool> done[kMaxDevices];
   hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv>, done);
   if (e != hipSuccess) return e;
@@ -764,7 +764,7 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     int64_t share = pp.phases > 1 ? nrb : (budget * nrb + total_rb - 1) / total_rb;
     if (share > nrb) share = nrb;
     if (share < 1) share = 1;
-    grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, gscale, (int)pv[i].n, (int)nrb,
+    grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, kNv ? pv[i].gscale : nullptr, (int)pv[i].n, (int)nrb,
                        y_vec4_ok(pv[i].y, pv[i].n), 0};
     grp.wg_start[i] = start;
     start += (int)share;
@@ -878,20 +878,43 @@ hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64
 }
 
 // NVFP4 weights: the skinny kernel for every m (a 16-position tile per grid row), k % 512 == 0
-// and 16-byte aligned scales checked by the caller.
-hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                                    int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
-                                    hipStream_t stream) {
-  const mxs_problem_view pv{codes, scales, x, y, n};
-  const Config c = choose(n, k);
+// and 16-byte aligned scales checked by the caller; up to kMaxGroup products per launch.
+static hipError_t launch_nvfp4_group(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                     hipStream_t stream) {
+  int64_t n_total = 0, nrb2 = 0;
+  for (int i = 0; i < count; ++i) {
+    n_total += pv[i].n;
+    nrb2 += (pv[i].n + 31) / 32;
+  }
+  const Config c = choose(n_total, k);
   PhasePlan pp;
   if (!plan_phases(k, m < 16 ? m : 16, c.R, c.G, pp)) return hipErrorInvalidValue;
   if (pp.phases > 1) {
+    // with several phases a workgroup owns one row block: two row tiles per block when
+    // that still leaves a workgroup per CU
     PhasePlan pp2;
-    if ((n + 31) / 32 >= kCUs && plan_phases(k, m < 16 ? m : 16, 2, c.G, pp2))
-      return launch_main<2, 4, 2, true>(Config{2, c.G, c.D, c.per_cu}, pp2, &pv, 1, k, m, stream, gscale);
+    if (nrb2 >= kCUs && plan_phases(k, m < 16 ? m : 16, 2, c.G, pp2))
+      return launch_main<2, 4, 2, true>(Config{2, c.G, c.D, c.per_cu}, pp2, pv, count, k, m, stream);
   }
-  return launch_main<1, 4, 2, true>(c, pp, &pv, 1, k, m, stream, gscale);
+  return launch_main<1, 4, 2, true>(c, pp, pv, count, k, m, stream);
+}
+
+hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                                    int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
+                                    hipStream_t stream) {
+  mxs_problem_view pv{codes, scales, x, y, n};
+  pv.gscale = gscale;
+  return launch_nvfp4_group(&pv, 1, k, m, stream);
+}
+
+hipError_t launch_nvfp4_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                            hipStream_t stream) {
+  for (int i0 = 0; i0 < count; i0 += kMaxGroup) {
+    const int cnt = count - i0 < kMaxGroup ? count - i0 : kMaxGroup;
+    const hipError_t e = launch_nvfp4_group(pv + i0, cnt, k, m, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,

@@ -14,6 +14,7 @@ struct mxs_problem_view {
   const uint16_t* x;
   float* y;
   int64_t n;
+  const float* gscale = nullptr;  // NVFP4 tensor scale (device), null for MX-FP4
 };
 
 hipError_t launch_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
@@ -39,6 +40,10 @@ hipError_t launch_nvfp4_quantize(const float* w, int64_t n, int64_t k, uint8_t* 
 hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* gscale,
                                     int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
                                     hipStream_t stream);
+
+// Several NVFP4 products with the same k (% 512 == 0) and m, each with its own tensor scale.
+hipError_t launch_nvfp4_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                            hipStream_t stream);
 
 // MX activations (fmt MXS_ACT_FP8 or MXS_ACT_FP4) and the W4A8 / W4A4 product.
 hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,

@@ -255,3 +255,22 @@ def test_act_gemm_host_errors():
         assert _ga(**kw) == mxs.MXS_ERR_ALIGN
     assert _ga(scales=0x2004, asc=0x400C, fmt=4) == mxs.MXS_ERR_DEVICE
     assert _ga() == mxs.MXS_ERR_DEVICE
+
+
+def test_nvfp4_grouped_host_errors():
+    lib = mxs.get_lib()
+    arr = (mxs.NvProblem * 2)()
+    for i in range(2):
+        arr[i] = mxs.NvProblem(0x10000 * (i + 1), 0x200000, 0x300000, 0x400000, 0x500000, 64)
+    assert lib.nvfp4_verify_gemm_grouped(None, 2, 512, 5, None) == mxs.MXS_ERR_NULL
+    assert lib.nvfp4_verify_gemm_grouped(arr, 0, 512, 5, None) == mxs.MXS_ERR_SHAPE
+    assert lib.nvfp4_verify_gemm_grouped(arr, 2, 256, 5, None) == mxs.MXS_ERR_SHAPE
+    assert lib.nvfp4_verify_gemm_grouped(arr, 2, 512, 0, None) == mxs.MXS_ERR_SHAPE
+    assert lib.nvfp4_verify_gemm_grouped(arr, 2, 512, 5, None) == mxs.MXS_ERR_DEVICE
+    arr[1].global_scale = 0
+    assert lib.nvfp4_verify_gemm_grouped(arr, 2, 512, 5, None) == mxs.MXS_ERR_NULL
+    arr[1].global_scale = 0x300002
+    assert lib.nvfp4_verify_gemm_grouped(arr, 2, 512, 5, None) == mxs.MXS_ERR_ALIGN
+    arr[1].global_scale = 0x300000
+    arr[0].scales = 0x200008
+    assert lib.nvfp4_verify_gemm_grouped(arr, 2, 512, 5, None) == mxs.MXS_ERR_ALIGN

@@ -246,3 +246,26 @@ def test_reused_outputs_and_inputs():
         y = mxs.nvfp4_verify_gemm(dc, ds, dg, dev_bf16(x), y=ybuf[:m])
         torch.cuda.synchronize()
         check_gemm(codes, scales, g, x, host(y), label=f"reuse m={m}")
+
+
+@pytest.mark.parametrize("shapes,k,m", [
+    ([4096 // 8, 1024 // 8, 1024 // 8], 4096, 5),        # q | k | v shapes, scaled down
+    ([300, 17, 1000, 64, 129, 5, 77, 256, 33, 500], 1024, 3),   # more than 8 products: two launches
+    ([300, 70], 14336, 8),                                 # k walked in phases
+    ([2000, 2000], 4096, 20),                              # two 16-position tiles
+])
+def test_grouped_matches_single(shapes, k, m):
+    """Products with their own tensor scales in one launch: each equals its oracle product."""
+    say(f"nvfp4 gemm grouped: {len(shapes)} products k={k} m={m}")
+    items, refs = [], []
+    for i, n in enumerate(shapes):
+        w = synth.weights(77, 100 * i + n, n, k, sigma=0.02 * (i + 1))
+        c, s, g, _ = nv.quantize(w)
+        x = synth.activations(77, 100 * i + n, m, k)
+        items.append((dev(c), dev(s), torch.tensor([g], dtype=torch.float32, device="cuda"), dev_bf16(x)))
+        refs.append((c, s, g, x))
+    # the products share the activations only in the layer case; here each has its own
+    ys = mxs.nvfp4_verify_gemm_grouped(items)
+    torch.cuda.synchronize()
+    for (c, s, g, x), y in zip(refs, ys):
+        check_gemm(c, s, g, x, host(y), label=f"grouped n={c.shape[0]}")
