@@ -23,6 +23,15 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // past any num_records: the load reads 0
 
+// A buffer-load offset passed through an empty asm. Without it the compiler folds an
+// unrolled step's constant into the load's immediate field and branches around the
+// load on its validity select, and a load on one side of a branch makes the later
+// wait counts conservative (waiting for loads just issued).
+__device__ inline uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Workgroup barrier that orders LDS accesses only (global loads stay in flight).
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");

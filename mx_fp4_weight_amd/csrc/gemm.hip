@@ -29,6 +29,7 @@
 // reused by its R row tiles. Partial 16×16 tiles are summed across waves in
 // LDS in wave order: results are deterministic.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -406,7 +407,14 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   const int g = lane >> 4;
   const int kb = k >> 5;
   const int ngroups = kb >> 2;
-  const int nsteps = (ngroups + 3) >> 2;  // 512-k windows
+  // Each wave walks 4 consecutive groups in 4 steps: in step s (block b = s / 4,
+  // j = s % 4) wave kq owns group 16b + 4kq + j, and the window staged for the step
+  // holds the groups of the 4 k quarters. A wave's 4 groups of a block then have their
+  // 16 scale bytes side by side in each row: one 16-byte load per row tile and block
+  // instead of a byte load per row tile and step (a per-lane load over 16 rows costs
+  // the address unit as much as a code load).
+  const int nsteps = 4 * ((ngroups + 15) >> 4);
+  auto group_of = [&](int s, int q) { return 16 * (s >> 2) + 4 * q + (s & 3); };
   const uint32_t row_bytes = (uint32_t)(k >> 1);
   const int row0 = nt * kDenseRows;
   const int rows = min(kDenseRows, n - row0);
@@ -417,22 +425,32 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)mrows * (uint32_t)k * 2u);
 
-  // codes and scales of this wave's 4 row tiles for its group of step s
+  // codes of this wave's 4 row tiles for its group of step s
   struct W4 {
     u32x4 c[4];
-    uint32_t s[4];
   };
   auto load_w = [&](int s, W4& w) {
-    const int grp = 4 * s + kq;
+    const int grp = group_of(s, kq);
     const int blk = grp * 4 + g;
     const bool ok = grp < ngroups;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t row = (uint32_t)(rh * 64 + 16 * i + r);
-      const uint32_t co = ok ? row * row_bytes + (uint32_t)blk * 16 : kOutOfRange;
-      const uint32_t so = ok ? row * (uint32_t)kb + (uint32_t)blk : kOutOfRange;
+      const uint32_t co = opaque(ok ? row * row_bytes + (uint32_t)blk * 16 : kOutOfRange);
       w.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, co, 0, 0));
-      w.s[i] = __builtin_amdgcn_raw_buffer_load_b8(sr, so, 0, 0);
+    }
+  };
+  // scale bytes of this wave's 4 groups of block b, per row tile: byte 4j + g' is block
+  // g' of the block's group j. A block past k reads zeros; in a block that k ends
+  // inside, the bytes of groups past k are not used (see scale_of).
+  auto load_sc = [&](int b, u32x4 (&sc)[4]) {
+    const int grp = 16 * b + 4 * kq;
+    const bool ok = grp < ngroups;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = (uint32_t)(rh * 64 + 16 * i + r);
+      const uint32_t so = opaque(ok ? row * (uint32_t)kb + (uint32_t)grp * 4 : kOutOfRange);
+      sc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, so, 0, 0));
     }
   };
   // Stage the window of step s into buffer buf: wave w stages tile rows w, w + 8, ...;
@@ -444,8 +462,11 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
     for (int i = 0; i < BM / kWaves; ++i) {
       const int t = wave + kWaves * i;
       const int q = lane ^ (t & 15);
-      const bool ok = 4 * s + (q >> 4) < ngroups;
-      const uint32_t off = ok ? ((uint32_t)t * (uint32_t)k + (uint32_t)(s * 512 + q * 8)) * 2u : kOutOfRange;
+      // slot q: chunk q % 16 of the group of k quarter q / 16
+      const int grp = group_of(s, q >> 4);
+      const bool ok = grp < ngroups;
+      const uint32_t off =
+          opaque(ok ? ((uint32_t)t * (uint32_t)k + (uint32_t)(grp * 128 + (q & 15) * 8)) * 2u : kOutOfRange);
       __attribute__((address_space(3))) void* dst =
           (__attribute__((address_space(3))) void*)(smem + buf * kUnits + 64 * t);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
@@ -458,11 +479,16 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
 #pragma unroll
     for (int c = 0; c < MC; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const W4& w) {
-    const u32x4* src = smem + buf * kUnits;
-    float sf[4];
+  // block scale of row tile i for step s from the block's scale bytes (1 for a group
+  // past k, whose codes read as zero)
+  auto scale_of = [&](const u32x4 (&sc)[4], int s, float (&sf)[4]) {
+    const bool ok = group_of(s, kq) < ngroups;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sf[i] = e8m0_to_f32(w.s[i] & 0xffu);
+    for (int i = 0; i < 4; ++i) sf[i] = ok ? e8m0_to_f32((sc[i][s & 3] >> (8 * g)) & 0xffu) : 1.0f;
+  };
+
+  auto compute = [&](int buf, const W4& w, const float (&sf)[4]) {
+    const u32x4* src = smem + buf * kUnits;
     // B operand of slice d, column tile c: lane (r, g) takes chunk kq*16 + 4g + d of
     // tile row 16c + r (the k permutation of the skinny kernel), stored at slot
     // (kq*16 + 4g + d) ^ r of that row. The operands of slice d + 1 are read before
@@ -493,32 +519,38 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   // s (scheduling barriers keep them there). After the compute each wave waits for
   // its staging loads only (the weight loads issued after them stay in flight; the
   // counter retires in order), then the barrier makes every wave's rows visible.
-  constexpr int kWLoads = 8;  // VMEM loads of one load_w: 4 code + 4 scale loads
+  constexpr int kWLoads = 4;  // VMEM loads of one load_w
   W4 wa, wb;
+  u32x4 sc[4], scn[4];
+  float sf[4];
+  load_sc(0, sc);
   stage_x(0, 0);
   load_w(0, wa);
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
-  // Two steps per iteration and a single exit, so the accumulators keep their
-  // registers across the loop; with an odd step count the last step reads only
-  // out-of-range (zero) weights and adds nothing.
-  for (int s = 0; s < nsteps; s += 2) {
-    stage_x(s + 1, 1);
+  // Four steps (one block) per iteration and a single exit, so the accumulators keep
+  // their registers across the loop; steps past k read only out-of-range (zero)
+  // codes and add nothing.
+  auto step = [&](int s, auto hc) {
+    constexpr int h = decltype(hc)::value;
+    stage_x(s + h + 1, (h + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(s + 1, wb);
+    load_w(s + h + 1, (h & 1) ? wa : wb);
+    if constexpr (h == 3) load_sc((s >> 2) + 1, scn);  // the next block's scales, with its first codes
     __builtin_amdgcn_sched_barrier(0);
-    compute(0, wa);
+    scale_of(sc, s + h, sf);
+    compute(h & 1, (h & 1) ? wb : wa, sf);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads + (h == 3 ? 4 : 0)));
     lds_barrier();
-    stage_x(s + 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(s + 2, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1, wb);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
-    lds_barrier();
+  };
+  for (int s = 0; s < nsteps; s += 4) {
+    step(s, std::integral_constant<int, 0>{});
+    step(s, std::integral_constant<int, 1>{});
+    step(s, std::integral_constant<int, 2>{});
+    step(s, std::integral_constant<int, 3>{});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = scn[i];
   }
 
   // sum the four k quarters in LDS (the staging buffers are free once every load

@@ -94,13 +94,7 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
       make_rsrc(acodes + (size_t)t0 * arow_bytes, (uint32_t)mrows * arow_bytes);
   const __amdgpu_buffer_rsrc_t xsr = make_rsrc(ascales + (size_t)t0 * kb, (uint32_t)mrows * (uint32_t)kb);
 
-  // Offsets pass through an empty asm: otherwise the compiler folds the unrolled step's
-  // constant into the immediate field and branches around the load on `ok`, and a load
-  // on one side of a branch makes its later wait counts conservative.
-  auto opaque = [](uint32_t v) {
-    asm volatile("" : "+v"(v));
-    return v;
-  };
+  // (load offsets pass through opaque(): see common.hpp)
   // the codes of this wave's RT row tiles for its group of step s (rows past n read 0)
   struct Ops {
     u32x4 c[RT];
