@@ -169,6 +169,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   __shared__ double lds_d[kThreads / kWave];
   __shared__ float lds_f[kThreads / kWave];
   __shared__ int lds_i[kThreads / kWave];
+  __shared__ double tab[32];  // 2^(j/32) for the table-driven exp (visible after block_max)
+  if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Table32[threadIdx.x];
   const int64_t rowg = blockIdx.x;  // row index over all sequences
   const int per_seq = 2 * kd + 1;
   const int64_t s = rowg / per_seq;
@@ -238,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
     const double m64 = (double)mx;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      if constexpr (kT) acc += exp_neg_f64(((double)vals[q] - m64) * tr.inv_tau);
-      else acc += exp_neg_f64((double)vals[q] - m64);
+      if constexpr (kT) acc += exp_neg_f64_tab(((double)vals[q] - m64) * tr.inv_tau, tab);
+      else acc += exp_neg_f64_tab((double)vals[q] - m64, tab);
     }
   }
   acc = block_sum_f64<kThreads>(acc, lds_d);
@@ -253,6 +255,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
 
 // p_n(t) and the final weight of token t: residual (p - q)+, or p for the bonus row.
 struct FinalRows {
+  const double* tab;  // kExp2Table32 in LDS, for exp_neg_f64_tab
   const float* zt;
   const float* zd;  // nullptr for the bonus row
   double mt, inv_st, md, inv_sd;
@@ -271,11 +274,11 @@ __device__ inline void weights_from(const FinalRows& fr, const float (&zt)[kWPer
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
     const double dt = kT ? ((double)zt[j] - fr.mt) * fr.inv_tau : (double)zt[j] - fr.mt;
-    const double p = exp_neg_f64(dt) * fr.inv_st;
+    const double p = exp_neg_f64_tab(dt, fr.tab) * fr.inv_st;
     wp[j] = p;
     if (fr.zd) {
       const double dd = kT ? ((double)zd[j] - fr.md) * fr.inv_tau : (double)zd[j] - fr.md;
-      const double q = exp_neg_f64(dd) * fr.inv_sd;
+      const double q = exp_neg_f64_tab(dd, fr.tab) * fr.inv_sd;
       const double d = p - q;
       wf[j] = d > 0.0 ? d : 0.0;
     } else {
@@ -779,6 +782,8 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   __shared__ int sbad[kMaxRows];
   __shared__ double lds_d[kWThreads / kWave];
   __shared__ int s_n;
+  __shared__ double tab[32];  // visible after the barrier before the piece totals
+  if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Table32[threadIdx.x];
   const int c = blockIdx.x;
   const int64_t s = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -949,6 +954,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   const int n = s_n;
   double a = 0.0, b = 0.0;
   FinalRows fr;
+  fr.tab = tab;
   if (n >= 0) {
     fr.zt = row_ptr(target, draft, s, kd, n, v);
     fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
@@ -1007,6 +1013,8 @@ __global__ __launch_bounds__(kWThreads) void sample_kernel(
   __shared__ double lds_scan[kWThreads / kWave];
   __shared__ double s_incl[kWThreads];
   __shared__ int s_fl[2 * kWWaves];
+  __shared__ double tab[32];  // visible after the piece selection's barriers
+  if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Table32[threadIdx.x];
   const int64_t s = blockIdx.x;
   // the piece totals do not depend on the decision: load them with it
   const bool mine = pieces <= kWThreads && (int)threadIdx.x < pieces;
@@ -1016,6 +1024,7 @@ __global__ __launch_bounds__(kWThreads) void sample_kernel(
   const Decision d = ws.dec[s];
   if (d.n < 0) return;
   FinalRows fr;
+  fr.tab = tab;
   fr.zt = row_ptr(target, draft, s, kd, d.n, v);
   fr.zd = d.n < kd ? row_ptr(target, draft, s, kd, kd + 1 + d.n, v) : nullptr;
   fr.mt = d.mt;

@@ -77,6 +77,42 @@ __device__ inline double exp_neg_f64(double d) {
   return __builtin_ldexp(p, (int)k);
 }
 
+// 2^(j/32), j = 0..31, each correctly rounded to fp64 (computed to 60 digits).
+constexpr double kExp2Table32[32] = {
+    0x1.0000000000000p+0, 0x1.059b0d3158574p+0, 0x1.0b5586cf9890fp+0, 0x1.11301d0125b51p+0,
+    0x1.172b83c7d517bp+0, 0x1.1d4873168b9aap+0, 0x1.2387a6e756238p+0, 0x1.29e9df51fdee1p+0,
+    0x1.306fe0a31b715p+0, 0x1.371a7373aa9cbp+0, 0x1.3dea64c123422p+0, 0x1.44e086061892dp+0,
+    0x1.4bfdad5362a27p+0, 0x1.5342b569d4f82p+0, 0x1.5ab07dd485429p+0, 0x1.6247eb03a5585p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.71f75e8ec5f74p+0, 0x1.7a11473eb0187p+0, 0x1.82589994cce13p+0,
+    0x1.8ace5422aa0dbp+0, 0x1.93737b0cdc5e5p+0, 0x1.9c49182a3f090p+0, 0x1.a5503b23e255dp+0,
+    0x1.ae89f995ad3adp+0, 0x1.b7f76f2fb5e47p+0, 0x1.c199bdd85529cp+0, 0x1.cb720dcef9069p+0,
+    0x1.d5818dcfba487p+0, 0x1.dfc97337b9b5fp+0, 0x1.ea4afa2a490dap+0, 0x1.f50765b6e4540p+0,
+};
+
+// exp(d) in fp64 for d <= 0 (d = -inf gives 0), relative error below 1e-14, by the
+// table-driven method of P. T. P. Tang (ACM TOMS 15(2), 1989): d = (32m + j) ln2/32 + r
+// with |r| <= ln2/64 (the same two-part ln 2 split as above, scaled by 1/32), then
+// e^d = 2^m * 2^(j/32) * p(r) with p the degree-5 Taylor polynomial of e^r (truncation
+// below 2.3e-15 relative). tab holds kExp2Table32 (in LDS: the index differs per lane).
+// About two thirds of the fp64 operations of exp_neg_f64.
+__host__ __device__ inline double exp_neg_f64_tab(double d, const double* tab) {
+  if (!(d > -745.0)) return 0.0;
+  const double kInvL = 46.166241308446828;  // 32 / ln 2
+  const double kL1 = 6.93147180369123816490e-01 / 32.0;
+  const double kL2 = 1.90821492927058770002e-10 / 32.0;
+  const double nd = __builtin_rint(d * kInvL);
+  double r = __builtin_fma(-nd, kL1, d);
+  r = __builtin_fma(-nd, kL2, r);
+  const int n = (int)nd;
+  double p = 8.33333333333333333333e-03;  // 1/5!
+  p = __builtin_fma(p, r, 4.16666666666666666667e-02);
+  p = __builtin_fma(p, r, 1.66666666666666666667e-01);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return __builtin_ldexp(tab[n & 31] * p, n >> 5);
+}
+
 // Block-wide reductions through LDS for blockDim.x == kThreads (a multiple of 64).
 template <int kThreads>
 __device__ inline float block_max(float v, float* lds) {
