@@ -234,26 +234,33 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     }
   };
 
-  // Activation staging of phase ph by direct global-to-LDS loads: wave-load L copies
-  // 64 consecutive chunks (1 KiB) of one activation row, so the LDS destination is
-  // contiguous as the load-to-LDS form requires (nq and the phase start are
-  // multiples of 64 chunks); the rest of each padded row is zero-filled.
+  // Activation staging of phase ph by direct global-to-LDS loads. A wave reads only
+  // the columns of its own k-slice (units [gs*16, (gs + nsub*G)*16) of every row), so
+  // each wave stages exactly those columns and zero-fills their part past the phase's
+  // valid chunks: no workgroup barrier between staging and use, at the start or
+  // between phases. A wave-load copies 64 consecutive chunks (1 KiB) of one row, so
+  // the LDS destination is contiguous as the load-to-LDS form requires (nq, the phase
+  // start and the slice start are multiples of 64 chunks).
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (size_t)t0 * (size_t)k, (uint32_t)(mt * nq) * 16u);
   auto stage = [&](int ph) {
     const int q0 = ph * ngroups_p * 16;                  // first chunk of the phase
     const int nv = min(ngroups_p * 16, nq - q0);         // valid chunks per row
-    const int per_row = nv >> 6;
-    for (int L = wave; L < mt * per_row; L += W) {
+    const int c0 = gs * 16;                              // first chunk of this wave's slice
+    const int cw = nsub * G * 16;                        // chunks in the slice
+    const int cv = max(0, min(cw, nv - c0));             // valid chunks of the slice
+    const int per_row = cv >> 6;
+    for (int L = 0; L < mt * per_row; ++L) {
       const int tt = L / per_row;
       const int c = L - tt * per_row;
       __attribute__((address_space(3))) void* dst =
-          (__attribute__((address_space(3))) void*)(smem + tt * xrs + c * 64);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, (uint32_t)((tt * nq + q0 + c * 64 + lane) * 16), 0,
-                                               0, 0);
+          (__attribute__((address_space(3))) void*)(smem + tt * xrs + c0 + c * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16,
+                                               (uint32_t)((tt * nq + q0 + c0 + c * 64 + lane) * 16), 0, 0, 0);
     }
-    for (int idx = (int)threadIdx.x; idx < mt * (nqp - nv); idx += (int)blockDim.x) {
-      const int tt = idx / (nqp - nv);
-      smem[tt * xrs + nv + (idx - tt * (nqp - nv))] = u32x4{0u, 0u, 0u, 0u};
+    const int zc = cw - cv;
+    for (int idx = lane; idx < mt * zc; idx += kWave) {
+      const int tt = idx / zc;
+      smem[tt * xrs + c0 + cv + (idx - tt * zc)] = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -269,12 +276,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   auto compute = [&](int u, const Block<R, G, kNv>& b) {
     const int uu = u % upr;
     if (phases > 1 && uu != 0 && uu % nsub == 0) {
-      // first unit of a later phase: stage its activations once every wave is done
-      // with the previous phase (this also waits for the prefetched unit)
-      lds_barrier();
+      // first unit of a later phase: this wave restages its own columns (its reads of
+      // the previous phase have completed; this also waits for the prefetched unit)
       stage(uu / nsub);
       __builtin_amdgcn_s_waitcnt(0);
-      lds_barrier();
     }
     const int gl0 = gs + (uu % nsub) * G;
 #pragma unroll
@@ -348,9 +353,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   stage(0);
 #pragma unroll
   for (int i = 0; i < D; ++i) load(i, buf[i]);
-  // the direct loads are counted by vmcnt; wait for them (and the first units)
+  // the direct loads are counted by vmcnt; wait for them (and the first units). No
+  // barrier: a wave reads only the columns it staged itself.
   __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
   for (int u = 0; u < nunits; u += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
