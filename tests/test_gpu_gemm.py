@@ -48,6 +48,8 @@ def test_one_hot_columns_exact():
     # several column tiles, k split into sub-slices, waves past the last group)
     (5, 8192, 1), (64, 512, 17), (1000, 4096, 5), (17, 1024, 3), (4100, 512, 9),
     (130, 14336, 5), (33, 2048, 16), (100, 512, 40), (70000, 512, 2), (3, 11776, 8),
+    # 16 positions over k = 4608 do not fit in LDS: two phases, 263 row blocks
+    (4200, 4608, 16),
 ])
 def test_ragged_shapes(n, k, m):
     say(f"gemm: ragged n={n} k={k} m={m}")
