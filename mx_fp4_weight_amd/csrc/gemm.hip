@@ -137,10 +137,12 @@ struct Group {
   int count;
 };
 
+// nred: partial-tile buffers for the cross-wave sum: 2 alternate between row blocks,
+// 1 when that is what lets the targeted number of workgroups share a CU's LDS.
 template <int R, int G, int D, bool kNv>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
                                                                          int nsub, int phases,
-                                                                         int ngroups_p) {
+                                                                         int ngroups_p, int nred) {
   extern __shared__ u32x4 smem[];
   int pi = 0;
   while (pi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[pi + 1]) ++pi;
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   const int nqp = W * nsub * G * 16;       // chunks per padded row of a phase
   const int xrs = nqp + 1;                 // row stride in units
   const int xunits = mt * xrs;
-  f32x4* red = reinterpret_cast<f32x4*>(smem + xunits);  // [2][W][R][64]
+  f32x4* red = reinterpret_cast<f32x4*>(smem + xunits);  // [nred][W][R][64]
   // Lane (r, g) reads chunk grp·16 + 4g + d of row r; rows past m read row 0, which
   // only feeds output columns that are never stored.
   const int xlane = (t_ok ? r : 0) * xrs + 4 * g;
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     if (uu != upr - 1) return;
     // last unit of the row block: sum the waves' partial tiles and store
     const int rb = wg + (u / upr) * ngrid;
-    f32x4* rp = red + (size_t)parity * W * R * kWave;
+    f32x4* rp = red + (size_t)(nred == 2 ? parity : 0) * W * R * kWave;
 #pragma unroll
     for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
     lds_barrier();
@@ -337,6 +339,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
         }
       }
     }
+    // one buffer: every wave waits until the sum has read it before the next row
+    // block's partial tiles overwrite it
+    if (nred == 1) lds_barrier();
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
@@ -758,11 +763,14 @@ inline void split_k(int64_t ngroups, int G, int& waves, int& nsub) {
 // phase starts on a 4-group (512-k) boundary so its activation rows stay in whole
 // 1 KiB windows. Returns false if even 4 groups per phase do not fit.
 struct PhasePlan {
-  int phases, ngroups_p, waves, nsub;
+  int phases, ngroups_p, waves, nsub, nred;
   size_t lds;
 };
 
-inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp) {
+// per_cu: resident workgroups per CU the grid is sized for. With one phase, a single
+// partial-tile buffer is taken when two would keep that many workgroups from sharing a
+// CU's LDS (8 positions over k = 4096: 82 048 bytes with two buffers, 73 856 with one).
+inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp, int per_cu = 1) {
   const int64_t ngroups = (k / 32 + 3) / 4;
   const int64_t mt = m < 16 ? m : 16;
   for (int64_t phases = 1; phases <= ngroups; ++phases) {
@@ -772,9 +780,10 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp) {
     int waves, nsub;
     split_k(ngp, G, waves, nsub);
     const int64_t xrs = (int64_t)waves * nsub * G * 16 + 1;  // padded row stride, 16-byte units
-    const size_t lds = (size_t)(mt * xrs) * 16 + 2 * sizeof(f32x4) * waves * R * kWave;
-    if (lds <= kMaxLds) {
-      pp = PhasePlan{(int)phases, (int)ngp, waves, nsub, lds};
+    const size_t xb = (size_t)(mt * xrs) * 16, rb = sizeof(f32x4) * waves * R * kWave;
+    if (xb + 2 * rb <= kMaxLds) {
+      const bool one = per_cu > 1 && xb + 2 * rb > kMaxLds / per_cu && xb + rb <= kMaxLds / per_cu;
+      pp = PhasePlan{(int)phases, (int)ngp, waves, nsub, one ? 1 : 2, xb + (one ? 1 : 2) * rb};
       return true;
     }
     if (ngp <= 4) break;
@@ -808,7 +817,7 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
   }
   grp.wg_start[count] = start;
   gemm_skinny_kernel<R, G, D, kNv><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(pp.waves * kWave),
-                             pp.lds, stream>>>(grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p);
+                             pp.lds, stream>>>(grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p, pp.nred);
   return hipGetLastError();
 }
 
@@ -866,7 +875,7 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
   for (int i = 0; i < count; ++i)
     aligned = aligned && ((reinterpret_cast<uintptr_t>(pv[i].scales) & 15) == 0);
   PhasePlan pp;
-  if (aligned && plan_phases(k, m, c.R, c.G, pp)) {
+  if (aligned && plan_phases(k, m, c.R, c.G, pp, c.per_cu)) {
     // With several phases a workgroup owns one row block of one row tile (16 rows).
     // Two row tiles per block (half the workgroups, all resident at once) measured
     // slower: 8192 x 28672 at T = 5 took 42.9 µs with two tiles, 39.4 µs with one.
@@ -917,7 +926,7 @@ static hipError_t launch_nvfp4_group(const mxs_problem_view* pv, int count, int6
   }
   const Config c = choose(n_total, k);
   PhasePlan pp;
-  if (!plan_phases(k, m < 16 ? m : 16, c.R, c.G, pp)) return hipErrorInvalidValue;
+  if (!plan_phases(k, m < 16 ? m : 16, c.R, c.G, pp, c.per_cu)) return hipErrorInvalidValue;
   if (pp.phases > 1) {
     // with several phases a workgroup owns one row block: two row tiles per block when
     // that still leaves a workgroup per CU

@@ -50,6 +50,9 @@ def test_one_hot_columns_exact():
     (130, 14336, 5), (33, 2048, 16), (100, 512, 40), (70000, 512, 2), (3, 11776, 8),
     # 16 positions over k = 4608 do not fit in LDS: two phases, 263 row blocks
     (4200, 4608, 16),
+    # one partial-tile buffer so that two workgroups share a CU's LDS (8 positions over
+    # k = 4096; 12 over k = 3072 with 563 row blocks, two on some workgroups)
+    (4100, 4096, 8), (9000, 3072, 12),
 ])
 def test_ragged_shapes(n, k, m):
     say(f"gemm: ragged n={n} k={k} m={m}")
