@@ -139,7 +139,11 @@ struct Group {
 
 // nred: partial-tile buffers for the cross-wave sum: 2 alternate between row blocks,
 // 1 when that is what lets the targeted number of workgroups share a CU's LDS.
-template <int R, int G, int D, bool kNv>
+// kPair (several phases only): a workgroup owns the row blocks wg and wg + gridDim
+// and walks them phase by phase (phase 0 of both, then phase 1 of both, ...), with a
+// second set of accumulators, so a phase's activations are staged once for two row
+// blocks and every workgroup is resident at once.
+template <int R, int G, int D, bool kNv, bool kPair = false>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
                                                                          int nsub, int phases,
                                                                          int ngroups_p, int nred) {
@@ -187,21 +191,43 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   const int xlane = (t_ok ? r : 0) * xrs + 4 * g;
 
   // this workgroup's work: its row blocks times the phases times the nsub
-  // sub-slices of G groups (with several phases a workgroup owns one row block)
-  const int upr = phases * nsub;  // units per row block
-  const int my_blocks = wg < nrb ? (nrb - 1 - wg) / ngrid + 1 : 0;
+  // sub-slices of G groups (with several phases a workgroup owns one row block, or
+  // in pair mode one pair walked phase-major: all its units form one sequence)
+  const int upr = phases * nsub * (kPair ? 2 : 1);  // units per row block (pair)
+  const int my_blocks = kPair ? (wg < nrb ? 1 : 0) : (wg < nrb ? (nrb - 1 - wg) / ngrid + 1 : 0);
   const int nunits = my_blocks * upr;
+  // unit u -> its row block, phase and sub-slice (j: which block of a pair)
+  struct Loc {
+    int rb, ph, sub, j;
+  };
+  auto locate = [&](int u) {
+    Loc l;
+    const int uu = u % upr;
+    l.sub = uu % nsub;
+    if constexpr (kPair) {
+      l.j = (uu / nsub) & 1;
+      l.ph = uu / (2 * nsub);
+      l.rb = wg + l.j * ngrid;
+    } else {
+      l.j = 0;
+      l.ph = uu / nsub;
+      l.rb = wg + (u / upr) * ngrid;
+    }
+    return l;
+  };
 
   const uint32_t srow = kNv ? (uint32_t)(k >> 4) : (uint32_t)kb;  // scale bytes per row
   auto load = [&](int u, Block<R, G, kNv>& b) {
-    const int rb = wg + (u / upr) * ngrid;
-    const int uu = u % upr;
-    const int gl0 = gs + (uu % nsub) * G;            // first group inside the phase
-    const int g0 = (uu / nsub) * ngroups_p + gl0;   // first group of k
-    // descriptors covering the valid rows of row block rb (none past the last unit)
+    const Loc l = locate(u);
+    const int rb = l.rb;
+    const int gl0 = gs + l.sub * G;            // first group inside the phase
+    const int g0 = l.ph * ngroups_p + gl0;   // first group of k
+    // descriptors covering the valid rows of row block rb (none past the last unit;
+    // none for the missing second block of a last pair)
     const int row0 = rb * 16 * R;
-    const int rows = u < nunits ? min(16 * R, n - row0) : 0;
-    const int rowc = u < nunits ? row0 : 0;
+    const bool live = u < nunits && rb < nrb;
+    const int rows = live ? min(16 * R, n - row0) : 0;
+    const int rowc = live ? row0 : 0;
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)rowc * srow, (uint32_t)rows * srow);
     // The whole offset goes in voffset (soffset = 0): the range check of a raw
@@ -269,21 +295,41 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   // four accumulator chains per row tile (one per MFMA slice d), so consecutive
   // MFMAs do not wait for each other; summed in a fixed order at the end
   f32x4 acc[R][4];
+  f32x4 acc2[kPair ? R : 1][4];  // pair mode: the other row block's accumulators
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int d = 0; d < 4; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (kPair) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) acc2[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   int parity = 0;
 
   auto compute = [&](int u, const Block<R, G, kNv>& b) {
-    const int uu = u % upr;
-    if (phases > 1 && uu != 0 && uu % nsub == 0) {
+    const Loc l = locate(u);
+    if (phases > 1 && l.ph > 0 && l.sub == 0 && l.j == 0) {
       // first unit of a later phase: this wave restages its own columns (its reads of
       // the previous phase have completed; this also waits for the prefetched unit)
-      stage(uu / nsub);
+      stage(l.ph);
       __builtin_amdgcn_s_waitcnt(0);
     }
-    const int gl0 = gs + (uu % nsub) * G;
+    if constexpr (kPair) {
+      // the pair's other row block starts: exchange the accumulator sets
+      if (l.sub == 0 && u % upr != 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const f32x4 tmp = acc[i][d];
+            acc[i][d] = acc2[i][d];
+            acc2[i][d] = tmp;
+          }
+      }
+    }
+    const int gl0 = gs + l.sub * G;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int gl = gl0 + j;
@@ -314,9 +360,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
         }
       }
     }
-    if (uu != upr - 1) return;
-    // last unit of the row block: sum the waves' partial tiles and store
-    const int rb = wg + (u / upr) * ngrid;
+    if (l.sub != nsub - 1 || l.ph != phases - 1) return;
+    // last unit of the row block: sum the waves' partial tiles and store (a missing
+    // second block of a pair has rows >= n: nothing is stored)
+    const int rb = l.rb;
     f32x4* rp = red + (size_t)(nred == 2 ? parity : 0) * W * R * kWave;
 #pragma unroll
     for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
@@ -791,11 +838,11 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp, int p
   return false;
 }
 
-template <int R, int G, int D, bool kNv = false>
+template <int R, int G, int D, bool kNv = false, bool kPair = false>
 hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
                        int64_t k, int64_t m, hipStream_t stream) {
   static std::atomic<bool> done[kMaxDevices];
-  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv>, done);
+  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv, kPair>, done);
   if (e != hipSuccess) return e;
   Group grp{};
   grp.count = count;
@@ -807,7 +854,7 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     const int64_t nrb = (pv[i].n + 16 * R - 1) / (16 * R);
     // persistent grid split in proportion to the row blocks (at least one workgroup
     // each); with several phases every row block gets its own workgroup
-    int64_t share = pp.phases > 1 ? nrb : (budget * nrb + total_rb - 1) / total_rb;
+    int64_t share = pp.phases > 1 ? (kPair ? (nrb + 1) / 2 : nrb) : (budget * nrb + total_rb - 1) / total_rb;
     if (share > nrb) share = nrb;
     if (share < 1) share = 1;
     grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, kNv ? pv[i].gscale : nullptr, (int)pv[i].n, (int)nrb,
@@ -816,8 +863,9 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     start += (int)share;
   }
   grp.wg_start[count] = start;
-  gemm_skinny_kernel<R, G, D, kNv><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)), dim3(pp.waves * kWave),
-                             pp.lds, stream>>>(grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p, pp.nred);
+  gemm_skinny_kernel<R, G, D, kNv, kPair><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)),
+                                           dim3(pp.waves * kWave), pp.lds, stream>>>(
+      grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p, pp.nred);
   return hipGetLastError();
 }
 
@@ -876,9 +924,15 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
     aligned = aligned && ((reinterpret_cast<uintptr_t>(pv[i].scales) & 15) == 0);
   PhasePlan pp;
   if (aligned && plan_phases(k, m, c.R, c.G, pp, c.per_cu)) {
-    // With several phases a workgroup owns one row block of one row tile (16 rows).
-    // Two row tiles per block (half the workgroups, all resident at once) measured
-    // slower: 8192 x 28672 at T = 5 took 42.9 µs with two tiles, 39.4 µs with one.
+    // With several phases a workgroup walks a pair of 16-row blocks phase by phase
+    // (kPair) when the pairs still give every CU a workgroup (8192 x 28672 at T = 5:
+    // 39.2 -> 33.2 µs); with fewer row blocks (4096 x 14336 at T = 8: 128 pairs,
+    // 13.0 -> 17.7 µs) each row block keeps its own workgroup. Two row tiles per
+    // block (R = 2) measured slower than either: 42.9 µs for 8192 x 28672.
+    int64_t pairs = 0;
+    for (int i = 0; i < count; ++i) pairs += ((pv[i].n + 15) / 16 + 1) / 2;
+    if (pp.phases > 1 && pairs >= kCUs && c.R == 1 && c.G == 4 && c.D == 2)
+      return launch_main<1, 4, 2, false, true>(c, pp, pv, count, k, m, stream);
 #define MXS_RG(RR, GG, DD) \
   if (c.R == RR && c.G == GG && c.D == DD) return launch_main<RR, GG, DD>(c, pp, pv, count, k, m, stream);
     MXS_RG(1, 4, 2) MXS_RG(2, 4, 2) MXS_RG(1, 8, 2) MXS_RG(2, 8, 2)

@@ -77,6 +77,25 @@ def test_phased_k_shapes(n, k, m):
 
 
 @pytest.mark.parametrize("n,k,m", [
+    # enough row blocks for one workgroup per pair of blocks on every CU: each workgroup
+    # walks its pair phase by phase (two and four phases); 513 row blocks leave the last
+    # pair without its second block
+    (8200, 14336, 8), (8193, 16384, 16),
+])
+def test_phased_pairs(n, k, m):
+    say(f"gemm: phased pairs n={n} k={k} m={m}")
+    w = synth.weights(11, n + k + m, n, k)
+    codes, scales, _ = omx.quantize(w)
+    del w
+    x = synth.activations(11, n + k + m, m, k)
+    rng = np.random.default_rng(n + k)
+    rows = np.unique(np.concatenate([rng.choice(n, size=160, replace=False),
+                                     np.arange(0, 16), np.arange(n - 24, n), [4112, 4128]]))
+    y = run_gemm(codes, scales, x)
+    check_gemm(codes, scales, n, k, x, y[:, rows], rows=rows, label=f"pairs {n}x{k}x{m}")
+
+
+@pytest.mark.parametrize("n,k,m", [
     # m > 32 with k % 128 == 0: the dense kernel (128 weight rows x 80 positions per tile,
     # k split in two halves of alternating 128-k groups)
     (1, 128, 33), (130, 384, 80), (257, 1024, 100), (1000, 2304, 161), (64, 128, 320),
