@@ -158,8 +158,13 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   const int nrb = grp.p[pi].nrb;
   const int y_vec4 = grp.p[pi].y_vec4;
   const float gscale = kNv ? *grp.p[pi].gscale : 1.0f;
-  const int wg = (int)blockIdx.x - grp.wg_start[pi];               // index among this problem's
-  const int ngrid = grp.wg_start[pi + 1] - grp.wg_start[pi];        // workgroups
+  const int ngrid = grp.wg_start[pi + 1] - grp.wg_start[pi];        // this problem's workgroups
+  // index among them; mirrored for every second product, so the workgroups holding one
+  // row block more than the others are the first ones of product 0 and the last ones of
+  // product 1 (the two resident workgroups of a CU, w and w + one grid, then sum to the
+  // same number of row blocks)
+  const int wgr = (int)blockIdx.x - grp.wg_start[pi];
+  const int wg = (pi & 1) ? ngrid - 1 - wgr : wgr;
   const int W = blockDim.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
