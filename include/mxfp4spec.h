@@ -241,6 +241,36 @@ mxs_status mx_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64
                               float* y, void* stream);
 
 /*
+ * mxfp4_tile_codes — MX-FP4 codes in the mxfp4_quantize row layout [n, k/2] -> the
+ * tiled layout read by mx_verify_gemm_act_tiled. This is a byte permutation done once
+ * at weight-prep time, like the quantization itself [M11 §12 fixes the values; the
+ * byte order in memory is this library's choice]. The scales are not tiled.
+ *
+ * Tiled layout: one 1 KiB tile per (16-row tile t, 128-k group q), at byte
+ * (t * (k/128) + q) * 1024. Its 16-byte unit L = 16 * g + r (g = 0..3, r = 0..15)
+ * holds the 16 bytes of row 16 t + r, MX block 4 q + g (columns 128 q + 32 g ..
+ * + 31, low nibble = even column, as in the row layout). Rows past n (up to the
+ * next multiple of 16) are zero.
+ *
+ * codes   [n, k/2], 16-byte aligned; k % 128 == 0, k >= 128.
+ * tiled   mxfp4_tiled_bytes(n, k) bytes (= ceil(n/16) * 16 * k/2), 16-byte aligned.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+size_t mxfp4_tiled_bytes(int64_t n, int64_t k); /* 0 when the sizes are out of range */
+mxs_status mxfp4_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t* tiled, void* stream);
+
+/*
+ * mx_verify_gemm_act_tiled — mx_verify_gemm_act with the weight codes in the tiled
+ * layout of mxfp4_tile_codes (scales in the row layout [n, k/32]). Every wave-wide
+ * weight load then reads 1 KiB contiguously instead of 64 bytes from each of 16 rows.
+ * The result is bit-identical to mx_verify_gemm_act on the same weights. Same
+ * arguments, rules and errors.
+ */
+mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* scales, int64_t n, int64_t k,
+                                    const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt, int64_t m,
+                                    float* y, void* stream);
+
+/*
  * spec_accept_workspace_bytes — device workspace spec_accept needs for
  * (b, kd, v). Returns 0 when the sizes are out of range.
  */

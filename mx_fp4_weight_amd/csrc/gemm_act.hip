@@ -31,7 +31,10 @@ constexpr int kRows = 128;  // weight rows per workgroup tile
 constexpr int kMC = 5;      // 16-position column tiles per workgroup tile
 constexpr int kRQ = 2;      // row groups per tile: 4·kRQ waves, 8/kRQ row tiles per wave
 
-template <int MC, int AF, int RQ>
+// kTiled: the weight codes come in the tiled layout of mxfp4_tile_codes (one 1 KiB tile
+// per 16 rows x 128-k group, the lanes of an operand load in order), so each wave-wide
+// operand load reads 1 KiB contiguously instead of 64 bytes from each of 16 rows.
+template <int MC, int AF, int RQ, bool kTiled = false>
 __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint8_t* __restrict__ acodes, const uint8_t* __restrict__ ascales, float* __restrict__ y,
@@ -86,7 +89,10 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
   const uint32_t arow_bytes = AF == MXS_ACT_FP8 ? (uint32_t)k : (uint32_t)(k >> 1);
   const int row0 = nt * kRows;
   const int rows = min(kRows, n - row0);
-  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
+  // a tiled matrix holds whole 16-row tiles (rows past n are zero); both layouts put
+  // row0 at byte row0 * row_bytes
+  const int crows = kTiled ? min(kRows, ((n + 15) & ~15) - row0) : rows;
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)row0 * row_bytes, (uint32_t)crows * row_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)row0 * kb, (uint32_t)rows * (uint32_t)kb);
   const int t0 = mtile * BM;
   const int mrows = min(BM, m - t0);
@@ -106,7 +112,11 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       const uint32_t row = (uint32_t)(rq * 16 * RT + 16 * i + r);
-      const uint32_t co = opaque(ok ? row * row_bytes + (uint32_t)blk * 16 : kOutOfRange);
+      // tiled: tile (row tile, group) is 1 KiB at ((row tile) * groups + group) * 1 KiB,
+      // and lane (r, g) holds the 16 bytes of row r, block g
+      const uint32_t tile = (uint32_t)(rq * RT + i) * (uint32_t)ngroups + (uint32_t)grp;
+      const uint32_t co = opaque(ok ? (kTiled ? tile * 1024u + (uint32_t)lane * 16u : row * row_bytes + (uint32_t)blk * 16)
+                                    : kOutOfRange);
       o.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, co, 0, 0));
     }
   };
@@ -279,25 +289,54 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
   }
 }
 
-template <int AF>
+template <int AF, bool kTiled>
 hipError_t launch(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k, const uint8_t* acodes,
                   const uint8_t* ascales, int64_t m, float* y, hipStream_t stream) {
   const int n_tiles = (int)((n + kRows - 1) / kRows);
   const int m_tiles = (int)((m + 16 * kMC - 1) / (16 * kMC));
   const int64_t wgs = (int64_t)((n_tiles + 7) / 8) * 8 * m_tiles;
   const int y_vec4 = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
-  gemm_act_kernel<kMC, AF, kRQ><<<dim3((unsigned)wgs), dim3(256 * kRQ), 0, stream>>>(
+  gemm_act_kernel<kMC, AF, kRQ, kTiled><<<dim3((unsigned)wgs), dim3(256 * kRQ), 0, stream>>>(
       codes, scales, acodes, ascales, y, (int)n, (int)k, (int)m, n_tiles, m_tiles, y_vec4);
   return hipGetLastError();
+}
+
+// Row-layout codes [n, k/2] -> tiled codes: unit (16 bytes) u of the output, with
+// u = (row tile * groups + group) * 64 + 16 * g + r, is row 16 * tile + r, MX block
+// 4 * group + g of the input; rows past n are zero. One thread per unit.
+__global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t* __restrict__ codes, int64_t n, int64_t k,
+                                                         uint8_t* __restrict__ tiled, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int64_t groups = k >> 7;
+  const int lane = (int)(u & 63);
+  const int64_t tg = u >> 6;
+  const int64_t tile = tg / groups;
+  const int64_t grp = tg - tile * groups;
+  const int64_t row = tile * 16 + (lane & 15);
+  const int64_t blk = grp * 4 + (lane >> 4);
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (row < n) v = *reinterpret_cast<const u32x4*>(codes + row * (k >> 1) + blk * 16);
+  *reinterpret_cast<u32x4*>(tiled + u * 16) = v;
 }
 
 }  // namespace
 
 hipError_t launch_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                                   const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt,
-                                  int64_t m, float* y, hipStream_t stream) {
-  if (fmt == MXS_ACT_FP8) return launch<MXS_ACT_FP8>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
-  return launch<MXS_ACT_FP4>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
+                                  int64_t m, float* y, bool tiled, hipStream_t stream) {
+  if (tiled) {
+    if (fmt == MXS_ACT_FP8) return launch<MXS_ACT_FP8, true>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
+    return launch<MXS_ACT_FP4, true>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
+  }
+  if (fmt == MXS_ACT_FP8) return launch<MXS_ACT_FP8, false>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
+  return launch<MXS_ACT_FP4, false>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
+}
+
+hipError_t launch_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t* tiled, hipStream_t stream) {
+  const int64_t units = (n + 15) / 16 * (k >> 7) * 64;
+  tile_codes_kernel<<<dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream>>>(codes, n, k, tiled, units);
+  return hipGetLastError();
 }
 
 }  // namespace mxs

@@ -274,3 +274,24 @@ def test_nvfp4_grouped_host_errors():
     arr[1].global_scale = 0x300000
     arr[0].scales = 0x200008
     assert lib.nvfp4_verify_gemm_grouped(arr, 2, 512, 5, None) == mxs.MXS_ERR_ALIGN
+
+
+def test_tiled_host_errors():
+    """mxfp4_tile_codes / mx_verify_gemm_act_tiled refuse malformed calls before any HIP call."""
+    lib = mxs.get_lib()
+    assert lib.mxfp4_tiled_bytes(17, 256) == 32 * 128
+    assert lib.mxfp4_tiled_bytes(16, 256) == 16 * 128
+    assert lib.mxfp4_tiled_bytes(16, 192) == 0 and lib.mxfp4_tiled_bytes(0, 256) == 0
+    a, b = P(0x100000), P(0x200000)
+    assert lib.mxfp4_tile_codes(None, 16, 256, b, None) == mxs.MXS_ERR_NULL
+    assert lib.mxfp4_tile_codes(a, 16, 192, b, None) == mxs.MXS_ERR_SHAPE
+    assert lib.mxfp4_tile_codes(a, 0, 256, b, None) == mxs.MXS_ERR_SHAPE
+    assert lib.mxfp4_tile_codes(P(0x100008), 16, 256, b, None) == mxs.MXS_ERR_ALIGN
+    assert lib.mxfp4_tile_codes(a, 16, 256, b, None) == mxs.MXS_ERR_DEVICE
+    call = lambda tc=0x100000, fmt=0, n=64, k=256, m=5: lib.mx_verify_gemm_act_tiled(
+        P(tc) if tc else None, P(0x300000), n, k, P(0x400000), P(0x500000), fmt, m, P(0x600000), None)
+    assert call(tc=0) == mxs.MXS_ERR_NULL
+    assert call(fmt=3) == mxs.MXS_ERR_VALUE
+    assert call(k=192) == mxs.MXS_ERR_SHAPE and call(m=0) == mxs.MXS_ERR_SHAPE and call(n=0) == mxs.MXS_ERR_SHAPE
+    assert call(tc=0x100004) == mxs.MXS_ERR_ALIGN
+    assert call() == mxs.MXS_ERR_DEVICE

@@ -199,3 +199,45 @@ def test_gemm_batched_shape_sampled(fmt):
     wonly = ogemm.verify_gemm(sub_c, sub_s, n, k, x, rows=rows)
     say(f"  {NAME[fmt]} activations vs bf16 activations: rel L2 "
         f"{np.linalg.norm(yr - wonly) / np.linalg.norm(wonly):.3e}")
+
+
+def tile_ref(codes, n, k):
+    """The tiled layout written out with NumPy: (16-row tile, 128-k group, block g, row r, 16 bytes)."""
+    n16 = (n + 15) // 16 * 16
+    full = np.zeros((n16, k // 2), np.uint8)
+    full[:n] = codes
+    t = full.reshape(n16 // 16, 16, k // 128, 4, 16)     # tile, r, group, g, byte
+    return t.transpose(0, 2, 3, 1, 4).reshape(-1)        # tile, group, g, r, byte
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (16, 256), (17, 384), (100, 1024), (1000, 2304), (4099, 4096)])
+def test_tile_codes_layout(n, k):
+    """mxfp4_tile_codes is the documented byte permutation (random bytes, ragged n)."""
+    say(f"tile codes n={n} k={k}")
+    codes = synth.rng(77, n, k).integers(0, 256, (n, k // 2), dtype=np.uint8)
+    got = host(mxs.mxfp4_tile_codes(dev(codes)))
+    torch.cuda.synchronize()
+    assert got.size == mxs.mxfp4_tiled_bytes(n, k)
+    assert np.array_equal(got, tile_ref(codes, n, k))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k,m", [
+    (1, 128, 1), (17, 128, 5), (130, 384, 80), (257, 1024, 100), (1000, 2304, 161), (300, 896, 81),
+    (129, 3200, 47), (1024, 1024, 240), (5, 512, 1),
+])
+def test_gemm_tiled_matches_row_layout(fmt, n, k, m):
+    """The tiled-weight product equals the row-layout product bit for bit (same operands, same
+    sums), and the oracle bar on one shape in three."""
+    say(f"act gemm tiled {NAME[fmt]}: n={n} k={k} m={m}")
+    idx = n + 3 * k + m
+    wc, ws, _ = omx.quantize(synth.weights(78, idx, n, k))
+    ac, asc, _ = oa.quantize(synth.activations(78, idx, m, k), fmt)
+    dwc, dws, dac, das = dev(wc), dev(ws), dev(ac), dev(asc)
+    y_row = host(mxs.mx_verify_gemm_act(dwc, dws, dac, das, fmt))
+    tiled = mxs.mxfp4_tile_codes(dwc)
+    y_tiled = host(mxs.mx_verify_gemm_act_tiled(tiled, dws, n, dac, das, fmt))
+    torch.cuda.synchronize()
+    assert np.array_equal(y_tiled, y_row), (n, k, m)
+    if idx % 3 == 0:
+        check_gemm(wc, ws, n, k, ac, asc, fmt, y_tiled, label=f"tiled {n}x{k}x{m}")
