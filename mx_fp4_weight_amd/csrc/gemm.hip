@@ -128,7 +128,8 @@ struct Problem {
   const uint16_t* x;
   float* y;
   const float* gscale;  // NVFP4 tensor scale (device), null for MX-FP4
-  int n, nrb, y_vec4, pad;
+  int n, nrb, y_vec4;
+  int brows;            // rows per row block: 16·R, or 8 (R = 1: the MFMA's upper 8 rows read zeros)
 };
 
 struct Group {
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   float* __restrict__ y = grp.p[pi].y;
   const int n = grp.p[pi].n;
   const int nrb = grp.p[pi].nrb;
+  const int brows = grp.p[pi].brows;
   const int y_vec4 = grp.p[pi].y_vec4;
   const float gscale = kNv ? *grp.p[pi].gscale : 1.0f;
   const int ngrid = grp.wg_start[pi + 1] - grp.wg_start[pi];        // this problem's workgroups
@@ -229,9 +231,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     const int g0 = l.ph * ngroups_p + gl0;   // first group of k
     // descriptors covering the valid rows of row block rb (none past the last unit;
     // none for the missing second block of a last pair)
-    const int row0 = rb * 16 * R;
+    const int row0 = rb * brows;
     const bool live = u < nunits && rb < nrb;
-    const int rows = live ? min(16 * R, n - row0) : 0;
+    // lanes of rows past `rows` (the rest of an 8-row block, or past n) read zero
+    const int rows = live ? min(brows, n - row0) : 0;
     const int rowc = live ? row0 : 0;
     const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)rowc * srow, (uint32_t)rows * srow);
@@ -373,14 +376,14 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
 #pragma unroll
     for (int i = 0; i < R; ++i) rp[(wave * R + i) * kWave + lane] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
     lds_barrier();
-    const int row0 = rb * 16 * R;
+    const int row0 = rb * brows;
     for (int i = wave; i < R; i += W) {
       f32x4 sum = rp[i * kWave + lane];
       for (int w = 1; w < W; ++w) sum += rp[(w * R + i) * kWave + lane];
       if constexpr (kNv) sum *= gscale;
       // lane holds C[4g + e][r]: output row row0 + 16 i + 4 g + e, position t
       const int orow = row0 + 16 * i + 4 * g;
-      if (t_ok) {
+      if (t_ok && 16 * i + 4 * g < brows) {
         float* yp = y + (size_t)t * (size_t)n + orow;
         if (y_vec4 && orow + 3 < n) {
           *reinterpret_cast<f32x4*>(yp) = sum;
@@ -851,8 +854,6 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
   if (e != hipSuccess) return e;
   Group grp{};
   grp.count = count;
-  int64_t total_rb = 0;
-  for (int i = 0; i < count; ++i) total_rb += (pv[i].n + 16 * R - 1) / (16 * R);
   const int64_t budget = (int64_t)kCUs * c.per_cu;
   // Persistent grid split between the products: in proportion to their row blocks, at
   // least one workgroup each, never more than a product's row blocks, and never more
@@ -862,9 +863,26 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
   // (or pair of row blocks) gets its own workgroup.
   int64_t share[kMaxGroup];
   int64_t nrbs[kMaxGroup];
-  int64_t sum = 0;
+  int brows[kMaxGroup];
+  // 8-row blocks for every product but the largest when the group's 16-row blocks leave
+  // resident slots unused and the halves still fit: q | k | v of the 8B-class layer is
+  // 256 + 64 + 64 blocks on 512 slots (two per CU), so half the CUs held two blocks and
+  // half one; with k and v in 8-row blocks every CU holds one q block and one half block.
+  int big = 0;
+  int64_t nrb16 = 0, half_total = 0;
   for (int i = 0; i < count; ++i) {
-    nrbs[i] = (pv[i].n + 16 * R - 1) / (16 * R);
+    nrb16 += (pv[i].n + 16 * R - 1) / (16 * R);
+    if (pv[i].n > pv[big].n) big = i;
+  }
+  for (int i = 0; i < count; ++i) half_total += i == big ? (pv[i].n + 15) / 16 : (pv[i].n + 7) / 8;
+  const bool halves = R == 1 && pp.phases == 1 && count > 1 && nrb16 < budget && half_total <= budget;
+  for (int i = 0; i < count; ++i) brows[i] = halves && i != big ? 8 : 16 * R;
+  int64_t sum = 0, total_rb = 0;
+  for (int i = 0; i < count; ++i) {
+    nrbs[i] = (pv[i].n + brows[i] - 1) / brows[i];
+    total_rb += nrbs[i];
+  }
+  for (int i = 0; i < count; ++i) {
     int64_t sh = pp.phases > 1 ? (kPair ? (nrbs[i] + 1) / 2 : nrbs[i]) : budget * nrbs[i] / total_rb;
     sh = sh > nrbs[i] ? nrbs[i] : sh;
     share[i] = sh < 1 ? 1 : sh;
@@ -872,11 +890,11 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
   }
   if (pp.phases == 1) {
     while (sum > budget) {  // only when the minimum of one per product overshoots
-      int big = 0;
+      int top = 0;
       for (int i = 1; i < count; ++i)
-        if (share[i] > share[big]) big = i;
-      if (share[big] <= 1) break;
-      --share[big];
+        if (share[i] > share[top]) top = i;
+      if (share[top] <= 1) break;
+      --share[top];
       --sum;
     }
     while (sum < budget) {
@@ -899,7 +917,7 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
   for (int i = 0; i < count; ++i) {
     const int64_t nrb = nrbs[i];
     grp.p[i] = Problem{pv[i].codes, pv[i].scales, pv[i].x, pv[i].y, kNv ? pv[i].gscale : nullptr, (int)pv[i].n, (int)nrb,
-                       y_vec4_ok(pv[i].y, pv[i].n), 0};
+                       y_vec4_ok(pv[i].y, pv[i].n), brows[i]};
     grp.wg_start[i] = start;
     start += (int)share[i];
   }

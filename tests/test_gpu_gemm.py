@@ -229,7 +229,9 @@ def test_batched_320_rows_sampled():
 
 
 @pytest.mark.parametrize("shapes,k,m", [
-    ([4096, 1024, 1024], 4096, 5),          # q | k | v
+    ([4096, 1024, 1024], 4096, 5),          # q | k | v (k and v in 8-row blocks)
+    ([1000, 130, 17, 9], 1024, 5),          # 8-row blocks for all but the largest, partial ones
+    ([1000, 130, 17, 9], 1024, 16),
     ([14336, 14336], 4096, 5),              # gate | up
     ([17, 300, 1, 4100, 64, 2048, 5, 33, 999], 512, 9),   # ten products: two launches, ragged
     ([130, 70], 1056, 3),                   # k % 512 != 0: one fallback launch per product
