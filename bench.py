@@ -365,11 +365,11 @@ def batched(torch, mxs, gen, reps=5):
             for (c, s, _), (ac, asc) in zip(copies, acts):
                 mxs.mx_verify_gemm_act(c, s, ac, asc, fmt, y=y)
         # weight codes in the tiled layout (a one-off permutation at weight-prep time)
-        tiled = [mxs.mxfp4_tile_codes(c) for (c, _, _) in copies]
+        tiled = [(mxs.mxfp4_tile_codes(c), mxs.mxfp4_tile_scales(s)) for (c, s, _) in copies]
 
         def body_t(fmt=fmt, acts=acts, tiled=tiled):
-            for (_, s, _), tc, (ac, asc) in zip(copies, tiled, acts):
-                mxs.mx_verify_gemm_act_tiled(tc, s, n, ac, asc, fmt, y=y)
+            for (tc, ts), (ac, asc) in zip(tiled, acts):
+                mxs.mx_verify_gemm_act_tiled(tc, ts, n, k, ac, asc, fmt, y=y)
         us_g = _graph_ms(torch, body_g, reps) * 1e3 / len(copies)
         us_t = _graph_ms(torch, body_t, reps) * 1e3 / len(copies)
         us_q = _graph_ms(torch, body_q, reps * 4) * 1e3 / len(copies)
@@ -381,8 +381,9 @@ def batched(torch, mxs, gen, reps=5):
                      "row_layout_us": round(us_g, 1),
                      "kernel": "gemm_act_kernel (v_mfma_scale_f32_16x16x128_f8f6f4, "
                                f"MX-FP4 x {'MX-FP8' if fmt == mxs.ACT_FP8 else 'MX-FP4'}; "
-                               f"dense peak {peak / 1e15:.1f} PFLOP/s); weight codes tiled by "
-                               "mxfp4_tile_codes (row_layout_us: the same product on the row layout)"}
+                               f"dense peak {peak / 1e15:.1f} PFLOP/s); weight codes and scales tiled by "
+                               "mxfp4_tile_codes / mxfp4_tile_scales (row_layout_us: the same product on "
+                               "the row layout)"}
         del acts, tiled
     del copies
     b = 64

@@ -260,13 +260,28 @@ size_t mxfp4_tiled_bytes(int64_t n, int64_t k); /* 0 when the sizes are out of r
 mxs_status mxfp4_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t* tiled, void* stream);
 
 /*
- * mx_verify_gemm_act_tiled — mx_verify_gemm_act with the weight codes in the tiled
- * layout of mxfp4_tile_codes (scales in the row layout [n, k/32]). Every wave-wide
- * weight load then reads 1 KiB contiguously instead of 64 bytes from each of 16 rows.
- * The result is bit-identical to mx_verify_gemm_act on the same weights. Same
- * arguments, rules and errors.
+ * mxfp4_tile_scales — E8M0 scales in the row layout [n, k/32] -> the tiled scale layout
+ * read by mx_verify_gemm_act_tiled: 2 KiB per (128-row tile t, 512-k window w) at byte
+ * (t * ceil(k/512) + w) * 2048. Its 16-byte unit r holds the scale bytes of columns
+ * 512 w .. 512 w + 511 (bytes 16 w .. 16 w + 15 of the row) of row 128 t + r. Bytes
+ * past k/32 and rows past n are zero.
+ *
+ * scales  [n, k/32], 4-byte aligned; k % 128 == 0, k >= 128.
+ * tiled   mxfp4_tiled_scale_bytes(n, k) bytes, 16-byte aligned.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
  */
-mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* scales, int64_t n, int64_t k,
+size_t mxfp4_tiled_scale_bytes(int64_t n, int64_t k); /* 0 when the sizes are out of range */
+mxs_status mxfp4_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8_t* tiled, void* stream);
+
+/*
+ * mx_verify_gemm_act_tiled — mx_verify_gemm_act with the weight codes in the tiled
+ * layout of mxfp4_tile_codes and the weight scales in that of mxfp4_tile_scales. Every
+ * wave-wide weight load then reads 1 KiB contiguously instead of 64 bytes from each of
+ * 16 rows, and a window's weight scales arrive in two 1 KiB loads. The result is
+ * bit-identical to mx_verify_gemm_act on the same weights. Same arguments, rules and
+ * errors; tiled_scales must be 16-byte aligned.
+ */
+mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
                                     const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt, int64_t m,
                                     float* y, void* stream);
 

@@ -33,7 +33,8 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept",
            "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
-           "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mx_verify_gemm_act_tiled"]
+           "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
+           "mx_verify_gemm_act_tiled"]
 
 
 class GemmProblem(ctypes.Structure):
@@ -95,6 +96,10 @@ def _load() -> ctypes.CDLL:
     lib.mxfp4_tiled_bytes.restype = ctypes.c_size_t
     lib.mxfp4_tile_codes.argtypes = [vp, i64, i64, vp, vp]
     lib.mxfp4_tile_codes.restype = ctypes.c_int
+    lib.mxfp4_tiled_scale_bytes.argtypes = [i64, i64]
+    lib.mxfp4_tiled_scale_bytes.restype = ctypes.c_size_t
+    lib.mxfp4_tile_scales.argtypes = [vp, i64, i64, vp, vp]
+    lib.mxfp4_tile_scales.restype = ctypes.c_int
     lib.mx_verify_gemm_act_tiled.argtypes = [vp, vp, i64, i64, vp, vp, i32, i64, vp, vp]
     lib.mx_verify_gemm_act_tiled.restype = ctypes.c_int
     return lib
@@ -430,22 +435,42 @@ def mxfp4_tile_codes(codes: torch.Tensor, tiled: torch.Tensor | None = None, str
     return tiled
 
 
-def mx_verify_gemm_act_tiled(tiled_codes: torch.Tensor, scales: torch.Tensor, n: int, act_codes: torch.Tensor,
-                             act_scales: torch.Tensor, fmt: int, y: torch.Tensor | None = None, stream=None):
-    """mx_verify_gemm_act with the weight codes tiled by mxfp4_tile_codes; scales [n, k/32] as quantized."""
-    for t, nm in ((tiled_codes, "tiled_codes"), (scales, "scales"), (act_codes, "act_codes"),
+def mxfp4_tiled_scale_bytes(n: int, k: int) -> int:
+    return int(get_lib().mxfp4_tiled_scale_bytes(n, k))
+
+
+def mxfp4_tile_scales(scales: torch.Tensor, tiled: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row-layout E8M0 scales [n, k/32] -> the tiled scale layout (uint8, mxfp4_tiled_scale_bytes(n, k) bytes)."""
+    _want(scales, torch.uint8, "scales")
+    n, k = scales.shape[0], scales.shape[1] * 32
+    nb = mxfp4_tiled_scale_bytes(n, k)
+    if nb == 0:
+        raise ValueError("k must be a multiple of 128")
+    if tiled is None:
+        tiled = torch.empty((nb,), dtype=torch.uint8, device=scales.device)
+    _want(tiled, torch.uint8, "tiled")
+    if tiled.numel() < nb:
+        raise ValueError(f"tiled needs {nb} bytes")
+    _check(get_lib().mxfp4_tile_scales(_ptr(scales), n, k, _ptr(tiled), _stream(stream)), "mxfp4_tile_scales")
+    return tiled
+
+
+def mx_verify_gemm_act_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tensor, n: int, k: int,
+                             act_codes: torch.Tensor, act_scales: torch.Tensor, fmt: int,
+                             y: torch.Tensor | None = None, stream=None):
+    """mx_verify_gemm_act on weights tiled by mxfp4_tile_codes / mxfp4_tile_scales (bit-identical result)."""
+    for t, nm in ((tiled_codes, "tiled_codes"), (tiled_scales, "tiled_scales"), (act_codes, "act_codes"),
                   (act_scales, "act_scales")):
         _want(t, torch.uint8, nm)
-    k = scales.shape[1] * 32
     m = act_codes.shape[0]
     want_cols = k if fmt == ACT_FP8 else k // 2
-    if scales.shape != (n, k // 32) or act_codes.shape != (m, want_cols) or act_scales.shape != (m, k // 32) \
-            or tiled_codes.numel() < mxfp4_tiled_bytes(n, k):
+    if act_codes.shape != (m, want_cols) or act_scales.shape != (m, k // 32) \
+            or tiled_codes.numel() < mxfp4_tiled_bytes(n, k) or tiled_scales.numel() < mxfp4_tiled_scale_bytes(n, k):
         raise ValueError("shape mismatch")
     if y is None:
-        y = torch.empty((m, n), dtype=torch.float32, device=scales.device)
+        y = torch.empty((m, n), dtype=torch.float32, device=act_codes.device)
     _want(y, torch.float32, "y")
-    _check(get_lib().mx_verify_gemm_act_tiled(_ptr(tiled_codes), _ptr(scales), n, k, _ptr(act_codes),
+    _check(get_lib().mx_verify_gemm_act_tiled(_ptr(tiled_codes), _ptr(tiled_scales), n, k, _ptr(act_codes),
                                               _ptr(act_scales), fmt, m, _ptr(y), _stream(stream)),
            "mx_verify_gemm_act_tiled")
     return y

@@ -211,15 +211,30 @@ mxs_status mxfp4_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t*
   return launched(mxs::launch_tile_codes(codes, n, k, tiled, static_cast<hipStream_t>(stream)));
 }
 
-mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* scales, int64_t n, int64_t k,
+size_t mxfp4_tiled_scale_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < 128 || k % 128 != 0 || n > (int64_t(1) << 40) / k) return 0;
+  return (size_t)((n + 127) / 128) * (size_t)((k + 511) / 512) * 2048u;
+}
+
+mxs_status mxfp4_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8_t* tiled, void* stream) {
+  if (!scales || !tiled) return MXS_ERR_NULL;
+  if (n < 1 || k < 128 || k % 128 != 0 || n > (int64_t(1) << 40) / k) return MXS_ERR_SHAPE;
+  if (!aligned(scales, 4) || !aligned(tiled, 16)) return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_tile_scales(scales, n, k, tiled, static_cast<hipStream_t>(stream)));
+}
+
+mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
                                     const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt, int64_t m,
                                     float* y, void* stream) {
+  const uint8_t* scales = tiled_scales;
   if (!tiled_codes || !scales || !act_codes || !act_scales || !y) return MXS_ERR_NULL;
   if (fmt != MXS_ACT_FP8 && fmt != MXS_ACT_FP4) return MXS_ERR_VALUE;
   if (n < 1 || n > (int64_t(1) << 31) - 16 || k < 128 || k % 128 != 0 || k > (int64_t(1) << 24) || m < 1 ||
       m > 65536)
     return MXS_ERR_SHAPE;
-  if (!aligned(tiled_codes, 16) || !aligned(act_codes, 16) || !aligned(scales, 4) || !aligned(act_scales, 4) ||
+  if (!aligned(tiled_codes, 16) || !aligned(act_codes, 16) || !aligned(scales, 16) || !aligned(act_scales, 4) ||
       !aligned(y, 4))
     return MXS_ERR_ALIGN;
   const mxs_status d = check_device();

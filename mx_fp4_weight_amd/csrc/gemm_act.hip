@@ -33,7 +33,9 @@ constexpr int kRQ = 2;      // row groups per tile: 4·kRQ waves, 8/kRQ row tile
 
 // kTiled: the weight codes come in the tiled layout of mxfp4_tile_codes (one 1 KiB tile
 // per 16 rows x 128-k group, the lanes of an operand load in order), so each wave-wide
-// operand load reads 1 KiB contiguously instead of 64 bytes from each of 16 rows.
+// operand load reads 1 KiB contiguously instead of 64 bytes from each of 16 rows; the
+// weight scales in the layout of mxfp4_tile_scales (2 KiB per 128 rows x 512-k window),
+// staged by two 1 KiB loads per window instead of eight loads of 16 rows x 16 bytes.
 template <int MC, int AF, int RQ, bool kTiled = false>
 __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -53,7 +55,6 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
   // as many address cycles as the codes (16 rows per instruction) for 1/16 the bytes.
   constexpr int kScaleLoads = (kRows + BM) / 16;   // 4-byte-per-lane loads: 16 rows each
   constexpr int kPerWave = (kLoads + kWaves - 1) / kWaves;
-  constexpr int kScalePerWave = (kScaleLoads + kWaves - 1) / kWaves;
   constexpr int kWsc = kUnits;              // first weight-scale unit
   constexpr int kXsc = kUnits + kRows;      // first activation-scale unit
   constexpr int kPadU = kUnits + kRows + BM;
@@ -93,7 +94,10 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
   // row0 at byte row0 * row_bytes
   const int crows = kTiled ? min(kRows, ((n + 15) & ~15) - row0) : rows;
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)row0 * row_bytes, (uint32_t)crows * row_bytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)row0 * kb, (uint32_t)rows * (uint32_t)kb);
+  // tiled scales: this tile's windows, 2 KiB each, at (nt * windows + window) * 2 KiB
+  const __amdgpu_buffer_rsrc_t sr =
+      kTiled ? make_rsrc(scales + (size_t)nt * (size_t)nsteps * 2048u, (uint32_t)nsteps * 2048u)
+             : make_rsrc(scales + (size_t)row0 * kb, (uint32_t)rows * (uint32_t)kb);
   const int t0 = mtile * BM;
   const int mrows = min(BM, m - t0);
   const __amdgpu_buffer_rsrc_t xr =
@@ -144,9 +148,22 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
           (__attribute__((address_space(3))) void*)(buf + (live ? kWave * L : kPadU));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
     }
+    if constexpr (kTiled) {
+      // weight scales: waves 0 and 1 each copy 1 KiB of the window's 2 KiB (rows 64w ..
+      // 64w + 63); the other waves issue the same load into the pad, reading nothing
+      const bool live = wave < 2;
+      const uint32_t off = live && s < nsteps ? (uint32_t)s * 2048u + (uint32_t)wave * 1024u + (uint32_t)lane * 16u
+                                              : kOutOfRange;
+      __attribute__((address_space(3))) void* dst =
+          (__attribute__((address_space(3))) void*)(buf + (live ? kWsc + 64 * wave : kPadU));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, dst, 16, off, 0, 0, 0);
+    }
+    // the remaining 4-byte-per-lane scale loads: weight rows (row layout only), then positions
+    constexpr int kJ0 = kTiled ? kRows / 16 : 0;
+    constexpr int kJPerWave = (kScaleLoads - kJ0 + kWaves - 1) / kWaves;
 #pragma unroll
-    for (int i = 0; i < kScalePerWave; ++i) {
-      const int J = wave + kWaves * i;  // wave-uniform
+    for (int i = 0; i < kJPerWave; ++i) {
+      const int J = kJ0 + wave + kWaves * i;  // wave-uniform
       const bool wsc = J < kRows / 16;
       const bool live = J < kScaleLoads;
       const int row = (wsc ? J : J - kRows / 16) * 16 + lane / 4;
@@ -320,6 +337,31 @@ __global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t* __restri
   *reinterpret_cast<u32x4*>(tiled + u * 16) = v;
 }
 
+// Row-layout scales [n, k/32] -> tiled scales: unit (16 bytes) u of the output, with
+// u = (row tile * windows + window) * 128 + r, holds scale bytes 16 * window .. + 15 of
+// row 128 * tile + r (zero past k/32 and past n). One thread per unit; k/32 is a multiple
+// of 4, so the row is read in 4-byte words.
+__global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restrict__ scales, int64_t n, int64_t k,
+                                                          uint8_t* __restrict__ tiled, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int64_t kb = k >> 5;
+  const int64_t windows = (k + 511) >> 9;
+  const int r = (int)(u & 127);
+  const int64_t tw = u >> 7;
+  const int64_t tile = tw / windows;
+  const int64_t w = tw - tile * windows;
+  const int64_t row = tile * 128 + r;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (row < n) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(scales + row * kb + w * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (w * 16 + 4 * j < kb) v[j] = src[j];
+  }
+  *reinterpret_cast<u32x4*>(tiled + u * 16) = v;
+}
+
 }  // namespace
 
 hipError_t launch_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
@@ -331,6 +373,12 @@ hipError_t launch_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, i
   }
   if (fmt == MXS_ACT_FP8) return launch<MXS_ACT_FP8, false>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
   return launch<MXS_ACT_FP4, false>(codes, scales, n, k, act_codes, act_scales, m, y, stream);
+}
+
+hipError_t launch_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8_t* tiled, hipStream_t stream) {
+  const int64_t units = (n + 127) / 128 * ((k + 511) >> 9) * 128;
+  tile_scales_kernel<<<dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream>>>(scales, n, k, tiled, units);
+  return hipGetLastError();
 }
 
 hipError_t launch_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t* tiled, hipStream_t stream) {

@@ -49,13 +49,18 @@ hipError_t launch_nvfp4_verify_gemm_grouped(const mxs_problem_view* pv, int coun
 hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,
                                uint8_t* scales, int32_t* flags, hipStream_t stream);
 
-// tiled: codes in the layout of launch_tile_codes (16-row x 128-k tiles of 1 KiB).
+// tiled: codes in the layout of launch_tile_codes (16-row x 128-k tiles of 1 KiB) and
+// scales in the layout of launch_tile_scales.
 hipError_t launch_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                                   const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt,
                                   int64_t m, float* y, bool tiled, hipStream_t stream);
 
 // Row-layout MX-FP4 codes [n, k/2] -> the tiled layout (k % 128 == 0; ceil(n/16)*16*k/2 bytes).
 hipError_t launch_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t* tiled, hipStream_t stream);
+
+// Row-layout scales [n, k/32] -> 2 KiB per (128 rows, 512-k window) (k % 128 == 0;
+// ceil(n/128) * ceil(k/512) * 2048 bytes).
+hipError_t launch_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8_t* tiled, hipStream_t stream);
 
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
 

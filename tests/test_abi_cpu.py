@@ -288,8 +288,16 @@ def test_tiled_host_errors():
     assert lib.mxfp4_tile_codes(a, 0, 256, b, None) == mxs.MXS_ERR_SHAPE
     assert lib.mxfp4_tile_codes(P(0x100008), 16, 256, b, None) == mxs.MXS_ERR_ALIGN
     assert lib.mxfp4_tile_codes(a, 16, 256, b, None) == mxs.MXS_ERR_DEVICE
-    call = lambda tc=0x100000, fmt=0, n=64, k=256, m=5: lib.mx_verify_gemm_act_tiled(
-        P(tc) if tc else None, P(0x300000), n, k, P(0x400000), P(0x500000), fmt, m, P(0x600000), None)
+    assert lib.mxfp4_tiled_scale_bytes(129, 640) == 2 * 2 * 2048
+    assert lib.mxfp4_tiled_scale_bytes(128, 192) == 0
+    assert lib.mxfp4_tile_scales(None, 16, 256, b, None) == mxs.MXS_ERR_NULL
+    assert lib.mxfp4_tile_scales(a, 16, 192, b, None) == mxs.MXS_ERR_SHAPE
+    assert lib.mxfp4_tile_scales(P(0x100002), 16, 256, b, None) == mxs.MXS_ERR_ALIGN
+    assert lib.mxfp4_tile_scales(a, 16, 256, P(0x200004), None) == mxs.MXS_ERR_ALIGN
+    assert lib.mxfp4_tile_scales(a, 16, 256, b, None) == mxs.MXS_ERR_DEVICE
+    call = lambda tc=0x100000, ts=0x300000, fmt=0, n=64, k=256, m=5: lib.mx_verify_gemm_act_tiled(
+        P(tc) if tc else None, P(ts), n, k, P(0x400000), P(0x500000), fmt, m, P(0x600000), None)
+    assert call(ts=0x300004) == mxs.MXS_ERR_ALIGN
     assert call(tc=0) == mxs.MXS_ERR_NULL
     assert call(fmt=3) == mxs.MXS_ERR_VALUE
     assert call(k=192) == mxs.MXS_ERR_SHAPE and call(m=0) == mxs.MXS_ERR_SHAPE and call(n=0) == mxs.MXS_ERR_SHAPE

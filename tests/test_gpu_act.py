@@ -236,8 +236,28 @@ def test_gemm_tiled_matches_row_layout(fmt, n, k, m):
     dwc, dws, dac, das = dev(wc), dev(ws), dev(ac), dev(asc)
     y_row = host(mxs.mx_verify_gemm_act(dwc, dws, dac, das, fmt))
     tiled = mxs.mxfp4_tile_codes(dwc)
-    y_tiled = host(mxs.mx_verify_gemm_act_tiled(tiled, dws, n, dac, das, fmt))
+    tiled_s = mxs.mxfp4_tile_scales(dws)
+    y_tiled = host(mxs.mx_verify_gemm_act_tiled(tiled, tiled_s, n, k, dac, das, fmt))
     torch.cuda.synchronize()
     assert np.array_equal(y_tiled, y_row), (n, k, m)
     if idx % 3 == 0:
         check_gemm(wc, ws, n, k, ac, asc, fmt, y_tiled, label=f"tiled {n}x{k}x{m}")
+
+
+def tile_scales_ref(scales, n, k):
+    """The tiled scale layout written out with NumPy: (128-row tile, 512-k window, row r, 16 bytes)."""
+    n128, kb, win = (n + 127) // 128 * 128, k // 32, (k + 511) // 512
+    full = np.zeros((n128, win * 16), np.uint8)
+    full[:n, :kb] = scales
+    return full.reshape(n128 // 128, 128, win, 16).transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (128, 512), (129, 384), (300, 1664), (1000, 2304), (257, 4096)])
+def test_tile_scales_layout(n, k):
+    """mxfp4_tile_scales is the documented byte layout (random bytes, ragged n and k)."""
+    say(f"tile scales n={n} k={k}")
+    scales = synth.rng(79, n, k).integers(0, 256, (n, k // 32), dtype=np.uint8)
+    got = host(mxs.mxfp4_tile_scales(dev(scales)))
+    torch.cuda.synchronize()
+    assert got.size == mxs.mxfp4_tiled_scale_bytes(n, k)
+    assert np.array_equal(got, tile_scales_ref(scales, n, k))
