@@ -770,8 +770,10 @@ __global__ __launch_bounds__(kThreads) void sel_pass_kernel(
 // ---------------------------------------------------------------- decide + piece totals
 // kPrefetch: small calls fetch every candidate final row with the statistics (one
 // workgroup per CU holds the extra registers); large calls load only the rows the
-// draw needs and fit two workgroups per CU.
-template <bool kPrefetch, bool kT>
+// draw needs and fit two workgroups per CU. Large calls also give a workgroup kPer
+// consecutive pieces (one decision, then the pieces' row loads together), so the
+// statistics combine is not repeated per piece and the grid is about one resident round.
+template <bool kPrefetch, bool kT, int kPer = kPrefetch ? 1 : 4>
 __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
     const float* __restrict__ target, const float* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int kd, int v,
@@ -795,7 +797,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   // further memory trip. That reads all 2K+1 rows again, so large batches (where
   // bandwidth, not latency, bounds the call) load only the rows step 3 needs.
   constexpr int kPre = kPrefetch ? 9 : 1;
-  const int t0w = c * kPiece + threadIdx.x * kWPer;
+  const int t0w = c * kPer * kPiece + threadIdx.x * kWPer;  // (prefetch: kPer = 1)
   const bool pre = kPrefetch && vec4 && kd <= 4 && t0w + kWPer <= v;
   f32x4 prow[kPre];
 #pragma unroll
@@ -952,6 +954,11 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   // 3. piece total of the final weights: thread totals in token order, then
   // the same block scan the sample kernel uses, so both see identical totals
   const int n = s_n;
+#pragma unroll
+  for (int pc = 0; pc < kPer; ++pc) {
+  const int cp = c * kPer + pc;  // this piece (uniform: the loop holds block scans)
+  if (cp >= pieces) break;
+  const int t0p = cp * kPiece + threadIdx.x * kWPer;
   double a = 0.0, b = 0.0;
   FinalRows fr;
   fr.tab = tab;
@@ -988,7 +995,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
       }
       weights_from<kT>(fr, zt, zd, wf, wp);
     } else {
-      thread_weights<kT>(fr, t0w, v, vec4, wf, wp);
+      thread_weights<kT>(fr, t0p, v, vec4, wf, wp);
     }
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) {
@@ -999,8 +1006,9 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   a = block_inclusive_scan_f64<kWThreads>(a, lds_d);
   b = block_inclusive_scan_f64<kWThreads>(b, lds_d);
   if (threadIdx.x == kWThreads - 1) {
-    ws.zres[s * pieces + c] = a;
-    ws.zp[s * pieces + c] = b;
+    ws.zres[s * pieces + cp] = a;
+    ws.zp[s * pieces + cp] = b;
+  }
   }
 }
 
@@ -1117,7 +1125,8 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // prefetch of all candidate rows while the batch's logits are at most 16 MB
   const bool prefetch = (int64_t)b * (2 * kd + 1) * v * 4 <= (int64_t(16) << 20);
-  const dim3 g2((unsigned)pieces, (unsigned)b);
+  const int per = prefetch ? 1 : 4;  // pieces per workgroup (decide_kernel's kPer)
+  const dim3 g2((unsigned)((pieces + per - 1) / per), (unsigned)b);
 #define MXS_DECIDE(P, T)                                                                          \
   decide_kernel<P, T><<<g2, dim3(kWThreads), 0, stream>>>(target, draft, tokens, uniforms, kd, v, \
                                                           chunks, pieces, ws, out_tokens, out_num, \
