@@ -956,59 +956,59 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   const int n = s_n;
 #pragma unroll
   for (int pc = 0; pc < kPer; ++pc) {
-  const int cp = c * kPer + pc;  // this piece (uniform: the loop holds block scans)
-  if (cp >= pieces) break;
-  const int t0p = cp * kPiece + threadIdx.x * kWPer;
-  double a = 0.0, b = 0.0;
-  FinalRows fr;
-  fr.tab = tab;
-  if (n >= 0) {
-    fr.zt = row_ptr(target, draft, s, kd, n, v);
-    fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
-    fr.mt = smax[n];
-    fr.inv_st = 1.0 / ssum[n];
-    fr.md = n < kd ? smax[kd + 1 + n] : 0.0;
-    fr.inv_sd = n < kd ? 1.0 / ssum[kd + 1 + n] : 0.0;
-    if constexpr (kT) {
-      fr.inv_tau = tr.inv_tau;
-      fr.thr_t = tr.thr ? tr.thr[(size_t)s * per_seq + n] : 0u;
-      fr.thr_d = (tr.thr && n < kd) ? tr.thr[(size_t)s * per_seq + kd + 1 + n] : 0u;
-      fr.mw = mask_words(tr, s, kd, n);
-    }
-    double wf[kWPer], wp[kWPer];
-    if (pre) {
-      float zt[kWPer], zd[kWPer];
-      f32x4 at = prow[0], ad = prow[0];
-#pragma unroll
-      for (int r = 0; r < kPre; ++r) {  // select without indexing registers dynamically
-        if (r == n) at = prow[r];
-        if (r == kd + 1 + n) ad = prow[r];
+    const int cp = c * kPer + pc;  // this piece (uniform: the loop holds block scans)
+    if (cp >= pieces) break;
+    const int t0p = cp * kPiece + threadIdx.x * kWPer;
+    double a = 0.0, b = 0.0;
+    FinalRows fr;
+    fr.tab = tab;
+    if (n >= 0) {
+      fr.zt = row_ptr(target, draft, s, kd, n, v);
+      fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
+      fr.mt = smax[n];
+      fr.inv_st = 1.0 / ssum[n];
+      fr.md = n < kd ? smax[kd + 1 + n] : 0.0;
+      fr.inv_sd = n < kd ? 1.0 / ssum[kd + 1 + n] : 0.0;
+      if constexpr (kT) {
+        fr.inv_tau = tr.inv_tau;
+        fr.thr_t = tr.thr ? tr.thr[(size_t)s * per_seq + n] : 0u;
+        fr.thr_d = (tr.thr && n < kd) ? tr.thr[(size_t)s * per_seq + kd + 1 + n] : 0u;
+        fr.mw = mask_words(tr, s, kd, n);
       }
-#pragma unroll
-      for (int j = 0; j < kWPer; ++j) {
-        zt[j] = at[j];
-        zd[j] = ad[j];
-        if constexpr (kT) {
-          zt[j] = live_logit(zt[j], t0w + j, fr.mw, fr.thr_t);
-          zd[j] = live_logit(zd[j], t0w + j, fr.mw, fr.thr_d);
+      double wf[kWPer], wp[kWPer];
+      if (pre) {
+        float zt[kWPer], zd[kWPer];
+        f32x4 at = prow[0], ad = prow[0];
+  #pragma unroll
+        for (int r = 0; r < kPre; ++r) {  // select without indexing registers dynamically
+          if (r == n) at = prow[r];
+          if (r == kd + 1 + n) ad = prow[r];
         }
+  #pragma unroll
+        for (int j = 0; j < kWPer; ++j) {
+          zt[j] = at[j];
+          zd[j] = ad[j];
+          if constexpr (kT) {
+            zt[j] = live_logit(zt[j], t0w + j, fr.mw, fr.thr_t);
+            zd[j] = live_logit(zd[j], t0w + j, fr.mw, fr.thr_d);
+          }
+        }
+        weights_from<kT>(fr, zt, zd, wf, wp);
+      } else {
+        thread_weights<kT>(fr, t0p, v, vec4, wf, wp);
       }
-      weights_from<kT>(fr, zt, zd, wf, wp);
-    } else {
-      thread_weights<kT>(fr, t0p, v, vec4, wf, wp);
+  #pragma unroll
+      for (int j = 0; j < kWPer; ++j) {
+        a += wf[j];
+        b += wp[j];
+      }
     }
-#pragma unroll
-    for (int j = 0; j < kWPer; ++j) {
-      a += wf[j];
-      b += wp[j];
+    a = block_inclusive_scan_f64<kWThreads>(a, lds_d);
+    b = block_inclusive_scan_f64<kWThreads>(b, lds_d);
+    if (threadIdx.x == kWThreads - 1) {
+      ws.zres[s * pieces + cp] = a;
+      ws.zp[s * pieces + cp] = b;
     }
-  }
-  a = block_inclusive_scan_f64<kWThreads>(a, lds_d);
-  b = block_inclusive_scan_f64<kWThreads>(b, lds_d);
-  if (threadIdx.x == kWThreads - 1) {
-    ws.zres[s * pieces + cp] = a;
-    ws.zp[s * pieces + cp] = b;
-  }
   }
 }
 

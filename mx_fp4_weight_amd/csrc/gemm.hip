@@ -140,8 +140,8 @@ struct Group {
 
 // nred: partial-tile buffers for the cross-wave sum: 2 alternate between row blocks,
 // 1 when that is what lets the targeted number of workgroups share a CU's LDS.
-// kPair (several phases only): a workgroup owns the row blocks wg and wg + gridDim
-// and walks them phase by phase (phase 0 of both, then phase 1 of both, ...), with a
+// kPair (several phases only): a workgroup owns the row blocks wg and wg + ngrid (ngrid:
+// the product's workgroups) and walks them phase by phase (phase 0 of both, then phase 1 of both, ...), with a
 // second set of accumulators, so a phase's activations are staged once for two row
 // blocks and every workgroup is resident at once.
 template <int R, int G, int D, bool kNv, bool kPair = false>
