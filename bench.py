@@ -343,16 +343,27 @@ def batched(torch, mxs, gen, reps=5):
     copies = [(*_gpu_mx(torch, mxs, gen, n, k), _rand_bf16(torch, gen, m, k)) for _ in range(3)]
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
 
-    def body():
+    # weight codes and scales in the tiled layouts (a one-off permutation at weight-prep time)
+    tiled = [(mxs.mxfp4_tile_codes(c), mxs.mxfp4_tile_scales(s)) for (c, s, _) in copies]
+
+    def body_row():
         for (c, s, x) in copies:
             mxs.mxfp4_verify_gemm(c, s, x, y=y)
+
+    def body():
+        for (tc, ts), (_, _, x) in zip(tiled, copies):
+            mxs.mxfp4_verify_gemm_tiled(tc, ts, n, k, x, y=y)
+    us_row = _graph_ms(torch, body_row, reps) * 1e3 / len(copies)
     us = _graph_ms(torch, body, reps) * 1e3 / len(copies)
     flops = 2.0 * m * n * k
     byts = gemm_alg_bytes(n, k, m)
     out = {"gemm": {"us": round(us, 1), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
                     "mfma_util_vs_bf16_dense_peak": round(flops / (us * 1e-6) / 2.5e15, 4),
                     "GBps": round(byts / (us * 1e-6) / 1e9, 1),
-                    "kernel": "gemm_dense_kernel (v_mfma_f32_16x16x32_bf16; peak 2.5 PFLOP/s dense bf16)"}}
+                    "row_layout_us": round(us_row, 1),
+                    "kernel": "gemm_dense_kernel (v_mfma_f32_16x16x32_bf16; peak 2.5 PFLOP/s dense bf16); weight "
+                              "codes and scales tiled by mxfp4_tile_codes / mxfp4_tile_scales (row_layout_us: "
+                              "mxfp4_verify_gemm on the row layout)"}}
     # the same product with MX-quantized activations (W4A8 / W4A4) on the block-scaled MFMA
     for fmt, name, peak in ((mxs.ACT_FP8, "gemm_w4a8", 5.0e15), (mxs.ACT_FP4, "gemm_w4a4", 10.1e15)):
         acts = [mxs.mx_quantize_act(x, fmt) for (_, _, x) in copies]
@@ -364,9 +375,6 @@ def batched(torch, mxs, gen, reps=5):
         def body_g(fmt=fmt, acts=acts):
             for (c, s, _), (ac, asc) in zip(copies, acts):
                 mxs.mx_verify_gemm_act(c, s, ac, asc, fmt, y=y)
-        # weight codes in the tiled layout (a one-off permutation at weight-prep time)
-        tiled = [(mxs.mxfp4_tile_codes(c), mxs.mxfp4_tile_scales(s)) for (c, s, _) in copies]
-
         def body_t(fmt=fmt, acts=acts, tiled=tiled):
             for (tc, ts), (ac, asc) in zip(tiled, acts):
                 mxs.mx_verify_gemm_act_tiled(tc, ts, n, k, ac, asc, fmt, y=y)
@@ -384,8 +392,8 @@ def batched(torch, mxs, gen, reps=5):
                                f"dense peak {peak / 1e15:.1f} PFLOP/s); weight codes and scales tiled by "
                                "mxfp4_tile_codes / mxfp4_tile_scales (row_layout_us: the same product on "
                                "the row layout)"}
-        del acts, tiled
-    del copies
+        del acts
+    del copies, tiled
     b = 64
     base = torch.randn((b, KD + 1, V), generator=gen, device="cuda", dtype=torch.float32) * 3.0
     tgt = base + torch.randn((b, KD + 1, V), generator=gen, device="cuda", dtype=torch.float32)

@@ -242,9 +242,10 @@ mxs_status mx_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64
 
 /*
  * mxfp4_tile_codes — MX-FP4 codes in the mxfp4_quantize row layout [n, k/2] -> the
- * tiled layout read by mx_verify_gemm_act_tiled. This is a byte permutation done once
- * at weight-prep time, like the quantization itself [M11 §12 fixes the values; the
- * byte order in memory is this library's choice]. The scales are not tiled.
+ * tiled layout read by mx_verify_gemm_act_tiled and mxfp4_verify_gemm_tiled. This is a
+ * byte permutation done once at weight-prep time, like the quantization itself [M11 §12
+ * fixes the values; the byte order in memory is this library's choice]. The scales have
+ * a tiled layout of their own (mxfp4_tile_scales).
  *
  * Tiled layout: one 1 KiB tile per (16-row tile t, 128-k group q), at byte
  * (t * (k/128) + q) * 1024. Its 16-byte unit L = 16 * g + r (g = 0..3, r = 0..15)
@@ -261,7 +262,7 @@ mxs_status mxfp4_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t*
 
 /*
  * mxfp4_tile_scales — E8M0 scales in the row layout [n, k/32] -> the tiled scale layout
- * read by mx_verify_gemm_act_tiled: 2 KiB per (128-row tile t, 512-k window w) at byte
+ * read by mx_verify_gemm_act_tiled and mxfp4_verify_gemm_tiled: 2 KiB per (128-row tile t, 512-k window w) at byte
  * (t * ceil(k/512) + w) * 2048. Its 16-byte unit r holds the scale bytes of columns
  * 512 w .. 512 w + 511 (bytes 16 w .. 16 w + 15 of the row) of row 128 t + r. Bytes
  * past k/32 and rows past n are zero.
@@ -284,6 +285,27 @@ mxs_status mxfp4_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8_
 mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
                                     const uint8_t* act_codes, const uint8_t* act_scales, int32_t fmt, int64_t m,
                                     float* y, void* stream);
+
+/*
+ * mxfp4_verify_gemm_tiled — mxfp4_verify_gemm for batched verification (many
+ * sequences: m = B·T well above 32) with the weight codes in the tiled layout of
+ * mxfp4_tile_codes and the weight scales in that of mxfp4_tile_scales [M11 §4, §10;
+ * the byte order is this library's choice]. It always runs the dense kernel that
+ * mxfp4_verify_gemm runs for m > 32 with k % 128 == 0, and its result is bit-identical
+ * to mxfp4_verify_gemm's there; for m <= 32 the result is the same product (same
+ * numerics) but the row-layout call, which then runs the skinny kernel, is faster.
+ *
+ * tiled_codes   mxfp4_tiled_bytes(n, k) bytes, 16-byte aligned.
+ * tiled_scales  mxfp4_tiled_scale_bytes(n, k) bytes, 16-byte aligned.
+ * n, k          1 <= n <= 2^31 - 16; 128 <= k <= 2^23, k % 128 == 0.
+ * x             [m, k] bf16 bit patterns, 16-byte aligned.
+ * m             1 <= m <= 65536, and ceil(n/1024) * 8 * ceil(m/80) <= 2^23 - 1 (the
+ *               launch grid: n up to about 1M rows at m = 65536).
+ * y             [m, n] fp32, 4-byte aligned. Fully overwritten.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status mxfp4_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
+                                   const uint16_t* x, int64_t m, float* y, void* stream);
 
 /*
  * spec_accept_workspace_bytes — device workspace spec_accept needs for

@@ -34,7 +34,7 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
-           "mx_verify_gemm_act_tiled"]
+           "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled"]
 
 
 class GemmProblem(ctypes.Structure):
@@ -102,6 +102,8 @@ def _load() -> ctypes.CDLL:
     lib.mxfp4_tile_scales.restype = ctypes.c_int
     lib.mx_verify_gemm_act_tiled.argtypes = [vp, vp, i64, i64, vp, vp, i32, i64, vp, vp]
     lib.mx_verify_gemm_act_tiled.restype = ctypes.c_int
+    lib.mxfp4_verify_gemm_tiled.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    lib.mxfp4_verify_gemm_tiled.restype = ctypes.c_int
     return lib
 
 
@@ -473,4 +475,25 @@ def mx_verify_gemm_act_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tens
     _check(get_lib().mx_verify_gemm_act_tiled(_ptr(tiled_codes), _ptr(tiled_scales), n, k, _ptr(act_codes),
                                               _ptr(act_scales), fmt, m, _ptr(y), _stream(stream)),
            "mx_verify_gemm_act_tiled")
+    return y
+
+
+def mxfp4_verify_gemm_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tensor, n: int, k: int,
+                            x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mxfp4_verify_gemm on weights tiled by mxfp4_tile_codes / mxfp4_tile_scales (the dense kernel at every m;
+    bit-identical to mxfp4_verify_gemm where that runs the dense kernel, m > 32)."""
+    _want(tiled_codes, torch.uint8, "tiled_codes")
+    _want(tiled_scales, torch.uint8, "tiled_scales")
+    _want(x, torch.bfloat16, "x")
+    m = x.shape[0]
+    if x.shape[1] != k or tiled_codes.numel() < mxfp4_tiled_bytes(n, k) \
+            or tiled_scales.numel() < mxfp4_tiled_scale_bytes(n, k):
+        raise ValueError("shape mismatch")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _want(y, torch.float32, "y")
+    if y.shape != (m, n):
+        raise ValueError("y must be [m, n]")
+    _check(get_lib().mxfp4_verify_gemm_tiled(_ptr(tiled_codes), _ptr(tiled_scales), n, k, _ptr(x), m, _ptr(y),
+                                             _stream(stream)), "mxfp4_verify_gemm_tiled")
     return y

@@ -243,6 +243,22 @@ mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* t
                                               static_cast<hipStream_t>(stream)));
 }
 
+mxs_status mxfp4_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
+                                   const uint16_t* x, int64_t m, float* y, void* stream) {
+  if (!tiled_codes || !tiled_scales || !x || !y) return MXS_ERR_NULL;
+  if (n < 1 || n > (int64_t(1) << 31) - 16 || k < 128 || k % 128 != 0 || k > (int64_t(1) << 23) || m < 1 ||
+      m > 65536)
+    return MXS_ERR_SHAPE;
+  // the grid: 8 x ceil(n / 1024) row tiles x ceil(m / 80) position tiles of 512 threads
+  if ((n + 1023) / 1024 * 8 * ((m + 79) / 80) > (int64_t)0xffffffffu / 512) return MXS_ERR_SHAPE;
+  if (!aligned(tiled_codes, 16) || !aligned(tiled_scales, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_verify_gemm_tiled(tiled_codes, tiled_scales, n, k, x, m, y,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
   if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
   return mxs::accept_workspace_bytes(b, kd, v, false);

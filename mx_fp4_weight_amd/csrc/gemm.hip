@@ -440,10 +440,13 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
 // each B operand read feeds 4 MFMAs. The k quarters are summed in LDS at the end
 // in a fixed order. Tiles are mapped to XCDs so that the position tiles of one
 // weight tile run on the same XCD and share its L2: the weights come from HBM once.
+// kTiled: codes in the 1 KiB (16 rows x 128 k) tile layout and scales in the 2 KiB
+// (128 rows x 512 k) window layout, so a wave's weight load reads 1 KiB contiguously
+// and its scale load of a row tile 256 bytes; the arithmetic is unchanged.
 constexpr int kDenseRows = 128;
 constexpr int kDenseThreads = 512;
 
-template <int MC>
+template <int MC, bool kTiled>
 __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m, int n_tiles,
@@ -483,8 +486,14 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   const uint32_t row_bytes = (uint32_t)(k >> 1);
   const int row0 = nt * kDenseRows;
   const int rows = min(kDenseRows, n - row0);
-  const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)row0 * row_bytes, (uint32_t)rows * row_bytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)row0 * kb, (uint32_t)rows * (uint32_t)kb);
+  // tiled: rows are zero-padded to a multiple of 16, and the tile's scales are its
+  // ceil(k/512) windows of 2 KiB
+  const int nwin = (ngroups + 3) >> 2;
+  const __amdgpu_buffer_rsrc_t cr =
+      make_rsrc(codes + (size_t)row0 * row_bytes, (uint32_t)(kTiled ? (rows + 15) & ~15 : rows) * row_bytes);
+  const __amdgpu_buffer_rsrc_t sr =
+      kTiled ? make_rsrc(scales + (size_t)nt * (size_t)nwin * 2048u, (uint32_t)nwin * 2048u)
+             : make_rsrc(scales + (size_t)row0 * kb, (uint32_t)rows * (uint32_t)kb);
   const int t0 = mtile * BM;
   const int mrows = min(BM, m - t0);
   const __amdgpu_buffer_rsrc_t xr =
@@ -500,8 +509,11 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
     const bool ok = grp < ngroups;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t row = (uint32_t)(rh * 64 + 16 * i + r);
-      const uint32_t co = opaque(ok ? row * row_bytes + (uint32_t)blk * 16 : kOutOfRange);
+      // tiled: tile (row tile, grp) starts 16 rows' bytes per row tile in, lane L = 16g + r
+      const uint32_t rt = (uint32_t)(rh * 64 + 16 * i);
+      const uint32_t co = opaque(ok ? (kTiled ? rt * row_bytes + (uint32_t)grp * 1024u + (uint32_t)lane * 16u
+                                              : (rt + (uint32_t)r) * row_bytes + (uint32_t)blk * 16)
+                                    : kOutOfRange);
       w.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, co, 0, 0));
     }
   };
@@ -514,7 +526,10 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t row = (uint32_t)(rh * 64 + 16 * i + r);
-      const uint32_t so = opaque(ok ? row * (uint32_t)kb + (uint32_t)grp * 4 : kOutOfRange);
+      // tiled: the 4 groups from grp on are 512-k window grp / 4, whose unit for row is row
+      const uint32_t so =
+          opaque(ok ? (kTiled ? (uint32_t)(grp >> 2) * 2048u + row * 16u : row * (uint32_t)kb + (uint32_t)grp * 4)
+                    : kOutOfRange);
       sc[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, so, 0, 0));
     }
   };
@@ -951,16 +966,24 @@ inline bool dense_ok(int64_t k, int64_t m) {
   return m > kDenseMinM && k % 128 == 0 && k <= (int64_t(1) << 23);
 }
 
+// the dense grid's thread count must fit 32 bits (n beyond ~1M rows at m = 65536)
+inline bool dense_grid_ok(int64_t n, int64_t m) {
+  const int64_t wgs = (n + 8 * kDenseRows - 1) / (8 * kDenseRows) * 8 * ((m + 16 * kDenseMC - 1) / (16 * kDenseMC));
+  return wgs <= (int64_t)0xffffffffu / kDenseThreads;
+}
+
+template <bool kTiled>
 hipError_t launch_dense(const mxs_problem_view& p, int64_t k, int64_t m, hipStream_t stream) {
   constexpr int MC = kDenseMC;
   static std::atomic<bool> done[kMaxDevices];
-  hipError_t e = allow_lds(&gemm_dense_kernel<MC>, done);
+  hipError_t e = allow_lds(&gemm_dense_kernel<MC, kTiled>, done);
   if (e != hipSuccess) return e;
   const int n_tiles = (int)((p.n + kDenseRows - 1) / kDenseRows);
   const int m_tiles = (int)((m + 16 * MC - 1) / (16 * MC));
   const int64_t wgs = (int64_t)((n_tiles + 7) / 8) * 8 * m_tiles;
+  if (!dense_grid_ok(p.n, m)) return hipErrorInvalidConfiguration;
   const size_t lds = 2 * sizeof(u32x4) * (16 * MC * 64);
-  gemm_dense_kernel<MC><<<dim3((unsigned)wgs), dim3(kDenseThreads), lds, stream>>>(
+  gemm_dense_kernel<MC, kTiled><<<dim3((unsigned)wgs), dim3(kDenseThreads), lds, stream>>>(
       p.codes, p.scales, p.x, p.y, (int)p.n, (int)k, (int)m, n_tiles, m_tiles, y_vec4_ok(p.y, p.n));
   return hipGetLastError();
 }
@@ -969,9 +992,11 @@ hipError_t launch_dense(const mxs_problem_view& p, int64_t k, int64_t m, hipStre
 // one dense or fallback launch per problem.
 hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t k, int64_t m,
                         hipStream_t stream) {
-  if (dense_ok(k, m)) {
+  bool dense = dense_ok(k, m);
+  for (int i = 0; i < count; ++i) dense = dense && dense_grid_ok(pv[i].n, m);
+  if (dense) {
     for (int i = 0; i < count; ++i) {
-      const hipError_t e = launch_dense(pv[i], k, m, stream);
+      const hipError_t e = launch_dense<false>(pv[i], k, m, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1026,6 +1051,12 @@ Config choose(int64_t n, int64_t k) {
 hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
   return launch_cfg(choose(n, k), codes, scales, n, k, x, m, y, stream);
+}
+
+hipError_t launch_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
+                                    const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
+  const mxs_problem_view pv{tiled_codes, tiled_scales, x, y, n};
+  return launch_dense<true>(pv, k, m, stream);
 }
 
 // NVFP4 weights: the skinny kernel for every m (a 16-position tile per grid row), k % 512 == 0

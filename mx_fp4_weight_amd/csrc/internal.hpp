@@ -26,6 +26,11 @@ hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes,
 hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint16_t* x, int64_t m, float* y, hipStream_t stream);
 
+// The dense kernel over tiled codes (launch_tile_codes) and tiled scales (launch_tile_scales);
+// k % 128 == 0 and k <= 2^23, checked by the caller.
+hipError_t launch_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
+                                    const uint16_t* x, int64_t m, float* y, hipStream_t stream);
+
 // Sampling transforms of spec_accept_sampled (validated by the caller).
 struct SamplingParams {
   float temperature;      // > 0

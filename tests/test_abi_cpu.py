@@ -303,3 +303,20 @@ def test_tiled_host_errors():
     assert call(k=192) == mxs.MXS_ERR_SHAPE and call(m=0) == mxs.MXS_ERR_SHAPE and call(n=0) == mxs.MXS_ERR_SHAPE
     assert call(tc=0x100004) == mxs.MXS_ERR_ALIGN
     assert call() == mxs.MXS_ERR_DEVICE
+
+
+def test_verify_gemm_tiled_host_errors():
+    """mxfp4_verify_gemm_tiled refuses malformed calls before any HIP call."""
+    lib = mxs.get_lib()
+    call = lambda tc=0x100000, ts=0x300000, x=0x400000, n=64, k=256, m=40: lib.mxfp4_verify_gemm_tiled(
+        P(tc) if tc else None, P(ts) if ts else None, n, k, P(x), m, P(0x600000), None)
+    assert call(tc=0) == mxs.MXS_ERR_NULL and call(ts=0) == mxs.MXS_ERR_NULL
+    assert call(k=192) == mxs.MXS_ERR_SHAPE and call(k=64) == mxs.MXS_ERR_SHAPE
+    assert call(k=(1 << 23) + 128) == mxs.MXS_ERR_SHAPE
+    assert call(m=0) == mxs.MXS_ERR_SHAPE and call(m=65537) == mxs.MXS_ERR_SHAPE and call(n=0) == mxs.MXS_ERR_SHAPE
+    # launch grid beyond 32 bits of threads: 2^21 rows at m = 65536
+    assert call(n=1 << 21, m=65536) == mxs.MXS_ERR_SHAPE
+    assert call(tc=0x100004) == mxs.MXS_ERR_ALIGN and call(ts=0x300004) == mxs.MXS_ERR_ALIGN
+    assert call(x=0x400008) == mxs.MXS_ERR_ALIGN
+    assert call() == mxs.MXS_ERR_DEVICE
+    assert call(n=1 << 20, m=65536) == mxs.MXS_ERR_DEVICE

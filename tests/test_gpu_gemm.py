@@ -254,3 +254,48 @@ def test_grouped_matches_oracle(shapes, k, m):
     y1 = mxs.mxfp4_verify_gemm(*items[0])
     torch.cuda.synchronize()
     assert np.array_equal(host(y1), host(ys[0]))
+
+
+@pytest.mark.parametrize("n,k,m", [
+    # m > 32: the row-layout call runs the same dense kernel, so the sums are bit-identical
+    (1, 128, 33), (17, 384, 80), (130, 384, 81), (257, 1024, 100), (1000, 2304, 161), (300, 896, 320),
+    (129, 3200, 47), (1024, 1024, 240), (2049, 4096, 96),
+    # m <= 32: the dense kernel against the oracle only (the row layout runs the skinny kernel)
+    (5, 512, 1), (200, 640, 5), (1000, 1152, 32),
+])
+def test_tiled_dense_matches_row_layout(n, k, m):
+    """mxfp4_verify_gemm_tiled over mxfp4_tile_codes / mxfp4_tile_scales: bit-identical to
+    mxfp4_verify_gemm where both run the dense kernel, and the oracle bar on every shape."""
+    say(f"gemm: tiled dense n={n} k={k} m={m}")
+    idx = n + 3 * k + m
+    codes, scales, _ = omx.quantize(synth.weights(10, idx, n, k))
+    x = synth.activations(10, idx, m, k)
+    dc, ds, dx = dev(codes), dev(scales), dev_bf16(x)
+    tc, ts = mxs.mxfp4_tile_codes(dc), mxs.mxfp4_tile_scales(ds)
+    y_tiled = host(mxs.mxfp4_verify_gemm_tiled(tc, ts, n, k, dx))
+    torch.cuda.synchronize()
+    if m > 32:
+        y_row = host(mxs.mxfp4_verify_gemm(dc, ds, dx))
+        assert np.array_equal(y_tiled, y_row), (n, k, m)
+    check_gemm(codes, scales, n, k, x, y_tiled, label=f"tiled dense {n}x{k}x{m}")
+
+
+def test_tiled_batched_320_rows_sampled():
+    """The batched verification case (64 sequences x 5 positions, 8192x28672) through the tiled
+    weights: bit-identical to the row layout, and sampled rows against the oracle."""
+    say("gemm: tiled batched 320x8192x28672")
+    n, k, m = 8192, 28672, 320
+    w = synth.weights(11, 0, n, k)
+    dcodes, dscales = mxs.mxfp4_quantize(dev(w))
+    x = synth.activations(11, 0, m, k)
+    dx = dev_bf16(x)
+    y_row = mxs.mxfp4_verify_gemm(dcodes, dscales, dx)
+    y = mxs.mxfp4_verify_gemm_tiled(mxs.mxfp4_tile_codes(dcodes), mxs.mxfp4_tile_scales(dscales), n, k, dx)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_row)
+    rows = np.unique(np.concatenate([np.random.default_rng(11).choice(n, 126, replace=False), [0, n - 1]]))
+    rc, rs, _ = omx.quantize(w[rows])
+    sub_c = np.zeros((n, k // 2), np.uint8)
+    sub_s = np.zeros((n, k // 32), np.uint8)
+    sub_c[rows], sub_s[rows] = rc, rs
+    check_gemm(sub_c, sub_s, n, k, x, host(y)[:, rows], rows=rows, label="tiled batched")
