@@ -121,7 +121,8 @@ def summarize_pmc(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
                         "copy_kib": max(copy), "factor": factor,
                         "bytes_per_launch": sum(gemm) / len(gemm) * 1024 / factor}
     summary = {
-        "kernel": "gemm_skinny_kernel (mxfp4_verify_gemm), 8B-class layer shapes at T=5",
+        "kernel": "gemm_skinny_kernel on tiled weights (mxfp4_verify_gemm_tiled / _grouped_tiled), "
+                  "8B-class layer shapes at T=5",
         "gemm_source_sha": source_sha(GEMM_SRC),
         "traffic_bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"],
         "alg_bytes_per_launch": sum(gemm_alg_bytes(n, k, T) for _, n, k in LAYER) / len(LAUNCHES),
@@ -248,8 +249,22 @@ def _rand_bf16(torch, gen, m, k):
     return torch.randn((m, k), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
 
 
+def _tile(mxs, c, s, x):
+    """(codes, scales, x) -> (tiled codes, tiled scales, n, x): the one-off weight-prep permutation."""
+    return (mxs.mxfp4_tile_codes(c), mxs.mxfp4_tile_scales(s), c.shape[0], x)
+
+
+def _gemm(mxs, items, ys, stream=None):
+    """The verify GEMM of items [(tiled codes, tiled scales, n, x)] into ys: one product or a group."""
+    if len(items) == 1:
+        tc, ts, n, x = items[0]
+        mxs.mxfp4_verify_gemm_tiled(tc, ts, n, x.shape[1], x, y=ys[0], stream=stream)
+    else:
+        mxs.mxfp4_verify_gemm_grouped_tiled(items, ys=ys, stream=stream)
+
+
 def t_sweep(torch, mxs, pool, gen, reps=3):
-    """8B-class shapes at T = 1..8 over the cold pool: per launch type, µs and GB/s."""
+    """8B-class shapes at T = 1..8 over the cold pool (tiled weights): per launch type, µs and GB/s."""
     n_layers = len(pool)
     out = {}
     for t in range(1, 9):
@@ -259,11 +274,7 @@ def t_sweep(torch, mxs, pool, gen, reps=3):
         for name, idx in LAUNCHES:
             def body(idx=idx):
                 for li in range(n_layers):
-                    items = [(pool[li][i][0], pool[li][i][1], xs[li][i]) for i in idx]
-                    if len(items) == 1:
-                        mxs.mxfp4_verify_gemm(*items[0], y=ys[idx[0]])
-                    else:
-                        mxs.mxfp4_verify_gemm_grouped(items, ys=[ys[i] for i in idx])
+                    _gemm(mxs, [(*pool[li][i][:3], xs[li][i]) for i in idx], [ys[i] for i in idx])
             us = _graph_ms(torch, body, reps) * 1e3 / n_layers
             byts = sum(gemm_alg_bytes(LAYER[i][1], LAYER[i][2], t) for i in idx)
             row[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
@@ -283,7 +294,7 @@ MODEL70_BYTES = 80 * sum(mx_bytes(n, k) for _, n, k in L70) + mx_bytes(*LM70)
 
 
 def shapes_70b(torch, mxs, synth, gen, reps=3):
-    """70B-class shapes at T=5 with 1% outlier input channels x20: per launch µs and GB/s.
+    """70B-class shapes at T=5 with 1% outlier input channels x20, tiled weights: per launch µs and GB/s.
 
     Copies per shape are chosen so each timed graph streams > 256 MB (cold weights).
     """
@@ -299,6 +310,10 @@ def shapes_70b(torch, mxs, synth, gen, reps=3):
                      _rand_bf16(torch, gen, T, k)) for (_, n, k) in L70[4:]])
     for c in range(copies["lm"]):
         lm.append((*_gpu_mx(torch, mxs, gen, *LM70, outlier_cols=outl[8192]), _rand_bf16(torch, gen, T, LM70[1])))
+    # tiled weights (the row-layout copies are dropped)
+    attn = [[_tile(mxs, *t) for t in st] for st in attn]
+    mlp = [[_tile(mxs, *t) for t in st] for st in mlp]
+    lm = [_tile(mxs, *t) for t in lm]
     y_attn = [torch.empty((T, n), dtype=torch.float32, device="cuda") for (_, n, _) in L70[:4]]
     y_mlp = [torch.empty((T, n), dtype=torch.float32, device="cuda") for (_, n, _) in L70[4:]]
     y_lm = torch.empty((T, LM70[0]), dtype=torch.float32, device="cuda")
@@ -309,21 +324,16 @@ def shapes_70b(torch, mxs, synth, gen, reps=3):
     for name, sets, idx, ybuf in plans:
         if name == "lm_head":
             def body():
-                for (c, s, x) in lm:
-                    mxs.mxfp4_verify_gemm(c, s, x, y=y_lm)
+                for t in lm:
+                    _gemm(mxs, [t], [y_lm])
             us = _graph_ms(torch, body, reps) * 1e3 / len(lm)
             byts = gemm_alg_bytes(LM70[0], LM70[1], T)
         else:
             def body(sets=sets, idx=idx, ybuf=ybuf):
                 for st in sets:
-                    items = [st[i] for i in idx]
-                    outs = [ybuf[i] for i in idx]
-                    if len(items) == 1:
-                        mxs.mxfp4_verify_gemm(*items[0], y=outs[0])
-                    else:
-                        mxs.mxfp4_verify_gemm_grouped(items, ys=outs)
+                    _gemm(mxs, [st[i] for i in idx], [ybuf[i] for i in idx])
             us = _graph_ms(torch, body, reps) * 1e3 / len(sets)
-            byts = sum(gemm_alg_bytes(sets[0][i][0].shape[0], sets[0][i][0].shape[1] * 2, T) for i in idx)
+            byts = sum(gemm_alg_bytes(sets[0][i][2], sets[0][i][3].shape[1], T) for i in idx)
             layer_b += byts
             layer_us += us
         out[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
@@ -531,7 +541,7 @@ def _overlap(torch, p_logits, q_logits):
 
 
 def full_8b_step(torch, mxs, gen, steps=10, trials=4096):
-    """32 decoder layers + lm_head 128256x4096 at T=5, then spec_accept on the lm_head output.
+    """32 decoder layers + lm_head 128256x4096 at T=5 (tiled weights), then spec_accept on the lm_head output.
 
     Draft rows i < 4 are target row i + lam_i * N(0,1), with lam_i bisected (fp64, torch,
     outside the timed region) so the per-position acceptance alpha = sum_x min(p, q)
@@ -540,9 +550,9 @@ def full_8b_step(torch, mxs, gen, steps=10, trials=4096):
     """
     layers = []
     for li in range(32):
-        layers.append([(*_gpu_mx(torch, mxs, gen, n, k), _rand_bf16(torch, gen, T, k)) for (_, n, k) in LAYER])
-    lm_c, lm_s = _gpu_mx(torch, mxs, gen, V, 4096)
-    lm_x = _rand_bf16(torch, gen, T, 4096)
+        layers.append([_tile(mxs, *_gpu_mx(torch, mxs, gen, n, k), _rand_bf16(torch, gen, T, k))
+                       for (_, n, k) in LAYER])
+    lm = _tile(mxs, *_gpu_mx(torch, mxs, gen, V, 4096), _rand_bf16(torch, gen, T, 4096))
     ys = [torch.empty((T, n), dtype=torch.float32, device="cuda") for (_, n, _) in LAYER]
     y_lm = torch.empty((1, T, V), dtype=torch.float32, device="cuda")
     model_bytes = 32 * sum(mx_bytes(n, k) for _, n, k in LAYER) + mx_bytes(V, 4096)
@@ -551,11 +561,8 @@ def full_8b_step(torch, mxs, gen, steps=10, trials=4096):
     def gemms():
         for mats in layers:
             for _, idx in LAUNCHES:
-                if len(idx) == 1:
-                    mxs.mxfp4_verify_gemm(*mats[idx[0]], y=ys[idx[0]])
-                else:
-                    mxs.mxfp4_verify_gemm_grouped([mats[i] for i in idx], ys=[ys[i] for i in idx])
-        mxs.mxfp4_verify_gemm(lm_c, lm_s, lm_x, y=y_lm.view(T, V))
+                _gemm(mxs, [mats[i] for i in idx], [ys[i] for i in idx])
+        _gemm(mxs, [lm], [y_lm.view(T, V)])
     gemms()
     torch.cuda.synchronize()
     # The lm_head output [1, T, V] is the target law of spec_accept (its rows are the
@@ -634,6 +641,9 @@ def main():
                     help="run one workload alone (profiling); 'headline' = the default line without "
                          "the secondary workloads")
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--layout", choices=["tiled", "row"], default="tiled",
+                    help="weight byte order of the headline: tiled (mxfp4_tile_codes / mxfp4_tile_scales, "
+                         "done once at weight-prep time) or the mxfp4_quantize row layout")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -676,10 +686,30 @@ def main():
             mats.append((codes, scales, x))
         pool.append(mats)
     ys = [torch.empty((T, n), dtype=torch.float32, device=dev) for _, n, _ in LAYER]
+    # the same weights permuted once into the tiled layouts (for these shapes the same bytes)
+    tpool = [[(mxs.mxfp4_tile_codes(c), mxs.mxfp4_tile_scales(s), n, x)
+              for (c, s, x), (_, n, _) in zip(mats, LAYER)] for mats in pool]
+
+    def run_launch(li, idx, st, layout):
+        """One launch of layer li: the products idx (one, or several sharing the input)."""
+        if layout == "tiled":
+            tm = tpool[li]
+            if len(idx) == 1:
+                tc, ts, n, x = tm[idx[0]]
+                mxs.mxfp4_verify_gemm_tiled(tc, ts, n, x.shape[1], x, y=ys[idx[0]], stream=st)
+            else:
+                mxs.mxfp4_verify_gemm_grouped_tiled([tm[i] for i in idx], ys=[ys[i] for i in idx], stream=st)
+        else:
+            mats = pool[li]
+            if len(idx) == 1:
+                codes, scales, x = mats[idx[0]]
+                mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[idx[0]], stream=st)
+            else:
+                mxs.mxfp4_verify_gemm_grouped([mats[i] for i in idx], ys=[ys[i] for i in idx], stream=st)
 
     gen2 = torch.Generator(device=dev)
     gen2.manual_seed(args.seed * 7919 + 17)
-    extras = (("t_sweep_8b", lambda: t_sweep(torch, mxs, pool, gen2)),
+    extras = (("t_sweep_8b", lambda: t_sweep(torch, mxs, tpool, gen2)),
               ("shapes_70b_t5", lambda: shapes_70b(torch, mxs, synth, gen2)),
               ("batched_64x5", lambda: batched(torch, mxs, gen2)),
               ("sampled_accept", lambda: sampled_accept(torch, mxs, gen2)),
@@ -714,14 +744,8 @@ def main():
         cost more than the overlap gains on this stack).
         """
         st = torch.cuda.current_stream()
-        mats = pool[s % n_layers]
         for _, idx in LAUNCHES:
-            if len(idx) == 1:
-                codes, scales, x = mats[idx[0]]
-                mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[idx[0]], stream=st)
-            else:
-                mxs.mxfp4_verify_gemm_grouped([mats[i] for i in idx], ys=[ys[i] for i in idx],
-                                              stream=st)
+            run_launch(s % n_layers, idx, st, args.layout)
         mxs.spec_accept(d_tgt, d_dft, d_tok, d_u, out_tokens=out_tok, out_num=out_n, workspace=ws,
                         stream=st)
 
@@ -752,15 +776,8 @@ def main():
     # Kernel durations: for each launch type one graph that runs it on every pool
     # layer back to back (cold weights, no host gaps between kernels), bracketed by
     # two events on the replay stream; the same for spec_accept alone.
-    def launch(j, li):
-        mats = pool[li]
-        _, idx = LAUNCHES[j]
-        st = torch.cuda.current_stream()
-        if len(idx) == 1:
-            codes, scales, x = mats[idx[0]]
-            mxs.mxfp4_verify_gemm(codes, scales, x, y=ys[idx[0]], stream=st)
-        else:
-            mxs.mxfp4_verify_gemm_grouped([mats[i] for i in idx], ys=[ys[i] for i in idx], stream=st)
+    def launch(j, li, layout=args.layout):
+        run_launch(li, LAUNCHES[j][1], torch.cuda.current_stream(), layout)
 
     def accept_only():
         mxs.spec_accept(d_tgt, d_dft, d_tok, d_u, out_tokens=out_tok, out_num=out_n, workspace=ws,
@@ -795,6 +812,21 @@ def main():
 
     launch_ms = [time_graph(g) for g in type_graphs]
     acc_ms_mean = time_graph(acc_graph)
+    del type_graphs
+    # the other layout's launches for comparison (not in the single-workload runs that
+    # profiles and counters are taken from)
+    other = "row" if args.layout == "tiled" else "tiled"
+    other_ms = None
+    if not args.only:
+        other_ms = []
+        for j in range(len(LAUNCHES)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for li in range(n_layers):
+                    launch(j, li, other)
+            torch.cuda.synchronize()
+            other_ms.append(time_graph(g))
+            del g
 
     step_gemm_bytes = sum(gemm_alg_bytes(n, k, T) for _, n, k in LAYER)
     value = step_gemm_bytes * args.steps / wall / 1e9
@@ -824,19 +856,25 @@ def main():
             "workload": "8B-class layer shapes at T=5: q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; "
                         "down 4096x14336 (MX-FP4 weights, bf16 activations, fp32 out) + spec_accept "
                         "B=1 K=4 V=128256",
-            "T": T, "K_draft": KD, "vocab": V,
+            "T": T, "K_draft": KD, "vocab": V, "weight_layout": args.layout,
             "pool_layers": n_layers, "pool_bytes": layer_bytes * n_layers,
             "gemm_bytes_per_step": step_gemm_bytes,
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "gemm_launches": per_shape,
+        "weight_layout": args.layout,
+        f"gemm_launches_{other}_layout": None if other_ms is None else {
+            name: {"us": round(other_ms[j] * 1e3, 2), "GBps": round(b / (other_ms[j] * 1e-3) / 1e9, 1)}
+            for j, ((name, _), b) in enumerate(zip(LAUNCHES, launch_bytes))},
         "spec_accept_positions_per_s": round((KD + 1) / (acc_ms_mean * 1e-3), 1),
         "spec_accept_us": round(acc_ms_mean * 1e3, 2),
         "numerics": "E2M1 weights decoded exactly to bf16, bf16 x bf16 products summed in fp32 (MFMA); "
                     "spec_accept probabilities in fp64",
         "roofline": {
-            "kernel": "gemm_skinny_kernel (mxfp4_verify_gemm)",
+            "kernel": ("gemm_skinny_kernel<1, 4, 2, false, false, true> (mxfp4_verify_gemm_tiled / "
+                       "mxfp4_verify_gemm_grouped_tiled: tiled weight codes and scales)") if args.layout == "tiled"
+                      else "gemm_skinny_kernel<1, 4, 2, false, false, false> (mxfp4_verify_gemm / _grouped)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -287,13 +287,14 @@ mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* t
                                     float* y, void* stream);
 
 /*
- * mxfp4_verify_gemm_tiled — mxfp4_verify_gemm for batched verification (many
- * sequences: m = B·T well above 32) with the weight codes in the tiled layout of
- * mxfp4_tile_codes and the weight scales in that of mxfp4_tile_scales [M11 §4, §10;
- * the byte order is this library's choice]. It always runs the dense kernel that
- * mxfp4_verify_gemm runs for m > 32 with k % 128 == 0, and its result is bit-identical
- * to mxfp4_verify_gemm's there; for m <= 32 the result is the same product (same
- * numerics) but the row-layout call, which then runs the skinny kernel, is faster.
+ * mxfp4_verify_gemm_tiled — mxfp4_verify_gemm with the weight codes in the tiled
+ * layout of mxfp4_tile_codes and the weight scales in that of mxfp4_tile_scales
+ * [M11 §4, §10; the byte order is this library's choice]. Every wave-wide weight load
+ * then reads 1 KiB contiguously instead of 64 bytes from each of 16 rows. Same product
+ * and numerics. Kernels: for m <= 32 with k % 512 == 0 the skinny kernel of
+ * mxfp4_verify_gemm, otherwise its dense kernel (any m, k % 128 == 0). Where
+ * mxfp4_verify_gemm runs the same kernel (m <= 32 with k % 512 == 0 and 16-byte
+ * aligned row-layout scales; m > 32) the result is bit-identical to it.
  *
  * tiled_codes   mxfp4_tiled_bytes(n, k) bytes, 16-byte aligned.
  * tiled_scales  mxfp4_tiled_scale_bytes(n, k) bytes, 16-byte aligned.
@@ -306,6 +307,21 @@ mxs_status mx_verify_gemm_act_tiled(const uint8_t* tiled_codes, const uint8_t* t
  */
 mxs_status mxfp4_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
                                    const uint16_t* x, int64_t m, float* y, void* stream);
+
+/*
+ * mxfp4_verify_gemm_grouped_tiled — mxfp4_verify_gemm_grouped on tiled weights: each
+ * descriptor's codes and scales are the mxfp4_tile_codes / mxfp4_tile_scales outputs of
+ * that product's weights. Per product the rules, kernels and result are those of
+ * mxfp4_verify_gemm_tiled; up to 8 products share one launch of the skinny kernel, and
+ * with the dense kernel each product has its own launch [M11 §4, §10].
+ *
+ * problems  HOST array of `count` descriptors, read during the call only.
+ * count     1 <= count <= 65536.
+ * k, m      as mxfp4_verify_gemm_tiled, for every product.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status mxfp4_verify_gemm_grouped_tiled(const mxs_gemm_problem* problems, int32_t count, int64_t k, int64_t m,
+                                           void* stream);
 
 /*
  * spec_accept_workspace_bytes — device workspace spec_accept needs for

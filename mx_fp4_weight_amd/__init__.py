@@ -34,7 +34,7 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
-           "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled"]
+           "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled"]
 
 
 class GemmProblem(ctypes.Structure):
@@ -104,6 +104,8 @@ def _load() -> ctypes.CDLL:
     lib.mx_verify_gemm_act_tiled.restype = ctypes.c_int
     lib.mxfp4_verify_gemm_tiled.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     lib.mxfp4_verify_gemm_tiled.restype = ctypes.c_int
+    lib.mxfp4_verify_gemm_grouped_tiled.argtypes = [ctypes.POINTER(GemmProblem), i32, i64, i64, vp]
+    lib.mxfp4_verify_gemm_grouped_tiled.restype = ctypes.c_int
     return lib
 
 
@@ -480,8 +482,8 @@ def mx_verify_gemm_act_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tens
 
 def mxfp4_verify_gemm_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tensor, n: int, k: int,
                             x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """mxfp4_verify_gemm on weights tiled by mxfp4_tile_codes / mxfp4_tile_scales (the dense kernel at every m;
-    bit-identical to mxfp4_verify_gemm where that runs the dense kernel, m > 32)."""
+    """mxfp4_verify_gemm on weights tiled by mxfp4_tile_codes / mxfp4_tile_scales (bit-identical to
+    mxfp4_verify_gemm wherever both run the same kernel)."""
     _want(tiled_codes, torch.uint8, "tiled_codes")
     _want(tiled_scales, torch.uint8, "tiled_scales")
     _want(x, torch.bfloat16, "x")
@@ -497,3 +499,32 @@ def mxfp4_verify_gemm_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tenso
     _check(get_lib().mxfp4_verify_gemm_tiled(_ptr(tiled_codes), _ptr(tiled_scales), n, k, _ptr(x), m, _ptr(y),
                                              _stream(stream)), "mxfp4_verify_gemm_tiled")
     return y
+
+
+def mxfp4_verify_gemm_grouped_tiled(items, ys=None, stream=None):
+    """mxfp4_verify_gemm_grouped on tiled weights.
+
+    items: list of (tiled_codes uint8, tiled_scales uint8, n, x [m, k] bf16), the tiled buffers
+    as mxfp4_tile_codes / mxfp4_tile_scales return them. Returns the list of y_i [m, n_i] fp32
+    (or fills the given ys).
+    """
+    if not items:
+        raise ValueError("no products")
+    m, k = items[0][3].shape
+    arr = (GemmProblem * len(items))()
+    out = []
+    for i, (tc, ts, n, x) in enumerate(items):
+        _want(tc, torch.uint8, "tiled_codes")
+        _want(ts, torch.uint8, "tiled_scales")
+        _want(x, torch.bfloat16, "x")
+        if x.shape != (m, k) or tc.numel() < mxfp4_tiled_bytes(n, k) or ts.numel() < mxfp4_tiled_scale_bytes(n, k):
+            raise ValueError("all products must share k and m, and tiled buffers must hold their weights")
+        y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+        _want(y, torch.float32, "y")
+        if y.shape != (m, n):
+            raise ValueError("y must be [m, n]")
+        arr[i] = GemmProblem(tc.data_ptr(), ts.data_ptr(), x.data_ptr(), y.data_ptr(), n)
+        out.append(y)
+    _check(get_lib().mxfp4_verify_gemm_grouped_tiled(arr, len(items), k, m, _stream(stream)),
+           "mxfp4_verify_gemm_grouped_tiled")
+    return out

@@ -259,6 +259,36 @@ mxs_status mxfp4_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* ti
                                                 static_cast<hipStream_t>(stream)));
 }
 
+mxs_status mxfp4_verify_gemm_grouped_tiled(const mxs_gemm_problem* problems, int32_t count, int64_t k, int64_t m,
+                                           void* stream) {
+  if (!problems) return MXS_ERR_NULL;
+  if (count < 1 || count > 65536 || k < 128 || k % 128 != 0 || k > (int64_t(1) << 23) || m < 1 || m > 65536)
+    return MXS_ERR_SHAPE;
+  for (int32_t i = 0; i < count; ++i) {
+    const mxs_gemm_problem& p = problems[i];
+    if (!p.codes || !p.scales || !p.x || !p.y) return MXS_ERR_NULL;
+    if (p.n < 1 || p.n > (int64_t(1) << 31) - 16) return MXS_ERR_SHAPE;
+    if ((p.n + 1023) / 1024 * 8 * ((m + 79) / 80) > (int64_t)0xffffffffu / 512) return MXS_ERR_SHAPE;
+    if (!aligned(p.codes, 16) || !aligned(p.scales, 16) || !aligned(p.x, 16) || !aligned(p.y, 4))
+      return MXS_ERR_ALIGN;
+  }
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  constexpr int kBatch = 64;  // descriptors converted per host-side batch
+  mxs::mxs_problem_view pv[kBatch];
+  for (int32_t i0 = 0; i0 < count; i0 += kBatch) {
+    const int cnt = count - i0 < kBatch ? count - i0 : kBatch;
+    for (int j = 0; j < cnt; ++j) {
+      const mxs_gemm_problem& p = problems[i0 + j];
+      pv[j] = mxs::mxs_problem_view{p.codes, p.scales, p.x, p.y, p.n};
+    }
+    const mxs_status st =
+        launched(mxs::launch_verify_gemm_grouped_tiled(pv, cnt, k, m, static_cast<hipStream_t>(stream)));
+    if (st != MXS_OK) return st;
+  }
+  return MXS_OK;
+}
+
 size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
   if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
   return mxs::accept_workspace_bytes(b, kd, v, false);

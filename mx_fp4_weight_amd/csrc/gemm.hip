@@ -110,6 +110,11 @@ __device__ inline int xunit(int grp, int d, int t, int g, int mt) { return ((grp
 
 // kNv: NVFP4 weights (an E4M3 scale per 16 values: 32 scale bytes per 4 groups of a row)
 // instead of MX-FP4 (an E8M0 scale per 32 values: 16 bytes per 4 groups).
+// kTiled (MX-FP4, G = 4): codes in the 1 KiB (16 rows x 128 k) tile layout and scales in
+// the 2 KiB (128 rows x 512 k) window layout. A unit's code load of one row tile and group
+// then reads 1 KiB contiguously (64 bytes of each of 16 rows otherwise), and its scale
+// load 256 bytes. Every unit's 4 groups are one 512-k window: slices and phases start on
+// multiples of 4 groups.
 template <int R, int G, bool kNv>
 struct Block {
   u32x4 c[R][G];                      // 16 code bytes per row tile and group
@@ -144,10 +149,11 @@ struct Group {
 // the product's workgroups) and walks them phase by phase (phase 0 of both, then phase 1 of both, ...), with a
 // second set of accumulators, so a phase's activations are staged once for two row
 // blocks and every workgroup is resident at once.
-template <int R, int G, int D, bool kNv, bool kPair = false>
+template <int R, int G, int D, bool kNv, bool kPair = false, bool kTiled = false>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
                                                                          int nsub, int phases,
                                                                          int ngroups_p, int nred) {
+  static_assert(!kTiled || (G == 4 && !kNv), "tiled weights: MX-FP4, one 512-k window per unit");
   extern __shared__ u32x4 smem[];
   int pi = 0;
   while (pi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[pi + 1]) ++pi;
@@ -236,27 +242,48 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     // lanes of rows past `rows` (the rest of an 8-row block, or past n) read zero
     const int rows = live ? min(brows, n - row0) : 0;
     const int rowc = live ? row0 : 0;
-    const __amdgpu_buffer_rsrc_t cr = make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (size_t)rowc * srow, (uint32_t)rows * srow);
+    // tiled: the codes descriptor starts at the 16-row tile holding row0 (sub8 = 8 for the
+    // second 8-row block of a tile) and covers whole tiles (rows past n are zero there);
+    // the scales descriptor covers the ceil(k/512) windows of the 128-row tile holding row0
+    const int sub8 = kTiled ? (rowc & 15) : 0;
+    const __amdgpu_buffer_rsrc_t cr =
+        kTiled ? make_rsrc(codes + (size_t)(rowc - sub8) * row_bytes,
+                           (uint32_t)(rows > 0 ? (sub8 + rows + 15) & ~15 : 0) * row_bytes)
+               : make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t sr =
+        kTiled ? make_rsrc(scales + (size_t)(rowc >> 7) * (size_t)(ngroups >> 2) * 2048u,
+                           rows > 0 ? (uint32_t)(ngroups >> 2) * 2048u : 0u)
+               : make_rsrc(scales + (size_t)rowc * srow, (uint32_t)rows * srow);
+    // tiled: in an 8-row block the lanes of the tile's other 8 rows read nothing
+    const bool lane_ok = !kTiled || brows != 8 || r < rows;
     // The whole offset goes in voffset (soffset = 0): the range check of a raw
     // buffer load covers voffset + the immediate only.
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int blk = (g0 + j) * 4 + g;
-      const bool ok = gl0 + j < ngroups_p && blk < kb;
+      const bool ok = gl0 + j < ngroups_p && blk < kb && lane_ok;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const uint32_t off = ok ? (uint32_t)(16 * i + r) * row_bytes + (uint32_t)blk * 16 : kOutOfRange;
+        // tiled: tile (row tile i, group g0 + j), unit 16g + (row inside the tile)
+        const uint32_t off =
+            !ok ? kOutOfRange
+                : kTiled ? (uint32_t)(16 * i) * row_bytes + (uint32_t)(g0 + j) * 1024u + (uint32_t)(16 * g + sub8 + r) * 16u
+                         : (uint32_t)(16 * i + r) * row_bytes + (uint32_t)blk * 16;
         b.c[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
       }
     }
 #pragma unroll
     for (int q = 0; q < G / 4; ++q) {
       const int grp0 = g0 + 4 * q;
-      const bool ok = gl0 + 4 * q < ngroups_p && grp0 < ngroups;
+      const bool ok = gl0 + 4 * q < ngroups_p && grp0 < ngroups && lane_ok;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        if constexpr (kNv) {
+        if constexpr (kTiled) {
+          // window grp0 / 4, unit = the row's place in its 128-row tile
+          const uint32_t off =
+              ok ? (uint32_t)(grp0 >> 2) * 2048u + (uint32_t)((rowc & 127) + 16 * i + r) * 16u : kOutOfRange;
+          b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+        } else if constexpr (kNv) {
           // 8 scale bytes per group: two 16-byte loads for 4 groups
           const uint32_t off = ok ? (uint32_t)(16 * i + r) * srow + (uint32_t)grp0 * 8 : kOutOfRange;
           b.s[i][2 * q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
@@ -861,11 +888,11 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp, int p
   return false;
 }
 
-template <int R, int G, int D, bool kNv = false, bool kPair = false>
+template <int R, int G, int D, bool kNv = false, bool kPair = false, bool kTiled = false>
 hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
                        int64_t k, int64_t m, hipStream_t stream) {
   static std::atomic<bool> done[kMaxDevices];
-  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv, kPair>, done);
+  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv, kPair, kTiled>, done);
   if (e != hipSuccess) return e;
   Group grp{};
   grp.count = count;
@@ -937,8 +964,8 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     start += (int)share[i];
   }
   grp.wg_start[count] = start;
-  gemm_skinny_kernel<R, G, D, kNv, kPair><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)),
-                                           dim3(pp.waves * kWave), pp.lds, stream>>>(
+  gemm_skinny_kernel<R, G, D, kNv, kPair, kTiled><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)),
+                                                   dim3(pp.waves * kWave), pp.lds, stream>>>(
       grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p, pp.nred);
   return hipGetLastError();
 }
@@ -1031,6 +1058,29 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
   return hipSuccess;
 }
 
+// Tiled codes and scales (launch_tile_codes / launch_tile_scales): the skinny kernel (one
+// 16-row tile per row block, 4 groups per unit, so a unit is one 512-k window) for m <= 32
+// with k % 512 == 0, with the same pair rule as the row layout; else the dense kernel per
+// product.
+hipError_t launch_group_tiled(Config c, const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                              hipStream_t stream) {
+  PhasePlan pp;
+  const bool skinny = m <= kDenseMinM && k % 512 == 0 && k <= (int64_t(1) << 24) &&
+                      plan_phases(k, m, 1, 4, pp, c.per_cu) && pp.ngroups_p % 4 == 0;
+  if (!skinny) {
+    for (int i = 0; i < count; ++i) {
+      const hipError_t e = launch_dense<true>(pv[i], k, m, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const Config c1{1, 4, 2, c.per_cu};
+  int64_t pairs = 0;
+  for (int i = 0; i < count; ++i) pairs += ((pv[i].n + 15) / 16 + 1) / 2;
+  if (pp.phases > 1 && pairs >= kCUs) return launch_main<1, 4, 2, false, true, true>(c1, pp, pv, count, k, m, stream);
+  return launch_main<1, 4, 2, false, false, true>(c1, pp, pv, count, k, m, stream);
+}
+
 hipError_t launch_cfg(Config c, const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                       const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
   const mxs_problem_view pv{codes, scales, x, y, n};
@@ -1056,7 +1106,19 @@ hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64
 hipError_t launch_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
                                     const uint16_t* x, int64_t m, float* y, hipStream_t stream) {
   const mxs_problem_view pv{tiled_codes, tiled_scales, x, y, n};
-  return launch_dense<true>(pv, k, m, stream);
+  return launch_group_tiled(choose(n, k), &pv, 1, k, m, stream);
+}
+
+hipError_t launch_verify_gemm_grouped_tiled(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                            hipStream_t stream) {
+  int64_t n_total = 0;
+  for (int i = 0; i < count; ++i) n_total += pv[i].n;
+  for (int i0 = 0; i0 < count; i0 += kMaxGroup) {
+    const int cnt = count - i0 < kMaxGroup ? count - i0 : kMaxGroup;
+    const hipError_t e = launch_group_tiled(choose(n_total, k), pv + i0, cnt, k, m, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // NVFP4 weights: the skinny kernel for every m (a 16-position tile per grid row), k % 512 == 0

@@ -26,10 +26,13 @@ hipError_t launch_quantize(const float* w, int64_t n, int64_t k, uint8_t* codes,
 hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint16_t* x, int64_t m, float* y, hipStream_t stream);
 
-// The dense kernel over tiled codes (launch_tile_codes) and tiled scales (launch_tile_scales);
-// k % 128 == 0 and k <= 2^23, checked by the caller.
+// Tiled codes (launch_tile_codes) and tiled scales (launch_tile_scales): the skinny kernel for
+// m <= 32 with k % 512 == 0, else the dense kernel; k % 128 == 0 and k <= 2^23, checked by
+// the caller. The grouped form takes up to 8 products per launch as the row layout's does.
 hipError_t launch_verify_gemm_tiled(const uint8_t* tiled_codes, const uint8_t* tiled_scales, int64_t n, int64_t k,
                                     const uint16_t* x, int64_t m, float* y, hipStream_t stream);
+hipError_t launch_verify_gemm_grouped_tiled(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                            hipStream_t stream);
 
 // Sampling transforms of spec_accept_sampled (validated by the caller).
 struct SamplingParams {

@@ -299,3 +299,73 @@ def test_tiled_batched_320_rows_sampled():
     sub_s = np.zeros((n, k // 32), np.uint8)
     sub_c[rows], sub_s[rows] = rc, rs
     check_gemm(sub_c, sub_s, n, k, x, host(y)[:, rows], rows=rows, label="tiled batched")
+
+
+def _tiled(dc, ds):
+    return mxs.mxfp4_tile_codes(dc), mxs.mxfp4_tile_scales(ds)
+
+
+@pytest.mark.parametrize("n,k,m", [
+    (17, 512, 1), (300, 1024, 5), (4096, 4096, 5), (4100, 4096, 8), (1000, 2048, 16), (129, 3072, 32),
+    (2048, 14336, 5),   # k walked in two phases
+    # k % 512 != 0: the dense kernel on tiled weights (the row layout runs the fallback): oracle only
+    (130, 1152, 5), (50, 640, 1),
+])
+def test_tiled_skinny_matches_row_layout(n, k, m):
+    """mxfp4_verify_gemm_tiled at m <= 32: the skinny kernel on tiled codes and scales returns the
+    row-layout result bit for bit, and the oracle bar."""
+    say(f"gemm: tiled skinny n={n} k={k} m={m}")
+    idx = n + 3 * k + m
+    codes, scales, _ = omx.quantize(synth.weights(12, idx, n, k))
+    x = synth.activations(12, idx, m, k)
+    dc, ds, dx = dev(codes), dev(scales), dev_bf16(x)
+    tc, ts = _tiled(dc, ds)
+    y_tiled = host(mxs.mxfp4_verify_gemm_tiled(tc, ts, n, k, dx))
+    torch.cuda.synchronize()
+    if k % 512 == 0:
+        assert np.array_equal(y_tiled, host(mxs.mxfp4_verify_gemm(dc, ds, dx))), (n, k, m)
+    check_gemm(codes, scales, n, k, x, y_tiled, label=f"tiled skinny {n}x{k}x{m}")
+
+
+@pytest.mark.parametrize("n,k,m", [(8200, 14336, 8), (8193, 16384, 16), (8192, 28672, 5)])
+def test_tiled_phased_pairs_match_row_layout(n, k, m):
+    """Several phases and pairs of row blocks (and a ragged last pair) on tiled weights:
+    bit-identical to the row layout."""
+    say(f"gemm: tiled phased pairs n={n} k={k} m={m}")
+    dc, ds = mxs.mxfp4_quantize(dev(synth.weights(13, n + k + m, n, k)))
+    dx = dev_bf16(synth.activations(13, n + k + m, m, k))
+    tc, ts = _tiled(dc, ds)
+    y_row = mxs.mxfp4_verify_gemm(dc, ds, dx)
+    y_tiled = mxs.mxfp4_verify_gemm_tiled(tc, ts, n, k, dx)
+    torch.cuda.synchronize()
+    assert torch.equal(y_tiled, y_row), (n, k, m)
+
+
+@pytest.mark.parametrize("shapes,k,m", [
+    ([4096, 1024, 1024], 4096, 5),          # q | k | v: k and v in 8-row blocks
+    ([1000, 130, 17, 9], 1024, 5),          # 8-row blocks, partial ones, both halves of a tile
+    ([1000, 130, 17, 9], 1024, 16),
+    ([14336, 14336], 4096, 5),              # gate | up
+    ([17, 300, 1, 4100, 64, 2048, 5, 33, 999], 512, 9),   # two launches, ragged
+    ([300, 129], 14336, 8),                 # two phases
+    ([300, 129], 1024, 64),                 # dense kernel per product
+])
+def test_grouped_tiled_matches_row_layout(shapes, k, m):
+    """mxfp4_verify_gemm_grouped_tiled returns the row-layout grouped result bit for bit, and
+    the oracle bar on the small products."""
+    say(f"gemm: grouped tiled {shapes} k={k} m={m}")
+    items, tiled, host_w = [], [], []
+    for i, n in enumerate(shapes):
+        codes, scales, _ = omx.quantize(synth.weights(14, 100 * i + len(shapes), n, k))
+        x = synth.activations(14, len(shapes), m, k)
+        dc, ds, dx = dev(codes), dev(scales), dev_bf16(x)
+        items.append((dc, ds, dx))
+        tiled.append((*_tiled(dc, ds), n, dx))
+        host_w.append((codes, scales, x))
+    ys_row = mxs.mxfp4_verify_gemm_grouped(items)
+    ys_t = mxs.mxfp4_verify_gemm_grouped_tiled(tiled)
+    torch.cuda.synchronize()
+    for n, yr, yt, (codes, scales, x) in zip(shapes, ys_row, ys_t, host_w):
+        assert torch.equal(yt, yr), (n, k, m)
+        if n * k <= 1 << 22:
+            check_gemm(codes, scales, n, k, x, host(yt), label=f"grouped tiled {n}x{k}x{m}")
