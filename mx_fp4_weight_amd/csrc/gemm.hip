@@ -242,40 +242,35 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
     // lanes of rows past `rows` (the rest of an 8-row block, or past n) read zero
     const int rows = live ? min(brows, n - row0) : 0;
     const int rowc = live ? row0 : 0;
-    // tiled: the codes descriptor starts at the 16-row tile holding row0 (sub8 = 8 for the
-    // second 8-row block of a tile) and covers whole tiles (rows past n are zero there);
-    // the scales descriptor covers the ceil(k/512) windows of the 128-row tile holding row0
-    const int sub8 = kTiled ? (rowc & 15) : 0;
+    // tiled (row blocks of 16·R rows): the codes descriptor covers the block's whole
+    // 16-row tiles (rows past n are zero there), the scales descriptor the ceil(k/512)
+    // windows of the 128-row tile holding the block
     const __amdgpu_buffer_rsrc_t cr =
-        kTiled ? make_rsrc(codes + (size_t)(rowc - sub8) * row_bytes,
-                           (uint32_t)(rows > 0 ? (sub8 + rows + 15) & ~15 : 0) * row_bytes)
+        kTiled ? make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)((rows + 15) & ~15) * row_bytes)
                : make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
     const __amdgpu_buffer_rsrc_t sr =
         kTiled ? make_rsrc(scales + (size_t)(rowc >> 7) * (size_t)(ngroups >> 2) * 2048u,
                            rows > 0 ? (uint32_t)(ngroups >> 2) * 2048u : 0u)
                : make_rsrc(scales + (size_t)rowc * srow, (uint32_t)rows * srow);
-    // tiled: in an 8-row block the lanes of the tile's other 8 rows read nothing
-    const bool lane_ok = !kTiled || brows != 8 || r < rows;
     // The whole offset goes in voffset (soffset = 0): the range check of a raw
     // buffer load covers voffset + the immediate only.
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int blk = (g0 + j) * 4 + g;
-      const bool ok = gl0 + j < ngroups_p && blk < kb && lane_ok;
+      const bool ok = gl0 + j < ngroups_p && blk < kb;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        // tiled: tile (row tile i, group g0 + j), unit 16g + (row inside the tile)
-        const uint32_t off =
-            !ok ? kOutOfRange
-                : kTiled ? (uint32_t)(16 * i) * row_bytes + (uint32_t)(g0 + j) * 1024u + (uint32_t)(16 * g + sub8 + r) * 16u
-                         : (uint32_t)(16 * i + r) * row_bytes + (uint32_t)blk * 16;
+        // tiled: tile (row tile i, group g0 + j), unit 16g + r
+        const uint32_t off = !ok     ? kOutOfRange
+                             : kTiled ? (uint32_t)(16 * i) * row_bytes + (uint32_t)(g0 + j) * 1024u + (uint32_t)lane * 16u
+                                      : (uint32_t)(16 * i + r) * row_bytes + (uint32_t)blk * 16;
         b.c[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
       }
     }
 #pragma unroll
     for (int q = 0; q < G / 4; ++q) {
       const int grp0 = g0 + 4 * q;
-      const bool ok = gl0 + 4 * q < ngroups_p && grp0 < ngroups && lane_ok;
+      const bool ok = gl0 + 4 * q < ngroups_p && grp0 < ngroups;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         if constexpr (kTiled) {
@@ -910,6 +905,9 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
   // resident slots unused and the halves still fit: q | k | v of the 8B-class layer is
   // 256 + 64 + 64 blocks on 512 slots (two per CU), so half the CUs held two blocks and
   // half one; with k and v in 8-row blocks every CU holds one q block and one half block.
+  // Tiled weights keep 16-row blocks: a half block would read 128-byte pieces of each tile,
+  // and q | k | v measured as fast or faster without halves there (8.3 vs 8.5 µs at T = 1,
+  // 9.5 vs 9.8 at T = 8).
   int big = 0;
   int64_t nrb16 = 0, half_total = 0;
   for (int i = 0; i < count; ++i) {
@@ -917,7 +915,7 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     if (pv[i].n > pv[big].n) big = i;
   }
   for (int i = 0; i < count; ++i) half_total += i == big ? (pv[i].n + 15) / 16 : (pv[i].n + 7) / 8;
-  const bool halves = R == 1 && pp.phases == 1 && count > 1 && nrb16 < budget && half_total <= budget;
+  const bool halves = !kTiled && R == 1 && pp.phases == 1 && count > 1 && nrb16 < budget && half_total <= budget;
   for (int i = 0; i < count; ++i) brows[i] = halves && i != big ? 8 : 16 * R;
   int64_t sum = 0, total_rb = 0;
   for (int i = 0; i < count; ++i) {

@@ -342,8 +342,8 @@ def test_tiled_phased_pairs_match_row_layout(n, k, m):
 
 
 @pytest.mark.parametrize("shapes,k,m", [
-    ([4096, 1024, 1024], 4096, 5),          # q | k | v: k and v in 8-row blocks
-    ([1000, 130, 17, 9], 1024, 5),          # 8-row blocks, partial ones, both halves of a tile
+    ([4096, 1024, 1024], 4096, 5),          # q | k | v (the row layout runs k and v in 8-row blocks)
+    ([1000, 130, 17, 9], 1024, 5),          # partial row blocks
     ([1000, 130, 17, 9], 1024, 16),
     ([14336, 14336], 4096, 5),              # gate | up
     ([17, 300, 1, 4100, 64, 2048, 5, 33, 999], 512, 9),   # two launches, ragged
@@ -351,8 +351,10 @@ def test_tiled_phased_pairs_match_row_layout(n, k, m):
     ([300, 129], 1024, 64),                 # dense kernel per product
 ])
 def test_grouped_tiled_matches_row_layout(shapes, k, m):
-    """mxfp4_verify_gemm_grouped_tiled returns the row-layout grouped result bit for bit, and
-    the oracle bar on the small products."""
+    """mxfp4_verify_gemm_grouped_tiled against the oracle on the small products, and bit for bit
+    against the row-layout grouped call where both use the same row blocks (the row layout splits
+    small products of a group into 8-row blocks, which changes nothing in any sum: a row's
+    products and their order are those of its 16-row block)."""
     say(f"gemm: grouped tiled {shapes} k={k} m={m}")
     items, tiled, host_w = [], [], []
     for i, n in enumerate(shapes):
