@@ -502,11 +502,15 @@ def nvfp4_8b(torch, mxs, gen, pool_gb=2.4, reps=3):
         mats = []
         for _, n, k in LAYER:
             w = torch.randn((n, k), generator=gen, device="cuda", dtype=torch.float32) * 0.02
-            mats.append(mxs.nvfp4_quantize(w))
+            c, sc, g = mxs.nvfp4_quantize(w)
             del w
+            # codes tiled once (weight prep); the E4M3 scales stay in the row layout
+            mats.append((mxs.mxfp4_tile_codes(c), sc, g, n))
+            del c
         pool.append(mats)
     out = {"pool_layers": n_layers, "pool_bytes": layer_b * n_layers,
-           "launches": "q|k|v and gate|up grouped (nvfp4_verify_gemm_grouped), o and down single"}
+           "launches": "q|k|v and gate|up grouped, o and down single (nvfp4_verify_gemm_grouped_tiled: "
+                       "codes tiled by mxfp4_tile_codes, scales in the row layout)"}
     for t in (1, 5, 8):
         xs = [_rand_bf16(torch, gen, t, k) for (_, _, k) in LAYER]
         ys = [torch.empty((t, n), dtype=torch.float32, device="cuda") for (_, n, _) in LAYER]
@@ -514,12 +518,8 @@ def nvfp4_8b(torch, mxs, gen, pool_gb=2.4, reps=3):
         for name, idx in LAUNCHES:
             def body(idx=idx):
                 for li in range(n_layers):
-                    items = [(*pool[li][i], xs[i]) for i in idx]
-                    if len(items) == 1:
-                        c, s, g, x = items[0]
-                        mxs.nvfp4_verify_gemm(c, s, g, x, y=ys[idx[0]])
-                    else:
-                        mxs.nvfp4_verify_gemm_grouped(items, ys=[ys[i] for i in idx])
+                    mxs.nvfp4_verify_gemm_grouped_tiled([(*pool[li][i], xs[i]) for i in idx],
+                                                        ys=[ys[i] for i in idx])
             us = _graph_ms(torch, body, reps) * 1e3 / n_layers
             byts = sum(nv_bytes(LAYER[i][1], LAYER[i][2]) + t * LAYER[i][2] * 2 + t * LAYER[i][1] * 4 for i in idx)
             row[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}

@@ -200,6 +200,17 @@ mxs_status nvfp4_verify_gemm_grouped(const mxs_nvfp4_problem* problems, int32_t 
                                      void* stream);
 
 /*
+ * nvfp4_verify_gemm_grouped_tiled — nvfp4_verify_gemm_grouped with each product's codes
+ * in the tiled layout of mxfp4_tile_codes (NVFP4 codes pack E2M1 values as MX-FP4 codes
+ * do; the E4M3 scales stay in the row layout [n, k/16]). Every wave-wide code load then
+ * reads 1 KiB contiguously [the byte order is this library's choice]. Same rules, errors
+ * and kernel; the result is bit-identical to nvfp4_verify_gemm_grouped's. One product is
+ * a group of one. n <= 2^31 - 16.
+ */
+mxs_status nvfp4_verify_gemm_grouped_tiled(const mxs_nvfp4_problem* problems, int32_t count, int64_t k, int64_t m,
+                                           void* stream);
+
+/*
  * mx_quantize_act — bf16 activations X[m, k] -> MX-FP8 or MX-FP4 [M11 §11: W4A8 /
  * W4A4 quantize activations as well as weights; §12: E4M3 = 8-bit float with 4
  * exponent and 3 fraction bits, E8M0 power-of-two scale; news page, "Microscaling

@@ -34,7 +34,8 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
-           "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled"]
+           "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled",
+           "nvfp4_verify_gemm_grouped_tiled"]
 
 
 class GemmProblem(ctypes.Structure):
@@ -106,6 +107,8 @@ def _load() -> ctypes.CDLL:
     lib.mxfp4_verify_gemm_tiled.restype = ctypes.c_int
     lib.mxfp4_verify_gemm_grouped_tiled.argtypes = [ctypes.POINTER(GemmProblem), i32, i64, i64, vp]
     lib.mxfp4_verify_gemm_grouped_tiled.restype = ctypes.c_int
+    lib.nvfp4_verify_gemm_grouped_tiled.argtypes = [ctypes.POINTER(NvProblem), i32, i64, i64, vp]
+    lib.nvfp4_verify_gemm_grouped_tiled.restype = ctypes.c_int
     return lib
 
 
@@ -527,4 +530,32 @@ def mxfp4_verify_gemm_grouped_tiled(items, ys=None, stream=None):
         out.append(y)
     _check(get_lib().mxfp4_verify_gemm_grouped_tiled(arr, len(items), k, m, _stream(stream)),
            "mxfp4_verify_gemm_grouped_tiled")
+    return out
+
+
+def nvfp4_verify_gemm_grouped_tiled(items, ys=None, stream=None):
+    """nvfp4_verify_gemm_grouped with the codes tiled by mxfp4_tile_codes (scales in the row layout).
+
+    items: list of (tiled_codes uint8, scales [n_i, k/16], global_scale fp32 [1], n_i, x [m, k] bf16).
+    """
+    if not items:
+        raise ValueError("no products")
+    m, k = items[0][4].shape
+    arr = (NvProblem * len(items))()
+    out = []
+    for i, (tc, scales, g, n, x) in enumerate(items):
+        _want(tc, torch.uint8, "tiled_codes")
+        _want(scales, torch.uint8, "scales")
+        _want(g, torch.float32, "global_scale")
+        _want(x, torch.bfloat16, "x")
+        if x.shape != (m, k) or scales.shape != (n, k // 16) or tc.numel() < mxfp4_tiled_bytes(n, k):
+            raise ValueError("all products must share k and m, and tiled codes must hold their weights")
+        y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
+        _want(y, torch.float32, "y")
+        if y.shape != (m, n):
+            raise ValueError("y must be [m, n]")
+        arr[i] = NvProblem(tc.data_ptr(), scales.data_ptr(), g.data_ptr(), x.data_ptr(), y.data_ptr(), n)
+        out.append(y)
+    _check(get_lib().nvfp4_verify_gemm_grouped_tiled(arr, len(items), k, m, _stream(stream)),
+           "nvfp4_verify_gemm_grouped_tiled")
     return out

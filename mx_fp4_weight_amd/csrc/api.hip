@@ -167,6 +167,36 @@ mxs_status nvfp4_verify_gemm_grouped(const mxs_nvfp4_problem* problems, int32_t 
   return MXS_OK;
 }
 
+mxs_status nvfp4_verify_gemm_grouped_tiled(const mxs_nvfp4_problem* problems, int32_t count, int64_t k, int64_t m,
+                                           void* stream) {
+  if (!problems) return MXS_ERR_NULL;
+  if (count < 1 || count > 65536 || k < 512 || k % 512 != 0 || k > (int64_t(1) << 24) || m < 1 || m > 65536)
+    return MXS_ERR_SHAPE;
+  for (int32_t i = 0; i < count; ++i) {
+    const mxs_nvfp4_problem& p = problems[i];
+    if (!p.codes || !p.scales || !p.global_scale || !p.x || !p.y) return MXS_ERR_NULL;
+    if (p.n < 1 || p.n > (int64_t(1) << 31) - 16) return MXS_ERR_SHAPE;
+    if (!aligned(p.codes, 16) || !aligned(p.scales, 16) || !aligned(p.global_scale, 4) || !aligned(p.x, 16) ||
+        !aligned(p.y, 4))
+      return MXS_ERR_ALIGN;
+  }
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  constexpr int kBatch = 64;  // descriptors converted per host-side batch
+  mxs::mxs_problem_view pv[kBatch];
+  for (int32_t i0 = 0; i0 < count; i0 += kBatch) {
+    const int cnt = count - i0 < kBatch ? count - i0 : kBatch;
+    for (int j = 0; j < cnt; ++j) {
+      const mxs_nvfp4_problem& p = problems[i0 + j];
+      pv[j] = mxs::mxs_problem_view{p.codes, p.scales, p.x, p.y, p.n, p.global_scale};
+    }
+    const mxs_status st =
+        launched(mxs::launch_nvfp4_verify_gemm_grouped_tiled(pv, cnt, k, m, static_cast<hipStream_t>(stream)));
+    if (st != MXS_OK) return st;
+  }
+  return MXS_OK;
+}
+
 mxs_status mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,
                            uint8_t* scales, int32_t* dev_flags, void* stream) {
   if (!x || !codes || !scales) return MXS_ERR_NULL;

@@ -110,8 +110,8 @@ __device__ inline int xunit(int grp, int d, int t, int g, int mt) { return ((grp
 
 // kNv: NVFP4 weights (an E4M3 scale per 16 values: 32 scale bytes per 4 groups of a row)
 // instead of MX-FP4 (an E8M0 scale per 32 values: 16 bytes per 4 groups).
-// kTiled (MX-FP4, G = 4): codes in the 1 KiB (16 rows x 128 k) tile layout and scales in
-// the 2 KiB (128 rows x 512 k) window layout. A unit's code load of one row tile and group
+// kTiled (G = 4): codes in the 1 KiB (16 rows x 128 k) tile layout and, for MX-FP4, scales
+// in the 2 KiB (128 rows x 512 k) window layout (NVFP4 scales stay in the row layout). A unit's code load of one row tile and group
 // then reads 1 KiB contiguously (64 bytes of each of 16 rows otherwise), and its scale
 // load 256 bytes. Every unit's 4 groups are one 512-k window: slices and phases start on
 // multiples of 4 groups.
@@ -153,7 +153,7 @@ template <int R, int G, int D, bool kNv, bool kPair = false, bool kTiled = false
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
                                                                          int nsub, int phases,
                                                                          int ngroups_p, int nred) {
-  static_assert(!kTiled || (G == 4 && !kNv), "tiled weights: MX-FP4, one 512-k window per unit");
+  static_assert(!kTiled || G == 4, "tiled weights: one 512-k window per unit");
   extern __shared__ u32x4 smem[];
   int pi = 0;
   while (pi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[pi + 1]) ++pi;
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
         kTiled ? make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)((rows + 15) & ~15) * row_bytes)
                : make_rsrc(codes + (size_t)rowc * row_bytes, (uint32_t)rows * row_bytes);
     const __amdgpu_buffer_rsrc_t sr =
-        kTiled ? make_rsrc(scales + (size_t)(rowc >> 7) * (size_t)(ngroups >> 2) * 2048u,
+        kTiled && !kNv ? make_rsrc(scales + (size_t)(rowc >> 7) * (size_t)(ngroups >> 2) * 2048u,
                            rows > 0 ? (uint32_t)(ngroups >> 2) * 2048u : 0u)
                : make_rsrc(scales + (size_t)rowc * srow, (uint32_t)rows * srow);
     // The whole offset goes in voffset (soffset = 0): the range check of a raw
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
       const bool ok = gl0 + 4 * q < ngroups_p && grp0 < ngroups;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        if constexpr (kTiled) {
+        if constexpr (kTiled && !kNv) {
           // window grp0 / 4, unit = the row's place in its 128-row tile
           const uint32_t off =
               ok ? (uint32_t)(grp0 >> 2) * 2048u + (uint32_t)((rowc & 127) + 16 * i + r) * 16u : kOutOfRange;
@@ -1121,6 +1121,8 @@ hipError_t launch_verify_gemm_grouped_tiled(const mxs_problem_view* pv, int coun
 
 // NVFP4 weights: the skinny kernel for every m (a 16-position tile per grid row), k % 512 == 0
 // and 16-byte aligned scales checked by the caller; up to kMaxGroup products per launch.
+// kTiled: codes in the tiled layout of launch_tile_codes, scales in the row layout.
+template <bool kTiled = false>
 static hipError_t launch_nvfp4_group(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
                                      hipStream_t stream) {
   int64_t n_total = 0, nrb2 = 0;
@@ -1136,9 +1138,9 @@ static hipError_t launch_nvfp4_group(const mxs_problem_view* pv, int count, int6
     // that still leaves a workgroup per CU
     PhasePlan pp2;
     if (nrb2 >= kCUs && plan_phases(k, m < 16 ? m : 16, 2, c.G, pp2))
-      return launch_main<2, 4, 2, true>(Config{2, c.G, c.D, c.per_cu}, pp2, pv, count, k, m, stream);
+      return launch_main<2, 4, 2, true, false, kTiled>(Config{2, c.G, c.D, c.per_cu}, pp2, pv, count, k, m, stream);
   }
-  return launch_main<1, 4, 2, true>(c, pp, pv, count, k, m, stream);
+  return launch_main<1, 4, 2, true, false, kTiled>(c, pp, pv, count, k, m, stream);
 }
 
 hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales, const float* gscale,
@@ -1154,6 +1156,16 @@ hipError_t launch_nvfp4_verify_gemm_grouped(const mxs_problem_view* pv, int coun
   for (int i0 = 0; i0 < count; i0 += kMaxGroup) {
     const int cnt = count - i0 < kMaxGroup ? count - i0 : kMaxGroup;
     const hipError_t e = launch_nvfp4_group(pv + i0, cnt, k, m, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_nvfp4_verify_gemm_grouped_tiled(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                                  hipStream_t stream) {
+  for (int i0 = 0; i0 < count; i0 += kMaxGroup) {
+    const int cnt = count - i0 < kMaxGroup ? count - i0 : kMaxGroup;
+    const hipError_t e = launch_nvfp4_group<true>(pv + i0, cnt, k, m, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

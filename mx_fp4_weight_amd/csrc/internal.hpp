@@ -50,6 +50,9 @@ hipError_t launch_nvfp4_verify_gemm(const uint8_t* codes, const uint8_t* scales,
                                     hipStream_t stream);
 
 // Several NVFP4 products with the same k (% 512 == 0) and m, each with its own tensor scale.
+// The same with the codes in the tiled layout of launch_tile_codes (scales in the row layout).
+hipError_t launch_nvfp4_verify_gemm_grouped_tiled(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
+                                                  hipStream_t stream);
 hipError_t launch_nvfp4_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
                                             hipStream_t stream);
 

@@ -340,3 +340,22 @@ def test_grouped_tiled_host_errors():
     assert call(n=1 << 21, m=65536) == mxs.MXS_ERR_SHAPE
     assert call(scales=0x200004) == mxs.MXS_ERR_ALIGN and call(codes=0x100008) == mxs.MXS_ERR_ALIGN
     assert call() == mxs.MXS_ERR_DEVICE and call(k=640) == mxs.MXS_ERR_DEVICE
+
+
+def test_nvfp4_grouped_tiled_host_errors():
+    """nvfp4_verify_gemm_grouped_tiled refuses malformed calls before any HIP call."""
+    lib = mxs.get_lib()
+
+    def call(count=2, k=512, m=5, **kw):
+        arr = (mxs.NvProblem * 2)()
+        for i in range(2):
+            arr[i] = mxs.NvProblem(0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 64)
+        for name, v in kw.items():
+            setattr(arr[1], name, v)
+        return lib.nvfp4_verify_gemm_grouped_tiled(arr, count, k, m, None)
+    assert lib.nvfp4_verify_gemm_grouped_tiled(None, 1, 512, 5, None) == mxs.MXS_ERR_NULL
+    assert call(codes=0) == mxs.MXS_ERR_NULL and call(global_scale=0) == mxs.MXS_ERR_NULL
+    assert call(count=0) == mxs.MXS_ERR_SHAPE and call(k=640) == mxs.MXS_ERR_SHAPE
+    assert call(m=0) == mxs.MXS_ERR_SHAPE and call(n=0) == mxs.MXS_ERR_SHAPE
+    assert call(codes=0x100008) == mxs.MXS_ERR_ALIGN and call(scales=0x200004) == mxs.MXS_ERR_ALIGN
+    assert call() == mxs.MXS_ERR_DEVICE

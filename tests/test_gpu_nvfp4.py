@@ -269,3 +269,33 @@ def test_grouped_matches_single(shapes, k, m):
     torch.cuda.synchronize()
     for (c, s, g, x), y in zip(refs, ys):
         check_gemm(c, s, g, x, host(y), label=f"grouped n={c.shape[0]}")
+
+
+@pytest.mark.parametrize("shapes,k,m", [
+    ([4096, 1024, 1024], 4096, 5),                         # q | k | v
+    ([300, 17, 1000, 64, 129, 5, 77, 256, 33, 500], 1024, 3),   # two launches, ragged
+    ([8192], 14336, 5),                                    # phases with two row tiles per block
+    ([300, 70], 14336, 8),                                 # phases, one row tile per block
+    ([2000, 2000], 4096, 20),                              # two 16-position tiles
+])
+def test_grouped_tiled_matches_row_layout(shapes, k, m):
+    """nvfp4_verify_gemm_grouped_tiled (codes tiled by mxfp4_tile_codes) returns the row-layout
+    result bit for bit, and the oracle bar on the small products."""
+    say(f"nvfp4 gemm grouped tiled: {shapes} k={k} m={m}")
+    items, titems, hosts = [], [], []
+    for i, n in enumerate(shapes):
+        w = synth.weights(78, 100 * i + n, n, k, sigma=0.02 * (i + 1))
+        xb = synth.activations(78, 100 * i + n, m, k)
+        dc, ds, dg = mxs.nvfp4_quantize(dev(w))
+        x = dev_bf16(xb)
+        items.append((dc, ds, dg, x))
+        titems.append((mxs.mxfp4_tile_codes(dc), ds, dg, n, x))
+        hosts.append((w, xb))
+    ys = mxs.nvfp4_verify_gemm_grouped(items)
+    yt = mxs.nvfp4_verify_gemm_grouped_tiled(titems)
+    torch.cuda.synchronize()
+    for n, a, b, (w, xb) in zip(shapes, ys, yt, hosts):
+        assert torch.equal(a, b), (n, k, m)
+        if n * k <= 1 << 22:
+            c, s, g, _ = nv.quantize(w)
+            check_gemm(c, s, g, xb, host(b), label=f"grouped tiled n={n}")
