@@ -253,8 +253,9 @@ mxs_status mx_verify_gemm_act(const uint8_t* codes, const uint8_t* scales, int64
 
 /*
  * mxfp4_tile_codes — MX-FP4 codes in the mxfp4_quantize row layout [n, k/2] -> the
- * tiled layout read by mx_verify_gemm_act_tiled and mxfp4_verify_gemm_tiled. This is a
- * byte permutation done once at weight-prep time, like the quantization itself [M11 §12
+ * tiled layout read by mx_verify_gemm_act_tiled, mxfp4_verify_gemm_tiled,
+ * mxfp4_verify_gemm_grouped_tiled and (for NVFP4 codes, which pack E2M1 values the same way)
+ * nvfp4_verify_gemm_grouped_tiled. This is a byte permutation done once at weight-prep time, like the quantization itself [M11 §12
  * fixes the values; the byte order in memory is this library's choice]. The scales have
  * a tiled layout of their own (mxfp4_tile_scales).
  *
@@ -273,7 +274,8 @@ mxs_status mxfp4_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t*
 
 /*
  * mxfp4_tile_scales — E8M0 scales in the row layout [n, k/32] -> the tiled scale layout
- * read by mx_verify_gemm_act_tiled and mxfp4_verify_gemm_tiled: 2 KiB per (128-row tile t, 512-k window w) at byte
+ * read by mx_verify_gemm_act_tiled, mxfp4_verify_gemm_tiled and
+ * mxfp4_verify_gemm_grouped_tiled: 2 KiB per (128-row tile t, 512-k window w) at byte
  * (t * ceil(k/512) + w) * 2048. Its 16-byte unit r holds the scale bytes of columns
  * 512 w .. 512 w + 511 (bytes 16 w .. 16 w + 15 of the row) of row 128 t + r. Bytes
  * past k/32 and rows past n are zero.
