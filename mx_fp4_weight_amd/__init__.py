@@ -142,11 +142,21 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _want(t, dtype, name):
+def _want(t, dtype, name, shape=None):
+    """Type check of a tensor argument; with `shape`, also its exact shape (raised before any launch:
+    the C ABI sees only pointers, so a short output buffer would otherwise be written past its end)."""
     if t is None:
         return
     if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous {dtype} CUDA/HIP tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _want_flags(dev_flags):
+    _want(dev_flags, torch.int32, "dev_flags")
+    if dev_flags is not None and dev_flags.numel() < 1:
+        raise ValueError("dev_flags must hold at least one int32")
 
 
 def mxfp4_quantize(w: torch.Tensor, codes: torch.Tensor | None = None,
@@ -159,9 +169,9 @@ def mxfp4_quantize(w: torch.Tensor, codes: torch.Tensor | None = None,
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
     if scales is None:
         scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
-    _want(codes, torch.uint8, "codes")
-    _want(scales, torch.uint8, "scales")
-    _want(dev_flags, torch.int32, "dev_flags")
+    _want(codes, torch.uint8, "codes", (n, k // 2))
+    _want(scales, torch.uint8, "scales", (n, k // 32))
+    _want_flags(dev_flags)
     _check(get_lib().mxfp4_quantize(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(dev_flags),
                               _stream(stream)), "mxfp4_quantize")
     return codes, scales
@@ -180,9 +190,7 @@ def mxfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, x: torch.Tensor
         raise ValueError("shape mismatch between codes, scales and x")
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _want(y, torch.float32, "y")
-    if y.shape != (m, n):
-        raise ValueError("y must be [m, n]")
+    _want(y, torch.float32, "y", (m, n))
     _check(get_lib().mxfp4_verify_gemm(_ptr(codes), _ptr(scales), n, k, _ptr(x), m, _ptr(y),
                                  _stream(stream)), "mxfp4_verify_gemm")
     return y
@@ -208,9 +216,7 @@ def mxfp4_verify_gemm_grouped(items, ys=None, stream=None):
         if codes.shape[1] * 2 != k or x.shape != (m, k) or scales.shape != (n, k // 32):
             raise ValueError("all products must share k and m")
         y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
-        _want(y, torch.float32, "y")
-        if y.shape != (m, n):
-            raise ValueError("y must be [m, n]")
+        _want(y, torch.float32, "y", (m, n))
         arr[i] = GemmProblem(codes.data_ptr(), scales.data_ptr(), x.data_ptr(), y.data_ptr(), n)
         out.append(y)
     _check(get_lib().mxfp4_verify_gemm_grouped(arr, len(items), k, m, _stream(stream)),
@@ -249,11 +255,13 @@ def spec_accept(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
         out_tokens = torch.empty((b, kd + 1), dtype=torch.int32, device=dev)
     if out_num is None:
         out_num = torch.empty((b,), dtype=torch.int32, device=dev)
+    _want(out_tokens, torch.int32, "out_tokens", (b, kd + 1))
+    _want(out_num, torch.int32, "out_num", (b,))
     need = spec_accept_workspace_bytes(b, kd, v)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     _want(workspace, torch.uint8, "workspace")
-    _want(dev_flags, torch.int32, "dev_flags")
+    _want_flags(dev_flags)
     _check(get_lib().spec_accept(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), b, kd, v,
                            _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
                            _ptr(dev_flags), _stream(stream)), "spec_accept")
@@ -297,11 +305,13 @@ def spec_accept_sampled(target: torch.Tensor, draft: torch.Tensor | None, tokens
         out_tokens = torch.empty((b, kd + 1), dtype=torch.int32, device=dev)
     if out_num is None:
         out_num = torch.empty((b,), dtype=torch.int32, device=dev)
+    _want(out_tokens, torch.int32, "out_tokens", (b, kd + 1))
+    _want(out_num, torch.int32, "out_num", (b,))
     need = spec_accept_sampled_workspace_bytes(b, kd, v)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     _want(workspace, torch.uint8, "workspace")
-    _want(dev_flags, torch.int32, "dev_flags")
+    _want_flags(dev_flags)
     _check(get_lib().spec_accept_sampled(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), b, kd, v,
                                          float(temperature), int(top_k), float(top_p), _ptr(mask),
                                          _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
@@ -322,10 +332,10 @@ def nvfp4_quantize(w: torch.Tensor, codes: torch.Tensor | None = None, scales: t
         scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
     if global_scale is None:
         global_scale = torch.empty((1,), dtype=torch.float32, device=dev)
-    _want(codes, torch.uint8, "codes")
-    _want(scales, torch.uint8, "scales")
-    _want(global_scale, torch.float32, "global_scale")
-    _want(dev_flags, torch.int32, "dev_flags")
+    _want(codes, torch.uint8, "codes", (n, k // 2))
+    _want(scales, torch.uint8, "scales", (n, k // 16))
+    _want(global_scale, torch.float32, "global_scale", (1,))
+    _want_flags(dev_flags)
     _check(get_lib().nvfp4_quantize(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(global_scale),
                                     _ptr(dev_flags), _stream(stream)), "nvfp4_quantize")
     return codes, scales, global_scale
@@ -336,7 +346,7 @@ def nvfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, global_scale: t
     """Y[m, n] = X[m, k] · Ŵᵀ over NVFP4 weights (codes [n, k/2], E4M3 scales [n, k/16], fp32 g)."""
     _want(codes, torch.uint8, "codes")
     _want(scales, torch.uint8, "scales")
-    _want(global_scale, torch.float32, "global_scale")
+    _want(global_scale, torch.float32, "global_scale", (1,))
     _want(x, torch.bfloat16, "x")
     n = codes.shape[0]
     k = codes.shape[1] * 2
@@ -345,7 +355,7 @@ def nvfp4_verify_gemm(codes: torch.Tensor, scales: torch.Tensor, global_scale: t
         raise ValueError("shape mismatch")
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _want(y, torch.float32, "y")
+    _want(y, torch.float32, "y", (m, n))
     _check(get_lib().nvfp4_verify_gemm(_ptr(codes), _ptr(scales), _ptr(global_scale), n, k, _ptr(x), m,
                                        _ptr(y), _stream(stream)), "nvfp4_verify_gemm")
     return y
@@ -372,9 +382,7 @@ def nvfp4_verify_gemm_grouped(items, ys=None, stream=None):
         if codes.shape[1] * 2 != k or x.shape != (m, k) or scales.shape != (n, k // 16):
             raise ValueError("all products must share k and m")
         y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
-        _want(y, torch.float32, "y")
-        if y.shape != (m, n):
-            raise ValueError("y must be [m, n]")
+        _want(y, torch.float32, "y", (m, n))
         arr[i] = NvProblem(codes.data_ptr(), scales.data_ptr(), g.data_ptr(), x.data_ptr(), y.data_ptr(), n)
         out.append(y)
     _check(get_lib().nvfp4_verify_gemm_grouped(arr, len(items), k, m, _stream(stream)),
@@ -391,13 +399,15 @@ def mx_quantize_act(x: torch.Tensor, fmt: int, codes: torch.Tensor | None = None
     """bf16 X[m, k] -> (codes, scales): MX-FP8 codes [m, k] or MX-FP4 codes [m, k/2]; scales [m, k/32]."""
     _want(x, torch.bfloat16, "x")
     m, k = x.shape
+    if fmt not in (ACT_FP8, ACT_FP4):
+        raise ValueError("fmt must be ACT_FP8 or ACT_FP4")
     if codes is None:
         codes = torch.empty((m, k if fmt == ACT_FP8 else k // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
-    _want(codes, torch.uint8, "codes")
-    _want(scales, torch.uint8, "scales")
-    _want(dev_flags, torch.int32, "dev_flags")
+    _want(codes, torch.uint8, "codes", (m, k if fmt == ACT_FP8 else k // 2))
+    _want(scales, torch.uint8, "scales", (m, k // 32))
+    _want_flags(dev_flags)
     _check(get_lib().mx_quantize_act(_ptr(x), m, k, fmt, _ptr(codes), _ptr(scales), _ptr(dev_flags),
                                      _stream(stream)), "mx_quantize_act")
     return codes, scales
@@ -416,7 +426,7 @@ def mx_verify_gemm_act(codes: torch.Tensor, scales: torch.Tensor, act_codes: tor
         raise ValueError("shape mismatch")
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=codes.device)
-    _want(y, torch.float32, "y")
+    _want(y, torch.float32, "y", (m, n))
     _check(get_lib().mx_verify_gemm_act(_ptr(codes), _ptr(scales), n, k, _ptr(act_codes), _ptr(act_scales), fmt,
                                         m, _ptr(y), _stream(stream)), "mx_verify_gemm_act")
     return y
@@ -476,7 +486,7 @@ def mx_verify_gemm_act_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tens
         raise ValueError("shape mismatch")
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=act_codes.device)
-    _want(y, torch.float32, "y")
+    _want(y, torch.float32, "y", (m, n))
     _check(get_lib().mx_verify_gemm_act_tiled(_ptr(tiled_codes), _ptr(tiled_scales), n, k, _ptr(act_codes),
                                               _ptr(act_scales), fmt, m, _ptr(y), _stream(stream)),
            "mx_verify_gemm_act_tiled")
@@ -496,9 +506,7 @@ def mxfp4_verify_gemm_tiled(tiled_codes: torch.Tensor, tiled_scales: torch.Tenso
         raise ValueError("shape mismatch")
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    _want(y, torch.float32, "y")
-    if y.shape != (m, n):
-        raise ValueError("y must be [m, n]")
+    _want(y, torch.float32, "y", (m, n))
     _check(get_lib().mxfp4_verify_gemm_tiled(_ptr(tiled_codes), _ptr(tiled_scales), n, k, _ptr(x), m, _ptr(y),
                                              _stream(stream)), "mxfp4_verify_gemm_tiled")
     return y
@@ -523,9 +531,7 @@ def mxfp4_verify_gemm_grouped_tiled(items, ys=None, stream=None):
         if x.shape != (m, k) or tc.numel() < mxfp4_tiled_bytes(n, k) or ts.numel() < mxfp4_tiled_scale_bytes(n, k):
             raise ValueError("all products must share k and m, and tiled buffers must hold their weights")
         y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
-        _want(y, torch.float32, "y")
-        if y.shape != (m, n):
-            raise ValueError("y must be [m, n]")
+        _want(y, torch.float32, "y", (m, n))
         arr[i] = GemmProblem(tc.data_ptr(), ts.data_ptr(), x.data_ptr(), y.data_ptr(), n)
         out.append(y)
     _check(get_lib().mxfp4_verify_gemm_grouped_tiled(arr, len(items), k, m, _stream(stream)),
@@ -551,9 +557,7 @@ def nvfp4_verify_gemm_grouped_tiled(items, ys=None, stream=None):
         if x.shape != (m, k) or scales.shape != (n, k // 16) or tc.numel() < mxfp4_tiled_bytes(n, k):
             raise ValueError("all products must share k and m, and tiled codes must hold their weights")
         y = ys[i] if ys is not None else torch.empty((m, n), dtype=torch.float32, device=x.device)
-        _want(y, torch.float32, "y")
-        if y.shape != (m, n):
-            raise ValueError("y must be [m, n]")
+        _want(y, torch.float32, "y", (m, n))
         arr[i] = NvProblem(tc.data_ptr(), scales.data_ptr(), g.data_ptr(), x.data_ptr(), y.data_ptr(), n)
         out.append(y)
     _check(get_lib().nvfp4_verify_gemm_grouped_tiled(arr, len(items), k, m, _stream(stream)),

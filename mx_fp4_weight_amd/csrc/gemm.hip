@@ -818,7 +818,22 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_xglobal_kernel(
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int64_t kDenseMinM = 32;  // above this many activation rows the dense kernel runs
 constexpr int kMaxDevices = 64;
-constexpr int kCUs = 256;
+
+// Compute units of the current device (256 on MI355X), read once per device: the
+// persistent grids are sized as resident workgroups per CU times this count.
+int device_cus() {
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+  if (dev < kMaxDevices) cus[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
 
 // Raise a kernel's dynamic-LDS limit once per device.
 template <typename F>
@@ -891,7 +906,7 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
   if (e != hipSuccess) return e;
   Group grp{};
   grp.count = count;
-  const int64_t budget = (int64_t)kCUs * c.per_cu;
+  const int64_t budget = (int64_t)device_cus() * c.per_cu;
   // Persistent grid split between the products: in proportion to their row blocks, at
   // least one workgroup each, never more than a product's row blocks, and never more
   // than the budget in total (one workgroup past it would run as a second round: the
@@ -1040,7 +1055,7 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
     // block (R = 2) measured slower than either: 42.9 µs for 8192 x 28672.
     int64_t pairs = 0;
     for (int i = 0; i < count; ++i) pairs += ((pv[i].n + 15) / 16 + 1) / 2;
-    if (pp.phases > 1 && pairs >= kCUs && c.R == 1 && c.G == 4 && c.D == 2)
+    if (pp.phases > 1 && pairs >= device_cus() && c.R == 1 && c.G == 4 && c.D == 2)
       return launch_main<1, 4, 2, false, true>(c, pp, pv, count, k, m, stream);
 #define MXS_RG(RR, GG, DD) \
   if (c.R == RR && c.G == GG && c.D == DD) return launch_main<RR, GG, DD>(c, pp, pv, count, k, m, stream);
@@ -1075,7 +1090,7 @@ hipError_t launch_group_tiled(Config c, const mxs_problem_view* pv, int count, i
   const Config c1{1, 4, 2, c.per_cu};
   int64_t pairs = 0;
   for (int i = 0; i < count; ++i) pairs += ((pv[i].n + 15) / 16 + 1) / 2;
-  if (pp.phases > 1 && pairs >= kCUs) return launch_main<1, 4, 2, false, true, true>(c1, pp, pv, count, k, m, stream);
+  if (pp.phases > 1 && pairs >= device_cus()) return launch_main<1, 4, 2, false, true, true>(c1, pp, pv, count, k, m, stream);
   return launch_main<1, 4, 2, false, false, true>(c1, pp, pv, count, k, m, stream);
 }
 
@@ -1137,7 +1152,7 @@ static hipError_t launch_nvfp4_group(const mxs_problem_view* pv, int count, int6
     // with several phases a workgroup owns one row block: two row tiles per block when
     // that still leaves a workgroup per CU
     PhasePlan pp2;
-    if (nrb2 >= kCUs && plan_phases(k, m < 16 ? m : 16, 2, c.G, pp2))
+    if (nrb2 >= device_cus() && plan_phases(k, m < 16 ? m : 16, 2, c.G, pp2))
       return launch_main<2, 4, 2, true, false, kTiled>(Config{2, c.G, c.D, c.per_cu}, pp2, pv, count, k, m, stream);
   }
   return launch_main<1, 4, 2, true, false, kTiled>(c, pp, pv, count, k, m, stream);
@@ -1183,20 +1198,5 @@ hipError_t launch_verify_gemm_grouped(const mxs_problem_view* pv, int count, int
   return hipSuccess;
 }
 
-#ifdef MXS_TUNING
-hipError_t launch_verify_gemm_cfg(int R, int G, int D, int per_cu, const mxs_problem_view* pv,
-                                  int count, int64_t k, int64_t m, hipStream_t stream) {
-  return launch_group(Config{R, G, D, per_cu}, pv, count, k, m, stream);
-}
-#endif
 
 }  // namespace mxs
-
-#ifdef MXS_TUNING
-// Tuning builds only (not part of the product library): explicit tile configuration.
-extern "C" int mxs_tune_verify_gemm(const mxs::mxs_problem_view* pv, int count, int64_t k,
-                                    int64_t m, int R, int G, int D, int per_cu, void* stream) {
-  return (int)mxs::launch_verify_gemm_cfg(R, G, D, per_cu, pv, count, k, m,
-                                          static_cast<hipStream_t>(stream));
-}
-#endif
