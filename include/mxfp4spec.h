@@ -22,7 +22,9 @@
  * Conventions for every entry point
  *   - Every data pointer is a DEVICE pointer, allocated and owned by the caller.
  *     The library allocates no memory, keeps no mutable global state and is
- *     safe to call from several host threads.
+ *     safe to call from several host threads. The one exception is
+ *     spec_accept_noalloc, whose workspace is a static device array of the
+ *     library (calls on one GPU share it and must not overlap).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
  *     and runs asynchronously: the caller synchronizes before reading outputs.
  *   - Arrays are row-major and contiguous.
@@ -381,6 +383,32 @@ mxs_status spec_accept(const float* target_logits, const float* draft_logits,
                        int32_t kd, int32_t v, int32_t* out_tokens,
                        int32_t* out_num_accepted, void* workspace, size_t workspace_bytes,
                        int32_t* dev_flags, void* stream);
+
+/*
+ * spec_accept_noalloc — spec_accept with a built-in workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It calls no hipMalloc / hipFree and allocates nothing: the
+ * workspace is a static device array of MXS_NOALLOC_SCRATCH_BYTES in the library, one
+ * copy per GPU, held until the process ends; its address is looked up once per device on
+ * the first call made with that device current. Same rule, arguments (minus the
+ * workspace), outputs and errors as spec_accept, and bit-identical results.
+ *
+ * The array is shared by every call on one GPU and keeps the last call's contents
+ * (which no call depends on: every word a call reads it first writes). Calls that
+ * overlap on one GPU (two host threads, or two streams without ordering between them)
+ * race on it and give undefined results: serialize them, or use spec_accept with a
+ * workspace each.
+ *
+ * Returns MXS_ERR_WORKSPACE when spec_accept_workspace_bytes(b, kd, v) exceeds
+ * MXS_NOALLOC_SCRATCH_BYTES (e.g. b = 64, kd = 4, v = 128256 needs about 0.43 MB; the
+ * limit admits b up to ~590 at that kd and v), before any HIP call; MXS_ERR_DEVICE when
+ * the array's device address cannot be obtained; otherwise as spec_accept.
+ */
+#define MXS_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+mxs_status spec_accept_noalloc(const float* target_logits, const float* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms, int32_t b,
+                               int32_t kd, int32_t v, int32_t* out_tokens,
+                               int32_t* out_num_accepted, int32_t* dev_flags, void* stream);
 
 /*
  * spec_accept_sampled_workspace_bytes — device workspace spec_accept_sampled

@@ -35,7 +35,9 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
            "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled",
-           "nvfp4_verify_gemm_grouped_tiled"]
+           "nvfp4_verify_gemm_grouped_tiled", "spec_accept_noalloc"]
+
+NOALLOC_SCRATCH_BYTES = 4 << 20  # MXS_NOALLOC_SCRATCH_BYTES
 
 
 class GemmProblem(ctypes.Structure):
@@ -77,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_accept.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.spec_accept.restype = ctypes.c_int
+    lib.spec_accept_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.spec_accept_noalloc.restype = ctypes.c_int
     lib.spec_accept_sampled_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_accept_sampled_workspace_bytes.restype = ctypes.c_size_t
     f32 = ctypes.c_float
@@ -265,6 +269,35 @@ def spec_accept(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
     _check(get_lib().spec_accept(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), b, kd, v,
                            _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
                            _ptr(dev_flags), _stream(stream)), "spec_accept")
+    return out_tokens, out_num
+
+
+def spec_accept_noalloc(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor | None,
+                        uniforms: torch.Tensor, out_tokens: torch.Tensor, out_num: torch.Tensor,
+                        dev_flags: torch.Tensor | None = None, stream=None):
+    """spec_accept with the library's built-in workspace (the C call allocates nothing).
+
+    The caller supplies every output: out_tokens int32 [b, kd+1], out_num int32 [b]. Calls on
+    one GPU share the built-in workspace, so they must not overlap (one stream, or ordered).
+    Raises MxsError(MXS_ERR_WORKSPACE) when (b, kd, v) needs more than NOALLOC_SCRATCH_BYTES.
+    """
+    _want(target, torch.float32, "target")
+    b, kd1, v = target.shape
+    kd = kd1 - 1
+    if kd > 0:
+        _want(draft, torch.float32, "draft", (b, kd, v))
+        _want(tokens, torch.int32, "tokens", (b, kd))
+    else:
+        draft = tokens = None
+    _want(uniforms, torch.float32, "uniforms", (b, kd + 1))
+    if out_tokens is None or out_num is None:
+        raise ValueError("spec_accept_noalloc needs caller-supplied out_tokens and out_num")
+    _want(out_tokens, torch.int32, "out_tokens", (b, kd + 1))
+    _want(out_num, torch.int32, "out_num", (b,))
+    _want_flags(dev_flags)
+    _check(get_lib().spec_accept_noalloc(_ptr(target), _ptr(draft), _ptr(tokens), _ptr(uniforms), b, kd, v,
+                                         _ptr(out_tokens), _ptr(out_num), _ptr(dev_flags), _stream(stream)),
+           "spec_accept_noalloc")
     return out_tokens, out_num
 
 

@@ -28,6 +28,8 @@
 // end. Rounding guards: if no crossing is found where the level above
 // placed it, the last positive-weight token of that range is taken, so a
 // zero-weight token is never returned.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -1050,7 +1052,32 @@ __global__ __launch_bounds__(kWThreads) void sample_kernel(
              s_incl, s_fl);
 }
 
+// Built-in workspace of spec_accept_noalloc: a file-scope device array, one copy per GPU
+// for the life of the process. In host code `scratch` names a host-side stand-in, not the
+// device address: every host use goes through the address hipGetSymbolAddress returns.
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
 }  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // once per device, with that device current (two threads racing here store the same address)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled) {
   return layout(b, kd, v, sampled).total;

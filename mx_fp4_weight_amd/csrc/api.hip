@@ -351,6 +351,29 @@ mxs_status spec_accept(const float* target_logits, const float* draft_logits,
                                           vec4, nullptr, static_cast<hipStream_t>(stream)));
 }
 
+mxs_status spec_accept_noalloc(const float* target_logits, const float* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms, int32_t b, int32_t kd,
+                               int32_t v, int32_t* out_tokens, int32_t* out_num_accepted,
+                               int32_t* dev_flags, void* stream) {
+  if (!target_logits || !uniforms || !out_tokens || !out_num_accepted) return MXS_ERR_NULL;
+  if (kd > 0 && (!draft_logits || !draft_tokens)) return MXS_ERR_NULL;
+  if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return MXS_ERR_SHAPE;
+  if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+      !aligned(dev_flags, 4))
+    return MXS_ERR_ALIGN;
+  if (mxs::accept_workspace_bytes(b, kd, v, false) > mxs::kNoAllocScratchBytes) return MXS_ERR_WORKSPACE;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  void* ws = nullptr;
+  if (mxs::noalloc_scratch(&ws) != hipSuccess) return MXS_ERR_DEVICE;
+  const bool vec4 = (v % 4 == 0) && aligned(target_logits, 16) &&
+                    (kd == 0 || aligned(draft_logits, 16));
+  return launched(mxs::launch_spec_accept(target_logits, draft_logits, draft_tokens, uniforms, b,
+                                          kd, v, out_tokens, out_num_accepted, ws, dev_flags,
+                                          vec4, nullptr, static_cast<hipStream_t>(stream)));
+}
+
 mxs_status spec_accept_sampled(const float* target_logits, const float* draft_logits,
                                const int32_t* draft_tokens, const float* uniforms, int32_t b,
                                int32_t kd, int32_t v, float temperature, int32_t top_k, float top_p,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mxfp4spec.h"
+
 namespace mxs {
 
 // One product of a grouped verify GEMM (host-side view).
@@ -74,6 +76,12 @@ hipError_t launch_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t
 hipError_t launch_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8_t* tiled, hipStream_t stream);
 
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
+
+// The built-in workspace of spec_accept_noalloc: a static device array of this many bytes
+// (one per GPU, kept until the process ends). noalloc_scratch returns its device address
+// on the current device, looked up once per device with hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = MXS_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
 
 // sp == nullptr: the plain laws (no transform kernels, the same code as without transforms).
 hipError_t launch_spec_accept(const float* target, const float* draft, const int32_t* tokens,

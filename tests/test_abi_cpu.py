@@ -117,6 +117,34 @@ def test_accept_host_errors():
     assert _a(wsb=need) == mxs.MXS_ERR_DEVICE
 
 
+def _na(t=0x1000, d=0x2000, tok=0x3000, u=0x4000, b=1, kd=4, v=1024, ot=0x5000, on=0x6000, flags=None):
+    f = lambda a: P(a) if a else None
+    return mxs.get_lib().spec_accept_noalloc(f(t), f(d), f(tok), f(u), b, kd, v, f(ot), f(on), f(flags), None)
+
+
+def test_accept_noalloc_host_errors():
+    for kw in [dict(t=0), dict(d=0), dict(tok=0), dict(u=0), dict(ot=0), dict(on=0)]:
+        assert _na(**kw) == mxs.MXS_ERR_NULL
+    assert _na(d=0, tok=0, kd=0) == mxs.MXS_ERR_DEVICE
+    for kw in [dict(b=0), dict(kd=-1), dict(kd=33), dict(v=1), dict(v=(1 << 26) + 1)]:
+        assert _na(**kw) == mxs.MXS_ERR_SHAPE
+    for kw in [dict(t=0x1002), dict(tok=0x3001), dict(ot=0x5002), dict(flags=0x8001)]:
+        assert _na(**kw) == mxs.MXS_ERR_ALIGN
+    # the built-in workspace bounds the size: past it the call is refused before any HIP call
+    lib = mxs.get_lib()
+    assert lib.spec_accept_workspace_bytes(64, 4, 128256) <= mxs.NOALLOC_SCRATCH_BYTES
+    assert _na(b=64, kd=4, v=128256) == mxs.MXS_ERR_DEVICE
+    big = (4096, 8, 131072)
+    assert lib.spec_accept_workspace_bytes(*big) > mxs.NOALLOC_SCRATCH_BYTES
+    assert _na(b=big[0], kd=big[1], v=big[2]) == mxs.MXS_ERR_WORKSPACE
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MXS_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mxs.NOALLOC_SCRATCH_BYTES
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     code = (
         "import mx_fp4_weight_amd as m\n"

@@ -61,3 +61,5 @@ def test_accept_outputs_checked():
         mxs.spec_accept(t, d, tok, u, out_num=z((b,), torch.int64))
     with pytest.raises(ValueError):
         mxs.spec_accept_sampled(t, d, tok, u, out_num=z((b + 1,), torch.int32))
+    with pytest.raises(ValueError):
+        mxs.spec_accept_noalloc(t, d, tok, u, z((b, kd + 1), torch.int32), z((1,), torch.int32))
