@@ -143,12 +143,125 @@ def summarize_pmc(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
     print(json.dumps(summary, indent=1))
 
 
-def cpu_baseline(seconds_budget=15.0):
+def _short_kernel_name(name):
+    return name.replace("void ", "").replace("mxs::(anonymous namespace)::", "").split("(")[0]
+
+
+def _label(name, wgs, lds, grid_y):
+    """What a library dispatch of the headline workload is, from its kernel, workgroup count and LDS
+    (tiled 8B-class layer at T = 5: q|k|v 384 workgroups, o and down 256 with o's smaller activation
+    tile, gate|up 512)."""
+    if "quantize_act" in name:
+        return "activation quantization (W4A8 / W4A4)"
+    if "tile_codes" in name or "tile_scales" in name or "quantize" in name:
+        return "weight prep (one-off, untimed)"
+    if "stream_read" in name:
+        return "read-stream ceiling"
+    if any(a in name for a in ("stats_kernel", "decide_kernel", "sample_kernel", "sel_")):
+        return "spec_accept"
+    if "gemm_skinny" in name:
+        return {384: "q|k|v grouped", 512: "gate|up grouped",
+                256: "o and down (256 workgroups each)"}.get(wgs, f"{wgs} workgroups")
+    if "gemm_dense" in name:
+        return "bf16 dense product" + (" (tiled weights)" if ", true>" in name else " (row layout)")
+    if "gemm_act" in name:
+        fmt = "W4A8" if "<5, 0," in name else "W4A4"
+        return fmt + (" (tiled weights)" if ", true>" in name else " (row layout)")
+    return ""
+
+
+def summarize_trace(trace_dir, out_path, title, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run: per library kernel and launch
+    shape (workgroups, LDS bytes), dispatches and mean / median / min duration, then the --stats
+    table of the library kernels."""
+    import csv
+    import glob
+    import statistics as st
+    tr = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not tr:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    groups = {}
+    for r in csv.DictReader(open(tr[0])):
+        if "mxs::" not in r["Kernel_Name"]:
+            continue
+        n = _short_kernel_name(r["Kernel_Name"])
+        wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        key = (n, wgs, int(r["Grid_Size_Y"]), int(r["LDS_Block_Size"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = [f"# Kernel trace: {title}", "", "Command (from /tmp, TMPDIR=/tmp):", "", "```", command, "```", "",
+             "Durations from the kernel trace (start to end of each dispatch, µs).", "",
+             "| kernel | workgroups x grid y | LDS bytes | what | dispatches | mean µs | median µs | min µs |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (n, wgs, gy, lds), v in sorted(groups.items()):
+        lines.append(f"| `{n}` | {wgs} x {gy} | {lds} | {_label(n, wgs, lds, gy)} | {len(v)} | {st.mean(v):.2f} | "
+                     f"{st.median(v):.2f} | {min(v):.2f} |")
+    ks = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if ks:
+        lines += ["", "rocprofv3 --stats summary (library kernels):", "",
+                  "| Name | Calls | AverageNs | MinNs | MaxNs |", "|---|---|---|---|---|"]
+        for r in csv.DictReader(open(ks[0])):
+            if "mxs::" in r["Name"]:
+                lines.append(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                             f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_busy(pmc_dir, out_path, title, command):
+    """Markdown summary of a rocprofv3 --pmc run of VALUBusy / MfmaUtil (and any other counters in
+    it): the mean per dispatch of each counter, per library kernel and launch shape."""
+    import csv
+    import glob
+    import statistics as st
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter collection under {pmc_dir}")
+    vals, counters = {}, set()
+    for r in csv.DictReader(open(files[0])):
+        if "mxs::" not in r["Kernel_Name"]:
+            continue
+        n = _short_kernel_name(r["Kernel_Name"])
+        wgs = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+        key = (n, wgs, int(r["LDS_Block_Size"]))
+        counters.add(r["Counter_Name"])
+        vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cs = sorted(counters)
+    lines = [f"# Counters: {title}", "", "Command (from /tmp, TMPDIR=/tmp):", "", "```", command, "```", "",
+             "Mean per dispatch. VALUBusy = 100 x SQ_ACTIVE_INST_VALU / CU_NUM / GRBM_GUI_ACTIVE (share of "
+             "the kernel's GPU-active time the vector ALUs issue); MfmaUtil = 100 x SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(GRBM_GUI_ACTIVE x SIMD_NUM) (share of SIMD cycles the matrix cores are busy).", "",
+             "| kernel | workgroups | LDS bytes | what | dispatches | " + " | ".join(cs) + " |",
+             "|---|---|---|---|---|" + "---|" * len(cs)]
+    for (n, wgs, lds), d in sorted(vals.items()):
+        cnt = max(len(v) for v in d.values())
+        cells = " | ".join(f"{st.mean(d[c]):.2f}" if c in d else "" for c in cs)
+        lines.append(f"| `{n}` | {wgs} | {lds} | {_label(n, wgs, lds, 1)} | {cnt} | {cells} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(seconds_budget=20.0):
     """The oracle (fp64 NumPy) on the host cores, on a bounded sample of the same workload.
 
     Sample: rows [0, 512) of each of the 7 layer matrices (oracle-quantized from
-    the shared generator), verify GEMM at T = 5, repeated; plus the oracle
-    acceptance loop on sequences of the same spec_accept configuration.
+    the shared generator), verify GEMM at T = 5, repeated with the BLAS on all
+    host threads and on one; the oracle quantizer (one thread) on the same
+    rows; plus the oracle acceptance loop (one thread) on sequences of the
+    same spec_accept configuration.
     """
     import numpy as np
     import synth
@@ -161,23 +274,42 @@ def cpu_baseline(seconds_budget=15.0):
         threadpoolctl = None
 
     rows = 512
-    mats = []
+    mats, wts = [], []
     for i, (name, n, k) in enumerate(LAYER):
         w = synth.weights(2, 1000 + i, n, k, row_start=0, row_stop=rows)
         c, s, _ = omx.quantize(w)
         x = synth.activations(2, 1000 + i, T, k)
         mats.append((c, s, rows, k, x))
+        wts.append(w)
     ogemm.verify_gemm(*mats[0])  # warm BLAS
     byts = sum(gemm_alg_bytes(rows, k, T) for (_, _, _, k, _) in mats)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
+
+    def timed(fn, budget):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 > budget:
+                return reps, time.perf_counter() - t0
+
+    def gemm_pass():
         for m in mats:
             ogemm.verify_gemm(*m)
-        reps += 1
-        if time.perf_counter() - t0 > seconds_budget * 0.6:
-            break
-    t_gemm = time.perf_counter() - t0
+
+    reps, t_gemm = timed(gemm_pass, seconds_budget * 0.35)
+    threads = None
+    if threadpoolctl is not None:
+        info = threadpoolctl.threadpool_info()
+        if info:
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+        with threadpoolctl.threadpool_limits(1):
+            reps1, t_gemm1 = timed(gemm_pass, seconds_budget * 0.2)
+            qreps, t_q = timed(lambda: [omx.quantize(w) for w in wts], seconds_budget * 0.15)
+    else:
+        reps1, t_gemm1 = reps, t_gemm
+        qreps, t_q = timed(lambda: [omx.quantize(w) for w in wts], seconds_budget * 0.15)
+    q_bytes = sum(w.nbytes for w in wts)
     tgt, dft, tok, u = synth.accept_batch(2, 4, KD, V, 3.0, 1.0, seq0=500)
     t0 = time.perf_counter()
     seqs = 0
@@ -185,25 +317,88 @@ def cpu_baseline(seconds_budget=15.0):
         for b in range(4):
             oacc.step(tgt[b], dft[b], tok[b], u[b])
         seqs += 4
-        if time.perf_counter() - t0 > seconds_budget * 0.4:
+        if time.perf_counter() - t0 > seconds_budget * 0.3:
             break
     t_acc = time.perf_counter() - t0
-    threads = None
-    if threadpoolctl is not None:
-        info = threadpoolctl.threadpool_info()
-        if info:
-            threads = max(int(i.get("num_threads", 1)) for i in info)
     return {
         "value": byts * reps / t_gemm / 1e9,
         "unit": "GB/s",
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
         "sample": f"verify GEMM at T=5 on rows [0,{rows}) of each of the 7 layer matrices, "
-                  f"{reps} passes in {t_gemm:.1f} s (fp64 NumPy BLAS); acceptance loop on "
-                  f"{seqs} sequences (K=4, V=128256) in {t_acc:.1f} s",
+                  f"{reps} passes in {t_gemm:.1f} s (fp64 NumPy BLAS, all threads); the same at 1 thread "
+                  f"({reps1} passes in {t_gemm1:.1f} s); oracle quantizer on those rows' fp32 weights "
+                  f"(1 thread, {qreps} passes in {t_q:.1f} s); acceptance loop on {seqs} sequences "
+                  f"(K=4, V=128256, 1 thread) in {t_acc:.1f} s",
+        "gemm_GBps_1_thread": byts * reps1 / t_gemm1 / 1e9,
+        "quantize_MBps_fp32_in_1_thread": q_bytes * qreps / t_q / 1e6,
         "spec_accept_positions_per_s": seqs * (KD + 1) / t_acc,
         "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
+
+
+def gpu_clocks():
+    """Current shader (sclk), memory (mclk) and fabric (fclk) clock levels of the GPU, as the
+    amdgpu driver reports them (recorded, not locked). From sysfs; rocm-smi otherwise."""
+    import glob
+    out = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(card, name)) as f:
+                    cur = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in f if ln.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[name[-4:]] = cur[0]
+        if out:
+            out["source"] = card + "/pp_dpm_*"
+            return out
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout)
+        card = next(iter(d.values()))
+        out = {k: v for k, v in card.items() if "clock" in k.lower()}
+        out["source"] = "rocm-smi --showclocks"
+        return out
+    except Exception as e:  # clocks are context only: never fail the bench for them
+        return {"source": None, "error": repr(e)[:200]}
+
+
+STREAM_BYTES = 4 << 30  # read-ceiling buffer: 16x the 256 MB Infinity Cache, so the reads come from HBM
+
+
+def stream_ceiling(torch, mxs, reps=20):
+    """The measured read ceiling: mxs_stream_read over a 4 GiB buffer (cold: far larger than the
+    caches), each call between its own HIP events on the current stream; GB/s median, p10, p90."""
+    buf = torch.ones((STREAM_BYTES // 4,), dtype=torch.int32, device="cuda")
+    sink = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    for _ in range(3):
+        mxs.stream_read(buf, sink, stream=st)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(st)
+    for r in range(reps):
+        mxs.stream_read(buf, sink, stream=st)
+        ev[r + 1].record(st)
+    torch.cuda.synchronize()
+    gbps = [STREAM_BYTES / (ev[r].elapsed_time(ev[r + 1]) * 1e-3) / 1e9 for r in range(reps)]
+    del buf
+    q = pctl(gbps)
+    return {"GBps_median": round(q["median"], 1), "GBps_p10": round(q["p10"], 1), "GBps_p90": round(q["p90"], 1),
+            "frac_of_hbm_peak": round(q["median"] / HBM_PEAK_GBPS, 4), "bytes_per_call": STREAM_BYTES,
+            "calls": reps, "kernel": "stream_read_kernel (mxs_stream_read: 16-byte non-temporal loads, 8 per lane "
+                                     "in flight, two 256-thread workgroups per CU)"}
+
+
+def pctl(vals):
+    """median, p10 and p90 of a list (nearest-rank)."""
+    v = sorted(vals)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "n": len(v)}
 
 
 # ---------------------------------------------------------------------------
@@ -648,9 +843,19 @@ def main():
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs into the committed traffic file")
+    ap.add_argument("--summarize-busy", nargs=4, metavar=("PMC_DIR", "OUT_MD", "TITLE", "COMMAND"),
+                    help="summarize a rocprofv3 --pmc run of VALUBusy / MfmaUtil into a markdown table")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT_MD", "TITLE", "COMMAND"),
+                    help="summarize a rocprofv3 --kernel-trace --stats run into a markdown table")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_busy:
+        summarize_busy(*args.summarize_busy)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -795,23 +1000,33 @@ def main():
         for _ in range(n_layers):
             accept_only()
     torch.cuda.synchronize()
-    reps = max(1, args.steps // n_layers)
+    reps = max(20, args.steps // n_layers)
     mk = lambda: torch.cuda.Event(enable_timing=True)
 
-    def time_graph(g):
+    def time_graph(g, dist=None):
+        """Mean ms per launch over `reps` replays of g (each runs the launch on every pool layer);
+        each replay is bracketed by its own events, so the per-replay means (ms per launch) go to
+        `dist` for the median and p10 / p90."""
         g.replay()
         torch.cuda.synchronize()
         st = torch.cuda.current_stream()
-        e0, e1 = mk(), mk()
-        e0.record(st)
-        for _ in range(reps):
+        ev = [mk() for _ in range(reps + 1)]
+        ev[0].record(st)
+        for r in range(reps):
             g.replay()
-        e1.record(st)
+            ev[r + 1].record(st)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * n_layers)  # ms per launch
+        per = [ev[r].elapsed_time(ev[r + 1]) / n_layers for r in range(reps)]
+        if dist is not None:
+            dist.extend(per)
+        return ev[0].elapsed_time(ev[reps]) / (reps * n_layers)  # ms per launch
 
-    launch_ms = [time_graph(g) for g in type_graphs]
+    clocks_before = gpu_clocks()
+    stream = stream_ceiling(torch, mxs)
+    launch_dist = [[] for _ in type_graphs]
+    launch_ms = [time_graph(g, d) for g, d in zip(type_graphs, launch_dist)]
     acc_ms_mean = time_graph(acc_graph)
+    clocks_after = gpu_clocks()
     del type_graphs
     # the other layout's launches for comparison (not in the single-workload runs that
     # profiles and counters are taken from)
@@ -835,9 +1050,15 @@ def main():
     avg_launch_bytes = step_gemm_bytes / len(LAUNCHES)
     achieved = avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
     launch_bytes = [sum(gemm_alg_bytes(LAYER[i][1], LAYER[i][2], T) for i in idx) for _, idx in LAUNCHES]
-    per_shape = {name: {"GBps": round(b / (launch_ms[j] * 1e-3) / 1e9, 1),
-                        "us": round(launch_ms[j] * 1e3, 2)}
-                 for j, ((name, _), b) in enumerate(zip(LAUNCHES, launch_bytes))}
+    per_shape = {}
+    for j, ((name, _), b) in enumerate(zip(LAUNCHES, launch_bytes)):
+        q = pctl(launch_dist[j])
+        per_shape[name] = {"GBps": round(b / (launch_ms[j] * 1e-3) / 1e9, 1), "us": round(launch_ms[j] * 1e3, 2),
+                           "us_median": round(q["median"] * 1e3, 2), "us_p10": round(q["p10"] * 1e3, 2),
+                           "us_p90": round(q["p90"] * 1e3, 2), "replays": q["n"]}
+    # the per-replay distribution of the four-launch average (one replay of each launch type)
+    avg_dist = [sum(t) / len(t) for t in zip(*launch_dist)]
+    avg_q = pctl(avg_dist)
     traffic = load_traffic()
     result = {
         "metric": "MX-FP4 verify-GEMM HBM GB/s (% of peak) at T=5; spec_accept positions/s",
@@ -880,13 +1101,21 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac_of_stream_ceiling": round(achieved / stream["GBps_median"], 4),
             "traffic": traffic,
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+            "avg_launch_us_median": round(avg_q["median"] * 1e3, 3),
+            "avg_launch_us_p10": round(avg_q["p10"] * 1e3, 3),
+            "avg_launch_us_p90": round(avg_q["p90"] * 1e3, 3),
+            "replays_per_launch_type": avg_q["n"],
             "avg_launch_alg_bytes": avg_launch_bytes,
             "launches_timed": int(launches),
             "timing": "HIP events around graph replays that run one launch type on every pool "
-                      "layer back to back; average over the four launch types of a layer",
+                      "layer back to back; average over the four launch types of a layer (mean over "
+                      "all replays; median / p10 / p90 over the per-replay averages)",
         },
+        "gpu_clocks": {"before": clocks_before, "after": clocks_after},
+        "stream_ceiling": stream,
     }
     if not args.no_extra and not args.only:
         for key, fn in extras:

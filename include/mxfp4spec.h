@@ -459,6 +459,21 @@ mxs_status spec_accept_sampled(const float* target_logits, const float* draft_lo
                                int32_t* out_num_accepted, void* workspace,
                                size_t workspace_bytes, int32_t* dev_flags, void* stream);
 
+/*
+ * mxs_stream_read — read `bytes` of device memory once and discard them: the measured
+ * ceiling of the weight stream. A verification step that streams all weights is bounded by
+ * Q <= BW / W [M11 §1]; this plain read-only kernel measures the BW one kernel draws from
+ * HBM on the current device, against which the verify GEMM's achieved bandwidth is read
+ * (timing is the caller's: events around the call on `stream`).
+ *
+ * buf    device memory, 16-byte aligned, read only.
+ * bytes  >= 16, a multiple of 16.
+ * sink   one device uint32, 4-byte aligned: OR-ed with 1 only if the XOR of all words read
+ *        equals 0x9E3779B9 (it keeps the loads live; its value carries no meaning).
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status mxs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
            "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled",
-           "nvfp4_verify_gemm_grouped_tiled", "spec_accept_noalloc"]
+           "nvfp4_verify_gemm_grouped_tiled", "spec_accept_noalloc", "mxs_stream_read"]
 
 NOALLOC_SCRATCH_BYTES = 4 << 20  # MXS_NOALLOC_SCRATCH_BYTES
 
@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_accept.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.spec_accept.restype = ctypes.c_int
+    lib.mxs_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.mxs_stream_read.restype = ctypes.c_int
     lib.spec_accept_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     lib.spec_accept_noalloc.restype = ctypes.c_int
     lib.spec_accept_sampled_workspace_bytes.argtypes = [i32, i32, i32]
@@ -226,6 +228,16 @@ def mxfp4_verify_gemm_grouped(items, ys=None, stream=None):
     _check(get_lib().mxfp4_verify_gemm_grouped(arr, len(items), k, m, _stream(stream)),
            "mxfp4_verify_gemm_grouped")
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """One plain read of a contiguous device tensor (its byte size a multiple of 16): the measured
+    read ceiling against which the verify GEMM's bandwidth is read. sink: int32 [1] device word."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA/HIP tensor")
+    _want(sink, torch.int32, "sink", (1,))
+    _check(get_lib().mxs_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "mxs_stream_read")
 
 
 def spec_accept_workspace_bytes(b: int, kd: int, v: int) -> int:

@@ -319,6 +319,15 @@ mxs_status mxfp4_verify_gemm_grouped_tiled(const mxs_gemm_problem* problems, int
   return MXS_OK;
 }
 
+mxs_status mxs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return MXS_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return MXS_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return MXS_ERR_ALIGN;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  return launched(mxs::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {
   if (b < 1 || b > 65535 || kd < 0 || kd > 32 || v < 2 || v > (1 << 26)) return 0;
   return mxs::accept_workspace_bytes(b, kd, v, false);

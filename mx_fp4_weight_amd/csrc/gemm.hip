@@ -149,11 +149,16 @@ struct Group {
 // the product's workgroups) and walks them phase by phase (phase 0 of both, then phase 1 of both, ...), with a
 // second set of accumulators, so a phase's activations are staged once for two row
 // blocks and every workgroup is resident at once.
-template <int R, int G, int D, bool kNv, bool kPair = false, bool kTiled = false>
+// kStream: the weight codes and scales are loaded non-temporally (the cache policy of a stream
+// read once: measured 3-8% faster per launch than the default policy). Used when every weight is
+// read by one workgroup only (m <= 16: one position tile); with several position tiles the
+// workgroups of a row block read the same weights and the default policy keeps them in L2.
+template <int R, int G, int D, bool kNv, bool kPair = false, bool kTiled = false, bool kStream = false>
 __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Group grp, int k, int m,
                                                                          int nsub, int phases,
                                                                          int ngroups_p, int nred) {
   static_assert(!kTiled || G == 4, "tiled weights: one 512-k window per unit");
+  constexpr int kWAux = kStream ? 2 : 0;  // buffer-load cache policy of the weight loads (2: nt)
   extern __shared__ u32x4 smem[];
   int pi = 0;
   while (pi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[pi + 1]) ++pi;
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
         const uint32_t off = !ok     ? kOutOfRange
                              : kTiled ? (uint32_t)(16 * i) * row_bytes + (uint32_t)(g0 + j) * 1024u + (uint32_t)lane * 16u
                                       : (uint32_t)(16 * i + r) * row_bytes + (uint32_t)blk * 16;
-        b.c[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
+        b.c[i][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, kWAux));
       }
     }
 #pragma unroll
@@ -277,16 +282,16 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
           // window grp0 / 4, unit = the row's place in its 128-row tile
           const uint32_t off =
               ok ? (uint32_t)(grp0 >> 2) * 2048u + (uint32_t)((rowc & 127) + 16 * i + r) * 16u : kOutOfRange;
-          b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+          b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, kWAux));
         } else if constexpr (kNv) {
           // 8 scale bytes per group: two 16-byte loads for 4 groups
           const uint32_t off = ok ? (uint32_t)(16 * i + r) * srow + (uint32_t)grp0 * 8 : kOutOfRange;
-          b.s[i][2 * q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+          b.s[i][2 * q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, kWAux));
           b.s[i][2 * q + 1] =
-              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, ok ? off + 16u : kOutOfRange, 0, 0));
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, ok ? off + 16u : kOutOfRange, 0, kWAux));
         } else {
           const uint32_t off = ok ? (uint32_t)(16 * i + r) * srow + (uint32_t)grp0 * 4 : kOutOfRange;
-          b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+          b.s[i][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, kWAux));
         }
       }
     }
@@ -819,22 +824,6 @@ constexpr size_t kMaxLds = 160 * 1024;
 constexpr int64_t kDenseMinM = 32;  // above this many activation rows the dense kernel runs
 constexpr int kMaxDevices = 64;
 
-// Compute units of the current device (256 on MI355X), read once per device: the
-// persistent grids are sized as resident workgroups per CU times this count.
-int device_cus() {
-  static std::atomic<int> cus[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < kMaxDevices) {
-    const int c = cus[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int c = 0;
-  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-  if (dev < kMaxDevices) cus[dev].store(c, std::memory_order_relaxed);
-  return c;
-}
-
 // Raise a kernel's dynamic-LDS limit once per device.
 template <typename F>
 hipError_t allow_lds(F* kernel, std::atomic<bool>* done) {
@@ -898,11 +887,11 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp, int p
   return false;
 }
 
-template <int R, int G, int D, bool kNv = false, bool kPair = false, bool kTiled = false>
-hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
-                       int64_t k, int64_t m, hipStream_t stream) {
+template <int R, int G, int D, bool kNv, bool kPair, bool kTiled, bool kStream>
+hipError_t launch_main_k(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
+                         int64_t k, int64_t m, hipStream_t stream) {
   static std::atomic<bool> done[kMaxDevices];
-  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv, kPair, kTiled>, done);
+  hipError_t e = allow_lds(&gemm_skinny_kernel<R, G, D, kNv, kPair, kTiled, kStream>, done);
   if (e != hipSuccess) return e;
   Group grp{};
   grp.count = count;
@@ -977,10 +966,18 @@ hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_v
     start += (int)share[i];
   }
   grp.wg_start[count] = start;
-  gemm_skinny_kernel<R, G, D, kNv, kPair, kTiled><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)),
-                                                   dim3(pp.waves * kWave), pp.lds, stream>>>(
+  gemm_skinny_kernel<R, G, D, kNv, kPair, kTiled, kStream><<<dim3((unsigned)start, (unsigned)((m + 15) / 16)),
+                                                            dim3(pp.waves * kWave), pp.lds, stream>>>(
       grp, (int)k, (int)m, pp.nsub, pp.phases, pp.ngroups_p, pp.nred);
   return hipGetLastError();
+}
+
+// Non-temporal weight loads when one position tile reads every weight once (m <= 16).
+template <int R, int G, int D, bool kNv = false, bool kPair = false, bool kTiled = false>
+hipError_t launch_main(const Config& c, const PhasePlan& pp, const mxs_problem_view* pv, int count,
+                       int64_t k, int64_t m, hipStream_t stream) {
+  if (m <= 16) return launch_main_k<R, G, D, kNv, kPair, kTiled, true>(c, pp, pv, count, k, m, stream);
+  return launch_main_k<R, G, D, kNv, kPair, kTiled, false>(c, pp, pv, count, k, m, stream);
 }
 
 template <int R, int S>
@@ -1110,6 +1107,22 @@ Config choose(int64_t n, int64_t k) {
 }
 
 }  // namespace
+
+// Compute units of the current device (256 on MI355X), read once per device: the persistent
+// grids are sized as resident workgroups per CU times this count.
+int device_cus() {
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+  if (dev < kMaxDevices) cus[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
 
 hipError_t launch_verify_gemm(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                               const uint16_t* x, int64_t m, float* y, hipStream_t stream) {

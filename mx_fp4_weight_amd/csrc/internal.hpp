@@ -9,6 +9,12 @@
 
 namespace mxs {
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Plain read of bytes (a multiple of 16) at buf, 16-byte aligned: the measured read ceiling.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // One product of a grouped verify GEMM (host-side view).
 struct mxs_problem_view {
   const uint8_t* codes;

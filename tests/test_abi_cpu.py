@@ -145,6 +145,16 @@ def test_noalloc_scratch_size_matches_header():
     assert m and int(m.group(1)) << int(m.group(2)) == mxs.NOALLOC_SCRATCH_BYTES
 
 
+def test_stream_read_host_errors():
+    lib = mxs.get_lib()
+    f = lambda a: P(a) if a else None
+    sr = lambda buf=0x1000, nb=1 << 20, sink=0x2000: lib.mxs_stream_read(f(buf), nb, f(sink), None)
+    assert sr(buf=0) == mxs.MXS_ERR_NULL and sr(sink=0) == mxs.MXS_ERR_NULL
+    assert sr(nb=0) == mxs.MXS_ERR_SHAPE and sr(nb=8) == mxs.MXS_ERR_SHAPE and sr(nb=(1 << 20) + 4) == mxs.MXS_ERR_SHAPE
+    assert sr(buf=0x1008) == mxs.MXS_ERR_ALIGN and sr(sink=0x2002) == mxs.MXS_ERR_ALIGN
+    assert sr() == mxs.MXS_ERR_DEVICE
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     code = (
         "import mx_fp4_weight_amd as m\n"
