@@ -739,8 +739,10 @@ __global__ __launch_bounds__(kThreads) void sel_pass_kernel(
   }
   // arrival. The additions are device-scope atomics, performed where every CU reads them
   // with device-scope loads; each wave waits until its own have completed, so the count
-  // cannot run ahead of them (no L2 write-back is needed: no plain store is shared).
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // cannot run ahead of them. No plain store is shared, so no L2 write-back is needed: a
+  // release / acquire fence pair here (an L2 write-back and invalidation in every
+  // workgroup) measured 0.7 -> 10.7 ms for top-k + top-p at B = 64.
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   __syncthreads();
   if (tid == 0) {
     const uint32_t before = __hip_atomic_fetch_add(&sb.arrive[rowg], 1u, __ATOMIC_RELAXED,
