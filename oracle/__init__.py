@@ -14,6 +14,12 @@ the source pages:
                       supplied uniforms.
 * ``oracle.expect`` — closed forms used as pins (overlap mass, expected tokens
                       per cycle).
+* ``oracle.tree``   — verification of a tree of drafts: siblings tried in
+                      order against the running residual law, final draw
+                      from the last law (the linear rule for a chain).
+* ``oracle.kvcache`` — MX-FP4 KV cache codec: per-token head vectors coded in
+                      32-element blocks along the head dimension, written at
+                      cache slots.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product library must never call it:
@@ -24,4 +30,4 @@ Every function is pinned by a CPU test against facts the pages or mathematics
 fix (printed worked examples, the value grid, closed forms, brute force on tiny
 inputs); none is "parity unpinned".
 """
-from . import mx, gemm, accept, expect  # noqa: F401
+from . import mx, gemm, accept, expect, tree, kvcache  # noqa: F401

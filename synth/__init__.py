@@ -156,3 +156,34 @@ def pack_mask(mask) -> np.ndarray:
     pad[..., :v] = mask
     bits = pad.reshape(mask.shape[:-1] + (w, 32)).astype(np.uint64)
     return (bits << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
+
+
+def tree_batch(config: int, b: int, parent, v: int, base_sigma: float, noise_sigma: float, seq0: int = 0):
+    """Inputs of b verification cycles over one tree of N = len(parent) draft nodes.
+
+    Rows 0..N of each sequence are the laws of the root's history (row 0) and of the history
+    ending in node i (row i + 1). Base logits are drawn for every row; the draft rows are the
+    base and the target rows base + N(0, noise_sigma). Node i's token is drawn from the draft
+    row of its parent (row parent[i] + 1) by the Gumbel-max trick, independently for every
+    node (siblings are independent draws, with replacement).
+
+    Returns target, draft [b, N+1, v] fp32, tokens [b, N] int32, u [b, N+1] fp32.
+    """
+    parent = [int(p) for p in parent]
+    n = len(parent)
+    tgt = np.empty((b, n + 1, v), dtype=np.float32)
+    dft = np.empty((b, n + 1, v), dtype=np.float32)
+    tok = np.empty((b, n), dtype=np.int32)
+    uni = np.empty((b, n + 1), dtype=np.float32)
+    for i in range(b):
+        s = seq0 + i
+        base = rng(config, ROLE_BASE, s).standard_normal((n + 1, v), dtype=np.float32) * np.float32(base_sigma)
+        noise = rng(config, ROLE_NOISE, s).standard_normal((n + 1, v), dtype=np.float32)
+        tgt[i] = base + noise * np.float32(noise_sigma)
+        dft[i] = base
+        if n:
+            g = rng(config, ROLE_DRAFT, s).gumbel(size=(n, v))
+            for c in range(n):
+                tok[i, c] = int(np.argmax(base[parent[c] + 1].astype(np.float64) + g[c]))
+        uni[i] = rng(config, ROLE_U, s).random(n + 1, dtype=np.float32)
+    return tgt, dft, tok, uni
