@@ -460,6 +460,77 @@ mxs_status spec_accept_sampled(const float* target_logits, const float* draft_lo
                                size_t workspace_bytes, int32_t* dev_flags, void* stream);
 
 /*
+ * spec_accept_tree_workspace_bytes — device workspace spec_accept_tree needs for this tree
+ * (parent: HOST array of `nodes` entries, as spec_accept_tree takes it), b sequences and
+ * vocabulary v. Returns 0 when the sizes or the tree are out of range.
+ */
+size_t spec_accept_tree_workspace_bytes(const int32_t* parent, int32_t nodes, int32_t b, int32_t v);
+
+/*
+ * spec_accept_tree — one verification cycle over a tree of draft tokens for each of b
+ * sequences [M11 §4, applied at every node; §8: a tree verified by typical acceptance loses
+ * §4's guarantee, so this rule keeps §4's]. The tree is shared by the sequences; node i has
+ * parent parent[i] (-1 = the root, else a node before i) and draft token draft_tokens[s][i],
+ * drawn by the caller from the draft law of its parent's history, siblings independently.
+ *
+ * Laws: row 0 of target_logits / draft_logits is the root's history, row i + 1 the history
+ * ending in node i (softmax of the fp32 logits, temperature 1; -inf allowed). At the current
+ * node (the root first), with p = its target law and q = its draft law, the children are tried
+ * in index order: child j is accepted iff u_j < min(1, L_j(x_j) / q(x_j)), with L_1 = p and,
+ * after each rejection, L_{j+1} = norm((L_j - q)+) (0 when q(x_j) = 0: MXS_FLAG_Q_ZERO; 0 when
+ * x_j is outside [0, v): MXS_FLAG_TOKEN_RANGE); an accepted child becomes the current node.
+ * When every child is rejected, or the node is a leaf, the final token is drawn from the
+ * current law by inverse CDF on u[N]: t* = min{t : u * Z < C_t} over the law's prefix sums
+ * (the last positive token if rounding leaves none). A residual with no mass left (rounding)
+ * raises MXS_FLAG_RESIDUAL_ZERO and the draw uses the law before that try. A chain (one
+ * child per node) is spec_accept's rule. A sequence with a NaN / +inf logit or an all -inf
+ * row anywhere in its tree is refused: MXS_FLAG_NONFINITE, n = 0, all outputs -1.
+ * Probabilities and prefix sums are fp64.
+ *
+ * parent          HOST [nodes] int32, read during the call; nodes <= 64, at most 16 children
+ *                 per node (else MXS_ERR_VALUE). D below = the tree's depth (nodes on its
+ *                 longest root-to-leaf path).
+ * target_logits   [b, nodes+1, v] fp32.  draft_logits  [b, nodes+1, v] fp32 (leaf rows are
+ *                 examined for validity only).
+ * draft_tokens    [b, nodes] int32 (may be NULL when nodes == 0).
+ * uniforms        [b, nodes+1] fp32 in [0, 1): u[i] for node i's test, u[nodes] for the draw.
+ * b, v            1 <= b <= 65535, 2 <= v <= 2^26.
+ * out_tokens      [b, D+1] int32: the accepted path's tokens, then the final token, then -1.
+ * out_nodes       [b, D] int32: the accepted path's node indices, then -1 (may be NULL when
+ *                 nodes == 0).
+ * out_num_accepted[b] int32: accepted drafts n (the path length).
+ * workspace       spec_accept_tree_workspace_bytes(parent, nodes, b, v) bytes, 16-byte
+ *                 aligned; its contents on entry do not matter.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_VALUE (the tree), MXS_ERR_ALIGN,
+ * MXS_ERR_WORKSPACE.
+ */
+mxs_status spec_accept_tree(const float* target_logits, const float* draft_logits, const int32_t* parent,
+                            int32_t nodes, const int32_t* draft_tokens, const float* uniforms, int32_t b,
+                            int32_t v, int32_t* out_tokens, int32_t* out_nodes, int32_t* out_num_accepted,
+                            void* workspace, size_t workspace_bytes, int32_t* dev_flags, void* stream);
+
+/*
+ * mxfp4_kv_append — write t tokens' key (or value) vectors into an MX-FP4 KV cache [NEWS,
+ * "Microscaling FP4 (MX-FP4) Integration": the KV cache tensors are held in 4-bit MX
+ * values with an E8M0 scale per 32 elements, the FP4 KV cache pool of its pipeline figure].
+ * The cache is [capacity, heads, d] coded as the weights are (mxfp4_quantize's rule and
+ * layout with row = slot * heads + head): 32-element blocks run along d inside one token's
+ * one head, so appending a token codes only its own blocks and never touches other entries.
+ * Token i's vectors go to entry slots[i].
+ *
+ * kv        [t, heads, d] bf16 bit patterns, 16-byte aligned.
+ * t, heads  >= 1; d >= 32, d % 32 == 0; capacity >= 1 (entries of the cache).
+ * slots     [t] int32 device array: the cache entry of each token. A slot outside
+ *           [0, capacity) writes nothing and raises MXS_FLAG_TOKEN_RANGE.
+ * codes     [capacity, heads, d/2] bytes (low nibble = even element), 4-byte aligned.
+ * scales    [capacity, heads, d/32] E8M0 bytes.
+ * A block holding a NaN or infinity gets scale 0xFF and codes 0 and raises
+ * MXS_FLAG_NONFINITE. Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_ALIGN.
+ */
+mxs_status mxfp4_kv_append(const uint16_t* kv, int64_t t, int64_t heads, int64_t d, const int32_t* slots,
+                           int64_t capacity, uint8_t* codes, uint8_t* scales, int32_t* dev_flags, void* stream);
+
+/*
  * mxs_stream_read — read `bytes` of device memory once and discard them: the measured
  * ceiling of the weight stream. A verification step that streams all weights is bounded by
  * Q <= BW / W [M11 §1]; this plain read-only kernel measures the BW one kernel draws from

@@ -35,7 +35,8 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
            "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled",
-           "nvfp4_verify_gemm_grouped_tiled", "spec_accept_noalloc", "mxs_stream_read"]
+           "nvfp4_verify_gemm_grouped_tiled", "spec_accept_noalloc", "mxs_stream_read", "mxfp4_kv_append",
+           "spec_accept_tree_workspace_bytes", "spec_accept_tree"]
 
 NOALLOC_SCRATCH_BYTES = 4 << 20  # MXS_NOALLOC_SCRATCH_BYTES
 
@@ -79,6 +80,13 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_accept.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.spec_accept.restype = ctypes.c_int
+    lib.spec_accept_tree_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int32), i32, i32, i32]
+    lib.spec_accept_tree_workspace_bytes.restype = ctypes.c_size_t
+    lib.spec_accept_tree.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32), i32, vp, vp, i32, i32, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp, vp]
+    lib.spec_accept_tree.restype = ctypes.c_int
+    lib.mxfp4_kv_append.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
+    lib.mxfp4_kv_append.restype = ctypes.c_int
     lib.mxs_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.mxs_stream_read.restype = ctypes.c_int
     lib.spec_accept_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
@@ -228,6 +236,91 @@ def mxfp4_verify_gemm_grouped(items, ys=None, stream=None):
     _check(get_lib().mxfp4_verify_gemm_grouped(arr, len(items), k, m, _stream(stream)),
            "mxfp4_verify_gemm_grouped")
     return out
+
+
+def tree_depth(parent) -> int:
+    """Nodes on the longest root-to-leaf path of a tree given by its parent list."""
+    d = []
+    for i, p in enumerate(parent):
+        d.append(1 if p < 0 else d[p] + 1)
+    return max(d, default=0)
+
+
+def _parent_array(parent):
+    arr = (ctypes.c_int32 * max(1, len(parent)))(*[int(p) for p in parent])
+    return arr
+
+
+def spec_accept_tree_workspace_bytes(parent, b: int, v: int) -> int:
+    return int(get_lib().spec_accept_tree_workspace_bytes(_parent_array(parent), len(parent), b, v))
+
+
+def spec_accept_tree(parent, target: torch.Tensor, draft: torch.Tensor, tokens: torch.Tensor | None,
+                     uniforms: torch.Tensor, out_tokens: torch.Tensor | None = None,
+                     out_nodes: torch.Tensor | None = None, out_num: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, dev_flags: torch.Tensor | None = None, stream=None):
+    """One verification cycle over a tree of drafts for b sequences (see the C header).
+
+    parent: list of N ints (-1 = root); target, draft fp32 [b, N+1, v]; tokens int32 [b, N];
+    uniforms fp32 [b, N+1]. Returns (out_tokens [b, D+1], out_nodes [b, D], n [b]).
+    """
+    parent = [int(p) for p in parent]
+    nn = len(parent)
+    _want(target, torch.float32, "target")
+    b, rows, v = target.shape
+    if rows != nn + 1:
+        raise ValueError("target must be [b, N+1, v]")
+    _want(draft, torch.float32, "draft", (b, nn + 1, v))
+    if nn:
+        _want(tokens, torch.int32, "tokens", (b, nn))
+    else:
+        tokens = None
+    _want(uniforms, torch.float32, "uniforms", (b, nn + 1))
+    d = tree_depth(parent)
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((b, d + 1), dtype=torch.int32, device=dev)
+    if out_nodes is None:
+        out_nodes = torch.empty((b, max(d, 1)), dtype=torch.int32, device=dev)
+    if out_num is None:
+        out_num = torch.empty((b,), dtype=torch.int32, device=dev)
+    _want(out_tokens, torch.int32, "out_tokens", (b, d + 1))
+    if out_nodes.shape != (b, d) and not (d == 0 and out_nodes.shape == (b, 1)):
+        raise ValueError(f"out_nodes must have shape {(b, d)}")
+    _want(out_nodes, torch.int32, "out_nodes")
+    _want(out_num, torch.int32, "out_num", (b,))
+    need = spec_accept_tree_workspace_bytes(parent, b, v)
+    if need == 0:
+        raise ValueError("tree or sizes out of range")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    _want(workspace, torch.uint8, "workspace")
+    _want_flags(dev_flags)
+    _check(get_lib().spec_accept_tree(_ptr(target), _ptr(draft), _parent_array(parent), nn, _ptr(tokens),
+                                      _ptr(uniforms), b, v, _ptr(out_tokens), _ptr(out_nodes), _ptr(out_num),
+                                      _ptr(workspace), workspace.numel(), _ptr(dev_flags), _stream(stream)),
+           "spec_accept_tree")
+    return out_tokens, out_nodes[:, :d], out_num
+
+
+def mxfp4_kv_append(kv: torch.Tensor, slots: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                    dev_flags: torch.Tensor | None = None, stream=None):
+    """Code kv bf16 [t, heads, d] into the MX-FP4 KV cache codes uint8 [capacity, heads, d/2] and
+    scales uint8 [capacity, heads, d/32] at entries slots int32 [t] (in place)."""
+    _want(kv, torch.bfloat16, "kv")
+    if kv.dim() != 3:
+        raise ValueError("kv must be [t, heads, d]")
+    t, heads, d = kv.shape
+    _want(slots, torch.int32, "slots", (t,))
+    if codes is None or scales is None or codes.dim() != 3:
+        raise ValueError("codes must be [capacity, heads, d/2]")
+    cap = codes.shape[0]
+    _want(codes, torch.uint8, "codes", (cap, heads, d // 2))
+    _want(scales, torch.uint8, "scales", (cap, heads, d // 32))
+    _want_flags(dev_flags)
+    _check(get_lib().mxfp4_kv_append(_ptr(kv), t, heads, d, _ptr(slots), cap, _ptr(codes), _ptr(scales),
+                                     _ptr(dev_flags), _stream(stream)), "mxfp4_kv_append")
+    return codes, scales
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

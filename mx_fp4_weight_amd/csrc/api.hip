@@ -35,6 +35,34 @@ mxs_status check_device() {
 
 mxs_status launched(hipError_t e) { return e == hipSuccess ? MXS_OK : MXS_ERR_LAUNCH; }
 
+// Topology of a draft tree from its parent array (host): false if malformed or too large.
+bool make_topo(const int32_t* parent, int32_t n, mxs::TreeTopo& t) {
+  if (n < 0 || n > mxs::kMaxTreeNodes || (n > 0 && !parent)) return false;
+  int cnt[mxs::kMaxTreeNodes + 1] = {0};
+  int depth[mxs::kMaxTreeNodes] = {0};
+  t = mxs::TreeTopo{};
+  t.n = n;
+  for (int i = 0; i < n; ++i) {
+    const int p = parent[i];
+    if (p < -1 || p >= i) return false;
+    ++cnt[p + 1];
+    depth[i] = p < 0 ? 1 : depth[p] + 1;
+    t.depth = depth[i] > t.depth ? depth[i] : t.depth;
+  }
+  int most = 0;
+  t.off[0] = 0;
+  for (int r = 0; r <= n; ++r) {
+    t.off[r + 1] = (int8_t)(t.off[r] + cnt[r]);
+    most = cnt[r] > most ? cnt[r] : most;
+  }
+  if (most > mxs::kMaxTreeChildren) return false;
+  t.passes = most + 1;
+  int pos[mxs::kMaxTreeNodes + 1];
+  for (int r = 0; r <= n; ++r) pos[r] = t.off[r];
+  for (int i = 0; i < n; ++i) t.child[pos[parent[i] + 1]++] = (int8_t)i;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,6 +347,18 @@ mxs_status mxfp4_verify_gemm_grouped_tiled(const mxs_gemm_problem* problems, int
   return MXS_OK;
 }
 
+mxs_status mxfp4_kv_append(const uint16_t* kv, int64_t t, int64_t heads, int64_t d, const int32_t* slots,
+                           int64_t capacity, uint8_t* codes, uint8_t* scales, int32_t* dev_flags, void* stream) {
+  if (!kv || !slots || !codes || !scales) return MXS_ERR_NULL;
+  if (t < 1 || heads < 1 || d < 32 || d % 32 != 0 || capacity < 1) return MXS_ERR_SHAPE;
+  if (t > (int64_t(1) << 40) / (heads * d) || capacity > (int64_t(1) << 40) / (heads * d)) return MXS_ERR_SHAPE;
+  if (!aligned(kv, 16) || !aligned(slots, 4) || !aligned(codes, 4) || !aligned(dev_flags, 4)) return MXS_ERR_ALIGN;
+  const mxs_status dv = check_device();
+  if (dv != MXS_OK) return dv;
+  return launched(mxs::launch_kv_append(kv, t, heads, d, slots, capacity, codes, scales, dev_flags,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 mxs_status mxs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink) return MXS_ERR_NULL;
   if (bytes < 16 || bytes % 16 != 0) return MXS_ERR_SHAPE;
@@ -326,6 +366,35 @@ mxs_status mxs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* 
   const mxs_status d = check_device();
   if (d != MXS_OK) return d;
   return launched(mxs::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+size_t spec_accept_tree_workspace_bytes(const int32_t* parent, int32_t nodes, int32_t b, int32_t v) {
+  mxs::TreeTopo t;
+  if (b < 1 || b > 65535 || v < 2 || v > (1 << 26) || !make_topo(parent, nodes, t)) return 0;
+  return mxs::tree_workspace_bytes(b, t, v);
+}
+
+mxs_status spec_accept_tree(const float* target_logits, const float* draft_logits, const int32_t* parent,
+                            int32_t nodes, const int32_t* draft_tokens, const float* uniforms, int32_t b, int32_t v,
+                            int32_t* out_tokens, int32_t* out_nodes, int32_t* out_num_accepted, void* workspace,
+                            size_t workspace_bytes, int32_t* dev_flags, void* stream) {
+  if (!target_logits || !draft_logits || !uniforms || !out_tokens || !out_num_accepted || !workspace)
+    return MXS_ERR_NULL;
+  if (nodes > 0 && (!parent || !draft_tokens || !out_nodes)) return MXS_ERR_NULL;
+  if (b < 1 || b > 65535 || v < 2 || v > (1 << 26) || nodes < 0 || nodes > mxs::kMaxTreeNodes) return MXS_ERR_SHAPE;
+  mxs::TreeTopo t;
+  if (!make_topo(parent, nodes, t)) return MXS_ERR_VALUE;
+  if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(out_tokens, 4) || !aligned(out_nodes, 4) ||
+      !aligned(out_num_accepted, 4) || !aligned(workspace, 16) || !aligned(dev_flags, 4))
+    return MXS_ERR_ALIGN;
+  if (workspace_bytes < mxs::tree_workspace_bytes(b, t, v)) return MXS_ERR_WORKSPACE;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  const bool vec4 = (v % 4 == 0) && aligned(target_logits, 16) && aligned(draft_logits, 16);
+  return launched(mxs::launch_spec_accept_tree(target_logits, draft_logits, t, draft_tokens, uniforms, b, v,
+                                               out_tokens, out_nodes, out_num_accepted, workspace, dev_flags, vec4,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 size_t spec_accept_workspace_bytes(int32_t b, int32_t kd, int32_t v) {

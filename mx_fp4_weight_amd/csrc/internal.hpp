@@ -64,6 +64,11 @@ hipError_t launch_nvfp4_verify_gemm_grouped_tiled(const mxs_problem_view* pv, in
 hipError_t launch_nvfp4_verify_gemm_grouped(const mxs_problem_view* pv, int count, int64_t k, int64_t m,
                                             hipStream_t stream);
 
+// MX-FP4 KV cache append: kv [t, heads, d] bf16 -> entries slots[i] of codes [capacity, heads, d/2]
+// and scales [capacity, heads, d/32] (d % 32 == 0).
+hipError_t launch_kv_append(const uint16_t* kv, int64_t t, int64_t heads, int64_t d, const int32_t* slots,
+                            int64_t capacity, uint8_t* codes, uint8_t* scales, int32_t* flags, hipStream_t stream);
+
 // MX activations (fmt MXS_ACT_FP8 or MXS_ACT_FP4) and the W4A8 / W4A4 product.
 hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t fmt, uint8_t* codes,
                                uint8_t* scales, int32_t* flags, hipStream_t stream);
@@ -82,6 +87,22 @@ hipError_t launch_tile_codes(const uint8_t* codes, int64_t n, int64_t k, uint8_t
 hipError_t launch_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8_t* tiled, hipStream_t stream);
 
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
+
+// Tree of draft tokens (spec_accept_tree): topology passed by value to the kernels.
+constexpr int kMaxTreeNodes = 64;
+constexpr int kMaxTreeChildren = 16;
+struct TreeTopo {
+  int n;       // draft nodes
+  int depth;   // nodes on the longest root-to-leaf path
+  int passes;  // residual passes: the largest child count + 1
+  int8_t child[kMaxTreeNodes];    // nodes grouped by parent (the root's first), ascending
+  int8_t off[kMaxTreeNodes + 2];  // children of row rho (0: root, i + 1: node i): child[off[rho] .. off[rho + 1])
+};
+size_t tree_workspace_bytes(int64_t b, const TreeTopo& topo, int64_t v);
+hipError_t launch_spec_accept_tree(const float* target, const float* draft, const TreeTopo& topo,
+                                   const int32_t* tokens, const float* uniforms, int32_t b, int32_t v,
+                                   int32_t* out_tokens, int32_t* out_nodes, int32_t* out_num, void* workspace,
+                                   int32_t* flags, bool vec4, hipStream_t stream);
 
 // The built-in workspace of spec_accept_noalloc: a static device array of this many bytes
 // (one per GPU, kept until the process ends). noalloc_scratch returns its device address

@@ -279,15 +279,28 @@ __device__ inline uint32_t e4m3_code(uint32_t vbits, int e) {
 }
 
 // 4 lanes per 32-value block, one 16-byte load (8 bf16) each.
+// slots (KV cache append): input entry i (per_entry consecutive blocks: one token's heads x
+// d/32 blocks) is written at entry slots[i] of the output; a slot outside [0, capacity)
+// writes nothing and raises MXS_FLAG_TOKEN_RANGE. Without slots, block b goes to block b.
 template <int kFmt>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales,
-                                                           int32_t* __restrict__ flags) {
+                                                           int32_t* __restrict__ flags,
+                                                           const int32_t* __restrict__ slots = nullptr,
+                                                           int64_t per_entry = 1, int64_t capacity = 0) {
   const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t blk = gtid >> 2;
   const int sub = (int)(gtid & 3);
-  const bool live = blk < nblocks;
+  bool live = blk < nblocks;
+  int64_t oblk = blk;  // output block
+  bool out_of_range = false;
+  if (slots != nullptr && live) {
+    const int64_t entry = blk / per_entry;
+    const int64_t slot = slots[entry];
+    out_of_range = slot < 0 || slot >= capacity;
+    oblk = slot * per_entry + (blk - entry * per_entry);
+  }
   u32x4 v = {0u, 0u, 0u, 0u};
   if (live) v = *reinterpret_cast<const u32x4*>(x + blk * 32 + sub * 8);
   uint32_t f[8];  // fp32 bit patterns of the 8 values (element 2i in the low half of word i)
@@ -325,16 +338,17 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __res
       w1 |= e4m3_code(f[4 + i], e) << (8 * i);
     }
     if (bad) w0 = w1 = 0u;
-    if (live) *reinterpret_cast<uint2*>(codes + blk * 32 + sub * 8) = make_uint2(w0, w1);
+    if (live && !out_of_range) *reinterpret_cast<uint2*>(codes + oblk * 32 + sub * 8) = make_uint2(w0, w1);
   } else {
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) packed |= e2m1_code(f[i], e) << (4 * i);
     if (bad) packed = 0u;
-    if (live) *reinterpret_cast<uint32_t*>(codes + blk * 16 + sub * 4) = packed;
+    if (live && !out_of_range) *reinterpret_cast<uint32_t*>(codes + oblk * 16 + sub * 4) = packed;
   }
-  if (live && sub == 0) scales[blk] = sbyte;
-  if (__any(live && bad) && (threadIdx.x & (kWave - 1)) == 0) raise_flag(flags, MXS_FLAG_NONFINITE);
+  if (live && !out_of_range && sub == 0) scales[oblk] = sbyte;
+  if (__any(live && bad && !out_of_range) && (threadIdx.x & (kWave - 1)) == 0) raise_flag(flags, MXS_FLAG_NONFINITE);
+  if (__any(live && out_of_range) && (threadIdx.x & (kWave - 1)) == 0) raise_flag(flags, MXS_FLAG_TOKEN_RANGE);
 }
 
 }  // namespace
@@ -347,6 +361,16 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, int32_t 
     quantize_act_kernel<MXS_ACT_FP8><<<grid, block, 0, stream>>>(x, nblocks, codes, scales, flags);
   else
     quantize_act_kernel<MXS_ACT_FP4><<<grid, block, 0, stream>>>(x, nblocks, codes, scales, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const uint16_t* kv, int64_t t, int64_t heads, int64_t d, const int32_t* slots,
+                            int64_t capacity, uint8_t* codes, uint8_t* scales, int32_t* flags, hipStream_t stream) {
+  const int64_t per_entry = heads * (d / 32);
+  const int64_t nblocks = t * per_entry;
+  const dim3 grid((unsigned)((nblocks * 4 + 255) / 256)), block(256);
+  quantize_act_kernel<MXS_ACT_FP4><<<grid, block, 0, stream>>>(kv, nblocks, codes, scales, flags, slots, per_entry,
+                                                               capacity);
   return hipGetLastError();
 }
 

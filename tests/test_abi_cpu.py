@@ -145,6 +145,57 @@ def test_noalloc_scratch_size_matches_header():
     assert m and int(m.group(1)) << int(m.group(2)) == mxs.NOALLOC_SCRATCH_BYTES
 
 
+def test_tree_host_errors():
+    lib = mxs.get_lib()
+    f = lambda a: P(a) if a else None
+    arr = lambda ps: (ctypes.c_int32 * max(1, len(ps)))(*ps)
+    par = [-1, -1, 0, 0, 1]
+    need = lib.spec_accept_tree_workspace_bytes(arr(par), len(par), 2, 1024)
+    assert need > 0
+    assert lib.spec_accept_tree_workspace_bytes(arr([0]), 1, 2, 1024) == 0          # a node its own parent
+    assert lib.spec_accept_tree_workspace_bytes(arr([-1] * 17), 17, 2, 1024) == 0   # 17 children
+    assert lib.spec_accept_tree_workspace_bytes(arr(par), len(par), 0, 1024) == 0
+
+    def call(t=0x1000, d=0x2000, ps=par, nn=None, tok=0x3000, u=0x4000, b=2, v=1024, ot=0x5000, on=0x6000,
+             onum=0x7000, ws=0x8000, wsb=None, fl=None):
+        nn = len(ps) if nn is None else nn
+        wsb = need if wsb is None else wsb
+        return lib.spec_accept_tree(f(t), f(d), arr(ps), nn, f(tok), f(u), b, v, f(ot), f(on), f(onum), f(ws), wsb,
+                                    f(fl), None)
+    for a in [dict(t=0), dict(d=0), dict(tok=0), dict(u=0), dict(ot=0), dict(on=0), dict(onum=0), dict(ws=0)]:
+        assert call(**a) == mxs.MXS_ERR_NULL
+    assert call(ps=[], nn=0, tok=0, on=0, wsb=lib.spec_accept_tree_workspace_bytes(arr([]), 0, 2, 1024)) == \
+        mxs.MXS_ERR_DEVICE
+    for a in [dict(b=0), dict(v=1), dict(nn=65, ps=[-1] * 65)]:
+        assert call(**a) == mxs.MXS_ERR_SHAPE
+    for a in [dict(ps=[-1, 1]), dict(ps=[-1] * 17), dict(ps=[-2])]:
+        assert call(**a) == mxs.MXS_ERR_VALUE
+    for a in [dict(t=0x1002), dict(tok=0x3001), dict(ws=0x8008), dict(fl=0x9001)]:
+        assert call(**a) == mxs.MXS_ERR_ALIGN
+    assert call(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
+    assert call() == mxs.MXS_ERR_DEVICE
+
+
+def test_kv_slot_flag_is_the_token_range_bit():
+    from oracle import kvcache
+    assert kvcache.FLAG_SLOT_RANGE == mxs.FLAG_TOKEN_RANGE and kvcache.FLAG_NONFINITE == mxs.FLAG_NONFINITE
+
+
+def test_kv_append_host_errors():
+    lib = mxs.get_lib()
+    f = lambda a: P(a) if a else None
+    kv = lambda kv=0x1000, t=4, h=8, d=128, sl=0x2000, cap=64, c=0x3000, s=0x4000, fl=None: lib.mxfp4_kv_append(
+        f(kv), t, h, d, f(sl), cap, f(c), f(s), f(fl), None)
+    for a in [dict(kv=0), dict(sl=0), dict(c=0), dict(s=0)]:
+        assert kv(**a) == mxs.MXS_ERR_NULL
+    for a in [dict(t=0), dict(h=0), dict(d=16), dict(d=48), dict(cap=0)]:
+        assert kv(**a) == mxs.MXS_ERR_SHAPE
+    for a in [dict(kv=0x1008), dict(sl=0x2002), dict(c=0x3002), dict(fl=0x5001)]:
+        assert kv(**a) == mxs.MXS_ERR_ALIGN
+    assert kv(s=0x4001) == mxs.MXS_ERR_DEVICE   # scales: any alignment
+    assert kv() == mxs.MXS_ERR_DEVICE
+
+
 def test_stream_read_host_errors():
     lib = mxs.get_lib()
     f = lambda a: P(a) if a else None
