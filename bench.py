@@ -32,9 +32,11 @@ shapes with 1% outlier input channels x20, lm_head 128256x8192, and the
 its MFMA utilisation, spec_accept for 64 sequences) and `full_8b_step` (32
 layers + lm_head 128256x4096, then spec_accept on the lm_head output with draft
 rows tuned to acceptance 0.6 / 0.8 / 0.9: step time, tokens/s-equivalent and the
-GPU-measured tokens per step against the closed form) and `sampled_accept`
+GPU-measured tokens per step against the closed form), `sampled_accept`
 (spec_accept_sampled at B = 1 and 64 under temperature only, temperature + top-k +
-top-p + a 90% grammar mask, and top-p alone, next to plain spec_accept).
+top-p + a 90% grammar mask, and top-p alone, next to plain spec_accept),
+`tree_accept` (spec_accept_tree on three tree shapes at B = 1 and 64) and `kv_append`
+(mxfp4_kv_append of 5 and 4096 tokens into an 8-head MX-FP4 KV cache).
 """
 from __future__ import annotations
 
@@ -682,6 +684,82 @@ def sampled_accept(torch, mxs, gen, reps=20):
     return out
 
 
+TREE_SHAPES = {  # parent lists: a chain of 4, a 3-way root with 2 children each, a binary tree of depth 3
+    "chain4": [-1, 0, 1, 2],
+    "3x2": [-1, -1, -1, 0, 0, 1, 1, 2, 2],
+    "binary3": [-1, -1, 0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5],
+}
+
+
+def tree_accept(torch, mxs, gen, reps=20):
+    """spec_accept_tree over V = 128256 for B = 1 and 64 on three tree shapes (fp32 logits N(0, 3),
+    target = draft + N(0, 1), every node's token drawn from its parent's draft row), next to
+    plain spec_accept on the chain's inputs."""
+    out = {}
+    for b in (1, 64):
+        row = {}
+        for name, parent in TREE_SHAPES.items():
+            nn = len(parent)
+            base = torch.randn((b, nn + 1, V), generator=gen, device="cuda", dtype=torch.float32) * 3.0
+            tgt = base + torch.randn((b, nn + 1, V), generator=gen, device="cuda", dtype=torch.float32)
+            dft = base
+            del base
+            rows = torch.tensor([p + 1 for p in parent], device="cuda")
+            law = torch.softmax(dft[:, rows].double(), -1).reshape(b * nn, V)
+            tok = torch.multinomial(law, 1, generator=gen).reshape(b, nn).to(torch.int32)
+            del law
+            u = torch.rand((b, nn + 1), generator=gen, device="cuda", dtype=torch.float32)
+            d = mxs.tree_depth(parent)
+            ot = torch.empty((b, d + 1), dtype=torch.int32, device="cuda")
+            on = torch.empty((b, d), dtype=torch.int32, device="cuda")
+            onum = torch.empty((b,), dtype=torch.int32, device="cuda")
+            ws = torch.empty((mxs.spec_accept_tree_workspace_bytes(parent, b, V),), dtype=torch.uint8, device="cuda")
+
+            def call(parent=parent, tgt=tgt, dft=dft, tok=tok, u=u, ot=ot, on=on, onum=onum, ws=ws):
+                mxs.spec_accept_tree(parent, tgt, dft, tok, u, out_tokens=ot, out_nodes=on, out_num=onum,
+                                     workspace=ws)
+            us = _graph_ms(torch, call, reps) * 1e3
+            entry = {"nodes": nn, "depth": d, "us": round(us, 1),
+                     "positions_per_s": round(b * (nn + 1) / (us * 1e-6), 1),
+                     "mean_accepted": round(float(onum.float().mean()), 3),
+                     "kernels": 2 + (max([parent.count(p) for p in set(parent)] + [0]) + 1)}
+            if name == "chain4":
+                ot2 = torch.empty((b, nn + 1), dtype=torch.int32, device="cuda")
+                on2 = torch.empty((b,), dtype=torch.int32, device="cuda")
+                ws2 = torch.empty((mxs.spec_accept_workspace_bytes(b, nn, V),), dtype=torch.uint8, device="cuda")
+                tc, dc = tgt.contiguous(), dft[:, :nn].contiguous()
+
+                def lin(tc=tc, dc=dc, tok=tok, u=u, ot2=ot2, on2=on2, ws2=ws2):
+                    mxs.spec_accept(tc, dc, tok, u, out_tokens=ot2, out_num=on2, workspace=ws2)
+                entry["linear_spec_accept_us"] = round(_graph_ms(torch, lin, reps) * 1e3, 1)
+                del tc, dc, ws2
+            row[name] = entry
+            del tgt, dft, ws
+        out[f"B{b}"] = row
+    return out
+
+
+def kv_append(torch, mxs, gen, reps=20):
+    """mxfp4_kv_append for the 8B-class cache (8 KV heads of 128): a verification step's 5 new
+    tokens and a 4096-token prefill, into a 32768-entry cache; GB/s of bf16 read + codes and
+    scales written."""
+    heads, d, cap = 8, 128, 32768
+    codes = torch.zeros((cap, heads, d // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((cap, heads, d // 32), dtype=torch.uint8, device="cuda")
+    out = {"cache_entries": cap, "heads": heads, "d": d,
+           "footprint_vs_bf16": round((d // 2 + d // 32) / (2 * d), 6)}
+    for t in (5, 4096):
+        kv = torch.randn((t, heads, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        slots = torch.arange(1000, 1000 + t, dtype=torch.int32, device="cuda")
+
+        def call(kv=kv, slots=slots):
+            mxs.mxfp4_kv_append(kv, slots, codes, scales)
+        us = _graph_ms(torch, call, reps) * 1e3
+        byts = t * heads * (2 * d + d // 2 + d // 32)
+        out[f"t{t}"] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
 def nv_bytes(n, k):
     """NVFP4 weight bytes: 4-bit codes + one E4M3 byte per 16 values (the fp32 tensor scale aside)."""
     return n * k // 2 + n * k // 16
@@ -832,7 +910,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (T sweep, 70B shapes, batched, full 8B step)")
     ap.add_argument("--only", choices=["headline", "t_sweep_8b", "shapes_70b_t5", "batched_64x5", "sampled_accept",
-                                       "nvfp4_8b", "full_8b_step"],
+                                       "nvfp4_8b", "tree_accept", "kv_append", "full_8b_step"],
                     help="run one workload alone (profiling); 'headline' = the default line without "
                          "the secondary workloads")
     ap.add_argument("--seed", type=int, default=2)
@@ -919,6 +997,8 @@ def main():
               ("batched_64x5", lambda: batched(torch, mxs, gen2)),
               ("sampled_accept", lambda: sampled_accept(torch, mxs, gen2)),
               ("nvfp4_8b", lambda: nvfp4_8b(torch, mxs, gen2)),
+              ("tree_accept", lambda: tree_accept(torch, mxs, gen2)),
+              ("kv_append", lambda: kv_append(torch, mxs, gen2)),
               ("full_8b_step", lambda: full_8b_step(torch, mxs, gen2)))
     if args.only and args.only != "headline":
         # one secondary workload alone (for per-workload profiles)

@@ -13,12 +13,13 @@
 // w_j / Z_j. Kernels on the caller's stream:
 //   stats  grid (rows, chunks): chunk max (fp32) and sum exp(z - max) (fp64) of every target
 //          and draft row of every node (one full read of the logits).
+//   rowstat one workgroup per row: the chunk statistics combined into the row's (max, sum).
 //   pass r (r = 0 .. largest child count): grid (pieces, nodes, sequences): for every node
 //          with at least r children, the 1024-token piece totals of w_{r+1} (w_1 = p for
 //          r = 0), with Z_2 .. Z_r summed from the earlier passes' piece totals in a fixed
 //          order. Every node gets them, visited or not: the walk below needs them at once.
-//   walk   one workgroup per sequence: walks the tree with scalar decisions (the statistics
-//          and the Z values are recombined in the same fixed order as in the passes), then
+//   walk   one workgroup per sequence: walks the tree with scalar decisions (the row statistics
+//          are the stored ones and the Z values are summed in the passes' fixed order), then
 //          draws the final token: a scan of the final law's piece totals picks the piece, its
 //          weights are recomputed exactly as the pass computed them, a scan of the thread
 //          totals picks the thread, and its 4 weights give the token.
@@ -44,6 +45,8 @@ struct TreeWs {
   double* csum;   // [b][2(N+1)][chunks]
   int32_t* cbad;  // [b][2(N+1)][chunks]
   double* ptot;   // [passes][b][N+1][pieces]: piece totals of w_{r+1}
+  double* rms;    // [b][2(N+1)][2]: the row's max and sum exp(z - max)
+  int32_t* rbad;  // [b][2(N+1)]: the row is malformed (a NaN / +inf logit, or no finite logit)
 };
 
 __device__ inline const float* tree_row(const float* base, int64_t s, int n, int rho, int64_t v) {
@@ -140,6 +143,30 @@ __device__ RowStat row_stat(const TreeWs& ws, int64_t s, int n, int j, int chunk
   return r;
 }
 
+// One workgroup per row: its statistics combined once, for the passes and the walk to read.
+__global__ __launch_bounds__(kTh) void tree_rowstat_kernel(int n, int chunks, TreeWs ws) {
+  __shared__ double lds_d[kWavesT];
+  __shared__ float lds_f[kWavesT];
+  __shared__ int lds_i[kWavesT];
+  const int64_t g = blockIdx.x;
+  const int per = 2 * (n + 1);
+  const RowStat r = row_stat(ws, g / per, n, (int)(g % per), chunks, lds_d, lds_f, lds_i);
+  if (threadIdx.x == 0) {
+    ws.rms[2 * g] = r.m;
+    ws.rms[2 * g + 1] = r.s;
+    ws.rbad[g] = r.bad;
+  }
+}
+
+__device__ inline RowStat load_stat(const TreeWs& ws, int64_t s, int n, int j) {
+  const size_t g = (size_t)s * 2 * (n + 1) + j;
+  RowStat r;
+  r.m = ws.rms[2 * g];
+  r.s = ws.rms[2 * g + 1];
+  r.bad = ws.rbad[g];
+  return r;
+}
+
 // Sum of pass r's piece totals of node rho (Z_{r+1}), in piece order per thread, then the fixed
 // block order. Block-wide.
 __device__ double pass_sum(const TreeWs& ws, int r, int64_t s, int64_t b, int n, int rho, int pieces, double* lds_d) {
@@ -191,26 +218,25 @@ __device__ inline void law_weights(const NodeLaw& nl, int r, int t0, int v, bool
 }
 
 // ------------------------------------------------------------------ residual passes
+// ppw pieces per workgroup (consecutive), so large grids stay about one resident round.
 template <bool kVec4>
 __global__ __launch_bounds__(kTh) void tree_pass_kernel(const float* __restrict__ target,
                                                        const float* __restrict__ draft, TreeTopo topo, int r,
-                                                       int v, int chunks, int pieces, int64_t b, TreeWs ws) {
+                                                       int v, int pieces, int ppw, int64_t b, TreeWs ws) {
   __shared__ double lds_d[kWavesT];
-  __shared__ float lds_f[kWavesT];
-  __shared__ int lds_i[kWavesT];
   __shared__ double tab[32];
   __shared__ double s_z[kMaxTreeChildren + 2];
   if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Table32[threadIdx.x];
   const int n = topo.n;
   const int rho = blockIdx.y;
   const int64_t s = blockIdx.z;
-  const int piece = blockIdx.x;
   if (r > topo.off[rho + 1] - topo.off[rho]) return;  // uniform: fewer children than tries
-  const RowStat st = row_stat(ws, s, n, rho, chunks, lds_d, lds_f, lds_i);
-  const RowStat sd = row_stat(ws, s, n, n + 1 + rho, chunks, lds_d, lds_f, lds_i);
-  double* out = ws.ptot + (((size_t)r * b + s) * (n + 1) + rho) * pieces + piece;
+  const RowStat st = load_stat(ws, s, n, rho);
+  const RowStat sd = load_stat(ws, s, n, n + 1 + rho);
+  double* out = ws.ptot + (((size_t)r * b + s) * (n + 1) + rho) * pieces;
   if (st.bad || sd.bad) {  // the walk refuses the sequence
-    if (threadIdx.x == 0) *out = 0.0;
+    for (int i = threadIdx.x; i < ppw; i += kTh)
+      if ((int)blockIdx.x * ppw + i < pieces) out[blockIdx.x * ppw + i] = 0.0;
     return;
   }
   NodeLaw nl;
@@ -227,13 +253,17 @@ __global__ __launch_bounds__(kTh) void tree_pass_kernel(const float* __restrict_
   }
   __syncthreads();
   nl.z = s_z;
-  double w[kWPerT];
-  law_weights(nl, r, piece * kTPiece + (int)threadIdx.x * kWPerT, v, kVec4, tab, w);
-  double t = 0.0;
+  for (int i = 0; i < ppw; ++i) {
+    const int piece = (int)blockIdx.x * ppw + i;
+    if (piece >= pieces) break;  // uniform
+    double w[kWPerT];
+    law_weights(nl, r, piece * kTPiece + (int)threadIdx.x * kWPerT, v, kVec4, tab, w);
+    double t = 0.0;
 #pragma unroll
-  for (int j = 0; j < kWPerT; ++j) t += w[j];
-  t = block_inclusive_scan_f64<kTh>(t, lds_d);
-  if (threadIdx.x == kTh - 1) *out = t;
+    for (int j = 0; j < kWPerT; ++j) t += w[j];
+    t = block_inclusive_scan_f64<kTh>(t, lds_d);
+    if (threadIdx.x == kTh - 1) out[piece] = t;
+  }
 }
 
 // ------------------------------------------------------------------ walk and final draw
@@ -270,7 +300,6 @@ __global__ __launch_bounds__(kTh) void tree_walk_kernel(const float* __restrict_
                                                        int32_t* __restrict__ out_nodes,
                                                        int32_t* __restrict__ out_num, int32_t* __restrict__ flags) {
   __shared__ double lds_d[kWavesT];
-  __shared__ float lds_f[kWavesT];
   __shared__ int lds_i[kWavesT];
   __shared__ int s_fl[2 * kWavesT];
   __shared__ double s_incl[kTh];
@@ -285,15 +314,7 @@ __global__ __launch_bounds__(kTh) void tree_walk_kernel(const float* __restrict_
 
   // every row of the tree is examined: a malformed one refuses the sequence
   int bad = 0;
-  for (int j = threadIdx.x; j < 2 * (n + 1); j += kTh) {
-    const size_t o = ((size_t)s * 2 * (n + 1) + j) * chunks;
-    float m = -INFINITY;
-    for (int c = 0; c < chunks; ++c) {
-      m = fmaxf(m, ws.cmax[o + c]);
-      bad |= ws.cbad[o + c];
-    }
-    bad |= (m == -INFINITY);
-  }
+  for (int j = threadIdx.x; j < 2 * (n + 1); j += kTh) bad |= ws.rbad[(size_t)s * 2 * (n + 1) + j];
   bad = block_or<kTh>(bad, lds_i);
   for (int i = threadIdx.x; i <= topo.depth; i += kTh) {
     ot[i] = -1;
@@ -313,8 +334,8 @@ __global__ __launch_bounds__(kTh) void tree_walk_kernel(const float* __restrict_
   int fl = 0;
   NodeLaw nl;
   while (true) {
-    const RowStat st = row_stat(ws, s, n, rho, chunks, lds_d, lds_f, lds_i);
-    const RowStat sd = row_stat(ws, s, n, n + 1 + rho, chunks, lds_d, lds_f, lds_i);
+    const RowStat st = load_stat(ws, s, n, rho);
+    const RowStat sd = load_stat(ws, s, n, n + 1 + rho);
     nl.zt = tree_row(target, s, n, rho, v);
     nl.zd = tree_row(draft, s, n, rho, v);
     nl.mt = st.m;
@@ -447,6 +468,8 @@ size_t tree_workspace_bytes(int64_t b, const TreeTopo& topo, int64_t v) {
   off = al256(off + sizeof(double) * rows * chunks);
   off = al256(off + sizeof(int32_t) * rows * chunks);
   off = al256(off + sizeof(double) * (size_t)topo.passes * b * (topo.n + 1) * pieces);
+  off = al256(off + sizeof(double) * 2 * rows);
+  off = al256(off + sizeof(int32_t) * rows);
   return off;
 }
 
@@ -468,6 +491,10 @@ hipError_t launch_spec_accept_tree(const float* target, const float* draft, cons
   ws.cbad = reinterpret_cast<int32_t*>(base + off);
   off = al256(off + sizeof(int32_t) * rows * chunks);
   ws.ptot = reinterpret_cast<double*>(base + off);
+  off = al256(off + sizeof(double) * (size_t)topo.passes * b * (n + 1) * pieces);
+  ws.rms = reinterpret_cast<double*>(base + off);
+  off = al256(off + sizeof(double) * 2 * rows);
+  ws.rbad = reinterpret_cast<int32_t*>(base + off);
   if (vec4)
     tree_stats_kernel<true><<<dim3((unsigned)rows, (unsigned)chunks), dim3(kTh), 0, stream>>>(target, draft, n, v,
                                                                                              chunks, ws);
@@ -476,12 +503,16 @@ hipError_t launch_spec_accept_tree(const float* target, const float* draft, cons
                                                                                               chunks, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  tree_rowstat_kernel<<<dim3((unsigned)rows), dim3(kTh), 0, stream>>>(n, chunks, ws);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // four pieces per workgroup once one piece each would take several resident rounds
+  const int ppw = (int64_t)pieces * (n + 1) * b > 16384 ? 4 : 1;
   for (int r = 0; r < topo.passes; ++r) {
-    const dim3 grid((unsigned)pieces, (unsigned)(n + 1), (unsigned)b);
+    const dim3 grid((unsigned)((pieces + ppw - 1) / ppw), (unsigned)(n + 1), (unsigned)b);
     if (vec4)
-      tree_pass_kernel<true><<<grid, dim3(kTh), 0, stream>>>(target, draft, topo, r, v, chunks, pieces, b, ws);
+      tree_pass_kernel<true><<<grid, dim3(kTh), 0, stream>>>(target, draft, topo, r, v, pieces, ppw, b, ws);
     else
-      tree_pass_kernel<false><<<grid, dim3(kTh), 0, stream>>>(target, draft, topo, r, v, chunks, pieces, b, ws);
+      tree_pass_kernel<false><<<grid, dim3(kTh), 0, stream>>>(target, draft, topo, r, v, pieces, ppw, b, ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (vec4)
