@@ -13,7 +13,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4spec.so")
+# MXS_LIB: another build of the same library (the host-sanitizer build of the CPU checks)
+LIB_PATH = os.environ.get("MXS_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4spec.so")
 
 MXS_OK = 0
 MXS_ERR_NULL = 1
