@@ -20,6 +20,9 @@ the source pages:
 * ``oracle.kvcache`` — MX-FP4 KV cache codec: per-token head vectors coded in
                       32-element blocks along the head dimension, written at
                       cache slots.
+* ``oracle.attention`` — verification attention over the MX-FP4 cache: every
+                      query position sees the prefix and its own path among
+                      the new positions (chain or tree masks), fp64.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product library must never call it:
@@ -30,4 +33,4 @@ Every function is pinned by a CPU test against facts the pages or mathematics
 fix (printed worked examples, the value grid, closed forms, brute force on tiny
 inputs); none is "parity unpinned".
 """
-from . import mx, gemm, accept, expect, tree, kvcache  # noqa: F401
+from . import mx, gemm, accept, expect, tree, kvcache, attention  # noqa: F401
