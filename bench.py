@@ -35,8 +35,9 @@ rows tuned to acceptance 0.6 / 0.8 / 0.9: step time, tokens/s-equivalent and the
 GPU-measured tokens per step against the closed form), `sampled_accept`
 (spec_accept_sampled at B = 1 and 64 under temperature only, temperature + top-k +
 top-p + a 90% grammar mask, and top-p alone, next to plain spec_accept),
-`tree_accept` (spec_accept_tree on three tree shapes at B = 1 and 64) and `kv_append`
-(mxfp4_kv_append of 5 and 4096 tokens into an 8-head MX-FP4 KV cache).
+`tree_accept` (spec_accept_tree on three tree shapes at B = 1 and 64), `kv_append`
+(mxfp4_kv_append of 5 and 4096 tokens into an 8-head MX-FP4 KV cache) and `kv_attention`
+(mxfp4_kv_attention of a T = 5 pass over 4096- and 32768-entry MX-FP4 caches).
 """
 from __future__ import annotations
 
@@ -760,6 +761,44 @@ def kv_append(torch, mxs, gen, reps=20):
     return out
 
 
+def kv_attention(torch, mxs, gen, reps=10):
+    """mxfp4_kv_attention of the 8B-class verification pass (32 query heads on 8 KV heads of 128,
+    T = 5 positions with the chain mask) over MX-FP4 caches of 4096 and 32768 committed entries,
+    one sequence and 16; a pool of layers (> 512 MB of cache) is visited in turn so the caches come
+    from HBM. GB/s = cache bytes read (codes + scales of K and V over ctx + T entries) + q + out."""
+    hq, hkv, d, t = 32, 8, 128, 5
+    out = {}
+    for b, ctx in ((1, 4096), (1, 32768), (16, 4096)):
+        cap = ctx + t
+        layer_b = 2 * b * cap * hkv * (d // 2 + d // 32)
+        n_layers = max(2, math.ceil(512e6 / layer_b))
+        pool = []
+        for _ in range(n_layers):
+            kc = torch.randint(0, 256, (b, cap, hkv, d // 2), generator=gen, device="cuda", dtype=torch.uint8)
+            vc = torch.randint(0, 256, (b, cap, hkv, d // 2), generator=gen, device="cuda", dtype=torch.uint8)
+            ks = torch.randint(122, 128, (b, cap, hkv, d // 32), generator=gen, device="cuda", dtype=torch.uint8)
+            vs = torch.randint(122, 128, (b, cap, hkv, d // 32), generator=gen, device="cuda", dtype=torch.uint8)
+            pool.append((kc, ks, vc, vs))
+        q = torch.randn((b, t, hq, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        ctx_len = torch.full((b,), ctx, dtype=torch.int32, device="cuda")
+        o = torch.empty((b, t, hq, d), dtype=torch.float32, device="cuda")
+        ws = torch.empty((mxs.mxfp4_kv_attention_workspace_bytes(b, t, hq, hkv, cap),), dtype=torch.uint8,
+                         device="cuda")
+        masks = mxs.chain_masks(t)
+
+        def body(pool=pool, q=q, ctx_len=ctx_len, o=o, ws=ws):
+            for (kc, ks, vc, vs) in pool:
+                mxs.mxfp4_kv_attention(q, kc, ks, vc, vs, ctx_len, masks, out=o, workspace=ws)
+        us = _graph_ms(torch, body, reps) * 1e3 / n_layers
+        byts = layer_b + b * t * hq * d * (2 + 4)
+        out[f"B{b}_ctx{ctx}"] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                                 "pct_of_hbm_peak": round(100 * byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                                 "cache_bytes": layer_b, "pool_layers": n_layers}
+        del pool
+    out["note"] = "T = 5 chain masks, 32 query heads on 8 KV heads of 128 (one layer's attention per call)"
+    return out
+
+
 def nv_bytes(n, k):
     """NVFP4 weight bytes: 4-bit codes + one E4M3 byte per 16 values (the fp32 tensor scale aside)."""
     return n * k // 2 + n * k // 16
@@ -910,7 +949,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (T sweep, 70B shapes, batched, full 8B step)")
     ap.add_argument("--only", choices=["headline", "t_sweep_8b", "shapes_70b_t5", "batched_64x5", "sampled_accept",
-                                       "nvfp4_8b", "tree_accept", "kv_append", "full_8b_step"],
+                                       "nvfp4_8b", "tree_accept", "kv_append", "kv_attention", "full_8b_step"],
                     help="run one workload alone (profiling); 'headline' = the default line without "
                          "the secondary workloads")
     ap.add_argument("--seed", type=int, default=2)
@@ -999,6 +1038,7 @@ def main():
               ("nvfp4_8b", lambda: nvfp4_8b(torch, mxs, gen2)),
               ("tree_accept", lambda: tree_accept(torch, mxs, gen2)),
               ("kv_append", lambda: kv_append(torch, mxs, gen2)),
+              ("kv_attention", lambda: kv_attention(torch, mxs, gen2)),
               ("full_8b_step", lambda: full_8b_step(torch, mxs, gen2)))
     if args.only and args.only != "headline":
         # one secondary workload alone (for per-workload profiles)

@@ -531,6 +531,48 @@ mxs_status mxfp4_kv_append(const uint16_t* kv, int64_t t, int64_t heads, int64_t
                            int64_t capacity, uint8_t* codes, uint8_t* scales, int32_t* dev_flags, void* stream);
 
 /*
+ * mxfp4_kv_attention_workspace_bytes — device workspace mxfp4_kv_attention needs (the
+ * per-workgroup partial results). Returns 0 when the sizes are out of range.
+ */
+size_t mxfp4_kv_attention_workspace_bytes(int32_t b, int32_t t, int32_t hq, int32_t hkv, int64_t max_len);
+
+/*
+ * mxfp4_kv_attention — the verification pass's attention over an MX-FP4 KV cache [M11 §4:
+ * the target scores every draft position in one pass and stays causal, a row sees only its
+ * own history; NEWS, "Microscaling FP4 (MX-FP4) Integration": the KV cache held in MX-FP4].
+ * For each sequence s, query position i < t and query head h (KV head h / G, G = hq / hkv):
+ *   out[s, i, h] = sum_l softmax_l(scale * q[s, i, h] . K^[s, l, h/G]) V^[s, l, h/G]
+ * over the visible cache entries l: every l < ctx_len[s] (the committed prefix) and the new
+ * entry ctx_len[s] + r when bit r of masks[i] is set (a lower-triangular mask for a chain of
+ * drafts; a position's ancestors and itself for a tree). The t new entries must have been
+ * written (mxfp4_kv_append) at ctx_len[s] .. ctx_len[s] + t - 1 before the call. K^ and V^ are
+ * the entries decoded exactly (E2M1 x 2^(s-127)); scores, softmax and sums are fp32 (the
+ * probabilities enter the value product as a bf16 pair, error ~2^-17 relative). Every
+ * position must see at least one entry.
+ *
+ * q           [b, t, hq, d] bf16, 16-byte aligned.
+ * k_codes, v_codes    [b, capacity, hkv, d/2] (mxfp4_kv_append layout per sequence), 16-byte aligned.
+ * k_scales, v_scales  [b, capacity, hkv, d/32].
+ * ctx_len     [b] int32 device: committed entries of each sequence. A sequence with ctx_len < 0
+ *             or ctx_len + t > max_len is refused: its outputs are NaN, MXS_FLAG_TOKEN_RANGE.
+ * b, t        1 <= b <= 65535; 1 <= t <= 64 with t * hq / hkv <= 64 (query rows per KV head).
+ * hq, hkv     hq a multiple of hkv. d = 128.
+ * capacity    entries per sequence in the caches; max_len (host bound on ctx_len + t, sizes the
+ *             launch): t <= max_len <= capacity.
+ * masks       HOST [t] uint64, read during the call: bit r of masks[i] lets position i see new
+ *             entry r; bits >= t are refused (MXS_ERR_VALUE).
+ * scale       > 0 and finite (1/sqrt(d) for plain attention).
+ * out         [b, t, hq, d] fp32, 4-byte aligned.
+ * workspace   mxfp4_kv_attention_workspace_bytes(b, t, hq, hkv, max_len) bytes, 16-byte aligned.
+ * Returns MXS_ERR_NULL, MXS_ERR_SHAPE, MXS_ERR_VALUE, MXS_ERR_ALIGN, MXS_ERR_WORKSPACE.
+ */
+mxs_status mxfp4_kv_attention(const uint16_t* q, const uint8_t* k_codes, const uint8_t* k_scales, const uint8_t* v_codes,
+                              const uint8_t* v_scales, const int32_t* ctx_len, int32_t b, int32_t t, int32_t hq,
+                              int32_t hkv, int32_t d, int64_t capacity, int64_t max_len, const uint64_t* masks,
+                              float scale, float* out, void* workspace, size_t workspace_bytes, int32_t* dev_flags,
+                              void* stream);
+
+/*
  * mxs_stream_read — read `bytes` of device memory once and discard them: the measured
  * ceiling of the weight stream. A verification step that streams all weights is bounded by
  * Q <= BW / W [M11 §1]; this plain read-only kernel measures the BW one kernel draws from

@@ -37,7 +37,8 @@ EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_veri
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
            "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled",
            "nvfp4_verify_gemm_grouped_tiled", "spec_accept_noalloc", "mxs_stream_read", "mxfp4_kv_append",
-           "spec_accept_tree_workspace_bytes", "spec_accept_tree"]
+           "spec_accept_tree_workspace_bytes", "spec_accept_tree", "mxfp4_kv_attention_workspace_bytes",
+           "mxfp4_kv_attention"]
 
 NOALLOC_SCRATCH_BYTES = 4 << 20  # MXS_NOALLOC_SCRATCH_BYTES
 
@@ -66,7 +67,7 @@ def _load() -> ctypes.CDLL:
             f"{LIB_PATH} is missing: build it with `python -m mx_fp4_weight_amd.build` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     lib.mxs_status_string.argtypes = [ctypes.c_int]
     lib.mxs_status_string.restype = ctypes.c_char_p
     lib.mxs_abi_version.argtypes = []
@@ -86,6 +87,11 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_tree.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32), i32, vp, vp, i32, i32, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp, vp]
     lib.spec_accept_tree.restype = ctypes.c_int
+    lib.mxfp4_kv_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i64]
+    lib.mxfp4_kv_attention_workspace_bytes.restype = ctypes.c_size_t
+    lib.mxfp4_kv_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i64,
+                                       ctypes.POINTER(ctypes.c_uint64), f32, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.mxfp4_kv_attention.restype = ctypes.c_int
     lib.mxfp4_kv_append.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     lib.mxfp4_kv_append.restype = ctypes.c_int
     lib.mxs_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
@@ -94,7 +100,6 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_noalloc.restype = ctypes.c_int
     lib.spec_accept_sampled_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_accept_sampled_workspace_bytes.restype = ctypes.c_size_t
-    f32 = ctypes.c_float
     lib.spec_accept_sampled.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp, vp]
     lib.spec_accept_sampled.restype = ctypes.c_int
@@ -322,6 +327,65 @@ def mxfp4_kv_append(kv: torch.Tensor, slots: torch.Tensor, codes: torch.Tensor, 
     _check(get_lib().mxfp4_kv_append(_ptr(kv), t, heads, d, _ptr(slots), cap, _ptr(codes), _ptr(scales),
                                      _ptr(dev_flags), _stream(stream)), "mxfp4_kv_append")
     return codes, scales
+
+
+def chain_masks(t: int) -> list[int]:
+    """Attention masks of t positions of a chain: position i sees new positions 0..i."""
+    return [(1 << (i + 1)) - 1 for i in range(t)]
+
+
+def tree_masks(parent) -> list[int]:
+    """Attention masks of the N + 1 positions of a tree's pass (position 0 = the root's input, i + 1 =
+    node i): a position sees itself and its ancestors."""
+    masks = [1]
+    for i, p in enumerate(parent):
+        masks.append(masks[int(p) + 1] | (1 << (i + 1)))
+    return masks
+
+
+def mxfp4_kv_attention_workspace_bytes(b: int, t: int, hq: int, hkv: int, max_len: int) -> int:
+    return int(get_lib().mxfp4_kv_attention_workspace_bytes(b, t, hq, hkv, max_len))
+
+
+def mxfp4_kv_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                       v_scales: torch.Tensor, ctx_len: torch.Tensor, masks, scale: float | None = None,
+                       max_len: int | None = None, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, dev_flags: torch.Tensor | None = None, stream=None):
+    """Attention of q bf16 [b, t, hq, 128] over the MX-FP4 caches (codes uint8 [b, cap, hkv, 64],
+    scales uint8 [b, cap, hkv, 4]) with ctx_len int32 [b] committed entries and masks (t ints).
+    Returns out fp32 [b, t, hq, 128]."""
+    _want(q, torch.bfloat16, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [b, t, hq, d]")
+    b, t, hq, d = q.shape
+    if k_codes is None or k_codes.dim() != 4:
+        raise ValueError("k_codes must be [b, capacity, hkv, d/2]")
+    cap, hkv = k_codes.shape[1], k_codes.shape[2]
+    for nm, tt, shp in (("k_codes", k_codes, (b, cap, hkv, d // 2)), ("v_codes", v_codes, (b, cap, hkv, d // 2)),
+                        ("k_scales", k_scales, (b, cap, hkv, d // 32)), ("v_scales", v_scales, (b, cap, hkv, d // 32))):
+        _want(tt, torch.uint8, nm, shp)
+    _want(ctx_len, torch.int32, "ctx_len", (b,))
+    masks = [int(m) for m in masks]
+    if len(masks) != t:
+        raise ValueError("one mask per query position")
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    max_len = cap if max_len is None else int(max_len)
+    if out is None:
+        out = torch.empty((b, t, hq, d), dtype=torch.float32, device=q.device)
+    _want(out, torch.float32, "out", (b, t, hq, d))
+    need = mxfp4_kv_attention_workspace_bytes(b, t, hq, hkv, max_len)
+    if need == 0:
+        raise ValueError("sizes out of range")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    _want(workspace, torch.uint8, "workspace")
+    _want_flags(dev_flags)
+    marr = (ctypes.c_uint64 * t)(*masks)
+    _check(get_lib().mxfp4_kv_attention(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                                        _ptr(ctx_len), b, t, hq, hkv, d, cap, max_len, marr, scale, _ptr(out),
+                                        _ptr(workspace), workspace.numel(), _ptr(dev_flags), _stream(stream)),
+           "mxfp4_kv_attention")
+    return out
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp4spec.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_act.hip", "accept.hip", "stream.hip", "tree.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "gemm_act.hip", "accept.hip", "stream.hip", "tree.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

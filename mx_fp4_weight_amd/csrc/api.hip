@@ -359,6 +359,38 @@ mxs_status mxfp4_kv_append(const uint16_t* kv, int64_t t, int64_t heads, int64_t
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t mxfp4_kv_attention_workspace_bytes(int32_t b, int32_t t, int32_t hq, int32_t hkv, int64_t max_len) {
+  if (b < 1 || b > 65535 || t < 1 || t > mxs::kMaxAttnPositions || hkv < 1 || hq < hkv || hq % hkv != 0 ||
+      t * (hq / hkv) > 64 || max_len < t || max_len > (int64_t(1) << 31))
+    return 0;
+  return mxs::kv_attention_workspace_bytes(b, t, hq, hkv, max_len);
+}
+
+mxs_status mxfp4_kv_attention(const uint16_t* q, const uint8_t* k_codes, const uint8_t* k_scales, const uint8_t* v_codes,
+                              const uint8_t* v_scales, const int32_t* ctx_len, int32_t b, int32_t t, int32_t hq,
+                              int32_t hkv, int32_t d, int64_t capacity, int64_t max_len, const uint64_t* masks,
+                              float scale, float* out, void* workspace, size_t workspace_bytes, int32_t* dev_flags,
+                              void* stream) {
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !ctx_len || !masks || !out || !workspace)
+    return MXS_ERR_NULL;
+  if (b < 1 || b > 65535 || t < 1 || t > mxs::kMaxAttnPositions || hkv < 1 || hq < hkv || hq % hkv != 0 ||
+      t * (hq / hkv) > 64 || d != 128 || max_len < t || max_len > capacity || capacity > (int64_t(1) << 31) ||
+      (int64_t)b * capacity * hkv > (int64_t(1) << 34))
+    return MXS_ERR_SHAPE;
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return MXS_ERR_VALUE;
+  for (int i = 0; i < t; ++i)
+    if (masks[i] >> t) return MXS_ERR_VALUE;  // a bit for a position past t
+  if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(ctx_len, 4) ||
+      !aligned(out, 4) || !aligned(workspace, 16) || !aligned(dev_flags, 4))
+    return MXS_ERR_ALIGN;
+  if (workspace_bytes < mxs::kv_attention_workspace_bytes(b, t, hq, hkv, max_len)) return MXS_ERR_WORKSPACE;
+  const mxs_status dv = check_device();
+  if (dv != MXS_OK) return dv;
+  return launched(mxs::launch_kv_attention(q, k_codes, k_scales, v_codes, v_scales, ctx_len, b, t, hq, hkv, capacity,
+                                           max_len, masks, scale, out, workspace, dev_flags,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 mxs_status mxs_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink) return MXS_ERR_NULL;
   if (bytes < 16 || bytes % 16 != 0) return MXS_ERR_SHAPE;

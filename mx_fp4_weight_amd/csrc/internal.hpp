@@ -88,6 +88,14 @@ hipError_t launch_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8
 
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
 
+// Verification attention over the MX-FP4 KV cache (d = 128; rows = t * hq / hkv <= 64).
+constexpr int kMaxAttnPositions = 64;
+size_t kv_attention_workspace_bytes(int64_t b, int t, int hq, int hkv, int64_t max_len);
+hipError_t launch_kv_attention(const uint16_t* q, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                               const uint8_t* vs, const int32_t* ctx, int32_t b, int32_t t, int32_t hq, int32_t hkv,
+                               int64_t cap, int64_t max_len, const uint64_t* masks, float scale, float* out,
+                               void* workspace, int32_t* flags, hipStream_t stream);
+
 // Tree of draft tokens (spec_accept_tree): topology passed by value to the kernels.
 constexpr int kMaxTreeNodes = 64;
 constexpr int kMaxTreeChildren = 16;

@@ -176,6 +176,29 @@ def test_tree_host_errors():
     assert call() == mxs.MXS_ERR_DEVICE
 
 
+def test_kv_attention_host_errors():
+    lib = mxs.get_lib()
+    f = lambda a: P(a) if a else None
+    need = lib.mxfp4_kv_attention_workspace_bytes(1, 5, 32, 8, 4096)
+    assert need > 0 and lib.mxfp4_kv_attention_workspace_bytes(1, 5, 32, 7, 4096) == 0
+
+    def call(q=0x1000, kc=0x2000, ks=0x3000, vc=0x4000, vs=0x5000, cl=0x6000, b=1, t=5, hq=32, hkv=8, d=128,
+             cap=4096, ml=4096, masks=None, scale=0.088, out=0x7000, ws=0x8000, wsb=None, fl=None):
+        m = (ctypes.c_uint64 * 5)(*(masks or mxs.chain_masks(5)))
+        return lib.mxfp4_kv_attention(f(q), f(kc), f(ks), f(vc), f(vs), f(cl), b, t, hq, hkv, d, cap, ml, m, scale,
+                                      f(out), f(ws), need if wsb is None else wsb, f(fl), None)
+    for a in [dict(q=0), dict(kc=0), dict(vs=0), dict(cl=0), dict(out=0), dict(ws=0)]:
+        assert call(**a) == mxs.MXS_ERR_NULL
+    for a in [dict(d=64), dict(hkv=7), dict(t=0), dict(ml=4097), dict(ml=4), dict(hq=64, hkv=2)]:
+        assert call(**a) == mxs.MXS_ERR_SHAPE
+    for a in [dict(scale=0.0), dict(scale=float("inf")), dict(masks=[1, 3, 7, 15, 32])]:
+        assert call(**a) == mxs.MXS_ERR_VALUE
+    for a in [dict(q=0x1008), dict(kc=0x2004), dict(out=0x7002), dict(ws=0x8008)]:
+        assert call(**a) == mxs.MXS_ERR_ALIGN
+    assert call(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
+    assert call() == mxs.MXS_ERR_DEVICE
+
+
 def test_kv_slot_flag_is_the_token_range_bit():
     from oracle import kvcache
     assert kvcache.FLAG_SLOT_RANGE == mxs.FLAG_TOKEN_RANGE and kvcache.FLAG_NONFINITE == mxs.FLAG_NONFINITE
