@@ -32,7 +32,7 @@ def build() -> str:
     for src in b.SOURCES:
         obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
         extra = HOST_ASAN if src == "api.hip" else []
-        cmd = [b.HIPCC, *b.FLAGS, *extra, "-c", os.path.join(b.CSRC, src), "-o", obj]
+        cmd = [b.HIPCC, *b.FLAGS, *b.SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(b.CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -4,8 +4,9 @@ The caches are coded by the oracle (oracle.kvcache) and uploaded; queries are bf
 the verify GEMM's: relative L2 <= 2e-3 over the output, and every element within
 1e-4 * sum_l p_l |V^[l]| + 1e-6 (fp32 scores and sums over at most a few thousand entries per
 workgroup, probabilities entering the value product as a bf16 pair: errors of order 1e-6 of that
-scale). Chains (lower-triangular masks), trees, grouped-query shapes with 1..4 query tiles,
-ragged contexts, a plain decode step (t = 1) and a refused sequence are covered.
+scale). Chains (lower-triangular masks), trees, grouped-query shapes from 1 to 64 query rows per
+KV head (one or two 16-row tiles, one or two groups of 32 rows), contexts that end inside a step
+of 32 entries, a plain decode step (t = 1) and a refused sequence are covered.
 """
 import numpy as np
 import pytest
@@ -61,6 +62,7 @@ def check(got, kc, ks, vc, vs, q, ctxs, masks, label):
     (3, [0, 5, 130], 3, 4, 4, "chain"),   # one query head per KV head
     (1, [2047], 1, 16, 2, "chain"),       # a plain decode step
     (1, [300], 8, 8, 4, "tree8"),         # 16 query rows: one tile exactly
+    (1, [777], 16, 8, 2, "chain"),        # 64 query rows per KV head: two groups of 32
 ])
 def test_attention_matches_oracle(b, ctxs, t, hq, hkv, masks_of):
     say(f"attention b={b} ctx={ctxs} t={t} hq={hq} hkv={hkv} {masks_of}")
