@@ -52,6 +52,8 @@ constexpr int kWPer = 4;                   // logits per thread in decide / samp
 constexpr int kPiece = kWThreads * kWPer;  // 1024 logits per piece
 constexpr int kPassBatch = 3;              // statistics passes whose loads decide keeps in flight
 constexpr int kMaxRows = 65;               // 2 * 32 + 1 rows per sequence
+constexpr int kQuadChunks = 8;             // chunks per thread when a quad combines a row
+
 
 struct Decision {
   int32_t n;      // accepted drafts, or -1 for a refused sequence
@@ -235,8 +237,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
     mx = fmaxf(mx, vals[q]);
     if (e == xi) ws.gz[rowg] = vals[q];
   }
-  mx = block_max<kThreads>(mx, lds_f);
-  bad = block_or<kThreads>(bad, lds_i);
+  block_max_or<kThreads>(mx, bad, lds_f, lds_i);
   double acc = 0.0;
   if (mx != -INFINITY && !bad) {
     const double m64 = (double)mx;
@@ -786,7 +787,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   __shared__ double smax[kMaxRows];
   __shared__ double ssum[kMaxRows];
   __shared__ int sbad[kMaxRows];
-  __shared__ double lds_d[kWThreads / kWave];
+  __shared__ double lds_d[2 * kWThreads / kWave];
   __shared__ int s_n;
   __shared__ double tab[32];  // visible after the barrier before the piece totals
   if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Table32[threadIdx.x];
@@ -826,7 +827,53 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   //    inside its segment; the loads of up to kPassBatch passes are issued together.
   int seg = 1;
   while (seg < chunks) seg <<= 1;
-  if (seg <= kWave) {
+  if (kPrefetch && chunks <= 4 * kQuadChunks && per_seq <= kWThreads / 4) {
+    // small calls: four threads per row; thread qd of row j folds chunks qd, qd + 4, ... in
+    // registers (all loads issued together), and the quad is combined by two DPP exchanges
+    const int j = (int)threadIdx.x >> 2, qd = (int)threadIdx.x & 3;
+    const bool rowok = j < per_seq;
+    const size_t o = ((size_t)s * per_seq + (rowok ? j : 0)) * chunks;
+    float cm[kQuadChunks];
+    double cs[kQuadChunks];
+    int cb[kQuadChunks];
+#pragma unroll
+    for (int i = 0; i < kQuadChunks; ++i) {
+      const int cc = qd + 4 * i;
+      const bool live = rowok && cc < chunks;
+      const size_t oo = o + (live ? cc : 0);
+      cm[i] = ws.cmax[oo];
+      cs[i] = ws.csum[oo];
+      cb[i] = ws.cbad[oo];
+      cm[i] = live ? cm[i] : -INFINITY;
+      cs[i] = live ? cs[i] : 0.0;
+      cb[i] = live ? cb[i] : 0;
+    }
+    float m = -INFINITY;
+    int bad = 0;
+#pragma unroll
+    for (int i = 0; i < kQuadChunks; ++i) {
+      m = fmaxf(m, cm[i]);
+      bad |= cb[i];
+    }
+    m = fmaxf(m, dpp_f32<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_f32<kDppQuadXor2>(m));
+    bad |= dpp_i32<kDppQuadXor1>(bad);
+    bad |= dpp_i32<kDppQuadXor2>(bad);
+    bad |= (m == -INFINITY);
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < kQuadChunks; ++i) {
+      const double dm = kT ? ((double)cm[i] - (double)m) * tr.inv_tau : (double)cm[i] - (double)m;
+      sum += (!bad && cs[i] > 0.0) ? cs[i] * exp_neg_f64(dm) : 0.0;
+    }
+    sum += dpp_f64<kDppQuadXor1>(sum);  // the same total on every thread of the quad
+    sum += dpp_f64<kDppQuadXor2>(sum);
+    if (rowok && qd == 0) {
+      smax[j] = (double)m;
+      ssum[j] = sum;
+      sbad[j] = bad;
+    }
+  } else if (seg <= kWave) {
     const int rpp = kWThreads / seg;  // rows per pass
     const int passes = (per_seq + rpp - 1) / rpp;
     const int cc = threadIdx.x % seg;
@@ -927,8 +974,8 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
     const unsigned long long rej = __ballot(!acc);  // lanes >= kd vote "accept"
     const int n = bad ? -1 : (rej ? __ffsll(rej) - 1 : kd);
     if (lane > n) f = 0;  // positions after the first rejection are not examined
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) f |= __shfl_xor(f, off);
+    f = (__ballot(f & MXS_FLAG_TOKEN_RANGE) ? MXS_FLAG_TOKEN_RANGE : 0) |
+        (__ballot(f & MXS_FLAG_Q_ZERO) ? MXS_FLAG_Q_ZERO : 0);
     if (lane == 0) s_n = n;
     if (c == 0) {
       // accepted drafts, then -1; slot n (the final draw) is written by the sample kernel
@@ -1007,8 +1054,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
         b += wp[j];
       }
     }
-    a = block_inclusive_scan_f64<kWThreads>(a, lds_d);
-    b = block_inclusive_scan_f64<kWThreads>(b, lds_d);
+    block_inclusive_scan2_f64<kWThreads>(a, b, lds_d);
     if (threadIdx.x == kWThreads - 1) {
       ws.zres[s * pieces + cp] = a;
       ws.zp[s * pieces + cp] = b;

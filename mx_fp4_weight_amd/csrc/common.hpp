@@ -113,11 +113,85 @@ __host__ __device__ inline double exp_neg_f64_tab(double d, const double* tab) {
   return __builtin_ldexp(tab[n & 31] * p, n >> 5);
 }
 
+// Lane exchanges inside a wave. DPP moves (a VALU operand modifier, no LDS trip) cover the
+// steps inside each 16-lane row: swaps within groups of four, then rotations of the row by 4
+// and 8; the two steps across rows (16, 32) go through ds_bpermute.
+constexpr int kDppQuadXor1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);  // lane ^ 1
+constexpr int kDppQuadXor2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);  // lane ^ 2
+constexpr int kDppRowRor4 = 0x124;                                 // rotate the row by 4
+constexpr int kDppRowRor8 = 0x128;                                 // rotate the row by 8
+template <int kCtrl>
+__device__ inline int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ inline float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<kCtrl>(__float_as_int(v)));
+}
+template <int kCtrl>
+__device__ inline double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)dpp_i32<kCtrl>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)dpp_i32<kCtrl>((int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Wave-wide reductions (every lane of the wave active). wave_max and wave_or give every lane
+// the result; wave_sum_f64 adds in a fixed order and the result of lane 0 is the one to use
+// (other lanes may differ in the last bit).
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ inline int wave_or(int v) {
+  v |= dpp_i32<kDppQuadXor1>(v);
+  v |= dpp_i32<kDppQuadXor2>(v);
+  v |= dpp_i32<kDppRowRor4>(v);
+  v |= dpp_i32<kDppRowRor8>(v);
+  v |= __shfl_xor(v, 16);
+  return v | __shfl_xor(v, 32);
+}
+__device__ inline double wave_sum_f64(double v) {
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppRowRor4>(v);
+  v += dpp_f64<kDppRowRor8>(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// Inclusive fp64 scan over the wave in lane order (every lane active): shifts of 1, 2, 4, 8
+// inside each 16-lane row (DPP, lanes before the row start add 0), then each row adds the
+// totals of the rows before it, read from lanes 15, 31 and 47 and added in row order. The
+// order of the additions is fixed, so the same inputs give the same outputs.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+__device__ inline double readlane_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ inline double wave_inclusive_scan_f64(double v) {
+  v += dpp_f64<kDppRowShr1>(v);
+  v += dpp_f64<kDppRowShr2>(v);
+  v += dpp_f64<kDppRowShr4>(v);
+  v += dpp_f64<kDppRowShr8>(v);
+  const double r0 = readlane_f64(v, 15), r1 = readlane_f64(v, 31), r2 = readlane_f64(v, 47);
+  const int row = (int)(threadIdx.x & (kWave - 1)) >> 4;
+  double base = row >= 1 ? r0 : 0.0;
+  base = row >= 2 ? base + r1 : base;
+  base = row >= 3 ? base + r2 : base;
+  return base + v;
+}
+
 // Block-wide reductions through LDS for blockDim.x == kThreads (a multiple of 64).
 template <int kThreads>
 __device__ inline float block_max(float v, float* lds) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = wave_max(v);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
   __syncthreads();
@@ -128,12 +202,34 @@ __device__ inline float block_max(float v, float* lds) {
   return r;
 }
 
-// Deterministic fp64 block sum: a fixed butterfly inside each wave, then the
+// block_max of m and block_or of f in one round of barriers.
+template <int kThreads>
+__device__ inline void block_max_or(float& m, int& f, float* lds_f, int* lds_i) {
+  m = wave_max(m);
+  f = wave_or(f);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lds_f[w] = m;
+    lds_i[w] = f;
+  }
+  __syncthreads();
+  float r = lds_f[0];
+  int o = lds_i[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) {
+    r = fmaxf(r, lds_f[i]);
+    o |= lds_i[i];
+  }
+  __syncthreads();
+  m = r;
+  f = o;
+}
+
+// Deterministic fp64 block sum: a fixed order inside each wave (lane 0's total), then the
 // wave totals in wave order.
 template <int kThreads>
 __device__ inline double block_sum_f64(double v, double* lds) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_sum_f64(v);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
   __syncthreads();
@@ -146,8 +242,7 @@ __device__ inline double block_sum_f64(double v, double* lds) {
 
 template <int kThreads>
 __device__ inline int block_or(int v, int* lds) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
+  v = wave_or(v);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
   __syncthreads();
@@ -159,17 +254,13 @@ __device__ inline int block_or(int v, int* lds) {
 }
 
 // Inclusive fp64 scan of one value per thread over the block, in thread order:
-// Hillis–Steele steps inside each wave, then the exclusive prefix of the wave
+// wave_inclusive_scan_f64 inside each wave, then the exclusive prefix of the wave
 // totals. Same inputs always give bit-identical outputs.
 template <int kThreads>
 __device__ inline double block_inclusive_scan_f64(double v, double* lds) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_inclusive_scan_f64(v);
   if (lane == kWave - 1) lds[w] = v;
   __syncthreads();
   double base = 0.0;
@@ -178,6 +269,31 @@ __device__ inline double block_inclusive_scan_f64(double v, double* lds) {
     if (i < w) base += lds[i];
   __syncthreads();
   return base + v;
+}
+
+// Two block_inclusive_scan_f64 at once (the same arithmetic for each value, so each result is
+// bit-identical to its own call; the two chains overlap). lds: 2 * kThreads / kWave.
+template <int kThreads>
+__device__ inline void block_inclusive_scan2_f64(double& a, double& b, double* lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  a = wave_inclusive_scan_f64(a);
+  b = wave_inclusive_scan_f64(b);
+  if (lane == kWave - 1) {
+    lds[w] = a;
+    lds[kThreads / kWave + w] = b;
+  }
+  __syncthreads();
+  double base_a = 0.0, base_b = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i)
+    if (i < w) {
+      base_a += lds[i];
+      base_b += lds[kThreads / kWave + i];
+    }
+  __syncthreads();
+  a = base_a + a;
+  b = base_b + b;
 }
 
 }  // namespace mxs

@@ -93,8 +93,7 @@ __global__ __launch_bounds__(kTh) void tree_stats_kernel(const float* __restrict
     bad |= (vals[q] != vals[q]) | (vals[q] == INFINITY);
     mx = fmaxf(mx, vals[q]);
   }
-  mx = block_max<kTh>(mx, lds_f);
-  bad = block_or<kTh>(bad, lds_i);
+  block_max_or<kTh>(mx, bad, lds_f, lds_i);
   double acc = 0.0;
   if (mx != -INFINITY && !bad) {
     const double m64 = (double)mx;
@@ -127,8 +126,7 @@ __device__ RowStat row_stat(const TreeWs& ws, int64_t s, int n, int j, int chunk
     m = fmaxf(m, ws.cmax[o + c]);
     bad |= ws.cbad[o + c];
   }
-  m = block_max<kTh>(m, lds_f);
-  bad = block_or<kTh>(bad, lds_i);
+  block_max_or<kTh>(m, bad, lds_f, lds_i);
   RowStat r;
   r.m = (double)m;
   r.bad = bad | (m == -INFINITY);
