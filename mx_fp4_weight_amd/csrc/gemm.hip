@@ -440,9 +440,12 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void gemm_skinny_kernel(const Gr
   stage(0);
 #pragma unroll
   for (int i = 0; i < D; ++i) load(i, buf[i]);
-  // the direct loads are counted by vmcnt; wait for them (and the first units). No
-  // barrier: a wave reads only the columns it staged itself.
-  __builtin_amdgcn_s_waitcnt(0);
+  // The direct loads are counted by vmcnt and were issued first: wait for them and the first
+  // unit only (the later units' loads, kUnitLoads each, stay in flight while it is computed).
+  // No barrier: a wave reads only the columns it staged itself.
+  constexpr int kUnitLoads = R * G + R * (kNv ? G / 2 : G / 4);
+  static_assert((D - 1) * kUnitLoads < 64, "vmcnt holds at most 63");
+  __builtin_amdgcn_s_waitcnt(vmcnt_only((D - 1) * kUnitLoads));
   for (int u = 0; u < nunits; u += D) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -847,10 +850,11 @@ inline int y_vec4_ok(const float* y, int64_t n) {
   return (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
 }
 
-// Waves per workgroup and sub-slices per wave for a k of `ngroups` 128-k groups.
-inline void split_k(int64_t ngroups, int G, int& waves, int& nsub) {
+// Waves per workgroup (at most max_waves) and sub-slices per wave for a k of `ngroups`
+// 128-k groups.
+inline void split_k(int64_t ngroups, int G, int max_waves, int& waves, int& nsub) {
   const int64_t slices = (ngroups + G - 1) / G;  // sub-slices of G groups
-  nsub = (int)((slices + kMaxWaves - 1) / kMaxWaves);
+  nsub = (int)((slices + max_waves - 1) / max_waves);
   waves = (int)((ngroups + (int64_t)G * nsub - 1) / ((int64_t)G * nsub));
 }
 
@@ -873,8 +877,12 @@ inline bool plan_phases(int64_t k, int64_t m, int R, int G, PhasePlan& pp, int p
     int64_t ngp = (ngroups + phases - 1) / phases;
     if (phases > 1) ngp = (ngp + 3) / 4 * 4;
     if (phases > 1 && (phases - 1) * ngp >= ngroups) continue;  // no empty phase
+    // Two resident workgroups per CU (k <= 4096) take four waves of two sub-slices each rather
+    // than eight of one: the 8B-class q | k | v 8.38 -> 7.68 µs and gate | up 16.2 -> 15.6 µs at
+    // T = 5 (o unchanged); with one workgroup per CU and long k, eight waves stay (down
+    // 4096 x 14336: 10.7 µs against 11.9 with four).
     int waves, nsub;
-    split_k(ngp, G, waves, nsub);
+    split_k(ngp, G, per_cu > 1 ? kMaxWaves / 2 : kMaxWaves, waves, nsub);
     const int64_t xrs = (int64_t)waves * nsub * G * 16 + 1;  // padded row stride, 16-byte units
     const size_t xb = (size_t)(mt * xrs) * 16, rb = sizeof(f32x4) * waves * R * kWave;
     if (xb + 2 * rb <= kMaxLds) {
