@@ -78,3 +78,30 @@ def test_row_subset_matches_full():
     assert np.array_equal(sub, full[:, [8, 0, 3]])
     b = gemm.abs_bound(codes, scales, n, k, x)
     assert np.all(b >= np.abs(full) - 1e-15)
+
+
+def test_abs_bound_bruteforce_and_properties():
+    """abs_bound = sum_k |x_k w_k|: exact rational brute force over the nibbles; equal to |y| when
+    every product is non-negative; unchanged when activations change sign."""
+    codes, scales, x, m, n, k = _small_case(m=2, n=3, k=64, seed=5)
+    b = gemm.abs_bound(codes, scales, n, k, x)
+    flat = codes.reshape(-1)
+    for t in range(m):
+        for r in range(n):
+            acc = Fraction(0)
+            for c in range(k):
+                byte = int(flat[r * k // 2 + c // 2])
+                nib = byte & 0xF if c % 2 == 0 else byte >> 4
+                wv = Fraction(mx.e2m1_decode(nib)) * Fraction(2) ** (int(scales[r, c // 32]) - 127)
+                xv = Fraction(float(np.array([int(x[t, c]) << 16], np.uint32).view(np.float32)[0]))
+                acc += abs(wv * xv)
+            assert abs(b[t, r] - float(acc)) <= 1e-12 * float(acc)
+    # non-negative weights (codes 0..7) and activations: the bound is the product itself
+    pos_codes = (codes & 0x77).astype(np.uint8)
+    xf = (np.asarray(x, np.uint32) << 16).view(np.float32)
+    xa = synth.f32_to_bf16_bits(np.abs(xf))  # |bf16| is a bf16 value: exact
+    y = gemm.verify_gemm(pos_codes, scales, n, k, xa)
+    assert np.allclose(gemm.abs_bound(pos_codes, scales, n, k, xa), y, rtol=1e-14, atol=0)
+    # the sign of the activations does not matter
+    neg = (np.asarray(x, np.uint16) ^ np.uint16(0x8000)).astype(np.uint16)
+    assert np.array_equal(gemm.abs_bound(codes, scales, n, k, neg), b)
