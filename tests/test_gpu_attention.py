@@ -97,3 +97,33 @@ def test_refused_sequence_and_max_len():
     got = run(kc, ks, vc, vs, q, ctxs, mxs.chain_masks(t), max_len=40, flags=flags)
     assert np.all(np.isnan(got[1])) and int(flags.item()) == mxs.FLAG_TOKEN_RANGE
     check(got[:1], kc[:1], ks[:1], vc[:1], vs[:1], q[:1], ctxs[:1], mxs.chain_masks(t), "max_len")
+
+
+def test_append_then_attend_on_device():
+    """The verification pass end to end on the device: the prefix cache is coded by the oracle,
+    the T new keys and values are appended by mxfp4_kv_append on the GPU, and the attention reads
+    the cache the GPU wrote. The oracle appends the same bf16 rows itself and attends over its own
+    cache; the appended bytes must be identical and the outputs within the parity bar."""
+    say("attention after a device append")
+    b, t, hq, hkv, d = 2, 5, 16, 4, 128
+    ctxs = [300, 1023]
+    cap = max(ctxs) + t + 8
+    kc, ks, vc, vs, q = build(21, b, [c for c in ctxs], 0, hq, hkv, cap)  # prefixes only
+    newk = [synth.activations(21, 40 + s, t * hkv, d, sigma=1.0).reshape(t, hkv, d) for s in range(b)]
+    newv = [synth.activations(21, 50 + s, t * hkv, d).reshape(t, hkv, d) for s in range(b)]
+    q = synth.activations(21, 60, b * t * hq, d).reshape(b, t, hq, d)
+    dkc, dks, dvc, dvs = dev(kc), dev(ks), dev(vc), dev(vs)
+    for s in range(b):
+        slots = dev(np.arange(ctxs[s], ctxs[s] + t, dtype=np.int32))
+        mxs.mxfp4_kv_append(dev_bf16(newk[s]).view(t, hkv, d), slots, dkc[s], dks[s])
+        mxs.mxfp4_kv_append(dev_bf16(newv[s]).view(t, hkv, d), slots, dvc[s], dvs[s])
+        kvcache.append(kc[s], ks[s], newk[s], range(ctxs[s], ctxs[s] + t))
+        kvcache.append(vc[s], vs[s], newv[s], range(ctxs[s], ctxs[s] + t))
+    torch.cuda.synchronize()
+    for dv_, hv in ((dkc, kc), (dks, ks), (dvc, vc), (dvs, vs)):
+        assert np.array_equal(host(dv_), hv)
+    masks = mxs.chain_masks(t)
+    out = mxs.mxfp4_kv_attention(dev_bf16(q).view(q.shape), dkc, dks, dvc, dvs,
+                                 dev(np.asarray(ctxs, np.int32)), masks)
+    torch.cuda.synchronize()
+    check(host(out).astype(np.float64), kc, ks, vc, vs, q, ctxs, masks, "append+attend")
