@@ -1,7 +1,8 @@
 """Host-sanitizer build of the C-ABI layer, for the CPU checks of its argument validation.
 
 api.hip (the entry points: argument checks, topology building, dispatch) is compiled with
-AddressSanitizer on its HOST code only (device code is built as usual) and linked with the
+AddressSanitizer and UndefinedBehaviorSanitizer on its HOST code only (device code is built as
+usual) and linked with the
 regular objects of the kernel files into <repo>/_build/asan/libmxfp4spec.so. Run
 tests/test_abi_cpu.py against it with MXS_LIB pointing there and the clang ASan runtime
 preloaded (tests/test_abi_asan.py does both).
@@ -16,7 +17,10 @@ from mx_fp4_weight_amd import build as b
 
 OUT_DIR = os.path.join(b.BUILD, "asan")
 LIB = os.path.join(OUT_DIR, "libmxfp4spec.so")
-HOST_ASAN = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+# AddressSanitizer and UndefinedBehaviorSanitizer (shifts past the width, overflow, bad
+# alignment, ... abort the process) on the host code only.
+HOST_ASAN = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer").split()
 
 
 def asan_runtime() -> str | None:
@@ -37,7 +41,7 @@ def build() -> str:
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
         objs.append(obj)
-    cmd = [b.HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_ASAN[:2], *objs, "-o", LIB]
+    cmd = [b.HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_ASAN[:4], *objs, "-o", LIB]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -379,7 +379,7 @@ mxs_status mxfp4_kv_attention(const uint16_t* q, const uint8_t* k_codes, const u
     return MXS_ERR_SHAPE;
   if (!(scale > 0.0f) || !(scale < INFINITY)) return MXS_ERR_VALUE;
   for (int i = 0; i < t; ++i)
-    if (masks[i] >> t) return MXS_ERR_VALUE;  // a bit for a position past t
+    if (t < 64 && (masks[i] >> t)) return MXS_ERR_VALUE;  // a bit for a position past t (none at t = 64)
   if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(ctx_len, 4) ||
       !aligned(out, 4) || !aligned(workspace, 16) || !aligned(dev_flags, 4))
     return MXS_ERR_ALIGN;

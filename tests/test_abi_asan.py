@@ -1,4 +1,4 @@
-"""The C-ABI layer's host code under AddressSanitizer (CPU only).
+"""The C-ABI layer's host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
 
 Builds api.hip with host-side ASan (mx_fp4_weight_amd.build_asan) and runs the CPU checks of
 tests/test_abi_cpu.py against that library in a child python with the ASan runtime preloaded:
@@ -32,4 +32,5 @@ def test_abi_checks_under_host_asan():
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
     assert "AddressSanitizer" not in out, out[-4000:]
+    assert "runtime error" not in out, out[-4000:]  # UndefinedBehaviorSanitizer
     assert r.returncode == 0, out[-4000:]

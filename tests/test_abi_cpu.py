@@ -197,6 +197,18 @@ def test_kv_attention_host_errors():
         assert call(**a) == mxs.MXS_ERR_ALIGN
     assert call(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
     assert call() == mxs.MXS_ERR_DEVICE
+    # T = 64 (every bit of a mask may be set): the masks are valid, the call reaches the device
+    # check; one bit past t is refused for t < 64
+    need64 = lib.mxfp4_kv_attention_workspace_bytes(1, 64, 1, 1, 4096)
+    m64 = (ctypes.c_uint64 * 64)(*mxs.chain_masks(64))
+    assert m64[63] == (1 << 64) - 1
+    assert lib.mxfp4_kv_attention(f(0x1000), f(0x2000), f(0x3000), f(0x4000), f(0x5000), f(0x6000), 1, 64, 1, 1,
+                                  128, 4096, 4096, m64, 0.088, f(0x7000), f(0x8000), need64, None,
+                                  None) == mxs.MXS_ERR_DEVICE
+    m63 = (ctypes.c_uint64 * 63)(*(mxs.chain_masks(62) + [1 << 63]))
+    assert lib.mxfp4_kv_attention(f(0x1000), f(0x2000), f(0x3000), f(0x4000), f(0x5000), f(0x6000), 1, 63, 1, 1,
+                                  128, 4096, 4096, m63, 0.088, f(0x7000), f(0x8000), need64, None,
+                                  None) == mxs.MXS_ERR_VALUE
 
 
 def test_kv_slot_flag_is_the_token_range_bit():

@@ -63,6 +63,8 @@ def check(got, kc, ks, vc, vs, q, ctxs, masks, label):
     (1, [2047], 1, 16, 2, "chain"),       # a plain decode step
     (1, [300], 8, 8, 4, "tree8"),         # 16 query rows: one tile exactly
     (1, [777], 16, 8, 2, "chain"),        # 64 query rows per KV head: two groups of 32
+    (1, [60000], 4, 4, 1, "chain"),       # one KV head: 469 entry ranges (merged in batches of 32)
+    (2, [63, 200], 64, 2, 2, "chain"),    # T = 64 with one query head per KV head: 64 rows
 ])
 def test_attention_matches_oracle(b, ctxs, t, hq, hkv, masks_of):
     say(f"attention b={b} ctx={ctxs} t={t} hq={hq} hkv={hkv} {masks_of}")
