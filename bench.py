@@ -1219,7 +1219,7 @@ def main():
         "numerics": "E2M1 weights decoded exactly to bf16, bf16 x bf16 products summed in fp32 (MFMA); "
                     "spec_accept probabilities in fp64",
         "roofline": {
-            "kernel": ("gemm_skinny_kernel<1, 4, 2, false, false, true> (mxfp4_verify_gemm_tiled / "
+            "kernel": ("gemm_skinny_kernel<1, 4, 2, false, false, true, true> (mxfp4_verify_gemm_tiled / "
                        "mxfp4_verify_gemm_grouped_tiled: tiled weight codes and scales)") if args.layout == "tiled"
                       else "gemm_skinny_kernel<1, 4, 2, false, false, false> (mxfp4_verify_gemm / _grouped)",
             "bound": "hbm",
