@@ -166,7 +166,9 @@ def _label(name, wgs, lds, grid_y):
         return "weight prep (one-off, untimed)"
     if "stream_read" in name:
         return "read-stream ceiling"
-    if any(a in name for a in ("stats_kernel", "decide_kernel", "sample_kernel", "sel_")):
+    if "sel_" in name:
+        return "top-k / top-p thresholds (spec_accept_sampled)"
+    if any(a in name for a in ("stats_kernel", "decide_kernel", "sample_kernel")):
         return "spec_accept"
     if "gemm_skinny" in name:
         return {384: "q|k|v grouped", 512: "gate|up grouped",

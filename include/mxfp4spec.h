@@ -412,7 +412,7 @@ mxs_status spec_accept_noalloc(const float* target_logits, const float* draft_lo
 
 /*
  * spec_accept_sampled_workspace_bytes — device workspace spec_accept_sampled
- * needs for (b, kd, v): spec_accept's plus ~74 KB per logit row for the top-k /
+ * needs for (b, kd, v): spec_accept's plus ~80 KB per logit row for the top-k /
  * top-p selection. Returns 0 when the sizes are out of range.
  */
 size_t spec_accept_sampled_workspace_bytes(int32_t b, int32_t kd, int32_t v);
@@ -458,6 +458,44 @@ mxs_status spec_accept_sampled(const float* target_logits, const float* draft_lo
                                float top_p, const uint32_t* mask, int32_t* out_tokens,
                                int32_t* out_num_accepted, void* workspace,
                                size_t workspace_bytes, int32_t* dev_flags, void* stream);
+
+/*
+ * spec_sampling_thresholds_workspace_bytes — device workspace spec_sampling_thresholds
+ * needs for `rows` rows (~80 KB per row). Returns 0 when the sizes are out of range.
+ */
+size_t spec_sampling_thresholds_workspace_bytes(int32_t rows, int32_t v);
+
+/*
+ * spec_sampling_thresholds — the top-k / top-p selection of spec_accept_sampled on its own,
+ * for `rows` independent logit rows [M11 §4: the draft's tokens must be drawn from the same
+ * transformed law the acceptance test uses, so a draft sampler needs these sets too].
+ *
+ * A row's kept set is {t : mask bit t set, logit finite, key(z_t) >= out_thresholds[row]},
+ * where key is the order-preserving map of an fp32 logit to uint32 (bits | 0x80000000 for
+ * z >= 0, ~bits for z < 0; -0 maps as +0). It is the set spec_accept_sampled's rule gives:
+ * mask, then top-k (ties at the k-th value all stay), then top-p on the law top-k left, with
+ * masses exp((z - max z) / temperature). A threshold of 0 keeps every allowed finite token
+ * (also returned when top-k and top-p are both off, or the row has no allowed finite logit).
+ *
+ * logits          [rows, v] fp32 device, row-major, 4-byte aligned.
+ * temperature     > 0 and finite; top_k >= 0 (0 or >= v: off); top_p in (0, 1] (1: off).
+ *                 The top-p boundary sums are fp64; when top-p is on without top-k, the mass
+ *                 above the boundary's bucket is summed in an unspecified order, so a token
+ *                 whose strictly-larger mass is within ~1e-15 * S of top_p * S can fall on
+ *                 either side.
+ * mask            [rows, ceil(v/32)] uint32 device bits (1 = allowed), or NULL.
+ * out_thresholds  [rows] uint32 device, written.
+ * workspace       at least spec_sampling_thresholds_workspace_bytes(rows, v) device bytes,
+ *                 16-byte aligned, no initial contents required.
+ * stream          hipStream_t or NULL. Asynchronous; host errors come back before any launch:
+ *                 MXS_ERR_NULL, MXS_ERR_SHAPE (rows outside [1, 2^22], v outside [2, 2^26]),
+ *                 MXS_ERR_VALUE (temperature, top_k, top_p), MXS_ERR_ALIGN,
+ *                 MXS_ERR_WORKSPACE, MXS_ERR_DEVICE.
+ */
+mxs_status spec_sampling_thresholds(const float* logits, int32_t rows, int32_t v, float temperature,
+                                    int32_t top_k, float top_p, const uint32_t* mask,
+                                    uint32_t* out_thresholds, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /*
  * spec_accept_tree_workspace_bytes — device workspace spec_accept_tree needs for this tree

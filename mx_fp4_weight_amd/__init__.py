@@ -32,7 +32,8 @@ FLAG_RESIDUAL_ZERO = 8
 
 EXPORTS = ["mxs_status_string", "mxs_abi_version", "mxfp4_quantize", "mxfp4_verify_gemm",
            "mxfp4_verify_gemm_grouped", "spec_accept_workspace_bytes", "spec_accept",
-           "spec_accept_sampled_workspace_bytes", "spec_accept_sampled", "nvfp4_quantize",
+           "spec_accept_sampled_workspace_bytes", "spec_accept_sampled",
+           "spec_sampling_thresholds_workspace_bytes", "spec_sampling_thresholds", "nvfp4_quantize",
            "nvfp4_verify_gemm", "nvfp4_verify_gemm_grouped", "mx_quantize_act", "mx_verify_gemm_act",
            "mxfp4_tiled_bytes", "mxfp4_tile_codes", "mxfp4_tiled_scale_bytes", "mxfp4_tile_scales",
            "mx_verify_gemm_act_tiled", "mxfp4_verify_gemm_tiled", "mxfp4_verify_gemm_grouped_tiled",
@@ -103,6 +104,10 @@ def _load() -> ctypes.CDLL:
     lib.spec_accept_sampled.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp,
                                         ctypes.c_size_t, vp, vp]
     lib.spec_accept_sampled.restype = ctypes.c_int
+    lib.spec_sampling_thresholds_workspace_bytes.argtypes = [i32, i32]
+    lib.spec_sampling_thresholds_workspace_bytes.restype = ctypes.c_size_t
+    lib.spec_sampling_thresholds.argtypes = [vp, i32, i32, f32, i32, f32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.spec_sampling_thresholds.restype = ctypes.c_int
     lib.nvfp4_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     lib.nvfp4_quantize.restype = ctypes.c_int
     lib.nvfp4_verify_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp, vp]
@@ -520,6 +525,37 @@ def spec_accept_sampled(target: torch.Tensor, draft: torch.Tensor | None, tokens
                                          _ptr(out_tokens), _ptr(out_num), _ptr(workspace), workspace.numel(),
                                          _ptr(dev_flags), _stream(stream)), "spec_accept_sampled")
     return out_tokens, out_num
+
+
+def spec_sampling_thresholds_workspace_bytes(rows: int, v: int) -> int:
+    return int(get_lib().spec_sampling_thresholds_workspace_bytes(rows, v))
+
+
+def spec_sampling_thresholds(logits: torch.Tensor, temperature: float = 1.0, top_k: int = 0,
+                             top_p: float = 1.0, mask: torch.Tensor | None = None,
+                             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+    """Top-k / top-p thresholds of fp32 logit rows [rows, v] (see the C header).
+
+    Returns int32 [rows] holding the uint32 order-key thresholds (token t of a row is kept iff
+    allowed, finite and key(z_t) >= threshold). mask: int32 [rows, ceil(v/32)] of uint32 words.
+    """
+    _want(logits, torch.float32, "logits")
+    rows, v = logits.shape
+    if mask is not None:
+        _want(mask, torch.int32, "mask", (rows, (v + 31) // 32))
+    dev = logits.device
+    if out is None:
+        out = torch.empty((rows,), dtype=torch.int32, device=dev)
+    _want(out, torch.int32, "out", (rows,))
+    need = spec_sampling_thresholds_workspace_bytes(rows, v)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _want(workspace, torch.uint8, "workspace")
+    _check(get_lib().spec_sampling_thresholds(_ptr(logits), rows, v, float(temperature), int(top_k),
+                                              float(top_p), _ptr(mask), _ptr(out), _ptr(workspace),
+                                              workspace.numel(), _stream(stream)), "spec_sampling_thresholds")
+    return out
 
 
 def nvfp4_quantize(w: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,

@@ -28,6 +28,7 @@
 // end. Rounding guards: if no crossing is found where the level above
 // placed it, the last positive-weight token of that range is taken, so a
 // zero-weight token is never returned.
+#include <algorithm>
 #include <atomic>
 
 #include "common.hpp"
@@ -77,7 +78,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
   size_t cmax, csum, cbad, gz, dec, zres, zp;
   // sampling transforms only
-  size_t thr, selmax, selcnt, selmass, selstate, selarrive;
+  size_t thr, selcnt, selmass, selstate, selarrive, selrkey, selcandn, selcand;
   size_t total;
 };
 
@@ -104,11 +105,9 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v, bool sampled = false) {
   L.zp = off;
   off = align256(off + sizeof(double) * b * pieces);
   if (sampled) {
-    constexpr size_t kBuckets = 2048, kStateBytes = 32;
+    constexpr size_t kBuckets = 4096, kStateBytes = 48, kCandKeys = 8192;
     L.thr = off;
     off = align256(off + sizeof(uint32_t) * rows);
-    L.selmax = off;
-    off = align256(off + sizeof(float) * rows * chunks);
     L.selcnt = off;
     off = align256(off + sizeof(uint32_t) * rows * kBuckets);
     L.selmass = off;
@@ -117,6 +116,12 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v, bool sampled = false) {
     off = align256(off + kStateBytes * rows);
     L.selarrive = off;
     off = align256(off + sizeof(uint32_t) * rows);
+    L.selrkey = off;
+    off = align256(off + sizeof(uint32_t) * rows);
+    L.selcandn = off;
+    off = align256(off + sizeof(uint32_t) * rows);
+    L.selcand = off;
+    off = align256(off + sizeof(uint32_t) * rows * kCandKeys);
   }
   L.total = off;
   return L;
@@ -503,46 +508,85 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces
 }
 
 // ---------------------------------------------------------------- top-k / top-p thresholds
-// A row's threshold is an order key: a token stays iff its key is at least the
-// threshold. Both selections are radix walks over the 32-bit keys of the allowed
-// finite logits, top digit (11 bits) first, bottom digit (10 bits) last. A pass over
-// the row histograms the current digit of the tokens whose higher digits equal the
-// prefix found so far (counts for top-k; counts and fp64 masses exp((z - max) / tau)
-// of the tokens top-k kept, for top-p), each workgroup in LDS, then added into the
-// row's histogram in the workspace. The last workgroup of the row to finish walks
-// that histogram from the largest key down and takes the lowest non-empty bucket
-// whose tokens still have fewer than k tokens (top-k) or less than P·S mass (top-p)
-// strictly above them; its digit extends the prefix. It then clears the histogram
-// and the arrival counter for the next pass. After the last digit the prefix is the
-// row's threshold.
-constexpr int kSelBuckets = 2048;
-constexpr int kSelDigits = 3;
-__host__ __device__ constexpr int sel_shift(int d) { return d == 0 ? 21 : (d == 1 ? 10 : 0); }
-__host__ __device__ constexpr int sel_width(int d) { return d == 2 ? 10 : 11; }
+// A row's threshold is an order key: a token stays iff it is allowed, finite and its key
+// is at least the threshold (0 keeps every allowed finite token). The key splits into
+// digit 0 (its top 12 bits: sign, exponent and 3 fraction bits of the logit) and two
+// 10-bit digits. Per call:
+//   sel_clear     zeroes each row's digit-0 histogram, counters and maximum.
+//   sel_count     grid (rows, 4096-logit chunks), one read of the logits: the row maximum
+//                 (an atomic max of order keys) and the digit-0 histogram: counts for top-k;
+//                 for top-p alone counts and masses exp(z / tau) against the reference 0,
+//                 which needs no row maximum. The row's last workgroup to arrive finds the
+//                 digit-0 bucket holding the boundary (the lowest non-empty bucket with fewer
+//                 than k tokens, or less than P·S mass, strictly above it) and sets the row's
+//                 course (SelMode).
+//   sel_collect   grid (rows, chunks), one read: the candidate keys into the row's list — for
+//                 top-k every key from the boundary bucket up (fewer than k + the bucket's
+//                 count), for top-p the boundary bucket's keys.
+//   sel_finish    one workgroup per row: sorts the candidates in LDS (descending keys) and
+//                 reads the thresholds off the sorted list: top-k is the k-th key; top-p tests
+//                 each distinct key's strictly-larger mass, summed in the sorted order. A row
+//                 whose candidates do not fit the list, a top-p row whose top-k kept every
+//                 token, and a top-p row whose exp(z / tau) would leave fp64's range against 0
+//                 are finished by this workgroup alone with radix passes over the row
+//                 (histograms in LDS, masses against the row maximum).
+// The digit-0 histograms are added with device-scope atomics; each workgroup waits for its
+// own before it counts its arrival, and the resolving workgroup reads them with device-scope
+// loads: no plain store is shared between workgroups of one launch.
+constexpr int kSelBits0 = 12;
+constexpr int kSelB0 = 1 << kSelBits0;      // digit-0 buckets
+constexpr int kSelShift0 = 32 - kSelBits0;  // digit 0 = key >> 20
+constexpr int kSelBits1 = 10;               // digits 1 and 2
+constexpr int kCand = 8192;                 // candidate keys per row
+constexpr int kFThreads = 512;              // sel_finish
+constexpr int kFWaves = kFThreads / kWave;
+// top-p alone takes its digit-0 masses against the reference 0 when the row maximum m has
+// m / tau in this range: every exp(z / tau) and their sum stay finite, and a token that
+// underflows against 0 has mass below e^-45 of the maximum's (it cannot sit at a boundary
+// that P < 1 - 2^-24 places among at most 2^26 tokens).
+constexpr double kRef0Lo = -650.0, kRef0Hi = 690.0;
 
-struct SelState {
-  uint32_t prefix;  // resolved key digits (key >> shift of the last resolved digit)
-  uint32_t thr_k;   // top-k threshold once resolved (0: top-k off)
-  double carry;     // count (top-k) or mass (top-p) strictly above the prefix's key range
-  double s1;        // top-p: mass of the law top-k left
-  float rmax;       // largest allowed finite logit of the row
-  int empty;        // no allowed finite logit (or nothing to select): threshold 0
+enum SelMode : uint32_t {
+  kSelDone = 0,       // threshold known: state.thr
+  kSelCompactK = 1,   // candidates: every key >= state.lo (top-k, then top-p on them)
+  kSelCompactP = 2,   // candidates: the keys of digit-0 bucket state.lo (top-p)
+  kSelSlowK = 3,      // top-k continues in digit-0 bucket state.lo by sel_finish's radix passes
+  kSelSlowP = 4,      // top-p likewise
+  kSelSlowPFull = 5,  // top-p over every allowed token by sel_finish's radix passes
 };
 
+struct SelState {
+  uint32_t mode;   // SelMode
+  uint32_t lo;     // kSelCompactK: lowest candidate key; else the boundary's digit-0 bucket
+  uint32_t thr;    // kSelDone: the threshold
+  uint32_t pad;
+  double carry;    // count (top-k) or mass (top-p) strictly above the bucket
+  double s1;       // top-p: S, the mass of the tokens top-k left
+  float rmax;      // largest allowed finite logit (the mass reference)
+  uint32_t pad2[3];
+};
+static_assert(sizeof(SelState) == 48, "workspace layout assumes a 48-byte selection state");
+
 struct SelBufs {
-  uint32_t* cnt;     // [rows][kSelBuckets]
-  double* mass;      // [rows][kSelBuckets]
+  uint32_t* cnt;     // [rows][kSelB0] digit-0 counts
+  double* mass;      // [rows][kSelB0] digit-0 masses
   SelState* state;   // [rows]
-  uint32_t* arrive;  // [rows] workgroups of the current pass that have finished
-  float* cmax;       // [rows][chunks] chunk maxima of the allowed finite logits
-  uint32_t* thr;     // [rows] output thresholds
+  uint32_t* arrive;  // [rows] workgroups of the current launch that have finished
+  uint32_t* rkey;    // [rows] order key of the row maximum (0: no allowed finite logit)
+  uint32_t* candn;   // [rows] candidate keys collected
+  uint32_t* cand;    // [rows][kCand]
+  uint32_t* thr;     // [rows] the thresholds
 };
 
 struct SelArgs {
   int top_k;     // 0: off
   double top_p;  // >= 1: off
 };
-static_assert(sizeof(SelState) == 32, "workspace layout assumes a 32-byte selection state");
+
+// The logit of an order key (inverse of order_key; -0 comes back as +0).
+__device__ inline float key_logit(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 
 // The allowed logits of this thread's 16 tokens of a chunk (removed ones: NaN), in the
 // stats kernel's order.
@@ -578,198 +622,543 @@ __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t*
   }
 }
 
-// Walk the histogram of `digit` (mode 0: counts against k; mode 1: masses against P·S)
-// and extend st.prefix with the boundary bucket. Every thread returns the same state.
-// The histogram was filled by atomics of other workgroups of the same launch: it is
-// read with agent-scope atomic loads.
-__device__ void sel_resolve(int mode, int digit, uint32_t* cnt, double* mass, const SelArgs& sa,
-                            SelState& st,
-                            double* lds_scan, double* s_excl, int* s_fl, int* s_best,
-                            double* s_above) {
-  const int nb = 1 << sel_width(digit);
-  const int per = nb / kThreads;  // 8 or 4 buckets per thread, in descending key order
+// Block-wide max of one int per thread (kT threads); lds: kT / kWave ints.
+template <int kT>
+__device__ inline int block_max_i32(int v, int* lds) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = max(v, __shfl_xor(v, o));
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = lds[0];
+#pragma unroll
+  for (int i = 1; i < kT / kWave; ++i) r = max(r, lds[i]);
+  __syncthreads();
+  return r;
+}
+
+// The boundary bucket of one histogram walked from the largest key down. Thread t holds
+// buckets nb - 1 - (t·kPB + i), i < kPB (kT·kPB = nb): counts c and weights w (counts
+// for top-k, masses for top-p). Returns the lowest non-empty bucket whose weight strictly
+// above it, plus carry, is below target (-1: none) with that sum in *above, and the sum of
+// all weights in *total. Every thread returns the same values. lds: kT / kWave doubles,
+// s_d: 2 doubles, s_i: kT / kWave ints.
+template <int kT, int kPB>
+__device__ int resolve_desc(const uint32_t (&c)[kPB], const double (&w)[kPB], double carry, double target,
+                            double* above, double* total, double* lds, double* s_d, int* s_i) {
   const int tid = threadIdx.x;
-  uint32_t c[8];
-  double w[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = nb - 1 - (tid * per + i);
-    c[i] = i < per ? __hip_atomic_load(&cnt[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-    const double m = (i < per && mode == 1)
-                         ? __hip_atomic_load(&mass[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : 0.0;
-    w[i] = i < per ? (mode == 0 ? (double)c[i] : m) : 0.0;
-  }
-  if (mode == 1 && digit == 0) {
-    // S: the mass of every token top-k kept (all buckets of the first top-p digit)
-    double t = 0.0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t += w[i];
-    st.s1 = block_sum_f64<kThreads>(t, lds_scan);
-  }
-  const double target = mode == 0 ? (double)sa.top_k : sa.top_p * st.s1;
   double local = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) local += w[i];
-  const double incl = block_inclusive_scan_f64<kThreads>(local, lds_scan);
-  s_excl[tid] = incl;
-  __syncthreads();
-  double run = st.carry + (tid > 0 ? s_excl[tid - 1] : 0.0);
+  for (int i = 0; i < kPB; ++i) local += w[i];
+  const double incl = block_inclusive_scan_f64<kT>(local, lds);
+  if (tid == kT - 1) s_d[1] = incl;
+  double run = carry + (incl - local);
   int best = -1;
   double best_above = 0.0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i < per && run < target && c[i] > 0u) {
-      best = tid * per + i;
+  for (int i = 0; i < kPB; ++i) {
+    if (run < target && c[i] > 0u) {
+      best = tid * kPB + i;
       best_above = run;
     }
     run += w[i];
   }
-  // descending indices grow with the thread index: the last thread with a candidate
-  // holds the lowest qualifying bucket
-  const int2 fl = block_first_last(false, best >= 0, 0, s_fl);
-  if (tid == fl.y) {
-    *s_best = best;
-    *s_above = best_above;
-  }
+  // descending positions grow with the thread index: the largest qualifying position is the
+  // lowest qualifying bucket
+  const int b = block_max_i32<kT>(best, s_i);  // its barrier orders s_d[1] too
+  if (b >= 0 && best == b) s_d[0] = best_above;
   __syncthreads();
-  if (fl.y < 0) {
-    st.empty = 1;
-  } else {
-    st.prefix = (st.prefix << sel_width(digit)) | (uint32_t)(nb - 1 - *s_best);
-    st.carry = *s_above;
-  }
+  *above = b >= 0 ? s_d[0] : 0.0;
+  *total = s_d[1];
   __syncthreads();
+  return b >= 0 ? kT * kPB - 1 - b : -1;
 }
 
-// Chunk maxima of the allowed finite logits; clears the row's histogram and counter.
-template <bool kVec4>
-__global__ __launch_bounds__(kThreads) void sel_prep_kernel(const float* __restrict__ target,
-                                                            const float* __restrict__ draft, int kd,
-                                                            int v, int chunks, Transform tr,
-                                                            SelBufs sb) {
+// Zeroes the row's digit-0 histogram (counts, or with `mass` the masses), arrival count,
+// candidate count and maximum.
+__global__ __launch_bounds__(kThreads) void sel_clear_kernel(SelBufs sb, int mass) {
+  const int64_t row = blockIdx.x;
+  if (!mass) {
+    u32x4* c = reinterpret_cast<u32x4*>(sb.cnt + row * kSelB0);
+    for (int i = threadIdx.x; i < kSelB0 / 4; i += kThreads) c[i] = u32x4{0u, 0u, 0u, 0u};
+  } else {
+    u32x4* m = reinterpret_cast<u32x4*>(sb.mass + row * kSelB0);
+    for (int i = threadIdx.x; i < kSelB0 / 2; i += kThreads) m[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (threadIdx.x == 0) {
+    sb.arrive[row] = 0u;
+    sb.candn[row] = 0u;
+    sb.rkey[row] = 0u;
+  }
+}
+
+// This workgroup's histogram (in LDS: counts, or with kMass masses) added into the row's;
+// then its arrival. Returns true in the row's last workgroup to arrive.
+template <bool kMass>
+__device__ bool flush_and_arrive(const uint32_t* hc, const double* hm, uint32_t* gc, double* gm,
+                                 uint32_t* arrive, int wgs, int* s_last) {
+  __syncthreads();
+  for (int b = threadIdx.x; b < kSelB0; b += kThreads) {
+    if constexpr (kMass) {
+      if (hm[b] != 0.0) atomicAdd(&gm[b], hm[b]);
+    } else {
+      if (hc[b] != 0u) atomicAdd(&gc[b], hc[b]);
+    }
+  }
+  // the additions (and the maximum) are device-scope atomics performed in L2; each wave
+  // waits until its own have completed, so the count cannot run ahead of them
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = before == (uint32_t)(wgs - 1);
+  }
+  __syncthreads();
+  return *s_last != 0;
+}
+
+// Thread t's 16 digit-0 buckets of the row histogram, largest keys first (device-scope loads:
+// other workgroups of this launch added them): counts, or with kMass masses (a bucket is
+// non-empty when its mass is positive).
+template <bool kMass>
+__device__ inline void load_desc16(const uint32_t* gc, const double* gm, uint32_t (&c)[16], double (&w)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int b = kSelB0 - 1 - ((int)threadIdx.x * 16 + i);
+    if constexpr (kMass) {
+      w[i] = __hip_atomic_load(&gm[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      c[i] = w[i] > 0.0 ? 1u : 0u;
+    } else {
+      c[i] = __hip_atomic_load(&gc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w[i] = (double)c[i];
+    }
+  }
+}
+
+// kMass: top-p alone, the digit-0 masses exp(z / tau) against the reference 0 (a token whose
+// mass underflows there is below e^-45 of the maximum's and is never kept). Else top-k, the
+// digit-0 counts. A workgroup takes chunks [blockIdx.y · cpw, + cpw) of its row (several chunks
+// per workgroup at large batches: fewer histograms to add into the row's).
+template <bool kVec4, bool kMass>
+__global__ __launch_bounds__(kThreads) void sel_count_kernel(const float* __restrict__ target,
+                                                             const float* __restrict__ draft, int kd,
+                                                             int v, int chunks, int cpw, Transform tr,
+                                                             SelBufs sb, SelArgs sa) {
+  __shared__ uint32_t hc[kMass ? 1 : kSelB0];
+  __shared__ double hm[kMass ? kSelB0 : 1];
+  __shared__ double tab[32];
   __shared__ float lds_f[kThreads / kWave];
+  __shared__ double lds_scan[kThreads / kWave];
+  __shared__ double s_d[2];
+  __shared__ int s_i[kThreads / kWave];
+  __shared__ int s_last;
   const int64_t rowg = blockIdx.x;
   const int per_seq = 2 * kd + 1;
   const int64_t s = rowg / per_seq;
   const int j = (int)(rowg % per_seq);
-  const int c = blockIdx.y;
-  float vals[kPer];
-  chunk_logits<kVec4>(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)),
-                      c * kChunk, v, vals);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) mx = fmaxf(mx, vals[q]);  // NaN (removed) is ignored
-  mx = block_max<kThreads>(mx, lds_f);
-  if (threadIdx.x == 0) sb.cmax[rowg * chunks + c] = mx;
-  for (int b = c * kThreads + (int)threadIdx.x; b < kSelBuckets; b += chunks * kThreads) {
-    sb.cnt[rowg * kSelBuckets + b] = 0u;
-    sb.mass[rowg * kSelBuckets + b] = 0.0;
+  const int tid = threadIdx.x;
+  if (kMass && tid < 32) tab[tid] = kExp2Table32[tid];
+  for (int b = tid; b < kSelB0; b += kThreads) {
+    if constexpr (kMass) hm[b] = 0.0;
+    else hc[b] = 0u;
   }
-  if (c == 0 && threadIdx.x == 0) sb.arrive[rowg] = 0u;
+  __syncthreads();
+  const float* zrow = row_ptr(target, draft, s, kd, j, v);
+  const uint32_t* mw = mask_words(tr, s, kd, mask_row(j, kd));
+  float mx = -INFINITY;
+  const int c0 = (int)blockIdx.y * cpw, c1 = min(chunks, c0 + cpw);
+  for (int c = c0; c < c1; ++c) {
+    float vals[kPer];
+    chunk_logits<kVec4>(zrow, mw, c * kChunk, v, vals);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const float zq = vals[q];
+      if (zq != zq) continue;  // removed, non-finite or past the row
+      mx = fmaxf(mx, zq);
+      const int b = (int)(order_key(zq) >> kSelShift0);
+      // exp(z / tau) against 0 (the range check below discards rows where this overflows)
+      if constexpr (kMass) atomicAdd(&hm[b], exp_neg_f64_tab((double)zq * tr.inv_tau, tab));
+      else atomicAdd(&hc[b], 1u);
+    }
+  }
+  mx = block_max<kThreads>(mx, lds_f);
+  if (tid == 0 && mx > -INFINITY) atomicMax(&sb.rkey[rowg], order_key(mx));
+  uint32_t* gc = sb.cnt + rowg * kSelB0;
+  double* gm = sb.mass + rowg * kSelB0;
+  if (!flush_and_arrive<kMass>(hc, hm, gc, gm, &sb.arrive[rowg], (int)gridDim.y, &s_last)) return;
+
+  // the row's last workgroup: the boundary's digit-0 bucket and the row's course
+  const uint32_t rk = __hip_atomic_load(&sb.rkey[rowg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  SelState st{};
+  st.rmax = rk ? key_logit(rk) : -INFINITY;
+  st.mode = kSelDone;
+  st.thr = 0u;
+  if (rk != 0u) {
+    uint32_t cc[16];
+    double w[16];
+    double above, total;
+    if constexpr (!kMass) {
+      load_desc16<false>(gc, gm, cc, w);
+      const int b = resolve_desc<kThreads, 16>(cc, w, 0.0, (double)sa.top_k, &above, &total, lds_scan, s_d, s_i);
+      if (total <= (double)sa.top_k || b < 0) {
+        // top-k keeps every token: top-p (if on) runs over the full row
+        if (sa.top_p < 1.0) st.mode = kSelSlowPFull;
+      } else {
+        const uint32_t nb = __hip_atomic_load(&gc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st.mode = above + (double)nb <= (double)kCand ? kSelCompactK : kSelSlowK;
+        st.lo = st.mode == kSelCompactK ? (uint32_t)b << kSelShift0 : (uint32_t)b;
+        st.carry = above;
+      }
+    } else {
+      const double r = (double)st.rmax * tr.inv_tau;
+      st.mode = kSelSlowPFull;
+      if (r >= kRef0Lo && r <= kRef0Hi) {
+        load_desc16<true>(gc, gm, cc, w);
+        // the bucket masses summed in a fixed order give S (against 0) for the target P·S
+        double lsum = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lsum += w[i];
+        const double s0 = block_sum_f64<kThreads>(lsum, lds_scan);
+        const int b = resolve_desc<kThreads, 16>(cc, w, 0.0, sa.top_p * s0, &above, &total, lds_scan, s_d, s_i);
+        if (b >= 0) {
+          // to the row-maximum reference: multiply by exp(-m / tau) (within fp64's range here).
+          // The bucket's count is not kept: sel_finish reads it from the collected candidates.
+          const double f = exp_neg_f64(-r);
+          st.s1 = s0 * f;
+          st.carry = above * f;
+          st.lo = (uint32_t)b;
+          st.mode = kSelCompactP;
+        }
+      }
+    }
+  }
+  if (tid == 0) sb.state[rowg] = st;
 }
 
-// One pass of the walk: histogram (mode, digit) over this chunk into the row's
-// histogram; the row's last workgroup resolves the digit (and at the end of the walk
-// writes the threshold).
+// The candidate keys of kSelCompactK rows (every key from state.lo up) and kSelCompactP rows
+// (the keys of digit-0 bucket state.lo); other rows' workgroups return at once. One chunk per
+// workgroup and one slot reservation per workgroup (the reservations of a row serialize on its
+// counter; several chunks per workgroup or one reservation per wave measured slower).
 template <bool kVec4>
-__global__ __launch_bounds__(kThreads) void sel_pass_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft, int kd, int v, int chunks,
-    Transform tr, SelBufs sb, SelArgs sa, int first, int mode, int digit, int last) {
-  __shared__ uint32_t hc[kSelBuckets];
-  __shared__ double hm[kSelBuckets];
+__global__ __launch_bounds__(kThreads) void sel_collect_kernel(const float* __restrict__ target,
+                                                               const float* __restrict__ draft, int kd,
+                                                               int v, Transform tr, SelBufs sb) {
   __shared__ double lds_scan[kThreads / kWave];
-  __shared__ double s_excl[kThreads];
-  __shared__ float lds_f[kThreads / kWave];
-  __shared__ int s_fl[2 * (kThreads / kWave)];
-  __shared__ int s_best, s_last_wg;
-  __shared__ double s_above;
+  __shared__ uint32_t s_base;
   const int64_t rowg = blockIdx.x;
   const int per_seq = 2 * kd + 1;
   const int64_t s = rowg / per_seq;
   const int j = (int)(rowg % per_seq);
   const int c = blockIdx.y;
   const int tid = threadIdx.x;
+  const SelState st = sb.state[rowg];
+  if (st.mode != kSelCompactK && st.mode != kSelCompactP) return;
 
   float vals[kPer];
   chunk_logits<kVec4>(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)),
                       c * kChunk, v, vals);
-
-  SelState st;
-  if (first) {
-    float m = -INFINITY;
-    for (int cc = tid; cc < chunks; cc += kThreads) m = fmaxf(m, sb.cmax[rowg * chunks + cc]);
-    m = block_max<kThreads>(m, lds_f);
-    st.prefix = 0u;
-    st.thr_k = 0u;
-    st.carry = 0.0;
-    st.s1 = 0.0;
-    st.rmax = m;
-    st.empty = m == -INFINITY;
-  } else {
-    st = sb.state[rowg];
-  }
-
-  const int nb = 1 << sel_width(digit);
-  for (int b = tid; b < nb; b += kThreads) {
-    hc[b] = 0u;
-    hm[b] = 0.0;
-  }
-  __syncthreads();
-  if (!st.empty) {
+  const bool from = st.mode == kSelCompactK;
+  bool take[kPer];
+  int mine = 0;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const float zq = vals[q];
-      if (zq != zq) continue;  // removed, non-finite or past the row
-      const uint32_t key = order_key(zq);
-      if (mode == 1 && key < st.thr_k) continue;
-      if (digit > 0 && (key >> sel_shift(digit - 1)) != st.prefix) continue;
-      const int b = (int)((key >> sel_shift(digit)) & (uint32_t)(nb - 1));
-      atomicAdd(&hc[b], 1u);
-      if (mode == 1) atomicAdd(&hm[b], exp_neg_f64(((double)zq - (double)st.rmax) * tr.inv_tau));
+  for (int q = 0; q < kPer; ++q) {
+    const uint32_t key = order_key(vals[q]);
+    take[q] = vals[q] == vals[q] && (from ? key >= st.lo : (key >> kSelShift0) == st.lo);
+    mine += take[q] ? 1 : 0;
+  }
+  const double incl = block_inclusive_scan_f64<kThreads>((double)mine, lds_scan);
+  if (tid == kThreads - 1) {
+    const uint32_t tot = (uint32_t)incl;
+    s_base = tot ? atomicAdd(&sb.candn[rowg], tot) : 0u;
+  }
+  __syncthreads();
+  uint32_t slot = s_base + (uint32_t)incl - (uint32_t)mine;
+  uint32_t* out = sb.cand + rowg * kCand;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (take[q]) {
+      if (slot < (uint32_t)kCand) out[slot] = order_key(vals[q]);
+      ++slot;
     }
   }
-  __syncthreads();
-  uint32_t* gc = sb.cnt + rowg * kSelBuckets;
-  double* gm = sb.mass + rowg * kSelBuckets;
-  for (int b = tid; b < nb; b += kThreads) {
-    if (hc[b] != 0u) {
-      atomicAdd(&gc[b], hc[b]);
-      if (mode == 1) atomicAdd(&gm[b], hm[b]);
-    }
-  }
-  // arrival. The additions are device-scope atomics, performed where every CU reads them
-  // with device-scope loads; each wave waits until its own have completed, so the count
-  // cannot run ahead of them. No plain store is shared, so no L2 write-back is needed: a
-  // release / acquire fence pair here (an L2 write-back and invalidation in every
-  // workgroup) measured 0.7 -> 10.7 ms for top-k + top-p at B = 64.
-  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t before = __hip_atomic_fetch_add(&sb.arrive[rowg], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-    s_last_wg = before == (uint32_t)(chunks - 1);
-  }
-  __syncthreads();
-  if (!s_last_wg) return;
+}
 
-  // the row's last workgroup: resolve this digit from the complete histogram
-  if (!st.empty) sel_resolve(mode, digit, gc, gm, sa, st, lds_scan, s_excl, s_fl, &s_best, &s_above);
-  const bool k_done = mode == 0 && digit == kSelDigits - 1;
-  if (k_done) {
-    st.thr_k = st.empty ? 0u : st.prefix;  // top-k resolved; a top-p walk starts afresh
-    st.prefix = 0u;
-    st.carry = 0.0;
+// ---- sel_finish
+
+// Sorts keys[0, n) in LDS into descending order (bitonic network over the next power of two,
+// padded with key 0, which is below every finite logit's key).
+__device__ void sort_desc(uint32_t* keys, int n) {
+  int np = 1;
+  while (np < n) np <<= 1;
+  for (int i = n + (int)threadIdx.x; i < np; i += kFThreads) keys[i] = 0u;
+  __syncthreads();
+  for (int k = 2; k <= np; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < np; i += kFThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t a = keys[i], b = keys[l];
+          const bool desc = (i & k) == 0;  // this half of the merge ends descending
+          if (desc ? a < b : a > b) {
+            keys[i] = b;
+            keys[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
-  for (int b = tid; b < nb; b += kThreads) {
-    gc[b] = 0u;
-    gm[b] = 0.0;
+}
+
+struct FinishLds {
+  double scan[kFWaves];
+  double incl[kFThreads];
+  double d[2];
+  int i[kFWaves];
+};
+
+// top-p over the sorted candidates keys[0, lim): carry is the mass strictly above them; S is
+// s_given, or (s_from_sum) the candidates' own total. Thread t takes the contiguous positions
+// [t·per, t·per + per), so every sum runs in the sorted order. Returns the lowest key whose
+// strictly-larger mass is below P·S.
+__device__ uint32_t topp_sorted(const uint32_t* keys, int lim, double carry, double s_given, bool s_from_sum,
+                                float rmax, double inv_tau, double p, FinishLds& L) {
+  constexpr int kMaxPer = kCand / kFThreads;
+  const int tid = threadIdx.x;
+  const int per = (lim + kFThreads - 1) / kFThreads;
+  const int i0 = tid * per;
+  double e[kMaxPer];
+  double local = 0.0;
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) {
+    const int i = i0 + q;
+    e[q] = (q < per && i < lim) ? exp_neg_f64(((double)key_logit(keys[i]) - (double)rmax) * inv_tau) : 0.0;
+    local += e[q];
   }
-  if (tid == 0) {
-    sb.arrive[rowg] = 0u;
-    sb.state[rowg] = st;
-    if (last) sb.thr[rowg] = st.empty ? 0u : (k_done ? st.thr_k : st.prefix);
+  const double incl = block_inclusive_scan_f64<kFThreads>(local, L.scan);
+  L.incl[tid] = incl;
+  __syncthreads();
+  const double s = s_from_sum ? L.incl[kFThreads - 1] : s_given;
+  const double tgt = p * s;
+  double run = carry + (tid > 0 ? L.incl[tid - 1] : 0.0);
+  int best = -1;
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) {
+    const int i = i0 + q;
+    if (q < per && i < lim) {
+      const bool start = i == 0 || keys[i - 1] != keys[i];
+      if (start && run < tgt) best = i;
+      run += e[q];
+    }
   }
+  best = block_max_i32<kFThreads>(best, L.i);
+  return keys[best >= 0 ? best : 0];
+}
+
+// The tokens a finishing pass walks: the row itself (global memory, with its mask) or the
+// collected candidate keys in LDS. each(f) calls f(z, key) for every allowed finite token.
+template <bool kVec4>
+struct RowSrc {
+  const float* z;
+  const uint32_t* mw;
+  int v;
+  template <class F>
+  __device__ void each(F&& f) const {
+    auto one = [&](float zz, bool allowed) {
+      if (allowed && zz > -INFINITY && zz < INFINITY) f(zz, order_key(zz));
+    };
+    if constexpr (kVec4) {
+      for (int e4 = 4 * (int)threadIdx.x; e4 < v; e4 += 4 * kFThreads) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(z + e4);
+        const uint32_t w = mw ? mw[e4 >> 5] : 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) one(t[i], ((w >> ((e4 + i) & 31)) & 1u) != 0u);
+      }
+    } else {
+      for (int t = threadIdx.x; t < v; t += kFThreads)
+        one(z[t], mw ? ((mw[t >> 5] >> (t & 31)) & 1u) != 0u : true);
+    }
+  }
+};
+
+struct KeySrc {
+  const uint32_t* keys;
+  int n;
+  template <class F>
+  __device__ void each(F&& f) const {
+    for (int i = threadIdx.x; i < n; i += kFThreads) {
+      const uint32_t key = keys[i];
+      f(key_logit(key), key);
+    }
+  }
+};
+
+// One radix pass of the finishing workgroup: histogram of the digit (key >> shift) & (nb - 1)
+// of the source's tokens whose key is at least keep_lo and, when mshift < 32, whose
+// key >> mshift equals mval; counts, and with kMass masses exp((z - rmax) / tau) (their total
+// over the selected tokens in *s_out).
+template <bool kMass, class Src>
+__device__ void fin_hist(const Src& src, uint32_t keep_lo, int mshift, uint32_t mval, int shift, int nb,
+                         float rmax, double inv_tau, uint32_t* hc, double* hm, double* s_out, FinishLds& L) {
+  for (int b = threadIdx.x; b < nb; b += kFThreads) {
+    hc[b] = 0u;
+    if constexpr (kMass) hm[b] = 0.0;
+  }
+  __syncthreads();
+  double acc = 0.0;
+  src.each([&](float zz, uint32_t key) {
+    if (key < keep_lo || (mshift < 32 && (key >> mshift) != mval)) return;
+    const int b = (int)((key >> shift) & (uint32_t)(nb - 1));
+    atomicAdd(&hc[b], 1u);
+    if constexpr (kMass) {
+      const double e = exp_neg_f64(((double)zz - (double)rmax) * inv_tau);
+      atomicAdd(&hm[b], e);
+      acc += e;
+    }
+  });
+  if constexpr (kMass) {
+    const double tot = block_sum_f64<kFThreads>(acc, L.scan);
+    if (s_out) *s_out = tot;
+  }
+  __syncthreads();
+}
+
+// The boundary bucket of an LDS histogram of nb buckets (1024 or 4096) walked downwards.
+template <bool kMass>
+__device__ int fin_resolve(const uint32_t* hc, const double* hm, int nb, double carry, double target,
+                           double* above, FinishLds& L) {
+  double total;
+  if (nb == kSelB0) {
+    constexpr int kP = kSelB0 / kFThreads;
+    uint32_t c[kP];
+    double w[kP];
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int b = nb - 1 - ((int)threadIdx.x * kP + i);
+      c[i] = hc[b];
+      w[i] = kMass ? hm[b] : (double)c[i];
+    }
+    return resolve_desc<kFThreads, kP>(c, w, carry, target, above, &total, L.scan, L.d, L.i);
+  }
+  constexpr int kP = (1 << kSelBits1) / kFThreads;
+  uint32_t c[kP];
+  double w[kP];
+#pragma unroll
+  for (int i = 0; i < kP; ++i) {
+    const int b = nb - 1 - ((int)threadIdx.x * kP + i);
+    c[i] = hc[b];
+    w[i] = kMass ? hm[b] : (double)c[i];
+  }
+  return resolve_desc<kFThreads, kP>(c, w, carry, target, above, &total, L.scan, L.d, L.i);
+}
+
+// Digits 1 and 2 of a walk whose digit-0 bucket (prefix) and carry are known; returns the
+// threshold key. A bucket that does not resolve (only if the row changed during the call)
+// keeps every token of the prefix.
+template <bool kMass, class Src>
+__device__ uint32_t fin_digits12(const Src& src, uint32_t keep_lo, uint32_t prefix, double carry, double target,
+                                 float rmax, double inv_tau, uint32_t* hc, double* hm, FinishLds& L) {
+  for (int d = 1; d <= 2; ++d) {
+    const int mshift = d == 1 ? kSelShift0 : kSelBits1;
+    const int shift = d == 1 ? kSelBits1 : 0;
+    fin_hist<kMass>(src, keep_lo, mshift, prefix, shift, 1 << kSelBits1, rmax, inv_tau, hc, hm, nullptr, L);
+    double above = carry;
+    const int b = fin_resolve<kMass>(hc, hm, 1 << kSelBits1, carry, target, &above, L);
+    prefix = (prefix << kSelBits1) | (uint32_t)(b >= 0 ? b : 0);
+    carry = above;
+  }
+  return prefix;
+}
+
+// top-p over the source's tokens with key >= keep_lo (the tokens top-k kept), all three digits.
+template <class Src>
+__device__ uint32_t fin_topp(const Src& src, uint32_t keep_lo, double p, float rmax, double inv_tau, uint32_t* hc,
+                             double* hm, FinishLds& L) {
+  double s1 = 0.0;
+  fin_hist<true>(src, keep_lo, 32, 0u, kSelShift0, kSelB0, rmax, inv_tau, hc, hm, &s1, L);
+  double above = 0.0;
+  const int b = fin_resolve<true>(hc, hm, kSelB0, 0.0, p * s1, &above, L);
+  if (b < 0) return keep_lo;
+  return fin_digits12<true>(src, keep_lo, (uint32_t)b, above, p * s1, rmax, inv_tau, hc, hm, L);
+}
+
+constexpr int kSortMax = 512;  // candidate lists up to this size are sorted (fixed-order sums)
+
+template <bool kVec4>
+__global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __restrict__ target,
+                                                               const float* __restrict__ draft, int kd,
+                                                               int v, Transform tr, SelBufs sb,
+                                                               SelArgs sa) {
+  __shared__ uint32_t keys[kCand];  // the candidates
+  __shared__ uint32_t hc[kSelB0];   // radix passes: counts
+  __shared__ double hm[kSelB0];     // radix passes: masses
+  __shared__ FinishLds L;
+  const int64_t rowg = blockIdx.x;
+  const int tid = threadIdx.x;
+  SelState st = sb.state[rowg];
+  const bool use_p = sa.top_p < 1.0;
+  const double kf = (double)sa.top_k;
+  uint32_t thr = 0u;
+  if (st.mode == kSelCompactK || st.mode == kSelCompactP) {
+    const uint32_t cn = sb.candn[rowg];
+    if (cn > (uint32_t)kCand) {
+      // more candidates than the list holds (top-p buckets are not counted ahead): radix passes
+      // over the row
+      if (st.mode == kSelCompactK) {
+        st.mode = kSelSlowK;
+        st.lo >>= kSelShift0;
+      } else {
+        st.mode = kSelSlowP;
+      }
+    }
+  }
+  if (st.mode == kSelCompactK || st.mode == kSelCompactP) {
+    const int n = (int)sb.candn[rowg];
+    const uint32_t* src = sb.cand + rowg * kCand;
+    for (int i = tid; i < n; i += kFThreads) keys[i] = src[i];
+    __syncthreads();
+    if (n <= kSortMax) {
+      sort_desc(keys, n);
+      if (st.mode == kSelCompactK) {
+        // the candidates are the row's n largest keys: top-k's threshold is the k-th
+        const int kk = min(sa.top_k, n);
+        const uint32_t thr_k = n > 0 ? keys[kk - 1] : 0u;
+        thr = thr_k;
+        if (use_p && n > 0) {
+          // top-p on the tokens top-k kept: the first m sorted keys
+          int last = -1;
+          for (int i = tid; i < n; i += kFThreads)
+            if (keys[i] >= thr_k && (i + 1 == n || keys[i + 1] < thr_k)) last = i;
+          const int m = block_max_i32<kFThreads>(last, L.i) + 1;
+          thr = topp_sorted(keys, m, 0.0, 0.0, true, st.rmax, tr.inv_tau, sa.top_p, L);
+        }
+      } else if (n > 0) {
+        thr = topp_sorted(keys, n, st.carry, st.s1, false, st.rmax, tr.inv_tau, sa.top_p, L);
+      }
+    } else {
+      const KeySrc ks{keys, n};
+      if (st.mode == kSelCompactK) {
+        thr = fin_digits12<false>(ks, 0u, st.lo >> kSelShift0, st.carry, kf, st.rmax, tr.inv_tau, hc, hm, L);
+        if (use_p) thr = fin_topp(ks, thr, sa.top_p, st.rmax, tr.inv_tau, hc, hm, L);
+      } else {
+        thr = fin_digits12<true>(ks, 0u, st.lo, st.carry, sa.top_p * st.s1, st.rmax, tr.inv_tau, hc, hm, L);
+      }
+    }
+  } else if (st.mode == kSelSlowK || st.mode == kSelSlowP || st.mode == kSelSlowPFull) {
+    const int per_seq = 2 * kd + 1;
+    const int64_t s = rowg / per_seq;
+    const int j = (int)(rowg % per_seq);
+    const RowSrc<kVec4> rs{row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), v};
+    if (st.mode == kSelSlowP) {
+      thr = fin_digits12<true>(rs, 0u, st.lo, st.carry, sa.top_p * st.s1, st.rmax, tr.inv_tau, hc, hm, L);
+    } else {
+      if (st.mode == kSelSlowK)
+        thr = fin_digits12<false>(rs, 0u, st.lo, st.carry, kf, st.rmax, tr.inv_tau, hc, hm, L);
+      if (use_p) thr = fin_topp(rs, thr, sa.top_p, st.rmax, tr.inv_tau, hc, hm, L);
+    }
+  } else {
+    thr = st.thr;  // kSelDone
+  }
+  if (tid == 0) sb.thr[rowg] = thr;
 }
 
 // ---------------------------------------------------------------- decide + piece totals
@@ -1127,6 +1516,101 @@ hipError_t noalloc_scratch(void** ptr) {
   return hipSuccess;
 }
 
+namespace {
+
+// The top-k / top-p thresholds of every row into sb.thr, rows = b·(2kd + 1) numbered as
+// the stats kernel numbers them; at least one of top-k (sa.top_k > 0) and top-p
+// (sa.top_p < 1) is on.
+hipError_t launch_selection(const float* target, const float* draft, int32_t b, int32_t kd, int32_t v,
+                            const Transform& tr, const SelBufs& sb, const SelArgs& sa, bool vec4,
+                            hipStream_t stream) {
+  const int chunks = (v + kChunk - 1) / kChunk;
+  const int64_t rows = (int64_t)b * (2 * kd + 1);
+  const bool mass = sa.top_k == 0;  // top-p alone: digit-0 masses in sel_count
+  // chunks per counting workgroup: about eight resident workgroups per CU's worth of grid
+  const int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, rows * chunks / 2048));
+  const dim3 gc((unsigned)rows, (unsigned)((chunks + cpw - 1) / cpw));
+  sel_clear_kernel<<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(sb, mass ? 1 : 0);
+  if (vec4 && mass)
+    sel_count_kernel<true, true><<<gc, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, cpw, tr, sb, sa);
+  else if (vec4)
+    sel_count_kernel<true, false><<<gc, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, cpw, tr, sb, sa);
+  else if (mass)
+    sel_count_kernel<false, true><<<gc, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, cpw, tr, sb, sa);
+  else
+    sel_count_kernel<false, false><<<gc, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, cpw, tr, sb, sa);
+  const dim3 g1((unsigned)rows, (unsigned)chunks);
+  if (vec4) sel_collect_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb);
+  else sel_collect_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb);
+  if (vec4)
+    sel_finish_kernel<true><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa);
+  else
+    sel_finish_kernel<false><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa);
+  return hipGetLastError();
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t value) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+// Selection buffers of `rows` rows carved from a workspace (thresholds elsewhere).
+struct SelLayout {
+  size_t cnt, mass, state, arrive, rkey, candn, cand, total;
+};
+inline SelLayout sel_layout(int64_t rows) {
+  SelLayout L;
+  size_t off = 0;
+  L.cnt = off;
+  off = align256(off + sizeof(uint32_t) * rows * kSelB0);
+  L.mass = off;
+  off = align256(off + sizeof(double) * rows * kSelB0);
+  L.state = off;
+  off = align256(off + sizeof(SelState) * rows);
+  L.arrive = off;
+  off = align256(off + sizeof(uint32_t) * rows);
+  L.rkey = off;
+  off = align256(off + sizeof(uint32_t) * rows);
+  L.candn = off;
+  off = align256(off + sizeof(uint32_t) * rows);
+  L.cand = off;
+  off = align256(off + sizeof(uint32_t) * rows * kCand);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t sampling_thresholds_workspace_bytes(int64_t rows) { return sel_layout(rows).total; }
+
+hipError_t launch_sampling_thresholds(const float* logits, int32_t rows, int32_t v, const SamplingParams& sp,
+                                      uint32_t* out_thr, void* workspace, bool vec4, hipStream_t stream) {
+  const bool use_k = sp.top_k > 0 && sp.top_k < v;
+  const bool use_p = sp.top_p < 1.0f;
+  if (!use_k && !use_p) {
+    fill_u32_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream>>>(out_thr, rows, 0u);
+    return hipGetLastError();
+  }
+  Transform tr{};
+  tr.mask = sp.mask;
+  tr.inv_tau = 1.0 / (double)sp.temperature;
+  tr.words = (v + 31) / 32;
+  const SelLayout L = sel_layout(rows);
+  char* base = static_cast<char*>(workspace);
+  SelBufs sb;
+  sb.cnt = reinterpret_cast<uint32_t*>(base + L.cnt);
+  sb.mass = reinterpret_cast<double*>(base + L.mass);
+  sb.state = reinterpret_cast<SelState*>(base + L.state);
+  sb.arrive = reinterpret_cast<uint32_t*>(base + L.arrive);
+  sb.rkey = reinterpret_cast<uint32_t*>(base + L.rkey);
+  sb.candn = reinterpret_cast<uint32_t*>(base + L.candn);
+  sb.cand = reinterpret_cast<uint32_t*>(base + L.cand);
+  sb.thr = out_thr;
+  const SelArgs sa{use_k ? sp.top_k : 0, use_p ? (double)sp.top_p : 1.0};
+  // one "sequence" per row with no draft rows: row s is logits + s·v, mask row s
+  return launch_selection(logits, nullptr, rows, 0, v, tr, sb, sa, vec4, stream);
+}
+
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled) {
   return layout(b, kd, v, sampled).total;
 }
@@ -1166,28 +1650,12 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
       sb.mass = reinterpret_cast<double*>(base + L.selmass);
       sb.state = reinterpret_cast<SelState*>(base + L.selstate);
       sb.arrive = reinterpret_cast<uint32_t*>(base + L.selarrive);
-      sb.cmax = reinterpret_cast<float*>(base + L.selmax);
+      sb.rkey = reinterpret_cast<uint32_t*>(base + L.selrkey);
+      sb.candn = reinterpret_cast<uint32_t*>(base + L.selcandn);
+      sb.cand = reinterpret_cast<uint32_t*>(base + L.selcand);
       sb.thr = reinterpret_cast<uint32_t*>(base + L.thr);
       const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0};
-      if (vec4) sel_prep_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb);
-      else sel_prep_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      // passes: the top-k digits, then the top-p digits
-      const int npass = kSelDigits * ((use_k ? 1 : 0) + (use_p ? 1 : 0));
-      int h = 0;
-      for (int mode = 0; mode < 2; ++mode) {
-        if ((mode == 0 && !use_k) || (mode == 1 && !use_p)) continue;
-        for (int d = 0; d < kSelDigits; ++d, ++h) {
-          const int first = h == 0, last = h == npass - 1;
-          if (vec4)
-            sel_pass_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb,
-                                                                     sa, first, mode, d, last);
-          else
-            sel_pass_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, tr, sb,
-                                                                      sa, first, mode, d, last);
-          if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
-      }
+      if ((e = launch_selection(target, draft, b, kd, v, tr, sb, sa, vec4, stream)) != hipSuccess) return e;
       uint32_t* thr = sb.thr;
       tr.thr = thr;
     }

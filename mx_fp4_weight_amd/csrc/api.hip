@@ -513,4 +513,28 @@ mxs_status spec_accept_sampled(const float* target_logits, const float* draft_lo
                                           vec4, &sp, static_cast<hipStream_t>(stream)));
 }
 
+size_t spec_sampling_thresholds_workspace_bytes(int32_t rows, int32_t v) {
+  if (rows < 1 || rows > (1 << 22) || v < 2 || v > (1 << 26)) return 0;
+  return mxs::sampling_thresholds_workspace_bytes(rows);
+}
+
+mxs_status spec_sampling_thresholds(const float* logits, int32_t rows, int32_t v, float temperature,
+                                    int32_t top_k, float top_p, const uint32_t* mask, uint32_t* out_thresholds,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !out_thresholds || !workspace) return MXS_ERR_NULL;
+  if (rows < 1 || rows > (1 << 22) || v < 2 || v > (1 << 26)) return MXS_ERR_SHAPE;
+  if (!(temperature > 0.0f) || !(temperature < INFINITY) || top_k < 0 || !(top_p > 0.0f) ||
+      !(top_p <= 1.0f))
+    return MXS_ERR_VALUE;
+  if (!aligned(logits, 4) || !aligned(out_thresholds, 4) || !aligned(workspace, 16) || !aligned(mask, 4))
+    return MXS_ERR_ALIGN;
+  if (workspace_bytes < mxs::sampling_thresholds_workspace_bytes(rows)) return MXS_ERR_WORKSPACE;
+  const mxs_status d = check_device();
+  if (d != MXS_OK) return d;
+  const bool vec4 = (v % 4 == 0) && aligned(logits, 16);
+  const mxs::SamplingParams sp{temperature, top_k, top_p, mask};
+  return launched(mxs::launch_sampling_thresholds(logits, rows, v, sp, out_thresholds, workspace, vec4,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -51,7 +51,9 @@ __device__ inline void raise_flag(int32_t* flags, int32_t bit) {
 
 // exp(d) in fp64 for d <= 0 (d = -inf gives 0), relative error below 1e-14.
 // Cody–Waite reduction d = k ln2 + r with |r| <= ln2/2, then a degree-12
-// Taylor polynomial of e^r in Horner form and a scale by 2^k.
+// Taylor polynomial of e^r in Horner form and a scale by 2^k. The same steps
+// hold for positive d up to 709 (k <= 1023; the two-part ln 2 keeps k ln2
+// exact for |k| < 2^20), which the selection's masses against 0 use.
 __device__ inline double exp_neg_f64(double d) {
   if (!(d > -745.0)) return 0.0;  // also catches -inf; NaN never reaches here
   const double kLog2e = 1.4426950408889634;

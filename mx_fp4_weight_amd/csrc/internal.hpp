@@ -88,6 +88,12 @@ hipError_t launch_tile_scales(const uint8_t* scales, int64_t n, int64_t k, uint8
 
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled);
 
+// Top-k / top-p thresholds (order keys) of `rows` independent logit rows [rows, v] with masks
+// [rows, ceil(v/32)] (sp.mask, or null): the selection spec_accept_sampled runs.
+size_t sampling_thresholds_workspace_bytes(int64_t rows);
+hipError_t launch_sampling_thresholds(const float* logits, int32_t rows, int32_t v, const SamplingParams& sp,
+                                      uint32_t* out_thr, void* workspace, bool vec4, hipStream_t stream);
+
 // Verification attention over the MX-FP4 KV cache (d = 128; rows = t * hq / hkv <= 64).
 constexpr int kMaxAttnPositions = 64;
 size_t kv_attention_workspace_bytes(int64_t b, int t, int hq, int hkv, int64_t max_len);

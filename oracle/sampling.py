@@ -48,11 +48,22 @@ def transformed_law(z, temperature: float = 1.0, top_k: int = 0, top_p: float = 
     z = np.asarray(z, dtype=np.float32)
     if np.isnan(z).any() or np.isposinf(z).any():
         return None, np.inf
+    keep, e, margin = kept_set(z, temperature, top_k, top_p, allowed)
+    if not keep.any():
+        return None, np.inf
+    return e / e.sum(), margin
+
+
+def kept_set(z, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0, allowed=None):
+    """(keep, e, top_p_margin): the tokens the transforms keep (bool row), their weights
+    e_t = exp(y_t - max y) (0 elsewhere) and the top-p margin, for a row whose finite logits
+    are the candidates (non-finite logits are never kept)."""
+    z = np.asarray(z, dtype=np.float32)
     keep = np.isfinite(z)
     if allowed is not None:
         keep &= np.asarray(allowed, dtype=bool)
     if not keep.any():
-        return None, np.inf
+        return keep, np.zeros(z.shape, np.float64), np.inf
     zk = z.astype(np.float64)
 
     # top-k on the logits (dividing by tau > 0 keeps their order)
@@ -84,7 +95,7 @@ def transformed_law(z, temperature: float = 1.0, top_k: int = 0, top_p: float = 
         keep &= np.isin(zk, kept_vals)
         e = np.where(keep, e, 0.0)
 
-    return e / e.sum(), margin
+    return keep, e, margin
 
 
 def kept_set_brute(z, top_k: int = 0, top_p: float = 1.0, allowed=None, temperature: float = 1.0):

@@ -25,7 +25,7 @@ def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)
-    keep = [n for n in names if n.startswith(("mxs_", "mx_", "mxfp4_", "nvfp4_", "spec_accept"))]
+    keep = [n for n in names if n.startswith(("mxs_", "mx_", "mxfp4_", "nvfp4_", "spec_accept", "spec_sampling"))]
     return sorted(set(keep))
 
 
@@ -299,7 +299,8 @@ def test_sampled_host_errors():
     lib = mxs.get_lib()
     plain = lib.spec_accept_workspace_bytes(2, 4, 128256)
     sampled = lib.spec_accept_sampled_workspace_bytes(2, 4, 128256)
-    assert sampled >= plain + 2 * 9 * 2048 * 12   # a count + mass histogram per logit row
+    # per logit row: a 4096-bucket count + mass histogram and an 8192-key candidate list
+    assert sampled >= plain + 2 * 9 * (4096 * 12 + 8192 * 4)
     assert lib.spec_accept_sampled_workspace_bytes(0, 4, 1024) == 0
     for kw in [dict(t=0), dict(u=0), dict(ot=0), dict(on=0), dict(ws=0), dict(d=0), dict(tok=0)]:
         assert _as(**kw) == mxs.MXS_ERR_NULL
@@ -312,6 +313,35 @@ def test_sampled_host_errors():
     need = lib.spec_accept_sampled_workspace_bytes(1, 4, 1024)
     assert _as(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
     assert _as(wsb=need, tau=0.7, k=50, p=0.9, mask=0x8000) == mxs.MXS_ERR_DEVICE
+
+
+def _th(z=0x1000, rows=3, v=1024, tau=1.0, k=50, p=0.9, mask=None, out=0x2000, ws=0x3000, wsb=None):
+    lib = mxs.get_lib()
+    if wsb is None:
+        wsb = lib.spec_sampling_thresholds_workspace_bytes(max(rows, 1), max(v, 2))
+    f = lambda a: P(a) if a else None
+    return lib.spec_sampling_thresholds(f(z), rows, v, tau, k, p, f(mask), f(out), f(ws), wsb, None)
+
+
+def test_sampling_thresholds_host_errors():
+    lib = mxs.get_lib()
+    need = lib.spec_sampling_thresholds_workspace_bytes(3, 1024)
+    assert need >= 3 * (4096 * 12 + 8192 * 4)
+    assert lib.spec_sampling_thresholds_workspace_bytes(0, 1024) == 0
+    assert lib.spec_sampling_thresholds_workspace_bytes(3, 1) == 0
+    assert lib.spec_sampling_thresholds_workspace_bytes((1 << 22) + 1, 1024) == 0
+    for kw in [dict(z=0), dict(out=0), dict(ws=0)]:
+        assert _th(**kw) == mxs.MXS_ERR_NULL, kw
+    for kw in [dict(rows=0), dict(v=1), dict(v=(1 << 26) + 1)]:
+        assert _th(**kw) == mxs.MXS_ERR_SHAPE, kw
+    for kw in [dict(tau=0.0), dict(tau=float("inf")), dict(tau=float("nan")), dict(k=-1), dict(p=0.0),
+               dict(p=1.01), dict(p=float("nan"))]:
+        assert _th(**kw) == mxs.MXS_ERR_VALUE, kw
+    for kw in [dict(z=0x1002), dict(out=0x2001), dict(ws=0x3008), dict(mask=0x4002)]:
+        assert _th(**kw) == mxs.MXS_ERR_ALIGN, kw
+    assert _th(wsb=need - 1) == mxs.MXS_ERR_WORKSPACE
+    assert _th(wsb=need, mask=0x4000) == mxs.MXS_ERR_DEVICE
+    assert _th(k=0, p=1.0) == mxs.MXS_ERR_DEVICE   # both off: still a device call (zero fill)
 
 
 def _nq(w=0x1000, n=4, k=64, codes=0x2000, scales=0x3000, g=0x4000, flags=None):

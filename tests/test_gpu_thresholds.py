@@ -1,0 +1,151 @@
+"""spec_sampling_thresholds on the GPU vs the oracle's kept sets.
+
+A row's kept set on the device is {t : allowed, finite, key(z_t) >= threshold}; it must
+equal oracle.sampling.kept_set token for token, except on rows whose top-p boundary lies
+within 1e-9 of a tie (the oracle's margin), which are set aside. The inputs steer every
+route of the selection: candidates collected after the first digit (top-k, top-p, both),
+candidate lists too long for the workgroup (k = 9000; every logit in one bucket), top-k that
+keeps every token under top-p, logit ranges where exp(z / tau) against 0 would leave fp64's
+range, ties, vocabularies with ragged chunks or without vector loads, and rows with nothing
+allowed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_fp4_weight_amd as mxs
+import synth
+from oracle import sampling as osm
+from tests.gpu_util import dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def order_keys(z):
+    """uint32 keys with the logits' order (-0 as +0): bits | 2^31 for z >= 0, ~bits below."""
+    z = np.asarray(z, np.float32).copy()
+    z[z == 0] = 0.0
+    b = z.view(np.uint32)
+    return np.where(b & np.uint32(0x80000000), ~b, b | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def device_thresholds(z, tau, k, p, allowed):
+    m = None if allowed is None else dev(synth.pack_mask(allowed).view(np.int32))
+    out = mxs.spec_sampling_thresholds(dev(z), tau, k, p, m)
+    torch.cuda.synchronize()
+    return host(out).view(np.uint32)
+
+
+def compare(z, tau, k, p, allowed, label):
+    thr = device_thresholds(z, tau, k, p, allowed)
+    again = device_thresholds(z, tau, k, p, allowed)
+    assert np.array_equal(thr, again), (label, "thresholds differ between two calls")
+    keys = order_keys(z)
+    flagged = 0
+    for r in range(z.shape[0]):
+        al = None if allowed is None else allowed[r]
+        keep, _, margin = osm.kept_set(z[r], tau, k, p, al)
+        if margin < osm.TOP_P_MARGIN:
+            flagged += 1
+            continue
+        ok = np.isfinite(z[r]) & (np.ones(z.shape[1], bool) if al is None else al)
+        got = ok & (keys[r] >= thr[r])
+        if not np.array_equal(got, keep):
+            diff = np.nonzero(got != keep)[0]
+            raise AssertionError((label, r, int(thr[r]), int(got.sum()), int(keep.sum()), diff[:8].tolist()))
+    say(f"  {label}: {z.shape[0]} rows, {flagged} set aside")
+
+
+def normal_rows(seed, rows, v, sigma=3.0, mu=0.0):
+    return (mu + sigma * synth.rng(31, synth.ROLE_BASE, seed).standard_normal((rows, v))).astype(np.float32)
+
+
+SETTINGS_8B = [  # (temperature, top_k, top_p, mask keep fraction)
+    (0.8, 50, 0.9, 0.9),
+    (1.0, 0, 0.95, None),
+    (1.0, 50, 1.0, None),
+    (0.7, 0, 0.5, 0.7),
+    (1.0, 1, 1.0, None),
+    (0.05, 0, 0.9, None),     # sharp law: masses against 0 up to e^~300
+    (2.0, 300, 0.99, 0.9),
+    (1.0, 2000, 0.9, None),   # a few thousand candidates: radix passes over the list, both selections
+    (1.0, 8000, 1.0, None),   # ~8000 candidates: the list or the radix passes
+    (1.0, 9000, 1.0, None),   # more candidates than the list holds
+    (1.0, 9000, 0.8, None),
+]
+
+
+@pytest.mark.parametrize("tau,k,p,keep", SETTINGS_8B)
+def test_8b_vocab(tau, k, p, keep):
+    say(f"thresholds: V=128256 tau={tau} k={k} p={p} keep={keep}")
+    rows, v = 12, 128256
+    z = normal_rows(k + int(100 * tau), rows, v)
+    allowed = None if keep is None else synth.token_mask(31, k, rows, v, keep)
+    compare(z, tau, k, p, allowed, f"8b tau={tau} k={k} p={p}")
+
+
+@pytest.mark.parametrize("tau,k,p", [(1.0, 0, 0.9), (1.0, 50, 1.0), (1.0, 50, 0.5), (0.3, 0, 0.3)])
+def test_one_crowded_bucket(tau, k, p):
+    """Every logit in [1, 1.1): one first-digit bucket holds the whole row (radix passes)."""
+    say(f"thresholds: one bucket tau={tau} k={k} p={p}")
+    rows, v = 6, 128256
+    z = (1.0 + 0.1 * synth.rng(32, synth.ROLE_BASE, k).random((rows, v))).astype(np.float32)
+    compare(z, tau, k, p, None, f"bucket tau={tau} k={k} p={p}")
+
+
+def test_top_k_keeps_every_token_then_top_p():
+    say("thresholds: top-k above the allowed count, then top-p")
+    rows, v = 16, 1024
+    z = normal_rows(3, rows, v, sigma=2.0)
+    allowed = synth.token_mask(33, 0, rows, v, 0.3)
+    compare(z, 1.0, 500, 0.9, allowed, "k=500 of ~300 allowed, p=0.9")
+    compare(z, 1.0, 500, 1.0, allowed, "k=500 of ~300 allowed")
+
+
+@pytest.mark.parametrize("mu,tau", [(1000.0, 1.0), (-1000.0, 1.0), (0.0, 0.01)])
+def test_logit_ranges_outside_the_reference(mu, tau):
+    """max / tau above 690 or below -650: top-p masses against the row maximum only."""
+    say(f"thresholds: mu={mu} tau={tau}")
+    rows, v = 6, 20000
+    z = normal_rows(4, rows, v, sigma=1.0 if mu else 3.0, mu=mu)
+    compare(z, tau, 0, 0.9, None, f"mu={mu} tau={tau} p=0.9")
+    compare(z, tau, 40, 0.7, None, f"mu={mu} tau={tau} k=40 p=0.7")
+
+
+def test_ties():
+    say("thresholds: integer logits")
+    rows, v = 24, 4096
+    z = synth.rng(34, 3).integers(-3, 4, size=(rows, v)).astype(np.float32)
+    for tau, k, p in [(1.0, 10, 1.0), (1.0, 0, 0.7), (0.7, 30, 0.5), (1.0, 1, 1.0), (1.0, 4000, 0.99)]:
+        compare(z, tau, k, p, None, f"ties tau={tau} k={k} p={p}")
+
+
+@pytest.mark.parametrize("v", [2, 5, 4095, 4097, 12289])
+def test_vocab_edges(v):
+    say(f"thresholds: V={v}")
+    rows = 20
+    z = normal_rows(v, rows, v, sigma=2.0)
+    allowed = synth.token_mask(35, v, rows, v, 0.8)
+    compare(z, 0.9, 7, 0.85, allowed, f"v={v}")
+    compare(z, 1.1, 0, 0.6, None, f"v={v} top-p")
+
+
+def test_empty_and_nonfinite_rows():
+    """Rows with nothing allowed, only -inf, and NaN / +inf entries (never kept)."""
+    say("thresholds: empty and non-finite rows")
+    rows, v = 6, 4096
+    z = normal_rows(5, rows, v)
+    allowed = np.ones((rows, v), bool)
+    allowed[0] = False
+    z[1] = -np.inf
+    z[2, ::7] = np.nan
+    z[3, ::11] = np.inf
+    z[4, :4000] = -np.inf
+    for tau, k, p in [(1.0, 20, 0.9), (1.0, 0, 0.8), (1.0, 20, 1.0)]:
+        compare(z, tau, k, p, allowed, f"edge rows tau={tau} k={k} p={p}")
+
+
+def test_both_off_is_zero():
+    z = normal_rows(6, 4, 1000)
+    assert not device_thresholds(z, 1.0, 0, 1.0, None).any()
+    assert not device_thresholds(z, 1.0, 1000, 1.0, None).any()

@@ -47,11 +47,23 @@ def test_top_k_matches_enumeration_with_ties(seed):
         law, _ = osm.transformed_law(z, top_k=k, allowed=allowed)
         kept = sorted(np.nonzero(law > 0)[0].tolist())
         assert kept == osm.kept_set_brute(z, top_k=k, allowed=allowed), (seed, k)
+        assert np.nonzero(osm.kept_set(z, top_k=k, allowed=allowed)[0])[0].tolist() == kept
         # ties included: at least min(k, allowed) tokens, and every kept token beats every dropped one
         assert len(kept) >= min(k, int(allowed.sum()))
         dropped = [t for t in range(23) if allowed[t] and t not in kept]
         if dropped and kept:
             assert z[kept].min() > z[dropped].max()
+
+
+def test_kept_set_keeps_tokens_whose_weight_underflows():
+    """top-k keeps a token whose e_t underflows to 0 (logits 2000 apart): it is in the kept set
+    (so a sampler's support and a threshold include it) though the law gives it 0."""
+    z = np.array([0.0, -2000.0, -3000.0, 5.0], np.float32)
+    keep, e, _ = osm.kept_set(z, top_k=3)
+    assert np.nonzero(keep)[0].tolist() == osm.kept_set_brute(z, top_k=3) == [0, 1, 3]
+    assert e[1] == 0.0 and e[3] == 1.0
+    law, _ = osm.transformed_law(z, top_k=3)
+    assert law[1] == 0.0
 
 
 def test_top_k_without_ties_keeps_exactly_k():
@@ -99,6 +111,8 @@ def test_top_p_matches_enumeration(seed):
                 kept = sorted(np.nonzero(law > 0)[0].tolist())
                 assert kept == osm.kept_set_brute(z, top_k=k, top_p=P, allowed=allowed, temperature=tau), \
                     (seed, tau, k, P)
+                keep = osm.kept_set(z, temperature=tau, top_k=k, top_p=P, allowed=allowed)[0]
+                assert np.nonzero(keep)[0].tolist() == kept
 
 
 def test_top_p_kept_mass_reaches_p_minimally():
