@@ -63,6 +63,7 @@ LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 40
 # launches of a layer in dependency order; projections that read the same input share one
 LAUNCHES = [("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,))]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_gemm_8b_layer_t5_traffic.json")
+STEPS_PER_GRAPH = 8  # headline steps captured in one HIP graph (the pool's layer count is a multiple)
 CALIB_MB = 512
 GEMM_SRC = os.path.join(ROOT, "mx_fp4_weight_amd", "csrc", "gemm.hip")
 
@@ -1095,16 +1096,43 @@ def main():
             step(li)
         graphs.append(g)
     torch.cuda.synchronize()
+    # Graphs of STEPS_PER_GRAPH consecutive steps (pool layers i .. i + G - 1, each followed by
+    # its spec_accept), as a decoding step replays one graph for the whole forward pass: a graph
+    # per single step adds one inter-graph gap per step that a forward pass does not have.
+    G = min(STEPS_PER_GRAPH, n_layers)
+    group_graphs = []
+    for gi in range(0, n_layers - G + 1, G):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for li in range(gi, gi + G):
+                step(li)
+        group_graphs.append(g)
+    torch.cuda.synchronize()
     for s in range(args.warmup):
         graphs[s % n_layers].replay()
     torch.cuda.synchronize()
 
-    # timed region: K graph replays (one step each)
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        graphs[(args.warmup + s) % n_layers].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def timed_steps(grouped):
+        """Wall seconds for exactly args.steps steps after the warmup: whole groups of G steps
+        from the grouped graphs, the rest from single-step graphs (grouped=False: all single)."""
+        s = args.warmup
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        left = args.steps
+        if grouped:
+            while left >= G:
+                group_graphs[(s // G) % len(group_graphs)].replay()
+                s += G
+                left -= G
+        for _ in range(left):
+            graphs[s % n_layers].replay()
+            s += 1
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    # timed region: K steps, G per graph replay; then the same K steps one graph per step
+    wall = timed_steps(True)
+    wall_single = timed_steps(False)
 
     # Kernel durations: for each launch type one graph that runs it on every pool
     # layer back to back (cold weights, no host gaps between kernels), bracketed by
@@ -1196,6 +1224,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "steps_per_graph": G,
+        "ms_per_step_one_graph_per_step": round(wall_single / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
