@@ -567,9 +567,9 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   // lane L fetches the chunk that belongs at unit 64t + L. Rows past m and groups
   // past k are outside the descriptor and read as zero.
   static_assert(BM % kWaves == 0, "each wave stages the same number of rows");
-  auto stage_x = [&](int s, int buf) {
+  auto stage_x_rows = [&](int s, int buf, auto lo, auto hi) {
 #pragma unroll
-    for (int i = 0; i < BM / kWaves; ++i) {
+    for (int i = decltype(lo)::value; i < decltype(hi)::value; ++i) {
       const int t = wave + kWaves * i;
       const int q = lane ^ (t & 15);
       // slot q: chunk q % 16 of the group of k quarter q / 16
@@ -581,6 +581,16 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
           (__attribute__((address_space(3))) void*)(smem + buf * kUnits + 64 * t);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
     }
+  };
+  auto stage_x = [&](int s, int buf) {
+    stage_x_rows(s, buf, std::integral_constant<int, 0>{}, std::integral_constant<int, BM / kWaves>{});
+  };
+  // the rows of slice d's share when a step's staging is spread over its four MFMA slices
+  constexpr int kRowsPer = BM / kWaves;
+  auto stage_x_slice = [&](int s, int buf, auto dc) {
+    constexpr int d = decltype(dc)::value;
+    constexpr int lo = (kRowsPer * d) / 4, hi = (kRowsPer * (d + 1)) / 4;
+    stage_x_rows(s, buf, std::integral_constant<int, lo>{}, std::integral_constant<int, hi>{});
   };
 
   f32x4 acc[4][MC];
@@ -597,7 +607,7 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
     for (int i = 0; i < 4; ++i) sf[i] = ok ? e8m0_to_f32((sc[i][s & 3] >> (8 * g)) & 0xffu) : 1.0f;
   };
 
-  auto compute = [&](int buf, const W4& w, const float (&sf)[4]) {
+  auto compute = [&](int buf, const W4& w, const float (&sf)[4], auto&& before_slice) {
     const u32x4* src = smem + buf * kUnits;
     // B operand of slice d, column tile c: lane (r, g) takes chunk kq*16 + 4g + d of
     // tile row 16c + r (the k permutation of the skinny kernel), stored at slot
@@ -608,8 +618,9 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
     bf16x8 bb[2][MC];
 #pragma unroll
     for (int c = 0; c < MC; ++c) bb[0][c] = __builtin_bit_cast(bf16x8, bsrc[16 * c * 64 + xq]);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    auto slice = [&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      before_slice(dc);
       if (d < 3) {
 #pragma unroll
         for (int c = 0; c < MC; ++c)
@@ -622,14 +633,17 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
         for (int c = 0; c < MC; ++c)
           acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[d & 1][c], acc[i][c], 0, 0, 0);
       }
-    }
+    };
+    slice(std::integral_constant<int, 0>{});
+    slice(std::integral_constant<int, 1>{});
+    slice(std::integral_constant<int, 2>{});
+    slice(std::integral_constant<int, 3>{});
   };
 
   // The staging and weight loads of step s + 1 are issued before the MFMAs of step
   // s (scheduling barriers keep them there). After the compute each wave waits for
   // its staging loads only (the weight loads issued after them stay in flight; the
   // counter retires in order), then the barrier makes every wave's rows visible.
-  constexpr int kWLoads = 4;  // VMEM loads of one load_w
   W4 wa, wb;
   u32x4 sc[4], scn[4];
   float sf[4];
@@ -643,15 +657,19 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   // codes and add nothing.
   auto step = [&](int s, auto hc) {
     constexpr int h = decltype(hc)::value;
-    stage_x(s + h + 1, (h + 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
+    // the next step's weights first (from HBM: the longest trip), then its activation
+    // staging spread over this step's four MFMA slices, so no wave stalls behind a burst
+    // of memory instructions it cannot issue
     load_w(s + h + 1, (h & 1) ? wa : wb);
     if constexpr (h == 3) load_sc((s >> 2) + 1, scn);  // the next block's scales, with its first codes
     __builtin_amdgcn_sched_barrier(0);
     scale_of(sc, s + h, sf);
-    compute(h & 1, (h & 1) ? wb : wa, sf);
+    compute(h & 1, (h & 1) ? wb : wa, sf, [&](auto dc) {
+      stage_x_slice(s + h + 1, (h + 1) & 1, dc);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads + (h == 3 ? 4 : 0)));
+    __builtin_amdgcn_s_waitcnt(0);  // the staging was issued last: everything of this step has landed
     lds_barrier();
   };
   for (int s = 0; s < nsteps; s += 4) {
