@@ -21,6 +21,9 @@
 //           finds the piece holding u_K·Z; its weights are recomputed exactly
 //           as decide computed them, a block scan of the thread totals finds
 //           the thread, and that thread's 4 weights give t*.
+// With sampling transforms (spec_accept_sampled) four selection kernels run
+// first and leave one order-key threshold per row (top-k / top-p, see "top-k /
+// top-p thresholds" below); the three kernels then read the transformed laws.
 // The fp64 exponentials bound decide and sample at small batches, so their
 // pieces are small: many workgroups share the work of one sequence.
 // All probabilities and prefix sums are fp64; the result can differ from an
