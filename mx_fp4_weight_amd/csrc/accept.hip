@@ -81,7 +81,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Layout {
   size_t cmax, csum, cbad, gz, dec, zres, zp;
   // sampling transforms only
-  size_t thr, selcnt, selmass, selstate, selarrive, selrkey, selcandn, selcand;
+  size_t thr, selcnt, selmass, selstate, selarrive, selrkey, selcandn, selcand, selrbad, sdone;
   size_t total;
 };
 
@@ -125,6 +125,10 @@ inline Layout layout(int64_t b, int64_t kd, int64_t v, bool sampled = false) {
     off = align256(off + sizeof(uint32_t) * rows);
     L.selcand = off;
     off = align256(off + sizeof(uint32_t) * rows * kCandKeys);
+    L.selrbad = off;
+    off = align256(off + sizeof(uint32_t) * rows);
+    L.sdone = off;
+    off = align256(off + sizeof(uint32_t) * rows);
   }
   L.total = off;
   return L;
@@ -149,6 +153,7 @@ struct Transform {
   const uint32_t* thr;   // [rows] order-key thresholds; or null (no top-k / top-p)
   double inv_tau;        // 1 / temperature
   int words;             // ceil(v / 32)
+  const uint32_t* sdone; // [rows] 1: the row's statistics were written by the selection; or null
 };
 
 // fp32 -> uint32 with the same order (negatives reversed below the positives; -0 and
@@ -184,6 +189,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   __shared__ double tab[32];  // 2^(j/32) for the table-driven exp (visible after block_max)
   if (threadIdx.x < 32) tab[threadIdx.x] = kExp2Table32[threadIdx.x];
   const int64_t rowg = blockIdx.x;  // row index over all sequences
+  if constexpr (kT) {
+    if (tr.sdone && tr.sdone[rowg]) return;  // written by the selection (uniform per workgroup)
+  }
   const int per_seq = 2 * kd + 1;
   const int64_t s = rowg / per_seq;
   const int j = (int)(rowg % per_seq);
@@ -579,6 +587,20 @@ struct SelBufs {
   uint32_t* candn;   // [rows] candidate keys collected
   uint32_t* cand;    // [rows][kCand]
   uint32_t* thr;     // [rows] the thresholds
+  uint32_t* rbad;    // [rows] a NaN or +inf seen in the row (sel_count)
+};
+
+// spec_accept_sampled only: sel_finish writes the stats kernel's outputs for rows whose kept
+// set it holds sorted (top-k candidates, at most kSortMax) and marks them in sdone, so the
+// stats kernel skips them; null for the threshold-only entry point.
+struct SelStats {
+  float* cmax;            // [rows][chunks]
+  double* csum;           // [rows][chunks]
+  int32_t* cbad;          // [rows][chunks]
+  float* gz;              // [rows]
+  uint32_t* sdone;        // [rows] 1: statistics written here
+  const int32_t* tokens;  // [b][kd] draft tokens
+  int chunks;
 };
 
 struct SelArgs {
@@ -593,9 +615,11 @@ __device__ inline float key_logit(uint32_t key) {
 
 // The allowed logits of this thread's 16 tokens of a chunk (removed ones: NaN), in the
 // stats kernel's order.
+// *bad is ORed with 1 when a token of the chunk (allowed or not) is NaN or +inf.
 template <bool kVec4>
 __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t* mw, int base, int v,
-                                    float (&vals)[kPer]) {
+                                    float (&vals)[kPer], int* bad = nullptr) {
+  int b = 0;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) vals[q] = NAN;
   if constexpr (kVec4) {
@@ -607,6 +631,7 @@ __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t*
         const uint32_t w = mw ? mw[e >> 5] : 0xFFFFFFFFu;  // the 4 tokens share one mask word
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          b |= (t[i] != t[i]) | (t[i] == INFINITY);
           const bool ok = ((w >> ((e + i) & 31)) & 1u) && t[i] > -INFINITY && t[i] < INFINITY;
           vals[4 * q + i] = ok ? t[i] : NAN;
         }
@@ -618,11 +643,13 @@ __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t*
       const int e = base + (int)threadIdx.x + kThreads * q;
       if (e < v) {
         const float t = z[e];
+        b |= (t != t) | (t == INFINITY);
         const bool ok = (mw ? ((mw[e >> 5] >> (e & 31)) & 1u) != 0u : true) && t > -INFINITY && t < INFINITY;
         vals[q] = ok ? t : NAN;
       }
     }
   }
+  if (bad) *bad |= b;
 }
 
 // Block-wide max of one int per thread (kT threads); lds: kT / kWave ints.
@@ -691,6 +718,7 @@ __global__ __launch_bounds__(kThreads) void sel_clear_kernel(SelBufs sb, int mas
     sb.arrive[row] = 0u;
     sb.candn[row] = 0u;
     sb.rkey[row] = 0u;
+    sb.rbad[row] = 0u;
   }
 }
 
@@ -769,9 +797,10 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(const float* __rest
   const uint32_t* mw = mask_words(tr, s, kd, mask_row(j, kd));
   float mx = -INFINITY;
   const int c0 = (int)blockIdx.y * cpw, c1 = min(chunks, c0 + cpw);
+  int bad = 0;
   for (int c = c0; c < c1; ++c) {
     float vals[kPer];
-    chunk_logits<kVec4>(zrow, mw, c * kChunk, v, vals);
+    chunk_logits<kVec4>(zrow, mw, c * kChunk, v, vals, &bad);
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const float zq = vals[q];
@@ -783,6 +812,7 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(const float* __rest
       else atomicAdd(&hc[b], 1u);
     }
   }
+  if (bad) atomicOr(&sb.rbad[rowg], 1u);  // rare: a row that refuses its sequence
   mx = block_max<kThreads>(mx, lds_f);
   if (tid == 0 && mx > -INFINITY) atomicMax(&sb.rkey[rowg], order_key(mx));
   uint32_t* gc = sb.cnt + rowg * kSelB0;
@@ -1085,18 +1115,54 @@ __device__ uint32_t fin_topp(const Src& src, uint32_t keep_lo, double p, float r
 }
 
 constexpr int kSortMax = 512;  // candidate lists up to this size are sorted (fixed-order sums)
+static_assert(kSortMax <= kFThreads, "write_row_stats takes one sorted candidate per thread");
+
+// The stats kernel's outputs for a row whose kept set is the sorted candidates keys[0, n) from
+// thr up, none of the row's logits NaN or +inf: the row maximum and S = sum exp((z - max) / tau)
+// (one candidate per thread, a fixed-order block sum) in chunk 0 and empty other chunks, which
+// the decide kernel combines to the same (max, S); the live logit of the row's draft token.
+__device__ void write_row_stats(const uint32_t* keys, int n, uint32_t thr, float rmax, double inv_tau,
+                                const double* tab, const SelStats& ss, int64_t rowg, int64_t s, int j, int kd,
+                                int v, const float* __restrict__ z, const uint32_t* mw, FinishLds& L) {
+  const int tid = threadIdx.x;
+  const bool kept = tid < n && keys[tid] >= thr;
+  const double e = kept ? exp_neg_f64_tab(((double)key_logit(keys[tid]) - (double)rmax) * inv_tau, tab) : 0.0;
+  const double sum = block_sum_f64<kFThreads>(e, L.scan);
+  for (int c = tid; c < ss.chunks; c += kFThreads) {
+    const size_t o = (size_t)rowg * ss.chunks + c;
+    ss.cmax[o] = c == 0 ? rmax : -INFINITY;
+    ss.csum[o] = c == 0 ? sum : 0.0;
+    ss.cbad[o] = 0;
+  }
+  if (tid == 0) {
+    int xi = -1;
+    if (j < kd) xi = ss.tokens[(size_t)s * kd + j];
+    else if (j > kd) xi = ss.tokens[(size_t)s * kd + (j - kd - 1)];
+    if (xi >= 0 && xi < v) {
+      const float zx = z[xi];
+      const bool allowed = mw ? ((mw[xi >> 5] >> (xi & 31)) & 1u) != 0u : true;
+      ss.gz[rowg] = (allowed && order_key(zx) >= thr) ? zx : -INFINITY;
+    }
+  }
+}
 
 template <bool kVec4>
 __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __restrict__ target,
                                                                const float* __restrict__ draft, int kd,
                                                                int v, Transform tr, SelBufs sb,
-                                                               SelArgs sa) {
+                                                               SelArgs sa, SelStats ss) {
   __shared__ uint32_t keys[kCand];  // the candidates
   __shared__ uint32_t hc[kSelB0];   // radix passes: counts
   __shared__ double hm[kSelB0];     // radix passes: masses
   __shared__ FinishLds L;
+  __shared__ double tab[32];        // 2^(j/32) for write_row_stats (visible after the sort's barriers)
   const int64_t rowg = blockIdx.x;
   const int tid = threadIdx.x;
+  if (tid < 32) tab[tid] = kExp2Table32[tid];
+  const int per_seq = 2 * kd + 1;
+  const int64_t s = rowg / per_seq;
+  const int j = (int)(rowg % per_seq);
+  bool stats_done = false;
   SelState st = sb.state[rowg];
   const bool use_p = sa.top_p < 1.0;
   const double kf = (double)sa.top_k;
@@ -1134,6 +1200,12 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
           const int m = block_max_i32<kFThreads>(last, L.i) + 1;
           thr = topp_sorted(keys, m, 0.0, 0.0, true, st.rmax, tr.inv_tau, sa.top_p, L);
         }
+        // the kept set is here, sorted: the row's statistics too (the stats kernel skips it)
+        if (ss.cmax && n > 0 && sb.rbad[rowg] == 0u) {
+          write_row_stats(keys, n, thr, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
+                          row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
+          stats_done = true;
+        }
       } else if (n > 0) {
         thr = topp_sorted(keys, n, st.carry, st.s1, false, st.rmax, tr.inv_tau, sa.top_p, L);
       }
@@ -1147,9 +1219,6 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
       }
     }
   } else if (st.mode == kSelSlowK || st.mode == kSelSlowP || st.mode == kSelSlowPFull) {
-    const int per_seq = 2 * kd + 1;
-    const int64_t s = rowg / per_seq;
-    const int j = (int)(rowg % per_seq);
     const RowSrc<kVec4> rs{row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), v};
     if (st.mode == kSelSlowP) {
       thr = fin_digits12<true>(rs, 0u, st.lo, st.carry, sa.top_p * st.s1, st.rmax, tr.inv_tau, hc, hm, L);
@@ -1161,7 +1230,10 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
   } else {
     thr = st.thr;  // kSelDone
   }
-  if (tid == 0) sb.thr[rowg] = thr;
+  if (tid == 0) {
+    sb.thr[rowg] = thr;
+    if (ss.sdone) ss.sdone[rowg] = stats_done ? 1u : 0u;
+  }
 }
 
 // ---------------------------------------------------------------- decide + piece totals
@@ -1525,8 +1597,8 @@ namespace {
 // the stats kernel numbers them; at least one of top-k (sa.top_k > 0) and top-p
 // (sa.top_p < 1) is on.
 hipError_t launch_selection(const float* target, const float* draft, int32_t b, int32_t kd, int32_t v,
-                            const Transform& tr, const SelBufs& sb, const SelArgs& sa, bool vec4,
-                            hipStream_t stream) {
+                            const Transform& tr, const SelBufs& sb, const SelArgs& sa, const SelStats& ss,
+                            bool vec4, hipStream_t stream) {
   const int chunks = (v + kChunk - 1) / kChunk;
   const int64_t rows = (int64_t)b * (2 * kd + 1);
   const bool mass = sa.top_k == 0;  // top-p alone: digit-0 masses in sel_count
@@ -1546,9 +1618,9 @@ hipError_t launch_selection(const float* target, const float* draft, int32_t b, 
   if (vec4) sel_collect_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb);
   else sel_collect_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb);
   if (vec4)
-    sel_finish_kernel<true><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa);
+    sel_finish_kernel<true><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa, ss);
   else
-    sel_finish_kernel<false><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa);
+    sel_finish_kernel<false><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa, ss);
   return hipGetLastError();
 }
 
@@ -1559,7 +1631,7 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t value) {
 
 // Selection buffers of `rows` rows carved from a workspace (thresholds elsewhere).
 struct SelLayout {
-  size_t cnt, mass, state, arrive, rkey, candn, cand, total;
+  size_t cnt, mass, state, arrive, rkey, rbad, candn, cand, total;
 };
 inline SelLayout sel_layout(int64_t rows) {
   SelLayout L;
@@ -1573,6 +1645,8 @@ inline SelLayout sel_layout(int64_t rows) {
   L.arrive = off;
   off = align256(off + sizeof(uint32_t) * rows);
   L.rkey = off;
+  off = align256(off + sizeof(uint32_t) * rows);
+  L.rbad = off;
   off = align256(off + sizeof(uint32_t) * rows);
   L.candn = off;
   off = align256(off + sizeof(uint32_t) * rows);
@@ -1608,10 +1682,11 @@ hipError_t launch_sampling_thresholds(const float* logits, int32_t rows, int32_t
   sb.rkey = reinterpret_cast<uint32_t*>(base + L.rkey);
   sb.candn = reinterpret_cast<uint32_t*>(base + L.candn);
   sb.cand = reinterpret_cast<uint32_t*>(base + L.cand);
+  sb.rbad = reinterpret_cast<uint32_t*>(base + L.rbad);
   sb.thr = out_thr;
   const SelArgs sa{use_k ? sp.top_k : 0, use_p ? (double)sp.top_p : 1.0};
   // one "sequence" per row with no draft rows: row s is logits + s·v, mask row s
-  return launch_selection(logits, nullptr, rows, 0, v, tr, sb, sa, vec4, stream);
+  return launch_selection(logits, nullptr, rows, 0, v, tr, sb, sa, SelStats{}, vec4, stream);
 }
 
 size_t accept_workspace_bytes(int64_t b, int64_t kd, int64_t v, bool sampled) {
@@ -1657,10 +1732,13 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
       sb.candn = reinterpret_cast<uint32_t*>(base + L.selcandn);
       sb.cand = reinterpret_cast<uint32_t*>(base + L.selcand);
       sb.thr = reinterpret_cast<uint32_t*>(base + L.thr);
+      sb.rbad = reinterpret_cast<uint32_t*>(base + L.selrbad);
       const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0};
-      if ((e = launch_selection(target, draft, b, kd, v, tr, sb, sa, vec4, stream)) != hipSuccess) return e;
-      uint32_t* thr = sb.thr;
-      tr.thr = thr;
+      const SelStats ss{ws.cmax, ws.csum, ws.cbad, ws.gz, reinterpret_cast<uint32_t*>(base + L.sdone), tokens,
+                        chunks};
+      if ((e = launch_selection(target, draft, b, kd, v, tr, sb, sa, ss, vec4, stream)) != hipSuccess) return e;
+      tr.thr = sb.thr;
+      tr.sdone = ss.sdone;
     }
   }
 

@@ -164,3 +164,19 @@ def test_workspace_reused_across_settings():
         keep_rows = ~ref["flagged"]
         assert np.array_equal(out[keep_rows], ref["out_tokens"][keep_rows]), i
         assert f == int(np.bitwise_or.reduce(ref["flags"]))
+
+
+def test_nonfinite_rows_under_top_k():
+    """A NaN or +inf logit anywhere in a row refuses its sequence also when top-k / top-p leave
+    it out of the kept set (the selection then leaves that row's statistics to the stats pass);
+    the other sequences keep their tokens."""
+    say("sampled: non-finite logits under top-k")
+    b, kd, v = 6, 3, 8192
+    tgt, dft, _, u = synth.accept_batch(29, b, kd, v, 2.0, 0.7)
+    tgt[1, 0, 17] = np.nan      # target row 0 of sequence 1
+    dft[2, 1, 4000] = np.inf    # draft row 1 of sequence 2
+    tgt[3, kd, 5] = np.nan      # bonus row of sequence 3
+    for tau, k, p in [(1.0, 20, 1.0), (0.8, 50, 0.9)]:
+        tok = transformed_draft_tokens(np.nan_to_num(dft, nan=0.0, posinf=0.0), tau, k, p, None, 29, 0)
+        ref = compare(tgt, dft, tok, u, tau, k, p, None, f"nonfinite tau={tau} k={k} p={p}")
+        assert all(ref["n"][i] == 0 for i in (1, 2, 3)) and ref["flags"][1] & mxs.FLAG_NONFINITE
