@@ -180,3 +180,12 @@ def test_nonfinite_rows_under_top_k():
         tok = transformed_draft_tokens(np.nan_to_num(dft, nan=0.0, posinf=0.0), tau, k, p, None, 29, 0)
         ref = compare(tgt, dft, tok, u, tau, k, p, None, f"nonfinite tau={tau} k={k} p={p}")
         assert all(ref["n"][i] == 0 for i in (1, 2, 3)) and ref["flags"][1] & mxs.FLAG_NONFINITE
+
+
+@pytest.mark.parametrize("tau,k,p,keep", [(0.8, 50, 0.9, 0.9), (1.0, 0, 0.95, None)])
+def test_batch_64_full_vocab(tau, k, p, keep):
+    """The batched configuration the bench times: B = 64, K = 4, V = 128256 (576 rows; the counting
+    pass then takes 8 chunks per workgroup)."""
+    say(f"sampled: B=64 V=128256 K=4 tau={tau} k={k} p={p} keep={keep}")
+    tgt, dft, tok, u, mask = inputs(30, 64, 4, 128256, 3.0, 1.0, tau, k, p, keep, seq0=1000 + k)
+    compare(tgt, dft, tok, u, tau, k, p, mask, f"B=64 tau={tau} k={k} p={p}")

@@ -149,3 +149,14 @@ def test_both_off_is_zero():
     z = normal_rows(6, 4, 1000)
     assert not device_thresholds(z, 1.0, 0, 1.0, None).any()
     assert not device_thresholds(z, 1.0, 1000, 1.0, None).any()
+
+
+@pytest.mark.parametrize("rows", [300, 576])
+def test_many_rows_several_chunks_per_workgroup(rows):
+    """Batches large enough that each counting workgroup takes several 4096-logit chunks of its row
+    (rows x 32 chunks >= 4096: 4 and 8 chunks per workgroup), as spec_accept_sampled at B = 64."""
+    say(f"thresholds: {rows} rows of V=128256")
+    v = 128256
+    z = normal_rows(rows, rows, v)
+    for tau, k, p in [(0.8, 50, 0.9), (1.0, 0, 0.95), (1.0, 300, 1.0)]:
+        compare(z, tau, k, p, None, f"{rows} rows tau={tau} k={k} p={p}")
