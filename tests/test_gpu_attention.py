@@ -58,6 +58,7 @@ def check(got, kc, ks, vc, vs, q, ctxs, masks, label):
 
 @pytest.mark.parametrize("b,ctxs,t,hq,hkv,masks_of", [
     (1, [4096], 5, 32, 8, "chain"),       # 8B-class: 32 query heads on 8 KV heads, T = 5
+    (16, [4096] * 16, 5, 32, 8, "chain"), # the same for 16 sequences (the bench's batched call)
     (2, [1000, 37], 10, 8, 2, "tree"),    # a 3x2 tree (40 query rows per KV head: 4 tiles)
     (3, [0, 5, 130], 3, 4, 4, "chain"),   # one query head per KV head
     (1, [2047], 1, 16, 2, "chain"),       # a plain decode step

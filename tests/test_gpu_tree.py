@@ -55,11 +55,13 @@ def test_trees_match_oracle(name, v, sigma):
     compare(parent, tgt, dft, tok, u, f"{name} v={v}")
 
 
-def test_batched_64_binary_tree():
-    parent = TREES["binary3"]
-    say("tree: binary3 B=64 V=128256")
+@pytest.mark.parametrize("name", ["chain4", "3x2", "binary3"])
+def test_batched_64(name):
+    """B = 64 at V = 128256: the batched calls the bench times (large-grid passes)."""
+    parent = TREES[name]
+    say(f"tree: {name} B=64 V=128256")
     tgt, dft, tok, u = synth.tree_batch(10, 64, parent, 128256, 3.0, 0.5)
-    compare(parent, tgt, dft, tok, u, "binary3 b=64")
+    compare(parent, tgt, dft, tok, u, f"{name} b=64")
 
 
 def test_no_drafts_is_a_bonus_draw():
