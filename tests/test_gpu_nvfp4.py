@@ -299,3 +299,27 @@ def test_grouped_tiled_matches_row_layout(shapes, k, m):
         if n * k <= 1 << 22:
             c, s, g, _ = nv.quantize(w)
             check_gemm(c, s, g, xb, host(b), label=f"grouped tiled n={n}")
+
+
+@pytest.mark.parametrize("t", [1, 5, 8])
+def test_bench_launches_tiled_match_row_layout(t):
+    """The four launches the NVFP4 bench times on the 8B-class layer (q|k|v and gate|up grouped, o
+    and down single; codes tiled by mxfp4_tile_codes) return the row-layout results bit for bit,
+    the row layout being held to the oracle at these shapes above."""
+    say(f"nvfp4 bench launches, tiled vs row layout, T={t}")
+    groups = [([4096, 1024, 1024], 4096), ([4096], 4096), ([14336, 14336], 4096), ([4096], 14336)]
+    for gi, (shapes, k) in enumerate(groups):
+        items, titems = [], []
+        for i, n in enumerate(shapes):
+            w = synth.weights(79, 10 * gi + i, n, k)
+            dc, ds, dg = mxs.nvfp4_quantize(dev(w))
+            del w
+            x = dev_bf16(synth.activations(79, 10 * gi + i, t, k))
+            items.append((dc, ds, dg, x))
+            titems.append((mxs.mxfp4_tile_codes(dc), ds, dg, n, x))
+        ys = mxs.nvfp4_verify_gemm_grouped(items)
+        yt = mxs.nvfp4_verify_gemm_grouped_tiled(titems)
+        torch.cuda.synchronize()
+        for n, a, b in zip(shapes, ys, yt):
+            assert torch.equal(a, b), (shapes, n, k, t)
+        say(f"  {shapes} k={k}: bit-identical")
