@@ -524,22 +524,24 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces
 // digit 0 (its top 12 bits: sign, exponent and 3 fraction bits of the logit) and two
 // 10-bit digits. Per call:
 //   sel_clear     zeroes each row's digit-0 histogram, counters and maximum.
-//   sel_count     grid (rows, 4096-logit chunks), one read of the logits: the row maximum
-//                 (an atomic max of order keys) and the digit-0 histogram: counts for top-k;
-//                 for top-p alone counts and masses exp(z / tau) against the reference 0,
-//                 which needs no row maximum. The row's last workgroup to arrive finds the
-//                 digit-0 bucket holding the boundary (the lowest non-empty bucket with fewer
-//                 than k tokens, or less than P·S mass, strictly above it) and sets the row's
-//                 course (SelMode).
+//   sel_count     grid (rows, groups of 4096-logit chunks), one read of the logits: the row
+//                 maximum (an atomic max of order keys), whether the row holds a NaN or +inf,
+//                 and the digit-0 histogram: counts for top-k; for top-p alone masses
+//                 exp(z / tau) against the reference 0, which needs no row maximum. The row's
+//                 last workgroup to arrive finds the digit-0 bucket holding the boundary (the
+//                 lowest non-empty bucket with fewer than k tokens, or less than P·S mass,
+//                 strictly above it) and sets the row's course (SelMode).
 //   sel_collect   grid (rows, chunks), one read: the candidate keys into the row's list — for
 //                 top-k every key from the boundary bucket up (fewer than k + the bucket's
 //                 count), for top-p the boundary bucket's keys.
-//   sel_finish    one workgroup per row: sorts the candidates in LDS (descending keys) and
-//                 reads the thresholds off the sorted list: top-k is the k-th key; top-p tests
-//                 each distinct key's strictly-larger mass, summed in the sorted order. A row
-//                 whose candidates do not fit the list, a top-p row whose top-k kept every
-//                 token, and a top-p row whose exp(z / tau) would leave fp64's range against 0
-//                 are finished by this workgroup alone with radix passes over the row
+//   sel_finish    one workgroup per row, candidates in LDS: a list of up to kSortMax keys is
+//                 sorted (descending) and the thresholds read off it — top-k is the k-th key;
+//                 top-p tests each distinct key's strictly-larger mass, summed in the sorted
+//                 order — and for top-k the row's statistics are written too (the stats kernel
+//                 then skips the row); a longer list is resolved by radix passes over the keys
+//                 in LDS. A row whose candidates do not fit the list, a top-p row whose top-k
+//                 kept every token, and a top-p row whose exp(z / tau) would leave fp64's range
+//                 against 0 are finished by this workgroup alone with radix passes over the row
 //                 (histograms in LDS, masses against the row maximum).
 // The digit-0 histograms are added with device-scope atomics; each workgroup waits for its
 // own before it counts its arrival, and the resolving workgroup reads them with device-scope
@@ -551,6 +553,8 @@ constexpr int kSelBits1 = 10;               // digits 1 and 2
 constexpr int kCand = 8192;                 // candidate keys per row
 constexpr int kFThreads = 512;              // sel_finish
 constexpr int kFWaves = kFThreads / kWave;
+constexpr int kSortMax = 512;  // candidate lists up to this size are sorted (fixed-order sums)
+static_assert(kSortMax <= kFThreads, "a sorted list is walked with one candidate per thread");
 // top-p alone takes its digit-0 masses against the reference 0 when the row maximum m has
 // m / tau in this range: every exp(z / tau) and their sum stay finite, and a token that
 // underflows against 0 has mass below e^-45 of the maximum's (it cannot sit at a boundary
@@ -919,7 +923,7 @@ __global__ __launch_bounds__(kThreads) void sel_collect_kernel(const float* __re
 
 // Sorts keys[0, n) in LDS into descending order (bitonic network over the next power of two,
 // padded with key 0, which is below every finite logit's key).
-__device__ void sort_desc(uint32_t* keys, int n) {
+__device__ __forceinline__ void sort_desc(uint32_t* keys, int n) {
   int np = 1;
   while (np < n) np <<= 1;
   for (int i = n + (int)threadIdx.x; i < np; i += kFThreads) keys[i] = 0u;
@@ -949,13 +953,13 @@ struct FinishLds {
   int i[kFWaves];
 };
 
-// top-p over the sorted candidates keys[0, lim): carry is the mass strictly above them; S is
-// s_given, or (s_from_sum) the candidates' own total. Thread t takes the contiguous positions
-// [t·per, t·per + per), so every sum runs in the sorted order. Returns the lowest key whose
-// strictly-larger mass is below P·S.
-__device__ uint32_t topp_sorted(const uint32_t* keys, int lim, double carry, double s_given, bool s_from_sum,
+// top-p over the sorted candidates keys[0, lim), lim <= kSortMax: carry is the mass strictly
+// above them; S is s_given, or (s_from_sum) the candidates' own total. Thread t takes the
+// contiguous positions [t·per, t·per + per), so every sum runs in the sorted order. Returns the
+// lowest key whose strictly-larger mass is below P·S.
+__device__ __forceinline__ uint32_t topp_sorted(const uint32_t* keys, int lim, double carry, double s_given, bool s_from_sum,
                                 float rmax, double inv_tau, double p, FinishLds& L) {
-  constexpr int kMaxPer = kCand / kFThreads;
+  constexpr int kMaxPer = (kSortMax + kFThreads - 1) / kFThreads;
   const int tid = threadIdx.x;
   const int per = (lim + kFThreads - 1) / kFThreads;
   const int i0 = tid * per;
@@ -1027,11 +1031,11 @@ struct KeySrc {
 
 // One radix pass of the finishing workgroup: histogram of the digit (key >> shift) & (nb - 1)
 // of the source's tokens whose key is at least keep_lo and, when mshift < 32, whose
-// key >> mshift equals mval; counts, and with kMass masses exp((z - rmax) / tau) (their total
-// over the selected tokens in *s_out).
+// key >> mshift equals mval; counts, and with kMass masses exp((z - rmax) / tau). Returns the
+// masses' total over the selected tokens (0 without kMass).
 template <bool kMass, class Src>
-__device__ void fin_hist(const Src& src, uint32_t keep_lo, int mshift, uint32_t mval, int shift, int nb,
-                         float rmax, double inv_tau, uint32_t* hc, double* hm, double* s_out, FinishLds& L) {
+__device__ __forceinline__ double fin_hist(const Src& src, uint32_t keep_lo, int mshift, uint32_t mval, int shift, int nb,
+                           float rmax, double inv_tau, uint32_t* hc, double* hm, FinishLds& L) {
   for (int b = threadIdx.x; b < nb; b += kFThreads) {
     hc[b] = 0u;
     if constexpr (kMass) hm[b] = 0.0;
@@ -1048,16 +1052,15 @@ __device__ void fin_hist(const Src& src, uint32_t keep_lo, int mshift, uint32_t 
       acc += e;
     }
   });
-  if constexpr (kMass) {
-    const double tot = block_sum_f64<kFThreads>(acc, L.scan);
-    if (s_out) *s_out = tot;
-  }
+  double tot = 0.0;
+  if constexpr (kMass) tot = block_sum_f64<kFThreads>(acc, L.scan);
   __syncthreads();
+  return tot;
 }
 
 // The boundary bucket of an LDS histogram of nb buckets (1024 or 4096) walked downwards.
 template <bool kMass>
-__device__ int fin_resolve(const uint32_t* hc, const double* hm, int nb, double carry, double target,
+__device__ __forceinline__ int fin_resolve(const uint32_t* hc, const double* hm, int nb, double carry, double target,
                            double* above, FinishLds& L) {
   double total;
   if (nb == kSelB0) {
@@ -1088,12 +1091,12 @@ __device__ int fin_resolve(const uint32_t* hc, const double* hm, int nb, double 
 // threshold key. A bucket that does not resolve (only if the row changed during the call)
 // keeps every token of the prefix.
 template <bool kMass, class Src>
-__device__ uint32_t fin_digits12(const Src& src, uint32_t keep_lo, uint32_t prefix, double carry, double target,
+__device__ __forceinline__ uint32_t fin_digits12(const Src& src, uint32_t keep_lo, uint32_t prefix, double carry, double target,
                                  float rmax, double inv_tau, uint32_t* hc, double* hm, FinishLds& L) {
   for (int d = 1; d <= 2; ++d) {
     const int mshift = d == 1 ? kSelShift0 : kSelBits1;
     const int shift = d == 1 ? kSelBits1 : 0;
-    fin_hist<kMass>(src, keep_lo, mshift, prefix, shift, 1 << kSelBits1, rmax, inv_tau, hc, hm, nullptr, L);
+    fin_hist<kMass>(src, keep_lo, mshift, prefix, shift, 1 << kSelBits1, rmax, inv_tau, hc, hm, L);
     double above = carry;
     const int b = fin_resolve<kMass>(hc, hm, 1 << kSelBits1, carry, target, &above, L);
     prefix = (prefix << kSelBits1) | (uint32_t)(b >= 0 ? b : 0);
@@ -1104,24 +1107,21 @@ __device__ uint32_t fin_digits12(const Src& src, uint32_t keep_lo, uint32_t pref
 
 // top-p over the source's tokens with key >= keep_lo (the tokens top-k kept), all three digits.
 template <class Src>
-__device__ uint32_t fin_topp(const Src& src, uint32_t keep_lo, double p, float rmax, double inv_tau, uint32_t* hc,
+__device__ __forceinline__ uint32_t fin_topp(const Src& src, uint32_t keep_lo, double p, float rmax, double inv_tau, uint32_t* hc,
                              double* hm, FinishLds& L) {
-  double s1 = 0.0;
-  fin_hist<true>(src, keep_lo, 32, 0u, kSelShift0, kSelB0, rmax, inv_tau, hc, hm, &s1, L);
+  const double s1 = fin_hist<true>(src, keep_lo, 32, 0u, kSelShift0, kSelB0, rmax, inv_tau, hc, hm, L);
   double above = 0.0;
   const int b = fin_resolve<true>(hc, hm, kSelB0, 0.0, p * s1, &above, L);
   if (b < 0) return keep_lo;
   return fin_digits12<true>(src, keep_lo, (uint32_t)b, above, p * s1, rmax, inv_tau, hc, hm, L);
 }
 
-constexpr int kSortMax = 512;  // candidate lists up to this size are sorted (fixed-order sums)
-static_assert(kSortMax <= kFThreads, "write_row_stats takes one sorted candidate per thread");
 
 // The stats kernel's outputs for a row whose kept set is the sorted candidates keys[0, n) from
 // thr up, none of the row's logits NaN or +inf: the row maximum and S = sum exp((z - max) / tau)
 // (one candidate per thread, a fixed-order block sum) in chunk 0 and empty other chunks, which
 // the decide kernel combines to the same (max, S); the live logit of the row's draft token.
-__device__ void write_row_stats(const uint32_t* keys, int n, uint32_t thr, float rmax, double inv_tau,
+__device__ __forceinline__ void write_row_stats(const uint32_t* keys, int n, uint32_t thr, float rmax, double inv_tau,
                                 const double* tab, const SelStats& ss, int64_t rowg, int64_t s, int j, int kd,
                                 int v, const float* __restrict__ z, const uint32_t* mw, FinishLds& L) {
   const int tid = threadIdx.x;
