@@ -657,19 +657,34 @@ __global__ __launch_bounds__(kDenseThreads) void gemm_dense_kernel(
   // codes and add nothing.
   auto step = [&](int s, auto hc) {
     constexpr int h = decltype(hc)::value;
-    // the next step's weights first (from HBM: the longest trip), then its activation
-    // staging spread over this step's four MFMA slices, so no wave stalls behind a burst
-    // of memory instructions it cannot issue
-    load_w(s + h + 1, (h & 1) ? wa : wb);
-    if constexpr (h == 3) load_sc((s >> 2) + 1, scn);  // the next block's scales, with its first codes
-    __builtin_amdgcn_sched_barrier(0);
-    scale_of(sc, s + h, sf);
-    compute(h & 1, (h & 1) ? wb : wa, sf, [&](auto dc) {
-      stage_x_slice(s + h + 1, (h + 1) & 1, dc);
+    if constexpr (kTiled) {
+      // the next step's weights first (from HBM: the longest trip), then its activation
+      // staging spread over this step's four MFMA slices, so no wave stalls behind a burst
+      // of memory instructions it cannot issue
+      load_w(s + h + 1, (h & 1) ? wa : wb);
+      if constexpr (h == 3) load_sc((s >> 2) + 1, scn);  // the next block's scales, with its first codes
       __builtin_amdgcn_sched_barrier(0);
-    });
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);  // the staging was issued last: everything of this step has landed
+      scale_of(sc, s + h, sf);
+      compute(h & 1, (h & 1) ? wb : wa, sf, [&](auto dc) {
+        stage_x_slice(s + h + 1, (h + 1) & 1, dc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);  // the staging was issued last: everything of this step has landed
+    } else {
+      // row layout (the address arithmetic of its 16-row weight loads leaves no registers for
+      // the interleaving): the staging as one burst, then the weights; after the MFMAs wait
+      // for the staging only (the weight loads issued after it stay in flight)
+      stage_x(s + h + 1, (h + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(s + h + 1, (h & 1) ? wa : wb);
+      if constexpr (h == 3) load_sc((s >> 2) + 1, scn);
+      __builtin_amdgcn_sched_barrier(0);
+      scale_of(sc, s + h, sf);
+      compute(h & 1, (h & 1) ? wb : wa, sf, [](auto) {});
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(4 + (h == 3 ? 4 : 0)));  // 4 code loads (+ 4 scale loads)
+    }
     lds_barrier();
   };
   for (int s = 0; s < nsteps; s += 4) {
@@ -1080,11 +1095,8 @@ hipError_t launch_group(Config c, const mxs_problem_view* pv, int count, int64_t
     for (int i = 0; i < count; ++i) pairs += ((pv[i].n + 15) / 16 + 1) / 2;
     if (pp.phases > 1 && pairs >= device_cus() && c.R == 1 && c.G == 4 && c.D == 2)
       return launch_main<1, 4, 2, false, true>(c, pp, pv, count, k, m, stream);
-#define MXS_RG(RR, GG, DD) \
-  if (c.R == RR && c.G == GG && c.D == DD) return launch_main<RR, GG, DD>(c, pp, pv, count, k, m, stream);
-    MXS_RG(1, 4, 2) MXS_RG(2, 4, 2) MXS_RG(1, 8, 2) MXS_RG(2, 8, 2)
-#undef MXS_RG
-    return hipErrorInvalidValue;
+    if (c.R == 1 && c.G == 4 && c.D == 2) return launch_main<1, 4, 2>(c, pp, pv, count, k, m, stream);
+    return hipErrorInvalidValue;  // choose() returns the one configuration built
   }
   for (int i = 0; i < count; ++i) {
     const hipError_t e =
