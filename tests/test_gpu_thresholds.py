@@ -160,3 +160,26 @@ def test_many_rows_several_chunks_per_workgroup(rows):
     z = normal_rows(rows, rows, v)
     for tau, k, p in [(0.8, 50, 0.9), (1.0, 0, 0.95), (1.0, 300, 1.0)]:
         compare(z, tau, k, p, None, f"{rows} rows tau={tau} k={k} p={p}")
+
+
+def test_random_settings():
+    """A seeded sweep of 40 random settings: vocabulary 2..20000, 1..40 rows, logit spreads from
+    0.01 to 30 around offsets 0, 5 or -50 (or small integers: ties), temperature 0.05..3, top-k off /
+    1 / up to v, top-p off or 0.05..0.999, masks keeping 5% to 95% of tokens or none."""
+    r = synth.rng(36, 0)
+    for case in range(40):
+        v = int(r.integers(2, 20001))
+        rows = int(r.integers(1, 41))
+        if r.random() < 0.2:
+            z = r.integers(-3, 4, size=(rows, v)).astype(np.float32)
+        else:
+            sigma = float(r.choice([0.01, 0.3, 3.0, 30.0]))
+            mu = float(r.choice([0.0, 5.0, -50.0]))
+            z = (mu + sigma * r.standard_normal((rows, v))).astype(np.float32)
+        tau = float(np.float32(r.uniform(0.05, 3.0)))
+        kc = r.random()
+        k = 0 if kc < 0.3 else (1 if kc < 0.4 else int(r.integers(1, v + 1)))
+        p = 1.0 if r.random() < 0.3 else float(np.float32(r.uniform(0.05, 0.999)))
+        keep = None if r.random() < 0.5 else float(r.choice([0.05, 0.5, 0.95]))
+        allowed = None if keep is None else r.random((rows, v)) < keep
+        compare(z, tau, k, p, allowed, f"case {case}: v={v} rows={rows} tau={tau:.3f} k={k} p={p:.3f} keep={keep}")
