@@ -21,8 +21,8 @@
 //           finds the piece holding u_K·Z; its weights are recomputed exactly
 //           as decide computed them, a block scan of the thread totals finds
 //           the thread, and that thread's 4 weights give t*.
-// With sampling transforms (spec_accept_sampled) four selection kernels run
-// first and leave one order-key threshold per row (top-k / top-p, see "top-k /
+// With sampling transforms (spec_accept_sampled) two or four selection kernels
+// run first and leave one order-key threshold per row (top-k / top-p, see "top-k /
 // top-p thresholds" below); the three kernels then read the transformed laws.
 // The fp64 exponentials bound decide and sample at small batches, so their
 // pieces are small: many workgroups share the work of one sequence.
@@ -522,7 +522,13 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces
 // A row's threshold is an order key: a token stays iff it is allowed, finite and its key
 // is at least the threshold (0 keeps every allowed finite token). The key splits into
 // digit 0 (its top 12 bits: sign, exponent and 3 fraction bits of the logit) and two
-// 10-bit digits. Per call:
+// 10-bit digits. Top-k with k at most 256 and at least 2k list slots per chunk (every
+// common vocabulary) takes two kernels:
+//   sel_chunk     grid (rows, chunks), one read of the logits: each chunk's keys from a lower
+//                 bound of its own k-th largest up go to the chunk's own slots of the row's
+//                 list (see sel_chunk below), with a record of their count and bound.
+//   sel_finish    as below, on the union of the chunks' candidates from the largest bound up.
+// Top-p alone and larger k take four:
 //   sel_clear     zeroes each row's digit-0 histogram, counters and maximum.
 //   sel_count     grid (rows, groups of 4096-logit chunks), one read of the logits: the row
 //                 maximum (an atomic max of order keys), whether the row holds a NaN or +inf,
@@ -538,11 +544,14 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces
 //                 sorted (descending) and the thresholds read off it — top-k is the k-th key;
 //                 top-p tests each distinct key's strictly-larger mass, summed in the sorted
 //                 order — and for top-k the row's statistics are written too (the stats kernel
-//                 then skips the row); a longer list is resolved by radix passes over the keys
-//                 in LDS. A row whose candidates do not fit the list, a top-p row whose top-k
-//                 kept every token, and a top-p row whose exp(z / tau) would leave fp64's range
-//                 against 0 are finished by this workgroup alone with radix passes over the row
-//                 (histograms in LDS, masses against the row maximum).
+//                 then skips the row). A longer top-k list is first cut to the keys from a
+//                 lower bound of its k-th largest up (the k-th largest of the threads' maxima
+//                 over it), then, if still longer, resolved by radix passes over the keys in LDS
+//                 and cut to the kept set; top-p lists likewise by radix passes. A row whose
+//                 candidates do not fit the list, a top-p row whose top-k kept every token, and
+//                 a top-p row whose exp(z / tau) would leave fp64's range against 0 are finished
+//                 by this workgroup alone with radix passes over the row (histograms in LDS,
+//                 masses against the row maximum).
 // The digit-0 histograms are added with device-scope atomics; each workgroup waits for its
 // own before it counts its arrival, and the resolving workgroup reads them with device-scope
 // loads: no plain store is shared between workgroups of one launch.
@@ -568,6 +577,7 @@ enum SelMode : uint32_t {
   kSelSlowK = 3,      // top-k continues in digit-0 bucket state.lo by sel_finish's radix passes
   kSelSlowP = 4,      // top-p likewise
   kSelSlowPFull = 5,  // top-p over every allowed token by sel_finish's radix passes
+  kSelSlowKFull = 6,  // top-k (then top-p) over every allowed token by sel_finish's radix passes
 };
 
 struct SelState {
@@ -608,8 +618,10 @@ struct SelStats {
 };
 
 struct SelArgs {
-  int top_k;     // 0: off
-  double top_p;  // >= 1: off
+  int top_k;      // 0: off
+  double top_p;   // >= 1: off
+  int chunks;     // 4096-logit chunks per row
+  int slot_log2;  // > 0: top-k by per-chunk candidates, 2^slot_log2 slots per chunk (sel_chunk)
 };
 
 // The logit of an order key (inverse of order_key; -0 comes back as +0).
@@ -620,37 +632,71 @@ __device__ inline float key_logit(uint32_t key) {
 // The allowed logits of this thread's 16 tokens of a chunk (removed ones: NaN), in the
 // stats kernel's order.
 // *bad is ORed with 1 when a token of the chunk (allowed or not) is NaN or +inf.
+// Every load is issued before any is used (an index past the row reads the row's first element,
+// which is then discarded), so a workgroup waits for one memory trip, not one per load.
 template <bool kVec4>
 __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t* mw, int base, int v,
                                     float (&vals)[kPer], int* bad = nullptr) {
   int b = 0;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) vals[q] = NAN;
   if constexpr (kVec4) {
+    constexpr int kV = kPer / 4;
+    f32x4 t[kV];
+    uint32_t w[kV];
 #pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
+    for (int q = 0; q < kV; ++q) {
       const int e = base + 4 * ((int)threadIdx.x + kThreads * q);
-      if (e < v) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(z + e);
-        const uint32_t w = mw ? mw[e >> 5] : 0xFFFFFFFFu;  // the 4 tokens share one mask word
+      t[q] = *reinterpret_cast<const f32x4*>(z + (e < v ? e : 0));
+    }
+    if (mw) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          b |= (t[i] != t[i]) | (t[i] == INFINITY);
-          const bool ok = ((w >> ((e + i) & 31)) & 1u) && t[i] > -INFINITY && t[i] < INFINITY;
-          vals[4 * q + i] = ok ? t[i] : NAN;
-        }
+      for (int q = 0; q < kV; ++q) {
+        const int e = base + 4 * ((int)threadIdx.x + kThreads * q);
+        w[q] = mw[(e < v ? e : 0) >> 5];  // the 4 tokens share one mask word
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kV; ++q) w[q] = 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int q = 0; q < kV; ++q) {
+      const int e = base + 4 * ((int)threadIdx.x + kThreads * q);
+      const bool in = e < v;  // v % 4 == 0: the whole vector or none of it
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = t[q][i];
+        const uint32_t fin = __builtin_isfinite(x) ? 1u : 0u;
+        b |= (int)(in & !fin & (x > -INFINITY || x != x));  // NaN or +inf
+        const uint32_t ok = (uint32_t)in & (w[q] >> ((e + i) & 31)) & fin;
+        vals[4 * q + i] = ok ? x : NAN;
       }
     }
   } else {
+    float t[kPer];
+    uint32_t w[kPer];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int e = base + (int)threadIdx.x + kThreads * q;
-      if (e < v) {
-        const float t = z[e];
-        b |= (t != t) | (t == INFINITY);
-        const bool ok = (mw ? ((mw[e >> 5] >> (e & 31)) & 1u) != 0u : true) && t > -INFINITY && t < INFINITY;
-        vals[q] = ok ? t : NAN;
+      t[q] = z[e < v ? e : 0];
+    }
+    if (mw) {
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int e = base + (int)threadIdx.x + kThreads * q;
+        w[q] = mw[(e < v ? e : 0) >> 5];
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) w[q] = 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = base + (int)threadIdx.x + kThreads * q;
+      const bool in = e < v;
+      const float x = t[q];
+      const uint32_t fin = __builtin_isfinite(x) ? 1u : 0u;
+      b |= (int)(in & !fin & (x > -INFINITY || x != x));  // NaN or +inf
+      const uint32_t ok = (uint32_t)in & (w[q] >> (e & 31)) & fin;
+      vals[q] = ok ? x : NAN;
     }
   }
   if (bad) *bad |= b;
@@ -796,7 +842,6 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(const float* __rest
     if constexpr (kMass) hm[b] = 0.0;
     else hc[b] = 0u;
   }
-  __syncthreads();
   const float* zrow = row_ptr(target, draft, s, kd, j, v);
   const uint32_t* mw = mask_words(tr, s, kd, mask_row(j, kd));
   float mx = -INFINITY;
@@ -805,6 +850,7 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(const float* __rest
   for (int c = c0; c < c1; ++c) {
     float vals[kPer];
     chunk_logits<kVec4>(zrow, mw, c * kChunk, v, vals, &bad);
+    if (c == c0) __syncthreads();  // the cleared histogram (and tab): after the first loads are issued
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const float zq = vals[q];
@@ -916,6 +962,117 @@ __global__ __launch_bounds__(kThreads) void sel_collect_kernel(const float* __re
       if (slot < (uint32_t)kCand) out[slot] = order_key(vals[q]);
       ++slot;
     }
+  }
+}
+
+// ---- sel_chunk: top-k from per-chunk candidates
+// The row's k-th largest key K is at least every chunk's own k-th largest (that chunk's top k
+// are k keys of the row), so a chunk's keys from any lower bound L_c of its own k-th largest up
+// hold every key of the chunk that the row's top-k keeps. The k-th largest of the chunk's 256
+// per-thread maxima is such a bound (those k maxima are k distinct keys of the chunk), and a
+// close one: the chunk's largest keys mostly sit in different threads. One workgroup per chunk
+// finds it (to the top 16 bits of the key) with one wave (0 when fewer than k threads hold an allowed finite token: then every
+// such token is a candidate) and writes its keys from L_c up into its own slots of the
+// row's list: no histogram is shared, no counter is cleared, and the logits are read once. The
+// chunk's record holds the count (kRecOver: more keys than slots, none written; kRecBad: a NaN
+// or +inf in the chunk, allowed or not), L_c and the chunk's largest allowed finite key (0: none).
+constexpr int kMaxSelChunks = 1024;  // records of one row fill its digit-0 count area
+constexpr uint32_t kRecOver = 1u << 30, kRecBad = 1u << 31, kRecCount = kRecOver - 1u;
+static_assert(4 * kMaxSelChunks <= kSelB0, "chunk records live in the digit-0 count area");
+
+// A lower bound of the k-th largest of vals[0, kWave·kR) (LDS, kR values per lane), found by
+// the calling wave alone: the largest T whose low kSearchLow bits are 0 and with at least k
+// values >= T, built bit by bit from the top (each bit: kR compares whose ballots are counted
+// on the scalar unit). The bits below kSearchLow (below 2^-7 of a logit's magnitude) are left
+// 0: a bound a little under the k-th largest, at half the steps. Every lane returns it.
+constexpr int kSearchLow = 16;
+template <int kR>
+__device__ __forceinline__ uint32_t wave_kth_bound(const uint32_t* vals, int k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t x[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) x[r] = vals[lane * kR + r];
+  uint32_t t = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= kSearchLow; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) cnt += __popcll(__ballot(x[r] >= cand));
+    if (cnt >= k) t = cand;
+  }
+  return t;
+}
+
+// Wave-wide max of one uint32 per lane (every lane active; every lane gets it).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i32<kDppQuadXor1>((int)v));
+  v = max(v, (uint32_t)dpp_i32<kDppQuadXor2>((int)v));
+  v = max(v, (uint32_t)dpp_i32<kDppRowRor4>((int)v));
+  v = max(v, (uint32_t)dpp_i32<kDppRowRor8>((int)v));
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  return max(v, (uint32_t)__shfl_xor((int)v, 32));
+}
+
+template <bool kVec4>
+__global__ __launch_bounds__(kThreads) void sel_chunk_kernel(const float* __restrict__ target,
+                                                             const float* __restrict__ draft, int kd,
+                                                             int v, Transform tr, SelBufs sb, SelArgs sa) {
+  __shared__ __attribute__((aligned(16))) uint32_t tmax[kThreads];
+  __shared__ double lds_scan[kThreads / kWave];
+  __shared__ uint32_t s_lc, s_rk, s_bad;
+  __shared__ double s_n;
+  const int64_t rowg = blockIdx.x;
+  const int per_seq = 2 * kd + 1;
+  const int64_t s = rowg / per_seq;
+  const int j = (int)(rowg % per_seq);
+  const int c = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0u;
+  float vals[kPer];
+  int bad = 0;
+  chunk_logits<kVec4>(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)),
+                      c * kChunk, v, vals, &bad);
+  uint32_t key[kPer];
+  uint32_t m = 0u;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    key[q] = vals[q] == vals[q] ? order_key(vals[q]) : 0u;  // 0: removed (every live key is larger)
+    m = max(m, key[q]);
+  }
+  tmax[tid] = m;
+  if (bad) s_bad = 1u;
+  __syncthreads();
+  if (tid < kWave) {
+    // one wave: L_c (0 if fewer than k threads hold a live token) and the chunk's largest key
+    const uint32_t lc = wave_kth_bound<kThreads / kWave>(tmax, sa.top_k);
+    const u32x4 m4 = reinterpret_cast<const u32x4*>(tmax)[tid];
+    const uint32_t rk = wave_max_u32(max(max(m4[0], m4[1]), max(m4[2], m4[3])));
+    if (tid == 0) {
+      s_lc = lc;
+      s_rk = rk;
+    }
+  }
+  __syncthreads();
+  const uint32_t lc = s_lc;
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) mine += (key[q] && key[q] >= lc) ? 1 : 0;
+  const double incl = block_inclusive_scan_f64<kThreads>((double)mine, lds_scan);
+  if (tid == kThreads - 1) s_n = incl;
+  __syncthreads();
+  const uint32_t n = (uint32_t)s_n;
+  const bool over = n > (1u << sa.slot_log2);
+  if (!over) {
+    uint32_t* out = sb.cand + rowg * kCand + ((size_t)c << sa.slot_log2);
+    uint32_t slot = (uint32_t)incl - (uint32_t)mine;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (key[q] && key[q] >= lc) out[slot++] = key[q];
+  }
+  if (tid == 0) {
+    const u32x4 rec{(over ? kRecOver : n) | (s_bad ? kRecBad : 0u), lc, s_rk, 0u};
+    reinterpret_cast<u32x4*>(sb.cnt + rowg * kSelB0)[c] = rec;
   }
 }
 
@@ -1116,6 +1273,140 @@ __device__ __forceinline__ uint32_t fin_topp(const Src& src, uint32_t keep_lo, d
   return fin_digits12<true>(src, keep_lo, (uint32_t)b, above, p * s1, rmax, inv_tau, hc, hm, L);
 }
 
+// top-k over the source's tokens with key >= keep_lo, all three digits (keep_lo when there are
+// none).
+template <class Src>
+__device__ __forceinline__ uint32_t fin_select_k(const Src& src, uint32_t keep_lo, double k, float rmax, double inv_tau,
+                                                 uint32_t* hc, double* hm, FinishLds& L) {
+  fin_hist<false>(src, keep_lo, 32, 0u, kSelShift0, kSelB0, rmax, inv_tau, hc, hm, L);
+  double above = 0.0;
+  const int b = fin_resolve<false>(hc, hm, kSelB0, 0.0, k, &above, L);
+  if (b < 0) return keep_lo;
+  return fin_digits12<false>(src, keep_lo, (uint32_t)b, above, k, rmax, inv_tau, hc, hm, L);
+}
+
+// Block-wide max of one uint32 per thread (kT threads); lds: kT / kWave ints.
+template <int kT>
+__device__ inline uint32_t block_max_u32(uint32_t v, int* lds) {
+  return (uint32_t)block_max_i32<kT>((int)(v ^ 0x80000000u), lds) ^ 0x80000000u;
+}
+
+// Moves the keys of keys[0, n) that are at least lo to the front, in their order; returns
+// their number. Thread t takes the contiguous positions [t·per, t·per + per).
+__device__ __forceinline__ int compact_keys(uint32_t* keys, int n, uint32_t lo, FinishLds& L) {
+  constexpr int kMax = kCand / kFThreads;
+  const int per = (n + kFThreads - 1) / kFThreads;
+  const int i0 = (int)threadIdx.x * per;
+  uint32_t r[kMax];
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < kMax; ++q) {
+    const int i = i0 + q;
+    r[q] = (q < per && i < n) ? keys[i] : 0u;
+    mine += (q < per && i < n && r[q] >= lo) ? 1 : 0;
+  }
+  // the scan's barriers order every read above before the writes below
+  const double incl = block_inclusive_scan_f64<kFThreads>((double)mine, L.scan);
+  int o = (int)incl - mine;
+#pragma unroll
+  for (int q = 0; q < kMax; ++q)
+    if (q < per && i0 + q < n && r[q] >= lo) keys[o++] = r[q];
+  if (threadIdx.x == kFThreads - 1) L.i[0] = (int)incl;
+  __syncthreads();
+  const int m = L.i[0];
+  __syncthreads();
+  return m;
+}
+
+// A lower bound of the k-th largest of keys[0, n) (k <= kFThreads): the k-th largest of the
+// threads' maxima over contiguous runs of the keys (those k maxima are k distinct keys), to its
+// top 16 bits; 0 when fewer than k threads hold a key. tm: kFThreads words of LDS, 16-byte aligned.
+__device__ __forceinline__ uint32_t maxima_bound(const uint32_t* keys, int n, int k, uint32_t* tm, FinishLds& L) {
+  const int tid = threadIdx.x;
+  const int per = (n + kFThreads - 1) / kFThreads;
+  uint32_t m = 0u;
+  for (int i = tid * per; i < min(n, tid * per + per); ++i) m = max(m, keys[i]);
+  tm[tid] = m;
+  __syncthreads();
+  if (tid < kWave) {
+    const uint32_t b = wave_kth_bound<kFThreads / kWave>(tm, k);
+    if (tid == 0) L.i[0] = (int)b;
+  }
+  __syncthreads();
+  const uint32_t b = (uint32_t)L.i[0];
+  __syncthreads();
+  return b;
+}
+
+// sel_chunk's candidates of one row into keys[0, n): the keys of every chunk's written slots
+// from L* = max L_c up (L* is at most the row's k-th largest key, so every key the row's top-k
+// keeps is among them). Returns n, or -1 when a chunk had more candidates than its slots.
+// *rk: the row's largest allowed finite key (0: none); *bad: a NaN or +inf in the row. cnt_l:
+// LDS for the chunk counts (kMaxSelChunks words). The records and the slots load together.
+__device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, int chunks, int slot_log2,
+                                             uint32_t* keys, uint32_t* cnt_l, uint32_t* rk, bool* bad,
+                                             FinishLds& L) {
+  constexpr int kRecPer = kMaxSelChunks / kFThreads;
+  constexpr int kVecPer = kCand / 4 / kFThreads;
+  const int tid = threadIdx.x;
+  const u32x4* rec = reinterpret_cast<const u32x4*>(sb.cnt + rowg * kSelB0);
+  const u32x4* cs = reinterpret_cast<const u32x4*>(sb.cand + rowg * kCand);
+  const int slots = chunks << slot_log2;
+  u32x4 r[kRecPer], kv[kVecPer];
+#pragma unroll
+  for (int i = 0; i < kRecPer; ++i) {
+    const int c = tid + kFThreads * i;
+    r[i] = c < chunks ? rec[c] : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int u = 0; u < kVecPer; ++u) {
+    const int e4 = tid + kFThreads * u;
+    kv[u] = 4 * e4 < slots ? cs[e4] : u32x4{0u, 0u, 0u, 0u};
+  }
+  int flags = 0;
+  uint32_t lmax = 0u, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < kRecPer; ++i) {
+    const int c = tid + kFThreads * i;
+    if (c < chunks) {
+      cnt_l[c] = r[i][0] & kRecCount;
+      flags |= (int)(r[i][0] >> 30);
+      lmax = max(lmax, r[i][1]);
+      kmax = max(kmax, r[i][2]);
+    }
+  }
+  flags = block_or<kFThreads>(flags, L.i);  // its barriers publish cnt_l too
+  const uint32_t lstar = block_max_u32<kFThreads>(lmax, L.i);
+  *rk = block_max_u32<kFThreads>(kmax, L.i);
+  *bad = (flags & (int)(kRecBad >> 30)) != 0;
+  if (flags & (int)(kRecOver >> 30)) return -1;
+  const uint32_t smask = (1u << slot_log2) - 1u;
+  uint32_t take = 0u;  // bit 4u + i: kv[u][i]
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < kVecPer; ++u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * (tid + kFThreads * u) + i;
+      const bool ok = e < slots && ((uint32_t)e & smask) < cnt_l[e >> slot_log2] && kv[u][i] >= lstar;
+      take |= ok ? 1u << (4 * u + i) : 0u;
+      mine += ok ? 1 : 0;
+    }
+  }
+  const double incl = block_inclusive_scan_f64<kFThreads>((double)mine, L.scan);
+  int o = (int)incl - mine;
+#pragma unroll
+  for (int u = 0; u < kVecPer; ++u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (take & (1u << (4 * u + i))) keys[o++] = kv[u][i];
+  }
+  if (tid == kFThreads - 1) L.i[0] = (int)incl;
+  __syncthreads();
+  const int n = L.i[0];
+  __syncthreads();
+  return n;
+}
 
 // The stats kernel's outputs for a row whose kept set is the sorted candidates keys[0, n) from
 // thr up, none of the row's logits NaN or +inf: the row maximum and S = sum exp((z - max) / tau)
@@ -1152,7 +1443,8 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
                                                                int v, Transform tr, SelBufs sb,
                                                                SelArgs sa, SelStats ss) {
   __shared__ uint32_t keys[kCand];  // the candidates
-  __shared__ uint32_t hc[kSelB0];   // radix passes: counts
+  __shared__ __attribute__((aligned(16))) uint32_t hc[kSelB0];  // radix passes: counts (also the
+                                                                 // chunk counts, the thread maxima)
   __shared__ double hm[kSelB0];     // radix passes: masses
   __shared__ FinishLds L;
   __shared__ double tab[32];        // 2^(j/32) for write_row_stats (visible after the sort's barriers)
@@ -1162,69 +1454,90 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
   const int per_seq = 2 * kd + 1;
   const int64_t s = rowg / per_seq;
   const int j = (int)(rowg % per_seq);
-  bool stats_done = false;
-  SelState st = sb.state[rowg];
   const bool use_p = sa.top_p < 1.0;
   const double kf = (double)sa.top_k;
+  bool stats_done = false;
   uint32_t thr = 0u;
-  if (st.mode == kSelCompactK || st.mode == kSelCompactP) {
-    const uint32_t cn = sb.candn[rowg];
-    if (cn > (uint32_t)kCand) {
-      // more candidates than the list holds (top-p buckets are not counted ahead): radix passes
-      // over the row
-      if (st.mode == kSelCompactK) {
-        st.mode = kSelSlowK;
-        st.lo >>= kSelShift0;
+  SelState st{};
+  bool bad_row;
+  int n = 0;             // candidates in keys[0, n) (compact modes)
+  bool digit0 = false;   // kSelCompactK: the boundary's digit-0 bucket (st.lo) and carry are known
+  if (sa.slot_log2 > 0) {
+    uint32_t rk;
+    n = gather_chunks(sb, rowg, sa.chunks, sa.slot_log2, keys, hc, &rk, &bad_row, L);
+    st.rmax = rk ? key_logit(rk) : -INFINITY;
+    st.mode = rk == 0u ? kSelDone : (n < 0 ? kSelSlowKFull : kSelCompactK);
+  } else {
+    st = sb.state[rowg];
+    bad_row = sb.rbad[rowg] != 0u;
+    if (st.mode == kSelCompactK || st.mode == kSelCompactP) {
+      n = (int)sb.candn[rowg];
+      if (n > kCand) {
+        // more candidates than the list holds (top-p buckets are not counted ahead): radix
+        // passes over the row
+        if (st.mode == kSelCompactK) {
+          st.mode = kSelSlowK;
+          st.lo >>= kSelShift0;
+        } else {
+          st.mode = kSelSlowP;
+        }
       } else {
-        st.mode = kSelSlowP;
+        const uint32_t* src = sb.cand + rowg * kCand;
+        for (int i = tid; i < n; i += kFThreads) keys[i] = src[i];
+        __syncthreads();
+        digit0 = st.mode == kSelCompactK;
       }
     }
   }
-  if (st.mode == kSelCompactK || st.mode == kSelCompactP) {
-    const int n = (int)sb.candn[rowg];
-    const uint32_t* src = sb.cand + rowg * kCand;
-    for (int i = tid; i < n; i += kFThreads) keys[i] = src[i];
-    __syncthreads();
+  if (st.mode == kSelCompactK) {
+    // keys[0, n) hold every key the row's top-k keeps
+    uint32_t thr_k = 0u;
+    if (n > kSortMax && sa.top_k <= kFThreads) n = compact_keys(keys, n, maxima_bound(keys, n, sa.top_k, hc, L), L);
+    if (n > kSortMax) {
+      const KeySrc ks{keys, n};
+      thr_k = digit0 ? fin_digits12<false>(ks, 0u, st.lo >> kSelShift0, st.carry, kf, st.rmax, tr.inv_tau, hc, hm, L)
+                     : fin_select_k(ks, 0u, kf, st.rmax, tr.inv_tau, hc, hm, L);
+      n = compact_keys(keys, n, thr_k, L);  // now exactly the kept set
+      if (n > kSortMax) thr = use_p ? fin_topp(KeySrc{keys, n}, thr_k, sa.top_p, st.rmax, tr.inv_tau, hc, hm, L) : thr_k;
+    }
     if (n <= kSortMax) {
       sort_desc(keys, n);
-      if (st.mode == kSelCompactK) {
-        // the candidates are the row's n largest keys: top-k's threshold is the k-th
-        const int kk = min(sa.top_k, n);
-        const uint32_t thr_k = n > 0 ? keys[kk - 1] : 0u;
-        thr = thr_k;
-        if (use_p && n > 0) {
-          // top-p on the tokens top-k kept: the first m sorted keys
-          int last = -1;
-          for (int i = tid; i < n; i += kFThreads)
-            if (keys[i] >= thr_k && (i + 1 == n || keys[i + 1] < thr_k)) last = i;
-          const int m = block_max_i32<kFThreads>(last, L.i) + 1;
-          thr = topp_sorted(keys, m, 0.0, 0.0, true, st.rmax, tr.inv_tau, sa.top_p, L);
-        }
-        // the kept set is here, sorted: the row's statistics too (the stats kernel skips it)
-        if (ss.cmax && n > 0 && sb.rbad[rowg] == 0u) {
-          write_row_stats(keys, n, thr, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
-                          row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
-          stats_done = true;
-        }
-      } else if (n > 0) {
-        thr = topp_sorted(keys, n, st.carry, st.s1, false, st.rmax, tr.inv_tau, sa.top_p, L);
+      // the candidates hold the row's n largest keys that top-k can keep: its threshold is the k-th
+      const int kk = min(sa.top_k, n);
+      thr_k = n > 0 ? keys[kk - 1] : 0u;
+      thr = thr_k;
+      if (use_p && n > 0) {
+        // top-p on the tokens top-k kept: the first m sorted keys
+        int last = -1;
+        for (int i = tid; i < n; i += kFThreads)
+          if (keys[i] >= thr_k && (i + 1 == n || keys[i + 1] < thr_k)) last = i;
+        const int m = block_max_i32<kFThreads>(last, L.i) + 1;
+        thr = topp_sorted(keys, m, 0.0, 0.0, true, st.rmax, tr.inv_tau, sa.top_p, L);
       }
-    } else {
-      const KeySrc ks{keys, n};
-      if (st.mode == kSelCompactK) {
-        thr = fin_digits12<false>(ks, 0u, st.lo >> kSelShift0, st.carry, kf, st.rmax, tr.inv_tau, hc, hm, L);
-        if (use_p) thr = fin_topp(ks, thr, sa.top_p, st.rmax, tr.inv_tau, hc, hm, L);
-      } else {
-        thr = fin_digits12<true>(ks, 0u, st.lo, st.carry, sa.top_p * st.s1, st.rmax, tr.inv_tau, hc, hm, L);
+      // the kept set is here, sorted: the row's statistics too (the stats kernel skips it)
+      if (ss.cmax && n > 0 && !bad_row) {
+        write_row_stats(keys, n, thr, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
+                        row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
+        stats_done = true;
       }
     }
-  } else if (st.mode == kSelSlowK || st.mode == kSelSlowP || st.mode == kSelSlowPFull) {
+  } else if (st.mode == kSelCompactP) {
+    if (n <= kSortMax) {
+      sort_desc(keys, n);
+      if (n > 0) thr = topp_sorted(keys, n, st.carry, st.s1, false, st.rmax, tr.inv_tau, sa.top_p, L);
+    } else {
+      const KeySrc ks{keys, n};
+      thr = fin_digits12<true>(ks, 0u, st.lo, st.carry, sa.top_p * st.s1, st.rmax, tr.inv_tau, hc, hm, L);
+    }
+  } else if (st.mode != kSelDone) {
     const RowSrc<kVec4> rs{row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), v};
     if (st.mode == kSelSlowP) {
       thr = fin_digits12<true>(rs, 0u, st.lo, st.carry, sa.top_p * st.s1, st.rmax, tr.inv_tau, hc, hm, L);
     } else {
       if (st.mode == kSelSlowK)
         thr = fin_digits12<false>(rs, 0u, st.lo, st.carry, kf, st.rmax, tr.inv_tau, hc, hm, L);
+      else if (st.mode == kSelSlowKFull)
+        thr = fin_select_k(rs, 0u, kf, st.rmax, tr.inv_tau, hc, hm, L);
       if (use_p) thr = fin_topp(rs, thr, sa.top_p, st.rmax, tr.inv_tau, hc, hm, L);
     }
   } else {
@@ -1597,10 +1910,31 @@ namespace {
 // the stats kernel numbers them; at least one of top-k (sa.top_k > 0) and top-p
 // (sa.top_p < 1) is on.
 hipError_t launch_selection(const float* target, const float* draft, int32_t b, int32_t kd, int32_t v,
-                            const Transform& tr, const SelBufs& sb, const SelArgs& sa, const SelStats& ss,
+                            const Transform& tr, const SelBufs& sb, const SelArgs& sa_in, const SelStats& ss,
                             bool vec4, hipStream_t stream) {
   const int chunks = (v + kChunk - 1) / kChunk;
   const int64_t rows = (int64_t)b * (2 * kd + 1);
+  SelArgs sa = sa_in;
+  sa.chunks = chunks;
+  sa.slot_log2 = 0;
+  if (sa.top_k > 0 && chunks <= kMaxSelChunks) {
+    // top-k by per-chunk candidates when k is at most the threads of a chunk's workgroup and
+    // each chunk's share of the list (a power of two of at least 8 slots) holds twice k: the
+    // largest lg with chunks << lg <= kCand
+    int lg = 0;
+    while ((int64_t)chunks << (lg + 1) <= kCand) ++lg;
+    if (lg >= 3 && sa.top_k <= kThreads && 2 * (int64_t)sa.top_k <= (int64_t(1) << lg)) sa.slot_log2 = lg;
+  }
+  const dim3 g1((unsigned)rows, (unsigned)chunks);
+  if (sa.slot_log2 > 0) {
+    if (vec4) sel_chunk_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa);
+    else sel_chunk_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa);
+    if (vec4)
+      sel_finish_kernel<true><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa, ss);
+    else
+      sel_finish_kernel<false><<<dim3((unsigned)rows), dim3(kFThreads), 0, stream>>>(target, draft, kd, v, tr, sb, sa, ss);
+    return hipGetLastError();
+  }
   const bool mass = sa.top_k == 0;  // top-p alone: digit-0 masses in sel_count
   // chunks per counting workgroup: about eight resident workgroups per CU's worth of grid
   const int cpw = (int)std::max<int64_t>(1, std::min<int64_t>(8, rows * chunks / 2048));
@@ -1614,7 +1948,6 @@ hipError_t launch_selection(const float* target, const float* draft, int32_t b, 
     sel_count_kernel<false, true><<<gc, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, cpw, tr, sb, sa);
   else
     sel_count_kernel<false, false><<<gc, dim3(kThreads), 0, stream>>>(target, draft, kd, v, chunks, cpw, tr, sb, sa);
-  const dim3 g1((unsigned)rows, (unsigned)chunks);
   if (vec4) sel_collect_kernel<true><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb);
   else sel_collect_kernel<false><<<g1, dim3(kThreads), 0, stream>>>(target, draft, kd, v, tr, sb);
   if (vec4)
@@ -1684,7 +2017,7 @@ hipError_t launch_sampling_thresholds(const float* logits, int32_t rows, int32_t
   sb.cand = reinterpret_cast<uint32_t*>(base + L.cand);
   sb.rbad = reinterpret_cast<uint32_t*>(base + L.rbad);
   sb.thr = out_thr;
-  const SelArgs sa{use_k ? sp.top_k : 0, use_p ? (double)sp.top_p : 1.0};
+  const SelArgs sa{use_k ? sp.top_k : 0, use_p ? (double)sp.top_p : 1.0, 0, 0};
   // one "sequence" per row with no draft rows: row s is logits + s·v, mask row s
   return launch_selection(logits, nullptr, rows, 0, v, tr, sb, sa, SelStats{}, vec4, stream);
 }
@@ -1733,7 +2066,7 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
       sb.cand = reinterpret_cast<uint32_t*>(base + L.selcand);
       sb.thr = reinterpret_cast<uint32_t*>(base + L.thr);
       sb.rbad = reinterpret_cast<uint32_t*>(base + L.selrbad);
-      const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0};
+      const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0, 0, 0};
       const SelStats ss{ws.cmax, ws.csum, ws.cbad, ws.gz, reinterpret_cast<uint32_t*>(base + L.sdone), tokens,
                         chunks};
       if ((e = launch_selection(target, draft, b, kd, v, tr, sb, sa, ss, vec4, stream)) != hipSuccess) return e;
