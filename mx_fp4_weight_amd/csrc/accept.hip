@@ -525,9 +525,12 @@ __device__ void draw_final(const FinalRows& fr, int n, int kd, int v, int pieces
 // 10-bit digits. Top-k with k at most 256 and at least 2k list slots per chunk (every
 // common vocabulary) takes two kernels:
 //   sel_chunk     grid (rows, chunks), one read of the logits: each chunk's keys from a lower
-//                 bound of its own k-th largest up go to the chunk's own slots of the row's
-//                 list (see sel_chunk below), with a record of their count and bound.
-//   sel_finish    as below, on the union of the chunks' candidates from the largest bound up.
+//                 bound of its own k-th largest up go to the chunk's own (interleaved) slots of
+//                 the row's list (see sel_chunk below), with a record of their count and bound.
+//   sel_finish    the union of the chunks' candidates from the largest bound up, cut by the
+//                 k-th largest of its threads' maxima; at most 64 left (the usual case) are
+//                 finished by one wave without a barrier (sort, thresholds, row statistics),
+//                 more as below.
 // Top-p alone and larger k take four:
 //   sel_clear     zeroes each row's digit-0 histogram, counters and maximum.
 //   sel_count     grid (rows, groups of 4096-logit chunks), one read of the logits: the row
@@ -559,7 +562,8 @@ constexpr int kSelBits0 = 12;
 constexpr int kSelB0 = 1 << kSelBits0;      // digit-0 buckets
 constexpr int kSelShift0 = 32 - kSelBits0;  // digit 0 = key >> 20
 constexpr int kSelBits1 = 10;               // digits 1 and 2
-constexpr int kCand = 8192;                 // candidate keys per row
+constexpr int kCandLog2 = 13;
+constexpr int kCand = 1 << kCandLog2;       // candidate keys per row
 constexpr int kFThreads = 512;              // sel_finish
 constexpr int kFWaves = kFThreads / kWave;
 constexpr int kSortMax = 512;  // candidate lists up to this size are sorted (fixed-order sums)
@@ -621,7 +625,8 @@ struct SelArgs {
   int top_k;      // 0: off
   double top_p;   // >= 1: off
   int chunks;     // 4096-logit chunks per row
-  int slot_log2;  // > 0: top-k by per-chunk candidates, 2^slot_log2 slots per chunk (sel_chunk)
+  int slot_log2;  // > 0: top-k by per-chunk candidates (sel_chunk), 2^slot_log2 per chunk: candidate
+                  // i of chunk c at list position i·2^(kCandLog2 - slot_log2) + c
 };
 
 // The logit of an order key (inverse of order_key; -0 comes back as +0).
@@ -1064,11 +1069,14 @@ __global__ __launch_bounds__(kThreads) void sel_chunk_kernel(const float* __rest
   const uint32_t n = (uint32_t)s_n;
   const bool over = n > (1u << sa.slot_log2);
   if (!over) {
-    uint32_t* out = sb.cand + rowg * kCand + ((size_t)c << sa.slot_log2);
+    // interleaved with the other chunks' candidates, so that a contiguous run of the list holds
+    // candidates of many chunks
+    uint32_t* out = sb.cand + rowg * kCand + c;
+    const int c2 = kCandLog2 - sa.slot_log2;
     uint32_t slot = (uint32_t)incl - (uint32_t)mine;
 #pragma unroll
     for (int q = 0; q < kPer; ++q)
-      if (key[q] && key[q] >= lc) out[slot++] = key[q];
+      if (key[q] && key[q] >= lc) out[(size_t)(slot++) << c2] = key[q];
   }
   if (tid == 0) {
     const u32x4 rec{(over ? kRecOver : n) | (s_bad ? kRecBad : 0u), lc, s_rk, 0u};
@@ -1338,20 +1346,24 @@ __device__ __forceinline__ uint32_t maxima_bound(const uint32_t* keys, int n, in
   return b;
 }
 
-// sel_chunk's candidates of one row into keys[0, n): the keys of every chunk's written slots
-// from L* = max L_c up (L* is at most the row's k-th largest key, so every key the row's top-k
-// keeps is among them). Returns n, or -1 when a chunk had more candidates than its slots.
-// *rk: the row's largest allowed finite key (0: none); *bad: a NaN or +inf in the row. cnt_l:
-// LDS for the chunk counts (kMaxSelChunks words). The records and the slots load together.
-__device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, int chunks, int slot_log2,
-                                             uint32_t* keys, uint32_t* cnt_l, uint32_t* rk, bool* bad,
-                                             FinishLds& L) {
+// sel_chunk's candidates of one row, cut to the keys from a lower bound of the row's k-th
+// largest up, into keys[0, n) (in no particular order). The bound is the larger of L* = max L_c
+// (every L_c is at most the row's k-th largest key) and the k-th largest of the threads' maxima
+// over the candidates from L* up, to its top 16 bits (those k maxima are k distinct candidates,
+// and the candidates hold every key the row's top-k keeps). Returns n, or -1 when a chunk had
+// more candidates than its slots. *rk: the row's largest allowed finite key (0: none); *bad: a
+// NaN or +inf in the row. LDS: cnt_l (kMaxSelChunks words), tm (kFThreads words, 16-byte
+// aligned), red (4·kFWaves + 1 words). The records and the slots load together.
+__device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, int chunks, int slot_log2, int k,
+                                             uint32_t* keys, uint32_t* cnt_l, uint32_t* tm, uint32_t* red,
+                                             uint32_t* rk, bool* bad) {
   constexpr int kRecPer = kMaxSelChunks / kFThreads;
   constexpr int kVecPer = kCand / 4 / kFThreads;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const u32x4* rec = reinterpret_cast<const u32x4*>(sb.cnt + rowg * kSelB0);
   const u32x4* cs = reinterpret_cast<const u32x4*>(sb.cand + rowg * kCand);
-  const int slots = chunks << slot_log2;
+  const int c2 = kCandLog2 - slot_log2;  // list position i·2^c2 + c: candidate i of chunk c
   u32x4 r[kRecPer], kv[kVecPer];
 #pragma unroll
   for (int i = 0; i < kRecPer; ++i) {
@@ -1360,8 +1372,7 @@ __device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, in
   }
 #pragma unroll
   for (int u = 0; u < kVecPer; ++u) {
-    const int e4 = tid + kFThreads * u;
-    kv[u] = 4 * e4 < slots ? cs[e4] : u32x4{0u, 0u, 0u, 0u};
+    kv[u] = cs[tid + kFThreads * u];
   }
   int flags = 0;
   uint32_t lmax = 0u, kmax = 0u;
@@ -1375,37 +1386,143 @@ __device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, in
       kmax = max(kmax, r[i][2]);
     }
   }
-  flags = block_or<kFThreads>(flags, L.i);  // its barriers publish cnt_l too
-  const uint32_t lstar = block_max_u32<kFThreads>(lmax, L.i);
-  *rk = block_max_u32<kFThreads>(kmax, L.i);
-  *bad = (flags & (int)(kRecBad >> 30)) != 0;
-  if (flags & (int)(kRecOver >> 30)) return -1;
-  const uint32_t smask = (1u << slot_log2) - 1u;
+  flags = wave_or(flags);
+  lmax = wave_max_u32(lmax);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    red[wave] = (uint32_t)flags;
+    red[kFWaves + wave] = lmax;
+    red[2 * kFWaves + wave] = kmax;
+  }
+  __syncthreads();  // the chunk counts and the waves' partials
+  uint32_t f = 0u, lstar = 0u, kx = 0u;
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) {
+    f |= red[w];
+    lstar = max(lstar, red[kFWaves + w]);
+    kx = max(kx, red[2 * kFWaves + w]);
+  }
+  *rk = kx;
+  *bad = (f & (kRecBad >> 30)) != 0u;
+  if (f & (kRecOver >> 30)) return -1;
+  // this thread's candidates from L* up and their maximum
+  const int cmask = (1 << c2) - 1;
   uint32_t take = 0u;  // bit 4u + i: kv[u][i]
-  int mine = 0;
+  uint32_t m = 0u;
 #pragma unroll
   for (int u = 0; u < kVecPer; ++u) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * (tid + kFThreads * u) + i;
-      const bool ok = e < slots && ((uint32_t)e & smask) < cnt_l[e >> slot_log2] && kv[u][i] >= lstar;
+      const int c = e & cmask;
+      const bool ok = c < chunks && (uint32_t)(e >> c2) < cnt_l[c] && kv[u][i] >= lstar;
       take |= ok ? 1u << (4 * u + i) : 0u;
-      mine += ok ? 1 : 0;
+      m = ok ? max(m, kv[u][i]) : m;
     }
   }
-  const double incl = block_inclusive_scan_f64<kFThreads>((double)mine, L.scan);
-  int o = (int)incl - mine;
+  tm[tid] = m;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t b = wave_kth_bound<kFThreads / kWave>(tm, k);
+    if (lane == 0) red[3 * kFWaves] = b;
+  }
+  __syncthreads();
+  const uint32_t lo = max(lstar, red[3 * kFWaves]);
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < kVecPer; ++u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t bit = 1u << (4 * u + i);
+      if ((take & bit) && kv[u][i] < lo) take &= ~bit;
+      mine += (take & bit) ? 1 : 0;
+    }
+  }
+  // positions: a scan inside each wave, then the wave totals (one barrier)
+  const int incl = (int)wave_inclusive_scan_f64((double)mine);
+  if (lane == kWave - 1) red[3 * kFWaves + 1 + wave] = (uint32_t)incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) {
+    const int t = (int)red[3 * kFWaves + 1 + w];
+    base += w < wave ? t : 0;
+    total += t;
+  }
+  int o = base + incl - mine;
 #pragma unroll
   for (int u = 0; u < kVecPer; ++u) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (take & (1u << (4 * u + i))) keys[o++] = kv[u][i];
   }
-  if (tid == kFThreads - 1) L.i[0] = (int)incl;
   __syncthreads();
-  const int n = L.i[0];
-  __syncthreads();
-  return n;
+  return total;
+}
+
+__device__ inline double shfl_f64(double v, int src) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)b, src);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(b >> 32), src);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// The thresholds from n <= kWave candidates keys[0, n) (LDS; every key top-k keeps is among
+// them) on the calling wave alone, with no barrier: a bitonic sort, one key per lane, descending;
+// top-k's threshold is the k-th key (the last when n <= k); top-p (p < 1) then takes the lowest
+// key whose strictly-larger mass is below P·S among the keys top-k kept (masses
+// exp((z - rmax) / tau), S their sum, both summed in the sorted order by a wave scan). With
+// with_stats, the row's statistics as write_row_stats writes them. Returns the threshold (every lane).
+__device__ __forceinline__ uint32_t wave_tail(const uint32_t* keys, int n, int k, double p, float rmax, double inv_tau,
+                                              const double* tab, const SelStats& ss, bool with_stats, int64_t rowg,
+                                              int64_t s, int j,
+                                              int kd, int v, const float* __restrict__ z, const uint32_t* mw) {
+  if (n <= 0) return 0u;
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t x = lane < n ? keys[lane] : 0u;  // 0 is below every live key: the padding sorts last
+#pragma unroll
+  for (int kk = 2; kk <= kWave; kk <<= 1) {
+#pragma unroll
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      const uint32_t y = (uint32_t)__shfl_xor((int)x, jj);
+      const bool lower = (lane & jj) == 0;  // this lane holds the pair's lower position
+      const bool desc = (lane & kk) == 0;   // this block of kk ends descending
+      x = lower == desc ? max(x, y) : min(x, y);
+    }
+  }
+  const uint32_t thr_k = (uint32_t)__shfl((int)x, min(k, n) - 1);
+  uint32_t thr = thr_k;
+  const bool kept_k = lane < n && x >= thr_k;
+  const double e = kept_k ? exp_neg_f64_tab(((double)key_logit(x) - (double)rmax) * inv_tau, tab) : 0.0;
+  if (p < 1.0) {
+    const double incl = wave_inclusive_scan_f64(e);
+    const double tgt = p * readlane_f64(incl, kWave - 1);
+    const double run = shfl_f64(incl, lane > 0 ? lane - 1 : 0);
+    const uint32_t xp = (uint32_t)__shfl((int)x, lane > 0 ? lane - 1 : 0);
+    const bool start = kept_k && (lane == 0 || xp != x);
+    const uint64_t q = __ballot(start && (lane == 0 ? 0.0 : run) < tgt);
+    thr = (uint32_t)__shfl((int)x, q ? 63 - __clzll(q) : 0);
+  }
+  if (with_stats) {
+    const double sum = readlane_f64(wave_sum_f64(lane < n && x >= thr ? e : 0.0), 0);
+    for (int c = lane; c < ss.chunks; c += kWave) {
+      const size_t o = (size_t)rowg * ss.chunks + c;
+      ss.cmax[o] = c == 0 ? rmax : -INFINITY;
+      ss.csum[o] = c == 0 ? sum : 0.0;
+      ss.cbad[o] = 0;
+    }
+    if (lane == 0) {
+      int xi = -1;
+      if (j < kd) xi = ss.tokens[(size_t)s * kd + j];
+      else if (j > kd) xi = ss.tokens[(size_t)s * kd + (j - kd - 1)];
+      if (xi >= 0 && xi < v) {
+        const float zx = z[xi];
+        const bool allowed = mw ? ((mw[xi >> 5] >> (xi & 31)) & 1u) != 0u : true;
+        ss.gz[rowg] = (allowed && order_key(zx) >= thr) ? zx : -INFINITY;
+      }
+    }
+  }
+  return thr;
 }
 
 // The stats kernel's outputs for a row whose kept set is the sorted candidates keys[0, n) from
@@ -1448,6 +1565,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
   __shared__ double hm[kSelB0];     // radix passes: masses
   __shared__ FinishLds L;
   __shared__ double tab[32];        // 2^(j/32) for write_row_stats (visible after the sort's barriers)
+  __shared__ uint32_t red[4 * kFWaves + 1];
   const int64_t rowg = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid < 32) tab[tid] = kExp2Table32[tid];
@@ -1464,7 +1582,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
   bool digit0 = false;   // kSelCompactK: the boundary's digit-0 bucket (st.lo) and carry are known
   if (sa.slot_log2 > 0) {
     uint32_t rk;
-    n = gather_chunks(sb, rowg, sa.chunks, sa.slot_log2, keys, hc, &rk, &bad_row, L);
+    n = gather_chunks(sb, rowg, sa.chunks, sa.slot_log2, sa.top_k, keys, hc, hc + kMaxSelChunks, red, &rk, &bad_row);
     st.rmax = rk ? key_logit(rk) : -INFINITY;
     st.mode = rk == 0u ? kSelDone : (n < 0 ? kSelSlowKFull : kSelCompactK);
   } else {
@@ -1490,7 +1608,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
     }
   }
   if (st.mode == kSelCompactK) {
-    // keys[0, n) hold every key the row's top-k keeps
+    // keys[0, n) hold every key the row's top-k keeps; cut them towards the kept set
     uint32_t thr_k = 0u;
     if (n > kSortMax && sa.top_k <= kFThreads) n = compact_keys(keys, n, maxima_bound(keys, n, sa.top_k, hc, L), L);
     if (n > kSortMax) {
@@ -1498,15 +1616,25 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
       thr_k = digit0 ? fin_digits12<false>(ks, 0u, st.lo >> kSelShift0, st.carry, kf, st.rmax, tr.inv_tau, hc, hm, L)
                      : fin_select_k(ks, 0u, kf, st.rmax, tr.inv_tau, hc, hm, L);
       n = compact_keys(keys, n, thr_k, L);  // now exactly the kept set
-      if (n > kSortMax) thr = use_p ? fin_topp(KeySrc{keys, n}, thr_k, sa.top_p, st.rmax, tr.inv_tau, hc, hm, L) : thr_k;
+      if (n > kSortMax) {
+        thr = use_p ? fin_topp(KeySrc{keys, n}, thr_k, sa.top_p, st.rmax, tr.inv_tau, hc, hm, L) : thr_k;
+        n = -1;  // done, without the row's statistics
+      }
     }
-    if (n <= kSortMax) {
+    const bool with_stats = ss.cmax && n > 0 && !bad_row;
+    if (n >= 0 && n <= kWave) {
+      // the usual case: one wave, no barrier
+      if (tid < kWave)
+        thr = wave_tail(keys, n, sa.top_k, use_p ? sa.top_p : 1.0, st.rmax, tr.inv_tau, tab,
+                        ss, with_stats, rowg, s, j, kd, v, row_ptr(target, draft, s, kd, j, v),
+                        mask_words(tr, s, kd, mask_row(j, kd)));
+      stats_done = with_stats;
+    } else if (n > kWave) {
       sort_desc(keys, n);
       // the candidates hold the row's n largest keys that top-k can keep: its threshold is the k-th
-      const int kk = min(sa.top_k, n);
-      thr_k = n > 0 ? keys[kk - 1] : 0u;
+      thr_k = keys[min(sa.top_k, n) - 1];
       thr = thr_k;
-      if (use_p && n > 0) {
+      if (use_p) {
         // top-p on the tokens top-k kept: the first m sorted keys
         int last = -1;
         for (int i = tid; i < n; i += kFThreads)
@@ -1515,7 +1643,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
         thr = topp_sorted(keys, m, 0.0, 0.0, true, st.rmax, tr.inv_tau, sa.top_p, L);
       }
       // the kept set is here, sorted: the row's statistics too (the stats kernel skips it)
-      if (ss.cmax && n > 0 && !bad_row) {
+      if (with_stats) {
         write_row_stats(keys, n, thr, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
                         row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
         stats_done = true;
@@ -1919,10 +2047,11 @@ hipError_t launch_selection(const float* target, const float* draft, int32_t b, 
   sa.slot_log2 = 0;
   if (sa.top_k > 0 && chunks <= kMaxSelChunks) {
     // top-k by per-chunk candidates when k is at most the threads of a chunk's workgroup and
-    // each chunk's share of the list (a power of two of at least 8 slots) holds twice k: the
-    // largest lg with chunks << lg <= kCand
-    int lg = 0;
-    while ((int64_t)chunks << (lg + 1) <= kCand) ++lg;
+    // each chunk's share of the list holds twice k: the list splits into 2^c2 >= chunks
+    // interleaved shares of 2^(kCandLog2 - c2) slots
+    int c2 = 0;
+    while ((1 << c2) < chunks) ++c2;
+    const int lg = kCandLog2 - c2;
     if (lg >= 3 && sa.top_k <= kThreads && 2 * (int64_t)sa.top_k <= (int64_t(1) << lg)) sa.slot_log2 = lg;
   }
   const dim3 g1((unsigned)rows, (unsigned)chunks);
