@@ -1525,17 +1525,14 @@ __device__ __forceinline__ uint32_t wave_tail(const uint32_t* keys, int n, int k
   return thr;
 }
 
-// The stats kernel's outputs for a row whose kept set is the sorted candidates keys[0, n) from
-// thr up, none of the row's logits NaN or +inf: the row maximum and S = sum exp((z - max) / tau)
-// (one candidate per thread, a fixed-order block sum) in chunk 0 and empty other chunks, which
-// the decide kernel combines to the same (max, S); the live logit of the row's draft token.
-__device__ __forceinline__ void write_row_stats(const uint32_t* keys, int n, uint32_t thr, float rmax, double inv_tau,
-                                const double* tab, const SelStats& ss, int64_t rowg, int64_t s, int j, int kd,
-                                int v, const float* __restrict__ z, const uint32_t* mw, FinishLds& L) {
+// The stats kernel's outputs for a row whose kept set is known here, none of the row's logits
+// NaN or +inf: the row maximum and S = sum exp((z - max) / tau) over the kept set in chunk 0 and
+// empty other chunks, which the decide kernel combines to the same (max, S); the live logit of
+// the row's draft token (threshold thr). Every thread calls it with the same sum.
+__device__ __forceinline__ void put_row_stats(double sum, uint32_t thr, float rmax, const SelStats& ss, int64_t rowg,
+                                              int64_t s, int j, int kd, int v, const float* __restrict__ z,
+                                              const uint32_t* mw) {
   const int tid = threadIdx.x;
-  const bool kept = tid < n && keys[tid] >= thr;
-  const double e = kept ? exp_neg_f64_tab(((double)key_logit(keys[tid]) - (double)rmax) * inv_tau, tab) : 0.0;
-  const double sum = block_sum_f64<kFThreads>(e, L.scan);
   for (int c = tid; c < ss.chunks; c += kFThreads) {
     const size_t o = (size_t)rowg * ss.chunks + c;
     ss.cmax[o] = c == 0 ? rmax : -INFINITY;
@@ -1552,6 +1549,20 @@ __device__ __forceinline__ void write_row_stats(const uint32_t* keys, int n, uin
       ss.gz[rowg] = (allowed && order_key(zx) >= thr) ? zx : -INFINITY;
     }
   }
+}
+
+// put_row_stats for a kept set of carry (the mass of the kept tokens outside the list) plus the
+// keys of keys[0, n) from thr up, summed by a fixed-order block sum over the list's order (one
+// key per thread for n <= kFThreads, so a sorted list gives a sum in the sorted order).
+__device__ __forceinline__ void write_row_stats(const uint32_t* keys, int n, uint32_t thr, double carry, float rmax,
+                                                double inv_tau, const double* tab, const SelStats& ss,
+                                                int64_t rowg, int64_t s, int j, int kd, int v,
+                                                const float* __restrict__ z, const uint32_t* mw, FinishLds& L) {
+  double e = 0.0;
+  for (int i = threadIdx.x; i < n; i += kFThreads)
+    if (keys[i] >= thr) e += exp_neg_f64_tab(((double)key_logit(keys[i]) - (double)rmax) * inv_tau, tab);
+  const double sum = carry + block_sum_f64<kFThreads>(e, L.scan);
+  put_row_stats(sum, thr, rmax, ss, rowg, s, j, kd, v, z, mw);
 }
 
 template <bool kVec4>
@@ -1644,7 +1655,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
       }
       // the kept set is here, sorted: the row's statistics too (the stats kernel skips it)
       if (with_stats) {
-        write_row_stats(keys, n, thr, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
+        write_row_stats(keys, n, thr, 0.0, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
                         row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
         stats_done = true;
       }
@@ -1656,6 +1667,13 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
     } else {
       const KeySrc ks{keys, n};
       thr = fin_digits12<true>(ks, 0u, st.lo, st.carry, sa.top_p * st.s1, st.rmax, tr.inv_tau, hc, hm, L);
+    }
+    // the kept set: every token above the boundary bucket (mass st.carry) and the bucket's keys
+    // from thr up, so the row's statistics are known here too (the stats kernel skips the row)
+    if (ss.cmax && n > 0 && !bad_row) {
+      write_row_stats(keys, n, thr, st.carry, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
+                      row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
+      stats_done = true;
     }
   } else if (st.mode != kSelDone) {
     const RowSrc<kVec4> rs{row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), v};
