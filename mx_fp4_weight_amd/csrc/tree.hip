@@ -15,9 +15,10 @@
 //          and draft row of every node (one full read of the logits).
 //   rowstat one workgroup per row: the chunk statistics combined into the row's (max, sum).
 //   pass r (r = 0 .. largest child count): grid (pieces, nodes, sequences): for every node
-//          with at least r children, the 1024-token piece totals of w_{r+1} (w_1 = p for
-//          r = 0), with Z_2 .. Z_r summed from the earlier passes' piece totals in a fixed
-//          order. Every node gets them, visited or not: the walk below needs them at once.
+//          with at least r children (r >= 1), the 1024-token piece totals of w_{r+1}, with
+//          Z_2 .. Z_r summed from the earlier passes' piece totals in a fixed order; for r = 0
+//          the totals of w_1 = p of every leaf (the target row alone). Every node gets them,
+//          visited or not: the walk below needs them at once.
 //   walk   one workgroup per sequence: walks the tree with scalar decisions (the row statistics
 //          are the stored ones and the Z values are summed in the passes' fixed order), then
 //          draws the final token: a scan of the final law's piece totals picks the piece, its
@@ -187,7 +188,8 @@ __device__ inline void law_weights(const NodeLaw& nl, int r, int t0, int v, bool
   float zt[kWPerT], zd[kWPerT];
   if (vec4 && t0 + kWPerT <= v) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(nl.zt + t0);
-    const f32x4 c = *reinterpret_cast<const f32x4*>(nl.zd + t0);
+    f32x4 c = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (r > 0) c = *reinterpret_cast<const f32x4*>(nl.zd + t0);  // p alone needs no draft row
 #pragma unroll
     for (int j = 0; j < kWPerT; ++j) {
       zt[j] = a[j];
@@ -198,7 +200,7 @@ __device__ inline void law_weights(const NodeLaw& nl, int r, int t0, int v, bool
     for (int j = 0; j < kWPerT; ++j) {
       const bool in = t0 + j < v;
       zt[j] = in ? nl.zt[t0 + j] : -INFINITY;
-      zd[j] = in ? nl.zd[t0 + j] : -INFINITY;
+      zd[j] = (in && r > 0) ? nl.zd[t0 + j] : -INFINITY;
     }
   }
 #pragma unroll
@@ -228,7 +230,10 @@ __global__ __launch_bounds__(kTh) void tree_pass_kernel(const float* __restrict_
   const int n = topo.n;
   const int rho = blockIdx.y;
   const int64_t s = blockIdx.z;
-  if (r > topo.off[rho + 1] - topo.off[rho]) return;  // uniform: fewer children than tries
+  const int kids = topo.off[rho + 1] - topo.off[rho];
+  // uniform: fewer children than tries; and the totals of p (r = 0) only for leaves (an inner
+  // node draws from p only after a zero residual, a rounding case the walk covers itself)
+  if (r > kids || (r == 0 && kids > 0)) return;
   const RowStat st = load_stat(ws, s, n, rho);
   const RowStat sd = load_stat(ws, s, n, n + 1 + rho);
   double* out = ws.ptot + (((size_t)r * b + s) * (n + 1) + rho) * pieces;
@@ -395,7 +400,22 @@ __global__ __launch_bounds__(kTh) void tree_walk_kernel(const float* __restrict_
 
   // final token from L_f = w_f / Z_f of row rho by inverse CDF: the piece, then the thread,
   // then the token
-  const double* pt = ws.ptot + (((size_t)(f - 1) * b + s) * (n + 1) + rho) * pieces;
+  double* ptw = ws.ptot + (((size_t)(f - 1) * b + s) * (n + 1) + rho) * pieces;
+  if (f == 1 && topo.off[rho + 1] > topo.off[rho]) {
+    // an inner node drawing from p (after a zero residual): the pass left its totals of p out,
+    // so this workgroup computes them, piece by piece, exactly as the pass computes them
+    for (int pc = 0; pc < pieces; ++pc) {
+      double w[kWPerT];
+      law_weights(nl, 0, pc * kTPiece + (int)threadIdx.x * kWPerT, v, kVec4, tab, w);
+      double t = 0.0;
+#pragma unroll
+      for (int j = 0; j < kWPerT; ++j) t += w[j];
+      t = block_inclusive_scan_f64<kTh>(t, lds_d);
+      if (threadIdx.x == kTh - 1) ptw[pc] = t;
+    }
+    __syncthreads();
+  }
+  const double* pt = ptw;
   const float u = uniforms[(size_t)s * (n + 1) + n];
   double zsum = 0.0;
   for (int c0 = 0; c0 < pieces; c0 += kTh) {

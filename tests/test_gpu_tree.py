@@ -89,3 +89,21 @@ def test_edge_cases_and_shared_dirty_workspace():
         ref = compare(parent, tgt, dft, tok, u, f"edges call {rep}", workspace=ws)
     assert ref["flags"][0] & otree.FLAG_Q_ZERO and ref["flags"][1] & otree.FLAG_TOKEN_RANGE
     assert ref["flags"][2] == otree.FLAG_NONFINITE
+
+
+@pytest.mark.parametrize("name", ["3x2", "binary3", "chain4"])
+def test_zero_residual_at_an_inner_node(name):
+    """Identical target and draft rows at the root, its first child's token at -inf in both: the
+    child is refused (q(x) = 0), the residual (p - q)+ has no mass, and the final token is drawn
+    from p at the root, an inner node (R8's rule at a tree node)."""
+    parent = TREES[name]
+    say(f"tree: zero residual at the root, {name}")
+    for v, b in [(1024, 16), (128256, 4)]:
+        tgt, dft, tok, u = synth.tree_batch(13, b, parent, v, 3.0, 1.0, seq0=7 * len(parent))
+        dft[:, 0] = tgt[:, 0]
+        for s in range(b):
+            x = tok[s, 0]
+            tgt[s, 0, x] = dft[s, 0, x] = -np.inf
+        ref = compare(parent, tgt, dft, tok, u, f"{name} v={v}")
+        assert np.all(ref["n"] == 0)
+        assert np.all(ref["flags"] & otree.FLAG_RESIDUAL_ZERO) and np.all(ref["flags"] & otree.FLAG_Q_ZERO)
