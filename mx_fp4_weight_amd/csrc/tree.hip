@@ -55,10 +55,13 @@ __device__ inline const float* tree_row(const float* base, int64_t s, int n, int
 }
 
 // ------------------------------------------------------------------ statistics
+// A leaf's draft row (the law its children would be tested against: it has none) is read for
+// the malformed-row check alone: its chunks get the maximum and the flag, and a zero sum.
 template <bool kVec4>
 __global__ __launch_bounds__(kTh) void tree_stats_kernel(const float* __restrict__ target,
-                                                        const float* __restrict__ draft, int n, int v,
+                                                        const float* __restrict__ draft, TreeTopo topo, int v,
                                                         int chunks, TreeWs ws) {
+  const int n = topo.n;
   __shared__ double lds_d[kWavesT];
   __shared__ float lds_f[kWavesT];
   __shared__ int lds_i[kWavesT];
@@ -95,8 +98,9 @@ __global__ __launch_bounds__(kTh) void tree_stats_kernel(const float* __restrict
     mx = fmaxf(mx, vals[q]);
   }
   block_max_or<kTh>(mx, bad, lds_f, lds_i);
+  const bool leaf_draft = j > n && topo.off[j - n] == topo.off[j - n - 1];  // row j - n - 1 has no children
   double acc = 0.0;
-  if (mx != -INFINITY && !bad) {
+  if (mx != -INFINITY && !bad && !leaf_draft) {
     const double m64 = (double)mx;
 #pragma unroll
     for (int q = 0; q < kSPer; ++q) acc += exp_neg_f64_tab((double)vals[q] - m64, tab);
@@ -514,11 +518,11 @@ hipError_t launch_spec_accept_tree(const float* target, const float* draft, cons
   off = al256(off + sizeof(double) * 2 * rows);
   ws.rbad = reinterpret_cast<int32_t*>(base + off);
   if (vec4)
-    tree_stats_kernel<true><<<dim3((unsigned)rows, (unsigned)chunks), dim3(kTh), 0, stream>>>(target, draft, n, v,
+    tree_stats_kernel<true><<<dim3((unsigned)rows, (unsigned)chunks), dim3(kTh), 0, stream>>>(target, draft, topo, v,
                                                                                              chunks, ws);
   else
-    tree_stats_kernel<false><<<dim3((unsigned)rows, (unsigned)chunks), dim3(kTh), 0, stream>>>(target, draft, n, v,
-                                                                                              chunks, ws);
+    tree_stats_kernel<false><<<dim3((unsigned)rows, (unsigned)chunks), dim3(kTh), 0, stream>>>(target, draft, topo,
+                                                                                              v, chunks, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   tree_rowstat_kernel<<<dim3((unsigned)rows), dim3(kTh), 0, stream>>>(n, chunks, ws);
