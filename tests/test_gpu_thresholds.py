@@ -183,3 +183,26 @@ def test_random_settings():
         keep = None if r.random() < 0.5 else float(r.choice([0.05, 0.5, 0.95]))
         allowed = None if keep is None else r.random((rows, v)) < keep
         compare(z, tau, k, p, allowed, f"case {case}: v={v} rows={rows} tau={tau:.3f} k={k} p={p:.3f} keep={keep}")
+
+
+def test_top_k_chunk_route_branches():
+    """The per-chunk top-k route (k <= 128 at V = 128256) down each of its branches:
+    integer logits (every chunk holds ~590 keys tied at the top, more than its 256 list slots:
+    radix passes over the row); continuous logits with ~200 copies of the row maximum per chunk
+    (the chunks fit, but ~6400 candidates survive every cut: radix passes over the list);
+    k = 100 and 128 (the cut set holds more than 64 keys: the block sort instead of one wave)."""
+    rows, v = 6, 128256
+    ints = synth.rng(37, 0).integers(-3, 4, size=(rows, v)).astype(np.float32)
+    for k, p in [(10, 1.0), (50, 0.9), (128, 1.0)]:
+        say(f"thresholds: integer logits V={v} k={k} p={p}")
+        compare(ints, 1.0, k, p, None, f"ints k={k} p={p}")
+    dup = normal_rows(38, rows, v)
+    top = synth.rng(38, 1).random((rows, v)) < 200.0 / 4096
+    dup[top] = 20.0
+    for k, p in [(50, 1.0), (50, 0.9)]:
+        say(f"thresholds: tied maximum V={v} k={k} p={p}")
+        compare(dup, 1.0, k, p, None, f"tied max k={k} p={p}")
+    z = normal_rows(39, rows, v)
+    for k, p in [(100, 1.0), (100, 0.8), (128, 0.95)]:
+        say(f"thresholds: V={v} k={k} p={p}")
+        compare(z, 0.9, k, p, None, f"k={k} p={p}")
