@@ -84,7 +84,8 @@ def test_small_vocab_many_sequences(tau, k, p, keep):
 
 
 @pytest.mark.parametrize("tau,k,p,keep", [(0.8, 50, 0.9, None), (1.0, 0, 0.95, None),
-                                          (1.2, 1000, 1.0, 0.6), (1.0, 0, 0.6, 0.3)])
+                                          (1.2, 1000, 1.0, 0.6), (1.0, 0, 0.6, 0.3),
+                                          (0.9, 100, 0.8, None), (1.0, 128, 1.0, 0.9)])
 def test_8b_vocab(tau, k, p, keep):
     say(f"sampled: V=128256 K=4 tau={tau} k={k} p={p} keep={keep}")
     tgt, dft, tok, u, mask = inputs(22, 3, 4, 128256, 3.0, 1.0, tau, k, p, keep, seq0=k)
