@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
   // every wave issues the same loads without a branch, so wait counts stay exact.
   __shared__ u32x4 xbuf0[kBufU];
   __shared__ u32x4 xbuf1[kBufU];
+  __shared__ u32x4 xbuf2[kBufU];
   // workgroup b runs on XCD b % 8; consecutive workgroups of one XCD share a weight tile
   const int xcd = (int)blockIdx.x & 7;
   const int j = (int)blockIdx.x >> 3;
@@ -194,23 +195,28 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
 #pragma unroll
     for (int i = 0; i < RT; ++i)
       a[i] = i32x8{(int)o.c[i][0], (int)o.c[i][1], (int)o.c[i][2], (int)o.c[i][3], 0, 0, 0, 0};
-    // one column tile at a time: its B operand is read from LDS and feeds RT MFMAs
-#pragma unroll
-    for (int c = 0; c < MC; ++c) {
+    // one column tile at a time: its B operand, read from LDS while the previous tile's
+    // MFMAs run, feeds RT MFMAs
+    auto read_b = [&](int c) {
       const int t = 16 * c + r;  // t mod 16 == r
-      i32x8 bb;
       if constexpr (AF == MXS_ACT_FP8) {
         // values 16h .. 16h+15 of blocks g/2 and g/2 + 2 of group kq: chunks 8kq + g, 8kq + g + 4
         const u32x4 lo = src[t * kRowUnits + ((8 * kq + g) ^ r)];
         const u32x4 hi = src[t * kRowUnits + ((8 * kq + g + 4) ^ r)];
-        bb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       } else {
         const u32x4 v = src[t * kRowUnits + ((4 * kq + g) ^ r)];  // block g of group kq
-        bb = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
       }
+    };
+    i32x8 bb[2];
+    bb[0] = read_b(0);
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+      if (c + 1 < MC) bb[(c + 1) & 1] = read_b(c + 1);
 #pragma unroll
       for (int i = 0; i < RT; ++i)
-        acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bb, acc[i][c], MXS_ACT_FP4, AF, 0,
+        acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bb[c & 1], acc[i][c], MXS_ACT_FP4, AF, 0,
                                                                      (int)sw[i], 0, (int)sx[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -226,36 +232,40 @@ __global__ __launch_bounds__(256 * RQ) void gemm_act_kernel(
       for (int c = 0; c < MC; ++c) asm volatile("" : "+v"(acc[i][c]));
   };
 
-  // Staging and operand loads of step s + 1 go out before the MFMAs of step s; after
-  // the compute each wave waits for its staging loads only (the operand loads issued
-  // after them stay in flight: the counter retires in order), then the barrier makes
-  // every wave's positions visible.
-  Ops oa, ob;
+  // Staging and operand loads of step s + 2 go out before the MFMAs of step s, the staging
+  // first: the counter retires in order, so at the end of step s each wave waits for the
+  // staging of step s + 1 (issued a step before) while the operands of step s + 1 (issued
+  // after it) and everything of step s + 2 stay in flight; then the barrier makes every
+  // wave's positions visible. Three staging buffers and three operand sets rotate.
+  constexpr int kStageLoads = kPerWave + (kTiled ? 1 : 0) + ((kScaleLoads - (kTiled ? kRows / 16 : 0) + kWaves - 1) / kWaves);
+  Ops o0, o1, o2;
   stage_x(0, xbuf0);
-  load_ops(0, oa);
-  __builtin_amdgcn_s_waitcnt(0);
+  load_ops(0, o0);
+  stage_x(1, xbuf1);
+  load_ops(1, o1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(kStageLoads + kOpLoads));
   lds_barrier();
-  // two steps per iteration and one exit; with an odd step count the last step reads
-  // only out-of-range (zero) operands and adds nothing
-  for (int s = 0; s < nsteps; s += 2) {
-    stage_x(s + 1, xbuf1);
+  // The step barrier carries no LDS release fence: such a fence also waits for every direct
+  // global-to-LDS load in flight (they write LDS), which would drain the staging of step
+  // s + 2. Each wave has waited for its own staging of step s + 1 and read its operands of
+  // step s (the MFMAs consumed them), and LDS needs no cache maintenance inside a CU, so a
+  // bare barrier (with a compiler memory clobber) orders the steps.
+  auto step_barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+  auto step = [&](int sc, u32x4* cur, const Ops& oc, u32x4* nxt, Ops& on) {
+    stage_x(sc + 2, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    load_ops(s + 1, ob);
+    load_ops(sc + 2, on);
     __builtin_amdgcn_sched_barrier(0);
-    compute(xbuf0, oa);
+    if (sc < nsteps) compute(cur, oc);  // uniform: past the last window the step adds nothing
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(kOpLoads));
-    lds_barrier();
-    stage_x(s + 2, xbuf0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_ops(s + 2, oa);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(xbuf1, ob);
-    pin_acc();
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(kOpLoads));
-    lds_barrier();
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kOpLoads + kStageLoads));
+    step_barrier();
+  };
+  for (int s = 0; s < nsteps; s += 3) {
+    step(s, xbuf0, o0, xbuf2, o2);
+    step(s + 1, xbuf1, o1, xbuf0, o0);
+    step(s + 2, xbuf2, o2, xbuf1, o1);
   }
 
   // Sum the four k quarters through the staging buffers (free once every load has
