@@ -444,7 +444,10 @@ size_t spec_accept_sampled_workspace_bytes(int32_t b, int32_t kd, int32_t v);
  * top_p           in (0, 1] (1: none). The top-p boundary sums are fp64 with
  *                 an unspecified summation order, so a token whose strictly-
  *                 larger mass is within ~1e-15 * S of top_p * S can fall on
- *                 either side.
+ *                 either side. With top-p alone, the kept law's normaliser is
+ *                 summed in such an order too: its last bits can differ between
+ *                 calls, which moves a decision only where u * q(x) lies within
+ *                 ~1e-15 of p(x).
  * mask            [b, kd+1, ceil(v/32)] uint32 device bits, 4-byte aligned; or
  *                 NULL (no mask).
  * workspace       at least spec_accept_sampled_workspace_bytes(b, kd, v) bytes;
