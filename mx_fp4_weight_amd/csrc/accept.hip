@@ -1575,7 +1575,8 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
                                                                  // chunk counts, the thread maxima)
   __shared__ double hm[kSelB0];     // radix passes: masses
   __shared__ FinishLds L;
-  __shared__ double tab[32];        // 2^(j/32) for write_row_stats (visible after the sort's barriers)
+  __shared__ double tab[32];        // 2^(j/32) for the row statistics: written by wave 0, which the
+                                    // one-wave tail runs on; the other waves read it after a barrier
   __shared__ uint32_t red[4 * kFWaves + 1];
   const int64_t rowg = blockIdx.x;
   const int tid = threadIdx.x;
