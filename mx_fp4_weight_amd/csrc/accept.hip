@@ -626,7 +626,8 @@ struct SelArgs {
   double top_p;   // >= 1: off
   int chunks;     // 4096-logit chunks per row
   int slot_log2;  // > 0: top-k by per-chunk candidates (sel_chunk), 2^slot_log2 per chunk: candidate
-                  // i of chunk c at list position i·2^(kCandLog2 - slot_log2) + c
+                  // i of chunk c at list position i·2^chunk_log2 + c
+  int chunk_log2; // 2^chunk_log2 >= chunks (with slot_log2: the list's first 2^(sum) keys)
 };
 
 // The logit of an order key (inverse of order_key; -0 comes back as +0).
@@ -1072,7 +1073,7 @@ __global__ __launch_bounds__(kThreads) void sel_chunk_kernel(const float* __rest
     // interleaved with the other chunks' candidates, so that a contiguous run of the list holds
     // candidates of many chunks
     uint32_t* out = sb.cand + rowg * kCand + c;
-    const int c2 = kCandLog2 - sa.slot_log2;
+    const int c2 = sa.chunk_log2;
     uint32_t slot = (uint32_t)incl - (uint32_t)mine;
 #pragma unroll
     for (int q = 0; q < kPer; ++q)
@@ -1354,7 +1355,7 @@ __device__ __forceinline__ uint32_t maxima_bound(const uint32_t* keys, int n, in
 // more candidates than its slots. *rk: the row's largest allowed finite key (0: none); *bad: a
 // NaN or +inf in the row. LDS: cnt_l (kMaxSelChunks words), tm (kFThreads words, 16-byte
 // aligned), red (4·kFWaves + 1 words). The records and the slots load together.
-__device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, int chunks, int slot_log2, int k,
+__device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, int chunks, int slot_log2, int c2, int k,
                                              uint32_t* keys, uint32_t* cnt_l, uint32_t* tm, uint32_t* red,
                                              uint32_t* rk, bool* bad) {
   constexpr int kRecPer = kMaxSelChunks / kFThreads;
@@ -1363,7 +1364,7 @@ __device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, in
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const u32x4* rec = reinterpret_cast<const u32x4*>(sb.cnt + rowg * kSelB0);
   const u32x4* cs = reinterpret_cast<const u32x4*>(sb.cand + rowg * kCand);
-  const int c2 = kCandLog2 - slot_log2;  // list position i·2^c2 + c: candidate i of chunk c
+  const int slots = 1 << (slot_log2 + c2);  // list position i·2^c2 + c: candidate i of chunk c
   u32x4 r[kRecPer], kv[kVecPer];
 #pragma unroll
   for (int i = 0; i < kRecPer; ++i) {
@@ -1372,7 +1373,8 @@ __device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, in
   }
 #pragma unroll
   for (int u = 0; u < kVecPer; ++u) {
-    kv[u] = cs[tid + kFThreads * u];
+    const int e4 = tid + kFThreads * u;
+    kv[u] = 4 * e4 < slots ? cs[e4] : u32x4{0u, 0u, 0u, 0u};
   }
   int flags = 0;
   uint32_t lmax = 0u, kmax = 0u;
@@ -1415,7 +1417,7 @@ __device__ __forceinline__ int gather_chunks(const SelBufs& sb, int64_t rowg, in
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * (tid + kFThreads * u) + i;
       const int c = e & cmask;
-      const bool ok = c < chunks && (uint32_t)(e >> c2) < cnt_l[c] && kv[u][i] >= lstar;
+      const bool ok = e < slots && c < chunks && (uint32_t)(e >> c2) < cnt_l[c] && kv[u][i] >= lstar;
       take |= ok ? 1u << (4 * u + i) : 0u;
       m = ok ? max(m, kv[u][i]) : m;
     }
@@ -1594,7 +1596,8 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
   bool digit0 = false;   // kSelCompactK: the boundary's digit-0 bucket (st.lo) and carry are known
   if (sa.slot_log2 > 0) {
     uint32_t rk;
-    n = gather_chunks(sb, rowg, sa.chunks, sa.slot_log2, sa.top_k, keys, hc, hc + kMaxSelChunks, red, &rk, &bad_row);
+    n = gather_chunks(sb, rowg, sa.chunks, sa.slot_log2, sa.chunk_log2, sa.top_k, keys, hc, hc + kMaxSelChunks, red,
+                      &rk, &bad_row);
     st.rmax = rk ? key_logit(rk) : -INFINITY;
     st.mode = rk == 0u ? kSelDone : (n < 0 ? kSelSlowKFull : kSelCompactK);
   } else {
@@ -2066,12 +2069,16 @@ hipError_t launch_selection(const float* target, const float* draft, int32_t b, 
   sa.slot_log2 = 0;
   if (sa.top_k > 0 && chunks <= kMaxSelChunks) {
     // top-k by per-chunk candidates when k is at most the threads of a chunk's workgroup and
-    // each chunk's share of the list holds twice k: the list splits into 2^c2 >= chunks
-    // interleaved shares of 2^(kCandLog2 - c2) slots
+    // 2^c2 >= chunks interleaved shares of 2^lg slots, the smallest power of two (at least 8)
+    // holding twice k, fit the list (the finishing workgroup reads only those 2^(c2 + lg))
     int c2 = 0;
     while ((1 << c2) < chunks) ++c2;
-    const int lg = kCandLog2 - c2;
-    if (lg >= 3 && sa.top_k <= kThreads && 2 * (int64_t)sa.top_k <= (int64_t(1) << lg)) sa.slot_log2 = lg;
+    int lg = 3;
+    while ((int64_t(1) << lg) < 2 * (int64_t)sa.top_k) ++lg;
+    if (sa.top_k <= kThreads && c2 + lg <= kCandLog2) {
+      sa.slot_log2 = lg;
+      sa.chunk_log2 = c2;
+    }
   }
   const dim3 g1((unsigned)rows, (unsigned)chunks);
   if (sa.slot_log2 > 0) {
@@ -2165,7 +2172,7 @@ hipError_t launch_sampling_thresholds(const float* logits, int32_t rows, int32_t
   sb.cand = reinterpret_cast<uint32_t*>(base + L.cand);
   sb.rbad = reinterpret_cast<uint32_t*>(base + L.rbad);
   sb.thr = out_thr;
-  const SelArgs sa{use_k ? sp.top_k : 0, use_p ? (double)sp.top_p : 1.0, 0, 0};
+  const SelArgs sa{use_k ? sp.top_k : 0, use_p ? (double)sp.top_p : 1.0, 0, 0, 0};
   // one "sequence" per row with no draft rows: row s is logits + s·v, mask row s
   return launch_selection(logits, nullptr, rows, 0, v, tr, sb, sa, SelStats{}, vec4, stream);
 }
@@ -2214,7 +2221,7 @@ hipError_t launch_spec_accept(const float* target, const float* draft, const int
       sb.cand = reinterpret_cast<uint32_t*>(base + L.selcand);
       sb.thr = reinterpret_cast<uint32_t*>(base + L.thr);
       sb.rbad = reinterpret_cast<uint32_t*>(base + L.selrbad);
-      const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0, 0, 0};
+      const SelArgs sa{use_k ? sp->top_k : 0, use_p ? (double)sp->top_p : 1.0, 0, 0, 0};
       const SelStats ss{ws.cmax, ws.csum, ws.cbad, ws.gz, reinterpret_cast<uint32_t*>(base + L.sdone), tokens,
                         chunks};
       if ((e = launch_selection(target, draft, b, kd, v, tr, sb, sa, ss, vec4, stream)) != hipSuccess) return e;
