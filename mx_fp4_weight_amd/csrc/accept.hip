@@ -621,6 +621,33 @@ struct SelStats {
   int chunks;
 };
 
+// The logit of a row's draft token for the statistics the selection writes (the stats kernel's
+// gz), loaded by one thread early in the finishing workgroup so that its two dependent loads (the
+// token, then its logit and mask word) are not at the end of the workgroup's life.
+struct DraftLogit {
+  int xi = -1;          // the token; -1: the bonus row, no statistics, or a token outside [0, v)
+  float zx = 0.0f;      // its logit
+  uint32_t word = ~0u;  // its mask word (all ones without a mask)
+
+  __device__ void load_token(const SelStats& ss, int64_t s, int j, int kd, int v) {
+    if (!ss.cmax) return;
+    if (j < kd) xi = ss.tokens[(size_t)s * kd + j];
+    else if (j > kd) xi = ss.tokens[(size_t)s * kd + (j - kd - 1)];
+    if (xi >= v) xi = -1;
+  }
+  __device__ void load_logit(const float* __restrict__ z, const uint32_t* mw) {
+    if (xi < 0) return;
+    zx = z[xi];
+    if (mw) word = mw[xi >> 5];
+  }
+  // gz: the logit if the token is allowed and kept (key >= thr), else -inf
+  __device__ void put(const SelStats& ss, int64_t rowg, uint32_t thr) const {
+    if (xi < 0) return;
+    const bool allowed = ((word >> (xi & 31)) & 1u) != 0u;
+    ss.gz[rowg] = (allowed && order_key(zx) >= thr) ? zx : -INFINITY;
+  }
+};
+
 struct SelArgs {
   int top_k;      // 0: off
   double top_p;   // >= 1: off
@@ -1477,8 +1504,7 @@ __device__ inline double shfl_f64(double v, int src) {
 // with_stats, the row's statistics as write_row_stats writes them. Returns the threshold (every lane).
 __device__ __forceinline__ uint32_t wave_tail(const uint32_t* keys, int n, int k, double p, float rmax, double inv_tau,
                                               const double* tab, const SelStats& ss, bool with_stats, int64_t rowg,
-                                              int64_t s, int j,
-                                              int kd, int v, const float* __restrict__ z, const uint32_t* mw) {
+                                              const DraftLogit& dl) {
   if (n <= 0) return 0u;
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t x = lane < n ? keys[lane] : 0u;  // 0 is below every live key: the padding sorts last
@@ -1513,16 +1539,7 @@ __device__ __forceinline__ uint32_t wave_tail(const uint32_t* keys, int n, int k
       ss.csum[o] = c == 0 ? sum : 0.0;
       ss.cbad[o] = 0;
     }
-    if (lane == 0) {
-      int xi = -1;
-      if (j < kd) xi = ss.tokens[(size_t)s * kd + j];
-      else if (j > kd) xi = ss.tokens[(size_t)s * kd + (j - kd - 1)];
-      if (xi >= 0 && xi < v) {
-        const float zx = z[xi];
-        const bool allowed = mw ? ((mw[xi >> 5] >> (xi & 31)) & 1u) != 0u : true;
-        ss.gz[rowg] = (allowed && order_key(zx) >= thr) ? zx : -INFINITY;
-      }
-    }
+    if (lane == 0) dl.put(ss, rowg, thr);
   }
   return thr;
 }
@@ -1532,8 +1549,7 @@ __device__ __forceinline__ uint32_t wave_tail(const uint32_t* keys, int n, int k
 // empty other chunks, which the decide kernel combines to the same (max, S); the live logit of
 // the row's draft token (threshold thr). Every thread calls it with the same sum.
 __device__ __forceinline__ void put_row_stats(double sum, uint32_t thr, float rmax, const SelStats& ss, int64_t rowg,
-                                              int64_t s, int j, int kd, int v, const float* __restrict__ z,
-                                              const uint32_t* mw) {
+                                              const DraftLogit& dl) {
   const int tid = threadIdx.x;
   for (int c = tid; c < ss.chunks; c += kFThreads) {
     const size_t o = (size_t)rowg * ss.chunks + c;
@@ -1541,16 +1557,7 @@ __device__ __forceinline__ void put_row_stats(double sum, uint32_t thr, float rm
     ss.csum[o] = c == 0 ? sum : 0.0;
     ss.cbad[o] = 0;
   }
-  if (tid == 0) {
-    int xi = -1;
-    if (j < kd) xi = ss.tokens[(size_t)s * kd + j];
-    else if (j > kd) xi = ss.tokens[(size_t)s * kd + (j - kd - 1)];
-    if (xi >= 0 && xi < v) {
-      const float zx = z[xi];
-      const bool allowed = mw ? ((mw[xi >> 5] >> (xi & 31)) & 1u) != 0u : true;
-      ss.gz[rowg] = (allowed && order_key(zx) >= thr) ? zx : -INFINITY;
-    }
-  }
+  if (tid == 0) dl.put(ss, rowg, thr);
 }
 
 // put_row_stats for a kept set of carry (the mass of the kept tokens outside the list) plus the
@@ -1558,13 +1565,12 @@ __device__ __forceinline__ void put_row_stats(double sum, uint32_t thr, float rm
 // key per thread for n <= kFThreads, so a sorted list gives a sum in the sorted order).
 __device__ __forceinline__ void write_row_stats(const uint32_t* keys, int n, uint32_t thr, double carry, float rmax,
                                                 double inv_tau, const double* tab, const SelStats& ss,
-                                                int64_t rowg, int64_t s, int j, int kd, int v,
-                                                const float* __restrict__ z, const uint32_t* mw, FinishLds& L) {
+                                                int64_t rowg, const DraftLogit& dl, FinishLds& L) {
   double e = 0.0;
   for (int i = threadIdx.x; i < n; i += kFThreads)
     if (keys[i] >= thr) e += exp_neg_f64_tab(((double)key_logit(keys[i]) - (double)rmax) * inv_tau, tab);
   const double sum = carry + block_sum_f64<kFThreads>(e, L.scan);
-  put_row_stats(sum, thr, rmax, ss, rowg, s, j, kd, v, z, mw);
+  put_row_stats(sum, thr, rmax, ss, rowg, dl);
 }
 
 template <bool kVec4>
@@ -1588,6 +1594,8 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
   const int j = (int)(rowg % per_seq);
   const bool use_p = sa.top_p < 1.0;
   const double kf = (double)sa.top_k;
+  DraftLogit dl;
+  if (tid == 0) dl.load_token(ss, s, j, kd, v);  // first: its wait is absorbed by the next one
   bool stats_done = false;
   uint32_t thr = 0u;
   SelState st{};
@@ -1622,6 +1630,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
       }
     }
   }
+  if (tid == 0) dl.load_logit(row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)));
   if (st.mode == kSelCompactK) {
     // keys[0, n) hold every key the row's top-k keeps; cut them towards the kept set
     uint32_t thr_k = 0u;
@@ -1641,8 +1650,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
       // the usual case: one wave, no barrier
       if (tid < kWave)
         thr = wave_tail(keys, n, sa.top_k, use_p ? sa.top_p : 1.0, st.rmax, tr.inv_tau, tab,
-                        ss, with_stats, rowg, s, j, kd, v, row_ptr(target, draft, s, kd, j, v),
-                        mask_words(tr, s, kd, mask_row(j, kd)));
+                        ss, with_stats, rowg, dl);
       stats_done = with_stats;
     } else if (n > kWave) {
       sort_desc(keys, n);
@@ -1659,8 +1667,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
       }
       // the kept set is here, sorted: the row's statistics too (the stats kernel skips it)
       if (with_stats) {
-        write_row_stats(keys, n, thr, 0.0, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
-                        row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
+        write_row_stats(keys, n, thr, 0.0, st.rmax, tr.inv_tau, tab, ss, rowg, dl, L);
         stats_done = true;
       }
     }
@@ -1675,8 +1682,7 @@ __global__ __launch_bounds__(kFThreads) void sel_finish_kernel(const float* __re
     // the kept set: every token above the boundary bucket (mass st.carry) and the bucket's keys
     // from thr up, so the row's statistics are known here too (the stats kernel skips the row)
     if (ss.cmax && n > 0 && !bad_row) {
-      write_row_stats(keys, n, thr, st.carry, st.rmax, tr.inv_tau, tab, ss, rowg, s, j, kd, v,
-                      row_ptr(target, draft, s, kd, j, v), mask_words(tr, s, kd, mask_row(j, kd)), L);
+      write_row_stats(keys, n, thr, st.carry, st.rmax, tr.inv_tau, tab, ss, rowg, dl, L);
       stats_done = true;
     }
   } else if (st.mode != kSelDone) {
