@@ -257,10 +257,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   double acc = 0.0;
   if (mx != -INFINITY && !bad) {
     const double m64 = (double)mx;
+    const ExpK ek = exp_consts();
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      if constexpr (kT) acc += exp_neg_f64_tab(((double)vals[q] - m64) * tr.inv_tau, tab);
-      else acc += exp_neg_f64_tab((double)vals[q] - m64, tab);
+      if constexpr (kT) acc += exp_neg_f64_tab(((double)vals[q] - m64) * tr.inv_tau, tab, ek);
+      else acc += exp_neg_f64_tab((double)vals[q] - m64, tab, ek);
     }
   }
   acc = block_sum_f64<kThreads>(acc, lds_d);
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
 // p_n(t) and the final weight of token t: residual (p - q)+, or p for the bonus row.
 struct FinalRows {
   const double* tab;  // kExp2Table32 in LDS, for exp_neg_f64_tab
+  ExpK ek;            // its constants, in registers
   const float* zt;
   const float* zd;  // nullptr for the bonus row
   double mt, inv_st, md, inv_sd;
@@ -293,11 +295,11 @@ __device__ inline void weights_from(const FinalRows& fr, const float (&zt)[kWPer
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
     const double dt = kT ? ((double)zt[j] - fr.mt) * fr.inv_tau : (double)zt[j] - fr.mt;
-    const double p = exp_neg_f64_tab(dt, fr.tab) * fr.inv_st;
+    const double p = exp_neg_f64_tab(dt, fr.tab, fr.ek) * fr.inv_st;
     wp[j] = p;
     if (fr.zd) {
       const double dd = kT ? ((double)zd[j] - fr.md) * fr.inv_tau : (double)zd[j] - fr.md;
-      const double q = exp_neg_f64_tab(dd, fr.tab) * fr.inv_sd;
+      const double q = exp_neg_f64_tab(dd, fr.tab, fr.ek) * fr.inv_sd;
       const double d = p - q;
       wf[j] = d > 0.0 ? d : 0.0;
     } else {
@@ -880,6 +882,8 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(const float* __rest
   float mx = -INFINITY;
   const int c0 = (int)blockIdx.y * cpw, c1 = min(chunks, c0 + cpw);
   int bad = 0;
+  ExpK ek{};
+  if constexpr (kMass) ek = exp_consts();
   for (int c = c0; c < c1; ++c) {
     float vals[kPer];
     chunk_logits<kVec4>(zrow, mw, c * kChunk, v, vals, &bad);
@@ -891,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(const float* __rest
       mx = fmaxf(mx, zq);
       const int b = (int)(order_key(zq) >> kSelShift0);
       // exp(z / tau) against 0 (the range check below discards rows where this overflows)
-      if constexpr (kMass) atomicAdd(&hm[b], exp_neg_f64_tab((double)zq * tr.inv_tau, tab));
+      if constexpr (kMass) atomicAdd(&hm[b], exp_neg_f64_tab((double)zq * tr.inv_tau, tab, ek));
       else atomicAdd(&hc[b], 1u);
     }
   }
@@ -1946,6 +1950,7 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
     double a = 0.0, b = 0.0;
     FinalRows fr;
     fr.tab = tab;
+    fr.ek = exp_consts();
     if (n >= 0) {
       fr.zt = row_ptr(target, draft, s, kd, n, v);
       fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
@@ -2016,6 +2021,7 @@ __global__ __launch_bounds__(kWThreads) void sample_kernel(
   if (d.n < 0) return;
   FinalRows fr;
   fr.tab = tab;
+  fr.ek = exp_consts();
   fr.zt = row_ptr(target, draft, s, kd, d.n, v);
   fr.zd = d.n < kd ? row_ptr(target, draft, s, kd, kd + 1 + d.n, v) : nullptr;
   fr.mt = d.mt;

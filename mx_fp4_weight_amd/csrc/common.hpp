@@ -115,6 +115,34 @@ __host__ __device__ inline double exp_neg_f64_tab(double d, const double* tab) {
   return __builtin_ldexp(tab[n & 31] * p, n >> 5);
 }
 
+// The non-inline constants of exp_neg_f64_tab, held in registers. exp_consts() passes them
+// through an empty asm statement, so the compiler cannot rebuild them before every use (it
+// otherwise copies a constant into the accumulator of each Horner step: about six vector moves
+// per exponential). Same operations, same order: bit-identical results.
+struct ExpK {
+  double inv_l, l1, l2, c5, c4, c3;
+};
+__device__ inline ExpK exp_consts() {
+  ExpK k{46.166241308446828, 6.93147180369123816490e-01 / 32.0, 1.90821492927058770002e-10 / 32.0,
+         8.33333333333333333333e-03, 4.16666666666666666667e-02, 1.66666666666666666667e-01};
+  asm volatile("" : "+v"(k.inv_l), "+v"(k.l1), "+v"(k.l2), "+v"(k.c5), "+v"(k.c4), "+v"(k.c3));
+  return k;
+}
+__device__ inline double exp_neg_f64_tab(double d, const double* tab, const ExpK& k) {
+  if (!(d > -745.0)) return 0.0;
+  const double nd = __builtin_rint(d * k.inv_l);
+  double r = __builtin_fma(-nd, k.l1, d);
+  r = __builtin_fma(-nd, k.l2, r);
+  const int n = (int)nd;
+  double p = k.c5;
+  p = __builtin_fma(p, r, k.c4);
+  p = __builtin_fma(p, r, k.c3);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return __builtin_ldexp(tab[n & 31] * p, n >> 5);
+}
+
 // Lane exchanges inside a wave. DPP moves (a VALU operand modifier, no LDS trip) cover the
 // steps inside each 16-lane row: swaps within groups of four, then rotations of the row by 4
 // and 8; the two steps across rows (16, 32) go through ds_bpermute.

@@ -102,8 +102,9 @@ __global__ __launch_bounds__(kTh) void tree_stats_kernel(const float* __restrict
   double acc = 0.0;
   if (mx != -INFINITY && !bad && !leaf_draft) {
     const double m64 = (double)mx;
+    const ExpK ek = exp_consts();
 #pragma unroll
-    for (int q = 0; q < kSPer; ++q) acc += exp_neg_f64_tab((double)vals[q] - m64, tab);
+    for (int q = 0; q < kSPer; ++q) acc += exp_neg_f64_tab((double)vals[q] - m64, tab, ek);
   }
   acc = block_sum_f64<kTh>(acc, lds_d);
   if (threadIdx.x == 0) {
@@ -188,7 +189,7 @@ struct NodeLaw {
 };
 
 __device__ inline void law_weights(const NodeLaw& nl, int r, int t0, int v, bool vec4, const double* tab,
-                                   double (&w)[kWPerT]) {
+                                   const ExpK& ek, double (&w)[kWPerT]) {
   float zt[kWPerT], zd[kWPerT];
   if (vec4 && t0 + kWPerT <= v) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(nl.zt + t0);
@@ -209,9 +210,9 @@ __device__ inline void law_weights(const NodeLaw& nl, int r, int t0, int v, bool
   }
 #pragma unroll
   for (int j = 0; j < kWPerT; ++j) {
-    double x = exp_neg_f64_tab((double)zt[j] - nl.mt, tab) * nl.inv_st;
+    double x = exp_neg_f64_tab((double)zt[j] - nl.mt, tab, ek) * nl.inv_st;
     if (r > 0) {
-      const double q = exp_neg_f64_tab((double)zd[j] - nl.md, tab) * nl.inv_sd;
+      const double q = exp_neg_f64_tab((double)zd[j] - nl.md, tab, ek) * nl.inv_sd;
       for (int i = 1; i <= r; ++i) {
         const double d = x / nl.z[i] - q;
         x = d > 0.0 ? d : 0.0;
@@ -260,11 +261,12 @@ __global__ __launch_bounds__(kTh) void tree_pass_kernel(const float* __restrict_
   }
   __syncthreads();
   nl.z = s_z;
+  const ExpK ek = exp_consts();
   for (int i = 0; i < ppw; ++i) {
     const int piece = (int)blockIdx.x * ppw + i;
     if (piece >= pieces) break;  // uniform
     double w[kWPerT];
-    law_weights(nl, r, piece * kTPiece + (int)threadIdx.x * kWPerT, v, kVec4, tab, w);
+    law_weights(nl, r, piece * kTPiece + (int)threadIdx.x * kWPerT, v, kVec4, tab, ek, w);
     double t = 0.0;
 #pragma unroll
     for (int j = 0; j < kWPerT; ++j) t += w[j];
@@ -405,12 +407,13 @@ __global__ __launch_bounds__(kTh) void tree_walk_kernel(const float* __restrict_
   // final token from L_f = w_f / Z_f of row rho by inverse CDF: the piece, then the thread,
   // then the token
   double* ptw = ws.ptot + (((size_t)(f - 1) * b + s) * (n + 1) + rho) * pieces;
+  const ExpK ek = exp_consts();
   if (f == 1 && topo.off[rho + 1] > topo.off[rho]) {
     // an inner node drawing from p (after a zero residual): the pass left its totals of p out,
     // so this workgroup computes them, piece by piece, exactly as the pass computes them
     for (int pc = 0; pc < pieces; ++pc) {
       double w[kWPerT];
-      law_weights(nl, 0, pc * kTPiece + (int)threadIdx.x * kWPerT, v, kVec4, tab, w);
+      law_weights(nl, 0, pc * kTPiece + (int)threadIdx.x * kWPerT, v, kVec4, tab, ek, w);
       double t = 0.0;
 #pragma unroll
       for (int j = 0; j < kWPerT; ++j) t += w[j];
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(kTh) void tree_walk_kernel(const float* __restrict_
   if (piece >= 0) {
     const int t0 = piece * kTPiece + (int)threadIdx.x * kWPerT;
     double w[kWPerT];
-    law_weights(nl, f - 1, t0, v, kVec4, tab, w);
+    law_weights(nl, f - 1, t0, v, kVec4, tab, ek, w);
     double tt = 0.0;
 #pragma unroll
     for (int j = 0; j < kWPerT; ++j) tt += w[j];
