@@ -218,10 +218,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
       vals[q] = e < v ? z[e] : -INFINITY;
     }
   }
-  // the logit of this row's draft token x (target row i < kd or draft row i), if it is in this chunk
+  // the logit of this row's draft token x (target row i < kd or draft row i), if it is in this
+  // chunk: thread 0 loads it (and its mask word) with the chunk and stores it at the end
   int xi = -1;
   if (j < kd) xi = tokens[(size_t)s * kd + j];
   else if (j > kd) xi = tokens[(size_t)s * kd + (j - kd - 1)];
+  const bool x_here = xi >= base && xi < base + kChunk;  // uniform
   float mx = -INFINITY;
   int bad = 0;
   const uint32_t* mw = nullptr;
@@ -229,6 +231,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   if constexpr (kT) {
     mw = mask_words(tr, s, kd, mask_row(j, kd));
     thr = tr.thr ? tr.thr[rowg] : 0u;
+  }
+  float zx = -INFINITY;     // past the row: -inf, as the chunk's own padding
+  uint32_t xword = ~0u;
+  if (x_here && threadIdx.x == 0 && xi < v) {
+    zx = z[xi];
+    if (kT && mw) xword = mw[xi >> 5];
   }
   // mask words: one per 4 tokens on the vector path; the word index is clamped into the
   // row (tokens past v are already -inf)
@@ -251,7 +259,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
       vals[q] = ok ? vals[q] : -INFINITY;
     }
     mx = fmaxf(mx, vals[q]);
-    if (e == xi) ws.gz[rowg] = vals[q];
+  }
+  if (x_here && threadIdx.x == 0) {
+    if constexpr (kT) zx = (((xword >> (xi & 31)) & 1u) && order_key(zx) >= thr) ? zx : -INFINITY;
+    ws.gz[rowg] = zx;
   }
   block_max_or<kThreads>(mx, bad, lds_f, lds_i);
   double acc = 0.0;
