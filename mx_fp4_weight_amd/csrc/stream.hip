@@ -1,7 +1,7 @@
 // mxs_stream_read: a plain read of a device buffer, the measured ceiling of the weight stream.
 //
 // A verification step that streams every weight once is bounded by Q <= BW / W ("Module 11.
-// Speculative Decoding and Quantization", §1): the verify GEMM's achieved bandwidth is judged
+// Speculative Decoding and Quantization", §1): the verify GEMM's achieved bandwidth is measured
 // against BW. This kernel measures the BW a single kernel can draw from HBM on this device with
 // nothing else to do: every lane issues 8 independent 16-byte non-temporal loads per step (the
 // data is read once, so it is not kept in the caches), folds them into an XOR, and writes the

@@ -8,7 +8,7 @@ from oracle import gemm as ogemm
 
 DEV = "cuda"
 
-# GEMM tolerances: the judged bar is relative L2 <= 2e-3 against the fp64 oracle;
+# GEMM tolerances: the parity bar is relative L2 <= 2e-3 against the fp64 oracle;
 # each element must also sit within 1e-4 of sum_k |x_k w_k| (fp32 summation of
 # at most a few hundred partial sums per output is orders of magnitude tighter),
 # which catches a single wrong block that an L2 norm over many rows would hide.
