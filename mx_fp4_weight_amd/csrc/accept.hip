@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   }
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    bad |= (vals[q] != vals[q]) | (vals[q] == INFINITY);
+    bad |= (int)nan_or_pinf(vals[q]);
     const int e = kVec4 ? base + 4 * (threadIdx.x + kThreads * (q / 4)) + (q % 4)
                         : base + threadIdx.x + kThreads * q;
     if constexpr (kT) {
@@ -711,7 +711,7 @@ __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t*
       for (int i = 0; i < 4; ++i) {
         const float x = t[q][i];
         const uint32_t fin = __builtin_isfinite(x) ? 1u : 0u;
-        b |= (int)(in & !fin & (x > -INFINITY || x != x));  // NaN or +inf
+        b |= (int)(in & nan_or_pinf(x));
         const uint32_t ok = (uint32_t)in & (w[q] >> ((e + i) & 31)) & fin;
         vals[4 * q + i] = ok ? x : NAN;
       }
@@ -740,7 +740,7 @@ __device__ inline void chunk_logits(const float* __restrict__ z, const uint32_t*
       const bool in = e < v;
       const float x = t[q];
       const uint32_t fin = __builtin_isfinite(x) ? 1u : 0u;
-      b |= (int)(in & !fin & (x > -INFINITY || x != x));  // NaN or +inf
+      b |= (int)(in & nan_or_pinf(x));
       const uint32_t ok = (uint32_t)in & (w[q] >> (e & 31)) & fin;
       vals[q] = ok ? x : NAN;
     }

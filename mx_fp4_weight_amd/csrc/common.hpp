@@ -115,6 +115,9 @@ __host__ __device__ inline double exp_neg_f64_tab(double d, const double* tab) {
   return __builtin_ldexp(tab[n & 31] * p, n >> 5);
 }
 
+// NaN or +inf, in one class test (v_cmp_class_f32, class bits: signalling NaN, quiet NaN, +inf).
+__device__ inline bool nan_or_pinf(float x) { return __builtin_amdgcn_classf(x, 0x203); }
+
 // The non-inline constants of exp_neg_f64_tab, held in registers. exp_consts() passes them
 // through an empty asm statement, so the compiler cannot rebuild them before every use (it
 // otherwise copies a constant into the accumulator of each Horner step: about six vector moves

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kTh) void tree_stats_kernel(const float* __restrict
   int bad = 0;
 #pragma unroll
   for (int q = 0; q < kSPer; ++q) {
-    bad |= (vals[q] != vals[q]) | (vals[q] == INFINITY);
+    bad |= (int)nan_or_pinf(vals[q]);
     mx = fmaxf(mx, vals[q]);
   }
   block_max_or<kTh>(mx, bad, lds_f, lds_i);
