@@ -1953,28 +1953,31 @@ __global__ __launch_bounds__(kWThreads, kPrefetch ? 4 : 8) void decide_kernel(
   // 3. piece total of the final weights: thread totals in token order, then
   // the same block scan the sample kernel uses, so both see identical totals
   const int n = s_n;
+  // the final rows' laws, the same for every piece of this workgroup (set up once)
+  FinalRows fr;
+  fr.tab = tab;
+  fr.ek = exp_consts();
+  if (n >= 0) {
+    fr.zt = row_ptr(target, draft, s, kd, n, v);
+    fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
+    fr.mt = smax[n];
+    fr.inv_st = 1.0 / ssum[n];
+    fr.md = n < kd ? smax[kd + 1 + n] : 0.0;
+    fr.inv_sd = n < kd ? 1.0 / ssum[kd + 1 + n] : 0.0;
+    if constexpr (kT) {
+      fr.inv_tau = tr.inv_tau;
+      fr.thr_t = tr.thr ? tr.thr[(size_t)s * per_seq + n] : 0u;
+      fr.thr_d = (tr.thr && n < kd) ? tr.thr[(size_t)s * per_seq + kd + 1 + n] : 0u;
+      fr.mw = mask_words(tr, s, kd, n);
+    }
+  }
 #pragma unroll
   for (int pc = 0; pc < kPer; ++pc) {
     const int cp = c * kPer + pc;  // this piece (uniform: the loop holds block scans)
     if (cp >= pieces) break;
     const int t0p = cp * kPiece + threadIdx.x * kWPer;
     double a = 0.0, b = 0.0;
-    FinalRows fr;
-    fr.tab = tab;
-    fr.ek = exp_consts();
     if (n >= 0) {
-      fr.zt = row_ptr(target, draft, s, kd, n, v);
-      fr.zd = n < kd ? row_ptr(target, draft, s, kd, kd + 1 + n, v) : nullptr;
-      fr.mt = smax[n];
-      fr.inv_st = 1.0 / ssum[n];
-      fr.md = n < kd ? smax[kd + 1 + n] : 0.0;
-      fr.inv_sd = n < kd ? 1.0 / ssum[kd + 1 + n] : 0.0;
-      if constexpr (kT) {
-        fr.inv_tau = tr.inv_tau;
-        fr.thr_t = tr.thr ? tr.thr[(size_t)s * per_seq + n] : 0u;
-        fr.thr_d = (tr.thr && n < kd) ? tr.thr[(size_t)s * per_seq + kd + 1 + n] : 0u;
-        fr.mw = mask_words(tr, s, kd, n);
-      }
       double wf[kWPer], wp[kWPer];
       if (pre) {
         float zt[kWPer], zd[kWPer];
